@@ -1,0 +1,109 @@
+"""Alternative formulations of the delta-rule recurrence, used only to pin the
+oracle (tests infrastructure; nothing in the product imports this file).
+
+* ``unrolled_product`` -- explicit product of per-token transition matrices.
+* ``chunked_wy``       -- chunkwise UT/WY form with a triangular solve.
+
+Both take the per-token gates from ``oracle._gates_per_token`` so that the
+pins exercise the recurrence algebra; the gate definitions themselves are
+pinned separately by closed forms in ``test_oracle.py``.
+"""
+import numpy as np
+
+from oracle import ALPHA_NONE, ALPHA_SCALAR, ALPHA_VEC, GATE_SCALAR, GATE_VEC, GAMMA_SAME_AS_BETA
+from oracle import _gates_per_token, _f64
+
+
+def unrolled_product(q, k, v, alpha_mode, log_alpha, beta_mode, beta, gamma_mode,
+                     gamma, precond_eps=-1.0, A0=None, S0=None):
+    """Explicit transition-matrix form for tiny inputs.
+
+    With M_t = (I - kt kt^T) Diag(alpha_t) and Phi_{t:s} = M_t ... M_s,
+        S_t = Phi_{t:1} S_0 + sum_{s<=t} Phi_{t:s+1} kt_s vt_s^T,
+    which is the closed form of the delta rule written as a diagonal-plus-
+    low-rank linear recurrence (FG^2-GDN, 2.1 and 2.3).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    o = np.zeros((B, H, T, dv))
+    ST = np.zeros((B, H, dk, dv))
+    I = np.eye(dk)
+    for b in range(B):
+        for h in range(H):
+            sel = lambda x: None if x is None else _f64(x)[b, h]
+            alpha, be, ga, _ = _gates_per_token(alpha_mode, sel(log_alpha), beta_mode,
+                                                sel(beta), gamma_mode, sel(gamma),
+                                                precond_eps, sel(A0), k[b, h], dk, dv)
+            kts = [np.sqrt(be[t]) * k[b, h, t] for t in range(T)]
+            vts = [np.sqrt(ga[t]) * v[b, h, t] for t in range(T)]
+            Ms = [(I - np.outer(kts[t], kts[t])) @ np.diag(alpha[t]) for t in range(T)]
+            S0bh = np.zeros((dk, dv)) if S0 is None else _f64(S0)[b, h]
+            for t in range(T):
+                # Phi_{t:1}
+                Phi = I.copy()
+                for s in range(t + 1):
+                    Phi = Ms[s] @ Phi
+                St = Phi @ S0bh
+                for s in range(t + 1):
+                    P = I.copy()
+                    for r in range(s + 1, t + 1):
+                        P = Ms[r] @ P
+                    St = St + P @ np.outer(kts[s], vts[s])
+                o[b, h, t] = St.T @ q[b, h, t]
+                if t == T - 1:
+                    ST[b, h] = St
+            if T == 0:
+                ST[b, h] = S0bh
+    return o, ST
+
+
+def chunked_wy(q, k, v, alpha_mode, log_alpha, beta_mode, beta, gamma_mode,
+               gamma, precond_eps=-1.0, A0=None, S0=None, C=16):
+    """Chunkwise-parallel form with a per-chunk unit-lower-triangular solve.
+
+    Within a chunk (positions r = 1..C, cumulative log-decay G_r per key
+    channel, Gamma_r = exp(G_r)):
+        T_rs = sum_i kt_ri kt_si exp(G_ri - G_si)            (s < r)
+        P_rs = sum_i q_ri  kt_si exp(G_ri - G_si)            (s <= r)
+        (I + T) U = Vt - (Kt (.) Gamma) S_0                    (forward solve)
+        O = (Q (.) Gamma) S_0 + P U
+        S_C = Diag(Gamma_C) S_0 + (Kt (.) exp(G_C - G))^T U
+    This is the UT/WY chunk algorithm the pages describe (Gated DeltaNet-2,
+    "chunk parallel training": the decay absorbed into the erase/write
+    matrices and a lower-triangular (I+T)^-1 solve).  fp64, for pins only.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    o = np.zeros((B, H, T, dv))
+    ST = np.zeros((B, H, dk, dv))
+    for b in range(B):
+        for h in range(H):
+            sel = lambda x: None if x is None else _f64(x)[b, h]
+            alpha, be, ga, _ = _gates_per_token(alpha_mode, sel(log_alpha), beta_mode,
+                                                sel(beta), gamma_mode, sel(gamma),
+                                                precond_eps, sel(A0), k[b, h], dk, dv)
+            logal = np.log(alpha)
+            S = np.zeros((dk, dv)) if S0 is None else _f64(S0)[b, h].copy()
+            for c0 in range(0, T, C):
+                c1 = min(c0 + C, T)
+                Kt = np.sqrt(be[c0:c1]) * k[b, h, c0:c1]
+                Vt = np.sqrt(ga[c0:c1]) * v[b, h, c0:c1]
+                Q = q[b, h, c0:c1]
+                G = np.cumsum(logal[c0:c1], axis=0)
+                n = c1 - c0
+                Tm = np.zeros((n, n))
+                Pm = np.zeros((n, n))
+                for r in range(n):
+                    for s in range(r + 1):
+                        dec = np.exp(G[r] - G[s])
+                        if s < r:
+                            Tm[r, s] = np.sum(Kt[r] * Kt[s] * dec)
+                        Pm[r, s] = np.sum(Q[r] * Kt[s] * dec)
+                rhs = Vt - (Kt * np.exp(G)) @ S
+                U = np.linalg.solve(np.eye(n) + Tm, rhs)
+                o[b, h, c0:c1] = (Q * np.exp(G)) @ S + Pm @ U
+                S = np.exp(G[-1])[:, None] * S + (Kt * np.exp(G[-1] - G)).T @ U
+            ST[b, h] = S
+    return o, ST
