@@ -1,0 +1,261 @@
+"""MI355X (gfx950) gated delta-rule library: Python binding of libpdn.so.
+
+This layer only marshals arguments: it checks tensor placement, dtypes and
+shapes, passes raw device pointers and the current HIP stream to the C ABI
+(include/pdn.h), and raises on a non-zero return code.  Every step of the
+computation runs in the HIP kernels of libpdn.so; there is no fallback, and
+loading fails loudly when the library is missing.
+
+PyTorch is used for device memory and streams only.
+
+Entry points (same names as the C ABI):
+    pdn_chunk_fwd(...)                 prefill over [B,H,T,d]
+    pdn_chunk_fwd_workspace_size(...)  scratch bytes the prefill needs
+    pdn_decode_step(...)               one token against a resident state
+    pdn_abi_version(), pdn_strerror(code)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpdn.so")
+
+PDN_OK, PDN_EINVAL, PDN_EUNSUPPORTED, PDN_EWORKSPACE, PDN_EHIP = 0, -1, -2, -3, -4
+PDN_F32, PDN_BF16 = 0, 1
+PDN_ALPHA_NONE, PDN_ALPHA_SCALAR, PDN_ALPHA_VEC = 0, 1, 2
+PDN_GATE_SCALAR, PDN_GATE_VEC, PDN_GAMMA_SAME_AS_BETA = 1, 2, 3
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+
+
+class ChunkFwdArgs(ctypes.Structure):
+    """Mirror of ``pdn_chunk_fwd_args``."""
+    _fields_ = [("B", _I), ("H", _I), ("T", _I), ("dk", _I), ("dv", _I),
+                ("qkv_dtype", _I), ("o_dtype", _I),
+                ("q", _P), ("k", _P), ("v", _P),
+                ("alpha_mode", _I), ("log_alpha", _P),
+                ("beta_mode", _I), ("beta", _P),
+                ("gamma_mode", _I), ("gamma", _P),
+                ("precond_eps", ctypes.c_float), ("precond_A0", _P), ("precond_AT", _P),
+                ("S0", _P), ("ST", _P), ("o", _P),
+                ("workspace", _P), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class DecodeArgs(ctypes.Structure):
+    """Mirror of ``pdn_decode_args``."""
+    _fields_ = [("B", _I), ("H", _I), ("dk", _I), ("dv", _I),
+                ("qkv_dtype", _I), ("o_dtype", _I),
+                ("q", _P), ("k", _P), ("v", _P),
+                ("alpha_mode", _I), ("log_alpha", _P),
+                ("beta_mode", _I), ("beta", _P),
+                ("gamma_mode", _I), ("gamma", _P),
+                ("precond_eps", ctypes.c_float), ("precond_A", _P),
+                ("S", _P), ("o", _P)]
+
+
+EXPORTED = ("pdn_abi_version", "pdn_strerror", "pdn_chunk_fwd_workspace_size",
+            "pdn_chunk_fwd_check", "pdn_chunk_fwd", "pdn_decode_check", "pdn_decode_step")
+
+_lib = None
+_lock = threading.Lock()
+
+
+class PdnError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__("%s failed: %s (code %d)" % (where, pdn_strerror(code), code))
+
+
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load libpdn.so (built by ``gated_delta_rule_77_amd.build``); raise if absent."""
+    global _lib
+    with _lock:
+        if _lib is not None and path is None:
+            return _lib
+        p = path or LIB_PATH
+        if not os.path.exists(p):
+            raise RuntimeError("libpdn.so not found at %s: build it with "
+                               "`python -m gated_delta_rule_77_amd.build` (there is no "
+                               "fallback implementation)" % p)
+        lib = ctypes.CDLL(p)
+        lib.pdn_abi_version.argtypes = []
+        lib.pdn_abi_version.restype = ctypes.c_int
+        lib.pdn_strerror.argtypes = [ctypes.c_int]
+        lib.pdn_strerror.restype = ctypes.c_char_p
+        lib.pdn_chunk_fwd_workspace_size.argtypes = [ctypes.POINTER(ChunkFwdArgs),
+                                                     ctypes.POINTER(ctypes.c_size_t)]
+        lib.pdn_chunk_fwd_workspace_size.restype = ctypes.c_int
+        lib.pdn_chunk_fwd_check.argtypes = [ctypes.POINTER(ChunkFwdArgs)]
+        lib.pdn_chunk_fwd_check.restype = ctypes.c_int
+        lib.pdn_chunk_fwd.argtypes = [ctypes.POINTER(ChunkFwdArgs), _P]
+        lib.pdn_chunk_fwd.restype = ctypes.c_int
+        lib.pdn_decode_check.argtypes = [ctypes.POINTER(DecodeArgs)]
+        lib.pdn_decode_check.restype = ctypes.c_int
+        lib.pdn_decode_step.argtypes = [ctypes.POINTER(DecodeArgs), _P]
+        lib.pdn_decode_step.restype = ctypes.c_int
+        if path is None:
+            _lib = lib
+        return lib
+
+
+def pdn_abi_version() -> int:
+    return int(load_library().pdn_abi_version())
+
+
+def pdn_strerror(code: int) -> str:
+    return load_library().pdn_strerror(int(code)).decode()
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+
+def _ptr(t):
+    """Device pointer of a contiguous torch tensor (or None / raw int)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("tensor must live in device memory")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _qkv_dtype(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return PDN_BF16
+    if t.dtype == torch.float32:
+        return PDN_F32
+    raise ValueError("q/k/v/o must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _f32(t, name):
+    import torch
+    if t is None:
+        return
+    if t.dtype != torch.float32:
+        raise ValueError("%s must be float32" % name)
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _alpha_mode(log_alpha, lead):
+    if log_alpha is None:
+        return PDN_ALPHA_NONE
+    return PDN_ALPHA_SCALAR if log_alpha.dim() == lead else PDN_ALPHA_VEC
+
+
+def _gate_mode(g, lead):
+    return PDN_GATE_SCALAR if g.dim() == lead else PDN_GATE_VEC
+
+
+def _chunk_args(q, k, v, o, log_alpha, beta, gamma, precond_eps, precond_A0,
+                precond_AT, S0, ST, workspace):
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    if tuple(k.shape) != (B, H, T, dk) or tuple(v.shape[:3]) != (B, H, T):
+        raise ValueError("q, k must be [B,H,T,dk] and v [B,H,T,dv]")
+    if tuple(o.shape) != (B, H, T, dv):
+        raise ValueError("o must be [B,H,T,dv]")
+    if q.dtype != k.dtype or q.dtype != v.dtype:
+        raise ValueError("q, k, v must share one dtype")
+    for name, t in (("log_alpha", log_alpha), ("beta", beta), ("gamma", gamma),
+                    ("precond_A0", precond_A0), ("precond_AT", precond_AT),
+                    ("S0", S0), ("ST", ST)):
+        _f32(t, name)
+    a = ChunkFwdArgs()
+    a.B, a.H, a.T, a.dk, a.dv = B, H, T, dk, dv
+    a.qkv_dtype, a.o_dtype = _qkv_dtype(q), _qkv_dtype(o)
+    a.q, a.k, a.v, a.o = _ptr(q), _ptr(k), _ptr(v), _ptr(o)
+    a.alpha_mode = _alpha_mode(log_alpha, 3)
+    a.log_alpha = _ptr(log_alpha)
+    a.beta_mode = _gate_mode(beta, 3)
+    a.beta = _ptr(beta)
+    a.gamma_mode = PDN_GAMMA_SAME_AS_BETA if gamma is None else _gate_mode(gamma, 3)
+    a.gamma = _ptr(gamma)
+    a.precond_eps = -1.0 if precond_eps is None else float(precond_eps)
+    a.precond_A0, a.precond_AT = _ptr(precond_A0), _ptr(precond_AT)
+    a.S0, a.ST = _ptr(S0), _ptr(ST)
+    if workspace is not None:
+        a.workspace = _ptr(workspace)
+        a.workspace_bytes = workspace.numel() * workspace.element_size()
+    return a
+
+
+def pdn_chunk_fwd_workspace_size(q, k, v, o, log_alpha=None, beta=None, gamma=None,
+                                 precond_eps=None, precond_A0=None, precond_AT=None,
+                                 S0=None, ST=None) -> int:
+    a = _chunk_args(q, k, v, o, log_alpha, beta, gamma, precond_eps, precond_A0,
+                    precond_AT, S0, ST, None)
+    n = ctypes.c_size_t(0)
+    rc = load_library().pdn_chunk_fwd_workspace_size(ctypes.byref(a), ctypes.byref(n))
+    if rc != PDN_OK:
+        raise PdnError(rc, "pdn_chunk_fwd_workspace_size")
+    return int(n.value)
+
+
+def pdn_chunk_fwd(q, k, v, o, log_alpha=None, beta=None, gamma=None, precond_eps=None,
+                  precond_A0=None, precond_AT=None, S0=None, ST=None, workspace=None,
+                  stream=None) -> None:
+    """Prefill.  Tensors are device tensors in the layouts of include/pdn.h.
+
+    The gate modes follow from the tensors' ranks: log_alpha None / [B,H,T] /
+    [B,H,T,dk]; beta [B,H,T] / [B,H,T,dk]; gamma None (same as beta) / [B,H,T]
+    / [B,H,T,dv].  o (float32 or bfloat16) receives the output; ST and
+    precond_AT, when given, receive the final state and running k(.)k sum.
+    """
+    a = _chunk_args(q, k, v, o, log_alpha, beta, gamma, precond_eps, precond_A0,
+                    precond_AT, S0, ST, workspace)
+    rc = load_library().pdn_chunk_fwd(ctypes.byref(a), _stream(stream))
+    if rc != PDN_OK:
+        raise PdnError(rc, "pdn_chunk_fwd")
+
+
+def _decode_args(q, k, v, o, S, log_alpha, beta, gamma, precond_eps, precond_A):
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    if tuple(k.shape) != (B, H, dk) or tuple(v.shape[:2]) != (B, H):
+        raise ValueError("q, k must be [B,H,dk] and v [B,H,dv]")
+    if tuple(o.shape) != (B, H, dv) or tuple(S.shape) != (B, H, dk, dv):
+        raise ValueError("o must be [B,H,dv] and S [B,H,dk,dv]")
+    if q.dtype != k.dtype or q.dtype != v.dtype:
+        raise ValueError("q, k, v must share one dtype")
+    for name, t in (("log_alpha", log_alpha), ("beta", beta), ("gamma", gamma),
+                    ("precond_A", precond_A), ("S", S)):
+        _f32(t, name)
+    a = DecodeArgs()
+    a.B, a.H, a.dk, a.dv = B, H, dk, dv
+    a.qkv_dtype, a.o_dtype = _qkv_dtype(q), _qkv_dtype(o)
+    a.q, a.k, a.v, a.o, a.S = _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(S)
+    a.alpha_mode = _alpha_mode(log_alpha, 2)
+    a.log_alpha = _ptr(log_alpha)
+    a.beta_mode = _gate_mode(beta, 2)
+    a.beta = _ptr(beta)
+    a.gamma_mode = PDN_GAMMA_SAME_AS_BETA if gamma is None else _gate_mode(gamma, 2)
+    a.gamma = _ptr(gamma)
+    a.precond_eps = -1.0 if precond_eps is None else float(precond_eps)
+    a.precond_A = _ptr(precond_A)
+    return a
+
+
+def pdn_decode_step(q, k, v, o, S, log_alpha=None, beta=None, gamma=None,
+                    precond_eps=None, precond_A=None, stream=None) -> None:
+    """One decode token for all (b,h); S (and precond_A) updated in place."""
+    a = _decode_args(q, k, v, o, S, log_alpha, beta, gamma, precond_eps, precond_A)
+    rc = load_library().pdn_decode_step(ctypes.byref(a), _stream(stream))
+    if rc != PDN_OK:
+        raise PdnError(rc, "pdn_decode_step")

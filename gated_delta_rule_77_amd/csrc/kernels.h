@@ -1,0 +1,19 @@
+// Launch entry points of the gfx950 kernels, called by the host layer after
+// argument validation.  Not a public header.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "pdn.h"
+
+namespace pdn {
+
+// Single-token state update for every (b,h); returns a hipError_t.
+hipError_t launch_decode(const pdn_decode_args& a, hipStream_t stream);
+
+// Chunkwise prefill; returns a hipError_t.
+hipError_t launch_chunk_fwd(const pdn_chunk_fwd_args& a, hipStream_t stream);
+
+// Scratch bytes the prefill needs for these (valid) arguments.
+size_t chunk_fwd_workspace_bytes(const pdn_chunk_fwd_args& a);
+
+}  // namespace pdn

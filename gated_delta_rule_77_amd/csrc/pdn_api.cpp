@@ -1,0 +1,152 @@
+// Host layer of libpdn.so: the extern "C" entry points declared in pdn.h.
+// Every entry point validates its arguments before touching the GPU, maps
+// HIP errors to PDN_EHIP, and lets no exception escape.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "kernels.h"
+#include "pdn.h"
+
+namespace {
+
+bool valid_dtype(int32_t d) { return d == PDN_F32 || d == PDN_BF16; }
+bool valid_alpha(int32_t m) {
+    return m == PDN_ALPHA_NONE || m == PDN_ALPHA_SCALAR || m == PDN_ALPHA_VEC;
+}
+bool valid_beta(int32_t m) { return m == PDN_GATE_SCALAR || m == PDN_GATE_VEC; }
+bool valid_gamma(int32_t m) {
+    return m == PDN_GATE_SCALAR || m == PDN_GATE_VEC || m == PDN_GAMMA_SAME_AS_BETA;
+}
+
+// Largest B*H (and B*H*T) the launch grids and 32/64-bit index math accept.
+constexpr long kMaxBH = 1L << 24;
+constexpr long kMaxTokens = 1L << 40;
+
+int check_gates(int32_t amode, const float* la, int32_t bmode, const float* beta,
+                int32_t gmode, const float* gamma, float eps, int dk, int dv) {
+    if (!valid_alpha(amode) || !valid_beta(bmode) || !valid_gamma(gmode)) return PDN_EINVAL;
+    if (amode != PDN_ALPHA_NONE && !la) return PDN_EINVAL;
+    if (!beta) return PDN_EINVAL;
+    if (gmode != PDN_GAMMA_SAME_AS_BETA && !gamma) return PDN_EINVAL;
+    if (gmode == PDN_GAMMA_SAME_AS_BETA && bmode == PDN_GATE_VEC && dk != dv)
+        return PDN_EINVAL;
+    if (std::isnan(eps)) return PDN_EINVAL;
+    return PDN_OK;
+}
+
+int check_chunk(const pdn_chunk_fwd_args* a) {
+    if (!a) return PDN_EINVAL;
+    if (a->B < 1 || a->H < 1 || a->T < 0 || a->dk < 1 || a->dv < 1) return PDN_EINVAL;
+    if (!valid_dtype(a->qkv_dtype) || !valid_dtype(a->o_dtype)) return PDN_EINVAL;
+    if (static_cast<long>(a->B) * a->H > kMaxBH) return PDN_EUNSUPPORTED;
+    if (static_cast<long>(a->B) * a->H * a->T > kMaxTokens) return PDN_EUNSUPPORTED;
+    int rc = check_gates(a->alpha_mode, a->log_alpha, a->beta_mode, a->beta, a->gamma_mode,
+                         a->gamma, a->precond_eps, a->dk, a->dv);
+    if (rc != PDN_OK) return rc;
+    if (a->T > 0 && (!a->q || !a->k || !a->v || !a->o)) return PDN_EINVAL;
+    if (a->dk != 64 && a->dk != 128) return PDN_EUNSUPPORTED;
+    if (a->dv % 16 != 0 || a->dv > 256) return PDN_EUNSUPPORTED;
+    if (a->S0 && a->ST && a->S0 != a->ST) {
+        // distinct state buffers must not overlap
+        const long n = static_cast<long>(a->B) * a->H * a->dk * a->dv;
+        const float* s0 = a->S0;
+        const float* st = a->ST;
+        if (s0 < st + n && st < s0 + n) return PDN_EINVAL;
+    }
+    const size_t need = pdn::chunk_fwd_workspace_bytes(*a);
+    if (need > 0 && (!a->workspace || a->workspace_bytes < need)) return PDN_EWORKSPACE;
+    return PDN_OK;
+}
+
+int check_decode(const pdn_decode_args* a) {
+    if (!a) return PDN_EINVAL;
+    if (a->B < 1 || a->H < 1 || a->dk < 1 || a->dv < 1) return PDN_EINVAL;
+    if (!valid_dtype(a->qkv_dtype) || !valid_dtype(a->o_dtype)) return PDN_EINVAL;
+    if (!a->q || !a->k || !a->v || !a->o || !a->S) return PDN_EINVAL;
+    int rc = check_gates(a->alpha_mode, a->log_alpha, a->beta_mode, a->beta, a->gamma_mode,
+                         a->gamma, a->precond_eps, a->dk, a->dv);
+    if (rc != PDN_OK) return rc;
+    if (a->precond_eps >= 0.0f && !a->precond_A) return PDN_EINVAL;
+    if (static_cast<long>(a->B) * a->H > kMaxBH) return PDN_EUNSUPPORTED;
+    if ((a->dk != 64 && a->dk != 128) || (a->dv != 64 && a->dv != 128)) return PDN_EUNSUPPORTED;
+    return PDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pdn_abi_version(void) { return PDN_ABI_VERSION; }
+
+const char* pdn_strerror(int code) {
+    switch (code) {
+        case PDN_OK: return "success";
+        case PDN_EINVAL: return "invalid argument (null pointer, size or enum value)";
+        case PDN_EUNSUPPORTED: return "valid request outside what the kernels support";
+        case PDN_EWORKSPACE: return "workspace missing or too small";
+        case PDN_EHIP: return "HIP runtime error at launch";
+        default: return "unknown error code";
+    }
+}
+
+int pdn_chunk_fwd_workspace_size(const pdn_chunk_fwd_args* args, size_t* bytes) {
+    if (!args || !bytes) return PDN_EINVAL;
+    try {
+        pdn_chunk_fwd_args probe = *args;
+        probe.workspace = nullptr;
+        probe.workspace_bytes = 0;
+        // validate everything except the workspace itself
+        const size_t need = pdn::chunk_fwd_workspace_bytes(probe);
+        probe.workspace_bytes = need;
+        probe.workspace = need ? reinterpret_cast<void*>(uintptr_t(1)) : nullptr;
+        const int rc = check_chunk(&probe);
+        if (rc != PDN_OK) return rc;
+        *bytes = need;
+        return PDN_OK;
+    } catch (...) {
+        return PDN_EINVAL;
+    }
+}
+
+int pdn_chunk_fwd_check(const pdn_chunk_fwd_args* args) {
+    try {
+        return check_chunk(args);
+    } catch (...) {
+        return PDN_EINVAL;
+    }
+}
+
+int pdn_chunk_fwd(const pdn_chunk_fwd_args* args, void* stream) {
+    try {
+        const int rc = check_chunk(args);
+        if (rc != PDN_OK) return rc;
+        const hipError_t e = pdn::launch_chunk_fwd(*args, static_cast<hipStream_t>(stream));
+        if (e == hipErrorNotSupported) return PDN_EUNSUPPORTED;
+        return e == hipSuccess ? PDN_OK : PDN_EHIP;
+    } catch (...) {
+        return PDN_EHIP;
+    }
+}
+
+int pdn_decode_check(const pdn_decode_args* args) {
+    try {
+        return check_decode(args);
+    } catch (...) {
+        return PDN_EINVAL;
+    }
+}
+
+int pdn_decode_step(const pdn_decode_args* args, void* stream) {
+    try {
+        const int rc = check_decode(args);
+        if (rc != PDN_OK) return rc;
+        const hipError_t e = pdn::launch_decode(*args, static_cast<hipStream_t>(stream));
+        return e == hipSuccess ? PDN_OK : PDN_EHIP;
+    } catch (...) {
+        return PDN_EHIP;
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,181 @@
+/*
+ * pdn.h -- C ABI of the MI355X (gfx950) gated delta-rule library (libpdn.so).
+ *
+ * The operation (per batch b and head h, key width dk, value width dv):
+ *
+ *   state S in R^{dk x dv};  for t = 1..T:
+ *     alpha_t = exp(log_alpha_t)                 decay, scalar or per key channel
+ *     beta'_t = beta_t / (A_t + eps),            when the diagonal preconditioner
+ *       A_t = A_{t-1} + k_t (.) k_t              is on (A_t includes k_t); else beta_t
+ *     kt = sqrt(beta'_t) (.) k_t,  vt = sqrt(gamma_t) (.) v_t
+ *     S_t = Diag(alpha_t) S_{t-1} + kt (vt - (Diag(alpha_t) S_{t-1})^T kt)^T
+ *     o_t = S_t^T q_t
+ *
+ * Sources (titles of the pages this follows):
+ *   - "FG^2-GDN: Enhancing Long-Context Gated Delta Networks with Doubly
+ *     Fine-Grained Control", technical summary 2.1 (symmetric sqrt(beta) on key
+ *     and value, S_t = (I - kt kt^T) Diag(alpha_t) S_{t-1} + kt vt^T) and 2.2
+ *     (independent key-side and value-side gains).
+ *   - "Gated DeltaNet-2: Decoupling Erase and Write in Linear Attention",
+ *     method section 1 (channel-wise decay D_t = Diag(alpha_t) before the erase;
+ *     reduction to KDA / Gated DeltaNet for tied scalar gates) and section 3
+ *     (chunkwise WY form with a lower-triangular (I+T)^-1 solve).
+ *   - "Preconditioned DeltaNet: Curvature-aware Sequence Modeling for Linear
+ *     Recurrences", section 2.2 / 2B (running diagonal A_t = A_{t-1} + k_t (.) k_t,
+ *     P_t = Diag(A_t)^-1), folded here into the erase gain beta.
+ *   gamma is never preconditioned; "gamma same as beta" means the raw beta.
+ *   There is no 1/sqrt(dk) scaling inside the op.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers (HBM), row-major and contiguous,
+ *     owned by the caller.  The library allocates nothing and keeps no mutable
+ *     global state; it never frees or retains caller memory.
+ *   - Work is queued asynchronously on `stream` (a hipStream_t; NULL = the
+ *     default stream).  Outputs are valid once the stream is synchronised.
+ *   - Arguments are validated on the host BEFORE any launch; an invalid call
+ *     returns a negative PDN_E* code, touches no memory and launches nothing.
+ *     No C++ exception crosses this boundary.
+ *   - Calls that share an output (o, ST, S, precond_A) must not overlap.
+ */
+#ifndef PDN_H
+#define PDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PDN_ABI_VERSION 1
+
+/* Return codes. */
+#define PDN_OK 0
+#define PDN_EINVAL (-1)        /* null pointer, bad size, bad enum value          */
+#define PDN_EUNSUPPORTED (-2)  /* valid request outside what the kernels handle   */
+#define PDN_EWORKSPACE (-3)    /* workspace missing or smaller than required      */
+#define PDN_EHIP (-4)          /* the HIP runtime reported an error on launch     */
+
+/* Element types of q, k, v and o. */
+#define PDN_F32 0
+#define PDN_BF16 1
+
+/* Decay: none (alpha == 1), one scalar per (b,h,t), or one per key channel. */
+#define PDN_ALPHA_NONE 0
+#define PDN_ALPHA_SCALAR 1
+#define PDN_ALPHA_VEC 2
+
+/* Gains: one scalar per (b,h,t), one per channel, or (gamma only) raw beta. */
+#define PDN_GATE_SCALAR 1
+#define PDN_GATE_VEC 2
+#define PDN_GAMMA_SAME_AS_BETA 3
+
+/*
+ * Prefill over whole sequences, chunkwise-parallel on the GPU.
+ *
+ *   B, H, T, dk, dv   sizes.  B, H >= 1; T >= 0 (T == 0 copies S0 to ST and
+ *                     A0 to AT); dk in {64, 128}; dv a multiple of 32, <= 256.
+ *   qkv_dtype         PDN_F32 or PDN_BF16: element type of q, k, v.
+ *   o_dtype           PDN_F32 (default) or PDN_BF16.
+ *   q, k              [B,H,T,dk].      v: [B,H,T,dv].
+ *   alpha_mode        PDN_ALPHA_*;  log_alpha fp32, natural log of alpha, <= 0:
+ *                     [B,H,T] (SCALAR) or [B,H,T,dk] (VEC); NULL for NONE.
+ *                     Values below -10 (alpha < 4.5e-5) are clamped to -10.
+ *   beta_mode         PDN_GATE_SCALAR [B,H,T] or PDN_GATE_VEC [B,H,T,dk]; fp32 >= 0.
+ *   gamma_mode        PDN_GATE_SCALAR [B,H,T], PDN_GATE_VEC [B,H,T,dv] or
+ *                     PDN_GAMMA_SAME_AS_BETA (gamma NULL; a VEC beta then needs
+ *                     dk == dv); fp32 >= 0.
+ *   precond_eps       < 0: preconditioner off.  >= 0: on, with this epsilon.
+ *   precond_A0        [B,H,dk] fp32 start of the running k(.)k sum; NULL = zeros.
+ *   precond_AT        [B,H,dk] fp32 running sum after token T; NULL = not written.
+ *   S0                [B,H,dk,dv] fp32 initial state; NULL = zeros.
+ *   ST                [B,H,dk,dv] fp32 final state; NULL = not written.
+ *                     S0 == ST (in place) is allowed; no other aliasing is.
+ *   o                 [B,H,T,dv] output in o_dtype.
+ *   workspace, workspace_bytes   caller-owned device scratch of at least
+ *                     pdn_chunk_fwd_workspace_size() bytes (may be 0 / NULL).
+ */
+typedef struct pdn_chunk_fwd_args {
+    int32_t B, H, T, dk, dv;
+    int32_t qkv_dtype;
+    int32_t o_dtype;
+    const void *q;
+    const void *k;
+    const void *v;
+    int32_t alpha_mode;
+    const float *log_alpha;
+    int32_t beta_mode;
+    const float *beta;
+    int32_t gamma_mode;
+    const float *gamma;
+    float precond_eps;
+    const float *precond_A0;
+    float *precond_AT;
+    const float *S0;
+    float *ST;
+    void *o;
+    void *workspace;
+    size_t workspace_bytes;
+} pdn_chunk_fwd_args;
+
+/*
+ * One decode step for every (b,h) against a resident fp32 state, in place.
+ *
+ *   B, H, dk, dv      sizes; B, H >= 1; dk, dv in {64, 128}.
+ *   qkv_dtype         PDN_F32 or PDN_BF16;  q, k: [B,H,dk];  v: [B,H,dv].
+ *   o_dtype           PDN_F32 or PDN_BF16;  o: [B,H,dv].
+ *   alpha_mode, log_alpha ([B,H] or [B,H,dk]), beta_mode, beta ([B,H] or
+ *   [B,H,dk]), gamma_mode, gamma ([B,H] or [B,H,dv]): as for the prefill with
+ *   T == 1 (no clamp on log_alpha here).
+ *   precond_eps       < 0 off; >= 0 on, and then precond_A ([B,H,dk] fp32) is
+ *                     read, advanced by k(.)k and written back in place.
+ *   S                 [B,H,dk,dv] fp32, read and overwritten with S_t.
+ */
+typedef struct pdn_decode_args {
+    int32_t B, H, dk, dv;
+    int32_t qkv_dtype;
+    int32_t o_dtype;
+    const void *q;
+    const void *k;
+    const void *v;
+    int32_t alpha_mode;
+    const float *log_alpha;
+    int32_t beta_mode;
+    const float *beta;
+    int32_t gamma_mode;
+    const float *gamma;
+    float precond_eps;
+    float *precond_A;
+    float *S;
+    void *o;
+} pdn_decode_args;
+
+/* PDN_ABI_VERSION of the loaded library. */
+int pdn_abi_version(void);
+
+/* Static, human-readable text for a PDN_* return code (never NULL). */
+const char *pdn_strerror(int code);
+
+/* Device scratch bytes pdn_chunk_fwd needs for these arguments (0 is valid).
+ * Returns PDN_OK and writes *bytes, or a PDN_E* code for invalid arguments. */
+int pdn_chunk_fwd_workspace_size(const pdn_chunk_fwd_args *args, size_t *bytes);
+
+/* Validate only (no HIP call, no launch): PDN_OK or the code pdn_chunk_fwd
+ * would return for these arguments before launching. */
+int pdn_chunk_fwd_check(const pdn_chunk_fwd_args *args);
+
+/* Prefill: o, and ST / precond_AT when given.  Chunk length 64; T need not be
+ * a multiple of it and results do not depend on where chunks fall. */
+int pdn_chunk_fwd(const pdn_chunk_fwd_args *args, void *stream);
+
+/* Validate only, as pdn_chunk_fwd_check. */
+int pdn_decode_check(const pdn_decode_args *args);
+
+/* Decode one token for all (b,h): o, S in place, precond_A in place. */
+int pdn_decode_step(const pdn_decode_args *args, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PDN_H */

@@ -1,0 +1,186 @@
+"""Host-side checks of the C ABI (no GPU needed, no compute call made).
+
+* libpdn.so builds/loads and exports every function include/pdn.h declares;
+* the ctypes mirrors have the exact size and field offsets of the C structs
+  (a tiny C program compiled with gcc against pdn.h reports them);
+* argument validation returns the documented codes before any launch.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import gated_delta_rule_77_amd as pdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pdn.h")
+FAKE = 0x10000  # never dereferenced: only *_check entry points see it
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pdn.LIB_PATH):
+        from gated_delta_rule_77_amd import build
+        build.build()
+    return pdn.load_library()
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(pdn_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert set(names) == set(pdn.EXPORTED)
+    out = subprocess.run(["nm", "-D", "--defined-only", pdn.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (pdn_[a-z_0-9]+)", out))
+    for n in names:
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+def test_abi_version_and_strerror(lib):
+    assert pdn.pdn_abi_version() == 1
+    for code in (0, -1, -2, -3, -4):
+        assert pdn.pdn_strerror(code)
+    assert "unknown" in pdn.pdn_strerror(-99)
+
+
+def test_struct_layout_matches_header(tmp_path):
+    prog = tmp_path / "layout.c"
+    fields_c = [f for f, _ in pdn.ChunkFwdArgs._fields_]
+    fields_d = [f for f, _ in pdn.DecodeArgs._fields_]
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "pdn.h"', 'int main(void){']
+    lines.append('printf("chunk %zu\\n", sizeof(pdn_chunk_fwd_args));')
+    for f in fields_c:
+        lines.append('printf("c.%s %%zu\\n", offsetof(pdn_chunk_fwd_args, %s));' % (f, f))
+    lines.append('printf("decode %zu\\n", sizeof(pdn_decode_args));')
+    for f in fields_d:
+        lines.append('printf("d.%s %%zu\\n", offsetof(pdn_decode_args, %s));' % (f, f))
+    lines.append("return 0;}")
+    prog.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.check_call(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"),
+                           str(prog), "-o", str(exe)])
+    got = dict(l.split() for l in subprocess.check_output([str(exe)], text=True).splitlines())
+    assert int(got["chunk"]) == ctypes.sizeof(pdn.ChunkFwdArgs)
+    assert int(got["decode"]) == ctypes.sizeof(pdn.DecodeArgs)
+    for f in fields_c:
+        assert int(got["c." + f]) == getattr(pdn.ChunkFwdArgs, f).offset, f
+    for f in fields_d:
+        assert int(got["d." + f]) == getattr(pdn.DecodeArgs, f).offset, f
+
+
+def _chunk_ok():
+    a = pdn.ChunkFwdArgs()
+    a.B, a.H, a.T, a.dk, a.dv = 2, 3, 100, 128, 128
+    a.qkv_dtype, a.o_dtype = pdn.PDN_BF16, pdn.PDN_F32
+    a.q = a.k = a.v = a.o = FAKE
+    a.alpha_mode, a.log_alpha = pdn.PDN_ALPHA_VEC, FAKE
+    a.beta_mode, a.beta = pdn.PDN_GATE_VEC, FAKE
+    a.gamma_mode, a.gamma = pdn.PDN_GATE_VEC, FAKE
+    a.precond_eps = -1.0
+    return a
+
+
+def _decode_ok():
+    a = pdn.DecodeArgs()
+    a.B, a.H, a.dk, a.dv = 4, 2, 128, 64
+    a.qkv_dtype, a.o_dtype = pdn.PDN_BF16, pdn.PDN_F32
+    a.q = a.k = a.v = a.o = a.S = FAKE
+    a.alpha_mode, a.log_alpha = pdn.PDN_ALPHA_SCALAR, FAKE
+    a.beta_mode, a.beta = pdn.PDN_GATE_SCALAR, FAKE
+    a.gamma_mode, a.gamma = pdn.PDN_GAMMA_SAME_AS_BETA, None
+    a.precond_eps = -1.0
+    return a
+
+
+def _ccheck(lib, a):
+    return lib.pdn_chunk_fwd_check(ctypes.byref(a))
+
+
+def _dcheck(lib, a):
+    return lib.pdn_decode_check(ctypes.byref(a))
+
+
+def test_valid_arguments_pass_validation(lib):
+    assert _ccheck(lib, _chunk_ok()) == pdn.PDN_OK
+    assert _dcheck(lib, _decode_ok()) == pdn.PDN_OK
+    n = ctypes.c_size_t(123)
+    assert lib.pdn_chunk_fwd_workspace_size(ctypes.byref(_chunk_ok()), ctypes.byref(n)) == 0
+
+
+@pytest.mark.parametrize("mutate,code", [
+    (lambda a: setattr(a, "B", 0), pdn.PDN_EINVAL),
+    (lambda a: setattr(a, "H", -1), pdn.PDN_EINVAL),
+    (lambda a: setattr(a, "T", -5), pdn.PDN_EINVAL),
+    (lambda a: setattr(a, "q", None), pdn.PDN_EINVAL),
+    (lambda a: setattr(a, "o", None), pdn.PDN_EINVAL),
+    (lambda a: setattr(a, "qkv_dtype", 7), pdn.PDN_EINVAL),
+    (lambda a: setattr(a, "o_dtype", -1), pdn.PDN_EINVAL),
+    (lambda a: setattr(a, "alpha_mode", 9), pdn.PDN_EINVAL),
+    (lambda a: setattr(a, "log_alpha", None), pdn.PDN_EINVAL),
+    (lambda a: setattr(a, "beta_mode", pdn.PDN_GAMMA_SAME_AS_BETA), pdn.PDN_EINVAL),
+    (lambda a: setattr(a, "beta", None), pdn.PDN_EINVAL),
+    (lambda a: setattr(a, "gamma", None), pdn.PDN_EINVAL),
+    (lambda a: (setattr(a, "gamma_mode", pdn.PDN_GAMMA_SAME_AS_BETA), setattr(a, "dv", 64)),
+     pdn.PDN_EINVAL),
+    (lambda a: setattr(a, "precond_eps", float("nan")), pdn.PDN_EINVAL),
+    (lambda a: setattr(a, "dk", 96), pdn.PDN_EUNSUPPORTED),
+    (lambda a: setattr(a, "dv", 40), pdn.PDN_EUNSUPPORTED),
+    (lambda a: setattr(a, "dv", 512), pdn.PDN_EUNSUPPORTED),
+    (lambda a: (setattr(a, "B", 1 << 20), setattr(a, "H", 1 << 10)), pdn.PDN_EUNSUPPORTED),
+    (lambda a: (setattr(a, "S0", FAKE), setattr(a, "ST", FAKE + 64)), pdn.PDN_EINVAL),
+])
+def test_chunk_validation_codes(lib, mutate, code):
+    a = _chunk_ok()
+    mutate(a)
+    assert _ccheck(lib, a) == code
+    # the launching entry point returns the same code before touching the GPU
+    assert lib.pdn_chunk_fwd(ctypes.byref(a), None) == code
+
+
+def test_chunk_allows_in_place_state(lib):
+    a = _chunk_ok()
+    a.S0 = a.ST = FAKE
+    assert _ccheck(lib, a) == pdn.PDN_OK
+
+
+def test_chunk_empty_sequence_needs_no_tensors(lib):
+    a = _chunk_ok()
+    a.T = 0
+    a.q = a.k = a.v = a.o = None
+    assert _ccheck(lib, a) == pdn.PDN_OK
+
+
+@pytest.mark.parametrize("mutate,code", [
+    (lambda a: setattr(a, "B", 0), pdn.PDN_EINVAL),
+    (lambda a: setattr(a, "S", None), pdn.PDN_EINVAL),
+    (lambda a: setattr(a, "k", None), pdn.PDN_EINVAL),
+    (lambda a: setattr(a, "qkv_dtype", 3), pdn.PDN_EINVAL),
+    (lambda a: setattr(a, "alpha_mode", 5), pdn.PDN_EINVAL),
+    (lambda a: setattr(a, "log_alpha", None), pdn.PDN_EINVAL),
+    (lambda a: (setattr(a, "beta_mode", pdn.PDN_GATE_VEC), setattr(a, "dv", 64)),
+     pdn.PDN_EINVAL),
+    (lambda a: setattr(a, "precond_eps", 1e-6), pdn.PDN_EINVAL),  # no precond_A
+    (lambda a: setattr(a, "dk", 32), pdn.PDN_EUNSUPPORTED),
+    (lambda a: setattr(a, "dv", 256), pdn.PDN_EUNSUPPORTED),
+])
+def test_decode_validation_codes(lib, mutate, code):
+    a = _decode_ok()
+    mutate(a)
+    assert _dcheck(lib, a) == code
+    assert lib.pdn_decode_step(ctypes.byref(a), None) == code
+
+
+def test_null_args_pointer(lib):
+    assert lib.pdn_chunk_fwd_check(None) == pdn.PDN_EINVAL
+    assert lib.pdn_decode_check(None) == pdn.PDN_EINVAL
+    assert lib.pdn_chunk_fwd(None, None) == pdn.PDN_EINVAL
+    assert lib.pdn_decode_step(None, None) == pdn.PDN_EINVAL
+    assert lib.pdn_chunk_fwd_workspace_size(None, None) == pdn.PDN_EINVAL
