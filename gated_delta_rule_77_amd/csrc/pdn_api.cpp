@@ -24,12 +24,18 @@ bool valid_gamma(int32_t m) {
 constexpr long kMaxBH = 1L << 24;
 constexpr long kMaxTokens = 1L << 40;
 
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Gate enums and pointers.  With no tokens to process (need_data false) the
+// gate pointers may be NULL.
 int check_gates(int32_t amode, const float* la, int32_t bmode, const float* beta,
-                int32_t gmode, const float* gamma, float eps, int dk, int dv) {
+                int32_t gmode, const float* gamma, float eps, int dk, int dv, bool need_data) {
     if (!valid_alpha(amode) || !valid_beta(bmode) || !valid_gamma(gmode)) return PDN_EINVAL;
-    if (amode != PDN_ALPHA_NONE && !la) return PDN_EINVAL;
-    if (!beta) return PDN_EINVAL;
-    if (gmode != PDN_GAMMA_SAME_AS_BETA && !gamma) return PDN_EINVAL;
+    if (need_data) {
+        if (amode != PDN_ALPHA_NONE && !la) return PDN_EINVAL;
+        if (!beta) return PDN_EINVAL;
+        if (gmode != PDN_GAMMA_SAME_AS_BETA && !gamma) return PDN_EINVAL;
+    }
     if (gmode == PDN_GAMMA_SAME_AS_BETA && bmode == PDN_GATE_VEC && dk != dv)
         return PDN_EINVAL;
     if (std::isnan(eps)) return PDN_EINVAL;
@@ -43,11 +49,19 @@ int check_chunk(const pdn_chunk_fwd_args* a) {
     if (static_cast<long>(a->B) * a->H > kMaxBH) return PDN_EUNSUPPORTED;
     if (static_cast<long>(a->B) * a->H * a->T > kMaxTokens) return PDN_EUNSUPPORTED;
     int rc = check_gates(a->alpha_mode, a->log_alpha, a->beta_mode, a->beta, a->gamma_mode,
-                         a->gamma, a->precond_eps, a->dk, a->dv);
+                         a->gamma, a->precond_eps, a->dk, a->dv, a->T > 0);
     if (rc != PDN_OK) return rc;
     if (a->T > 0 && (!a->q || !a->k || !a->v || !a->o)) return PDN_EINVAL;
+    // the kernels use 16-byte vector loads and stores
+    const void* ptrs[] = {a->q, a->k, a->v, a->o, a->log_alpha, a->beta, a->gamma,
+                          a->precond_A0, a->precond_AT, a->S0, a->ST};
+    for (const void* ptr : ptrs)
+        if (ptr && !aligned16(ptr)) return PDN_EINVAL;
     if (a->dk != 64 && a->dk != 128) return PDN_EUNSUPPORTED;
     if (a->dv % 16 != 0 || a->dv > 256) return PDN_EUNSUPPORTED;
+    const bool vec = a->alpha_mode == PDN_ALPHA_VEC || a->beta_mode == PDN_GATE_VEC ||
+                     a->precond_eps >= 0.0f;
+    if (vec && a->dv % 32 != 0) return PDN_EUNSUPPORTED;
     if (a->S0 && a->ST && a->S0 != a->ST) {
         // distinct state buffers must not overlap
         const long n = static_cast<long>(a->B) * a->H * a->dk * a->dv;
@@ -66,9 +80,10 @@ int check_decode(const pdn_decode_args* a) {
     if (!valid_dtype(a->qkv_dtype) || !valid_dtype(a->o_dtype)) return PDN_EINVAL;
     if (!a->q || !a->k || !a->v || !a->o || !a->S) return PDN_EINVAL;
     int rc = check_gates(a->alpha_mode, a->log_alpha, a->beta_mode, a->beta, a->gamma_mode,
-                         a->gamma, a->precond_eps, a->dk, a->dv);
+                         a->gamma, a->precond_eps, a->dk, a->dv, true);
     if (rc != PDN_OK) return rc;
     if (a->precond_eps >= 0.0f && !a->precond_A) return PDN_EINVAL;
+    if (!aligned16(a->S)) return PDN_EINVAL;  // streamed with 16-byte accesses
     if (static_cast<long>(a->B) * a->H > kMaxBH) return PDN_EUNSUPPORTED;
     if ((a->dk != 64 && a->dk != 128) || (a->dv != 64 && a->dv != 128)) return PDN_EUNSUPPORTED;
     return PDN_OK;

@@ -74,7 +74,11 @@ extern "C" {
  * Prefill over whole sequences, chunkwise-parallel on the GPU.
  *
  *   B, H, T, dk, dv   sizes.  B, H >= 1; T >= 0 (T == 0 copies S0 to ST and
- *                     A0 to AT); dk in {64, 128}; dv a multiple of 32, <= 256.
+ *                     A0 to AT; the q/k/v/o/gate pointers may then be NULL);
+ *                     dk in {64, 128}; dv a multiple of 16 and <= 256, and a
+ *                     multiple of 32 when any gate is per-channel or the
+ *                     preconditioner is on.  Every pointer must be 16-byte
+ *                     aligned (PDN_EINVAL otherwise).
  *   qkv_dtype         PDN_F32 or PDN_BF16: element type of q, k, v.
  *   o_dtype           PDN_F32 (default) or PDN_BF16.
  *   q, k              [B,H,T,dk].      v: [B,H,T,dv].
@@ -129,7 +133,8 @@ typedef struct pdn_chunk_fwd_args {
  *   T == 1 (no clamp on log_alpha here).
  *   precond_eps       < 0 off; >= 0 on, and then precond_A ([B,H,dk] fp32) is
  *                     read, advanced by k(.)k and written back in place.
- *   S                 [B,H,dk,dv] fp32, read and overwritten with S_t.
+ *   S                 [B,H,dk,dv] fp32, read and overwritten with S_t; 16-byte
+ *                     aligned.
  */
 typedef struct pdn_decode_args {
     int32_t B, H, dk, dv;
