@@ -1,0 +1,305 @@
+#!/usr/bin/env python3
+"""Benchmark of the gfx950 delta-rule library on one MI355X.
+
+One step = one pdn_chunk_fwd call over the throughput workload (B=4 sequences,
+H=16 heads, T=8192 tokens, dk=dv=128, bf16 q/k/v, Gated-DeltaNet gating:
+scalar decay and gain per head and token, value gain = gain), producing the
+fp32 output and the final fp32 state.  Inputs are resident in HBM before the
+timed region.  The same run also times the recurrent decode
+(pdn_decode_step: B=256, H=16, d=128, fp32 resident state, channel-wise decay,
+vector key gain, scalar value gain) and, on rank 0, the fp64 CPU oracle on a
+bounded sample of the prefill workload.
+
+Prints one JSON line.  `value` is prefill tokens/s (tokens = batch x sequence
+positions, all heads); the roofline object describes the prefill kernel
+(HBM-bound: algorithmic bytes / kernel time vs 8 TB/s), and the decode object
+its own roofline.
+
+    python bench.py [--steps K] [--warmup W] [--decode-steps N] [--no-cpu-baseline]
+    python bench.py --copy-probe     # plain 1 GiB copy, to calibrate PMC byte counters
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tokens/s chunked delta-rule fwd (H=16,d=128,T=8K) + % MFMA peak; decode GB/s"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+CHUNK_FLOP_C = 64              # chunk length of the algorithmic FLOP count
+
+
+def alg_flops_per_token_head(dk: int, dv: int, C: int = CHUNK_FLOP_C) -> float:
+    """Algorithmic FLOPs of the chunkwise forward per (token, head):
+    2 * (3 dk dv + 1.5 C dk + C dv + C^2 / 6)  (KS, QS and the state update;
+    the decayed Gram blocks; the triangular solve and intra-chunk output)."""
+    return 2.0 * (3 * dk * dv + 1.5 * C * dk + C * dv + C * C / 6.0)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=200)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device copy (PMC calibration)")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gated_delta_rule_77_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from committed PMC summaries, if they were taken
+    on the current kernel sources (else None)."""
+    p = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+    except ValueError:
+        return None
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return d.get("bytes_per_launch")
+
+
+def copy_probe():
+    import torch
+    n = (1 << 30) // 4
+    src = torch.ones(n, device="cuda", dtype=torch.float32)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4,
+                      "launches": 3}))
+
+
+def to_dev(x, bf16=False):
+    import numpy as np
+    import torch
+    if x is None:
+        return None
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    if bf16:
+        t = t.to(torch.bfloat16)
+    return t.to("cuda").contiguous()
+
+
+def bench_prefill(args):
+    import torch
+    import gated_delta_rule_77_amd as pdn
+    from gated_delta_rule_77_amd import synth
+
+    w = synth.headline()
+    q, k, v = to_dev(w.q, True), to_dev(w.k, True), to_dev(w.v, True)
+    la, be = to_dev(w.log_alpha), to_dev(w.beta)
+    o = torch.empty((w.B, w.H, w.T, w.dv), device="cuda", dtype=torch.float32)
+    ST = torch.empty((w.B, w.H, w.dk, w.dv), device="cuda", dtype=torch.float32)
+
+    def step():
+        pdn.pdn_chunk_fwd(q, k, v, o, log_alpha=la, beta=be, ST=ST)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kern_ms = [a.elapsed_time(b) for a, b in ev]
+    kernel_ms = sum(kern_ms) / len(kern_ms)
+
+    BH, T, dk, dv = w.B * w.H, w.T, w.dk, w.dv
+    qkv_bytes = BH * T * (2 * dk + dv) * 2
+    gate_bytes = BH * T * 4 * 2                # scalar log-decay and gain
+    o_bytes = BH * T * dv * 4
+    st_bytes = BH * dk * dv * 4
+    alg_bytes = qkv_bytes + gate_bytes + o_bytes + st_bytes
+    alg_flops = alg_flops_per_token_head(dk, dv) * BH * T
+    ks = kernel_ms / 1e3
+    return {
+        "workload": w.name, "B": w.B, "H": w.H, "T": T, "dk": dk, "dv": dv,
+        "elapsed_s": t1 - t0, "tokens": w.B * T, "kernel_ms": kernel_ms,
+        "kernel_ms_min": min(kern_ms), "alg_bytes": alg_bytes, "alg_flops": alg_flops,
+        "achieved_gbs": alg_bytes / ks / 1e9, "achieved_tflops": alg_flops / ks / 1e12,
+        "sample": w,
+    }
+
+
+def bench_decode(args):
+    import torch
+    import gated_delta_rule_77_amd as pdn
+    from gated_delta_rule_77_amd import synth
+
+    pool = 8  # distinct per-step inputs, cycled
+    w = synth.decode(B=256, H=16, d=128, steps=pool)
+    S = to_dev(w.S0)
+    steps_in = []
+    for t in range(pool):
+        steps_in.append((to_dev(w.q[:, :, t], True), to_dev(w.k[:, :, t], True),
+                         to_dev(w.v[:, :, t], True), to_dev(w.log_alpha[:, :, t]),
+                         to_dev(w.beta[:, :, t]), to_dev(w.gamma[:, :, t])))
+    o = torch.empty((w.B, w.H, w.dv), device="cuda", dtype=torch.float32)
+
+    def step(i):
+        q, k, v, la, be, ga = steps_in[i % pool]
+        pdn.pdn_decode_step(q, k, v, o, S, log_alpha=la, beta=be, gamma=ga)
+
+    for i in range(10):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    n = args.decode_steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    t0 = time.perf_counter()
+    for i in range(n):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kern_ms = [a.elapsed_time(b) for a, b in ev]
+    kernel_ms = sum(kern_ms) / n
+    BH, dk, dv = w.B * w.H, w.dk, w.dv
+    alg_bytes = BH * (2 * dk * dv * 4 + (2 * dk + dv) * 2 + 2 * dk * 4 + 4 + dv * 4)
+    gbs = alg_bytes / (kernel_ms / 1e3) / 1e9
+    return {
+        "workload": "decode_B256_H16_d128", "steps": n, "ms_per_step": (t1 - t0) * 1e3 / n,
+        "kernel_ms": kernel_ms, "alg_bytes_per_step": alg_bytes,
+        "value": gbs, "unit": "GB/s", "tokens_per_s": w.B / ((t1 - t0) / n),
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": measured_traffic("decode_B256_H16_d128")},
+    }
+
+
+def cpu_baseline(w, target_s: float):
+    """The fp64 oracle on a bounded sample of the prefill workload."""
+    import numpy as np
+    sys.path.insert(0, ROOT)
+    import oracle
+
+    threads = oracle.num_threads()
+
+    def run(nbh, T):
+        b_idx = [i // w.H for i in range(nbh)]
+        h_idx = [i % w.H for i in range(nbh)]
+        sel = lambda x: None if x is None else np.ascontiguousarray(
+            x[b_idx, h_idx][:, None, :T])
+        args = (sel(w.q), sel(w.k), sel(w.v), w.alpha_mode, sel(w.log_alpha), w.beta_mode,
+                sel(w.beta), w.gamma_mode, sel(w.gamma))
+        t0 = time.perf_counter()
+        oracle.delta_rule(*args, want_state=False)
+        return time.perf_counter() - t0
+
+    # calibrate on one (b, h) pair, then size the sample to the target time
+    Tc = min(512, w.T)
+    tc = run(1, Tc)
+    per_tok_head = tc / Tc
+    nbh_max = w.B * w.H
+    T = w.T
+    nbh = int(max(1, min(nbh_max, target_s * threads / (per_tok_head * T))))
+    if nbh < threads:  # too slow for one pair per thread over full T: shorten T
+        nbh = min(threads, nbh_max)
+        T = int(max(64, min(w.T, target_s * threads / (per_tok_head * nbh))))
+    el = run(nbh, T)
+    tok_heads = nbh * T
+    return {"value": tok_heads / w.H / el, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "%d (batch, head) pairs x first %d tokens of the B%d H%d T%d workload "
+                      "(fp64 token recurrence, OpenMP over pairs; tokens/s = token-heads/s / H)"
+                      % (nbh, T, w.B, w.H, w.T),
+            "seconds": el}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only (no multi-GPU path); "
+              "use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_probe:
+        copy_probe()
+        return
+    import torch
+    import gated_delta_rule_77_amd as pdn
+    pdn.load_library()  # fail loudly if the HIP library is missing
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    pf = bench_prefill(args)
+    dec = None if args.no_decode else bench_decode(args)
+    cpu = None
+    if not args.no_cpu_baseline and int(os.environ.get("RANK", "0")) == 0:
+        cpu = cpu_baseline(pf["sample"], args.cpu_seconds)
+
+    value = pf["tokens"] * args.steps / pf["elapsed_s"]
+    frac = pf["achieved_gbs"] / HBM_PEAK_GBS
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": pf["elapsed_s"] * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "gated_delta_rule_prefill_B%d_H%d_T%d_d%d" % (
+                       pf["B"], pf["H"], pf["T"], pf["dk"]),
+                   "gating": "scalar decay + scalar gain per (head, token), gamma = beta",
+                   "qkv": "bf16", "o": "fp32", "final_state": "fp32",
+                   "global_batch": pf["B"], "seq_len": pf["T"], "heads": pf["H"],
+                   "dk": pf["dk"], "dv": pf["dv"]},
+        "roofline": {"bound": "hbm", "achieved": pf["achieved_gbs"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": frac,
+                     "traffic": measured_traffic(pf["workload"])},
+        "kernel_ms": pf["kernel_ms"],
+        "alg_bytes_per_launch": pf["alg_bytes"],
+        "mfma": {"alg_tflops": pf["achieved_tflops"], "peak_tflops": BF16_PEAK_TFLOPS,
+                 "frac_of_peak": pf["achieved_tflops"] / BF16_PEAK_TFLOPS,
+                 "alg_flops_per_launch": pf["alg_flops"],
+                 "ceiling_frac_at_hbm_bound": (pf["alg_flops"] / (pf["alg_bytes"] / (HBM_PEAK_GBS * 1e9)))
+                 / (BF16_PEAK_TFLOPS * 1e12)},
+        "decode": dec,
+        "cpu_baseline": cpu,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -59,16 +59,18 @@ struct ChunkParams {
     const void* v;
     const float* log_alpha;
     const float* beta;
-    const float* gamma;
     const float* A0;
     float* AT;
     const float* S0;
     float* ST;
     void* o;
+    const float* gsrc;  // value-side gain source: gamma, or beta when "same as beta"
+    long gts;           // its stride per token (elements)
     long T;
     int dv;
-    int alpha_mode, beta_mode, gamma_mode;
-    float eps;  // < 0: preconditioner off
+    int alpha_mode, beta_mode;
+    int gvec;           // value gain is per column (else one scalar per token)
+    float eps;          // < 0: preconditioner off
     int o_bf16;
 };
 
@@ -302,12 +304,18 @@ struct Stage {
     uint4 k[C::KP];
     uint4 q[C::KP];
     uint4 v[C::VP];
-    f32x4 gam[C::VP * Raw<F32IN>::PIECE / 4];
-    f32x4 la[VEC ? C::GP : 1];
-    f32x4 be[VEC ? C::GP : 1];
-    float la1, be1;  // FACTORED: per-token scalars (threads < 64)
+    f32x4 gam[C::VP * Raw<F32IN>::PIECE / 4];  // per-column value gain
+    float gam1[C::VP];                          // or one value gain per token
+    f32x4 la[VEC ? C::GP : 1];                  // per-channel log decay
+    f32x4 be[VEC ? C::GP : 1];                  // per-channel gain
+    float la1[VEC ? C::GP : 1];                 // or one value per token
+    float be1[VEC ? C::GP : 1];
+    float fla, fbe;  // FACTORED: per-token scalars (threads < 64)
 };
 
+// Loads are unconditional: rows past the end of the sequence read the last
+// valid token (always in bounds) and are zeroed when staged into LDS.  No
+// loaded value is touched here, so the loads stay in flight until staging.
 template <int DK, int NW, bool F32IN, bool VEC>
 __device__ __forceinline__ void prefetch(Stage<DK, NW, F32IN, VEC>& st, const ChunkParams& p,
                                          long bh, long t0, int j0, int tid) {
@@ -315,7 +323,7 @@ __device__ __forceinline__ void prefetch(Stage<DK, NW, F32IN, VEC>& st, const Ch
     using RawT = typename C::RawT;
     constexpr int PIECE = Raw<F32IN>::PIECE;
     constexpr int PPR = DK / PIECE;  // pieces per row
-    const uint4 zero = {0u, 0u, 0u, 0u};
+    const long tmax = p.T - 1;
     const RawT* K = static_cast<const RawT*>(p.k);
     const RawT* Q = static_cast<const RawT*>(p.q);
     const RawT* V = static_cast<const RawT*>(p.v);
@@ -323,39 +331,25 @@ __device__ __forceinline__ void prefetch(Stage<DK, NW, F32IN, VEC>& st, const Ch
     for (int m = 0; m < C::KP; ++m) {
         const int pi = tid + m * C::NTHR;
         const int row = pi / PPR, col = (pi % PPR) * PIECE;
-        const long t = t0 + row;
+        const long t = min(t0 + row, tmax);
         const long off = (bh * p.T + t) * DK + col;
-        st.k[m] = (t < p.T) ? *reinterpret_cast<const uint4*>(K + off) : zero;
-        st.q[m] = (t < p.T) ? *reinterpret_cast<const uint4*>(Q + off) : zero;
+        st.k[m] = *reinterpret_cast<const uint4*>(K + off);
+        st.q[m] = *reinterpret_cast<const uint4*>(Q + off);
     }
     constexpr int VPR = C::DVT / PIECE;
 #pragma unroll
     for (int m = 0; m < C::VP; ++m) {
         const int pi = tid + m * C::NTHR;
         const int row = pi / VPR, col = (pi % VPR) * PIECE;
-        const long t = t0 + row;
-        const bool ok = t < p.T;
-        const long voff = (bh * p.T + t) * p.dv + j0 + col;
-        st.v[m] = ok ? *reinterpret_cast<const uint4*>(V + voff) : zero;
-        // value-side gain for the same PIECE columns, as PIECE/4 float4s
+        const long tok = bh * p.T + min(t0 + row, tmax);
+        st.v[m] = *reinterpret_cast<const uint4*>(V + tok * p.dv + j0 + col);
+        if (p.gvec) {
 #pragma unroll
-        for (int h = 0; h < PIECE / 4; ++h) {
-            f32x4 g = {0.f, 0.f, 0.f, 0.f};
-            if (ok) {
-                const long tok = bh * p.T + t;
-                if (p.gamma_mode == PDN_GATE_VEC) {
-                    g = *reinterpret_cast<const f32x4*>(p.gamma + tok * p.dv + j0 + col + 4 * h);
-                } else if (p.gamma_mode == PDN_GATE_SCALAR) {
-                    const float s = p.gamma[tok];
-                    g = f32x4{s, s, s, s};
-                } else if (p.beta_mode == PDN_GATE_VEC) {  // same as beta, dk == dv
-                    g = *reinterpret_cast<const f32x4*>(p.beta + tok * DK + j0 + col + 4 * h);
-                } else {
-                    const float s = p.beta[tok];
-                    g = f32x4{s, s, s, s};
-                }
-            }
-            st.gam[m * (PIECE / 4) + h] = g;
+            for (int h = 0; h < PIECE / 4; ++h)
+                st.gam[m * (PIECE / 4) + h] =
+                    *reinterpret_cast<const f32x4*>(p.gsrc + tok * p.gts + j0 + col + 4 * h);
+        } else {
+            st.gam1[m] = p.gsrc[tok * p.gts];
         }
     }
     if constexpr (VEC) {
@@ -364,36 +358,21 @@ __device__ __forceinline__ void prefetch(Stage<DK, NW, F32IN, VEC>& st, const Ch
         for (int m = 0; m < C::GP; ++m) {
             const int pi = tid + m * C::NTHR;
             const int row = pi / GPR, col = (pi % GPR) * 4;
-            const long t = t0 + row;
-            f32x4 la = {0.f, 0.f, 0.f, 0.f}, be = {0.f, 0.f, 0.f, 0.f};
-            if (t < p.T) {
-                const long tok = bh * p.T + t;
-                if (p.alpha_mode == PDN_ALPHA_VEC)
-                    la = *reinterpret_cast<const f32x4*>(p.log_alpha + tok * DK + col);
-                else if (p.alpha_mode == PDN_ALPHA_SCALAR) {
-                    const float s = p.log_alpha[tok];
-                    la = f32x4{s, s, s, s};
-                }
-                if (p.beta_mode == PDN_GATE_VEC)
-                    be = *reinterpret_cast<const f32x4*>(p.beta + tok * DK + col);
-                else {
-                    const float s = p.beta[tok];
-                    be = f32x4{s, s, s, s};
-                }
-            }
-            st.la[m] = la;
-            st.be[m] = be;
+            const long tok = bh * p.T + min(t0 + row, tmax);
+            if (p.alpha_mode == PDN_ALPHA_VEC)
+                st.la[m] = *reinterpret_cast<const f32x4*>(p.log_alpha + tok * DK + col);
+            else if (p.alpha_mode == PDN_ALPHA_SCALAR)
+                st.la1[m] = p.log_alpha[tok];
+            if (p.beta_mode == PDN_GATE_VEC)
+                st.be[m] = *reinterpret_cast<const f32x4*>(p.beta + tok * DK + col);
+            else
+                st.be1[m] = p.beta[tok];
         }
     } else {
-        st.la1 = 0.0f;
-        st.be1 = 0.0f;
         if (tid < CH) {
-            const long t = t0 + tid;
-            if (t < p.T) {
-                const long tok = bh * p.T + t;
-                if (p.alpha_mode != PDN_ALPHA_NONE) st.la1 = p.log_alpha[tok];
-                st.be1 = p.beta[tok];
-            }
+            const long tok = bh * p.T + min(t0 + tid, tmax);
+            if (p.alpha_mode != PDN_ALPHA_NONE) st.fla = p.log_alpha[tok];
+            st.fbe = p.beta[tok];
         }
     }
 }
@@ -428,11 +407,16 @@ __global__ void __launch_bounds__(64 * NW) chunk_fwd_kernel(ChunkParams p) {
 
     // ---- state: S[16*ib + 4g + e][col] in sacc[ib][e] ----
     f32x4 sacc[NIB];
+    if (p.S0) {
 #pragma unroll
-    for (int ib = 0; ib < NIB; ++ib)
+        for (int ib = 0; ib < NIB; ++ib)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            sacc[ib][e] = p.S0 ? p.S0[(bh * DK + 16 * ib + 4 * g + e) * p.dv + col] : 0.0f;
+            for (int e = 0; e < 4; ++e)
+                sacc[ib][e] = p.S0[(bh * DK + 16 * ib + 4 * g + e) * p.dv + col];
+    } else {
+#pragma unroll
+        for (int ib = 0; ib < NIB; ++ib) sacc[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
     if constexpr (VEC) {
         float* Ac = reinterpret_cast<float*>(smem + C::V_AC);
@@ -457,6 +441,10 @@ __global__ void __launch_bounds__(64 * NW) chunk_fwd_kernel(ChunkParams p) {
             for (int m = 0; m < C::KP; ++m) {
                 const int pi = tid + m * C::NTHR;
                 const int row = pi / PPR, c0 = (pi % PPR) * PIECE;
+                if (t0 + row >= p.T) {
+                    st.k[m] = uint4{0u, 0u, 0u, 0u};
+                    st.q[m] = uint4{0u, 0u, 0u, 0u};
+                }
                 // write PIECE logical columns as 4-column groups at permuted spots
 #pragma unroll
                 for (int h = 0; h < PIECE / 4; ++h) {
@@ -485,13 +473,17 @@ __global__ void __launch_bounds__(64 * NW) chunk_fwd_kernel(ChunkParams p) {
             for (int m = 0; m < C::VP; ++m) {
                 const int pi = tid + m * C::NTHR;
                 const int row = pi / VPR, c0 = (pi % VPR) * PIECE;
+                const bool ok = t0 + row < p.T;
                 const RawT* ve = reinterpret_cast<const RawT*>(&st.v[m]);
 #pragma unroll
                 for (int h = 0; h < PIECE / 4; ++h) {
-                    const f32x4 gm = st.gam[m * (PIECE / 4) + h];
+                    f32x4 gm;
+                    if (p.gvec) gm = st.gam[m * (PIECE / 4) + h];
+                    else gm = f32x4{st.gam1[m], st.gam1[m], st.gam1[m], st.gam1[m]};
                     f32x4 out;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) out[e] = sqrtf(gm[e]) * raw_to_f32(ve[4 * h + e]);
+                    for (int e = 0; e < 4; ++e)
+                        out[e] = ok ? sqrtf(gm[e]) * raw_to_f32(ve[4 * h + e]) : 0.0f;
                     *reinterpret_cast<f32x4*>(sV + row * C::VS + c0 + 4 * h) = out;
                 }
             }
@@ -503,22 +495,33 @@ __global__ void __launch_bounds__(64 * NW) chunk_fwd_kernel(ChunkParams p) {
                 for (int m = 0; m < C::GP; ++m) {
                     const int pi = tid + m * C::NTHR;
                     const int row = pi / GPR, pc = perm_col((pi % GPR) * 4);
-                    *reinterpret_cast<f32x4*>(sA + row * C::FS + pc) = st.be[m];
-                    *reinterpret_cast<f32x4*>(sB + row * C::FS + pc) = st.la[m];
+                    const bool ok = t0 + row < p.T;
+                    f32x4 be = (p.beta_mode == PDN_GATE_VEC)
+                                   ? st.be[m]
+                                   : f32x4{st.be1[m], st.be1[m], st.be1[m], st.be1[m]};
+                    f32x4 la = {0.f, 0.f, 0.f, 0.f};
+                    if (p.alpha_mode == PDN_ALPHA_VEC) la = st.la[m];
+                    else if (p.alpha_mode == PDN_ALPHA_SCALAR)
+                        la = f32x4{st.la1[m], st.la1[m], st.la1[m], st.la1[m]};
+                    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+                    *reinterpret_cast<f32x4*>(sA + row * C::FS + pc) = ok ? be : zero;
+                    *reinterpret_cast<f32x4*>(sB + row * C::FS + pc) = ok ? la : zero;
                 }
             } else {
                 // per-token scalars: block-relative cumulative decay (log2 units)
                 float* sc = reinterpret_cast<float*>(smem + C::F_SC);
                 if (tid < CH) {
-                    float gl = clamp_log_alpha(st.la1);
-                    if (p.alpha_mode == PDN_ALPHA_NONE) gl = 0.0f;
+                    const bool ok = t0 + tid < p.T;
+                    float gl = clamp_log_alpha(st.fla);
+                    if (p.alpha_mode == PDN_ALPHA_NONE || !ok) gl = 0.0f;
+                    const float fbe = ok ? st.fbe : 0.0f;
 #pragma unroll
                     for (int d = 1; d < 16; d <<= 1) {
                         const float o = __shfl_up(gl, d, 16);
                         if ((tid & 15) >= d) gl += o;
                     }
                     const float last = __shfl(gl, (tid & ~15) + 15, 64);
-                    const float sb = sqrtf(st.be1);
+                    const float sb = sqrtf(fbe);
                     sc[0 * CH + tid] = gl;                          // G2
                     sc[1 * CH + tid] = sb;                          // sqrt(beta)
                     sc[2 * CH + tid] = sb * exp2f(gl);              // rows of K.Gamma
@@ -873,14 +876,24 @@ int choose_nw(long nbh, int dv, bool vec, bool f32in) {
 size_t chunk_fwd_workspace_bytes(const pdn_chunk_fwd_args&) { return 0; }
 
 hipError_t launch_chunk_fwd(const pdn_chunk_fwd_args& a, hipStream_t stream) {
+    if (a.T > 0 && chunk_fact_supported(a)) return launch_chunk_fact(a, stream);
     ChunkParams p;
     p.q = a.q; p.k = a.k; p.v = a.v;
-    p.log_alpha = a.log_alpha; p.beta = a.beta; p.gamma = a.gamma;
+    p.log_alpha = a.log_alpha; p.beta = a.beta;
     p.A0 = a.precond_A0; p.AT = a.precond_AT; p.S0 = a.S0; p.ST = a.ST;
     p.o = a.o;
     p.T = a.T;
     p.dv = a.dv;
-    p.alpha_mode = a.alpha_mode; p.beta_mode = a.beta_mode; p.gamma_mode = a.gamma_mode;
+    p.alpha_mode = a.alpha_mode; p.beta_mode = a.beta_mode;
+    if (a.gamma_mode == PDN_GATE_VEC) {
+        p.gsrc = a.gamma; p.gts = a.dv; p.gvec = 1;
+    } else if (a.gamma_mode == PDN_GATE_SCALAR) {
+        p.gsrc = a.gamma; p.gts = 1; p.gvec = 0;
+    } else if (a.beta_mode == PDN_GATE_VEC) {  // same as beta (dk == dv)
+        p.gsrc = a.beta; p.gts = a.dk; p.gvec = 1;
+    } else {
+        p.gsrc = a.beta; p.gts = 1; p.gvec = 0;
+    }
     p.eps = a.precond_eps;
     p.o_bf16 = a.o_dtype == PDN_BF16;
     const bool vec = a.alpha_mode == PDN_ALPHA_VEC || a.beta_mode == PDN_GATE_VEC ||

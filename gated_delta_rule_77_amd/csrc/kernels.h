@@ -13,6 +13,10 @@ hipError_t launch_decode(const pdn_decode_args& a, hipStream_t stream);
 // Chunkwise prefill; returns a hipError_t.
 hipError_t launch_chunk_fwd(const pdn_chunk_fwd_args& a, hipStream_t stream);
 
+// Throughput prefill for per-token scalar decay and gain, bf16, dk = 128.
+bool chunk_fact_supported(const pdn_chunk_fwd_args& a);
+hipError_t launch_chunk_fact(const pdn_chunk_fwd_args& a, hipStream_t stream);
+
 // Scratch bytes the prefill needs for these (valid) arguments.
 size_t chunk_fwd_workspace_bytes(const pdn_chunk_fwd_args& a);
 

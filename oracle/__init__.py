@@ -55,8 +55,15 @@ def _load():
             f.argtypes = [I, I, I, I, I, P, P, P, I, P, I, P, I, P,
                           ctypes.c_double, P, P, P, P, P]
             f.restype = I
+            lib.oracle_num_threads.argtypes = []
+            lib.oracle_num_threads.restype = I
             _lib = lib
     return _lib
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle runs on (its parallelism is over (b, h))."""
+    return int(_load().oracle_num_threads())
 
 
 def _f64(x):

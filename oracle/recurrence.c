@@ -34,6 +34,9 @@
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define OR_ALPHA_NONE 0
 #define OR_ALPHA_SCALAR 1
@@ -133,4 +136,14 @@ int oracle_delta_rule(int B, int H, int T, int dk, int dv,
         free(S); free(A); free(al); free(kt); free(vt); free(u);
     }
     return failed ? -2 : 0;
+}
+
+/* Threads an OpenMP parallel region of the oracle uses (1 without OpenMP). */
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
 }
