@@ -18,12 +18,15 @@
 // sequence and has four waves:
 //   waves 0-1 ("chain"): 16 state columns each, held in MFMA accumulator
 //     registers; per chunk 132 bf16 MFMAs (16x16x32) on hi/lo-split operands.
-//   waves 2-3 ("helpers"): while the chain waves work on chunk c, they load
-//     chunk c+1 from HBM and build everything the chain needs for it: the key
-//     and query tiles (XOR-swizzled bf16), the gate-scaled value tile, the
-//     per-token row scales, P, and M (helper 2 forms T^T with MFMAs, inverts
-//     the 16x16 diagonal blocks by forward substitution and fills the
-//     off-diagonal blocks with MFMAs; helper 3 forms P and stages q, v).
+//   waves 2-3 ("helpers"): while the chain waves work on chunk c, they build
+//     everything chunk c+1 needs, from data they loaded two chunks ahead:
+//     wave 2 stages the key tile, forms T with MFMAs, inverts its 16x16
+//     diagonal blocks by forward substitution and fills the off-diagonal
+//     blocks of M with MFMAs; wave 3 stages the query tile, the gate-scaled
+//     value tile and the per-row scales, and forms P.  M and P are written
+//     already split into bf16 hi/lo fragments in the per-lane order of the
+//     chain's MFMA operands, so the chain reads them with one 16-byte load
+//     per term and no conversion.
 // LDS holds two chunk buffers; one workgroup barrier per chunk hands a
 // buffer from the helpers to the chain waves.  The state-update operand K^T
 // is read from the row-major key tile with the gfx950 LDS transpose read
@@ -39,21 +42,22 @@ constexpr int CH = 64;
 constexpr int NCHAIN = 2;
 constexpr int NTHR = 64 * (NCHAIN + 2);
 constexpr int DVT = 16 * NCHAIN;
-constexpr int VS = DVT + 4;  // fp32 value tile row stride
+constexpr int VTS = CH + 4;  // row stride of the transposed value tile (floats)
+constexpr int NFRAG = 6;     // lower-triangular (block row, k-step) operand fragments
 
-// LDS layout (bytes).  Per buffer: K, Q (bf16 [64][128], swizzled), M, P
-// (fp32 [64][64], k-permuted columns, swizzled), V (fp32 [64][VS]), scalars.
+// LDS layout (bytes).  Per buffer: K, Q (bf16 [64][128], swizzled), M and P
+// fragments, the value tile transposed (fp32 [32][VTS]), per-row scales.
 constexpr int B_K = 0;
 constexpr int B_Q = B_K + CH * DK * 2;
-constexpr int B_M = B_Q + CH * DK * 2;
-constexpr int B_P = B_M + CH * CH * 4;
-constexpr int B_V = B_P + CH * CH * 4;
-constexpr int B_SC = B_V + CH * VS * 4;
-constexpr int SC_FLOATS = 3 * CH + 4;  // rsKS[64], rq[64], rk[64], gC
-constexpr int BUF = B_SC + ((SC_FLOATS * 4 + 15) / 16) * 16;
-constexpr int SCR = 2 * BUF;           // helper-2 scratch: 4 diagonal 16x16 blocks
-constexpr int SCR_STRIDE = 16 * 20 + 16;  // floats between blocks
-constexpr int LDS_BYTES = SCR + 4 * SCR_STRIDE * 4;
+constexpr int B_MF = B_Q + CH * DK * 2;
+constexpr int B_PF = B_MF + NFRAG * 2 * 64 * 16;
+constexpr int B_VT = B_PF + NFRAG * 2 * 64 * 16;
+constexpr int B_SC = B_VT + DVT * VTS * 4;
+constexpr int BUF = B_SC + 4 * CH * 4;  // rsKS[64], rq[64], rk[64], gC
+constexpr int SCR = 2 * BUF;            // wave 2: four diagonal 16x16 blocks
+constexpr int SCR_STRIDE = 16 * 20 + 16;
+constexpr int GA = SCR + 4 * SCR_STRIDE * 4;  // per helper: G2[64], sb[64]
+constexpr int LDS_BYTES = GA + 2 * 2 * CH * 4;
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 
 struct FactParams {
@@ -98,10 +102,11 @@ __device__ __forceinline__ int kq_off(int r, int pc) {
     return r * DK + ((((pc >> 3) ^ f) << 3) | (pc & 7));
 }
 
-// M/P tiles: element (row r, physical column pc) of a [64][64] fp32 tile with
-// the 16-byte chunks XORed with r % 16.
-__device__ __forceinline__ int mp_off(int r, int pc) {
-    return r * CH + ((((pc >> 2) ^ (r & 15)) << 2) | (pc & 3));
+// Byte offset of term `plane` (0 = hi, 1 = lo) for `lane` in the fragment of
+// (block row R, k-step t), t <= R / 2.
+__device__ __forceinline__ int frag_off(int R, int t, int plane, int lane) {
+    const int f = (R < 2) ? R : 2 + 2 * (R - 2) + t;
+    return ((f * 2 + plane) * 64 + lane) * 16;
 }
 
 template <int NT>
@@ -165,6 +170,8 @@ __device__ __forceinline__ void split_pair(const f32x4& lo4, const f32x4& hi4, b
     split8<2>(x, o);
 }
 
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8, u); }
+
 // ---------------------------------------------------------------------------
 // helper-wave pieces
 // ---------------------------------------------------------------------------
@@ -173,6 +180,14 @@ __device__ __forceinline__ void split_pair(const f32x4& lo4, const f32x4& hi4, b
 // R and k-step t, the 8 channels 32t + 8g .. +7 of token 16R + ln.
 struct RowOps {
     uint4 d[4][4];  // [R][t]
+};
+
+// One chunk's raw inputs as loaded by a helper wave.
+struct HelperRegs {
+    RowOps k, q;    // q: wave 3 only
+    uint4 v[4];     // wave 3: this lane's token, value columns 8m .. 8m + 7
+    float gam1;     // wave 3: this lane's scalar value gain
+    float la, be;   // this lane's token
 };
 
 __device__ __forceinline__ void load_rows(RowOps& ops, const uint16_t* base, long bh, long T,
@@ -208,29 +223,13 @@ __device__ __forceinline__ void stage_rows(const RowOps& ops, uint16_t* tile, in
         }
 }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8, u); }
-
-// Per-token gate quantities of one chunk, one token per lane (lane < 64):
-// inclusive cumulative log2 decay G2 and sqrt(beta); rows past T get G2 held
-// and sb = 0 (no erase, no write).
-struct Gates {
-    float G2, sb, G2last;
-};
-
-__device__ __forceinline__ Gates chunk_gates(const FactParams& p, long bh, long t0, int lane,
-                                             float la_raw, float be_raw) {
-    const bool ok = t0 + lane < p.T;
-    float gl = (p.has_alpha && ok) ? fmaxf(la_raw, kLogAlphaMin) * kLog2e : 0.0f;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const float o = __shfl_up(gl, d, 64);
-        if (lane >= d) gl += o;
-    }
-    Gates G;
-    G.G2 = gl;
-    G.sb = ok ? sqrtf(be_raw) : 0.0f;
-    G.G2last = __shfl(gl, 63, 64);
-    return G;
+// Write one operand fragment (8 values of this lane) as hi/lo bf16 terms.
+__device__ __forceinline__ void put_frag(char* base, int R, int t, int lane, const f32x4& lo4,
+                                         const f32x4& hi4) {
+    bf16x8 h[2];
+    split_pair(lo4, hi4, h);
+    *reinterpret_cast<bf16x8*>(base + frag_off(R, t, 0, lane)) = h[0];
+    *reinterpret_cast<bf16x8*>(base + frag_off(R, t, 1, lane)) = h[1];
 }
 
 // ---------------------------------------------------------------------------
@@ -249,192 +248,9 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
     const long bh = blockIdx.x / ntile;
     const int j0 = (blockIdx.x % ntile) * DVT;
     const long nchunks = (p.T + CH - 1) / CH;
-    const bool chain = wave < NCHAIN;
 
-    // ---------------- helper state ----------------
-    RowOps kops, qops;          // current chunk's rows (helpers)
-    float la_raw = 0.f, be_raw = 0.f;
-    uint4 vraw[4];              // helper 3: value tile pieces (row, 8 columns)
-    f32x4 gam[8];               // helper 3: value gains (per column) ...
-    float gam1[4];              // ... or one per row
-    auto issue_loads = [&](long t0) {
-        const long tok = bh * p.T + min(t0 + lane, p.T - 1);
-        la_raw = p.log_alpha[tok];
-        be_raw = p.beta[tok];
-        load_rows(kops, p.k, bh, p.T, t0, ln, g);
-        if (wave == NCHAIN + 1) {
-            load_rows(qops, p.q, bh, p.T, t0, ln, g);
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {  // 64 rows x 4 pieces of 8 columns
-                const int pi = lane + 64 * m;
-                const int row = pi >> 2, c0 = (pi & 3) * 8;
-                const long tk = bh * p.T + min(t0 + row, p.T - 1);
-                vraw[m] = *reinterpret_cast<const uint4*>(p.v + tk * p.dv + j0 + c0);
-                if (p.gvec) {
-                    gam[2 * m] = *reinterpret_cast<const f32x4*>(p.gsrc + tk * p.gts + j0 + c0);
-                    gam[2 * m + 1] = *reinterpret_cast<const f32x4*>(p.gsrc + tk * p.gts + j0 + c0 + 4);
-                } else {
-                    gam1[m] = p.gsrc[tk * p.gts];
-                }
-            }
-        }
-    };
-
-    // Build everything chunk `c` needs into buffer `buf` (helper waves only).
-    auto prepare = [&](long c, char* buf) {
-        const long t0 = c * CH;
-        mask_rows(kops, p.T, t0, ln);
-        const Gates G = chunk_gates(p, bh, t0, lane, la_raw, be_raw);
-        if (wave == NCHAIN) {
-            // ---- helper 2: stage K, form T^T, invert, write M ----
-            stage_rows(kops, reinterpret_cast<uint16_t*>(buf + B_K), ln, g);
-            float* scr = reinterpret_cast<float*>(smem + SCR);
-            // T^T blocks: tt[R][J] holds T[16R + ln][16J + 4g + e] (J < R) in registers;
-            // diagonal blocks go to the scratch in natural layout.
-            f32x4 tt[4][4];
-#pragma unroll
-            for (int R = 0; R < 4; ++R)
-#pragma unroll
-                for (int J = 0; J <= R; ++J) {
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int t = 0; t < 4; ++t)
-                        acc = mfma32(as_bf16x8(kops.d[J][t]), as_bf16x8(kops.d[R][t]), acc);
-                    const int r = 16 * R + ln;
-                    const float G2r = __shfl(G.G2, r, 64), sbr = __shfl(G.sb, r, 64);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int s = 16 * J + 4 * g + e;
-                        const float G2s = __shfl(G.G2, s, 64), sbs = __shfl(G.sb, s, 64);
-                        acc[e] = (s < r) ? acc[e] * sbr * sbs * exp2f(G2r - G2s) : 0.0f;
-                    }
-                    if (J == R)
-                        *reinterpret_cast<f32x4*>(scr + R * SCR_STRIDE + ln * 20 + 4 * g) = acc;
-                    else
-                        tt[R][J] = acc;
-                }
-            // diagonal blocks: (I + T_RR)^-1 by forward substitution, lane = (R, column)
-            {
-                float* B = scr + (lane >> 4) * SCR_STRIDE;
-                const int cc = lane & 15;
-                float x[16];
-#pragma unroll
-                for (int r = 0; r < 16; ++r) x[r] = (r == cc) ? 1.0f : 0.0f;
-#pragma unroll
-                for (int r = 1; r < 16; ++r) {
-                    float acc = 0.0f;
-#pragma unroll
-                    for (int j = 0; j < r; ++j) acc = fmaf(B[r * 20 + j], x[j], acc);
-                    if (r > cc) x[r] = -acc;
-                }
-#pragma unroll
-                for (int r = 0; r < 16; ++r) B[r * 20 + cc] = x[r];
-            }
-            // D_S in accumulator layout (lane holds D_S[4g+e][ln]) and -D_R as A operand
-            auto dblk = [&](int S) {
-                f32x4 v;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = scr[S * SCR_STRIDE + (4 * g + e) * 20 + ln];
-                return v;
-            };
-            auto negd_a = [&](int R, bf16x4 (&a)[2]) {
-                const f32x4 v = *reinterpret_cast<const f32x4*>(scr + R * SCR_STRIDE + ln * 20 + 4 * g);
-                float x[4] = {-v[0], -v[1], -v[2], -v[3]};
-                split4<2>(x, a);
-            };
-            // M_RS = -D_R sum_{J=S}^{R-1} T_RJ M_JS, in accumulator layout.
-            // T_RJ M_JS = X^T Y with X = T_RJ^T (held) and Y = M_JS (held).
-            f32x4 mo[4][4];
-#pragma unroll
-            for (int d = 1; d < 4; ++d)
-#pragma unroll
-                for (int S = 0; S + d < 4; ++S) {
-                    const int R = S + d;
-                    f32x4 w = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int J = S; J < R; ++J) {
-                        bf16x4 a[2], b[2];
-                        split_d(tt[R][J], a);
-                        split_d(J == S ? dblk(S) : mo[J][S], b);
-                        w = mm22x16(a, b, w);
-                    }
-                    bf16x4 a[2], b[2];
-                    negd_a(R, a);
-                    split_d(w, b);
-                    f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                    mo[R][S] = mm22x16(a, b, z);
-                }
-            // write M (fp32, k-permuted swizzled); zero the upper blocks the chain reads
-            float* sM = reinterpret_cast<float*>(buf + B_M);
-#pragma unroll
-            for (int R = 0; R < 4; ++R)
-#pragma unroll
-                for (int S = 0; S < 4; ++S) {
-                    if (S > R && !((R == 0 && S == 1) || (R == 2 && S == 3))) continue;
-                    f32x4 v = {0.f, 0.f, 0.f, 0.f};
-                    if (S == R) v = dblk(R);
-                    else if (S < R) v = mo[R][S];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        sM[mp_off(16 * R + 4 * g + e, kperm(16 * S + ln))] = v[e];
-                }
-        } else {
-            // ---- helper 3: stage Q, V, scalars; form P ----
-            mask_rows(qops, p.T, t0, ln);
-            stage_rows(qops, reinterpret_cast<uint16_t*>(buf + B_Q), ln, g);
-            float* sc = reinterpret_cast<float*>(buf + B_SC);
-            sc[lane] = G.sb * exp2f(G.G2);                    // rows of K.Gamma
-            sc[CH + lane] = exp2f(G.G2);                      // rows of Q.Gamma
-            sc[2 * CH + lane] = G.sb * exp2f(G.G2last - G.G2);  // rows of Khat
-            if (lane == 0) sc[3 * CH] = exp2f(G.G2last);       // chunk decay
-            float* sV = reinterpret_cast<float*>(buf + B_V);
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int pi = lane + 64 * m;
-                const int row = pi >> 2, c0 = (pi & 3) * 8;
-                const bool ok = t0 + row < p.T;
-                const uint16_t* ve = reinterpret_cast<const uint16_t*>(&vraw[m]);
-                f32x4 o0, o1;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float g0 = p.gvec ? gam[2 * m][e] : gam1[m];
-                    const float g1 = p.gvec ? gam[2 * m + 1][e] : gam1[m];
-                    o0[e] = ok ? sqrtf(g0) * bf16_bits_to_f32(ve[e]) : 0.0f;
-                    o1[e] = ok ? sqrtf(g1) * bf16_bits_to_f32(ve[4 + e]) : 0.0f;
-                }
-                *reinterpret_cast<f32x4*>(sV + row * VS + c0) = o0;
-                *reinterpret_cast<f32x4*>(sV + row * VS + c0 + 4) = o1;
-            }
-            float* sP = reinterpret_cast<float*>(buf + B_P);
-#pragma unroll
-            for (int R = 0; R < 4; ++R)
-#pragma unroll
-                for (int S = 0; S < 4; ++S) {
-                    if (S > R && !((R == 0 && S == 1) || (R == 2 && S == 3))) continue;
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                    if (S <= R) {
-#pragma unroll
-                        for (int t = 0; t < 4; ++t)
-                            acc = mfma32(as_bf16x8(qops.d[R][t]), as_bf16x8(kops.d[S][t]), acc);
-                        const int s = 16 * S + ln;
-                        const float G2s = __shfl(G.G2, s, 64), sbs = __shfl(G.sb, s, 64);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int r = 16 * R + 4 * g + e;
-                            const float G2r = __shfl(G.G2, r, 64);
-                            acc[e] = (s <= r) ? acc[e] * sbs * exp2f(G2r - G2s) : 0.0f;
-                        }
-                    }
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        sP[mp_off(16 * R + 4 * g + e, kperm(16 * S + ln))] = acc[e];
-                }
-        }
-    };
-
-    // The two roles run separate loops with the same number of barriers, so
-    // their register live ranges do not overlap.
-    if (chain) {
+    if (wave < NCHAIN) {
+        // =========================== chain waves ===========================
         f32x4 sacc[8];
         const int col = j0 + 16 * wave + ln;
         if (p.S0) {
@@ -452,10 +268,8 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
             const char* cur = smem + (c & 1) * BUF;
             const uint16_t* sK = reinterpret_cast<const uint16_t*>(cur + B_K);
             const uint16_t* sQ = reinterpret_cast<const uint16_t*>(cur + B_Q);
-            const float* sM = reinterpret_cast<const float*>(cur + B_M);
-            const float* sP = reinterpret_cast<const float*>(cur + B_P);
-            const float* sV = reinterpret_cast<const float*>(cur + B_V);
             const float* sc = reinterpret_cast<const float*>(cur + B_SC);
+            const float* sVt = reinterpret_cast<const float*>(cur + B_VT) + (16 * wave + ln) * VTS;
             const long t0 = c * CH;
 
             // state as x32 B operands (k = key channel)
@@ -481,28 +295,25 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
             // X = Vt - diag(sb Gamma) Y
             f32x4 x[4];
 #pragma unroll
-            for (int a = 0; a < 4; ++a)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 16 * a + 4 * g + e;
-                    x[a][e] = sV[r * VS + 16 * wave + ln] - sc[r] * y[a][e];
-                }
+            for (int a = 0; a < 4; ++a) {
+                const f32x4 rs = *reinterpret_cast<const f32x4*>(sc + 16 * a + 4 * g);
+                const f32x4 vv = *reinterpret_cast<const f32x4*>(sVt + 16 * a + 4 * g);
+                x[a] = vv - rs * y[a];
+            }
             bf16x8 bX[2][2];
             split_pair(x[0], x[1], bX[0]);
             split_pair(x[2], x[3], bX[1]);
             // U = M X  (M lower triangular: block row R uses k-steps t <= R/2)
+            const char* mf = cur + B_MF;
             f32x4 u[4];
 #pragma unroll
             for (int R = 0; R < 4; ++R) {
                 u[R] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int t = 0; t <= R / 2; ++t) {
-                    float mv[8];
-                    const int r = 16 * R + ln, pc = 32 * t + 8 * g;
-                    *reinterpret_cast<f32x4*>(mv) = *reinterpret_cast<const f32x4*>(sM + mp_off(r, pc));
-                    *reinterpret_cast<f32x4*>(mv + 4) = *reinterpret_cast<const f32x4*>(sM + mp_off(r, pc + 4));
                     bf16x8 am[2];
-                    split8<2>(mv, am);
+                    am[0] = *reinterpret_cast<const bf16x8*>(mf + frag_off(R, t, 0, lane));
+                    am[1] = *reinterpret_cast<const bf16x8*>(mf + frag_off(R, t, 1, lane));
                     u[R] = mm22(am, bX[t], u[R]);
                 }
             }
@@ -510,37 +321,37 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
             split_pair(u[0], u[1], bU[0]);
             split_pair(u[2], u[3], bU[1]);
             // O = diag(Gamma) Z + P U
+            const char* pf = cur + B_PF;
+            const bool full = t0 + CH <= p.T;
 #pragma unroll
             for (int R = 0; R < 4; ++R) {
-                f32x4 oacc;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) oacc[e] = z[R][e] * sc[CH + 16 * R + 4 * g + e];
+                const f32x4 rq = *reinterpret_cast<const f32x4*>(sc + CH + 16 * R + 4 * g);
+                f32x4 oacc = rq * z[R];
 #pragma unroll
                 for (int t = 0; t <= R / 2; ++t) {
-                    float pv[8];
-                    const int r = 16 * R + ln, pc = 32 * t + 8 * g;
-                    *reinterpret_cast<f32x4*>(pv) = *reinterpret_cast<const f32x4*>(sP + mp_off(r, pc));
-                    *reinterpret_cast<f32x4*>(pv + 4) = *reinterpret_cast<const f32x4*>(sP + mp_off(r, pc + 4));
                     bf16x8 ap[2];
-                    split8<2>(pv, ap);
+                    ap[0] = *reinterpret_cast<const bf16x8*>(pf + frag_off(R, t, 0, lane));
+                    ap[1] = *reinterpret_cast<const bf16x8*>(pf + frag_off(R, t, 1, lane));
                     oacc = mm22(ap, bU[t], oacc);
                 }
+                const long row0 = (bh * p.T + t0 + 16 * R + 4 * g) * p.dv + col;
+                if (p.o_bf16) {
+                    uint16_t* op = static_cast<uint16_t*>(p.o) + row0;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const long t = t0 + 16 * R + 4 * g + e;
-                    if (t < p.T) {
-                        const long oi = (bh * p.T + t) * p.dv + col;
-                        if (p.o_bf16) static_cast<uint16_t*>(p.o)[oi] = f32_to_bf16_bits(oacc[e]);
-                        else static_cast<float*>(p.o)[oi] = oacc[e];
-                    }
+                    for (int e = 0; e < 4; ++e)
+                        if (full || t0 + 16 * R + 4 * g + e < p.T) op[e * p.dv] = f32_to_bf16_bits(oacc[e]);
+                } else {
+                    float* op = static_cast<float*>(p.o) + row0;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (full || t0 + 16 * R + 4 * g + e < p.T) op[e * p.dv] = oacc[e];
                 }
             }
             // S <- Gamma_63 S + K^T diag(sb exp(G_63 - G)) U
             f32x4 us[4];
 #pragma unroll
             for (int R = 0; R < 4; ++R)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) us[R][e] = u[R][e] * sc[2 * CH + 16 * R + 4 * g + e];
+                us[R] = u[R] * *reinterpret_cast<const f32x4*>(sc + 2 * CH + 16 * R + 4 * g);
             bf16x8 bUs[2][2];
             split_pair(us[0], us[1], bUs[0]);
             split_pair(us[2], us[3], bUs[1]);
@@ -552,13 +363,12 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
                 for (int t = 0; t < 2; ++t) {
                     // A operand: K^T rows 16ib..16ib+15 (channels), k-slots = tokens
                     // {32t + 4g + 0..3, 32t + 16 + 4g + 0..3}, via transpose reads.
-                    const int q4 = ln & 3, jj = ln >> 2;
-                    const int pcol = kperm(16 * ib + 4 * q4);
-                    const int tokA = 32 * t + 4 * g + jj, tokB = tokA + 16;
+                    const int pcol = kperm(16 * ib + 4 * (ln & 3));
+                    const int tokA = 32 * t + 4 * g + (ln >> 2);
                     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                         (lds_s16x4*)(sK + kq_off(tokA, pcol)));
                     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_s16x4*)(sK + kq_off(tokB, pcol)));
+                        (lds_s16x4*)(sK + kq_off(tokA + 16, pcol)));
                     // whole-vector reinterpretation (an element-wise short -> bf16
                     // bit_cast loop is mis-lowered by this compiler: it replicates
                     // element 0)
@@ -576,20 +386,234 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
                 for (int e = 0; e < 4; ++e)
                     p.ST[(bh * DK + 16 * ib + 4 * g + e) * p.dv + col] = sacc[ib][e];
         }
-    } else {
-        if (nchunks > 0) {
-            issue_loads(0);
-            prepare(0, smem);
-            if (nchunks > 1) issue_loads(CH);
-        }
-        __syncthreads();
-        for (long c = 0; c < nchunks; ++c) {
-            if (c + 1 < nchunks) {
-                prepare(c + 1, smem + ((c + 1) & 1) * BUF);
-                if (c + 2 < nchunks) issue_loads((c + 2) * CH);
+        return;
+    }
+
+    // ============================= helper waves =============================
+    const bool w2 = wave == NCHAIN;  // else wave 3
+    float* ga = reinterpret_cast<float*>(smem + GA) + (w2 ? 0 : 2 * CH);
+
+    auto load = [&](long c, HelperRegs& H) {
+        const long t0 = c * CH;
+        const long tok = bh * p.T + min(t0 + lane, p.T - 1);
+        H.la = p.log_alpha[tok];
+        H.be = p.beta[tok];
+        load_rows(H.k, p.k, bh, p.T, t0, ln, g);
+        if (!w2) {
+            load_rows(H.q, p.q, bh, p.T, t0, ln, g);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {  // this lane's token, columns 8m .. 8m + 7
+                const int row = lane, c0 = 8 * m;
+                const long tk = bh * p.T + min(t0 + row, p.T - 1);
+                H.v[m] = *reinterpret_cast<const uint4*>(p.v + tk * p.dv + j0 + c0);
             }
-            __syncthreads();
+            if (!p.gvec) H.gam1 = p.gsrc[tok * p.gts];
         }
+    };
+
+    // Build everything chunk c needs into `buf` from the registers in H.
+    auto prepare = [&](long c, char* buf, HelperRegs& H) {
+        const long t0 = c * CH;
+        mask_rows(H.k, p.T, t0, ln);
+        // per-token gates: inclusive cumulative log2 decay and sqrt(beta);
+        // rows past T hold G and get sb = 0 (no erase, no write)
+        const bool ok = t0 + lane < p.T;
+        float gl = (p.has_alpha && ok) ? fmaxf(H.la, kLogAlphaMin) * kLog2e : 0.0f;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const float o = __shfl_up(gl, d, 64);
+            if (lane >= d) gl += o;
+        }
+        const float sb = ok ? sqrtf(H.be) : 0.0f;
+        const float G2last = __shfl(gl, 63, 64);
+        ga[lane] = gl;
+        ga[CH + lane] = sb;
+        // gate values at rows 16R + ln and at columns 16J + 4g + e
+        float Gr[4], sbr[4];
+        f32x4 Gs[4], sbs[4];
+#pragma unroll
+        for (int R = 0; R < 4; ++R) {
+            Gr[R] = ga[16 * R + ln];
+            sbr[R] = ga[CH + 16 * R + ln];
+            Gs[R] = *reinterpret_cast<const f32x4*>(ga + 16 * R + 4 * g);
+            sbs[R] = *reinterpret_cast<const f32x4*>(ga + CH + 16 * R + 4 * g);
+        }
+
+        if (w2) {
+            // ---- wave 2: form T, stage K, invert, write M fragments ----
+            // raw key Gram blocks first, so the key registers can be refilled
+            f32x4 tr[4][4];
+#pragma unroll
+            for (int R = 0; R < 4; ++R)
+#pragma unroll
+                for (int J = 0; J <= R; ++J) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        acc = mfma32(as_bf16x8(H.k.d[J][t]), as_bf16x8(H.k.d[R][t]), acc);
+                    tr[R][J] = acc;
+                }
+            stage_rows(H.k, reinterpret_cast<uint16_t*>(buf + B_K), ln, g);
+            if (c + 1 < nchunks) load(c + 1, H);
+            float* scr = reinterpret_cast<float*>(smem + SCR);
+            // tt[R][J] holds T[16R + ln][16J + 4g + e] for J < R (i.e. T_RJ^T in
+            // accumulator layout); diagonal blocks go to the scratch.
+            f32x4 tt[4][4];
+#pragma unroll
+            for (int R = 0; R < 4; ++R)
+#pragma unroll
+                for (int J = 0; J <= R; ++J) {
+                    f32x4 acc = tr[R][J];
+                    const int r = 16 * R + ln;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int s = 16 * J + 4 * g + e;
+                        acc[e] = (s < r) ? acc[e] * sbr[R] * sbs[J][e] * exp2f(Gr[R] - Gs[J][e]) : 0.0f;
+                    }
+                    if (J == R)
+                        *reinterpret_cast<f32x4*>(scr + R * SCR_STRIDE + ln * 20 + 4 * g) = acc;
+                    else
+                        tt[R][J] = acc;
+                }
+            // diagonal blocks: (I + T_RR)^-1 by forward substitution, lane = (R, column)
+            {
+                float* B = scr + (lane >> 4) * SCR_STRIDE;
+                const int cc = lane & 15;
+                float xs[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) xs[r] = (r == cc) ? 1.0f : 0.0f;
+#pragma unroll
+                for (int r = 1; r < 16; ++r) {
+                    float acc = 0.0f;
+#pragma unroll
+                    for (int j = 0; j < r; ++j) acc = fmaf(B[r * 20 + j], xs[j], acc);
+                    if (r > cc) xs[r] = -acc;
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) B[r * 20 + cc] = xs[r];
+            }
+            // dcol(S): D_S[4g+e][ln] (accumulator layout); drow(R): D_R[ln][4g+e]
+            auto dcol = [&](int S) {
+                f32x4 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = scr[S * SCR_STRIDE + (4 * g + e) * 20 + ln];
+                return v;
+            };
+            auto drow = [&](int R) {
+                return *reinterpret_cast<const f32x4*>(scr + R * SCR_STRIDE + ln * 20 + 4 * g);
+            };
+            // M_RS = -D_R sum_{J=S}^{R-1} T_RJ M_JS in accumulator layout (mo), and
+            // its transpose (mt) from the same operands with the roles swapped:
+            // a register block used as the A operand acts as its transpose.
+            f32x4 mo[4][4], mt[4][4];
+#pragma unroll
+            for (int d = 1; d < 4; ++d)
+#pragma unroll
+                for (int S = 0; S + d < 4; ++S) {
+                    const int R = S + d;
+                    f32x4 w = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int J = S; J < R; ++J) {
+                        bf16x4 a[2], b[2];
+                        split_d(tt[R][J], a);
+                        split_d(J == S ? dcol(S) : mo[J][S], b);
+                        w = mm22x16(a, b, w);
+                    }
+                    const f32x4 dr = drow(R);
+                    bf16x4 nd[2], bw[2];
+                    split_d(f32x4{-dr[0], -dr[1], -dr[2], -dr[3]}, nd);
+                    split_d(w, bw);
+                    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+                    mo[R][S] = mm22x16(nd, bw, zero);
+                    mt[R][S] = mm22x16(bw, nd, zero);
+                }
+            // M fragments: lane (ln, g) of fragment (R, t) holds M[16R + ln][32t + 4g + j]
+            // (j < 4) and M[16R + ln][32t + 16 + 4g + j - 4]: the transposed blocks
+            // (R, 2t) and (R, 2t + 1) in accumulator layout.
+            char* mf = buf + B_MF;
+            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+            put_frag(mf, 0, 0, lane, drow(0), zero);
+            put_frag(mf, 1, 0, lane, mt[1][0], drow(1));
+            put_frag(mf, 2, 0, lane, mt[2][0], mt[2][1]);
+            put_frag(mf, 2, 1, lane, drow(2), zero);
+            put_frag(mf, 3, 0, lane, mt[3][0], mt[3][1]);
+            put_frag(mf, 3, 1, lane, mt[3][2], drow(3));
+        } else {
+            // ---- wave 3: form P, stage Q, V (transposed), row scales ----
+            mask_rows(H.q, p.T, t0, ln);
+            // raw query-key products first, so the registers can be refilled
+            f32x4 pb[4][4];
+#pragma unroll
+            for (int R = 0; R < 4; ++R)
+#pragma unroll
+                for (int S = 0; S <= R; ++S) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        acc = mfma32(as_bf16x8(H.k.d[S][t]), as_bf16x8(H.q.d[R][t]), acc);
+                    pb[R][S] = acc;
+                }
+            stage_rows(H.q, reinterpret_cast<uint16_t*>(buf + B_Q), ln, g);
+            float* sc = reinterpret_cast<float*>(buf + B_SC);
+            sc[lane] = sb * exp2f(gl);                    // rows of K.Gamma
+            sc[CH + lane] = exp2f(gl);                    // rows of Q.Gamma
+            sc[2 * CH + lane] = sb * exp2f(G2last - gl);  // rows of Khat
+            if (lane == 0) sc[3 * CH] = exp2f(G2last);    // chunk decay
+            float* sVt = reinterpret_cast<float*>(buf + B_VT);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int row = lane, c0 = 8 * m;
+                const bool okr = t0 + row < p.T;
+                const uint16_t* ve = reinterpret_cast<const uint16_t*>(&H.v[m]);
+                float gam[8];
+                if (p.gvec) {
+                    const long tk = bh * p.T + min(t0 + row, p.T - 1);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) gam[e] = p.gsrc[tk * p.gts + j0 + c0 + e];
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) gam[e] = H.gam1;
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    sVt[(c0 + e) * VTS + row] = okr ? sqrtf(gam[e]) * bf16_bits_to_f32(ve[e]) : 0.0f;
+            }
+            if (c + 1 < nchunks) load(c + 1, H);
+            // P^T blocks: pb[R][S] holds P[16R + ln][16S + 4g + e]
+#pragma unroll
+            for (int R = 0; R < 4; ++R)
+#pragma unroll
+                for (int S = 0; S <= R; ++S) {
+                    const int r = 16 * R + ln;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int s = 16 * S + 4 * g + e;
+                        pb[R][S][e] = (s <= r) ? pb[R][S][e] * sbs[S][e] * exp2f(Gr[R] - Gs[S][e]) : 0.0f;
+                    }
+                }
+            char* pf = buf + B_PF;
+            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+            put_frag(pf, 0, 0, lane, pb[0][0], zero);
+            put_frag(pf, 1, 0, lane, pb[1][0], pb[1][1]);
+            put_frag(pf, 2, 0, lane, pb[2][0], pb[2][1]);
+            put_frag(pf, 2, 1, lane, pb[2][2], zero);
+            put_frag(pf, 3, 0, lane, pb[3][0], pb[3][1]);
+            put_frag(pf, 3, 1, lane, pb[3][2], pb[3][3]);
+        }
+    };
+
+    // The registers hold the inputs of the next chunk to prepare; prepare()
+    // refills them with the chunk after it as soon as they have been consumed,
+    // which leaves a whole chunk period for the loads to land.
+    HelperRegs H;
+    if (nchunks > 0) {
+        load(0, H);
+        prepare(0, smem, H);
+    }
+    __syncthreads();
+    for (long c = 0; c < nchunks; ++c) {
+        if (c + 1 < nchunks) prepare(c + 1, smem + ((c + 1) & 1) * BUF, H);
+        __syncthreads();
     }
 }
 
@@ -607,7 +631,7 @@ hipError_t launch_chunk_fact(const pdn_chunk_fwd_args& a, hipStream_t stream) {
     p.k = static_cast<const uint16_t*>(a.k);
     p.v = static_cast<const uint16_t*>(a.v);
     p.has_alpha = a.alpha_mode != PDN_ALPHA_NONE;
-    p.log_alpha = p.has_alpha ? a.log_alpha : a.beta;  // never read when no decay
+    p.log_alpha = p.has_alpha ? a.log_alpha : a.beta;  // never used when there is no decay
     p.beta = a.beta;
     if (a.gamma_mode == PDN_GATE_VEC) {
         p.gsrc = a.gamma; p.gts = a.dv; p.gvec = 1;
