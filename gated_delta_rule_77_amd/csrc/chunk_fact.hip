@@ -1,32 +1,33 @@
 // Prefill for per-token scalar decay and gain (Gated DeltaNet / DeltaNet
 // gating), bf16 q/k/v, dk = 128: the throughput path.
 //
-// Same chunk algebra as chunk_fwd.hip, but over whole 64-token chunks with a
-// precomputed 64x64 (I+T)^-1 ("Gated DeltaNet-2" method section 3: decay
-// absorbed into the erase/write matrices, one unit-lower-triangular solve per
-// chunk).  With G_r the cumulative log decay from the chunk start,
-// Gamma_r = exp(G_r), sb_r = sqrt(beta_r):
+// Same chunk algebra as chunk_fwd.hip, over whole 64-token chunks ("Gated
+// DeltaNet-2" method section 3: decay absorbed into the erase/write matrices,
+// one unit-lower-triangular solve per chunk).  With G_r the cumulative log
+// decay from the chunk start, Gamma_r = exp(G_r), sb_r = sqrt(beta_r):
 //
 //   T_rs = sb_r sb_s exp(G_r - G_s) (k_r . k_s)      s < r
 //   P_rs = sb_s exp(G_r - G_s) (q_r . k_s)           s <= r
-//   M    = (I + T)^-1
-//   U    = M (Vt - diag(sb Gamma) K S)
+//   X    = Vt - diag(sb Gamma) K S
+//   U    = (I + T)^-1 X
 //   O    = diag(Gamma) Q S + P U
 //   S   <- Gamma_63 S + K^T diag(sb exp(G_63 - G)) U
+//
+// U is found by block forward substitution over the four 16-token blocks of
+// the chunk: U_R = D_R (X_R - sum_{J<R} T_RJ U_J), D_R = (I + T_RR)^-1.
 //
 // Work split.  A workgroup owns (b, h, 32 value columns) for the whole
 // sequence and has four waves:
 //   waves 0-1 ("chain"): 16 state columns each, held in MFMA accumulator
-//     registers; per chunk 132 bf16 MFMAs (16x16x32) on hi/lo-split operands.
+//     registers; all products on hi/lo bf16 operands with fp32 accumulation.
 //   waves 2-3 ("helpers"): while the chain waves work on chunk c, they build
-//     everything chunk c+1 needs, from data they loaded two chunks ahead:
-//     wave 2 stages the key tile, forms T with MFMAs, inverts its 16x16
-//     diagonal blocks by forward substitution and fills the off-diagonal
-//     blocks of M with MFMAs; wave 3 stages the query tile, the gate-scaled
-//     value tile and the per-row scales, and forms P.  M and P are written
-//     already split into bf16 hi/lo fragments in the per-lane order of the
-//     chain's MFMA operands, so the chain reads them with one 16-byte load
-//     per term and no conversion.
+//     everything chunk c+1 needs from registers loaded one chunk ahead:
+//     wave 2 stages the key tile, forms T with MFMAs and inverts its 16x16
+//     diagonal blocks by forward substitution; wave 3 stages the query tile,
+//     the gain-scaled value tile and the per-row scales, and forms P.  The
+//     blocks of T, D and P are written already split into bf16 hi/lo
+//     fragments in the per-lane order of the chain's MFMA operands, so the
+//     chain reads them with one LDS load per term and no conversion.
 // LDS holds two chunk buffers; one workgroup barrier per chunk hands a
 // buffer from the helpers to the chain waves.  The state-update operand K^T
 // is read from the row-major key tile with the gfx950 LDS transpose read
@@ -43,14 +44,22 @@ constexpr int NCHAIN = 2;
 constexpr int NTHR = 64 * (NCHAIN + 2);
 constexpr int DVT = 16 * NCHAIN;
 constexpr int VTS = CH + 4;  // row stride of the transposed value tile (floats)
-constexpr int NFRAG = 6;     // lower-triangular (block row, k-step) operand fragments
+constexpr int NFRAG = 6;     // lower-triangular (block row, k-step) fragments of P
 
-// LDS layout (bytes).  Per buffer: K, Q (bf16 [64][128], swizzled), M and P
-// fragments, the value tile transposed (fp32 [32][VTS]), per-row scales.
+// Solve fragments (hi and lo terms, per lane): two 16x32 operands [-T_R0 | -T_R1]
+// for R = 2, 3 (16 bytes per lane and term), then six 16x16 operands D_0..D_3,
+// -T_10, -T_32 (8 bytes per lane and term).
+constexpr int TF16 = 2 * 2 * 64 * 16;
+constexpr int TF_BYTES = TF16 + 6 * 2 * 64 * 8;
+enum { F32_T2 = 0, F32_T3 = 1 };
+enum { F16_D0 = 0, F16_T10 = 4, F16_T32 = 5 };
+
+// LDS layout (bytes).  Per buffer: K, Q (bf16 [64][128], swizzled), solve and
+// P fragments, the value tile transposed (fp32 [32][VTS]), per-row scales.
 constexpr int B_K = 0;
 constexpr int B_Q = B_K + CH * DK * 2;
-constexpr int B_MF = B_Q + CH * DK * 2;
-constexpr int B_PF = B_MF + NFRAG * 2 * 64 * 16;
+constexpr int B_TF = B_Q + CH * DK * 2;
+constexpr int B_PF = B_TF + TF_BYTES;
 constexpr int B_VT = B_PF + NFRAG * 2 * 64 * 16;
 constexpr int B_SC = B_VT + DVT * VTS * 4;
 constexpr int BUF = B_SC + 4 * CH * 4;  // rsKS[64], rq[64], rk[64], gC
@@ -59,6 +68,7 @@ constexpr int SCR_STRIDE = 16 * 20 + 16;
 constexpr int GA = SCR + 4 * SCR_STRIDE * 4;  // per helper: G2[64], sb[64]
 constexpr int LDS_BYTES = GA + 2 * 2 * CH * 4;
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+static_assert(B_PF % 16 == 0 && B_VT % 16 == 0 && BUF % 16 == 0, "LDS alignment");
 
 struct FactParams {
     const uint16_t* q;
@@ -109,6 +119,11 @@ __device__ __forceinline__ int frag_off(int R, int t, int plane, int lane) {
     return ((f * 2 + plane) * 64 + lane) * 16;
 }
 
+__device__ __forceinline__ int f32_off(int s, int plane, int lane) { return ((s * 2 + plane) * 64 + lane) * 16; }
+__device__ __forceinline__ int f16_off(int s, int plane, int lane) {
+    return TF16 + ((s * 2 + plane) * 64 + lane) * 8;
+}
+
 template <int NT>
 __device__ __forceinline__ void split8(const float* x, bf16x8 (&o)[NT]) {
 #pragma unroll
@@ -123,25 +138,8 @@ __device__ __forceinline__ void split8(const float* x, bf16x8 (&o)[NT]) {
     }
 }
 
-template <int NT>
-__device__ __forceinline__ void split4(const float* x, bf16x4 (&o)[NT]) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        float r = x[e];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const bf16 h = static_cast<bf16>(r);
-            o[t][e] = h;
-            if (t + 1 < NT) r -= static_cast<float>(h);
-        }
-    }
-}
-
 __device__ __forceinline__ f32x4 mfma32(const bf16x8& a, const bf16x8& b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mfma16(const bf16x4& a, const bf16x4& b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
 // acc += a (1 term) * b (hi, lo)
@@ -155,22 +153,61 @@ __device__ __forceinline__ f32x4 mm22(const bf16x8 (&a)[2], const bf16x8 (&b)[2]
     c = mfma32(a[0], b[1], c);
     return mfma32(a[0], b[0], c);
 }
-__device__ __forceinline__ f32x4 mm22x16(const bf16x4 (&a)[2], const bf16x4 (&b)[2], f32x4 c) {
-    c = mfma16(a[1], b[0], c);
-    c = mfma16(a[0], b[1], c);
-    return mfma16(a[0], b[0], c);
-}
 
-__device__ __forceinline__ void split_d(const f32x4& v, bf16x4 (&o)[2]) {
-    float x[4] = {v[0], v[1], v[2], v[3]};
-    split4<2>(x, o);
-}
 __device__ __forceinline__ void split_pair(const f32x4& lo4, const f32x4& hi4, bf16x8 (&o)[2]) {
     float x[8] = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
     split8<2>(x, o);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8, u); }
+
+// Hardware exp2 / sqrt (about 1 ulp).  Decay exponents here are <= 0, so
+// exp2 only ever underflows towards 0.
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float sqrt_hw(float x) { return __builtin_amdgcn_sqrtf(x); }
+
+__device__ __forceinline__ f32x4 mfma16(const bf16x4& a, const bf16x4& b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+// acc += (hi, lo) * (hi, lo) on 16x16x16 operands, dropping lo*lo
+__device__ __forceinline__ f32x4 mm22x16(const bf16x4 (&a)[2], const bf16x4 (&b)[2], f32x4 c) {
+    c = mfma16(a[1], b[0], c);
+    c = mfma16(a[0], b[1], c);
+    return mfma16(a[0], b[0], c);
+}
+// hi/lo split of an accumulator block used as a 16x16x16 B operand
+__device__ __forceinline__ void split_d(const f32x4& v, bf16x4 (&o)[2]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const bf16 h = static_cast<bf16>(v[e]);
+        o[0][e] = h;
+        o[1][e] = static_cast<bf16>(v[e] - static_cast<float>(h));
+    }
+}
+// two 16x16x16 B operands stacked along k into one 16x16x32 B operand
+__device__ __forceinline__ bf16x8 cat4(const bf16x4& a, const bf16x4& b) {
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// DPP move of x from the lane given by `ctrl`; lanes with no source or
+// outside `row_mask` read 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp0(float x) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROW_MASK, 0xf, false));
+}
+
+// Inclusive prefix sum over the 64 lanes: shifts within 16-lane rows, then
+// the row totals carried across rows (row_bcast:15 / row_bcast:31).
+__device__ __forceinline__ float wave_incl_scan(float x) {
+    x += dpp0<0x111, 0xf>(x);  // row_shr:1
+    x += dpp0<0x112, 0xf>(x);  // row_shr:2
+    x += dpp0<0x114, 0xf>(x);  // row_shr:4
+    x += dpp0<0x118, 0xf>(x);  // row_shr:8
+    x += dpp0<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
+    x += dpp0<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
+    return x;
+}
 
 // ---------------------------------------------------------------------------
 // helper-wave pieces
@@ -232,6 +269,19 @@ __device__ __forceinline__ void put_frag(char* base, int R, int t, int lane, con
     *reinterpret_cast<bf16x8*>(base + frag_off(R, t, 1, lane)) = h[1];
 }
 
+__device__ __forceinline__ void put_f32(char* base, int s, int lane, const f32x4& lo4, const f32x4& hi4) {
+    bf16x8 h[2];
+    split_pair(lo4, hi4, h);
+    *reinterpret_cast<bf16x8*>(base + f32_off(s, 0, lane)) = h[0];
+    *reinterpret_cast<bf16x8*>(base + f32_off(s, 1, lane)) = h[1];
+}
+__device__ __forceinline__ void put_f16(char* base, int s, int lane, const f32x4& v) {
+    bf16x4 h[2];
+    split_d(v, h);
+    *reinterpret_cast<bf16x4*>(base + f16_off(s, 0, lane)) = h[0];
+    *reinterpret_cast<bf16x4*>(base + f16_off(s, 1, lane)) = h[1];
+}
+
 // ---------------------------------------------------------------------------
 // the kernel
 // ---------------------------------------------------------------------------
@@ -245,8 +295,21 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
     const int g = lane >> 4;
     const int ln = lane & 15;
     const int ntile = p.dv / DVT;
-    const long bh = blockIdx.x / ntile;
-    const int j0 = (blockIdx.x % ntile) * DVT;
+    // Workgroups are dealt round-robin to the 8 XCDs; when the head count allows,
+    // give all column tiles of a head the same XCD so they share its L2 for the
+    // key, query and gate reads.
+    const long nbh = gridDim.x / ntile;
+    long bh;
+    int tile;
+    if (nbh % 8 == 0) {
+        const long slot = blockIdx.x / 8;
+        tile = static_cast<int>(slot % ntile);
+        bh = (slot / ntile) * 8 + blockIdx.x % 8;
+    } else {
+        bh = blockIdx.x / ntile;
+        tile = static_cast<int>(blockIdx.x % ntile);
+    }
+    const int j0 = tile * DVT;
     const long nchunks = (p.T + CH - 1) / CH;
 
     if (wave < NCHAIN) {
@@ -300,54 +363,52 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
                 const f32x4 vv = *reinterpret_cast<const f32x4*>(sVt + 16 * a + 4 * g);
                 x[a] = vv - rs * y[a];
             }
-            bf16x8 bX[2][2];
-            split_pair(x[0], x[1], bX[0]);
-            split_pair(x[2], x[3], bX[1]);
-            // U = M X  (M lower triangular: block row R uses k-steps t <= R/2)
-            const char* mf = cur + B_MF;
+            // U by block forward substitution; the B operands of later steps are
+            // the hi/lo splits of the blocks already solved
+            const char* tf = cur + B_TF;
+            auto a16 = [&](int sl, bf16x4 (&o)[2]) {
+                o[0] = *reinterpret_cast<const bf16x4*>(tf + f16_off(sl, 0, lane));
+                o[1] = *reinterpret_cast<const bf16x4*>(tf + f16_off(sl, 1, lane));
+            };
+            auto a32 = [&](int sl, bf16x8 (&o)[2]) {
+                o[0] = *reinterpret_cast<const bf16x8*>(tf + f32_off(sl, 0, lane));
+                o[1] = *reinterpret_cast<const bf16x8*>(tf + f32_off(sl, 1, lane));
+            };
+            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
             f32x4 u[4];
-#pragma unroll
-            for (int R = 0; R < 4; ++R) {
-                u[R] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int t = 0; t <= R / 2; ++t) {
-                    bf16x8 am[2];
-                    am[0] = *reinterpret_cast<const bf16x8*>(mf + frag_off(R, t, 0, lane));
-                    am[1] = *reinterpret_cast<const bf16x8*>(mf + frag_off(R, t, 1, lane));
-                    u[R] = mm22(am, bX[t], u[R]);
-                }
-            }
+            bf16x4 bu[4][2], bw[2], a4[2];
+            bf16x8 a8[2];
+            split_d(x[0], bw);
+            a16(F16_D0 + 0, a4);
+            u[0] = mm22x16(a4, bw, zero);
+            split_d(u[0], bu[0]);
+            a16(F16_T10, a4);
+            f32x4 w = mm22x16(a4, bu[0], x[1]);
+            split_d(w, bw);
+            a16(F16_D0 + 1, a4);
+            u[1] = mm22x16(a4, bw, zero);
+            split_d(u[1], bu[1]);
             bf16x8 bU[2][2];
-            split_pair(u[0], u[1], bU[0]);
-            split_pair(u[2], u[3], bU[1]);
-            // O = diag(Gamma) Z + P U
-            const char* pf = cur + B_PF;
-            const bool full = t0 + CH <= p.T;
-#pragma unroll
-            for (int R = 0; R < 4; ++R) {
-                const f32x4 rq = *reinterpret_cast<const f32x4*>(sc + CH + 16 * R + 4 * g);
-                f32x4 oacc = rq * z[R];
-#pragma unroll
-                for (int t = 0; t <= R / 2; ++t) {
-                    bf16x8 ap[2];
-                    ap[0] = *reinterpret_cast<const bf16x8*>(pf + frag_off(R, t, 0, lane));
-                    ap[1] = *reinterpret_cast<const bf16x8*>(pf + frag_off(R, t, 1, lane));
-                    oacc = mm22(ap, bU[t], oacc);
-                }
-                const long row0 = (bh * p.T + t0 + 16 * R + 4 * g) * p.dv + col;
-                if (p.o_bf16) {
-                    uint16_t* op = static_cast<uint16_t*>(p.o) + row0;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (full || t0 + 16 * R + 4 * g + e < p.T) op[e * p.dv] = f32_to_bf16_bits(oacc[e]);
-                } else {
-                    float* op = static_cast<float*>(p.o) + row0;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (full || t0 + 16 * R + 4 * g + e < p.T) op[e * p.dv] = oacc[e];
-                }
-            }
-            // S <- Gamma_63 S + K^T diag(sb exp(G_63 - G)) U
+            bU[0][0] = cat4(bu[0][0], bu[1][0]);
+            bU[0][1] = cat4(bu[0][1], bu[1][1]);
+            a32(F32_T2, a8);
+            w = mm22(a8, bU[0], x[2]);
+            split_d(w, bw);
+            a16(F16_D0 + 2, a4);
+            u[2] = mm22x16(a4, bw, zero);
+            split_d(u[2], bu[2]);
+            a32(F32_T3, a8);
+            w = mm22(a8, bU[0], x[3]);
+            a16(F16_T32, a4);
+            w = mm22x16(a4, bu[2], w);
+            split_d(w, bw);
+            a16(F16_D0 + 3, a4);
+            u[3] = mm22x16(a4, bw, zero);
+            split_d(u[3], bu[3]);
+            bU[1][0] = cat4(bu[2][0], bu[3][0]);
+            bU[1][1] = cat4(bu[2][1], bu[3][1]);
+
+            // S <- Gamma_63 S + K^T diag(sb exp(G_63 - G)) U  (first: it feeds the next chunk)
             f32x4 us[4];
 #pragma unroll
             for (int R = 0; R < 4; ++R)
@@ -376,6 +437,49 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
                         bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                     sacc[ib] = mm12(ak, bUs[t], sacc[ib]);
                 }
+            }
+
+            // O = diag(Gamma) Z + P U, all four row blocks before any store
+            const char* pf = cur + B_PF;
+            f32x4 oacc[4];
+#pragma unroll
+            for (int R = 0; R < 4; ++R) {
+                const f32x4 rq = *reinterpret_cast<const f32x4*>(sc + CH + 16 * R + 4 * g);
+                oacc[R] = rq * z[R];
+#pragma unroll
+                for (int t = 0; t <= R / 2; ++t) {
+                    bf16x8 ap[2];
+                    ap[0] = *reinterpret_cast<const bf16x8*>(pf + frag_off(R, t, 0, lane));
+                    ap[1] = *reinterpret_cast<const bf16x8*>(pf + frag_off(R, t, 1, lane));
+                    oacc[R] = mm22(ap, bU[t], oacc[R]);
+                }
+            }
+            // lane (ln, g) holds rows 16R + 4g + e of column col
+            const long orow = bh * p.T + t0 + 4 * g;
+            if (t0 + CH <= p.T) {
+                if (p.o_bf16) {
+                    uint16_t* op = static_cast<uint16_t*>(p.o) + orow * p.dv + col;
+#pragma unroll
+                    for (int R = 0; R < 4; ++R)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) op[(16 * R + e) * p.dv] = f32_to_bf16_bits(oacc[R][e]);
+                } else {
+                    float* op = static_cast<float*>(p.o) + orow * p.dv + col;
+#pragma unroll
+                    for (int R = 0; R < 4; ++R)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) op[(16 * R + e) * p.dv] = oacc[R][e];
+                }
+            } else {
+#pragma unroll
+                for (int R = 0; R < 4; ++R)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        if (t0 + 4 * g + 16 * R + e >= p.T) continue;
+                        const long oi = (orow + 16 * R + e) * p.dv + col;
+                        if (p.o_bf16) static_cast<uint16_t*>(p.o)[oi] = f32_to_bf16_bits(oacc[R][e]);
+                        else static_cast<float*>(p.o)[oi] = oacc[R][e];
+                    }
             }
             __syncthreads();
         }
@@ -418,14 +522,10 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
         // per-token gates: inclusive cumulative log2 decay and sqrt(beta);
         // rows past T hold G and get sb = 0 (no erase, no write)
         const bool ok = t0 + lane < p.T;
-        float gl = (p.has_alpha && ok) ? fmaxf(H.la, kLogAlphaMin) * kLog2e : 0.0f;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const float o = __shfl_up(gl, d, 64);
-            if (lane >= d) gl += o;
-        }
-        const float sb = ok ? sqrtf(H.be) : 0.0f;
-        const float G2last = __shfl(gl, 63, 64);
+        const float gl = wave_incl_scan((p.has_alpha && ok) ? fmaxf(H.la, kLogAlphaMin) * kLog2e : 0.0f);
+        const float sb = ok ? sqrt_hw(H.be) : 0.0f;
+        const float G2last =
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gl), 63));
         ga[lane] = gl;
         ga[CH + lane] = sb;
         // gate values at rows 16R + ln and at columns 16J + 4g + e
@@ -438,9 +538,20 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
             Gs[R] = *reinterpret_cast<const f32x4*>(ga + 16 * R + 4 * g);
             sbs[R] = *reinterpret_cast<const f32x4*>(ga + CH + 16 * R + 4 * g);
         }
+        // Off-diagonal blocks (row block R > column block J) split the decay at
+        // the last row of block J: exp2(G_r - G_s) = exp2(G_r - Ge_J) exp2(Ge_J - G_s),
+        // both factors <= 1.  cJ[J] holds sb_s exp2(Ge_J - G_s) for this lane's columns.
+        float Ge[3];
+        f32x4 cJ[3];
+#pragma unroll
+        for (int J = 0; J < 3; ++J) {
+            Ge[J] = ga[16 * J + 15];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) cJ[J][e] = sbs[J][e] * ex2(Ge[J] - Gs[J][e]);
+        }
 
         if (w2) {
-            // ---- wave 2: form T, stage K, invert, write M fragments ----
+            // ---- wave 2: form T, stage K, invert the diagonal blocks ----
             // raw key Gram blocks first, so the key registers can be refilled
             f32x4 tr[4][4];
 #pragma unroll
@@ -464,80 +575,53 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
 #pragma unroll
                 for (int J = 0; J <= R; ++J) {
                     f32x4 acc = tr[R][J];
-                    const int r = 16 * R + ln;
+                    if (J == R) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int s = 16 * J + 4 * g + e;
-                        acc[e] = (s < r) ? acc[e] * sbr[R] * sbs[J][e] * exp2f(Gr[R] - Gs[J][e]) : 0.0f;
-                    }
-                    if (J == R)
+                        for (int e = 0; e < 4; ++e) {
+                            const int s = 4 * g + e;
+                            acc[e] = (s < ln) ? acc[e] * sbr[R] * sbs[R][e] * ex2(Gr[R] - Gs[R][e]) : 0.0f;
+                        }
                         *reinterpret_cast<f32x4*>(scr + R * SCR_STRIDE + ln * 20 + 4 * g) = acc;
-                    else
-                        tt[R][J] = acc;
+                    } else {
+                        const float rf = sbr[R] * ex2(Gr[R] - Ge[J]);
+                        tt[R][J] = acc * rf * cJ[J];
+                    }
                 }
-            // diagonal blocks: (I + T_RR)^-1 by forward substitution, lane = (R, column)
+            // diagonal blocks: D_R = (I + T_RR)^-1 by forward substitution, one
+            // column per lane (lane = (R, column cc)); column cc of a unit lower
+            // triangular inverse is zero above the diagonal, so every row can use
+            // x_r = [r == cc] - sum_{j<r} T_rj x_j without a lane condition.
+            // D_R overwrites T_RR in the scratch (row-major, row stride 20).
             {
                 float* B = scr + (lane >> 4) * SCR_STRIDE;
                 const int cc = lane & 15;
                 float xs[16];
-#pragma unroll
-                for (int r = 0; r < 16; ++r) xs[r] = (r == cc) ? 1.0f : 0.0f;
+                xs[0] = (cc == 0) ? 1.0f : 0.0f;
 #pragma unroll
                 for (int r = 1; r < 16; ++r) {
-                    float acc = 0.0f;
+                    float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
-                    for (int j = 0; j < r; ++j) acc = fmaf(B[r * 20 + j], xs[j], acc);
-                    if (r > cc) xs[r] = -acc;
+                    for (int j = 0; j < r; ++j) {
+                        if (j & 1) a1 = fmaf(B[r * 20 + j], xs[j], a1);
+                        else a0 = fmaf(B[r * 20 + j], xs[j], a0);
+                    }
+                    xs[r] = ((r == cc) ? 1.0f : 0.0f) - (a0 + a1);
                 }
 #pragma unroll
                 for (int r = 0; r < 16; ++r) B[r * 20 + cc] = xs[r];
             }
-            // dcol(S): D_S[4g+e][ln] (accumulator layout); drow(R): D_R[ln][4g+e]
-            auto dcol = [&](int S) {
-                f32x4 v;
+            // solve fragments: lane (ln, g) holds row ln, columns 4g .. 4g + 3 of each
+            // block, which is tt[R][J] (T_RJ^T in accumulator layout) for T and a
+            // row read of the scratch for D
+            char* tf = buf + B_TF;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = scr[S * SCR_STRIDE + (4 * g + e) * 20 + ln];
-                return v;
-            };
-            auto drow = [&](int R) {
-                return *reinterpret_cast<const f32x4*>(scr + R * SCR_STRIDE + ln * 20 + 4 * g);
-            };
-            // M_RS = -D_R sum_{J=S}^{R-1} T_RJ M_JS in accumulator layout (mo), and
-            // its transpose (mt) from the same operands with the roles swapped:
-            // a register block used as the A operand acts as its transpose.
-            f32x4 mo[4][4], mt[4][4];
-#pragma unroll
-            for (int d = 1; d < 4; ++d)
-#pragma unroll
-                for (int S = 0; S + d < 4; ++S) {
-                    const int R = S + d;
-                    f32x4 w = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int J = S; J < R; ++J) {
-                        bf16x4 a[2], b[2];
-                        split_d(tt[R][J], a);
-                        split_d(J == S ? dcol(S) : mo[J][S], b);
-                        w = mm22x16(a, b, w);
-                    }
-                    const f32x4 dr = drow(R);
-                    bf16x4 nd[2], bw[2];
-                    split_d(f32x4{-dr[0], -dr[1], -dr[2], -dr[3]}, nd);
-                    split_d(w, bw);
-                    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-                    mo[R][S] = mm22x16(nd, bw, zero);
-                    mt[R][S] = mm22x16(bw, nd, zero);
-                }
-            // M fragments: lane (ln, g) of fragment (R, t) holds M[16R + ln][32t + 4g + j]
-            // (j < 4) and M[16R + ln][32t + 16 + 4g + j - 4]: the transposed blocks
-            // (R, 2t) and (R, 2t + 1) in accumulator layout.
-            char* mf = buf + B_MF;
-            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-            put_frag(mf, 0, 0, lane, drow(0), zero);
-            put_frag(mf, 1, 0, lane, mt[1][0], drow(1));
-            put_frag(mf, 2, 0, lane, mt[2][0], mt[2][1]);
-            put_frag(mf, 2, 1, lane, drow(2), zero);
-            put_frag(mf, 3, 0, lane, mt[3][0], mt[3][1]);
-            put_frag(mf, 3, 1, lane, mt[3][2], drow(3));
+            for (int R = 0; R < 4; ++R)
+                put_f16(tf, F16_D0 + R, lane,
+                        *reinterpret_cast<const f32x4*>(scr + R * SCR_STRIDE + ln * 20 + 4 * g));
+            put_f16(tf, F16_T10, lane, -tt[1][0]);
+            put_f16(tf, F16_T32, lane, -tt[3][2]);
+            put_f32(tf, F32_T2, lane, -tt[2][0], -tt[2][1]);
+            put_f32(tf, F32_T3, lane, -tt[3][0], -tt[3][1]);
         } else {
             // ---- wave 3: form P, stage Q, V (transposed), row scales ----
             mask_rows(H.q, p.T, t0, ln);
@@ -555,28 +639,30 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
                 }
             stage_rows(H.q, reinterpret_cast<uint16_t*>(buf + B_Q), ln, g);
             float* sc = reinterpret_cast<float*>(buf + B_SC);
-            sc[lane] = sb * exp2f(gl);                    // rows of K.Gamma
-            sc[CH + lane] = exp2f(gl);                    // rows of Q.Gamma
-            sc[2 * CH + lane] = sb * exp2f(G2last - gl);  // rows of Khat
-            if (lane == 0) sc[3 * CH] = exp2f(G2last);    // chunk decay
+            const float eg = ex2(gl);
+            sc[lane] = sb * eg;                         // rows of K.Gamma
+            sc[CH + lane] = eg;                         // rows of Q.Gamma
+            sc[2 * CH + lane] = sb * ex2(G2last - gl);  // rows of Khat
+            if (lane == 0) sc[3 * CH] = ex2(G2last);    // chunk decay
             float* sVt = reinterpret_cast<float*>(buf + B_VT);
+            const bool okr = t0 + lane < p.T;
+            if (!p.gvec) {
+                const float sg = okr ? sqrt_hw(H.gam1) : 0.0f;
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int row = lane, c0 = 8 * m;
-                const bool okr = t0 + row < p.T;
-                const uint16_t* ve = reinterpret_cast<const uint16_t*>(&H.v[m]);
-                float gam[8];
-                if (p.gvec) {
-                    const long tk = bh * p.T + min(t0 + row, p.T - 1);
+                for (int m = 0; m < 4; ++m) {
+                    const uint16_t* ve = reinterpret_cast<const uint16_t*>(&H.v[m]);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) gam[e] = p.gsrc[tk * p.gts + j0 + c0 + e];
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) gam[e] = H.gam1;
+                    for (int e = 0; e < 8; ++e) sVt[(8 * m + e) * VTS + lane] = sg * bf16_bits_to_f32(ve[e]);
                 }
+            } else {
+                const float* gr = p.gsrc + (bh * p.T + min(t0 + lane, p.T - 1)) * p.gts + j0;
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    sVt[(c0 + e) * VTS + row] = okr ? sqrtf(gam[e]) * bf16_bits_to_f32(ve[e]) : 0.0f;
+                for (int m = 0; m < 4; ++m) {
+                    const uint16_t* ve = reinterpret_cast<const uint16_t*>(&H.v[m]);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        sVt[(8 * m + e) * VTS + lane] = okr ? sqrt_hw(gr[8 * m + e]) * bf16_bits_to_f32(ve[e]) : 0.0f;
+                }
             }
             if (c + 1 < nchunks) load(c + 1, H);
             // P^T blocks: pb[R][S] holds P[16R + ln][16S + 4g + e]
@@ -584,11 +670,14 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
             for (int R = 0; R < 4; ++R)
 #pragma unroll
                 for (int S = 0; S <= R; ++S) {
-                    const int r = 16 * R + ln;
+                    if (S == R) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int s = 16 * S + 4 * g + e;
-                        pb[R][S][e] = (s <= r) ? pb[R][S][e] * sbs[S][e] * exp2f(Gr[R] - Gs[S][e]) : 0.0f;
+                        for (int e = 0; e < 4; ++e) {
+                            const int s = 4 * g + e;
+                            pb[R][S][e] = (s <= ln) ? pb[R][S][e] * sbs[S][e] * ex2(Gr[R] - Gs[S][e]) : 0.0f;
+                        }
+                    } else {
+                        pb[R][S] = pb[R][S] * ex2(Gr[R] - Ge[S]) * cJ[S];
                     }
                 }
             char* pf = buf + B_PF;
