@@ -142,11 +142,6 @@ __device__ __forceinline__ f32x4 mfma32(const bf16x8& a, const bf16x8& b, f32x4 
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// acc += a (1 term) * b (hi, lo)
-__device__ __forceinline__ f32x4 mm12(const bf16x8& a, const bf16x8 (&b)[2], f32x4 c) {
-    c = mfma32(a, b[1], c);
-    return mfma32(a, b[0], c);
-}
 // acc += (hi, lo) * (hi, lo), dropping lo*lo
 __device__ __forceinline__ f32x4 mm22(const bf16x8 (&a)[2], const bf16x8 (&b)[2], f32x4 c) {
     c = mfma32(a[1], b[0], c);
@@ -339,22 +334,27 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
             bf16x8 bS[4][2];
 #pragma unroll
             for (int t = 0; t < 4; ++t) split_pair(sacc[2 * t], sacc[2 * t + 1], bS[t]);
-            // Y = K S, Z = Q S (raw bf16 rows as A operands)
+            // Y = K S and Z = Q S with raw bf16 rows as A operands.  The four row
+            // blocks are independent accumulation chains; each k-step issues one
+            // MFMA per block so consecutive MFMAs never wait on each other.
             f32x4 y[4], z[4];
+            auto rows_x_state = [&](const uint16_t* tile, int t, f32x4 (&acc)[4]) {
+                bf16x8 a[4];
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    a[b] = *reinterpret_cast<const bf16x8*>(tile + kq_off(16 * b + ln, 32 * t + 8 * g));
+#pragma unroll
+                for (int b = 0; b < 4; ++b) acc[b] = mfma32(a[b], bS[t][1], acc[b]);
+#pragma unroll
+                for (int b = 0; b < 4; ++b) acc[b] = mfma32(a[b], bS[t][0], acc[b]);
+            };
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
                 y[a] = f32x4{0.f, 0.f, 0.f, 0.f};
                 z[a] = f32x4{0.f, 0.f, 0.f, 0.f};
-                const int r = 16 * a + ln;
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const int pc = 32 * t + 8 * g;
-                    const bf16x8 ak = *reinterpret_cast<const bf16x8*>(sK + kq_off(r, pc));
-                    const bf16x8 aq = *reinterpret_cast<const bf16x8*>(sQ + kq_off(r, pc));
-                    y[a] = mm12(ak, bS[t], y[a]);
-                    z[a] = mm12(aq, bS[t], z[a]);
-                }
             }
+#pragma unroll
+            for (int t = 0; t < 4; ++t) rows_x_state(sK, t, y);
             // X = Vt - diag(sb Gamma) Y
             f32x4 x[4];
 #pragma unroll
@@ -381,12 +381,16 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
             split_d(x[0], bw);
             a16(F16_D0 + 0, a4);
             u[0] = mm22x16(a4, bw, zero);
+            // Z = Q S does not depend on the solve: its k-steps fill the gaps
+            // between the dependent solve steps
+            rows_x_state(sQ, 0, z);
             split_d(u[0], bu[0]);
             a16(F16_T10, a4);
             f32x4 w = mm22x16(a4, bu[0], x[1]);
             split_d(w, bw);
             a16(F16_D0 + 1, a4);
             u[1] = mm22x16(a4, bw, zero);
+            rows_x_state(sQ, 1, z);
             split_d(u[1], bu[1]);
             bf16x8 bU[2][2];
             bU[0][0] = cat4(bu[0][0], bu[1][0]);
@@ -396,6 +400,7 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
             split_d(w, bw);
             a16(F16_D0 + 2, a4);
             u[2] = mm22x16(a4, bw, zero);
+            rows_x_state(sQ, 2, z);
             split_d(u[2], bu[2]);
             a32(F32_T3, a8);
             w = mm22(a8, bU[0], x[3]);
@@ -404,6 +409,7 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
             split_d(w, bw);
             a16(F16_D0 + 3, a4);
             u[3] = mm22x16(a4, bw, zero);
+            rows_x_state(sQ, 3, z);
             split_d(u[3], bu[3]);
             bU[1][0] = cat4(bu[2][0], bu[3][0]);
             bU[1][1] = cat4(bu[2][1], bu[3][1]);
@@ -418,14 +424,16 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
             split_pair(us[2], us[3], bUs[1]);
             const float gC = sc[3 * CH];
 #pragma unroll
-            for (int ib = 0; ib < 8; ++ib) {
-                sacc[ib] *= gC;
+            for (int ib = 0; ib < 8; ++ib) sacc[ib] *= gC;
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    // A operand: K^T rows 16ib..16ib+15 (channels), k-slots = tokens
-                    // {32t + 4g + 0..3, 32t + 16 + 4g + 0..3}, via transpose reads.
+            for (int t = 0; t < 2; ++t) {
+                // A operand: K^T rows 16ib..16ib+15 (channels), k-slots = tokens
+                // {32t + 4g + 0..3, 32t + 16 + 4g + 0..3}, via transpose reads.
+                bf16x8 ak[8];
+                const int tokA = 32 * t + 4 * g + (ln >> 2);
+#pragma unroll
+                for (int ib = 0; ib < 8; ++ib) {
                     const int pcol = kperm(16 * ib + 4 * (ln & 3));
-                    const int tokA = 32 * t + 4 * g + (ln >> 2);
                     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                         (lds_s16x4*)(sK + kq_off(tokA, pcol)));
                     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -433,26 +441,34 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
                     // whole-vector reinterpretation (an element-wise short -> bf16
                     // bit_cast loop is mis-lowered by this compiler: it replicates
                     // element 0)
-                    const bf16x8 ak = __builtin_bit_cast(
-                        bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                    sacc[ib] = mm12(ak, bUs[t], sacc[ib]);
+                    ak[ib] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                 }
+#pragma unroll
+                for (int ib = 0; ib < 8; ++ib) sacc[ib] = mfma32(ak[ib], bUs[t][1], sacc[ib]);
+#pragma unroll
+                for (int ib = 0; ib < 8; ++ib) sacc[ib] = mfma32(ak[ib], bUs[t][0], sacc[ib]);
             }
 
             // O = diag(Gamma) Z + P U, all four row blocks before any store
             const char* pf = cur + B_PF;
             f32x4 oacc[4];
 #pragma unroll
-            for (int R = 0; R < 4; ++R) {
-                const f32x4 rq = *reinterpret_cast<const f32x4*>(sc + CH + 16 * R + 4 * g);
-                oacc[R] = rq * z[R];
+            for (int R = 0; R < 4; ++R)
+                oacc[R] = *reinterpret_cast<const f32x4*>(sc + CH + 16 * R + 4 * g) * z[R];
 #pragma unroll
-                for (int t = 0; t <= R / 2; ++t) {
-                    bf16x8 ap[2];
-                    ap[0] = *reinterpret_cast<const bf16x8*>(pf + frag_off(R, t, 0, lane));
-                    ap[1] = *reinterpret_cast<const bf16x8*>(pf + frag_off(R, t, 1, lane));
-                    oacc[R] = mm22(ap, bU[t], oacc[R]);
+            for (int t = 0; t < 2; ++t) {
+                bf16x8 ap[4][2];
+#pragma unroll
+                for (int R = 2 * t; R < 4; ++R) {
+                    ap[R][0] = *reinterpret_cast<const bf16x8*>(pf + frag_off(R, t, 0, lane));
+                    ap[R][1] = *reinterpret_cast<const bf16x8*>(pf + frag_off(R, t, 1, lane));
                 }
+#pragma unroll
+                for (int R = 2 * t; R < 4; ++R) oacc[R] = mfma32(ap[R][1], bU[t][0], oacc[R]);
+#pragma unroll
+                for (int R = 2 * t; R < 4; ++R) oacc[R] = mfma32(ap[R][0], bU[t][1], oacc[R]);
+#pragma unroll
+                for (int R = 2 * t; R < 4; ++R) oacc[R] = mfma32(ap[R][0], bU[t][0], oacc[R]);
             }
             // lane (ln, g) holds rows 16R + 4g + e of column col
             const long orow = bh * p.T + t0 + 4 * g;
