@@ -264,6 +264,22 @@ __device__ __forceinline__ void put_frag(char* base, int R, int t, int lane, con
     *reinterpret_cast<bf16x8*>(base + frag_off(R, t, 1, lane)) = h[1];
 }
 
+// Broadcast of lane J of each 16-lane row to the whole row (DPP row_newbcast).
+template <int J>
+__device__ __forceinline__ float row_bcast(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + J, 0xf, 0xf, true));
+}
+// Steps J .. 14 of the per-row block solve (see the diagonal-block inverse).
+template <int J>
+__device__ __forceinline__ void block_row_solve(float (&x)[16], const float (&ntr)[16]) {
+    if constexpr (J < 15) {
+#pragma unroll
+        for (int c = 0; c <= J; ++c) x[c] = fmaf(row_bcast<J>(x[c]), ntr[J], x[c]);
+        block_row_solve<J + 1>(x, ntr);
+    }
+}
+__device__ __forceinline__ void block_row_solve(float (&x)[16], const float (&ntr)[16]) { block_row_solve<0>(x, ntr); }
+
 __device__ __forceinline__ void put_f32(char* base, int s, int lane, const f32x4& lo4, const f32x4& hi4) {
     bf16x8 h[2];
     split_pair(lo4, hi4, h);
@@ -603,28 +619,28 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
                         tt[R][J] = acc * rf * cJ[J];
                     }
                 }
-            // diagonal blocks: D_R = (I + T_RR)^-1 by forward substitution, one
-            // column per lane (lane = (R, column cc)); column cc of a unit lower
-            // triangular inverse is zero above the diagonal, so every row can use
-            // x_r = [r == cc] - sum_{j<r} T_rj x_j without a lane condition.
+            // diagonal blocks: D_R = (I + T_RR)^-1 row by row, one row per lane
+            // (lane = (R, row r); a DPP row of 16 lanes is one block).  Once row j
+            // is final it is broadcast across its block and every row r takes
+            // x_r -= T_rj x_j; rows r <= j have T_rj = 0 and stay unchanged, and
+            // x_j is zero beyond column j, so step j touches columns 0..j only.
             // D_R overwrites T_RR in the scratch (row-major, row stride 20).
             {
-                float* B = scr + (lane >> 4) * SCR_STRIDE;
-                const int cc = lane & 15;
-                float xs[16];
-                xs[0] = (cc == 0) ? 1.0f : 0.0f;
+                float* Brow = scr + (lane >> 4) * SCR_STRIDE + (lane & 15) * 20;
+                float ntr[16];
 #pragma unroll
-                for (int r = 1; r < 16; ++r) {
-                    float a0 = 0.0f, a1 = 0.0f;
+                for (int q = 0; q < 4; ++q) {
+                    const f32x4 v = *reinterpret_cast<const f32x4*>(Brow + 4 * q);
 #pragma unroll
-                    for (int j = 0; j < r; ++j) {
-                        if (j & 1) a1 = fmaf(B[r * 20 + j], xs[j], a1);
-                        else a0 = fmaf(B[r * 20 + j], xs[j], a0);
-                    }
-                    xs[r] = ((r == cc) ? 1.0f : 0.0f) - (a0 + a1);
+                    for (int e = 0; e < 4; ++e) ntr[4 * q + e] = -v[e];
                 }
+                float x[16];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) B[r * 20 + cc] = xs[r];
+                for (int cc = 0; cc < 16; ++cc) x[cc] = (cc == (lane & 15)) ? 1.0f : 0.0f;
+                block_row_solve(x, ntr);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    *reinterpret_cast<f32x4*>(Brow + 4 * q) = f32x4{x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]};
             }
             // solve fragments: lane (ln, g) holds row ln, columns 4g .. 4g + 3 of each
             // block, which is tt[R][J] (T_RJ^T in accumulator layout) for T and a
