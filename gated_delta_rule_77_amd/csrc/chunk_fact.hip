@@ -354,15 +354,24 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
             // blocks are independent accumulation chains; each k-step issues one
             // MFMA per block so consecutive MFMAs never wait on each other.
             f32x4 y[4], z[4];
-            auto rows_x_state = [&](const uint16_t* tile, int t, f32x4 (&acc)[4]) {
+            auto rows_x_state = [&](const uint16_t* tile, bool transposed, int t, f32x4 (&acc)[4]) {
                 bf16x8 a[4];
 #pragma unroll
                 for (int b = 0; b < 4; ++b)
                     a[b] = *reinterpret_cast<const bf16x8*>(tile + kq_off(16 * b + ln, 32 * t + 8 * g));
+                if (!transposed) {
 #pragma unroll
-                for (int b = 0; b < 4; ++b) acc[b] = mfma32(a[b], bS[t][1], acc[b]);
+                    for (int b = 0; b < 4; ++b) acc[b] = mfma32(a[b], bS[t][1], acc[b]);
 #pragma unroll
-                for (int b = 0; b < 4; ++b) acc[b] = mfma32(a[b], bS[t][0], acc[b]);
+                    for (int b = 0; b < 4; ++b) acc[b] = mfma32(a[b], bS[t][0], acc[b]);
+                } else {
+                    // operands swapped: the result is the transposed block, lane (ln, g)
+                    // holding row 16b + ln, value columns 4g .. 4g + 3
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) acc[b] = mfma32(bS[t][1], a[b], acc[b]);
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) acc[b] = mfma32(bS[t][0], a[b], acc[b]);
+                }
             };
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
@@ -370,7 +379,7 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
                 z[a] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
 #pragma unroll
-            for (int t = 0; t < 4; ++t) rows_x_state(sK, t, y);
+            for (int t = 0; t < 4; ++t) rows_x_state(sK, false, t, y);
             // X = Vt - diag(sb Gamma) Y
             f32x4 x[4];
 #pragma unroll
@@ -399,14 +408,14 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
             u[0] = mm22x16(a4, bw, zero);
             // Z = Q S does not depend on the solve: its k-steps fill the gaps
             // between the dependent solve steps
-            rows_x_state(sQ, 0, z);
+            rows_x_state(sQ, true, 0, z);
             split_d(u[0], bu[0]);
             a16(F16_T10, a4);
             f32x4 w = mm22x16(a4, bu[0], x[1]);
             split_d(w, bw);
             a16(F16_D0 + 1, a4);
             u[1] = mm22x16(a4, bw, zero);
-            rows_x_state(sQ, 1, z);
+            rows_x_state(sQ, true, 1, z);
             split_d(u[1], bu[1]);
             bf16x8 bU[2][2];
             bU[0][0] = cat4(bu[0][0], bu[1][0]);
@@ -416,7 +425,7 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
             split_d(w, bw);
             a16(F16_D0 + 2, a4);
             u[2] = mm22x16(a4, bw, zero);
-            rows_x_state(sQ, 2, z);
+            rows_x_state(sQ, true, 2, z);
             split_d(u[2], bu[2]);
             a32(F32_T3, a8);
             w = mm22(a8, bU[0], x[3]);
@@ -425,7 +434,7 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
             split_d(w, bw);
             a16(F16_D0 + 3, a4);
             u[3] = mm22x16(a4, bw, zero);
-            rows_x_state(sQ, 3, z);
+            rows_x_state(sQ, true, 3, z);
             split_d(u[3], bu[3]);
             bU[1][0] = cat4(bu[2][0], bu[3][0]);
             bU[1][1] = cat4(bu[2][1], bu[3][1]);
@@ -465,12 +474,14 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
                 for (int ib = 0; ib < 8; ++ib) sacc[ib] = mfma32(ak[ib], bUs[t][0], sacc[ib]);
             }
 
-            // O = diag(Gamma) Z + P U, all four row blocks before any store
+            // O = diag(Gamma) Z + P U, transposed: with U as the A operand and the P
+            // fragments as the B operand, lane (ln, g) ends up with row 16R + ln,
+            // value columns 4g .. 4g + 3 (the layout z already has), so each row
+            // block leaves in one 16-byte store per lane
             const char* pf = cur + B_PF;
             f32x4 oacc[4];
 #pragma unroll
-            for (int R = 0; R < 4; ++R)
-                oacc[R] = *reinterpret_cast<const f32x4*>(sc + CH + 16 * R + 4 * g) * z[R];
+            for (int R = 0; R < 4; ++R) oacc[R] = sc[CH + 16 * R + ln] * z[R];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 bf16x8 ap[4][2];
@@ -480,38 +491,28 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
                     ap[R][1] = *reinterpret_cast<const bf16x8*>(pf + frag_off(R, t, 1, lane));
                 }
 #pragma unroll
-                for (int R = 2 * t; R < 4; ++R) oacc[R] = mfma32(ap[R][1], bU[t][0], oacc[R]);
+                for (int R = 2 * t; R < 4; ++R) oacc[R] = mfma32(bU[t][0], ap[R][1], oacc[R]);
 #pragma unroll
-                for (int R = 2 * t; R < 4; ++R) oacc[R] = mfma32(ap[R][0], bU[t][1], oacc[R]);
+                for (int R = 2 * t; R < 4; ++R) oacc[R] = mfma32(bU[t][1], ap[R][0], oacc[R]);
 #pragma unroll
-                for (int R = 2 * t; R < 4; ++R) oacc[R] = mfma32(ap[R][0], bU[t][0], oacc[R]);
+                for (int R = 2 * t; R < 4; ++R) oacc[R] = mfma32(bU[t][0], ap[R][0], oacc[R]);
             }
-            // lane (ln, g) holds rows 16R + 4g + e of column col
-            const long orow = bh * p.T + t0 + 4 * g;
-            if (t0 + CH <= p.T) {
-                if (p.o_bf16) {
-                    uint16_t* op = static_cast<uint16_t*>(p.o) + orow * p.dv + col;
+            {
+                const int c4 = j0 + 16 * wave + 4 * g;
 #pragma unroll
-                    for (int R = 0; R < 4; ++R)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) op[(16 * R + e) * p.dv] = f32_to_bf16_bits(oacc[R][e]);
-                } else {
-                    float* op = static_cast<float*>(p.o) + orow * p.dv + col;
-#pragma unroll
-                    for (int R = 0; R < 4; ++R)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) op[(16 * R + e) * p.dv] = oacc[R][e];
-                }
-            } else {
-#pragma unroll
-                for (int R = 0; R < 4; ++R)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        if (t0 + 4 * g + 16 * R + e >= p.T) continue;
-                        const long oi = (orow + 16 * R + e) * p.dv + col;
-                        if (p.o_bf16) static_cast<uint16_t*>(p.o)[oi] = f32_to_bf16_bits(oacc[R][e]);
-                        else static_cast<float*>(p.o)[oi] = oacc[R][e];
+                for (int R = 0; R < 4; ++R) {
+                    const long tok = t0 + 16 * R + ln;
+                    if (tok >= p.T) continue;
+                    const long oi = (bh * p.T + tok) * p.dv + c4;
+                    if (p.o_bf16) {
+                        uint2 pk;
+                        pk.x = f32_to_bf16_bits(oacc[R][0]) | (static_cast<uint32_t>(f32_to_bf16_bits(oacc[R][1])) << 16);
+                        pk.y = f32_to_bf16_bits(oacc[R][2]) | (static_cast<uint32_t>(f32_to_bf16_bits(oacc[R][3])) << 16);
+                        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.o) + oi) = pk;
+                    } else {
+                        *reinterpret_cast<f32x4*>(static_cast<float*>(p.o) + oi) = oacc[R];
                     }
+                }
             }
             __syncthreads();
         }
