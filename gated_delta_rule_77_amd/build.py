@@ -26,6 +26,11 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-I" + INCLUDE, "-I" + CSRC,
           "-Wno-unused-command-line-argument"]
 
 
+# Per-source extra flags.  The scalar-gate prefill keeps its MFMA accumulators
+# in ordinary VGPRs (no accumulator-register copies around every VALU use).
+EXTRA = {"chunk_fact.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _hipcc() -> str:
     p = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(p):
@@ -43,7 +48,7 @@ def sources():
 
 def _compile(src: str, hipcc: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc, *COMMON, "-c", src, "-o", obj]
+    cmd = [hipcc, *COMMON, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd = [hipcc, *COMMON, "-x", "hip", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
