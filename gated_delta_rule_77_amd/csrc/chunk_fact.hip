@@ -65,8 +65,8 @@ constexpr int B_SC = B_VT + DVT * VTS * 4;
 constexpr int BUF = B_SC + 4 * CH * 4;  // rsKS[64], rq[64], rk[64], gC
 constexpr int SCR = 2 * BUF;            // wave 2: four diagonal 16x16 blocks
 constexpr int SCR_STRIDE = 16 * 20 + 16;
-constexpr int GA = SCR + 4 * SCR_STRIDE * 4;  // per helper: G2[64], sb[64]
-constexpr int LDS_BYTES = GA + 2 * 2 * CH * 4;
+constexpr int GA = SCR + 4 * SCR_STRIDE * 4;  // wave 2: G2[64], sb[64]; wave 3: + sg[64]
+constexpr int LDS_BYTES = GA + 5 * CH * 4;
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 static_assert(B_PF % 16 == 0 && B_VT % 16 == 0 && BUF % 16 == 0, "LDS alignment");
 
@@ -95,15 +95,14 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 // layouts
 // ---------------------------------------------------------------------------
 
-// k-permutation inside each 32-column group (see chunk_fwd.hip): one 16-byte
-// read yields the k-slots {4g..4g+3, 16+4g..16+4g+3}.
-__device__ __forceinline__ int kperm(int k) {
-    const int q = k >> 2;
-    const int pq = (q & ~7) | ((q & 3) << 1) | ((q >> 2) & 1);
-    return (pq << 2) | (k & 3);
-}
+// State rows.  The chain keeps S in 8 accumulator blocks; lane (ln, g) holds
+// element e of block ib as state row (key channel) srow(ib, g, e) and value
+// column ln of its 16.  Pairing blocks 2t and 2t + 1 as one 16x16x32 B operand
+// then gives lane g the contiguous channels 32t + 8g .. 32t + 8g + 7, the same
+// channels a 16-byte read of a key or query row hands to the A operand.
+__device__ __forceinline__ int srow(int ib, int g, int e) { return 32 * (ib >> 1) + 8 * g + 4 * (ib & 1) + e; }
 
-// K/Q tiles: element (token r, physical column pc) of a [64][128] bf16 tile.
+// K/Q tiles: element (token r, channel pc) of a [64][128] bf16 tile.
 // 16-byte chunks are XORed with f(r) = 4 (r % 4) + (r / 4) % 4, which makes
 // both the 16-row MFMA operand reads and the 4x4 transpose reads hit 16
 // distinct 16-byte bank groups.
@@ -217,7 +216,7 @@ struct RowOps {
 // One chunk's raw inputs as loaded by a helper wave.
 struct HelperRegs {
     RowOps k, q;    // q: wave 3 only
-    uint4 v[4];     // wave 3: this lane's token, value columns 8m .. 8m + 7
+    uint4 v[4];     // wave 3: tokens 4q + i (q = lane % 16), value columns 8m .. 8m + 7 (m = lane / 16)
     float gam1;     // wave 3: this lane's scalar value gain
     float la, be;   // this lane's token
 };
@@ -241,18 +240,13 @@ __device__ __forceinline__ void mask_rows(RowOps& ops, long T, long t0, int ln) 
             for (int tt = 0; tt < 4; ++tt) ops.d[R][tt] = uint4{0u, 0u, 0u, 0u};
 }
 
-// Stage operand rows into a swizzled, k-permuted LDS tile.
+// Stage operand rows into a swizzled LDS tile (one 16-byte chunk per row and k-step).
 __device__ __forceinline__ void stage_rows(const RowOps& ops, uint16_t* tile, int ln, int g) {
 #pragma unroll
     for (int R = 0; R < 4; ++R)
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            const int r = 16 * R + ln;
-            const int c0 = 32 * tt + 8 * g;  // logical channels c0..c0+7 = two 4-groups
-            const uint4 d = ops.d[R][tt];
-            *reinterpret_cast<uint2*>(tile + kq_off(r, kperm(c0))) = uint2{d.x, d.y};
-            *reinterpret_cast<uint2*>(tile + kq_off(r, kperm(c0 + 4))) = uint2{d.z, d.w};
-        }
+        for (int tt = 0; tt < 4; ++tt)
+            *reinterpret_cast<uint4*>(tile + kq_off(16 * R + ln, 32 * tt + 8 * g)) = ops.d[R][tt];
 }
 
 // Write one operand fragment (8 values of this lane) as hi/lo bf16 terms.
@@ -332,7 +326,7 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
             for (int ib = 0; ib < 8; ++ib)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    sacc[ib][e] = p.S0[(bh * DK + 16 * ib + 4 * g + e) * p.dv + col];
+                    sacc[ib][e] = p.S0[(bh * DK + srow(ib, g, e)) * p.dv + col];
         } else {
 #pragma unroll
             for (int ib = 0; ib < 8; ++ib) sacc[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -452,13 +446,15 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
             for (int ib = 0; ib < 8; ++ib) sacc[ib] *= gC;
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                // A operand: K^T rows 16ib..16ib+15 (channels), k-slots = tokens
-                // {32t + 4g + 0..3, 32t + 16 + 4g + 0..3}, via transpose reads.
+                // A operand: K^T rows srow(ib, .) (channels), k-slots = tokens
+                // {32t + 4g + 0..3, 32t + 16 + 4g + 0..3}, via transpose reads: lane
+                // ln of each 16 points at token 32t + 4g + ln / 4 and the 4 channels
+                // 32 (ib / 2) + 4 (ib % 2) + 8 (ln % 4) .. + 3.
                 bf16x8 ak[8];
                 const int tokA = 32 * t + 4 * g + (ln >> 2);
 #pragma unroll
                 for (int ib = 0; ib < 8; ++ib) {
-                    const int pcol = kperm(16 * ib + 4 * (ln & 3));
+                    const int pcol = 32 * (ib >> 1) + 4 * (ib & 1) + 8 * (ln & 3);
                     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                         (lds_s16x4*)(sK + kq_off(tokA, pcol)));
                     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -521,7 +517,7 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
             for (int ib = 0; ib < 8; ++ib)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    p.ST[(bh * DK + 16 * ib + 4 * g + e) * p.dv + col] = sacc[ib][e];
+                    p.ST[(bh * DK + srow(ib, g, e)) * p.dv + col] = sacc[ib][e];
         }
         return;
     }
@@ -539,10 +535,9 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
         if (!w2) {
             load_rows(H.q, p.q, bh, p.T, t0, ln, g);
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {  // this lane's token, columns 8m .. 8m + 7
-                const int row = lane, c0 = 8 * m;
-                const long tk = bh * p.T + min(t0 + row, p.T - 1);
-                H.v[m] = *reinterpret_cast<const uint4*>(p.v + tk * p.dv + j0 + c0);
+            for (int i = 0; i < 4; ++i) {
+                const long tk = bh * p.T + min(t0 + 4 * ln + i, p.T - 1);
+                H.v[i] = *reinterpret_cast<const uint4*>(p.v + tk * p.dv + j0 + 8 * g);
             }
             if (!p.gvec) H.gam1 = p.gsrc[tok * p.gts];
         }
@@ -677,25 +672,32 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
             sc[CH + lane] = eg;                         // rows of Q.Gamma
             sc[2 * CH + lane] = sb * ex2(G2last - gl);  // rows of Khat
             if (lane == 0) sc[3 * CH] = ex2(G2last);    // chunk decay
+            // value tile, transposed and scaled by sqrt(gamma): lane (q = ln, m = g)
+            // holds tokens 4q .. 4q + 3 of columns 8m .. 8m + 7, one 16-byte write
+            // per column; rows past T get 0
             float* sVt = reinterpret_cast<float*>(buf + B_VT);
-            const bool okr = t0 + lane < p.T;
+            f32x4 sg4[8];
             if (!p.gvec) {
-                const float sg = okr ? sqrt_hw(H.gam1) : 0.0f;
+                ga[2 * CH + lane] = ok ? sqrt_hw(H.gam1) : 0.0f;
+                const f32x4 s4 = *reinterpret_cast<const f32x4*>(ga + 2 * CH + 4 * ln);
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const uint16_t* ve = reinterpret_cast<const uint16_t*>(&H.v[m]);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) sVt[(8 * m + e) * VTS + lane] = sg * bf16_bits_to_f32(ve[e]);
-                }
+                for (int cc = 0; cc < 8; ++cc) sg4[cc] = s4;
             } else {
-                const float* gr = p.gsrc + (bh * p.T + min(t0 + lane, p.T - 1)) * p.gts + j0;
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const uint16_t* ve = reinterpret_cast<const uint16_t*>(&H.v[m]);
+                for (int i = 0; i < 4; ++i) {
+                    const long tok = t0 + 4 * ln + i;
+                    const float* gr = p.gsrc + (bh * p.T + min(tok, p.T - 1)) * p.gts + j0 + 8 * g;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        sVt[(8 * m + e) * VTS + lane] = okr ? sqrt_hw(gr[8 * m + e]) * bf16_bits_to_f32(ve[e]) : 0.0f;
+                    for (int cc = 0; cc < 8; ++cc) sg4[cc][i] = tok < p.T ? sqrt_hw(gr[cc]) : 0.0f;
                 }
+            }
+#pragma unroll
+            for (int cc = 0; cc < 8; ++cc) {
+                f32x4 col4;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    col4[i] = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(&H.v[i])[cc]);
+                *reinterpret_cast<f32x4*>(sVt + (8 * g + cc) * VTS + 4 * ln) = sg4[cc] * col4;
             }
             if (c + 1 < nchunks) load(c + 1, H);
             // P^T blocks: pb[R][S] holds P[16R + ln][16S + 4g + e]
