@@ -54,16 +54,20 @@ constexpr int TF_BYTES = TF16 + 6 * 2 * 64 * 8;
 enum { F32_T2 = 0, F32_T3 = 1 };
 enum { F16_D0 = 0, F16_T10 = 4, F16_T32 = 5 };
 
-// LDS layout (bytes).  Per buffer: K, Q (bf16 [64][128], swizzled), solve and
-// P fragments, the value tile transposed (fp32 [32][VTS]), per-row scales.
-constexpr int B_K = 0;
-constexpr int B_Q = B_K + CH * DK * 2;
+// LDS layout (bytes).  Three key tiles (bf16 [64][128], swizzled; chunk c in
+// slot c % 3: the chain reads chunk c while the helpers read chunk c + 1 and
+// wave 2 stages chunk c + 2), then two per-parity buffers holding the query
+// tile, solve and P fragments, the value tile transposed (fp32 [32][VTS]) and
+// the per-row scales.
+constexpr int KTILE = CH * DK * 2;
+constexpr int B_Q = 0;
 constexpr int B_TF = B_Q + CH * DK * 2;
 constexpr int B_PF = B_TF + TF_BYTES;
 constexpr int B_VT = B_PF + NFRAG * 2 * 64 * 16;
 constexpr int B_SC = B_VT + DVT * VTS * 4;
 constexpr int BUF = B_SC + 4 * CH * 4;  // rsKS[64], rq[64], rk[64], gC
-constexpr int SCR = 2 * BUF;            // wave 2: four diagonal 16x16 blocks
+constexpr int PBUF = 3 * KTILE;         // first per-parity buffer
+constexpr int SCR = PBUF + 2 * BUF;     // wave 2: four diagonal 16x16 blocks
 constexpr int SCR_STRIDE = 16 * 20 + 16;
 constexpr int GA = SCR + 4 * SCR_STRIDE * 4;  // wave 2: G2[64], sb[64]; wave 3: + sg[64]
 constexpr int LDS_BYTES = GA + 5 * CH * 4;
@@ -213,12 +217,15 @@ struct RowOps {
     uint4 d[4][4];  // [R][t]
 };
 
-// One chunk's raw inputs as loaded by a helper wave.
-struct HelperRegs {
-    RowOps k, q;    // q: wave 3 only
-    uint4 v[4];     // wave 3: tokens 4q + i (q = lane % 16), value columns 8m .. 8m + 7 (m = lane / 16)
-    float gam1;     // wave 3: this lane's scalar value gain
-    float la, be;   // this lane's token
+// Registers each helper wave carries from one chunk to the next.
+struct Wave2Regs {
+    float la, be;   // this lane's token gates
+};
+struct Wave3Regs {
+    RowOps q;       // query rows
+    uint4 v[4];     // tokens 4q + i (q = lane % 16), value columns 8m .. 8m + 7 (m = lane / 16)
+    float gam1;     // this lane's scalar value gain
+    float la, be;   // this lane's token gates
 };
 
 __device__ __forceinline__ void load_rows(RowOps& ops, const uint16_t* base, long bh, long T,
@@ -230,14 +237,6 @@ __device__ __forceinline__ void load_rows(RowOps& ops, const uint16_t* base, lon
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) ops.d[R][tt] = *reinterpret_cast<const uint4*>(row + 32 * tt + 8 * g);
     }
-}
-
-__device__ __forceinline__ void mask_rows(RowOps& ops, long T, long t0, int ln) {
-#pragma unroll
-    for (int R = 0; R < 4; ++R)
-        if (t0 + 16 * R + ln >= T)
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt) ops.d[R][tt] = uint4{0u, 0u, 0u, 0u};
 }
 
 // Stage operand rows into a swizzled LDS tile (one 16-byte chunk per row and k-step).
@@ -331,10 +330,11 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
 #pragma unroll
             for (int ib = 0; ib < 8; ++ib) sacc[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        __syncthreads();
+        __syncthreads();  // the helpers have staged the first key tile
+        __syncthreads();  // ... and prepared chunk 0
         for (long c = 0; c < nchunks; ++c) {
-            const char* cur = smem + (c & 1) * BUF;
-            const uint16_t* sK = reinterpret_cast<const uint16_t*>(cur + B_K);
+            const char* cur = smem + PBUF + (c & 1) * BUF;
+            const uint16_t* sK = reinterpret_cast<const uint16_t*>(smem + (c % 3) * KTILE);
             const uint16_t* sQ = reinterpret_cast<const uint16_t*>(cur + B_Q);
             const float* sc = reinterpret_cast<const float*>(cur + B_SC);
             const float* sVt = reinterpret_cast<const float*>(cur + B_VT) + (16 * wave + ln) * VTS;
@@ -526,32 +526,58 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
     const bool w2 = wave == NCHAIN;  // else wave 3
     float* ga = reinterpret_cast<float*>(smem + GA) + (w2 ? 0 : 2 * CH);
 
-    auto load = [&](long c, HelperRegs& H) {
-        const long t0 = c * CH;
-        const long tok = bh * p.T + min(t0 + lane, p.T - 1);
-        H.la = p.log_alpha[tok];
-        H.be = p.beta[tok];
-        load_rows(H.k, p.k, bh, p.T, t0, ln, g);
-        if (!w2) {
-            load_rows(H.q, p.q, bh, p.T, t0, ln, g);
+    // Registers: both helpers hold their chunk-c gates while they prepare chunk
+    // c, wave 3 also its chunk-c query rows and value tile; wave 2 fetches key
+    // tiles into LDS one chunk ahead.  Loads are clamped to row T - 1; rows past T are
+    // finite copies that every product below multiplies by a zero gain.
+    auto load_gates = [&](long c, float& la, float& be) {
+        const long tok = bh * p.T + min(c * CH + lane, p.T - 1);
+        la = p.log_alpha[tok];
+        be = p.beta[tok];
+    };
+    // Key tile of chunk c straight from HBM into its LDS slot (LDS DMA, no
+    // registers): instruction m fills rows 4m .. 4m + 3, lane i landing at row
+    // 4m + i / 16, physical 16-byte chunk i % 16, so it fetches the logical
+    // chunk that the tile swizzle puts there.
+    auto dma_keys = [&](long c) {
+        uint16_t* tile = reinterpret_cast<uint16_t*>(smem + (c % 3) * KTILE);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const long tk = bh * p.T + min(t0 + 4 * ln + i, p.T - 1);
-                H.v[i] = *reinterpret_cast<const uint4*>(p.v + tk * p.dv + j0 + 8 * g);
-            }
-            if (!p.gvec) H.gam1 = p.gsrc[tok * p.gts];
+        for (int m = 0; m < 16; ++m) {
+            const int r = 4 * m + (lane >> 4);
+            const int f = ((r & 3) << 2) | ((r >> 2) & 3);
+            const long t = min(c * CH + r, p.T - 1);
+            const uint16_t* src = p.k + (bh * p.T + t) * DK + 8 * ((lane & 15) ^ f);
+            __builtin_amdgcn_global_load_lds(static_cast<const void*>(src),
+                                             (__attribute__((address_space(3))) void*)(tile + 4 * m * DK), 16, 0, 0);
         }
     };
-
-    // Build everything chunk c needs into `buf` from the registers in H.
-    auto prepare = [&](long c, char* buf, HelperRegs& H) {
+    auto load3 = [&](long c, Wave3Regs& R3) {
         const long t0 = c * CH;
-        mask_rows(H.k, p.T, t0, ln);
+        load_gates(c, R3.la, R3.be);
+        load_rows(R3.q, p.q, bh, p.T, t0, ln, g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const long tk = bh * p.T + min(t0 + 4 * ln + i, p.T - 1);
+            R3.v[i] = *reinterpret_cast<const uint4*>(p.v + tk * p.dv + j0 + 8 * g);
+        }
+        if (!p.gvec) R3.gam1 = p.gsrc[(bh * p.T + min(t0 + lane, p.T - 1)) * p.gts];
+    };
+    auto ktile = [&](long c) { return reinterpret_cast<uint16_t*>(smem + (c % 3) * KTILE); };
+    // rows of a staged tile as 16x16x32 operands: block b, k-step t
+    auto tile_op = [&](const uint16_t* tile, int b, int t) {
+        return *reinterpret_cast<const bf16x8*>(tile + kq_off(16 * b + ln, 32 * t + 8 * g));
+    };
+
+    // Everything chunk c needs goes into `buf`; wave 2 additionally stages the
+    // key tile of chunk c + 1.  The gate prologue is the same for both waves.
+    auto prepare2 = [&](long c, char* buf, Wave2Regs& R2) {
+        const float la = R2.la, be = R2.be;
+        const long t0 = c * CH;
         // per-token gates: inclusive cumulative log2 decay and sqrt(beta);
         // rows past T hold G and get sb = 0 (no erase, no write)
         const bool ok = t0 + lane < p.T;
-        const float gl = wave_incl_scan((p.has_alpha && ok) ? fmaxf(H.la, kLogAlphaMin) * kLog2e : 0.0f);
-        const float sb = ok ? sqrt_hw(H.be) : 0.0f;
+        const float gl = wave_incl_scan((p.has_alpha && ok) ? fmaxf(la, kLogAlphaMin) * kLog2e : 0.0f);
+        const float sb = ok ? sqrt_hw(be) : 0.0f;
         const float G2last =
             __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gl), 63));
         ga[lane] = gl;
@@ -578,166 +604,223 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
             for (int e = 0; e < 4; ++e) cJ[J][e] = sbs[J][e] * ex2(Ge[J] - Gs[J][e]);
         }
 
-        if (w2) {
-            // ---- wave 2: form T, stage K, invert the diagonal blocks ----
-            // raw key Gram blocks first, so the key registers can be refilled
-            f32x4 tr[4][4];
+        // ---- wave 2: fetch the next key tile, form T, invert the diagonal blocks ----
+        if (c + 1 < nchunks) dma_keys(c + 1);
+        if (c + 1 < nchunks) load_gates(c + 1, R2.la, R2.be);
+        const uint16_t* kt = ktile(c);
+        f32x4 tr[4][4];
+#pragma unroll
+        for (int R = 0; R < 4; ++R)
+#pragma unroll
+            for (int J = 0; J <= R; ++J) tr[R][J] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            bf16x8 kr[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) kr[b] = tile_op(kt, b, t);
 #pragma unroll
             for (int R = 0; R < 4; ++R)
 #pragma unroll
-                for (int J = 0; J <= R; ++J) {
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int t = 0; t < 4; ++t)
-                        acc = mfma32(as_bf16x8(H.k.d[J][t]), as_bf16x8(H.k.d[R][t]), acc);
-                    tr[R][J] = acc;
-                }
-            stage_rows(H.k, reinterpret_cast<uint16_t*>(buf + B_K), ln, g);
-            if (c + 1 < nchunks) load(c + 1, H);
-            float* scr = reinterpret_cast<float*>(smem + SCR);
-            // tt[R][J] holds T[16R + ln][16J + 4g + e] for J < R (i.e. T_RJ^T in
-            // accumulator layout); diagonal blocks go to the scratch.
-            f32x4 tt[4][4];
-#pragma unroll
-            for (int R = 0; R < 4; ++R)
-#pragma unroll
-                for (int J = 0; J <= R; ++J) {
-                    f32x4 acc = tr[R][J];
-                    if (J == R) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int s = 4 * g + e;
-                            acc[e] = (s < ln) ? acc[e] * sbr[R] * sbs[R][e] * ex2(Gr[R] - Gs[R][e]) : 0.0f;
-                        }
-                        *reinterpret_cast<f32x4*>(scr + R * SCR_STRIDE + ln * 20 + 4 * g) = acc;
-                    } else {
-                        const float rf = sbr[R] * ex2(Gr[R] - Ge[J]);
-                        tt[R][J] = acc * rf * cJ[J];
-                    }
-                }
-            // diagonal blocks: D_R = (I + T_RR)^-1 row by row, one row per lane
-            // (lane = (R, row r); a DPP row of 16 lanes is one block).  Once row j
-            // is final it is broadcast across its block and every row r takes
-            // x_r -= T_rj x_j; rows r <= j have T_rj = 0 and stay unchanged, and
-            // x_j is zero beyond column j, so step j touches columns 0..j only.
-            // D_R overwrites T_RR in the scratch (row-major, row stride 20).
-            {
-                float* Brow = scr + (lane >> 4) * SCR_STRIDE + (lane & 15) * 20;
-                float ntr[16];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const f32x4 v = *reinterpret_cast<const f32x4*>(Brow + 4 * q);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) ntr[4 * q + e] = -v[e];
-                }
-                float x[16];
-#pragma unroll
-                for (int cc = 0; cc < 16; ++cc) x[cc] = (cc == (lane & 15)) ? 1.0f : 0.0f;
-                block_row_solve(x, ntr);
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    *reinterpret_cast<f32x4*>(Brow + 4 * q) = f32x4{x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]};
-            }
-            // solve fragments: lane (ln, g) holds row ln, columns 4g .. 4g + 3 of each
-            // block, which is tt[R][J] (T_RJ^T in accumulator layout) for T and a
-            // row read of the scratch for D
-            char* tf = buf + B_TF;
-#pragma unroll
-            for (int R = 0; R < 4; ++R)
-                put_f16(tf, F16_D0 + R, lane,
-                        *reinterpret_cast<const f32x4*>(scr + R * SCR_STRIDE + ln * 20 + 4 * g));
-            put_f16(tf, F16_T10, lane, -tt[1][0]);
-            put_f16(tf, F16_T32, lane, -tt[3][2]);
-            put_f32(tf, F32_T2, lane, -tt[2][0], -tt[2][1]);
-            put_f32(tf, F32_T3, lane, -tt[3][0], -tt[3][1]);
-        } else {
-            // ---- wave 3: form P, stage Q, V (transposed), row scales ----
-            mask_rows(H.q, p.T, t0, ln);
-            // raw query-key products first, so the registers can be refilled
-            f32x4 pb[4][4];
-#pragma unroll
-            for (int R = 0; R < 4; ++R)
-#pragma unroll
-                for (int S = 0; S <= R; ++S) {
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int t = 0; t < 4; ++t)
-                        acc = mfma32(as_bf16x8(H.k.d[S][t]), as_bf16x8(H.q.d[R][t]), acc);
-                    pb[R][S] = acc;
-                }
-            stage_rows(H.q, reinterpret_cast<uint16_t*>(buf + B_Q), ln, g);
-            float* sc = reinterpret_cast<float*>(buf + B_SC);
-            const float eg = ex2(gl);
-            sc[lane] = sb * eg;                         // rows of K.Gamma
-            sc[CH + lane] = eg;                         // rows of Q.Gamma
-            sc[2 * CH + lane] = sb * ex2(G2last - gl);  // rows of Khat
-            if (lane == 0) sc[3 * CH] = ex2(G2last);    // chunk decay
-            // value tile, transposed and scaled by sqrt(gamma): lane (q = ln, m = g)
-            // holds tokens 4q .. 4q + 3 of columns 8m .. 8m + 7, one 16-byte write
-            // per column; rows past T get 0
-            float* sVt = reinterpret_cast<float*>(buf + B_VT);
-            f32x4 sg4[8];
-            if (!p.gvec) {
-                ga[2 * CH + lane] = ok ? sqrt_hw(H.gam1) : 0.0f;
-                const f32x4 s4 = *reinterpret_cast<const f32x4*>(ga + 2 * CH + 4 * ln);
-#pragma unroll
-                for (int cc = 0; cc < 8; ++cc) sg4[cc] = s4;
-            } else {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const long tok = t0 + 4 * ln + i;
-                    const float* gr = p.gsrc + (bh * p.T + min(tok, p.T - 1)) * p.gts + j0 + 8 * g;
-#pragma unroll
-                    for (int cc = 0; cc < 8; ++cc) sg4[cc][i] = tok < p.T ? sqrt_hw(gr[cc]) : 0.0f;
-                }
-            }
-#pragma unroll
-            for (int cc = 0; cc < 8; ++cc) {
-                f32x4 col4;
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    col4[i] = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(&H.v[i])[cc]);
-                *reinterpret_cast<f32x4*>(sVt + (8 * g + cc) * VTS + 4 * ln) = sg4[cc] * col4;
-            }
-            if (c + 1 < nchunks) load(c + 1, H);
-            // P^T blocks: pb[R][S] holds P[16R + ln][16S + 4g + e]
-#pragma unroll
-            for (int R = 0; R < 4; ++R)
-#pragma unroll
-                for (int S = 0; S <= R; ++S) {
-                    if (S == R) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int s = 4 * g + e;
-                            pb[R][S][e] = (s <= ln) ? pb[R][S][e] * sbs[S][e] * ex2(Gr[R] - Gs[S][e]) : 0.0f;
-                        }
-                    } else {
-                        pb[R][S] = pb[R][S] * ex2(Gr[R] - Ge[S]) * cJ[S];
-                    }
-                }
-            char* pf = buf + B_PF;
-            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-            put_frag(pf, 0, 0, lane, pb[0][0], zero);
-            put_frag(pf, 1, 0, lane, pb[1][0], pb[1][1]);
-            put_frag(pf, 2, 0, lane, pb[2][0], pb[2][1]);
-            put_frag(pf, 2, 1, lane, pb[2][2], zero);
-            put_frag(pf, 3, 0, lane, pb[3][0], pb[3][1]);
-            put_frag(pf, 3, 1, lane, pb[3][2], pb[3][3]);
+                for (int J = 0; J <= R; ++J) tr[R][J] = mfma32(kr[J], kr[R], tr[R][J]);
         }
+        float* scr = reinterpret_cast<float*>(smem + SCR);
+        // tt[R][J] holds T[16R + ln][16J + 4g + e] for J < R (i.e. T_RJ^T in
+        // accumulator layout); diagonal blocks go to the scratch.
+        f32x4 tt[4][4];
+#pragma unroll
+        for (int R = 0; R < 4; ++R)
+#pragma unroll
+            for (int J = 0; J <= R; ++J) {
+                f32x4 acc = tr[R][J];
+                if (J == R) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int s = 4 * g + e;
+                        acc[e] = (s < ln) ? acc[e] * sbr[R] * sbs[R][e] * ex2(Gr[R] - Gs[R][e]) : 0.0f;
+                    }
+                    *reinterpret_cast<f32x4*>(scr + R * SCR_STRIDE + ln * 20 + 4 * g) = acc;
+                } else {
+                    const float rf = sbr[R] * ex2(Gr[R] - Ge[J]);
+                    tt[R][J] = acc * rf * cJ[J];
+                }
+            }
+        // diagonal blocks: D_R = (I + T_RR)^-1 row by row, one row per lane
+        // (lane = (R, row r); a DPP row of 16 lanes is one block).  Once row j
+        // is final it is broadcast across its block and every row r takes
+        // x_r -= T_rj x_j; rows r <= j have T_rj = 0 and stay unchanged, and
+        // x_j is zero beyond column j, so step j touches columns 0..j only.
+        // D_R overwrites T_RR in the scratch (row-major, row stride 20).
+        {
+            float* Brow = scr + (lane >> 4) * SCR_STRIDE + (lane & 15) * 20;
+            float ntr[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 v = *reinterpret_cast<const f32x4*>(Brow + 4 * q);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ntr[4 * q + e] = -v[e];
+            }
+            float x[16];
+#pragma unroll
+            for (int cc = 0; cc < 16; ++cc) x[cc] = (cc == (lane & 15)) ? 1.0f : 0.0f;
+            block_row_solve(x, ntr);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<f32x4*>(Brow + 4 * q) = f32x4{x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]};
+        }
+        // solve fragments: lane (ln, g) holds row ln, columns 4g .. 4g + 3 of each
+        // block, which is tt[R][J] (T_RJ^T in accumulator layout) for T and a
+        // row read of the scratch for D
+        char* tf = buf + B_TF;
+#pragma unroll
+        for (int R = 0; R < 4; ++R)
+            put_f16(tf, F16_D0 + R, lane,
+                    *reinterpret_cast<const f32x4*>(scr + R * SCR_STRIDE + ln * 20 + 4 * g));
+        put_f16(tf, F16_T10, lane, -tt[1][0]);
+        put_f16(tf, F16_T32, lane, -tt[3][2]);
+        put_f32(tf, F32_T2, lane, -tt[2][0], -tt[2][1]);
+        put_f32(tf, F32_T3, lane, -tt[3][0], -tt[3][1]);
+    };
+    auto prepare3 = [&](long c, char* buf, Wave3Regs& R3) {
+        const float la = R3.la, be = R3.be;
+        const long t0 = c * CH;
+        // per-token gates: inclusive cumulative log2 decay and sqrt(beta);
+        // rows past T hold G and get sb = 0 (no erase, no write)
+        const bool ok = t0 + lane < p.T;
+        const float gl = wave_incl_scan((p.has_alpha && ok) ? fmaxf(la, kLogAlphaMin) * kLog2e : 0.0f);
+        const float sb = ok ? sqrt_hw(be) : 0.0f;
+        const float G2last =
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gl), 63));
+        ga[lane] = gl;
+        ga[CH + lane] = sb;
+        // gate values at rows 16R + ln and at columns 16J + 4g + e
+        float Gr[4], sbr[4];
+        f32x4 Gs[4], sbs[4];
+#pragma unroll
+        for (int R = 0; R < 4; ++R) {
+            Gr[R] = ga[16 * R + ln];
+            sbr[R] = ga[CH + 16 * R + ln];
+            Gs[R] = *reinterpret_cast<const f32x4*>(ga + 16 * R + 4 * g);
+            sbs[R] = *reinterpret_cast<const f32x4*>(ga + CH + 16 * R + 4 * g);
+        }
+        // Off-diagonal blocks (row block R > column block J) split the decay at
+        // the last row of block J: exp2(G_r - G_s) = exp2(G_r - Ge_J) exp2(Ge_J - G_s),
+        // both factors <= 1.  cJ[J] holds sb_s exp2(Ge_J - G_s) for this lane's columns.
+        float Ge[3];
+        f32x4 cJ[3];
+#pragma unroll
+        for (int J = 0; J < 3; ++J) {
+            Ge[J] = ga[16 * J + 15];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) cJ[J][e] = sbs[J][e] * ex2(Ge[J] - Gs[J][e]);
+        }
+
+        // ---- wave 3: form P, stage Q, V (transposed), row scales ----
+        // raw query-key products (keys from the staged tile) first, so the
+        // registers can be refilled
+        const uint16_t* kt = ktile(c);
+        f32x4 pb[4][4];
+#pragma unroll
+        for (int R = 0; R < 4; ++R)
+#pragma unroll
+            for (int S = 0; S <= R; ++S) pb[R][S] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            bf16x8 kr[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) kr[b] = tile_op(kt, b, t);
+#pragma unroll
+            for (int R = 0; R < 4; ++R)
+#pragma unroll
+                for (int S = 0; S <= R; ++S) pb[R][S] = mfma32(kr[S], as_bf16x8(R3.q.d[R][t]), pb[R][S]);
+        }
+        stage_rows(R3.q, reinterpret_cast<uint16_t*>(buf + B_Q), ln, g);
+        float* sc = reinterpret_cast<float*>(buf + B_SC);
+        const float eg = ex2(gl);
+        sc[lane] = sb * eg;                         // rows of K.Gamma
+        sc[CH + lane] = eg;                         // rows of Q.Gamma
+        sc[2 * CH + lane] = sb * ex2(G2last - gl);  // rows of Khat
+        if (lane == 0) sc[3 * CH] = ex2(G2last);    // chunk decay
+        // value tile, transposed and scaled by sqrt(gamma): lane (q = ln, m = g)
+        // holds tokens 4q .. 4q + 3 of columns 8m .. 8m + 7, one 16-byte write
+        // per column; rows past T get 0
+        float* sVt = reinterpret_cast<float*>(buf + B_VT);
+        f32x4 sg4[8];
+        if (!p.gvec) {
+            ga[2 * CH + lane] = ok ? sqrt_hw(R3.gam1) : 0.0f;
+            const f32x4 s4 = *reinterpret_cast<const f32x4*>(ga + 2 * CH + 4 * ln);
+#pragma unroll
+            for (int cc = 0; cc < 8; ++cc) sg4[cc] = s4;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const long tok = t0 + 4 * ln + i;
+                const float* gr = p.gsrc + (bh * p.T + min(tok, p.T - 1)) * p.gts + j0 + 8 * g;
+#pragma unroll
+                for (int cc = 0; cc < 8; ++cc) sg4[cc][i] = tok < p.T ? sqrt_hw(gr[cc]) : 0.0f;
+            }
+        }
+#pragma unroll
+        for (int cc = 0; cc < 8; ++cc) {
+            f32x4 col4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                col4[i] = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(&R3.v[i])[cc]);
+            *reinterpret_cast<f32x4*>(sVt + (8 * g + cc) * VTS + 4 * ln) = sg4[cc] * col4;
+        }
+        if (c + 1 < nchunks) load3(c + 1, R3);
+        // P^T blocks: pb[R][S] holds P[16R + ln][16S + 4g + e]
+#pragma unroll
+        for (int R = 0; R < 4; ++R)
+#pragma unroll
+            for (int S = 0; S <= R; ++S) {
+                if (S == R) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int s = 4 * g + e;
+                        pb[R][S][e] = (s <= ln) ? pb[R][S][e] * sbs[S][e] * ex2(Gr[R] - Gs[S][e]) : 0.0f;
+                    }
+                } else {
+                    pb[R][S] = pb[R][S] * ex2(Gr[R] - Ge[S]) * cJ[S];
+                }
+            }
+        char* pf = buf + B_PF;
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        put_frag(pf, 0, 0, lane, pb[0][0], zero);
+        put_frag(pf, 1, 0, lane, pb[1][0], pb[1][1]);
+        put_frag(pf, 2, 0, lane, pb[2][0], pb[2][1]);
+        put_frag(pf, 2, 1, lane, pb[2][2], zero);
+        put_frag(pf, 3, 0, lane, pb[3][0], pb[3][1]);
+        put_frag(pf, 3, 1, lane, pb[3][2], pb[3][3]);
     };
 
-    // The registers hold the inputs of the next chunk to prepare; prepare()
-    // refills them with the chunk after it as soon as they have been consumed,
-    // which leaves a whole chunk period for the loads to land.
-    HelperRegs H;
-    if (nchunks > 0) {
-        load(0, H);
-        prepare(0, smem, H);
-    }
-    __syncthreads();
-    for (long c = 0; c < nchunks; ++c) {
-        if (c + 1 < nchunks) prepare(c + 1, smem + ((c + 1) & 1) * BUF, H);
+    // Prologue: wave 2 fetches the first key tile; both helpers hold the gates
+    // (wave 3 also the queries and values) of chunk 0.  prepare(c) refills the registers as soon as they
+    // have been consumed, which leaves a whole chunk period for loads to land.
+    // The two waves run separate copies of the loop (same barrier sequence) so
+    // that each keeps only its own registers live.
+    if (w2) {
+        Wave2Regs R2;
+        if (nchunks > 0) {
+            dma_keys(0);
+            load_gates(0, R2.la, R2.be);
+        }
         __syncthreads();
+        if (nchunks > 0) prepare2(0, smem + PBUF, R2);
+        __syncthreads();
+        for (long c = 0; c < nchunks; ++c) {
+            if (c + 1 < nchunks) prepare2(c + 1, smem + PBUF + ((c + 1) & 1) * BUF, R2);
+            __syncthreads();
+        }
+    } else {
+        Wave3Regs R3;
+        if (nchunks > 0) load3(0, R3);
+        __syncthreads();
+        if (nchunks > 0) prepare3(0, smem + PBUF, R3);
+        __syncthreads();
+        for (long c = 0; c < nchunks; ++c) {
+            if (c + 1 < nchunks) prepare3(c + 1, smem + PBUF + ((c + 1) & 1) * BUF, R3);
+            __syncthreads();
+        }
     }
 }
 
