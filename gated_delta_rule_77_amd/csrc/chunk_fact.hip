@@ -14,7 +14,8 @@
 //   S   <- Gamma_63 S + K^T diag(sb exp(G_63 - G)) U
 //
 // U is found by block forward substitution over the four 16-token blocks of
-// the chunk: U_R = D_R (X_R - sum_{J<R} T_RJ U_J), D_R = (I + T_RR)^-1.
+// the chunk: U_R = D_R X_R - sum_{J<R} N_RJ U_J with D_R = (I + T_RR)^-1 and
+// N_RJ = D_R T_RJ, so the only dependent steps are the three N products.
 //
 // Work split.  A workgroup owns (b, h, 32 value columns) for the whole
 // sequence and has four waves:
@@ -25,7 +26,7 @@
 //     wave 2 stages the key tile, forms T with MFMAs and inverts its 16x16
 //     diagonal blocks by forward substitution; wave 3 stages the query tile,
 //     the gain-scaled value tile and the per-row scales, and forms P.  The
-//     blocks of T, D and P are written already split into bf16 hi/lo
+//     blocks of D, N and P are written already split into bf16 hi/lo
 //     fragments in the per-lane order of the chain's MFMA operands, so the
 //     chain reads them with one LDS load per term and no conversion.
 // LDS holds two chunk buffers; one workgroup barrier per chunk hands a
@@ -46,13 +47,13 @@ constexpr int DVT = 16 * NCHAIN;
 constexpr int VTS = CH + 4;  // row stride of the transposed value tile (floats)
 constexpr int NFRAG = 6;     // lower-triangular (block row, k-step) fragments of P
 
-// Solve fragments (hi and lo terms, per lane): two 16x32 operands [-T_R0 | -T_R1]
+// Solve fragments (hi and lo terms, per lane): two 16x32 operands [-N_R0 | -N_R1]
 // for R = 2, 3 (16 bytes per lane and term), then six 16x16 operands D_0..D_3,
-// -T_10, -T_32 (8 bytes per lane and term).
+// -N_10, -N_32 (8 bytes per lane and term).
 constexpr int TF16 = 2 * 2 * 64 * 16;
 constexpr int TF_BYTES = TF16 + 6 * 2 * 64 * 8;
-enum { F32_T2 = 0, F32_T3 = 1 };
-enum { F16_D0 = 0, F16_T10 = 4, F16_T32 = 5 };
+enum { F32_N2 = 0, F32_N3 = 1 };
+enum { F16_D0 = 0, F16_N10 = 4, F16_N32 = 5 };
 
 // LDS layout (bytes).  Three key tiles (bf16 [64][128], swizzled; chunk c in
 // slot c % 3: the chain reads chunk c while the helpers read chunk c + 1 and
@@ -163,6 +164,15 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) { return __builtin_b
 // exp2 only ever underflows towards 0.
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float sqrt_hw(float x) { return __builtin_amdgcn_sqrtf(x); }
+
+// acc += X^T Y for 16x16 fp32 blocks X, Y in accumulator layout (lane (ln, g)
+// element e holds row 4g + e, column ln).  Element e of every lane forms the
+// k-slice {4g + e}, so four 16x16x4 fp32 MFMAs give the product in fp32.
+__device__ __forceinline__ f32x4 mm_t(const f32x4& x, const f32x4& y, f32x4 c) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(x[e], y[e], c, 0, 0, 0);
+    return c;
+}
 
 __device__ __forceinline__ f32x4 mfma16(const bf16x4& a, const bf16x4& b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
@@ -394,40 +404,37 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
                 o[1] = *reinterpret_cast<const bf16x8*>(tf + f32_off(sl, 1, lane));
             };
             const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-            f32x4 u[4];
-            bf16x4 bu[4][2], bw[2], a4[2];
+            f32x4 u[4], W[4];
+            bf16x4 bu[4][2], a4[2];
             bf16x8 a8[2];
-            split_d(x[0], bw);
-            a16(F16_D0 + 0, a4);
-            u[0] = mm22x16(a4, bw, zero);
+            // W_R = D_R X_R: independent of each other and of U
+#pragma unroll
+            for (int R = 0; R < 4; ++R) {
+                bf16x4 bx[2];
+                split_d(x[R], bx);
+                a16(F16_D0 + R, a4);
+                W[R] = mm22x16(a4, bx, zero);
+            }
+            u[0] = W[0];
+            split_d(u[0], bu[0]);
             // Z = Q S does not depend on the solve: its k-steps fill the gaps
             // between the dependent solve steps
             rows_x_state(sQ, true, 0, z);
-            split_d(u[0], bu[0]);
-            a16(F16_T10, a4);
-            f32x4 w = mm22x16(a4, bu[0], x[1]);
-            split_d(w, bw);
-            a16(F16_D0 + 1, a4);
-            u[1] = mm22x16(a4, bw, zero);
+            a16(F16_N10, a4);
+            u[1] = mm22x16(a4, bu[0], W[1]);
             rows_x_state(sQ, true, 1, z);
             split_d(u[1], bu[1]);
             bf16x8 bU[2][2];
             bU[0][0] = cat4(bu[0][0], bu[1][0]);
             bU[0][1] = cat4(bu[0][1], bu[1][1]);
-            a32(F32_T2, a8);
-            w = mm22(a8, bU[0], x[2]);
-            split_d(w, bw);
-            a16(F16_D0 + 2, a4);
-            u[2] = mm22x16(a4, bw, zero);
+            a32(F32_N2, a8);
+            u[2] = mm22(a8, bU[0], W[2]);
+            a32(F32_N3, a8);
+            f32x4 w3 = mm22(a8, bU[0], W[3]);
             rows_x_state(sQ, true, 2, z);
             split_d(u[2], bu[2]);
-            a32(F32_T3, a8);
-            w = mm22(a8, bU[0], x[3]);
-            a16(F16_T32, a4);
-            w = mm22x16(a4, bu[2], w);
-            split_d(w, bw);
-            a16(F16_D0 + 3, a4);
-            u[3] = mm22x16(a4, bw, zero);
+            a16(F16_N32, a4);
+            u[3] = mm22x16(a4, bu[2], w3);
             rows_x_state(sQ, true, 3, z);
             split_d(u[3], bu[3]);
             bU[1][0] = cat4(bu[2][0], bu[3][0]);
@@ -619,14 +626,20 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
 #pragma unroll
             for (int b = 0; b < 4; ++b) kr[b] = tile_op(kt, b, t);
 #pragma unroll
-            for (int R = 0; R < 4; ++R)
+            for (int R = 0; R < 4; ++R) {
+                // diagonal blocks as row segments (lane (ln, g): row ln, columns
+                // 4g + e), off-diagonal blocks in accumulator layout of T_RJ
+                tr[R][R] = mfma32(kr[R], kr[R], tr[R][R]);
 #pragma unroll
-                for (int J = 0; J <= R; ++J) tr[R][J] = mfma32(kr[J], kr[R], tr[R][J]);
+                for (int J = 0; J < R; ++J) tr[R][J] = mfma32(kr[R], kr[J], tr[R][J]);
+            }
         }
         float* scr = reinterpret_cast<float*>(smem + SCR);
-        // tt[R][J] holds T[16R + ln][16J + 4g + e] for J < R (i.e. T_RJ^T in
-        // accumulator layout); diagonal blocks go to the scratch.
-        f32x4 tt[4][4];
+        // tc[R][J] holds T[16R + 4g + e][16J + ln] for J < R (T_RJ in accumulator
+        // layout); diagonal blocks go to the scratch.  The off-diagonal decay is
+        // split at the last row of block J (Ge_J): the row factor
+        // sb_r exp2(G_r - Ge_J) varies with e, the column factor with the lane.
+        f32x4 tc[4][4];
 #pragma unroll
         for (int R = 0; R < 4; ++R)
 #pragma unroll
@@ -640,8 +653,10 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
                     }
                     *reinterpret_cast<f32x4*>(scr + R * SCR_STRIDE + ln * 20 + 4 * g) = acc;
                 } else {
-                    const float rf = sbr[R] * ex2(Gr[R] - Ge[J]);
-                    tt[R][J] = acc * rf * cJ[J];
+                    f32x4 rf;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) rf[e] = sbs[R][e] * ex2(Gs[R][e] - Ge[J]);
+                    tc[R][J] = acc * rf * (sbr[J] * ex2(Ge[J] - Gr[J]));
                 }
             }
         // diagonal blocks: D_R = (I + T_RR)^-1 row by row, one row per lane
@@ -667,18 +682,27 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
             for (int q = 0; q < 4; ++q)
                 *reinterpret_cast<f32x4*>(Brow + 4 * q) = f32x4{x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]};
         }
-        // solve fragments: lane (ln, g) holds row ln, columns 4g .. 4g + 3 of each
-        // block, which is tt[R][J] (T_RJ^T in accumulator layout) for T and a
-        // row read of the scratch for D
-        char* tf = buf + B_TF;
+        // N_RJ = D_R T_RJ.  With tc = T_RJ and drow(R) = D_R^T in accumulator
+        // layout, mm_t gives (D_R T_RJ)^T in accumulator layout: lane (ln, g)
+        // holds row ln, columns 4g .. 4g + 3 of N_RJ, which is its A-operand
+        // fragment.  The same holds for drow(R) and D_R.
+        f32x4 drow[4];
 #pragma unroll
         for (int R = 0; R < 4; ++R)
-            put_f16(tf, F16_D0 + R, lane,
-                    *reinterpret_cast<const f32x4*>(scr + R * SCR_STRIDE + ln * 20 + 4 * g));
-        put_f16(tf, F16_T10, lane, -tt[1][0]);
-        put_f16(tf, F16_T32, lane, -tt[3][2]);
-        put_f32(tf, F32_T2, lane, -tt[2][0], -tt[2][1]);
-        put_f32(tf, F32_T3, lane, -tt[3][0], -tt[3][1]);
+            drow[R] = *reinterpret_cast<const f32x4*>(scr + R * SCR_STRIDE + ln * 20 + 4 * g);
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        f32x4 nb[4][4];
+#pragma unroll
+        for (int R = 1; R < 4; ++R)
+#pragma unroll
+            for (int J = 0; J < R; ++J) nb[R][J] = -mm_t(tc[R][J], drow[R], zero);
+        char* tf = buf + B_TF;
+#pragma unroll
+        for (int R = 0; R < 4; ++R) put_f16(tf, F16_D0 + R, lane, drow[R]);
+        put_f16(tf, F16_N10, lane, nb[1][0]);
+        put_f16(tf, F16_N32, lane, nb[3][2]);
+        put_f32(tf, F32_N2, lane, nb[2][0], nb[2][1]);
+        put_f32(tf, F32_N3, lane, nb[3][0], nb[3][1]);
     };
     auto prepare3 = [&](long c, char* buf, Wave3Regs& R3) {
         const float la = R3.la, be = R3.be;
