@@ -47,8 +47,8 @@ def alg_flops_per_token_head(dk: int, dv: int, C: int = CHUNK_FLOP_C) -> float:
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--decode-steps", type=int, default=200)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -60,11 +60,14 @@ def parse():
 
 
 def kernel_source_hash() -> str:
+    """Hash of everything that decides the kernels' machine code: the HIP
+    sources and the build script (compiler flags)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gated_delta_rule_77_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
         if f.endswith((".hip", ".h", ".cpp")):
             h.update(open(os.path.join(csrc, f), "rb").read())
+    h.update(open(os.path.join(ROOT, "gated_delta_rule_77_amd", "build.py"), "rb").read())
     return h.hexdigest()[:16]
 
 
