@@ -33,6 +33,8 @@
 // buffer from the helpers to the chain waves.  The state-update operand K^T
 // is read from the row-major key tile with the gfx950 LDS transpose read
 // (ds_read_b64_tr_b16), so no transposed copy of K is stored.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -67,12 +69,11 @@ constexpr int B_PF = B_TF + TF_BYTES;
 constexpr int B_VT = B_PF + NFRAG * 2 * 64 * 16;
 constexpr int B_SC = B_VT + DVT * VTS * 4;
 constexpr int BUF = B_SC + 4 * CH * 4;  // rsKS[64], rq[64], rk[64], gC
-constexpr int PBUF = 3 * KTILE;         // first per-parity buffer
-constexpr int SCR = PBUF + 2 * BUF;     // wave 2: four diagonal 16x16 blocks
+constexpr int SCR = 2 * BUF;            // wave 2: four diagonal 16x16 blocks
 constexpr int SCR_STRIDE = 16 * 20 + 16;
 constexpr int GA = SCR + 4 * SCR_STRIDE * 4;  // wave 2: G2[64], sb[64]; wave 3: + sg[64]
 constexpr int LDS_BYTES = GA + 5 * CH * 4;
-static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+static_assert(LDS_BYTES + 3 * KTILE <= 160 * 1024, "LDS budget");
 static_assert(B_PF % 16 == 0 && B_VT % 16 == 0 && BUF % 16 == 0, "LDS alignment");
 
 struct FactParams {
@@ -95,6 +96,7 @@ struct FactParams {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
 // ---------------------------------------------------------------------------
 // layouts
@@ -301,7 +303,25 @@ __device__ __forceinline__ void put_f16(char* base, int s, int lane, const f32x4
 // ---------------------------------------------------------------------------
 
 __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
+    // Key tiles: a ring of three slots, chunk c in slot c % 3.  The slots are
+    // separate LDS objects so that the compiler can tell the slot being filled
+    // by DMA from the slot being read (a compile-time choice in wave 2's loop)
+    // and does not make the reads wait for the DMA.
+    __shared__ __attribute__((aligned(16))) uint16_t ks0[CH * DK];
+    __shared__ __attribute__((aligned(16))) uint16_t ks1[CH * DK];
+    __shared__ __attribute__((aligned(16))) uint16_t ks2[CH * DK];
     __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
+    auto ktile = [&](long c) -> uint16_t* {
+        const long m = c % 3;
+        return m == 0 ? ks0 : (m == 1 ? ks1 : ks2);
+    };
+    // slot S as an LDS-typed pointer (S known at compile time)
+    auto kslot = [&](auto slot) -> lds_u16* {
+        constexpr int S = decltype(slot)::value;
+        if constexpr (S == 0) return (lds_u16*)(ks0);
+        else if constexpr (S == 1) return (lds_u16*)(ks1);
+        else return (lds_u16*)(ks2);
+    };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -343,8 +363,8 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
         __syncthreads();  // the helpers have staged the first key tile
         __syncthreads();  // ... and prepared chunk 0
         for (long c = 0; c < nchunks; ++c) {
-            const char* cur = smem + PBUF + (c & 1) * BUF;
-            const uint16_t* sK = reinterpret_cast<const uint16_t*>(smem + (c % 3) * KTILE);
+            const char* cur = smem + (c & 1) * BUF;
+            const uint16_t* sK = ktile(c);
             const uint16_t* sQ = reinterpret_cast<const uint16_t*>(cur + B_Q);
             const float* sc = reinterpret_cast<const float*>(cur + B_SC);
             const float* sVt = reinterpret_cast<const float*>(cur + B_VT) + (16 * wave + ln) * VTS;
@@ -546,8 +566,7 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
     // registers): instruction m fills rows 4m .. 4m + 3, lane i landing at row
     // 4m + i / 16, physical 16-byte chunk i % 16, so it fetches the logical
     // chunk that the tile swizzle puts there.
-    auto dma_keys = [&](long c) {
-        uint16_t* tile = reinterpret_cast<uint16_t*>(smem + (c % 3) * KTILE);
+    auto dma_keys = [&](long c, lds_u16* tile) {
 #pragma unroll
         for (int m = 0; m < 16; ++m) {
             const int r = 4 * m + (lane >> 4);
@@ -569,7 +588,6 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
         }
         if (!p.gvec) R3.gam1 = p.gsrc[(bh * p.T + min(t0 + lane, p.T - 1)) * p.gts];
     };
-    auto ktile = [&](long c) { return reinterpret_cast<uint16_t*>(smem + (c % 3) * KTILE); };
     // rows of a staged tile as 16x16x32 operands: block b, k-step t
     auto tile_op = [&](const uint16_t* tile, int b, int t) {
         return *reinterpret_cast<const bf16x8*>(tile + kq_off(16 * b + ln, 32 * t + 8 * g));
@@ -577,7 +595,7 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
 
     // Everything chunk c needs goes into `buf`; wave 2 additionally stages the
     // key tile of chunk c + 1.  The gate prologue is the same for both waves.
-    auto prepare2 = [&](long c, char* buf, Wave2Regs& R2) {
+    auto prepare2 = [&](long c, char* buf, Wave2Regs& R2, auto slot) {
         const float la = R2.la, be = R2.be;
         const long t0 = c * CH;
         // per-token gates: inclusive cumulative log2 decay and sqrt(beta);
@@ -612,9 +630,12 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
         }
 
         // ---- wave 2: fetch the next key tile, form T, invert the diagonal blocks ----
-        if (c + 1 < nchunks) dma_keys(c + 1);
+        // (unconditional: past the last chunk it refetches row T - 1 into a slot
+        // that nothing reads any more, which keeps the destination a constant)
+        constexpr int S = decltype(slot)::value;
+        dma_keys(c + 1, kslot(std::integral_constant<int, (S + 1) % 3>{}));
         if (c + 1 < nchunks) load_gates(c + 1, R2.la, R2.be);
-        const uint16_t* kt = ktile(c);
+        const uint16_t* kt = (const uint16_t*)kslot(slot);
         f32x4 tr[4][4];
 #pragma unroll
         for (int R = 0; R < 4; ++R)
@@ -825,24 +846,34 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
     if (w2) {
         Wave2Regs R2;
         if (nchunks > 0) {
-            dma_keys(0);
+            dma_keys(0, kslot(std::integral_constant<int, 0>{}));
             load_gates(0, R2.la, R2.be);
         }
         __syncthreads();
-        if (nchunks > 0) prepare2(0, smem + PBUF, R2);
+        if (nchunks > 0) prepare2(0, smem, R2, std::integral_constant<int, 0>{});
         __syncthreads();
-        for (long c = 0; c < nchunks; ++c) {
-            if (c + 1 < nchunks) prepare2(c + 1, smem + PBUF + ((c + 1) & 1) * BUF, R2);
+        // unrolled by three so that every key slot index is a compile-time
+        // constant; one barrier per chunk as in the other waves
+        for (long c = 0; c < nchunks; c += 3) {
+            if (c + 1 < nchunks) prepare2(c + 1, smem + ((c + 1) & 1) * BUF, R2, std::integral_constant<int, 1>{});
             __syncthreads();
+            if (c + 1 < nchunks) {
+                if (c + 2 < nchunks) prepare2(c + 2, smem + ((c + 2) & 1) * BUF, R2, std::integral_constant<int, 2>{});
+                __syncthreads();
+            }
+            if (c + 2 < nchunks) {
+                if (c + 3 < nchunks) prepare2(c + 3, smem + ((c + 3) & 1) * BUF, R2, std::integral_constant<int, 0>{});
+                __syncthreads();
+            }
         }
     } else {
         Wave3Regs R3;
         if (nchunks > 0) load3(0, R3);
         __syncthreads();
-        if (nchunks > 0) prepare3(0, smem + PBUF, R3);
+        if (nchunks > 0) prepare3(0, smem, R3);
         __syncthreads();
         for (long c = 0; c < nchunks; ++c) {
-            if (c + 1 < nchunks) prepare3(c + 1, smem + PBUF + ((c + 1) & 1) * BUF, R3);
+            if (c + 1 < nchunks) prepare3(c + 1, smem + ((c + 1) & 1) * BUF, R3);
             __syncthreads();
         }
     }
