@@ -71,8 +71,9 @@ constexpr int B_SC = B_VT + DVT * VTS * 4;
 constexpr int BUF = B_SC + 4 * CH * 4;  // rsKS[64], rq[64], rk[64], gC
 constexpr int SCR = 2 * BUF;            // wave 2: four diagonal 16x16 blocks
 constexpr int SCR_STRIDE = 16 * 20 + 16;
-constexpr int GA = SCR + 4 * SCR_STRIDE * 4;  // wave 2: G2[64], sb[64]; wave 3: + sg[64]
-constexpr int LDS_BYTES = GA + 5 * CH * 4;
+constexpr int NGF = 7;                        // per-token factor arrays per helper
+constexpr int GA = SCR + 4 * SCR_STRIDE * 4;  // wave 2 and wave 3 factor arrays
+constexpr int LDS_BYTES = GA + 2 * NGF * CH * 4;
 static_assert(LDS_BYTES + 3 * KTILE <= 160 * 1024, "LDS budget");
 static_assert(B_PF % 16 == 0 && B_VT % 16 == 0 && BUF % 16 == 0, "LDS alignment");
 
@@ -551,7 +552,6 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
 
     // ============================= helper waves =============================
     const bool w2 = wave == NCHAIN;  // else wave 3
-    float* ga = reinterpret_cast<float*>(smem + GA) + (w2 ? 0 : 2 * CH);
 
     // Registers: both helpers hold their chunk-c gates while they prepare chunk
     // c, wave 3 also its chunk-c query rows and value tile; wave 2 fetches key
@@ -565,17 +565,22 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
     // Key tile of chunk c straight from HBM into its LDS slot (LDS DMA, no
     // registers): instruction m fills rows 4m .. 4m + 3, lane i landing at row
     // 4m + i / 16, physical 16-byte chunk i % 16, so it fetches the logical
-    // chunk that the tile swizzle puts there.
-    auto dma_keys = [&](long c, lds_u16* tile) {
+    // chunk that the tile swizzle puts there.  A buffer resource per head
+    // (records = T rows) makes rows past T read as zeros.  The swizzle of row
+    // r = 4m + i / 16 is f = 4 (r % 4) + (r / 4) % 4 = 4 (i / 16) + m % 4, so
+    // four per-lane offsets cover all m.
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(p.k + bh * p.T * DK), 0, static_cast<int>(p.T * DK * 2), 0x00020000);
+    unsigned koff[4];
 #pragma unroll
-        for (int m = 0; m < 16; ++m) {
-            const int r = 4 * m + (lane >> 4);
-            const int f = ((r & 3) << 2) | ((r >> 2) & 3);
-            const long t = min(c * CH + r, p.T - 1);
-            const uint16_t* src = p.k + (bh * p.T + t) * DK + 8 * ((lane & 15) ^ f);
-            __builtin_amdgcn_global_load_lds(static_cast<const void*>(src),
-                                             (__attribute__((address_space(3))) void*)(tile + 4 * m * DK), 16, 0, 0);
-        }
+    for (int q = 0; q < 4; ++q)
+        koff[q] = (lane >> 4) * DK * 2 + 16 * ((lane & 15) ^ (((lane >> 4) << 2) | q));
+    auto dma_keys = [&](long c, lds_u16* tile) {
+        const unsigned cb = static_cast<unsigned>(c * CH * DK * 2);
+#pragma unroll
+        for (int m = 0; m < 16; ++m)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)(tile + 4 * m * DK), 16,
+                                                     cb + m * 4 * DK * 2 + koff[m & 3], 0, 0, 0);
     };
     auto load3 = [&](long c, Wave3Regs& R3) {
         const long t0 = c * CH;
@@ -593,42 +598,52 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
         return *reinterpret_cast<const bf16x8*>(tile + kq_off(16 * b + ln, 32 * t + 8 * g));
     };
 
-    // Everything chunk c needs goes into `buf`; wave 2 additionally stages the
-    // key tile of chunk c + 1.  The gate prologue is the same for both waves.
+    // Per-token gates and decay factors of chunk c.  Lane r holds token r:
+    // inclusive cumulative log2 decay G_r (rows past T add nothing) and
+    // sb_r = sqrt(beta_r) (0 past T: no erase, no write).  The decay between
+    // two tokens of a chunk is split into a row and a column factor, each a
+    // power of two of one token's G relative to a reference, so that the
+    // Gram blocks need no per-element exponentials:
+    //   diagonal block R (reference Gm = G at row 16R + 7, |G_r - Gm| <= 115
+    //   by the per-token clamp): FA = [sb_r] 2^(G_r - Gm), FB = sb_s 2^(Gm - G_s);
+    //   off-diagonal R > J (reference Ge_J = G at row 16J + 15, both factors
+    //   <= 1): FE_J = [sb_r] 2^(G_r - Ge_J), FF = sb_s 2^(Ge_J - G_s) for s in J.
+    // Row factors carry sb_r only for T (wave 2), not for P (wave 3).
+    struct GateVals {
+        float gl, sb, G2last;
+    };
+    float* gw = reinterpret_cast<float*>(smem + GA) + (w2 ? 0 : NGF * CH);
+    enum { FA = 0, FB = CH, FF = 2 * CH, FE = 3 * CH, SG = 6 * CH };
+    auto gate_prologue = [&](long c, float la, float be, bool row_sb) {
+        GateVals v;
+        const bool ok = c * CH + lane < p.T;
+        v.gl = wave_incl_scan((p.has_alpha && ok) ? fmaxf(la, kLogAlphaMin) * kLog2e : 0.0f);
+        v.sb = ok ? sqrt_hw(be) : 0.0f;
+        auto at = [&](int r) {
+            return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v.gl), r));
+        };
+        v.G2last = at(63);
+        const float ge0 = at(15), ge1 = at(31), ge2 = at(47);
+        const float gm0 = at(7), gm1 = at(23), gm2 = at(39), gm3 = at(55);
+        const int R = lane >> 4;
+        const float gm = R == 0 ? gm0 : (R == 1 ? gm1 : (R == 2 ? gm2 : gm3));
+        const float geR = R == 0 ? ge0 : (R == 1 ? ge1 : ge2);  // unused for R == 3
+        const float rs = row_sb ? v.sb : 1.0f;
+        gw[FA + lane] = rs * ex2(v.gl - gm);
+        gw[FB + lane] = v.sb * ex2(gm - v.gl);
+        gw[FF + lane] = v.sb * ex2(fminf(geR - v.gl, 0.0f));
+        gw[FE + lane] = rs * ex2(fminf(v.gl - ge0, 0.0f));
+        gw[FE + CH + lane] = rs * ex2(fminf(v.gl - ge1, 0.0f));
+        gw[FE + 2 * CH + lane] = rs * ex2(fminf(v.gl - ge2, 0.0f));
+        return v;
+    };
+
+    // Everything chunk c needs goes into `buf`; wave 2 additionally fetches the
+    // key tile of chunk c + 1.
     auto prepare2 = [&](long c, char* buf, Wave2Regs& R2, auto slot) {
         const float la = R2.la, be = R2.be;
         const long t0 = c * CH;
-        // per-token gates: inclusive cumulative log2 decay and sqrt(beta);
-        // rows past T hold G and get sb = 0 (no erase, no write)
-        const bool ok = t0 + lane < p.T;
-        const float gl = wave_incl_scan((p.has_alpha && ok) ? fmaxf(la, kLogAlphaMin) * kLog2e : 0.0f);
-        const float sb = ok ? sqrt_hw(be) : 0.0f;
-        const float G2last =
-            __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gl), 63));
-        ga[lane] = gl;
-        ga[CH + lane] = sb;
-        // gate values at rows 16R + ln and at columns 16J + 4g + e
-        float Gr[4], sbr[4];
-        f32x4 Gs[4], sbs[4];
-#pragma unroll
-        for (int R = 0; R < 4; ++R) {
-            Gr[R] = ga[16 * R + ln];
-            sbr[R] = ga[CH + 16 * R + ln];
-            Gs[R] = *reinterpret_cast<const f32x4*>(ga + 16 * R + 4 * g);
-            sbs[R] = *reinterpret_cast<const f32x4*>(ga + CH + 16 * R + 4 * g);
-        }
-        // Off-diagonal blocks (row block R > column block J) split the decay at
-        // the last row of block J: exp2(G_r - G_s) = exp2(G_r - Ge_J) exp2(Ge_J - G_s),
-        // both factors <= 1.  cJ[J] holds sb_s exp2(Ge_J - G_s) for this lane's columns.
-        float Ge[3];
-        f32x4 cJ[3];
-#pragma unroll
-        for (int J = 0; J < 3; ++J) {
-            Ge[J] = ga[16 * J + 15];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) cJ[J][e] = sbs[J][e] * ex2(Ge[J] - Gs[J][e]);
-        }
-
+        const GateVals gv = gate_prologue(c, la, be, true);
         // ---- wave 2: fetch the next key tile, form T, invert the diagonal blocks ----
         // (unconditional: past the last chunk it refetches row T - 1 into a slot
         // that nothing reads any more, which keeps the destination a constant)
@@ -657,9 +672,7 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
         }
         float* scr = reinterpret_cast<float*>(smem + SCR);
         // tc[R][J] holds T[16R + 4g + e][16J + ln] for J < R (T_RJ in accumulator
-        // layout); diagonal blocks go to the scratch.  The off-diagonal decay is
-        // split at the last row of block J (Ge_J): the row factor
-        // sb_r exp2(G_r - Ge_J) varies with e, the column factor with the lane.
+        // layout); diagonal blocks (row ln, columns 4g + e) go to the scratch.
         f32x4 tc[4][4];
 #pragma unroll
         for (int R = 0; R < 4; ++R)
@@ -667,17 +680,14 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
             for (int J = 0; J <= R; ++J) {
                 f32x4 acc = tr[R][J];
                 if (J == R) {
+                    const f32x4 cf = *reinterpret_cast<const f32x4*>(gw + FB + 16 * R + 4 * g);
+                    const float rf = gw[FA + 16 * R + ln];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int s = 4 * g + e;
-                        acc[e] = (s < ln) ? acc[e] * sbr[R] * sbs[R][e] * ex2(Gr[R] - Gs[R][e]) : 0.0f;
-                    }
+                    for (int e = 0; e < 4; ++e) acc[e] = (4 * g + e < ln) ? acc[e] * rf * cf[e] : 0.0f;
                     *reinterpret_cast<f32x4*>(scr + R * SCR_STRIDE + ln * 20 + 4 * g) = acc;
                 } else {
-                    f32x4 rf;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) rf[e] = sbs[R][e] * ex2(Gs[R][e] - Ge[J]);
-                    tc[R][J] = acc * rf * (sbr[J] * ex2(Ge[J] - Gr[J]));
+                    const f32x4 rf = *reinterpret_cast<const f32x4*>(gw + FE + J * CH + 16 * R + 4 * g);
+                    tc[R][J] = acc * rf * gw[FF + 16 * J + ln];
                 }
             }
         // diagonal blocks: D_R = (I + T_RR)^-1 row by row, one row per lane
@@ -728,37 +738,7 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
     auto prepare3 = [&](long c, char* buf, Wave3Regs& R3) {
         const float la = R3.la, be = R3.be;
         const long t0 = c * CH;
-        // per-token gates: inclusive cumulative log2 decay and sqrt(beta);
-        // rows past T hold G and get sb = 0 (no erase, no write)
-        const bool ok = t0 + lane < p.T;
-        const float gl = wave_incl_scan((p.has_alpha && ok) ? fmaxf(la, kLogAlphaMin) * kLog2e : 0.0f);
-        const float sb = ok ? sqrt_hw(be) : 0.0f;
-        const float G2last =
-            __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gl), 63));
-        ga[lane] = gl;
-        ga[CH + lane] = sb;
-        // gate values at rows 16R + ln and at columns 16J + 4g + e
-        float Gr[4], sbr[4];
-        f32x4 Gs[4], sbs[4];
-#pragma unroll
-        for (int R = 0; R < 4; ++R) {
-            Gr[R] = ga[16 * R + ln];
-            sbr[R] = ga[CH + 16 * R + ln];
-            Gs[R] = *reinterpret_cast<const f32x4*>(ga + 16 * R + 4 * g);
-            sbs[R] = *reinterpret_cast<const f32x4*>(ga + CH + 16 * R + 4 * g);
-        }
-        // Off-diagonal blocks (row block R > column block J) split the decay at
-        // the last row of block J: exp2(G_r - G_s) = exp2(G_r - Ge_J) exp2(Ge_J - G_s),
-        // both factors <= 1.  cJ[J] holds sb_s exp2(Ge_J - G_s) for this lane's columns.
-        float Ge[3];
-        f32x4 cJ[3];
-#pragma unroll
-        for (int J = 0; J < 3; ++J) {
-            Ge[J] = ga[16 * J + 15];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) cJ[J][e] = sbs[J][e] * ex2(Ge[J] - Gs[J][e]);
-        }
-
+        const GateVals gv = gate_prologue(c, la, be, false);
         // ---- wave 3: form P, stage Q, V (transposed), row scales ----
         // raw query-key products (keys from the staged tile) first, so the
         // registers can be refilled
@@ -780,19 +760,19 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
         }
         stage_rows(R3.q, reinterpret_cast<uint16_t*>(buf + B_Q), ln, g);
         float* sc = reinterpret_cast<float*>(buf + B_SC);
-        const float eg = ex2(gl);
-        sc[lane] = sb * eg;                         // rows of K.Gamma
+        const float eg = ex2(gv.gl);
+        sc[lane] = gv.sb * eg;                      // rows of K.Gamma
         sc[CH + lane] = eg;                         // rows of Q.Gamma
-        sc[2 * CH + lane] = sb * ex2(G2last - gl);  // rows of Khat
-        if (lane == 0) sc[3 * CH] = ex2(G2last);    // chunk decay
+        sc[2 * CH + lane] = gv.sb * ex2(gv.G2last - gv.gl);  // rows of Khat
+        if (lane == 0) sc[3 * CH] = ex2(gv.G2last);          // chunk decay
         // value tile, transposed and scaled by sqrt(gamma): lane (q = ln, m = g)
         // holds tokens 4q .. 4q + 3 of columns 8m .. 8m + 7, one 16-byte write
         // per column; rows past T get 0
         float* sVt = reinterpret_cast<float*>(buf + B_VT);
         f32x4 sg4[8];
         if (!p.gvec) {
-            ga[2 * CH + lane] = ok ? sqrt_hw(R3.gam1) : 0.0f;
-            const f32x4 s4 = *reinterpret_cast<const f32x4*>(ga + 2 * CH + 4 * ln);
+            gw[SG + lane] = (c * CH + lane < p.T) ? sqrt_hw(R3.gam1) : 0.0f;
+            const f32x4 s4 = *reinterpret_cast<const f32x4*>(gw + SG + 4 * ln);
 #pragma unroll
             for (int cc = 0; cc < 8; ++cc) sg4[cc] = s4;
         } else {
@@ -819,13 +799,13 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
 #pragma unroll
             for (int S = 0; S <= R; ++S) {
                 if (S == R) {
+                    const f32x4 cf = *reinterpret_cast<const f32x4*>(gw + FB + 16 * R + 4 * g);
+                    const float rf = gw[FA + 16 * R + ln];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int s = 4 * g + e;
-                        pb[R][S][e] = (s <= ln) ? pb[R][S][e] * sbs[S][e] * ex2(Gr[R] - Gs[S][e]) : 0.0f;
-                    }
+                    for (int e = 0; e < 4; ++e) pb[R][S][e] = (4 * g + e <= ln) ? pb[R][S][e] * rf * cf[e] : 0.0f;
                 } else {
-                    pb[R][S] = pb[R][S] * ex2(Gr[R] - Ge[S]) * cJ[S];
+                    const f32x4 cf = *reinterpret_cast<const f32x4*>(gw + FF + 16 * S + 4 * g);
+                    pb[R][S] = pb[R][S] * (gw[FE + S * CH + 16 * R + ln] * cf);
                 }
             }
         char* pf = buf + B_PF;
@@ -882,7 +862,9 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
 }  // namespace
 
 bool chunk_fact_supported(const pdn_chunk_fwd_args& a) {
+    // key rows of one head are addressed with 32-bit byte offsets
     return a.qkv_dtype == PDN_BF16 && a.dk == DK && a.dv % DVT == 0 &&
+           static_cast<long>(a.T) * DK * 2 <= 0x7fffffffL &&
            a.alpha_mode != PDN_ALPHA_VEC && a.beta_mode == PDN_GATE_SCALAR &&
            a.precond_eps < 0.0f;
 }
