@@ -131,18 +131,16 @@ __device__ __forceinline__ int f16_off(int s, int plane, int lane) {
     return TF16 + ((s * 2 + plane) * 64 + lane) * 8;
 }
 
-template <int NT>
-__device__ __forceinline__ void split8(const float* x, bf16x8 (&o)[NT]) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        float r = x[e];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const bf16 h = static_cast<bf16>(r);
-            o[t][e] = h;
-            if (t + 1 < NT) r -= static_cast<float>(h);
-        }
-    }
+typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// hi/lo bf16 split of two values, as packed words: hi = RNE(x), lo = RNE(x - hi).
+// One packed conversion gives both hi halves; they are widened back with a
+// shift and a mask, so the split costs three operations per value.
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+    hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+    const float ah = __builtin_bit_cast(float, hi << 16);
+    const float bh = __builtin_bit_cast(float, hi & 0xffff0000u);
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a - ah, b - bh}, bf16x2));
 }
 
 __device__ __forceinline__ f32x4 mfma32(const bf16x8& a, const bf16x8& b, f32x4 c) {
@@ -156,9 +154,16 @@ __device__ __forceinline__ f32x4 mm22(const bf16x8 (&a)[2], const bf16x8 (&b)[2]
     return mfma32(a[0], b[0], c);
 }
 
+// hi/lo split of two accumulator blocks stacked as one 16x16x32 operand
+// (elements lo4[0..3], hi4[0..3])
 __device__ __forceinline__ void split_pair(const f32x4& lo4, const f32x4& hi4, bf16x8 (&o)[2]) {
-    float x[8] = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-    split8<2>(x, o);
+    uint4 h, l;
+    split2(lo4[0], lo4[1], h.x, l.x);
+    split2(lo4[2], lo4[3], h.y, l.y);
+    split2(hi4[0], hi4[1], h.z, l.z);
+    split2(hi4[2], hi4[3], h.w, l.w);
+    o[0] = __builtin_bit_cast(bf16x8, h);
+    o[1] = __builtin_bit_cast(bf16x8, l);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8, u); }
@@ -188,12 +193,11 @@ __device__ __forceinline__ f32x4 mm22x16(const bf16x4 (&a)[2], const bf16x4 (&b)
 }
 // hi/lo split of an accumulator block used as a 16x16x16 B operand
 __device__ __forceinline__ void split_d(const f32x4& v, bf16x4 (&o)[2]) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const bf16 h = static_cast<bf16>(v[e]);
-        o[0][e] = h;
-        o[1][e] = static_cast<bf16>(v[e] - static_cast<float>(h));
-    }
+    uint2 h, l;
+    split2(v[0], v[1], h.x, l.x);
+    split2(v[2], v[3], h.y, l.y);
+    o[0] = __builtin_bit_cast(bf16x4, h);
+    o[1] = __builtin_bit_cast(bf16x4, l);
 }
 // two 16x16x16 B operands stacked along k into one 16x16x32 B operand
 __device__ __forceinline__ bf16x8 cat4(const bf16x4& a, const bf16x4& b) {
@@ -313,7 +317,7 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
     __shared__ __attribute__((aligned(16))) uint16_t ks2[CH * DK];
     __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
     auto ktile = [&](long c) -> uint16_t* {
-        const long m = c % 3;
+        const unsigned m = static_cast<unsigned>(c) % 3u;
         return m == 0 ? ks0 : (m == 1 ? ks1 : ks2);
     };
     // slot S as an LDS-typed pointer (S known at compile time)
@@ -371,6 +375,13 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
             const float* sVt = reinterpret_cast<const float*>(cur + B_VT) + (16 * wave + ln) * VTS;
             const long t0 = c * CH;
 
+            // key rows for Y first: their LDS latency overlaps the state split
+            bf16x8 ka[4][4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    ka[t][b] = *reinterpret_cast<const bf16x8*>(sK + kq_off(16 * b + ln, 32 * t + 8 * g));
             // state as x32 B operands (k = key channel)
             bf16x8 bS[4][2];
 #pragma unroll
@@ -404,7 +415,12 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
                 z[a] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
 #pragma unroll
-            for (int t = 0; t < 4; ++t) rows_x_state(sK, false, t, y);
+            for (int t = 0; t < 4; ++t) {
+#pragma unroll
+                for (int b = 0; b < 4; ++b) y[b] = mfma32(ka[t][b], bS[t][1], y[b]);
+#pragma unroll
+                for (int b = 0; b < 4; ++b) y[b] = mfma32(ka[t][b], bS[t][0], y[b]);
+            }
             // X = Vt - diag(sb Gamma) Y
             f32x4 x[4];
 #pragma unroll
