@@ -173,15 +173,6 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) { return __builtin_b
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float sqrt_hw(float x) { return __builtin_amdgcn_sqrtf(x); }
 
-// acc += X^T Y for 16x16 fp32 blocks X, Y in accumulator layout (lane (ln, g)
-// element e holds row 4g + e, column ln).  Element e of every lane forms the
-// k-slice {4g + e}, so four 16x16x4 fp32 MFMAs give the product in fp32.
-__device__ __forceinline__ f32x4 mm_t(const f32x4& x, const f32x4& y, f32x4 c) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(x[e], y[e], c, 0, 0, 0);
-    return c;
-}
-
 __device__ __forceinline__ f32x4 mfma16(const bf16x4& a, const bf16x4& b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
@@ -730,22 +721,28 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
                 *reinterpret_cast<f32x4*>(Brow + 4 * q) = f32x4{x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]};
         }
         // N_RJ = D_R T_RJ.  With tc = T_RJ and drow(R) = D_R^T in accumulator
-        // layout, mm_t gives (D_R T_RJ)^T in accumulator layout: lane (ln, g)
-        // holds row ln, columns 4g .. 4g + 3 of N_RJ, which is its A-operand
-        // fragment.  The same holds for drow(R) and D_R.
-        f32x4 drow[4];
+        // layout, an MFMA with the T block as the A operand (a register block
+        // used as A acts as its transpose) gives (D_R T_RJ)^T in accumulator
+        // layout: lane (ln, g) holds row ln, columns 4g .. 4g + 3 of N_RJ,
+        // which is its A-operand fragment.  The same holds for drow(R) and D_R.
+        char* tf = buf + B_TF;
+        bf16x4 bd[4][2];
 #pragma unroll
-        for (int R = 0; R < 4; ++R)
-            drow[R] = *reinterpret_cast<const f32x4*>(scr + R * SCR_STRIDE + ln * 20 + 4 * g);
+        for (int R = 0; R < 4; ++R) {
+            split_d(*reinterpret_cast<const f32x4*>(scr + R * SCR_STRIDE + ln * 20 + 4 * g), bd[R]);
+            *reinterpret_cast<bf16x4*>(tf + f16_off(F16_D0 + R, 0, lane)) = bd[R][0];
+            *reinterpret_cast<bf16x4*>(tf + f16_off(F16_D0 + R, 1, lane)) = bd[R][1];
+        }
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
         f32x4 nb[4][4];
 #pragma unroll
         for (int R = 1; R < 4; ++R)
 #pragma unroll
-            for (int J = 0; J < R; ++J) nb[R][J] = -mm_t(tc[R][J], drow[R], zero);
-        char* tf = buf + B_TF;
-#pragma unroll
-        for (int R = 0; R < 4; ++R) put_f16(tf, F16_D0 + R, lane, drow[R]);
+            for (int J = 0; J < R; ++J) {
+                bf16x4 bt[2];
+                split_d(-tc[R][J], bt);
+                nb[R][J] = mm22x16(bt, bd[R], zero);
+            }
         put_f16(tf, F16_N10, lane, nb[1][0]);
         put_f16(tf, F16_N32, lane, nb[3][2]);
         put_f32(tf, F32_N2, lane, nb[2][0], nb[2][1]);
