@@ -445,12 +445,8 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
             }
             u[0] = W[0];
             split_d(u[0], bu[0]);
-            // Z = Q S does not depend on the solve: its k-steps fill the gaps
-            // between the dependent solve steps
-            rows_x_state(sQ, true, 0, z);
             a16(F16_N10, a4);
             u[1] = mm22x16(a4, bu[0], W[1]);
-            rows_x_state(sQ, true, 1, z);
             split_d(u[1], bu[1]);
             bf16x8 bU[2][2];
             bU[0][0] = cat4(bu[0][0], bu[1][0]);
@@ -459,11 +455,9 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
             u[2] = mm22(a8, bU[0], W[2]);
             a32(F32_N3, a8);
             f32x4 w3 = mm22(a8, bU[0], W[3]);
-            rows_x_state(sQ, true, 2, z);
             split_d(u[2], bu[2]);
             a16(F16_N32, a4);
             u[3] = mm22x16(a4, bu[2], w3);
-            rows_x_state(sQ, true, 3, z);
             split_d(u[3], bu[3]);
             bU[1][0] = cat4(bu[2][0], bu[3][0]);
             bU[1][1] = cat4(bu[2][1], bu[3][1]);
@@ -504,6 +498,11 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
 #pragma unroll
                 for (int ib = 0; ib < 8; ++ib) sacc[ib] = mfma32(ak[ib], bUs[t][0], sacc[ib]);
             }
+
+            // Z = Q S with the state of the chunk start (bS): off the recurrence's
+            // critical path, so it is issued after the state update
+#pragma unroll
+            for (int t = 0; t < 4; ++t) rows_x_state(sQ, true, t, z);
 
             // O = diag(Gamma) Z + P U, transposed: with U as the A operand and the P
             // fragments as the B operand, lane (ln, g) ends up with row 16R + ln,
