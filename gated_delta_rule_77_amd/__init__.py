@@ -217,10 +217,25 @@ def pdn_chunk_fwd(q, k, v, o, log_alpha=None, beta=None, gamma=None, precond_eps
     [B,H,T,dk]; beta [B,H,T] / [B,H,T,dk]; gamma None (same as beta) / [B,H,T]
     / [B,H,T,dv].  o (float32 or bfloat16) receives the output; ST and
     precond_AT, when given, receive the final state and running k(.)k sum.
+    workspace: a device tensor of at least pdn_chunk_fwd_workspace_size() bytes.
+    When None and the call needs one, it is allocated here with torch's caching
+    allocator, whose stream-ordered reuse makes that safe on torch's current
+    stream; pass one explicitly when launching on another stream.
     """
     a = _chunk_args(q, k, v, o, log_alpha, beta, gamma, precond_eps, precond_A0,
                     precond_AT, S0, ST, workspace)
-    rc = load_library().pdn_chunk_fwd(ctypes.byref(a), _stream(stream))
+    lib = load_library()
+    if workspace is None:
+        n = ctypes.c_size_t(0)
+        rc = lib.pdn_chunk_fwd_workspace_size(ctypes.byref(a), ctypes.byref(n))
+        if rc != PDN_OK:
+            raise PdnError(rc, "pdn_chunk_fwd_workspace_size")
+        if n.value:
+            import torch
+            workspace = torch.empty(int(n.value), dtype=torch.uint8, device=q.device)
+            a.workspace = _ptr(workspace)
+            a.workspace_bytes = int(n.value)
+    rc = lib.pdn_chunk_fwd(ctypes.byref(a), _stream(stream))
     if rc != PDN_OK:
         raise PdnError(rc, "pdn_chunk_fwd")
 

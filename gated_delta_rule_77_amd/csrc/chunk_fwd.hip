@@ -873,10 +873,14 @@ int choose_nw(long nbh, int dv, bool vec, bool f32in) {
 
 }  // namespace
 
-size_t chunk_fwd_workspace_bytes(const pdn_chunk_fwd_args&) { return 0; }
+size_t chunk_fwd_workspace_bytes(const pdn_chunk_fwd_args& a) {
+    if (a.T > 0 && !chunk_fact_supported(a) && chunk_vec_supported(a)) return chunk_vec_workspace_bytes(a);
+    return 0;
+}
 
 hipError_t launch_chunk_fwd(const pdn_chunk_fwd_args& a, hipStream_t stream) {
     if (a.T > 0 && chunk_fact_supported(a)) return launch_chunk_fact(a, stream);
+    if (a.T > 0 && chunk_vec_supported(a)) return launch_chunk_vec(a, stream);
     ChunkParams p;
     p.q = a.q; p.k = a.k; p.v = a.v;
     p.log_alpha = a.log_alpha; p.beta = a.beta;

@@ -1,0 +1,789 @@
+// Prefill for per-channel decay and gains and the diagonal preconditioner
+// (KDA / FG^2-GDN / Gated DeltaNet-2 gating), bf16 q/k/v, dk = 128.
+//
+// Chunk algebra over 32-token chunks ("Gated DeltaNet-2" method section 3:
+// the cumulative decay goes into the erase/write matrices and each chunk
+// solves one unit-lower-triangular system; "FG^2-GDN" 2.3: the transition is
+// diagonal plus low rank).  With G_ri the cumulative log2 decay of channel i
+// from the chunk start, Gamma = 2^G, kt_r = sqrt(beta'_r) (.) k_r and
+// vt_r = sqrt(gamma_r) (.) v_r:
+//
+//   T_rs = sum_i kt_ri kt_si 2^(G_ri - G_si)          s < r
+//   P_rs = sum_i q_ri  kt_si 2^(G_ri - G_si)          s <= r
+//   U    = (I + T)^-1 (Vt - (Kt . Gamma) S)
+//   O    = (Q . Gamma) S + P U
+//   S   <- Diag(Gamma_31) S + (Kt . 2^(G_31 - G))^T U
+//
+// Everything that depends only on q, k and the gates is independent across
+// chunks, so it runs first, fully parallel over (b, h, chunk):
+//
+//   vec_prep_kernel (one wave per chunk) forms the gate-scaled operands
+//     Kg = Kt . Gamma, Qg = Q . Gamma, Kd = Kt . 2^(G_31 - G), the blocks of T
+//     and P (fp32 MFMAs), the inverses D_R = (I + T_RR)^-1 of the two 16x16
+//     diagonal blocks and N = D_1 T_10, and writes them as one chunk record
+//     to the workspace: bf16 hi/lo tiles and MFMA fragments laid out exactly
+//     as the chain kernel's LDS expects them.
+//
+//   vec_chain_kernel carries the state: one workgroup per (b, h, 32 value
+//     columns); waves 0-1 hold 16 state columns each in registers and run
+//     the sequential part (KS, the block solve U_0 = D_0 X_0,
+//     U_1 = D_1 X_1 - N U_0, QS, PU, the state update), wave 2 copies the
+//     next chunk's record from HBM into LDS by DMA, wave 3 stages the
+//     gain-scaled value tile.  One barrier per chunk.
+//
+// The per-channel decay inside a 16-token block is split around the block's
+// middle token (2^(G_r - Gm) 2^(Gm - G_s)); the per-token clamp of
+// log(alpha) at -10 keeps both factors below 2^116.  Between the two blocks
+// the split is at the last token of block 0, where both factors are <= 1.
+//
+// With the preconditioner, beta'_t = beta_t / (A_t + eps) with the running
+// sum A_t = A_0 + sum_{s<=t} k_s (.) k_s ("Preconditioned DeltaNet" 2.2):
+// vec_ksq_kernel sums k (.) k per chunk and vec_kscan_kernel turns the sums
+// into the value of A before every chunk (and A_T).
+#include "chunk_tile.h"
+#include "kernels.h"
+
+namespace pdn {
+namespace {
+
+using namespace tile;
+
+constexpr int VC = 32;  // tokens per chunk
+constexpr int NCHAIN = 2;
+constexpr int NTHR = 64 * (NCHAIN + 2);
+constexpr int DVT = 16 * NCHAIN;
+constexpr int VTS = VC + 4;  // row stride of the transposed value tile (floats)
+
+// Chunk record (bytes).  Six bf16 [32][128] tiles with the swizzle of kq_off:
+// hi and lo terms of Kg, Qg, Kd.  Then the solve fragments (16x16x16 A
+// operands, 8 bytes per lane and term): D_0, D_1, -N; the P fragments
+// (16x16x32 B operands for row blocks 0 and 1, 16 bytes per lane and term);
+// and Gamma_31 per channel (fp32).  Padded to whole KiB for the DMA.
+constexpr int TILEB = VC * DK * 2;
+constexpr int R_KGH = 0;
+constexpr int R_KGL = TILEB;
+constexpr int R_QGH = 2 * TILEB;
+constexpr int R_QGL = 3 * TILEB;
+constexpr int R_KDH = 4 * TILEB;
+constexpr int R_KDL = 5 * TILEB;
+constexpr int R_F16 = 6 * TILEB;
+constexpr int R_PF = R_F16 + 3 * 2 * 64 * 8;
+constexpr int R_GC = R_PF + 2 * 2 * 64 * 16;
+constexpr int REC = (R_GC + DK * 4 + 1023) / 1024 * 1024;
+enum { F16_D0 = 0, F16_D1 = 1, F16_N10 = 2 };
+
+__device__ __forceinline__ int f16_off(int s, int plane, int lane) { return R_F16 + ((s * 2 + plane) * 64 + lane) * 8; }
+__device__ __forceinline__ int pf_off(int R, int plane, int lane) { return R_PF + ((R * 2 + plane) * 64 + lane) * 16; }
+
+// Chain kernel LDS: two buffers, each a record image followed by the value
+// tile transposed (fp32 [32 columns][VTS]).
+constexpr int B_VT = REC;
+constexpr int BUFV = REC + DVT * VTS * 4;
+constexpr int LDS_CHAIN = 2 * BUFV;
+static_assert(LDS_CHAIN <= 160 * 1024, "LDS budget");
+static_assert(REC % 1024 == 0 && BUFV % 16 == 0, "record alignment");
+
+// Preparation kernel: scratch for the two diagonal blocks of each wave.
+constexpr int SCR_STRIDE = 16 * 20 + 16;
+
+struct PrepParams {
+    const uint16_t* q;
+    const uint16_t* k;
+    const float* log_alpha;  // may be null when there is no decay
+    const float* beta;
+    const float* astart;     // [BH][nc][DK] running k.k sum before each chunk
+    char* rec;               // [BH][nc] records
+    long T;
+    long nc;
+    long nbh;
+    float eps;
+    int has_alpha;
+};
+
+struct ChainParams {
+    const uint16_t* v;
+    const char* rec;
+    const float* gsrc;
+    long gts;
+    int gvec;
+    const float* S0;
+    float* ST;
+    void* o;
+    long T;
+    long nc;
+    int dv;
+    int o_bf16;
+};
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+// Element j (0..7) of eight packed bf16 values.
+__device__ __forceinline__ float bf16_at(const uint4& u, int j) {
+    const uint32_t w = j < 2 ? u.x : (j < 4 ? u.y : (j < 6 ? u.z : u.w));
+    return (j & 1) ? bf16_hi(w) : bf16_lo(w);
+}
+
+// hi/lo split of eight values into two 16-byte words
+__device__ __forceinline__ void split8(const float (&x)[8], uint4& h, uint4& l) {
+    split2(x[0], x[1], h.x, l.x);
+    split2(x[2], x[3], h.y, l.y);
+    split2(x[4], x[5], h.z, l.z);
+    split2(x[6], x[7], h.w, l.w);
+}
+
+// Decay factors of one channel (or of a scalar decay) for the two tokens a
+// lane holds: token ln of block 0 and token 16 + ln of block 1.  lg0 / lg1 are
+// the clamped log2 decays of those tokens; the scans run along the 16 tokens
+// of a DPP row.
+struct Decay {
+    float e0, ei0, e1, ei1;  // 2^(G - Gm) and 2^(Gm - G) around each block's middle token
+    float f0;                // block 0: 2^(G_15 - G)
+    float f1;                // block 1: 2^(G - G_15)
+    float gm0, gm1;          // Gamma = 2^G
+    float kd0, kd1;          // 2^(G_31 - G)
+    float gc;                // 2^(G_31), the chunk decay
+};
+
+__device__ __forceinline__ Decay decay_factors(float lg0, float lg1) {
+    Decay d;
+    const float G0 = row_incl_scan(lg0);
+    const float G15 = row_bcast<15>(G0);
+    const float G1 = row_incl_scan(lg1) + G15;
+    const float Gm0 = row_bcast<7>(G0);
+    const float Gm1 = row_bcast<7>(G1);
+    const float G31 = row_bcast<15>(G1);
+    d.e0 = ex2(G0 - Gm0);
+    d.ei0 = ex2(Gm0 - G0);
+    d.e1 = ex2(G1 - Gm1);
+    d.ei1 = ex2(Gm1 - G1);
+    d.f0 = ex2(G15 - G0);
+    d.f1 = ex2(G1 - G15);
+    d.gm0 = ex2(G0);
+    const float g15 = row_bcast<15>(d.gm0);   // 2^G_15
+    const float d15 = row_bcast<15>(d.f1);    // 2^(G_31 - G_15)
+    d.gm1 = d.f1 * g15;
+    d.kd0 = d.f0 * d15;
+    d.kd1 = ex2(G31 - G1);
+    d.gc = d15 * g15;
+    return d;
+}
+
+// ---------------------------------------------------------------------------
+// preconditioner pre-pass
+// ---------------------------------------------------------------------------
+
+// Sum of k (.) k over each chunk: one workgroup per (b, h, chunk), one thread
+// per channel.
+__global__ void __launch_bounds__(DK) vec_ksq_kernel(const uint16_t* k, float* ks, long T, long nc) {
+    const long id = blockIdx.x;
+    const long bh = id / nc;
+    const long t0 = (id % nc) * VC;
+    const int i = threadIdx.x;
+    float s = 0.0f;
+    for (int r = 0; r < VC; ++r) {
+        const long t = t0 + r;
+        if (t < T) {
+            const float x = bf16_bits_to_f32(k[(bh * T + t) * DK + i]);
+            s = fmaf(x, x, s);
+        }
+    }
+    ks[id * DK + i] = s;
+}
+
+// Exclusive running sum over the chunks of each (b, h), in place, starting
+// from A0; the total goes to AT.
+__global__ void __launch_bounds__(DK) vec_kscan_kernel(float* ks, const float* A0, float* AT, long nc) {
+    const long bh = blockIdx.x;
+    const int i = threadIdx.x;
+    float run = A0 ? A0[bh * DK + i] : 0.0f;
+    float* col = ks + bh * nc * DK + i;
+    long c = 0;
+    for (; c + 8 <= nc; c += 8) {
+        float s[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s[u] = col[(c + u) * DK];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            col[(c + u) * DK] = run;
+            run += s[u];
+        }
+    }
+    for (; c < nc; ++c) {
+        const float s = col[c * DK];
+        col[c * DK] = run;
+        run += s;
+    }
+    if (AT) AT[bh * DK + i] = run;
+}
+
+// ---------------------------------------------------------------------------
+// preparation: one wave per (b, h, chunk)
+// ---------------------------------------------------------------------------
+
+// Lane (ln, g) holds tokens ln (block 0) and 16 + ln (block 1) and, in k-step
+// t, the channels 32t + 8g .. 32t + 8g + 7: the MFMA operand layout, so the
+// Gram blocks are formed straight from registers with 16x16x4 fp32 MFMAs
+// (k-slot g of MFMA (t, j) is channel 32t + 8g + j).  Results in accumulator
+// layout (lane (ln, g) holds rows 4g + e, column ln):
+//   T_RR with A = Kt 2^(Gm - G) rows, B = Kt 2^(G - Gm) rows gives T_RR^T, i.e.
+//     lane (ln, g) holds row ln, columns 4g + e of T_RR;
+//   T_10 with A = block-1 rows 2^(G - G_15), B = block-0 rows 2^(G_15 - G);
+//   P_RS with A = block-S key rows, B = block-R query rows gives P_RS^T.
+template <bool AVEC, bool BVEC, bool PRE>
+__global__ void __launch_bounds__(256) vec_prep_kernel(PrepParams p) {
+    __shared__ __attribute__((aligned(16))) float scr_all[4][2 * SCR_STRIDE];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int g = lane >> 4;
+    const int ln = lane & 15;
+    const long id = blockIdx.x * 4L + wave;
+    if (id >= p.nbh * p.nc) return;
+    const long bh = id / p.nc;
+    const long c = id % p.nc;
+    char* rec = p.rec + id * REC;
+    float* scr = scr_all[wave];
+
+    long row[2];
+    bool ok[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        const long t = c * VC + 16 * b + ln;
+        ok[b] = t < p.T;
+        row[b] = bh * p.T + min(t, p.T - 1);
+    }
+    // per-token (scalar) gates
+    float lgs[2] = {0.0f, 0.0f}, bes[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        if (!AVEC && p.has_alpha && ok[b]) lgs[b] = fmaxf(p.log_alpha[row[b]], kLogAlphaMin) * kLog2e;
+        if (!BVEC && ok[b]) bes[b] = p.beta[row[b]];
+    }
+    Decay ds;
+    if constexpr (!AVEC) ds = decay_factors(lgs[0], lgs[1]);
+    float sbs[2] = {0.0f, 0.0f};
+    if constexpr (!BVEC && !PRE) {
+        sbs[0] = sqrt_hw(bes[0]);
+        sbs[1] = sqrt_hw(bes[1]);
+    }
+
+    f32x4 t00 = {0.f, 0.f, 0.f, 0.f}, t11 = t00, t10 = t00, p00 = t00, p11 = t00, p10 = t00;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int cb = 32 * t + 8 * g;  // this lane's first channel in k-step t
+        uint4 kr[2], qr[2];
+        float la[2][8], be[2][8], as[8];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            kr[b] = *reinterpret_cast<const uint4*>(p.k + row[b] * DK + cb);
+            qr[b] = *reinterpret_cast<const uint4*>(p.q + row[b] * DK + cb);
+            if constexpr (AVEC) {
+                const f32x4 a0 = *reinterpret_cast<const f32x4*>(p.log_alpha + row[b] * DK + cb);
+                const f32x4 a1 = *reinterpret_cast<const f32x4*>(p.log_alpha + row[b] * DK + cb + 4);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    la[b][j] = a0[j];
+                    la[b][4 + j] = a1[j];
+                }
+            }
+            if constexpr (BVEC) {
+                const f32x4 b0 = *reinterpret_cast<const f32x4*>(p.beta + row[b] * DK + cb);
+                const f32x4 b1 = *reinterpret_cast<const f32x4*>(p.beta + row[b] * DK + cb + 4);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    be[b][j] = b0[j];
+                    be[b][4 + j] = b1[j];
+                }
+            }
+        }
+        if constexpr (PRE) {
+            const float* ap = p.astart + id * DK + cb;
+            const f32x4 a0 = *reinterpret_cast<const f32x4*>(ap);
+            const f32x4 a1 = *reinterpret_cast<const f32x4*>(ap + 4);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                as[j] = a0[j];
+                as[4 + j] = a1[j];
+            }
+        }
+        float kg[2][8], qg[2][8], kd[2][8], gcv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float k0 = ok[0] ? bf16_at(kr[0], j) : 0.0f;
+            const float k1 = ok[1] ? bf16_at(kr[1], j) : 0.0f;
+            const float q0 = ok[0] ? bf16_at(qr[0], j) : 0.0f;
+            const float q1 = ok[1] ? bf16_at(qr[1], j) : 0.0f;
+            Decay d;
+            if constexpr (AVEC) {
+                const float l0 = (p.has_alpha && ok[0]) ? fmaxf(la[0][j], kLogAlphaMin) * kLog2e : 0.0f;
+                const float l1 = (p.has_alpha && ok[1]) ? fmaxf(la[1][j], kLogAlphaMin) * kLog2e : 0.0f;
+                d = decay_factors(l0, l1);
+            } else {
+                d = ds;
+            }
+            float sb0, sb1;
+            if constexpr (BVEC || PRE) {
+                float b0 = BVEC ? (ok[0] ? be[0][j] : 0.0f) : bes[0];
+                float b1 = BVEC ? (ok[1] ? be[1][j] : 0.0f) : bes[1];
+                if constexpr (PRE) {
+                    const float a0 = row_incl_scan(k0 * k0) + as[j];
+                    const float a1 = row_incl_scan(k1 * k1) + row_bcast<15>(a0);
+                    b0 *= __builtin_amdgcn_rcpf(a0 + p.eps);
+                    b1 *= __builtin_amdgcn_rcpf(a1 + p.eps);
+                }
+                sb0 = sqrt_hw(b0);
+                sb1 = sqrt_hw(b1);
+            } else {
+                sb0 = sbs[0];
+                sb1 = sbs[1];
+            }
+            const float kt0 = sb0 * k0, kt1 = sb1 * k1;
+            kg[0][j] = kt0 * d.gm0;
+            kg[1][j] = kt1 * d.gm1;
+            qg[0][j] = q0 * d.gm0;
+            qg[1][j] = q1 * d.gm1;
+            kd[0][j] = kt0 * d.kd0;
+            kd[1][j] = kt1 * d.kd1;
+            gcv[j] = d.gc;
+            const float bd0 = kt0 * d.ei0, bd1 = kt1 * d.ei1;
+            const float bo = kt0 * d.f0;
+            t00 = mfma4(bd0, kt0 * d.e0, t00);
+            p00 = mfma4(bd0, q0 * d.e0, p00);
+            t11 = mfma4(bd1, kt1 * d.e1, t11);
+            p11 = mfma4(bd1, q1 * d.e1, p11);
+            t10 = mfma4(kt1 * d.f1, bo, t10);
+            p10 = mfma4(bo, q1 * d.f1, p10);
+        }
+        // gate-scaled operand rows for the chain, hi/lo, into the swizzled tiles
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const int off = 2 * kq_off(16 * b + ln, cb);
+            uint4 h, l;
+            split8(kg[b], h, l);
+            *reinterpret_cast<uint4*>(rec + R_KGH + off) = h;
+            *reinterpret_cast<uint4*>(rec + R_KGL + off) = l;
+            split8(qg[b], h, l);
+            *reinterpret_cast<uint4*>(rec + R_QGH + off) = h;
+            *reinterpret_cast<uint4*>(rec + R_QGL + off) = l;
+            split8(kd[b], h, l);
+            *reinterpret_cast<uint4*>(rec + R_KDH + off) = h;
+            *reinterpret_cast<uint4*>(rec + R_KDL + off) = l;
+        }
+        if (ln == 0) {
+            float* gc = reinterpret_cast<float*>(rec + R_GC) + cb;
+            *reinterpret_cast<f32x4*>(gc) = f32x4{gcv[0], gcv[1], gcv[2], gcv[3]};
+            *reinterpret_cast<f32x4*>(gc + 4) = f32x4{gcv[4], gcv[5], gcv[6], gcv[7]};
+        }
+    }
+
+    // strictly lower part of the diagonal T blocks (row ln, columns 4g + e) to
+    // the scratch; the upper part may hold overflowed products and is dropped
+#pragma unroll
+    for (int R = 0; R < 2; ++R) {
+        f32x4 acc = R == 0 ? t00 : t11;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = (4 * g + e < ln) ? acc[e] : 0.0f;
+        *reinterpret_cast<f32x4*>(scr + R * SCR_STRIDE + ln * 20 + 4 * g) = acc;
+    }
+    // D_R = (I + T_RR)^-1, one row per lane; lanes 32..63 repeat lanes 0..31
+    {
+        float* Brow = scr + ((lane >> 4) & 1) * SCR_STRIDE + ln * 20;
+        float ntr[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(Brow + 4 * q);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ntr[4 * q + e] = -v[e];
+        }
+        float x[16];
+#pragma unroll
+        for (int cc = 0; cc < 16; ++cc) x[cc] = (cc == ln) ? 1.0f : 0.0f;
+        block_row_solve(x, ntr);
+        if (lane < 32) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<f32x4*>(Brow + 4 * q) = f32x4{x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]};
+        }
+    }
+    // D fragments; -N = -D_1 T_10 with the T block as the A operand (a register
+    // block used as A acts as its transpose), which leaves lane (ln, g) with
+    // row ln, columns 4g .. 4g + 3 of -N: its A-operand fragment
+    bf16x4 bd[2][2];
+#pragma unroll
+    for (int R = 0; R < 2; ++R) {
+        split_d(*reinterpret_cast<const f32x4*>(scr + R * SCR_STRIDE + ln * 20 + 4 * g), bd[R]);
+        *reinterpret_cast<bf16x4*>(rec + f16_off(F16_D0 + R, 0, lane)) = bd[R][0];
+        *reinterpret_cast<bf16x4*>(rec + f16_off(F16_D0 + R, 1, lane)) = bd[R][1];
+    }
+    {
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        bf16x4 bt[2];
+        split_d(-t10, bt);
+        const f32x4 nb = mm22x16(bt, bd[1], zero);
+        bf16x4 h[2];
+        split_d(nb, h);
+        *reinterpret_cast<bf16x4*>(rec + f16_off(F16_N10, 0, lane)) = h[0];
+        *reinterpret_cast<bf16x4*>(rec + f16_off(F16_N10, 1, lane)) = h[1];
+    }
+    // P fragments: lane (ln, g) holds P[16R + ln][4g + e] (block 0 columns) and
+    // P[16R + ln][16 + 4g + e] (block 1 columns), the 16x16x32 B operand of
+    // row block R
+    {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            p00[e] = (4 * g + e <= ln) ? p00[e] : 0.0f;
+            p11[e] = (4 * g + e <= ln) ? p11[e] : 0.0f;
+        }
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        bf16x8 h[2];
+        split_pair(p00, zero, h);
+        *reinterpret_cast<bf16x8*>(rec + pf_off(0, 0, lane)) = h[0];
+        *reinterpret_cast<bf16x8*>(rec + pf_off(0, 1, lane)) = h[1];
+        split_pair(p10, p11, h);
+        *reinterpret_cast<bf16x8*>(rec + pf_off(1, 0, lane)) = h[0];
+        *reinterpret_cast<bf16x8*>(rec + pf_off(1, 1, lane)) = h[1];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// the chain
+// ---------------------------------------------------------------------------
+
+__global__ void __launch_bounds__(NTHR) vec_chain_kernel(ChainParams p) {
+    __shared__ __attribute__((aligned(16))) char smem[LDS_CHAIN];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int g = lane >> 4;
+    const int ln = lane & 15;
+    const int ntile = p.dv / DVT;
+    // all column tiles of a head on one XCD (when the head count allows), so
+    // that they share its L2 for the chunk records
+    const long nbh = gridDim.x / ntile;
+    long bh;
+    int tile;
+    if (nbh % 8 == 0) {
+        const long slot = blockIdx.x / 8;
+        tile = static_cast<int>(slot % ntile);
+        bh = (slot / ntile) * 8 + blockIdx.x % 8;
+    } else {
+        bh = blockIdx.x / ntile;
+        tile = static_cast<int>(blockIdx.x % ntile);
+    }
+    const int j0 = tile * DVT;
+    const long nc = p.nc;
+    const char* recs = p.rec + bh * nc * REC;
+
+    if (wave < NCHAIN) {
+        f32x4 sacc[8];
+        const int col = j0 + 16 * wave + ln;
+        if (p.S0) {
+#pragma unroll
+            for (int ib = 0; ib < 8; ++ib)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sacc[ib][e] = p.S0[(bh * DK + srow(ib, g, e)) * p.dv + col];
+        } else {
+#pragma unroll
+            for (int ib = 0; ib < 8; ++ib) sacc[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        __syncthreads();  // chunk 0 is staged
+        for (long c = 0; c < nc; ++c) {
+            const char* cur = smem + (c & 1) * BUFV;
+            const uint16_t* kgh = reinterpret_cast<const uint16_t*>(cur + R_KGH);
+            const uint16_t* kgl = reinterpret_cast<const uint16_t*>(cur + R_KGL);
+            const uint16_t* qgh = reinterpret_cast<const uint16_t*>(cur + R_QGH);
+            const uint16_t* qgl = reinterpret_cast<const uint16_t*>(cur + R_QGL);
+            const uint16_t* kdh = reinterpret_cast<const uint16_t*>(cur + R_KDH);
+            const uint16_t* kdl = reinterpret_cast<const uint16_t*>(cur + R_KDL);
+            const float* sVt = reinterpret_cast<const float*>(cur + B_VT) + (16 * wave + ln) * VTS;
+            const float* gcs = reinterpret_cast<const float*>(cur + R_GC);
+
+            bf16x8 ka[4][2][2];  // [k-step][row block][hi, lo]
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+                    ka[t][b][0] = *reinterpret_cast<const bf16x8*>(kgh + kq_off(16 * b + ln, 32 * t + 8 * g));
+                    ka[t][b][1] = *reinterpret_cast<const bf16x8*>(kgl + kq_off(16 * b + ln, 32 * t + 8 * g));
+                }
+            bf16x8 bS[4][2];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) split_pair(sacc[2 * t], sacc[2 * t + 1], bS[t]);
+            // Y = Kg S
+            f32x4 y[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+#pragma unroll
+                for (int b = 0; b < 2; ++b) y[b] = mfma32(ka[t][b][1], bS[t][0], y[b]);
+#pragma unroll
+                for (int b = 0; b < 2; ++b) y[b] = mfma32(ka[t][b][0], bS[t][1], y[b]);
+#pragma unroll
+                for (int b = 0; b < 2; ++b) y[b] = mfma32(ka[t][b][0], bS[t][0], y[b]);
+            }
+            // X = Vt - Y;  U_0 = D_0 X_0,  U_1 = D_1 X_1 - N U_0
+            auto a16 = [&](int sl, bf16x4 (&o)[2]) {
+                o[0] = *reinterpret_cast<const bf16x4*>(cur + f16_off(sl, 0, lane));
+                o[1] = *reinterpret_cast<const bf16x4*>(cur + f16_off(sl, 1, lane));
+            };
+            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+            f32x4 W[2];
+            bf16x4 a4[2];
+#pragma unroll
+            for (int R = 0; R < 2; ++R) {
+                const f32x4 x = *reinterpret_cast<const f32x4*>(sVt + 16 * R + 4 * g) - y[R];
+                bf16x4 bx[2];
+                split_d(x, bx);
+                a16(F16_D0 + R, a4);
+                W[R] = mm22x16(a4, bx, zero);
+            }
+            bf16x4 bu0[2], bu1[2];
+            split_d(W[0], bu0);
+            a16(F16_N10, a4);
+            const f32x4 u1 = mm22x16(a4, bu0, W[1]);
+            split_d(u1, bu1);
+            bf16x8 bU[2];
+            bU[0] = cat4(bu0[0], bu1[0]);
+            bU[1] = cat4(bu0[1], bu1[1]);
+
+            // S <- Diag(Gamma_31) S + Kd^T U; Kd^T via transpose reads of the
+            // row-major tiles: lane ln of each 16 points at token 4g + ln / 4 and
+            // the 4 channels 32 (ib / 2) + 4 (ib % 2) + 8 (ln % 4) .. + 3
+#pragma unroll
+            for (int ib = 0; ib < 8; ++ib) sacc[ib] *= *reinterpret_cast<const f32x4*>(gcs + srow(ib, g, 0));
+            {
+                const int tokA = 4 * g + (ln >> 2);
+                bf16x8 akh[8], akl[8];
+#pragma unroll
+                for (int ib = 0; ib < 8; ++ib) {
+                    const int pcol = 32 * (ib >> 1) + 4 * (ib & 1) + 8 * (ln & 3);
+                    const s16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(kdh + kq_off(tokA, pcol)));
+                    const s16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(kdh + kq_off(tokA + 16, pcol)));
+                    const s16x4 l0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(kdl + kq_off(tokA, pcol)));
+                    const s16x4 l1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(kdl + kq_off(tokA + 16, pcol)));
+                    // whole-vector reinterpretation (an element-wise short -> bf16
+                    // bit_cast loop is mis-lowered by this compiler)
+                    akh[ib] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
+                    akl[ib] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(l0, l1, 0, 1, 2, 3, 4, 5, 6, 7));
+                }
+#pragma unroll
+                for (int ib = 0; ib < 8; ++ib) sacc[ib] = mfma32(akl[ib], bU[0], sacc[ib]);
+#pragma unroll
+                for (int ib = 0; ib < 8; ++ib) sacc[ib] = mfma32(akh[ib], bU[1], sacc[ib]);
+#pragma unroll
+                for (int ib = 0; ib < 8; ++ib) sacc[ib] = mfma32(akh[ib], bU[0], sacc[ib]);
+            }
+
+            // O = Qg S + P U, transposed (state / U as the A operand): lane (ln, g)
+            // ends up with row 16R + ln, value columns 4g .. 4g + 3
+            f32x4 oacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                bf16x8 qh[2], ql[2];
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+                    qh[b] = *reinterpret_cast<const bf16x8*>(qgh + kq_off(16 * b + ln, 32 * t + 8 * g));
+                    ql[b] = *reinterpret_cast<const bf16x8*>(qgl + kq_off(16 * b + ln, 32 * t + 8 * g));
+                }
+#pragma unroll
+                for (int b = 0; b < 2; ++b) oacc[b] = mfma32(bS[t][0], ql[b], oacc[b]);
+#pragma unroll
+                for (int b = 0; b < 2; ++b) oacc[b] = mfma32(bS[t][1], qh[b], oacc[b]);
+#pragma unroll
+                for (int b = 0; b < 2; ++b) oacc[b] = mfma32(bS[t][0], qh[b], oacc[b]);
+            }
+            {
+                bf16x8 ap[2][2];
+#pragma unroll
+                for (int R = 0; R < 2; ++R) {
+                    ap[R][0] = *reinterpret_cast<const bf16x8*>(cur + pf_off(R, 0, lane));
+                    ap[R][1] = *reinterpret_cast<const bf16x8*>(cur + pf_off(R, 1, lane));
+                }
+#pragma unroll
+                for (int R = 0; R < 2; ++R) oacc[R] = mfma32(bU[0], ap[R][1], oacc[R]);
+#pragma unroll
+                for (int R = 0; R < 2; ++R) oacc[R] = mfma32(bU[1], ap[R][0], oacc[R]);
+#pragma unroll
+                for (int R = 0; R < 2; ++R) oacc[R] = mfma32(bU[0], ap[R][0], oacc[R]);
+            }
+            {
+                const int c4 = j0 + 16 * wave + 4 * g;
+#pragma unroll
+                for (int R = 0; R < 2; ++R) {
+                    const long tok = c * VC + 16 * R + ln;
+                    if (tok >= p.T) continue;
+                    const long oi = (bh * p.T + tok) * p.dv + c4;
+                    if (p.o_bf16) {
+                        uint2 pk;
+                        pk.x = f32_to_bf16_bits(oacc[R][0]) | (static_cast<uint32_t>(f32_to_bf16_bits(oacc[R][1])) << 16);
+                        pk.y = f32_to_bf16_bits(oacc[R][2]) | (static_cast<uint32_t>(f32_to_bf16_bits(oacc[R][3])) << 16);
+                        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.o) + oi) = pk;
+                    } else {
+                        *reinterpret_cast<f32x4*>(static_cast<float*>(p.o) + oi) = oacc[R];
+                    }
+                }
+            }
+            __syncthreads();
+        }
+        if (p.ST) {
+#pragma unroll
+            for (int ib = 0; ib < 8; ++ib)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) p.ST[(bh * DK + srow(ib, g, e)) * p.dv + col] = sacc[ib][e];
+        }
+        return;
+    }
+
+    if (wave == NCHAIN) {
+        // wave 2: the next chunk's record, HBM -> LDS by DMA (16 bytes per lane,
+        // 1 KiB per instruction, a straight copy)
+        auto dma = [&](long c, char* buf) {
+            const char* src = recs + c * REC + 16 * lane;
+#pragma unroll 8
+            for (int m = 0; m < REC / 1024; ++m)
+                __builtin_amdgcn_global_load_lds((const void*)(src + m * 1024),
+                                                 (__attribute__((address_space(3))) void*)(buf + m * 1024), 16, 0, 0);
+        };
+        if (nc > 0) dma(0, smem);
+        __syncthreads();
+        for (long c = 0; c < nc; ++c) {
+            if (c + 1 < nc) dma(c + 1, smem + ((c + 1) & 1) * BUFV);
+            __syncthreads();
+        }
+    } else {
+        // wave 3: value tile of a chunk, scaled by sqrt(gamma), transposed:
+        // lane (ln, g) holds tokens 2 ln, 2 ln + 1 of columns j0 + 8g .. + 7.
+        // Registers are refilled one chunk ahead; rows past T get 0.
+        uint4 vr[2];
+        f32x4 gv[2][2];
+        float gs[2];
+        auto load = [&](long c) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const long r = bh * p.T + min(c * VC + 2 * ln + i, p.T - 1);
+                vr[i] = *reinterpret_cast<const uint4*>(p.v + r * p.dv + j0 + 8 * g);
+                if (p.gvec) {
+                    gv[i][0] = *reinterpret_cast<const f32x4*>(p.gsrc + r * p.gts + j0 + 8 * g);
+                    gv[i][1] = *reinterpret_cast<const f32x4*>(p.gsrc + r * p.gts + j0 + 8 * g + 4);
+                } else {
+                    gs[i] = p.gsrc[r * p.gts];
+                }
+            }
+        };
+        auto stage = [&](long c, char* buf) {
+            float* sVt = reinterpret_cast<float*>(buf + B_VT);
+            bool okt[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) okt[i] = c * VC + 2 * ln + i < p.T;
+#pragma unroll
+            for (int cc = 0; cc < 8; ++cc) {
+                f32x2 v2;
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const float gam = p.gvec ? gv[i][cc >> 2][cc & 3] : gs[i];
+                    v2[i] = okt[i] ? bf16_at(vr[i], cc) * sqrt_hw(gam) : 0.0f;
+                }
+                *reinterpret_cast<f32x2*>(sVt + (8 * g + cc) * VTS + 2 * ln) = v2;
+            }
+        };
+        if (nc > 0) {
+            load(0);
+            stage(0, smem);
+            if (nc > 1) load(1);
+        }
+        __syncthreads();
+        for (long c = 0; c < nc; ++c) {
+            if (c + 1 < nc) {
+                stage(c + 1, smem + ((c + 1) & 1) * BUFV);
+                if (c + 2 < nc) load(c + 2);
+            }
+            __syncthreads();
+        }
+    }
+}
+
+bool vec_gates(const pdn_chunk_fwd_args& a) {
+    return a.alpha_mode == PDN_ALPHA_VEC || a.beta_mode == PDN_GATE_VEC || a.precond_eps >= 0.0f;
+}
+
+long num_chunks(const pdn_chunk_fwd_args& a) { return (static_cast<long>(a.T) + VC - 1) / VC; }
+
+template <bool AVEC, bool BVEC, bool PRE>
+void launch_prep(const PrepParams& pp, long nblk, hipStream_t stream) {
+    vec_prep_kernel<AVEC, BVEC, PRE><<<dim3(static_cast<unsigned>(nblk)), dim3(256), 0, stream>>>(pp);
+}
+
+}  // namespace
+
+bool chunk_vec_supported(const pdn_chunk_fwd_args& a) {
+    return a.qkv_dtype == PDN_BF16 && a.dk == DK && a.dv % DVT == 0 && vec_gates(a);
+}
+
+size_t chunk_vec_workspace_bytes(const pdn_chunk_fwd_args& a) {
+    const long nrec = static_cast<long>(a.B) * a.H * num_chunks(a);
+    size_t n = static_cast<size_t>(nrec) * REC;
+    if (a.precond_eps >= 0.0f) n += static_cast<size_t>(nrec) * DK * sizeof(float);
+    return n;
+}
+
+hipError_t launch_chunk_vec(const pdn_chunk_fwd_args& a, hipStream_t stream) {
+    const long nbh = static_cast<long>(a.B) * a.H;
+    const long nc = num_chunks(a);
+    char* ws = static_cast<char*>(a.workspace);
+    const bool pre = a.precond_eps >= 0.0f;
+    float* ksum = pre ? reinterpret_cast<float*>(ws + static_cast<size_t>(nbh * nc) * REC) : nullptr;
+    if (pre) {
+        vec_ksq_kernel<<<dim3(static_cast<unsigned>(nbh * nc)), dim3(DK), 0, stream>>>(
+            static_cast<const uint16_t*>(a.k), ksum, a.T, nc);
+        vec_kscan_kernel<<<dim3(static_cast<unsigned>(nbh)), dim3(DK), 0, stream>>>(ksum, a.precond_A0, a.precond_AT, nc);
+    }
+    PrepParams pp;
+    pp.q = static_cast<const uint16_t*>(a.q);
+    pp.k = static_cast<const uint16_t*>(a.k);
+    pp.has_alpha = a.alpha_mode != PDN_ALPHA_NONE;
+    pp.log_alpha = a.log_alpha;
+    pp.beta = a.beta;
+    pp.astart = ksum;
+    pp.rec = ws;
+    pp.T = a.T;
+    pp.nc = nc;
+    pp.nbh = nbh;
+    pp.eps = pre ? a.precond_eps : 0.0f;
+    const long nblk = (nbh * nc + 3) / 4;
+    const bool avec = a.alpha_mode == PDN_ALPHA_VEC, bvec = a.beta_mode == PDN_GATE_VEC;
+    if (avec) {
+        if (bvec) pre ? launch_prep<true, true, true>(pp, nblk, stream) : launch_prep<true, true, false>(pp, nblk, stream);
+        else pre ? launch_prep<true, false, true>(pp, nblk, stream) : launch_prep<true, false, false>(pp, nblk, stream);
+    } else {
+        if (bvec) pre ? launch_prep<false, true, true>(pp, nblk, stream) : launch_prep<false, true, false>(pp, nblk, stream);
+        else pre ? launch_prep<false, false, true>(pp, nblk, stream) : launch_prep<false, false, false>(pp, nblk, stream);
+    }
+
+    ChainParams cp;
+    cp.v = static_cast<const uint16_t*>(a.v);
+    cp.rec = ws;
+    if (a.gamma_mode == PDN_GATE_VEC) {
+        cp.gsrc = a.gamma; cp.gts = a.dv; cp.gvec = 1;
+    } else if (a.gamma_mode == PDN_GATE_SCALAR) {
+        cp.gsrc = a.gamma; cp.gts = 1; cp.gvec = 0;
+    } else if (a.beta_mode == PDN_GATE_VEC) {  // raw beta, dk == dv
+        cp.gsrc = a.beta; cp.gts = a.dk; cp.gvec = 1;
+    } else {
+        cp.gsrc = a.beta; cp.gts = 1; cp.gvec = 0;
+    }
+    cp.S0 = a.S0;
+    cp.ST = a.ST;
+    cp.o = a.o;
+    cp.T = a.T;
+    cp.nc = nc;
+    cp.dv = a.dv;
+    cp.o_bf16 = a.o_dtype == PDN_BF16;
+    const long nwg = nbh * (a.dv / DVT);
+    vec_chain_kernel<<<dim3(static_cast<unsigned>(nwg)), dim3(NTHR), 0, stream>>>(cp);
+    return hipGetLastError();
+}
+
+}  // namespace pdn

@@ -17,6 +17,12 @@ hipError_t launch_chunk_fwd(const pdn_chunk_fwd_args& a, hipStream_t stream);
 bool chunk_fact_supported(const pdn_chunk_fwd_args& a);
 hipError_t launch_chunk_fact(const pdn_chunk_fwd_args& a, hipStream_t stream);
 
+// Throughput prefill for per-channel gates and the preconditioner, bf16,
+// dk = 128; needs chunk_vec_workspace_bytes() of workspace.
+bool chunk_vec_supported(const pdn_chunk_fwd_args& a);
+size_t chunk_vec_workspace_bytes(const pdn_chunk_fwd_args& a);
+hipError_t launch_chunk_vec(const pdn_chunk_fwd_args& a, hipStream_t stream);
+
 // Scratch bytes the prefill needs for these (valid) arguments.
 size_t chunk_fwd_workspace_bytes(const pdn_chunk_fwd_args& a);
 

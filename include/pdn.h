@@ -162,15 +162,21 @@ int pdn_abi_version(void);
 const char *pdn_strerror(int code);
 
 /* Device scratch bytes pdn_chunk_fwd needs for these arguments (0 is valid).
- * Returns PDN_OK and writes *bytes, or a PDN_E* code for invalid arguments. */
+ * Returns PDN_OK and writes *bytes, or a PDN_E* code for invalid arguments.
+ * Non-zero only for bf16 q/k/v with dk == 128 and a per-channel gate or the
+ * preconditioner: those calls first write, for every (b, h) and 32-token
+ * chunk, a 56 KiB record of gate-scaled operands and solve blocks (plus 512
+ * bytes of k(.)k sums with the preconditioner), which the state-carrying
+ * kernel then reads once.  The workspace holds no state between calls. */
 int pdn_chunk_fwd_workspace_size(const pdn_chunk_fwd_args *args, size_t *bytes);
 
 /* Validate only (no HIP call, no launch): PDN_OK or the code pdn_chunk_fwd
  * would return for these arguments before launching. */
 int pdn_chunk_fwd_check(const pdn_chunk_fwd_args *args);
 
-/* Prefill: o, and ST / precond_AT when given.  Chunk length 64; T need not be
- * a multiple of it and results do not depend on where chunks fall. */
+/* Prefill: o, and ST / precond_AT when given.  Chunk length 64 (32 for the
+ * per-channel-gate path above); T need not be a multiple of it and results do
+ * not depend on where chunks fall. */
 int pdn_chunk_fwd(const pdn_chunk_fwd_args *args, void *stream);
 
 /* Validate only, as pdn_chunk_fwd_check. */

@@ -85,6 +85,7 @@ def _chunk_ok():
     a.beta_mode, a.beta = pdn.PDN_GATE_VEC, FAKE
     a.gamma_mode, a.gamma = pdn.PDN_GATE_VEC, FAKE
     a.precond_eps = -1.0
+    a.workspace, a.workspace_bytes = FAKE, 1 << 40  # at least what the call needs
     return a
 
 
@@ -111,8 +112,43 @@ def _dcheck(lib, a):
 def test_valid_arguments_pass_validation(lib):
     assert _ccheck(lib, _chunk_ok()) == pdn.PDN_OK
     assert _dcheck(lib, _decode_ok()) == pdn.PDN_OK
+
+
+def _ws_size(lib, a):
     n = ctypes.c_size_t(123)
-    assert lib.pdn_chunk_fwd_workspace_size(ctypes.byref(_chunk_ok()), ctypes.byref(n)) == 0
+    assert lib.pdn_chunk_fwd_workspace_size(ctypes.byref(a), ctypes.byref(n)) == pdn.PDN_OK
+    return n.value
+
+
+def test_workspace_size_and_check(lib):
+    # bf16, dk = 128, per-channel gates: one record of whole KiB per 32-token
+    # chunk and (b, h); scalar gates and fp32 inputs need none
+    a = _chunk_ok()
+    n = _ws_size(lib, a)
+    nchunk = a.B * a.H * ((a.T + 31) // 32)
+    assert n > 0 and n % (nchunk * 1024) == 0
+    a.precond_eps = 1e-6  # adds the per-chunk k.k sums
+    assert _ws_size(lib, a) == n + nchunk * 128 * 4
+    a.precond_eps = -1.0
+    a.T = 33  # ragged tail: two chunks
+    assert _ws_size(lib, a) == 2 * a.B * a.H * (n // nchunk)
+    a.T = 0
+    assert _ws_size(lib, a) == 0
+    s = _chunk_ok()
+    s.alpha_mode, s.beta_mode, s.gamma_mode = pdn.PDN_ALPHA_SCALAR, pdn.PDN_GATE_SCALAR, pdn.PDN_GATE_SCALAR
+    assert _ws_size(lib, s) == 0
+    f = _chunk_ok()
+    f.qkv_dtype = pdn.PDN_F32
+    assert _ws_size(lib, f) == 0
+    # too small or missing: PDN_EWORKSPACE, before any launch
+    a = _chunk_ok()
+    a.workspace_bytes = n - 1
+    assert _ccheck(lib, a) == pdn.PDN_EWORKSPACE
+    assert lib.pdn_chunk_fwd(ctypes.byref(a), None) == pdn.PDN_EWORKSPACE
+    a.workspace, a.workspace_bytes = None, 0
+    assert _ccheck(lib, a) == pdn.PDN_EWORKSPACE
+    a.workspace_bytes = n
+    assert _ccheck(lib, a) == pdn.PDN_EWORKSPACE
 
 
 @pytest.mark.parametrize("mutate,code", [
