@@ -26,9 +26,10 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-I" + INCLUDE, "-I" + CSRC,
           "-Wno-unused-command-line-argument"]
 
 
-# Per-source extra flags.  The scalar-gate prefill keeps its MFMA accumulators
-# in ordinary VGPRs (no accumulator-register copies around every VALU use).
-EXTRA = {"chunk_fact.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-source extra flags.  The prefill kernels keep their MFMA accumulators in
+# ordinary VGPRs (no accumulator-register copies around every VALU use).
+EXTRA = {"chunk_fact.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "chunk_vec.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _hipcc() -> str:

@@ -502,13 +502,19 @@ __global__ void __launch_bounds__(NTHR) vec_chain_kernel(ChainParams p) {
             const float* sVt = reinterpret_cast<const float*>(cur + B_VT) + (16 * wave + ln) * VTS;
             const float* gcs = reinterpret_cast<const float*>(cur + R_GC);
 
+            // LDS reads are issued well ahead of their use: Kg first (it starts
+            // the recurrence), then Qg, the transposed Kd and the fragments while
+            // the Y products run
+            auto rows = [&](const uint16_t* tile, int b, int t) {
+                return *reinterpret_cast<const bf16x8*>(tile + kq_off(16 * b + ln, 32 * t + 8 * g));
+            };
             bf16x8 ka[4][2][2];  // [k-step][row block][hi, lo]
 #pragma unroll
             for (int t = 0; t < 4; ++t)
 #pragma unroll
                 for (int b = 0; b < 2; ++b) {
-                    ka[t][b][0] = *reinterpret_cast<const bf16x8*>(kgh + kq_off(16 * b + ln, 32 * t + 8 * g));
-                    ka[t][b][1] = *reinterpret_cast<const bf16x8*>(kgl + kq_off(16 * b + ln, 32 * t + 8 * g));
+                    ka[t][b][0] = rows(kgh, b, t);
+                    ka[t][b][1] = rows(kgl, b, t);
                 }
             bf16x8 bS[4][2];
 #pragma unroll
@@ -524,39 +530,20 @@ __global__ void __launch_bounds__(NTHR) vec_chain_kernel(ChainParams p) {
 #pragma unroll
                 for (int b = 0; b < 2; ++b) y[b] = mfma32(ka[t][b][0], bS[t][0], y[b]);
             }
-            // X = Vt - Y;  U_0 = D_0 X_0,  U_1 = D_1 X_1 - N U_0
-            auto a16 = [&](int sl, bf16x4 (&o)[2]) {
-                o[0] = *reinterpret_cast<const bf16x4*>(cur + f16_off(sl, 0, lane));
-                o[1] = *reinterpret_cast<const bf16x4*>(cur + f16_off(sl, 1, lane));
-            };
-            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-            f32x4 W[2];
-            bf16x4 a4[2];
+            bf16x8 qa[4][2][2];
 #pragma unroll
-            for (int R = 0; R < 2; ++R) {
-                const f32x4 x = *reinterpret_cast<const f32x4*>(sVt + 16 * R + 4 * g) - y[R];
-                bf16x4 bx[2];
-                split_d(x, bx);
-                a16(F16_D0 + R, a4);
-                W[R] = mm22x16(a4, bx, zero);
-            }
-            bf16x4 bu0[2], bu1[2];
-            split_d(W[0], bu0);
-            a16(F16_N10, a4);
-            const f32x4 u1 = mm22x16(a4, bu0, W[1]);
-            split_d(u1, bu1);
-            bf16x8 bU[2];
-            bU[0] = cat4(bu0[0], bu1[0]);
-            bU[1] = cat4(bu0[1], bu1[1]);
-
-            // S <- Diag(Gamma_31) S + Kd^T U; Kd^T via transpose reads of the
-            // row-major tiles: lane ln of each 16 points at token 4g + ln / 4 and
-            // the 4 channels 32 (ib / 2) + 4 (ib % 2) + 8 (ln % 4) .. + 3
+            for (int t = 0; t < 4; ++t)
 #pragma unroll
-            for (int ib = 0; ib < 8; ++ib) sacc[ib] *= *reinterpret_cast<const f32x4*>(gcs + srow(ib, g, 0));
+                for (int b = 0; b < 2; ++b) {
+                    qa[t][b][0] = rows(qgh, b, t);
+                    qa[t][b][1] = rows(qgl, b, t);
+                }
+            // Kd^T via transpose reads of the row-major tiles: lane ln of each 16
+            // points at token 4g + ln / 4 and the 4 channels
+            // 32 (ib / 2) + 4 (ib % 2) + 8 (ln % 4) .. + 3
+            bf16x8 akh[8], akl[8];
             {
                 const int tokA = 4 * g + (ln >> 2);
-                bf16x8 akh[8], akl[8];
 #pragma unroll
                 for (int ib = 0; ib < 8; ++ib) {
                     const int pcol = 32 * (ib >> 1) + 4 * (ib & 1) + 8 * (ln & 3);
@@ -569,46 +556,76 @@ __global__ void __launch_bounds__(NTHR) vec_chain_kernel(ChainParams p) {
                     akh[ib] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
                     akl[ib] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(l0, l1, 0, 1, 2, 3, 4, 5, 6, 7));
                 }
-#pragma unroll
-                for (int ib = 0; ib < 8; ++ib) sacc[ib] = mfma32(akl[ib], bU[0], sacc[ib]);
-#pragma unroll
-                for (int ib = 0; ib < 8; ++ib) sacc[ib] = mfma32(akh[ib], bU[1], sacc[ib]);
-#pragma unroll
-                for (int ib = 0; ib < 8; ++ib) sacc[ib] = mfma32(akh[ib], bU[0], sacc[ib]);
             }
+            f32x4 gsc[8];
+#pragma unroll
+            for (int ib = 0; ib < 8; ++ib) gsc[ib] = *reinterpret_cast<const f32x4*>(gcs + srow(ib, g, 0));
+            auto a16 = [&](int sl, bf16x4 (&o)[2]) {
+                o[0] = *reinterpret_cast<const bf16x4*>(cur + f16_off(sl, 0, lane));
+                o[1] = *reinterpret_cast<const bf16x4*>(cur + f16_off(sl, 1, lane));
+            };
+            bf16x4 ad[2][2], an[2];
+            a16(F16_D0, ad[0]);
+            a16(F16_D1, ad[1]);
+            a16(F16_N10, an);
+            f32x4 vt[2];
+#pragma unroll
+            for (int R = 0; R < 2; ++R) vt[R] = *reinterpret_cast<const f32x4*>(sVt + 16 * R + 4 * g);
+            bf16x8 ap[2][2];
+#pragma unroll
+            for (int R = 0; R < 2; ++R) {
+                ap[R][0] = *reinterpret_cast<const bf16x8*>(cur + pf_off(R, 0, lane));
+                ap[R][1] = *reinterpret_cast<const bf16x8*>(cur + pf_off(R, 1, lane));
+            }
+            // keep the reads above the solve (the scheduler would otherwise sink
+            // each one next to its first use and expose its latency)
+            __builtin_amdgcn_sched_barrier(0);
+
+            // X = Vt - Y;  U_0 = D_0 X_0,  U_1 = D_1 X_1 - N U_0
+            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+            f32x4 W[2];
+#pragma unroll
+            for (int R = 0; R < 2; ++R) {
+                bf16x4 bx[2];
+                split_d(vt[R] - y[R], bx);
+                W[R] = mm22x16(ad[R], bx, zero);
+            }
+            bf16x4 bu0[2], bu1[2];
+            split_d(W[0], bu0);
+            const f32x4 u1 = mm22x16(an, bu0, W[1]);
+            split_d(u1, bu1);
+            bf16x8 bU[2];
+            bU[0] = cat4(bu0[0], bu1[0]);
+            bU[1] = cat4(bu0[1], bu1[1]);
+
+            // S <- Diag(Gamma_31) S + Kd^T U
+#pragma unroll
+            for (int ib = 0; ib < 8; ++ib) sacc[ib] *= gsc[ib];
+#pragma unroll
+            for (int ib = 0; ib < 8; ++ib) sacc[ib] = mfma32(akl[ib], bU[0], sacc[ib]);
+#pragma unroll
+            for (int ib = 0; ib < 8; ++ib) sacc[ib] = mfma32(akh[ib], bU[1], sacc[ib]);
+#pragma unroll
+            for (int ib = 0; ib < 8; ++ib) sacc[ib] = mfma32(akh[ib], bU[0], sacc[ib]);
 
             // O = Qg S + P U, transposed (state / U as the A operand): lane (ln, g)
             // ends up with row 16R + ln, value columns 4g .. 4g + 3
             f32x4 oacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                bf16x8 qh[2], ql[2];
 #pragma unroll
-                for (int b = 0; b < 2; ++b) {
-                    qh[b] = *reinterpret_cast<const bf16x8*>(qgh + kq_off(16 * b + ln, 32 * t + 8 * g));
-                    ql[b] = *reinterpret_cast<const bf16x8*>(qgl + kq_off(16 * b + ln, 32 * t + 8 * g));
-                }
+                for (int b = 0; b < 2; ++b) oacc[b] = mfma32(bS[t][0], qa[t][b][1], oacc[b]);
 #pragma unroll
-                for (int b = 0; b < 2; ++b) oacc[b] = mfma32(bS[t][0], ql[b], oacc[b]);
+                for (int b = 0; b < 2; ++b) oacc[b] = mfma32(bS[t][1], qa[t][b][0], oacc[b]);
 #pragma unroll
-                for (int b = 0; b < 2; ++b) oacc[b] = mfma32(bS[t][1], qh[b], oacc[b]);
-#pragma unroll
-                for (int b = 0; b < 2; ++b) oacc[b] = mfma32(bS[t][0], qh[b], oacc[b]);
+                for (int b = 0; b < 2; ++b) oacc[b] = mfma32(bS[t][0], qa[t][b][0], oacc[b]);
             }
-            {
-                bf16x8 ap[2][2];
 #pragma unroll
-                for (int R = 0; R < 2; ++R) {
-                    ap[R][0] = *reinterpret_cast<const bf16x8*>(cur + pf_off(R, 0, lane));
-                    ap[R][1] = *reinterpret_cast<const bf16x8*>(cur + pf_off(R, 1, lane));
-                }
+            for (int R = 0; R < 2; ++R) oacc[R] = mfma32(bU[0], ap[R][1], oacc[R]);
 #pragma unroll
-                for (int R = 0; R < 2; ++R) oacc[R] = mfma32(bU[0], ap[R][1], oacc[R]);
+            for (int R = 0; R < 2; ++R) oacc[R] = mfma32(bU[1], ap[R][0], oacc[R]);
 #pragma unroll
-                for (int R = 0; R < 2; ++R) oacc[R] = mfma32(bU[1], ap[R][0], oacc[R]);
-#pragma unroll
-                for (int R = 0; R < 2; ++R) oacc[R] = mfma32(bU[0], ap[R][0], oacc[R]);
-            }
+            for (int R = 0; R < 2; ++R) oacc[R] = mfma32(bU[0], ap[R][0], oacc[R]);
             {
                 const int c4 = j0 + 16 * wave + 4 * g;
 #pragma unroll
@@ -639,7 +656,8 @@ __global__ void __launch_bounds__(NTHR) vec_chain_kernel(ChainParams p) {
 
     if (wave == NCHAIN) {
         // wave 2: the next chunk's record, HBM -> LDS by DMA (16 bytes per lane,
-        // 1 KiB per instruction, a straight copy)
+        // 1 KiB per instruction, a straight copy), issued as soon as the
+        // barrier frees its buffer
         auto dma = [&](long c, char* buf) {
             const char* src = recs + c * REC + 16 * lane;
 #pragma unroll 8
