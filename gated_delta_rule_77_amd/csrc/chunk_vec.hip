@@ -177,48 +177,86 @@ __device__ __forceinline__ Decay decay_factors(float lg0, float lg1) {
 // preconditioner pre-pass
 // ---------------------------------------------------------------------------
 
-// Sum of k (.) k over each chunk: one workgroup per (b, h, chunk), one thread
-// per channel.
-__global__ void __launch_bounds__(DK) vec_ksq_kernel(const uint16_t* k, float* ks, long T, long nc) {
-    const long id = blockIdx.x;
+// Sum of k (.) k over each chunk: one wave per (b, h, chunk), four chunks per
+// workgroup.  Lane (ln, g) reads channels 8 ln .. 8 ln + 7 (16 bytes) of the
+// tokens 4s + g, s = 0..7; the four token groups are then added across lanes.
+constexpr int KSQ_NTHR = 256;
+__global__ void __launch_bounds__(KSQ_NTHR) vec_ksq_kernel(const uint16_t* k, float* ks, long T, long nc, long nid) {
+    const int lane = threadIdx.x & 63;
+    const long id = blockIdx.x * (KSQ_NTHR / 64L) + (threadIdx.x >> 6);
+    if (id >= nid) return;
     const long bh = id / nc;
     const long t0 = (id % nc) * VC;
-    const int i = threadIdx.x;
-    float s = 0.0f;
-    for (int r = 0; r < VC; ++r) {
-        const long t = t0 + r;
+    const int ln = lane & 15, g = lane >> 4;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s4 = 0; s4 < VC / 4; ++s4) {
+        const long t = t0 + 4 * s4 + g;
         if (t < T) {
-            const float x = bf16_bits_to_f32(k[(bh * T + t) * DK + i]);
-            s = fmaf(x, x, s);
+            const uint4 u = *reinterpret_cast<const uint4*>(k + (bh * T + t) * DK + 8 * ln);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float x = bf16_at(u, j);
+                acc[j] = fmaf(x, x, acc[j]);
+            }
         }
     }
-    ks[id * DK + i] = s;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        acc[j] += __shfl_xor(acc[j], 16, 64);
+        acc[j] += __shfl_xor(acc[j], 32, 64);
+    }
+    if (g == 0) {
+        float* dst = ks + id * DK + 8 * ln;
+        *reinterpret_cast<f32x4*>(dst) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+        *reinterpret_cast<f32x4*>(dst + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+    }
 }
 
 // Exclusive running sum over the chunks of each (b, h), in place, starting
-// from A0; the total goes to AT.
-__global__ void __launch_bounds__(DK) vec_kscan_kernel(float* ks, const float* A0, float* AT, long nc) {
+// from A0; the total goes to AT.  One workgroup per (b, h): thread (segment,
+// channel) sums its run of chunks, the segment totals are prefixed through
+// LDS, and a second pass writes the running values.
+constexpr int KSCAN_SEG = 8;
+__global__ void __launch_bounds__(KSCAN_SEG * DK) vec_kscan_kernel(float* ks, const float* A0, float* AT, long nc) {
+    __shared__ float tot[KSCAN_SEG][DK];
     const long bh = blockIdx.x;
-    const int i = threadIdx.x;
-    float run = A0 ? A0[bh * DK + i] : 0.0f;
+    const int i = threadIdx.x % DK;
+    const int sg = threadIdx.x / DK;
+    const long len = (nc + KSCAN_SEG - 1) / KSCAN_SEG;
+    const long c0 = min(sg * len, nc), c1 = min(c0 + len, nc);
     float* col = ks + bh * nc * DK + i;
-    long c = 0;
-    for (; c + 8 <= nc; c += 8) {
-        float s[8];
+    float sum = 0.0f;
+    long c = c0;
+    for (; c + 8 <= c1; c += 8) {
+        float v[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) s[u] = col[(c + u) * DK];
+        for (int u = 0; u < 8; ++u) v[u] = col[(c + u) * DK];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) sum += v[u];
+    }
+    for (; c < c1; ++c) sum += col[c * DK];
+    tot[sg][i] = sum;
+    __syncthreads();
+    float run = A0 ? A0[bh * DK + i] : 0.0f;
+    for (int q = 0; q < sg; ++q) run += tot[q][i];
+    c = c0;
+    for (; c + 8 <= c1; c += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = col[(c + u) * DK];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             col[(c + u) * DK] = run;
-            run += s[u];
+            run += v[u];
         }
     }
-    for (; c < nc; ++c) {
-        const float s = col[c * DK];
+    for (; c < c1; ++c) {
+        const float v = col[c * DK];
         col[c * DK] = run;
-        run += s;
+        run += v;
     }
-    if (AT) AT[bh * DK + i] = run;
+    if (AT && sg == KSCAN_SEG - 1) AT[bh * DK + i] = run;
 }
 
 // ---------------------------------------------------------------------------
@@ -754,9 +792,11 @@ hipError_t launch_chunk_vec(const pdn_chunk_fwd_args& a, hipStream_t stream) {
     const bool pre = a.precond_eps >= 0.0f;
     float* ksum = pre ? reinterpret_cast<float*>(ws + static_cast<size_t>(nbh * nc) * REC) : nullptr;
     if (pre) {
-        vec_ksq_kernel<<<dim3(static_cast<unsigned>(nbh * nc)), dim3(DK), 0, stream>>>(
-            static_cast<const uint16_t*>(a.k), ksum, a.T, nc);
-        vec_kscan_kernel<<<dim3(static_cast<unsigned>(nbh)), dim3(DK), 0, stream>>>(ksum, a.precond_A0, a.precond_AT, nc);
+        const long nid = nbh * nc;
+        vec_ksq_kernel<<<dim3(static_cast<unsigned>((nid + 3) / 4)), dim3(KSQ_NTHR), 0, stream>>>(
+            static_cast<const uint16_t*>(a.k), ksum, a.T, nc, nid);
+        vec_kscan_kernel<<<dim3(static_cast<unsigned>(nbh)), dim3(KSCAN_SEG * DK), 0, stream>>>(
+            ksum, a.precond_A0, a.precond_AT, nc);
     }
     PrepParams pp;
     pp.q = static_cast<const uint16_t*>(a.q);
