@@ -7,15 +7,18 @@ scalar decay and gain per head and token, value gain = gain), producing the
 fp32 output and the final fp32 state.  Inputs are resident in HBM before the
 timed region.  The same run also times the recurrent decode
 (pdn_decode_step: B=256, H=16, d=128, fp32 resident state, channel-wise decay,
-vector key gain, scalar value gain) and, on rank 0, the fp64 CPU oracle on a
-bounded sample of the prefill workload.
+vector key gain, scalar value gain), the per-channel-gate prefill on the
+KDA / FG^2-GDN workload (B=2, H=32, T=8192, channel-wise decay and key gain)
+and the Gated DeltaNet-2 + preconditioner workload (B=1, H=16, T=65536,
+channel-wise decay, key and value gains), and, on rank 0, the fp64 CPU oracle
+on a bounded sample of the prefill workload.
 
 Prints one JSON line.  `value` is prefill tokens/s (tokens = batch x sequence
 positions, all heads); the roofline object describes the prefill kernel
 (HBM-bound: algorithmic bytes / kernel time vs 8 TB/s), and the decode object
 its own roofline.
 
-    python bench.py [--steps K] [--warmup W] [--decode-steps N] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--decode-steps N] [--no-cpu-baseline] [--no-gated]
     python bench.py --copy-probe     # plain 1 GiB copy, to calibrate PMC byte counters
 """
 from __future__ import annotations
@@ -51,6 +54,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--decode-steps", type=int, default=200)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-gated", action="store_true",
+                    help="skip the per-channel-gate prefill workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
@@ -205,6 +210,58 @@ def bench_decode(args):
     }
 
 
+def bench_gated(args):
+    """Per-channel-gate prefill workloads, timed per call (every kernel of the
+    call: preparation, optional preconditioner pre-pass, chain) with the
+    workspace allocated before the timed region."""
+    import torch
+    import gated_delta_rule_77_amd as pdn
+    from gated_delta_rule_77_amd import synth
+
+    res = {}
+    for mk, steps in ((synth.kda_fg2, 10), (synth.gdn2_precond, 5)):
+        w = mk()
+        q, k, v = to_dev(w.q, True), to_dev(w.k, True), to_dev(w.v, True)
+        la, be, ga = to_dev(w.log_alpha), to_dev(w.beta), to_dev(w.gamma)
+        pre = w.precond_eps >= 0
+        o = torch.empty((w.B, w.H, w.T, w.dv), device="cuda", dtype=torch.float32)
+        ST = torch.empty((w.B, w.H, w.dk, w.dv), device="cuda", dtype=torch.float32)
+        AT = torch.empty((w.B, w.H, w.dk), device="cuda", dtype=torch.float32) if pre else None
+        S0 = to_dev(w.S0)
+        kw = dict(log_alpha=la, beta=be, gamma=ga, precond_eps=(w.precond_eps if pre else None),
+                  precond_AT=AT, S0=S0, ST=ST)
+        ws = torch.empty(pdn.pdn_chunk_fwd_workspace_size(q, k, v, o, **kw), dtype=torch.uint8,
+                         device="cuda")
+        for _ in range(3):
+            pdn.pdn_chunk_fwd(q, k, v, o, workspace=ws, **kw)
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for i in range(steps):
+            ev[i][0].record(stream)
+            pdn.pdn_chunk_fwd(q, k, v, o, workspace=ws, **kw)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+        BH, T, dk, dv = w.B * w.H, w.T, w.dk, w.dv
+        gate = lambda x: 0 if x is None else x.size * 4
+        alg = (BH * T * (2 * dk + dv) * 2 + gate(w.log_alpha) + gate(w.beta) + gate(w.gamma)
+               + BH * T * dv * 4 + BH * dk * dv * 4 * (2 if w.S0 is not None else 1)
+               + (BH * dk * 4 if pre else 0))
+        gbs = alg / (ms / 1e3) / 1e9
+        res["%s_B%d_H%d_T%d_d%d" % (w.name, w.B, w.H, w.T, w.dk)] = {
+            "B": w.B, "H": w.H, "T": T, "dk": dk, "dv": dv, "steps": steps,
+            "call_ms": ms, "tokens_per_s": w.B * T / (ms / 1e3),
+            "alg_bytes_per_call": alg, "workspace_bytes": ws.numel(),
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS},
+        }
+        del q, k, v, la, be, ga, o, ST, AT, S0, ws, w
+        torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(w, target_s: float):
     """The fp64 oracle on a bounded sample of the prefill workload."""
     import numpy as np
@@ -262,6 +319,7 @@ def main():
 
     pf = bench_prefill(args)
     dec = None if args.no_decode else bench_decode(args)
+    gated = None if args.no_gated else bench_gated(args)
     cpu = None
     if not args.no_cpu_baseline and int(os.environ.get("RANK", "0")) == 0:
         cpu = cpu_baseline(pf["sample"], args.cpu_seconds)
@@ -298,6 +356,7 @@ def main():
                  "ceiling_frac_at_hbm_bound": (pf["alg_flops"] / (pf["alg_bytes"] / (HBM_PEAK_GBS * 1e9)))
                  / (BF16_PEAK_TFLOPS * 1e12)},
         "decode": dec,
+        "per_channel_gates": gated,
         "cpu_baseline": cpu,
         "kernel_source_hash": kernel_source_hash(),
     }
