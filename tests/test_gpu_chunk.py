@@ -337,6 +337,42 @@ def test_vector_gates_with_equal_entries_match_scalar_path():
     assert rel_l2(S_v, S_s) < 1e-4
 
 
+@pytest.mark.parametrize("pre", [False, True])
+@pytest.mark.parametrize("gmode", ["same", "scalar", "vec"])
+@pytest.mark.parametrize("bmode", ["scalar", "vec"])
+@pytest.mark.parametrize("amode", ["none", "scalar", "vec"])
+def test_gate_mode_matrix(amode, bmode, gmode, pre):
+    """Every combination of decay (none / per token / per channel), key gain
+    (per token / per channel), value gain (the key gain / per token / per value
+    channel) and the preconditioner, on a ragged length with a non-zero start
+    state (and start sum A0): per-channel gates and the preconditioner run the
+    per-channel-gate kernels, the rest the scalar-gate kernel."""
+    seed = (["none", "scalar", "vec"].index(amode) * 2 + ["scalar", "vec"].index(bmode)) * 6 \
+        + ["same", "scalar", "vec"].index(gmode) * 2 + int(pre)
+    rng = np.random.default_rng(100 + seed)
+    w = synth.kda_fg2(B=1, H=2, T=147, d=128, seed=21)
+    if amode == "none":
+        w.alpha_mode, w.log_alpha = synth.ALPHA_NONE, None
+    elif amode == "scalar":
+        w.alpha_mode, w.log_alpha = synth.ALPHA_SCALAR, np.ascontiguousarray(w.log_alpha[..., 0])
+    if bmode == "scalar":
+        w.beta_mode, w.beta = synth.GATE_SCALAR, np.ascontiguousarray(w.beta[..., 0])
+    if gmode == "same":
+        w.gamma_mode, w.gamma = synth.GAMMA_SAME_AS_BETA, None
+    elif gmode == "scalar":
+        w.gamma_mode = synth.GATE_SCALAR
+        w.gamma = (1.0 / (1.0 + np.exp(-rng.standard_normal((1, 2, 147))))).astype(np.float32)
+    else:
+        w.gamma_mode = synth.GATE_VEC
+        w.gamma = (1.0 / (1.0 + np.exp(-rng.standard_normal((1, 2, 147, 128))))).astype(np.float32)
+    w.S0 = (0.1 * rng.standard_normal((1, 2, 128, 128))).astype(np.float32)
+    A0 = None
+    if pre:
+        w.precond_eps = 1e-6
+        A0 = rng.uniform(0.0, 2.0, (1, 2, 128)).astype(np.float32)
+    check("gates a=%s b=%s g=%s pre=%d" % (amode, bmode, gmode, pre), w, TOL_BF16, A0=A0)
+
+
 def test_deterministic():
     w = synth.gdn2_precond(B=1, H=2, T=333, d=128, seed=16, n_pairs=4)
     o1, S1, A1 = run_chunk(w)
