@@ -310,15 +310,30 @@ __global__ void __launch_bounds__(256) vec_prep_kernel(PrepParams p) {
     }
 
     f32x4 t00 = {0.f, 0.f, 0.f, 0.f}, t11 = t00, t10 = t00, p00 = t00, p11 = t00, p10 = t00;
+    // k-steps in pairs (2tp, 2tp + 1): the two halves of every 128-byte line of
+    // the q/k rows are loaded together, and the two halves of every record line
+    // (the tile swizzle keeps them in the same pair) are stored back to back,
+    // so no line is fetched twice or written back half-filled
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int tp = 0; tp < 2; ++tp) {
+    uint4 kp[2][2], qp[2][2];  // [step in pair][row block]
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            kp[u][b] = *reinterpret_cast<const uint4*>(p.k + row[b] * DK + 32 * (2 * tp + u) + 8 * g);
+            qp[u][b] = *reinterpret_cast<const uint4*>(p.q + row[b] * DK + 32 * (2 * tp + u) + 8 * g);
+        }
+    uint4 held[2][6];  // hi/lo record words of the first step of the pair
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int t = 2 * tp + u;
         const int cb = 32 * t + 8 * g;  // this lane's first channel in k-step t
-        uint4 kr[2], qr[2];
+        const uint4* kr = kp[u];
+        const uint4* qr = qp[u];
         float la[2][8], be[2][8], as[8];
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
-            kr[b] = *reinterpret_cast<const uint4*>(p.k + row[b] * DK + cb);
-            qr[b] = *reinterpret_cast<const uint4*>(p.q + row[b] * DK + cb);
             if constexpr (AVEC) {
                 const f32x4 a0 = *reinterpret_cast<const f32x4*>(p.log_alpha + row[b] * DK + cb);
                 const f32x4 a1 = *reinterpret_cast<const f32x4*>(p.log_alpha + row[b] * DK + cb + 4);
@@ -397,25 +412,37 @@ __global__ void __launch_bounds__(256) vec_prep_kernel(PrepParams p) {
             p10 = mfma4(bo, q1 * d.f1, p10);
         }
         // gate-scaled operand rows for the chain, hi/lo, into the swizzled tiles
+        uint4 w[2][6];
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
-            const int off = 2 * kq_off(16 * b + ln, cb);
-            uint4 h, l;
-            split8(kg[b], h, l);
-            *reinterpret_cast<uint4*>(rec + R_KGH + off) = h;
-            *reinterpret_cast<uint4*>(rec + R_KGL + off) = l;
-            split8(qg[b], h, l);
-            *reinterpret_cast<uint4*>(rec + R_QGH + off) = h;
-            *reinterpret_cast<uint4*>(rec + R_QGL + off) = l;
-            split8(kd[b], h, l);
-            *reinterpret_cast<uint4*>(rec + R_KDH + off) = h;
-            *reinterpret_cast<uint4*>(rec + R_KDL + off) = l;
+            split8(kg[b], w[b][0], w[b][1]);
+            split8(qg[b], w[b][2], w[b][3]);
+            split8(kd[b], w[b][4], w[b][5]);
+        }
+        if (u == 0) {
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int x = 0; x < 6; ++x) held[b][x] = w[b][x];
+        } else {
+            constexpr int tiles[6] = {R_KGH, R_KGL, R_QGH, R_QGL, R_KDH, R_KDL};
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                const int off0 = 2 * kq_off(16 * b + ln, cb - 32);
+                const int off1 = 2 * kq_off(16 * b + ln, cb);
+#pragma unroll
+                for (int x = 0; x < 6; ++x) {
+                    *reinterpret_cast<uint4*>(rec + tiles[x] + off0) = held[b][x];
+                    *reinterpret_cast<uint4*>(rec + tiles[x] + off1) = w[b][x];
+                }
+            }
         }
         if (ln == 0) {
             float* gc = reinterpret_cast<float*>(rec + R_GC) + cb;
             *reinterpret_cast<f32x4*>(gc) = f32x4{gcv[0], gcv[1], gcv[2], gcv[3]};
             *reinterpret_cast<f32x4*>(gc + 4) = f32x4{gcv[4], gcv[5], gcv[6], gcv[7]};
         }
+    }
     }
 
     // strictly lower part of the diagonal T blocks (row ln, columns 4g + e) to
