@@ -237,6 +237,27 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
 #pragma unroll
             for (int ib = 0; ib < 8; ++ib) sacc[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
+        // o of chunk c is stored during chunk c + 1, after its Y products are
+        // issued: the stores can then wait for the memory pipe (shared with the
+        // helpers' key DMA and loads) while the MFMAs run
+        f32x4 opend[4];
+        auto store_o = [&](long cc) {
+            const int c4 = j0 + 16 * wave + 4 * g;
+#pragma unroll
+            for (int R = 0; R < 4; ++R) {
+                const long tok = cc * CH + 16 * R + ln;
+                if (tok >= p.T) continue;
+                const long oi = (bh * p.T + tok) * p.dv + c4;
+                if (p.o_bf16) {
+                    uint2 pk;
+                    pk.x = f32_to_bf16_bits(opend[R][0]) | (static_cast<uint32_t>(f32_to_bf16_bits(opend[R][1])) << 16);
+                    pk.y = f32_to_bf16_bits(opend[R][2]) | (static_cast<uint32_t>(f32_to_bf16_bits(opend[R][3])) << 16);
+                    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.o) + oi) = pk;
+                } else {
+                    *reinterpret_cast<f32x4*>(static_cast<float*>(p.o) + oi) = opend[R];
+                }
+            }
+        };
         __syncthreads();  // the helpers have staged the first key tile
         __syncthreads();  // ... and prepared chunk 0
         for (long c = 0; c < nchunks; ++c) {
@@ -245,7 +266,6 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
             const uint16_t* sQ = reinterpret_cast<const uint16_t*>(cur + B_Q);
             const float* sc = reinterpret_cast<const float*>(cur + B_SC);
             const float* sVt = reinterpret_cast<const float*>(cur + B_VT) + (16 * wave + ln) * VTS;
-            const long t0 = c * CH;
 
             // key rows for Y first: their LDS latency overlaps the state split
             bf16x8 ka[4][4];
@@ -293,6 +313,7 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
 #pragma unroll
                 for (int b = 0; b < 4; ++b) y[b] = mfma32(ka[t][b], bS[t][0], y[b]);
             }
+            if (c > 0) store_o(c - 1);
             // X = Vt - diag(sb Gamma) Y
             f32x4 x[4];
 #pragma unroll
@@ -408,25 +429,11 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
 #pragma unroll
                 for (int R = 2 * t; R < 4; ++R) oacc[R] = mfma32(bU[t][0], ap[R][0], oacc[R]);
             }
-            {
-                const int c4 = j0 + 16 * wave + 4 * g;
 #pragma unroll
-                for (int R = 0; R < 4; ++R) {
-                    const long tok = t0 + 16 * R + ln;
-                    if (tok >= p.T) continue;
-                    const long oi = (bh * p.T + tok) * p.dv + c4;
-                    if (p.o_bf16) {
-                        uint2 pk;
-                        pk.x = f32_to_bf16_bits(oacc[R][0]) | (static_cast<uint32_t>(f32_to_bf16_bits(oacc[R][1])) << 16);
-                        pk.y = f32_to_bf16_bits(oacc[R][2]) | (static_cast<uint32_t>(f32_to_bf16_bits(oacc[R][3])) << 16);
-                        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.o) + oi) = pk;
-                    } else {
-                        *reinterpret_cast<f32x4*>(static_cast<float*>(p.o) + oi) = oacc[R];
-                    }
-                }
-            }
+            for (int R = 0; R < 4; ++R) opend[R] = oacc[R];
             __syncthreads();
         }
+        if (nchunks > 0) store_o(nchunks - 1);
         if (p.ST) {
 #pragma unroll
             for (int ib = 0; ib < 8; ++ib)
