@@ -258,7 +258,24 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
                 }
             }
         };
+        // Key rows of a chunk as Y's A operands, and the state as x32 B operands
+        // (k = key channel).  The key tile of chunk c + 1 is in LDS while chunk
+        // c is processed (it is fetched two chunks ahead), so both are prepared
+        // at the end of chunk c, before the barrier the chain would otherwise
+        // wait at, and chunk c + 1 starts with its Y products.
+        bf16x8 ka[4][4], bS[4][2];
+        auto prep_next = [&](long cn) {
+            const uint16_t* sK = ktile(cn);
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    ka[t][b] = *reinterpret_cast<const bf16x8*>(sK + kq_off(16 * b + ln, 32 * t + 8 * g));
+#pragma unroll
+            for (int t = 0; t < 4; ++t) split_pair(sacc[2 * t], sacc[2 * t + 1], bS[t]);
+        };
         __syncthreads();  // the helpers have staged the first key tile
+        if (nchunks > 0) prep_next(0);
         __syncthreads();  // ... and prepared chunk 0
         for (long c = 0; c < nchunks; ++c) {
             const char* cur = smem + (c & 1) * BUF;
@@ -266,18 +283,6 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
             const uint16_t* sQ = reinterpret_cast<const uint16_t*>(cur + B_Q);
             const float* sc = reinterpret_cast<const float*>(cur + B_SC);
             const float* sVt = reinterpret_cast<const float*>(cur + B_VT) + (16 * wave + ln) * VTS;
-
-            // key rows for Y first: their LDS latency overlaps the state split
-            bf16x8 ka[4][4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-#pragma unroll
-                for (int b = 0; b < 4; ++b)
-                    ka[t][b] = *reinterpret_cast<const bf16x8*>(sK + kq_off(16 * b + ln, 32 * t + 8 * g));
-            // state as x32 B operands (k = key channel)
-            bf16x8 bS[4][2];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) split_pair(sacc[2 * t], sacc[2 * t + 1], bS[t]);
             // Y = K S and Z = Q S with raw bf16 rows as A operands.  The four row
             // blocks are independent accumulation chains; each k-step issues one
             // MFMA per block so consecutive MFMAs never wait on each other.
@@ -431,6 +436,7 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
             }
 #pragma unroll
             for (int R = 0; R < 4; ++R) opend[R] = oacc[R];
+            if (c + 1 < nchunks) prep_next(c + 1);
             __syncthreads();
         }
         if (nchunks > 0) store_o(nchunks - 1);
