@@ -13,9 +13,10 @@
 // DeltaNet-2" method section 1, with the "Preconditioned DeltaNet" 2.2 running
 // diagonal advanced in place when enabled.
 //
-// Work split: one 256-thread workgroup per (b,h).  Each thread owns a float4
-// column group and DK/NRG rows, so every wave-wide load or store covers whole
-// 512-byte (dv = 128) or 256-byte (dv = 64) rows: fully coalesced streaming.
+// Work split: 256-thread workgroups, each walking (b,h) pairs.  Each thread
+// owns a float4 column group and DK/NRG rows, so every wave-wide load or store
+// covers whole 512-byte (dv = 128) or 256-byte (dv = 64) rows: fully
+// coalesced streaming.
 #include "common.h"
 #include "kernels.h"
 
@@ -37,111 +38,129 @@ struct DecodeParams {
 };
 
 template <int DK, int DV, bool BF16IN, bool BF16OUT>
-__global__ void __launch_bounds__(256) decode_kernel(DecodeParams p) {
+__global__ void __launch_bounds__(256, 3) decode_kernel(DecodeParams p, long nbh) {
     constexpr int NCG = DV / 4;       // float4 column groups
     constexpr int NRG = 256 / NCG;    // row groups
     constexpr int RPT = DK / NRG;     // rows per thread
     static_assert(RPT * NRG == DK, "row split");
 
-    const long bh = blockIdx.x;
     const int tid = threadIdx.x;
     const int cg = tid % NCG;
     const int rg = tid / NCG;
-    float* S = p.S + bh * DK * DV;
-
-    // Issue the state stream first; the gate math below overlaps its latency.
-    f32x4 s[RPT];
-#pragma unroll
-    for (int m = 0; m < RPT; ++m)
-        s[m] = *reinterpret_cast<const f32x4*>(S + (long)(rg + NRG * m) * DV + 4 * cg);
 
     __shared__ float s_alpha[DK], s_kt[DK], s_q[DK], s_vt[DV], s_u[DV];
     __shared__ f32x4 s_red[NRG][2][NCG];
     __shared__ float s_kq[4];
 
-    if (tid < DK) {
-        const int i = tid;
-        const float kk = load_in<BF16IN>(p.k, bh * DK + i);
-        const float qq = load_in<BF16IN>(p.q, bh * DK + i);
-        float la = 0.0f;
-        if (p.alpha_mode == PDN_ALPHA_SCALAR) la = p.log_alpha[bh];
-        else if (p.alpha_mode == PDN_ALPHA_VEC) la = p.log_alpha[bh * DK + i];
-        float b = (p.beta_mode == PDN_GATE_SCALAR) ? p.beta[bh] : p.beta[bh * DK + i];
-        if (p.precond_eps >= 0.0f) {
-            const float A = p.precond_A[bh * DK + i] + kk * kk;
-            p.precond_A[bh * DK + i] = A;
-            b = b / (A + p.precond_eps);
+    // Persistent workgroups: each walks (b,h) pairs with a stride of the grid
+    // and loads the next pair's state while it finishes the current one, so
+    // the state stream never stalls on a workgroup's reduction and the grid
+    // has no tail.
+    auto load_state = [&](long bh, f32x4 (&s)[RPT]) {
+        const float* S = p.S + bh * DK * DV;
+#pragma unroll
+        for (int m = 0; m < RPT; ++m)
+            s[m] = *reinterpret_cast<const f32x4*>(S + (long)(rg + NRG * m) * DV + 4 * cg);
+    };
+    f32x4 s[RPT], sn[RPT];
+    long bh = blockIdx.x;
+    if (bh < nbh) load_state(bh, s);
+    for (; bh < nbh; bh += gridDim.x) {
+        const long bn = bh + gridDim.x;
+        if (bn < nbh) load_state(bn, sn);
+        float* S = p.S + bh * DK * DV;
+
+        if (tid < DK) {
+            const int i = tid;
+            const float kk = load_in<BF16IN>(p.k, bh * DK + i);
+            const float qq = load_in<BF16IN>(p.q, bh * DK + i);
+            float la = 0.0f;
+            if (p.alpha_mode == PDN_ALPHA_SCALAR) la = p.log_alpha[bh];
+            else if (p.alpha_mode == PDN_ALPHA_VEC) la = p.log_alpha[bh * DK + i];
+            float b = (p.beta_mode == PDN_GATE_SCALAR) ? p.beta[bh] : p.beta[bh * DK + i];
+            if (p.precond_eps >= 0.0f) {
+                const float A = p.precond_A[bh * DK + i] + kk * kk;
+                p.precond_A[bh * DK + i] = A;
+                b = b / (A + p.precond_eps);
+            }
+            const float kt = sqrtf(b) * kk;
+            s_alpha[i] = expf(la);
+            s_kt[i] = kt;
+            s_q[i] = qq;
+            const float part = wave_sum(kt * qq);
+            if ((tid & 63) == 0) s_kq[tid >> 6] = part;
         }
-        const float kt = sqrtf(b) * kk;
-        s_alpha[i] = expf(la);
-        s_kt[i] = kt;
-        s_q[i] = qq;
-        const float part = wave_sum(kt * qq);
-        if ((tid & 63) == 0) s_kq[tid >> 6] = part;
-    }
-    if (tid < DV) {
-        const int j = tid;
-        float g;
-        if (p.gamma_mode == PDN_GAMMA_SAME_AS_BETA)
-            g = (p.beta_mode == PDN_GATE_SCALAR) ? p.beta[bh] : p.beta[bh * DK + j];
-        else if (p.gamma_mode == PDN_GATE_SCALAR)
-            g = p.gamma[bh];
-        else
-            g = p.gamma[bh * DV + j];
-        s_vt[j] = sqrtf(g) * load_in<BF16IN>(p.v, bh * DV + j);
-    }
-    __syncthreads();
-
-    // A = Diag(alpha) S and the two partial column sums over this thread's rows.
-    f32x4 u = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int m = 0; m < RPT; ++m) {
-        const int row = rg + NRG * m;
-        s[m] *= s_alpha[row];
-        u += s[m] * s_kt[row];
-        pq += s[m] * s_q[row];
-    }
-    s_red[rg][0][cg] = u;
-    s_red[rg][1][cg] = pq;
-    __syncthreads();
-
-    if (tid < DV) {
-        const int j = tid;
-        float su = 0.0f, sp = 0.0f;
-#pragma unroll
-        for (int r = 0; r < NRG; ++r) {
-            su += s_red[r][0][j >> 2][j & 3];
-            sp += s_red[r][1][j >> 2][j & 3];
+        if (tid < DV) {
+            const int j = tid;
+            float g;
+            if (p.gamma_mode == PDN_GAMMA_SAME_AS_BETA)
+                g = (p.beta_mode == PDN_GATE_SCALAR) ? p.beta[bh] : p.beta[bh * DK + j];
+            else if (p.gamma_mode == PDN_GATE_SCALAR)
+                g = p.gamma[bh];
+            else
+                g = p.gamma[bh * DV + j];
+            s_vt[j] = sqrtf(g) * load_in<BF16IN>(p.v, bh * DV + j);
         }
-        float kq = s_kq[0];
-        if constexpr (DK > 64) kq += s_kq[1];
-        const float uj = s_vt[j] - su;
-        const float oj = sp + uj * kq;
-        if constexpr (BF16OUT)
-            static_cast<uint16_t*>(p.o)[bh * DV + j] = f32_to_bf16_bits(oj);
-        else
-            static_cast<float*>(p.o)[bh * DV + j] = oj;
-        s_u[j] = uj;
-    }
-    __syncthreads();
+        __syncthreads();
 
-    const f32x4 uc = *reinterpret_cast<const f32x4*>(&s_u[4 * cg]);
+        // A = Diag(alpha) S and the two partial column sums over this thread's rows.
+        f32x4 u = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int m = 0; m < RPT; ++m) {
-        const int row = rg + NRG * m;
-        s[m] += s_kt[row] * uc;
-        *reinterpret_cast<f32x4*>(S + (long)row * DV + 4 * cg) = s[m];
+        for (int m = 0; m < RPT; ++m) {
+            const int row = rg + NRG * m;
+            s[m] *= s_alpha[row];
+            u += s[m] * s_kt[row];
+            pq += s[m] * s_q[row];
+        }
+        s_red[rg][0][cg] = u;
+        s_red[rg][1][cg] = pq;
+        __syncthreads();
+
+        if (tid < DV) {
+            const int j = tid;
+            float su = 0.0f, sp = 0.0f;
+#pragma unroll
+            for (int r = 0; r < NRG; ++r) {
+                su += s_red[r][0][j >> 2][j & 3];
+                sp += s_red[r][1][j >> 2][j & 3];
+            }
+            float kq = s_kq[0];
+            if constexpr (DK > 64) kq += s_kq[1];
+            const float uj = s_vt[j] - su;
+            const float oj = sp + uj * kq;
+            if constexpr (BF16OUT)
+                static_cast<uint16_t*>(p.o)[bh * DV + j] = f32_to_bf16_bits(oj);
+            else
+                static_cast<float*>(p.o)[bh * DV + j] = oj;
+            s_u[j] = uj;
+        }
+        __syncthreads();
+
+        const f32x4 uc = *reinterpret_cast<const f32x4*>(&s_u[4 * cg]);
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) {
+            const int row = rg + NRG * m;
+            s[m] += s_kt[row] * uc;
+            *reinterpret_cast<f32x4*>(S + (long)row * DV + 4 * cg) = s[m];
+        }
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) s[m] = sn[m];
+        __syncthreads();  // the shared arrays are rewritten for the next pair
     }
 }
 
 template <int DK, int DV>
 hipError_t launch_dk_dv(const DecodeParams& p, bool bf16in, bool bf16out, long nbh,
                         hipStream_t st) {
-    dim3 grid(static_cast<unsigned>(nbh)), block(256);
-    if (bf16in && bf16out) decode_kernel<DK, DV, true, true><<<grid, block, 0, st>>>(p);
-    else if (bf16in) decode_kernel<DK, DV, true, false><<<grid, block, 0, st>>>(p);
-    else if (bf16out) decode_kernel<DK, DV, false, true><<<grid, block, 0, st>>>(p);
-    else decode_kernel<DK, DV, false, false><<<grid, block, 0, st>>>(p);
+    // exactly the resident workgroups (three per compute unit: the launch
+    // bounds keep the kernel within a third of the register file), each
+    // walking many (b,h) pairs
+    constexpr long kResident = 256L * 3;
+    dim3 grid(static_cast<unsigned>(nbh < kResident ? nbh : kResident)), block(256);
+    if (bf16in && bf16out) decode_kernel<DK, DV, true, true><<<grid, block, 0, st>>>(p, nbh);
+    else if (bf16in) decode_kernel<DK, DV, true, false><<<grid, block, 0, st>>>(p, nbh);
+    else if (bf16out) decode_kernel<DK, DV, false, true><<<grid, block, 0, st>>>(p, nbh);
+    else decode_kernel<DK, DV, false, false><<<grid, block, 0, st>>>(p, nbh);
     return hipGetLastError();
 }
 
