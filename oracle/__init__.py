@@ -31,6 +31,7 @@ _lib = None
 
 ALPHA_NONE, ALPHA_SCALAR, ALPHA_VEC = 0, 1, 2
 GATE_SCALAR, GATE_VEC, GAMMA_SAME_AS_BETA = 1, 2, 3
+KEY_SYMMETRIC, KEY_ERASE_GATE, KEY_WRITE_GATE = 0, 1, 2
 
 
 def build(force: bool = False) -> str:
@@ -53,7 +54,7 @@ def _load():
             P = ctypes.c_void_p
             I = ctypes.c_int
             f.argtypes = [I, I, I, I, I, P, P, P, I, P, I, P, I, P,
-                          ctypes.c_double, P, P, P, P, P]
+                          ctypes.c_double, P, P, P, P, P, I]
             f.restype = I
             lib.oracle_num_threads.argtypes = []
             lib.oracle_num_threads.restype = I
@@ -78,11 +79,12 @@ def _ptr(x):
 
 def delta_rule(q, k, v, alpha_mode, log_alpha, beta_mode, beta, gamma_mode,
                gamma, precond_eps: float = -1.0, A0=None, S0=None,
-               want_state: bool = True):
+               want_state: bool = True, key_mode: int = KEY_SYMMETRIC):
     """Run the fp64 recurrence.  Returns (o, S_T, A_T) as float64 arrays.
 
-    Shapes follow the C ABI: q, k [B,H,T,dk]; v [B,H,T,dv]; gates as in
-    ``recurrence.c``.  A_T is None unless the preconditioner is on.
+    Shapes follow the C ABI: q, k [B,H,T,dk]; v [B,H,T,dv]; gates and
+    ``key_mode`` as in ``recurrence.c``.  A_T is None unless the
+    preconditioner is on.
     """
     lib = _load()
     q, k, v = _f64(q), _f64(k), _f64(v)
@@ -96,7 +98,8 @@ def delta_rule(q, k, v, alpha_mode, log_alpha, beta_mode, beta, gamma_mode,
     rc = lib.oracle_delta_rule(B, H, T, dk, dv, _ptr(q), _ptr(k), _ptr(v),
                                int(alpha_mode), _ptr(la), int(beta_mode), _ptr(be),
                                int(gamma_mode), _ptr(ga), float(precond_eps),
-                               _ptr(A0), _ptr(AT), _ptr(S0), _ptr(ST), _ptr(o))
+                               _ptr(A0), _ptr(AT), _ptr(S0), _ptr(ST), _ptr(o),
+                               int(key_mode))
     if rc != 0:
         raise ValueError("oracle_delta_rule failed with code %d" % rc)
     return o, ST, AT
@@ -107,7 +110,20 @@ def run_workload(w, S0="from_workload", want_state=True):
     s0 = w.S0 if isinstance(S0, str) else S0
     return delta_rule(w.q, w.k, w.v, w.alpha_mode, w.log_alpha, w.beta_mode,
                       w.beta, w.gamma_mode, w.gamma, w.precond_eps, w.A0, s0,
-                      want_state=want_state)
+                      want_state=want_state, key_mode=getattr(w, "key_mode", KEY_SYMMETRIC))
+
+
+def keys_and_value(key_mode, b, g, k, v, gamma_same):
+    """Write key, read key and written value of one token for a key mode
+    (b: erase gain with the preconditioner folded in, g: value gain)."""
+    if key_mode == KEY_SYMMETRIC:
+        kw = np.sqrt(b) * k
+        return kw, kw, np.sqrt(g) * v
+    if key_mode == KEY_ERASE_GATE:
+        return k, b * k, g * v
+    if key_mode == KEY_WRITE_GATE:
+        return b * k, k, (v if gamma_same else g * v)
+    raise ValueError("unknown key mode %r" % (key_mode,))
 
 
 def _gates_per_token(alpha_mode, log_alpha, beta_mode, beta, gamma_mode, gamma,
@@ -137,7 +153,7 @@ def _gates_per_token(alpha_mode, log_alpha, beta_mode, beta, gamma_mode, gamma,
 
 
 def delta_rule_py(q, k, v, alpha_mode, log_alpha, beta_mode, beta, gamma_mode,
-                  gamma, precond_eps=-1.0, A0=None, S0=None):
+                  gamma, precond_eps=-1.0, A0=None, S0=None, key_mode=KEY_SYMMETRIC):
     """Numpy token loop for tiny inputs (same definition as the C oracle)."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, H, T, dk = q.shape
@@ -153,10 +169,10 @@ def delta_rule_py(q, k, v, alpha_mode, log_alpha, beta_mode, beta, gamma_mode,
                                                  precond_eps, sel(A0), k[b, h], dk, dv)
             S = np.zeros((dk, dv)) if S0 is None else _f64(S0)[b, h].copy()
             for t in range(T):
-                kt = np.sqrt(be[t]) * k[b, h, t]
-                vt = np.sqrt(ga[t]) * v[b, h, t]
+                kw, kr, vw = keys_and_value(key_mode, be[t], ga[t], k[b, h, t], v[b, h, t],
+                                            gamma_mode == GAMMA_SAME_AS_BETA)
                 Ad = alpha[t][:, None] * S
-                S = Ad + np.outer(kt, vt - Ad.T @ kt)
+                S = Ad + np.outer(kw, vw - Ad.T @ kr)
                 o[b, h, t] = S.T @ q[b, h, t]
             ST[b, h] = S
             if AT is not None:

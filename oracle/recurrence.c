@@ -27,6 +27,17 @@
  *                                           + kt vt^T   (FG^2-GDN, 2.1)
  *   o_t = S_t^T q_t                       read-out with the updated state
  *
+ * key_mode selects where the gains act (write key kw, read key kr, value vw;
+ * every mode is S_t = Ad + kw (vw - Ad^T kr)^T = (I - kw kr^T) Ad + kw vw^T):
+ *   0 symmetric   kw = kr = sqrt(beta') (.) k, vw = sqrt(gamma') (.) v   (above)
+ *   1 erase gate  kw = k, kr = beta' (.) k, vw = gamma' (.) v
+ *                 ("Gated DeltaNet-2" method 1: (I - k (b (.) k)^T) D S +
+ *                 k (w (.) v)^T with erase gate b = beta', write gate w = gamma')
+ *   2 write gate  kw = beta' (.) k, kr = k, vw = v if gamma is "same as beta"
+ *                 (the gain rides on the write key), else gamma (.) v
+ *                 ("Preconditioned DeltaNet" apply-to-key: the write key is
+ *                 transformed, the read key is k)
+ *
  * Layouts (row-major, contiguous): q, k [B,H,T,dk]; v, o [B,H,T,dv];
  * log_alpha [B,H,T] (scalar) or [B,H,T,dk] (vector); beta [B,H,T] or
  * [B,H,T,dk]; gamma [B,H,T] or [B,H,T,dv]; S0, ST [B,H,dk,dv]; A0, AT [B,H,dk].
@@ -44,6 +55,9 @@
 #define OR_GATE_SCALAR 1
 #define OR_GATE_VEC 2
 #define OR_GAMMA_SAME 3
+#define OR_KEY_SYMMETRIC 0
+#define OR_KEY_ERASE_GATE 1
+#define OR_KEY_WRITE_GATE 2
 
 /* Returns 0 on success, -1 on a bad argument, -2 when out of memory. */
 int oracle_delta_rule(int B, int H, int T, int dk, int dv,
@@ -52,7 +66,7 @@ int oracle_delta_rule(int B, int H, int T, int dk, int dv,
                       int beta_mode, const double *beta,
                       int gamma_mode, const double *gamma,
                       double precond_eps, const double *A0, double *AT,
-                      const double *S0, double *ST, double *o)
+                      const double *S0, double *ST, double *o, int key_mode)
 {
     if (B < 0 || H < 0 || T < 0 || dk <= 0 || dv <= 0) return -1;
     if (alpha_mode != OR_ALPHA_NONE && alpha_mode != OR_ALPHA_SCALAR &&
@@ -63,6 +77,8 @@ int oracle_delta_rule(int B, int H, int T, int dk, int dv,
     if (gamma_mode == OR_GAMMA_SAME && beta_mode == OR_GATE_VEC && dk != dv) return -1;
     if (alpha_mode != OR_ALPHA_NONE && !log_alpha) return -1;
     if (!beta || (gamma_mode != OR_GAMMA_SAME && !gamma)) return -1;
+    if (key_mode != OR_KEY_SYMMETRIC && key_mode != OR_KEY_ERASE_GATE &&
+        key_mode != OR_KEY_WRITE_GATE) return -1;
 
     const long BH = (long)B * H;
     int failed = 0;
@@ -73,12 +89,13 @@ int oracle_delta_rule(int B, int H, int T, int dk, int dv,
         double *A = (double *)malloc(sizeof(double) * (size_t)dk);
         double *al = (double *)malloc(sizeof(double) * (size_t)dk);
         double *kt = (double *)malloc(sizeof(double) * (size_t)dk);
+        double *kr = (double *)malloc(sizeof(double) * (size_t)dk);
         double *vt = (double *)malloc(sizeof(double) * (size_t)dv);
         double *u = (double *)malloc(sizeof(double) * (size_t)dv);
-        if (!S || !A || !al || !kt || !vt || !u) {
+        if (!S || !A || !al || !kt || !kr || !vt || !u) {
 #pragma omp atomic write
             failed = 1;
-            free(S); free(A); free(al); free(kt); free(vt); free(u);
+            free(S); free(A); free(al); free(kt); free(kr); free(vt); free(u);
             continue;
         }
         if (S0) memcpy(S, S0 + bh * dk * dv, sizeof(double) * (size_t)dk * dv);
@@ -97,14 +114,24 @@ int oracle_delta_rule(int B, int H, int T, int dk, int dv,
                 else if (alpha_mode == OR_ALPHA_SCALAR) al[i] = exp(log_alpha[tok]);
                 else al[i] = exp(log_alpha[tok * dk + i]);
             }
-            /* key-side gain, with the preconditioner folded in */
+            /* key-side gain, with the preconditioner folded in; kt is the
+               write key and kr the read key */
             for (int i = 0; i < dk; ++i) {
                 double b = (beta_mode == OR_GATE_SCALAR) ? beta[tok] : beta[tok * dk + i];
                 if (precond_eps >= 0.0) {
                     A[i] += kk[i] * kk[i];
                     b = b / (A[i] + precond_eps);
                 }
-                kt[i] = sqrt(b) * kk[i];
+                if (key_mode == OR_KEY_SYMMETRIC) {
+                    kt[i] = sqrt(b) * kk[i];
+                    kr[i] = kt[i];
+                } else if (key_mode == OR_KEY_ERASE_GATE) {
+                    kt[i] = kk[i];
+                    kr[i] = b * kk[i];
+                } else {
+                    kt[i] = b * kk[i];
+                    kr[i] = kk[i];
+                }
             }
             /* value-side gain */
             for (int j = 0; j < dv; ++j) {
@@ -113,15 +140,17 @@ int oracle_delta_rule(int B, int H, int T, int dk, int dv,
                     g = (beta_mode == OR_GATE_SCALAR) ? beta[tok] : beta[tok * dk + j];
                 else if (gamma_mode == OR_GATE_SCALAR) g = gamma[tok];
                 else g = gamma[tok * dv + j];
-                vt[j] = sqrt(g) * vv[j];
+                if (key_mode == OR_KEY_SYMMETRIC) vt[j] = sqrt(g) * vv[j];
+                else if (key_mode == OR_KEY_WRITE_GATE && gamma_mode == OR_GAMMA_SAME) vt[j] = vv[j];
+                else vt[j] = g * vv[j];
             }
             /* S <- Diag(alpha) S */
             for (int i = 0; i < dk; ++i)
                 for (int j = 0; j < dv; ++j) S[(long)i * dv + j] *= al[i];
-            /* u = vt - S^T kt */
+            /* u = vt - S^T kr */
             for (int j = 0; j < dv; ++j) u[j] = vt[j];
             for (int i = 0; i < dk; ++i)
-                for (int j = 0; j < dv; ++j) u[j] -= S[(long)i * dv + j] * kt[i];
+                for (int j = 0; j < dv; ++j) u[j] -= S[(long)i * dv + j] * kr[i];
             /* S <- S + kt u^T */
             for (int i = 0; i < dk; ++i)
                 for (int j = 0; j < dv; ++j) S[(long)i * dv + j] += kt[i] * u[j];
@@ -133,7 +162,7 @@ int oracle_delta_rule(int B, int H, int T, int dk, int dv,
         }
         if (ST) memcpy(ST + bh * dk * dv, S, sizeof(double) * (size_t)dk * dv);
         if (AT) for (int i = 0; i < dk; ++i) AT[bh * dk + i] = A[i];
-        free(S); free(A); free(al); free(kt); free(vt); free(u);
+        free(S); free(A); free(al); free(kt); free(kr); free(vt); free(u);
     }
     return failed ? -2 : 0;
 }

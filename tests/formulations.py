@@ -11,15 +11,18 @@ pinned separately by closed forms in ``test_oracle.py``.
 import numpy as np
 
 from oracle import ALPHA_NONE, ALPHA_SCALAR, ALPHA_VEC, GATE_SCALAR, GATE_VEC, GAMMA_SAME_AS_BETA
-from oracle import _gates_per_token, _f64
+from oracle import KEY_SYMMETRIC
+from oracle import _gates_per_token, _f64, keys_and_value
 
 
 def unrolled_product(q, k, v, alpha_mode, log_alpha, beta_mode, beta, gamma_mode,
-                     gamma, precond_eps=-1.0, A0=None, S0=None):
+                     gamma, precond_eps=-1.0, A0=None, S0=None, key_mode=KEY_SYMMETRIC):
     """Explicit transition-matrix form for tiny inputs.
 
-    With M_t = (I - kt kt^T) Diag(alpha_t) and Phi_{t:s} = M_t ... M_s,
-        S_t = Phi_{t:1} S_0 + sum_{s<=t} Phi_{t:s+1} kt_s vt_s^T,
+    With write key kw, read key kr and written value vw of each token (equal
+    keys kt in the symmetric mode), M_t = (I - kw_t kr_t^T) Diag(alpha_t) and
+    Phi_{t:s} = M_t ... M_s,
+        S_t = Phi_{t:1} S_0 + sum_{s<=t} Phi_{t:s+1} kw_s vw_s^T,
     which is the closed form of the delta rule written as a diagonal-plus-
     low-rank linear recurrence (FG^2-GDN, 2.1 and 2.3).
     """
@@ -35,9 +38,12 @@ def unrolled_product(q, k, v, alpha_mode, log_alpha, beta_mode, beta, gamma_mode
             alpha, be, ga, _ = _gates_per_token(alpha_mode, sel(log_alpha), beta_mode,
                                                 sel(beta), gamma_mode, sel(gamma),
                                                 precond_eps, sel(A0), k[b, h], dk, dv)
-            kts = [np.sqrt(be[t]) * k[b, h, t] for t in range(T)]
-            vts = [np.sqrt(ga[t]) * v[b, h, t] for t in range(T)]
-            Ms = [(I - np.outer(kts[t], kts[t])) @ np.diag(alpha[t]) for t in range(T)]
+            kv = [keys_and_value(key_mode, be[t], ga[t], k[b, h, t], v[b, h, t],
+                                 gamma_mode == GAMMA_SAME_AS_BETA) for t in range(T)]
+            kts = [x[0] for x in kv]
+            krs = [x[1] for x in kv]
+            vts = [x[2] for x in kv]
+            Ms = [(I - np.outer(kts[t], krs[t])) @ np.diag(alpha[t]) for t in range(T)]
             S0bh = np.zeros((dk, dv)) if S0 is None else _f64(S0)[b, h]
             for t in range(T):
                 # Phi_{t:1}
@@ -59,16 +65,17 @@ def unrolled_product(q, k, v, alpha_mode, log_alpha, beta_mode, beta, gamma_mode
 
 
 def chunked_wy(q, k, v, alpha_mode, log_alpha, beta_mode, beta, gamma_mode,
-               gamma, precond_eps=-1.0, A0=None, S0=None, C=16):
+               gamma, precond_eps=-1.0, A0=None, S0=None, C=16, key_mode=KEY_SYMMETRIC):
     """Chunkwise-parallel form with a per-chunk unit-lower-triangular solve.
 
     Within a chunk (positions r = 1..C, cumulative log-decay G_r per key
-    channel, Gamma_r = exp(G_r)):
-        T_rs = sum_i kt_ri kt_si exp(G_ri - G_si)            (s < r)
-        P_rs = sum_i q_ri  kt_si exp(G_ri - G_si)            (s <= r)
-        (I + T) U = Vt - (Kt (.) Gamma) S_0                    (forward solve)
+    channel, Gamma_r = exp(G_r), write keys Kw, read keys Kr, written values
+    Vw; Kw = Kr = Kt in the symmetric mode):
+        T_rs = sum_i kr_ri kw_si exp(G_ri - G_si)            (s < r)
+        P_rs = sum_i q_ri  kw_si exp(G_ri - G_si)            (s <= r)
+        (I + T) U = Vw - (Kr (.) Gamma) S_0                    (forward solve)
         O = (Q (.) Gamma) S_0 + P U
-        S_C = Diag(Gamma_C) S_0 + (Kt (.) exp(G_C - G))^T U
+        S_C = Diag(Gamma_C) S_0 + (Kw (.) exp(G_C - G))^T U
     This is the UT/WY chunk algorithm the pages describe (Gated DeltaNet-2,
     "chunk parallel training": the decay absorbed into the erase/write
     matrices and a lower-triangular (I+T)^-1 solve).  fp64, for pins only.
@@ -88,8 +95,11 @@ def chunked_wy(q, k, v, alpha_mode, log_alpha, beta_mode, beta, gamma_mode,
             S = np.zeros((dk, dv)) if S0 is None else _f64(S0)[b, h].copy()
             for c0 in range(0, T, C):
                 c1 = min(c0 + C, T)
-                Kt = np.sqrt(be[c0:c1]) * k[b, h, c0:c1]
-                Vt = np.sqrt(ga[c0:c1]) * v[b, h, c0:c1]
+                kv = [keys_and_value(key_mode, be[t], ga[t], k[b, h, t], v[b, h, t],
+                                     gamma_mode == GAMMA_SAME_AS_BETA) for t in range(c0, c1)]
+                Kt = np.array([x[0] for x in kv])
+                Kr = np.array([x[1] for x in kv])
+                Vt = np.array([x[2] for x in kv])
                 Q = q[b, h, c0:c1]
                 G = np.cumsum(logal[c0:c1], axis=0)
                 n = c1 - c0
@@ -99,9 +109,9 @@ def chunked_wy(q, k, v, alpha_mode, log_alpha, beta_mode, beta, gamma_mode,
                     for s in range(r + 1):
                         dec = np.exp(G[r] - G[s])
                         if s < r:
-                            Tm[r, s] = np.sum(Kt[r] * Kt[s] * dec)
+                            Tm[r, s] = np.sum(Kr[r] * Kt[s] * dec)
                         Pm[r, s] = np.sum(Q[r] * Kt[s] * dec)
-                rhs = Vt - (Kt * np.exp(G)) @ S
+                rhs = Vt - (Kr * np.exp(G)) @ S
                 U = np.linalg.solve(np.eye(n) + Tm, rhs)
                 o[b, h, c0:c1] = (Q * np.exp(G)) @ S + Pm @ U
                 S = np.exp(G[-1])[:, None] * S + (Kt * np.exp(G[-1] - G)).T @ U

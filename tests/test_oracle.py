@@ -366,3 +366,114 @@ def test_planted_pairs_are_recalled_without_decay():
     T = w.T
     assert np.array_equal(w.q[0, 0, T - 8:], w.k[0, 0, pos][perm])
     assert np.array_equal(w.v[0, 0, pos][perm], w.v[0, 0, pos[perm]])
+
+
+# ---------------------------------------------------------------------------
+# read / write key modes: Gated DeltaNet-2's erase gate (method 1) and
+# Preconditioned DeltaNet's apply-to-key write key
+# ---------------------------------------------------------------------------
+
+KEY_MODES = [oracle.KEY_ERASE_GATE, oracle.KEY_WRITE_GATE]
+ASYM_GATES = [
+    (ALPHA_VEC, GATE_VEC, GATE_VEC, False),
+    (ALPHA_VEC, GATE_VEC, GAMMA_SAME_AS_BETA, True),
+    (ALPHA_SCALAR, GATE_SCALAR, GATE_SCALAR, True),
+    (ALPHA_NONE, GATE_VEC, GATE_SCALAR, False),
+]
+
+
+@pytest.mark.parametrize("key_mode", KEY_MODES)
+@pytest.mark.parametrize("amode", [ALPHA_NONE, ALPHA_SCALAR, ALPHA_VEC])
+def test_key_modes_reduce_to_tied_scalar_gain(key_mode, amode):
+    # With one scalar gain per token serving as erase gate, write gate and
+    # key gain, the erase-gate and apply-to-key updates are both
+    # (I - beta k k^T) D S + beta k v^T: the symmetric form (Gated DeltaNet /
+    # KDA), which the pins above fix.
+    rng = np.random.default_rng(40)
+    c = _rand_case(rng, 1, 2, 23, 6, 5, amode, GATE_SCALAR, GAMMA_SAME_AS_BETA)
+    o_ref, S_ref, _ = oracle.delta_rule(**c)
+    o, S, _ = oracle.delta_rule(**c, key_mode=key_mode)
+    np.testing.assert_allclose(o, o_ref, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(S, S_ref, rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("key_mode", KEY_MODES)
+@pytest.mark.parametrize("gmode", [GAMMA_SAME_AS_BETA, GATE_VEC])
+def test_key_modes_read_back_the_written_value(key_mode, gmode):
+    # The fast-weight view of the update ("Gated DeltaNet-2" method 2): one
+    # step edits the memory so that reading it with the read key returns the
+    # gated target, whenever write key . read key = 1.  The read key is
+    # e = b (.) k for the erase gate and the plain key for apply-to-key
+    # (whose write key carries the gain); the target is w (.) v for the erase
+    # gate, and v (or gamma (.) v) for apply-to-key.  Reading with the other
+    # key does not return it, so a swap of the two keys fails here.
+    rng = np.random.default_rng(41)
+    dk = 5
+    dv = dk if gmode == GAMMA_SAME_AS_BETA else 4   # a vector gain read as gamma needs dk == dv
+    k = rng.standard_normal(dk)
+    b = rng.uniform(0.2, 0.9, dk)
+    k /= np.sqrt(np.sum(b * k * k))           # b (.) k . k = 1
+    v = rng.standard_normal(dv)
+    g = rng.uniform(0.2, 0.9, dv) if gmode == GATE_VEC else None
+    S0 = rng.standard_normal((dk, dv))
+    la = -rng.uniform(0.05, 0.5, dk)
+    o, S, _ = oracle.delta_rule(np.zeros((1, 1, 1, dk)), k[None, None, None], v[None, None, None],
+                                ALPHA_VEC, la[None, None, None], GATE_VEC, b[None, None, None],
+                                gmode, None if g is None else g[None, None, None],
+                                S0=S0[None, None], key_mode=key_mode)
+    S = S[0, 0]
+    if key_mode == oracle.KEY_ERASE_GATE:
+        read, other = b * k, k
+        target = (b if gmode == GAMMA_SAME_AS_BETA else g) * v
+    else:
+        read, other = k, b * k
+        target = v if gmode == GAMMA_SAME_AS_BETA else g * v
+    np.testing.assert_allclose(S.T @ read, target, rtol=1e-12, atol=1e-12)
+    assert np.linalg.norm(S.T @ other - target) > 1e-3
+
+
+@pytest.mark.parametrize("key_mode", KEY_MODES)
+@pytest.mark.parametrize("amode,bmode,gmode,pre", ASYM_GATES)
+def test_key_modes_match_unrolled_transition_product(key_mode, amode, bmode, gmode, pre):
+    rng = np.random.default_rng(42)
+    dv = 4 if not (gmode == GAMMA_SAME_AS_BETA and bmode == GATE_VEC) else 5
+    c = _rand_case(rng, 1, 2, 7, 5, dv, amode, bmode, gmode, pre, a0=pre)
+    o, ST, _ = oracle.delta_rule(**c, key_mode=key_mode)
+    o2, ST2 = unrolled_product(**c, key_mode=key_mode)
+    np.testing.assert_allclose(o, o2, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(ST, ST2, rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("key_mode", KEY_MODES)
+@pytest.mark.parametrize("amode,bmode,gmode,pre", ASYM_GATES)
+@pytest.mark.parametrize("T,C", [(37, 16), (5, 16)])
+def test_key_modes_match_chunked_wy_form(key_mode, amode, bmode, gmode, pre, T, C):
+    rng = np.random.default_rng(43)
+    dv = 8 if not (gmode == GAMMA_SAME_AS_BETA and bmode == GATE_VEC) else 6
+    c = _rand_case(rng, 2, 1, T, 6, dv, amode, bmode, gmode, pre)
+    o, ST, _ = oracle.delta_rule(**c, key_mode=key_mode)
+    o2, ST2 = chunked_wy(**c, C=C, key_mode=key_mode)
+    assert rel_l2(o2, o) < 1e-11
+    assert rel_l2(ST2, ST) < 1e-11
+
+
+@pytest.mark.parametrize("key_mode", KEY_MODES)
+def test_key_modes_c_oracle_matches_numpy_loop(key_mode):
+    rng = np.random.default_rng(44)
+    c = _rand_case(rng, 2, 2, 9, 4, 4, ALPHA_VEC, GATE_VEC, GATE_VEC, True, a0=True)
+    o, ST, AT = oracle.delta_rule(**c, key_mode=key_mode)
+    o2, ST2, AT2 = oracle.delta_rule_py(**c, key_mode=key_mode)
+    np.testing.assert_allclose(o, o2, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(ST, ST2, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(AT, AT2, rtol=1e-12, atol=1e-14)
+
+
+def test_key_modes_differ_with_vector_gains():
+    # with a per-channel gain the three modes are three different recurrences
+    rng = np.random.default_rng(45)
+    c = _rand_case(rng, 1, 1, 12, 5, 5, ALPHA_VEC, GATE_VEC, GATE_VEC)
+    outs = [oracle.delta_rule(**c, key_mode=m)[0] for m in
+            (oracle.KEY_SYMMETRIC, oracle.KEY_ERASE_GATE, oracle.KEY_WRITE_GATE)]
+    for i in range(3):
+        for j in range(i + 1, 3):
+            assert rel_l2(outs[i], outs[j]) > 1e-3
