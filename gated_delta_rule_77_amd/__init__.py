@@ -27,6 +27,7 @@ PDN_OK, PDN_EINVAL, PDN_EUNSUPPORTED, PDN_EWORKSPACE, PDN_EHIP = 0, -1, -2, -3, 
 PDN_F32, PDN_BF16 = 0, 1
 PDN_ALPHA_NONE, PDN_ALPHA_SCALAR, PDN_ALPHA_VEC = 0, 1, 2
 PDN_GATE_SCALAR, PDN_GATE_VEC, PDN_GAMMA_SAME_AS_BETA = 1, 2, 3
+PDN_KEY_SYMMETRIC, PDN_KEY_ERASE_GATE, PDN_KEY_WRITE_GATE = 0, 1, 2
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int32
@@ -40,6 +41,7 @@ class ChunkFwdArgs(ctypes.Structure):
                 ("alpha_mode", _I), ("log_alpha", _P),
                 ("beta_mode", _I), ("beta", _P),
                 ("gamma_mode", _I), ("gamma", _P),
+                ("key_mode", _I),
                 ("precond_eps", ctypes.c_float), ("precond_A0", _P), ("precond_AT", _P),
                 ("S0", _P), ("ST", _P), ("o", _P),
                 ("workspace", _P), ("workspace_bytes", ctypes.c_size_t)]
@@ -53,6 +55,7 @@ class DecodeArgs(ctypes.Structure):
                 ("alpha_mode", _I), ("log_alpha", _P),
                 ("beta_mode", _I), ("beta", _P),
                 ("gamma_mode", _I), ("gamma", _P),
+                ("key_mode", _I),
                 ("precond_eps", ctypes.c_float), ("precond_A", _P),
                 ("S", _P), ("o", _P)]
 
@@ -164,7 +167,7 @@ def _gate_mode(g, lead):
 
 
 def _chunk_args(q, k, v, o, log_alpha, beta, gamma, precond_eps, precond_A0,
-                precond_AT, S0, ST, workspace):
+                precond_AT, S0, ST, workspace, key_mode):
     B, H, T, dk = q.shape
     dv = v.shape[-1]
     if tuple(k.shape) != (B, H, T, dk) or tuple(v.shape[:3]) != (B, H, T):
@@ -187,6 +190,7 @@ def _chunk_args(q, k, v, o, log_alpha, beta, gamma, precond_eps, precond_A0,
     a.beta = _ptr(beta)
     a.gamma_mode = PDN_GAMMA_SAME_AS_BETA if gamma is None else _gate_mode(gamma, 3)
     a.gamma = _ptr(gamma)
+    a.key_mode = int(key_mode)
     a.precond_eps = -1.0 if precond_eps is None else float(precond_eps)
     a.precond_A0, a.precond_AT = _ptr(precond_A0), _ptr(precond_AT)
     a.S0, a.ST = _ptr(S0), _ptr(ST)
@@ -198,9 +202,9 @@ def _chunk_args(q, k, v, o, log_alpha, beta, gamma, precond_eps, precond_A0,
 
 def pdn_chunk_fwd_workspace_size(q, k, v, o, log_alpha=None, beta=None, gamma=None,
                                  precond_eps=None, precond_A0=None, precond_AT=None,
-                                 S0=None, ST=None) -> int:
+                                 S0=None, ST=None, key_mode=PDN_KEY_SYMMETRIC) -> int:
     a = _chunk_args(q, k, v, o, log_alpha, beta, gamma, precond_eps, precond_A0,
-                    precond_AT, S0, ST, None)
+                    precond_AT, S0, ST, None, key_mode)
     n = ctypes.c_size_t(0)
     rc = load_library().pdn_chunk_fwd_workspace_size(ctypes.byref(a), ctypes.byref(n))
     if rc != PDN_OK:
@@ -210,12 +214,13 @@ def pdn_chunk_fwd_workspace_size(q, k, v, o, log_alpha=None, beta=None, gamma=No
 
 def pdn_chunk_fwd(q, k, v, o, log_alpha=None, beta=None, gamma=None, precond_eps=None,
                   precond_A0=None, precond_AT=None, S0=None, ST=None, workspace=None,
-                  stream=None) -> None:
+                  stream=None, key_mode=PDN_KEY_SYMMETRIC) -> None:
     """Prefill.  Tensors are device tensors in the layouts of include/pdn.h.
 
     The gate modes follow from the tensors' ranks: log_alpha None / [B,H,T] /
     [B,H,T,dk]; beta [B,H,T] / [B,H,T,dk]; gamma None (same as beta) / [B,H,T]
-    / [B,H,T,dv].  o (float32 or bfloat16) receives the output; ST and
+    / [B,H,T,dv].  key_mode is one of PDN_KEY_*.  o (float32 or bfloat16)
+    receives the output; ST and
     precond_AT, when given, receive the final state and running k(.)k sum.
     workspace: a device tensor of at least pdn_chunk_fwd_workspace_size() bytes.
     When None and the call needs one, it is allocated here with torch's caching
@@ -223,7 +228,7 @@ def pdn_chunk_fwd(q, k, v, o, log_alpha=None, beta=None, gamma=None, precond_eps
     stream; pass one explicitly when launching on another stream.
     """
     a = _chunk_args(q, k, v, o, log_alpha, beta, gamma, precond_eps, precond_A0,
-                    precond_AT, S0, ST, workspace)
+                    precond_AT, S0, ST, workspace, key_mode)
     lib = load_library()
     if workspace is None:
         n = ctypes.c_size_t(0)
@@ -240,7 +245,7 @@ def pdn_chunk_fwd(q, k, v, o, log_alpha=None, beta=None, gamma=None, precond_eps
         raise PdnError(rc, "pdn_chunk_fwd")
 
 
-def _decode_args(q, k, v, o, S, log_alpha, beta, gamma, precond_eps, precond_A):
+def _decode_args(q, k, v, o, S, log_alpha, beta, gamma, precond_eps, precond_A, key_mode):
     B, H, dk = q.shape
     dv = v.shape[-1]
     if tuple(k.shape) != (B, H, dk) or tuple(v.shape[:2]) != (B, H):
@@ -262,15 +267,18 @@ def _decode_args(q, k, v, o, S, log_alpha, beta, gamma, precond_eps, precond_A):
     a.beta = _ptr(beta)
     a.gamma_mode = PDN_GAMMA_SAME_AS_BETA if gamma is None else _gate_mode(gamma, 2)
     a.gamma = _ptr(gamma)
+    a.key_mode = int(key_mode)
     a.precond_eps = -1.0 if precond_eps is None else float(precond_eps)
     a.precond_A = _ptr(precond_A)
     return a
 
 
 def pdn_decode_step(q, k, v, o, S, log_alpha=None, beta=None, gamma=None,
-                    precond_eps=None, precond_A=None, stream=None) -> None:
+                    precond_eps=None, precond_A=None, stream=None,
+                    key_mode=PDN_KEY_SYMMETRIC) -> None:
     """One decode token for all (b,h); S (and precond_A) updated in place."""
-    a = _decode_args(q, k, v, o, S, log_alpha, beta, gamma, precond_eps, precond_A)
+    a = _decode_args(q, k, v, o, S, log_alpha, beta, gamma, precond_eps, precond_A,
+                     key_mode)
     rc = load_library().pdn_decode_step(ctypes.byref(a), _stream(stream))
     if rc != PDN_OK:
         raise PdnError(rc, "pdn_decode_step")

@@ -772,7 +772,7 @@ bool chunk_fact_supported(const pdn_chunk_fwd_args& a) {
     return a.qkv_dtype == PDN_BF16 && a.dk == DK && a.dv % DVT == 0 &&
            static_cast<long>(a.T) * DK * 2 <= 0x7fffffffL &&
            a.alpha_mode != PDN_ALPHA_VEC && a.beta_mode == PDN_GATE_SCALAR &&
-           a.precond_eps < 0.0f;
+           a.precond_eps < 0.0f && a.key_mode == PDN_KEY_SYMMETRIC;
 }
 
 hipError_t launch_chunk_fact(const pdn_chunk_fwd_args& a, hipStream_t stream) {

@@ -5,20 +5,27 @@
 // the cumulative decay goes into the erase/write matrices and each chunk
 // solves one unit-lower-triangular system; "FG^2-GDN" 2.3: the transition is
 // diagonal plus low rank).  With G_ri the cumulative log2 decay of channel i
-// from the chunk start, Gamma = 2^G, kt_r = sqrt(beta'_r) (.) k_r and
-// vt_r = sqrt(gamma_r) (.) v_r:
+// from the chunk start, Gamma = 2^G, and per token a read key kr_r (the one
+// the state is read with), a write key kw_r (the one the correction is
+// written along) and a written value vw_r:
 //
-//   T_rs = sum_i kt_ri kt_si 2^(G_ri - G_si)          s < r
-//   P_rs = sum_i q_ri  kt_si 2^(G_ri - G_si)          s <= r
-//   U    = (I + T)^-1 (Vt - (Kt . Gamma) S)
+//   T_rs = sum_i kr_ri kw_si 2^(G_ri - G_si)          s < r
+//   P_rs = sum_i q_ri  kw_si 2^(G_ri - G_si)          s <= r
+//   U    = (I + T)^-1 (Vw - (Kr . Gamma) S)
 //   O    = (Q . Gamma) S + P U
-//   S   <- Diag(Gamma_31) S + (Kt . 2^(G_31 - G))^T U
+//   S   <- Diag(Gamma_31) S + (Kw . 2^(G_31 - G))^T U
+//
+// Symmetric keys: kr = kw = sqrt(beta') (.) k, vw = sqrt(gamma) (.) v.  Erase
+// gate ("Gated DeltaNet-2" method section 1): kw = k, kr = beta' (.) k,
+// vw = gamma (.) v.  Write gate ("Preconditioned DeltaNet" 2.2, the gain on
+// the write key): kw = beta' (.) k, kr = k, vw = v (gamma (.) v when a
+// separate value gain is given).
 //
 // Everything that depends only on q, k and the gates is independent across
 // chunks, so it runs first, fully parallel over (b, h, chunk):
 //
 //   vec_prep_kernel (one wave per chunk) forms the gate-scaled operands
-//     Kg = Kt . Gamma, Qg = Q . Gamma, Kd = Kt . 2^(G_31 - G), the blocks of T
+//     Kg = Kr . Gamma, Qg = Q . Gamma, Kd = Kw . 2^(G_31 - G), the blocks of T
 //     and P (fp32 MFMAs), the inverses D_R = (I + T_RR)^-1 of the two 16x16
 //     diagonal blocks and N = D_1 T_10, and writes them as one chunk record
 //     to the workspace: bf16 hi/lo tiles and MFMA fragments laid out exactly
@@ -100,12 +107,16 @@ struct PrepParams {
     int has_alpha;
 };
 
+// How the written value follows from v and the value gain gamma.
+enum { VAL_SQRT_GAIN = 0, VAL_GAIN = 1, VAL_UNIT = 2 };
+
 struct ChainParams {
     const uint16_t* v;
     const char* rec;
     const float* gsrc;
     long gts;
     int gvec;
+    int vmode;  // VAL_*
     const float* S0;
     float* ST;
     void* o;
@@ -268,11 +279,12 @@ __global__ void __launch_bounds__(KSCAN_SEG * DK) vec_kscan_kernel(float* ks, co
 // Gram blocks are formed straight from registers with 16x16x4 fp32 MFMAs
 // (k-slot g of MFMA (t, j) is channel 32t + 8g + j).  Results in accumulator
 // layout (lane (ln, g) holds rows 4g + e, column ln):
-//   T_RR with A = Kt 2^(Gm - G) rows, B = Kt 2^(G - Gm) rows gives T_RR^T, i.e.
+//   T_RR with A = Kw 2^(Gm - G) rows, B = Kr 2^(G - Gm) rows gives T_RR^T, i.e.
 //     lane (ln, g) holds row ln, columns 4g + e of T_RR;
-//   T_10 with A = block-1 rows 2^(G - G_15), B = block-0 rows 2^(G_15 - G);
-//   P_RS with A = block-S key rows, B = block-R query rows gives P_RS^T.
-template <bool AVEC, bool BVEC, bool PRE>
+//   T_10 with A = block-1 Kr rows 2^(G - G_15), B = block-0 Kw rows 2^(G_15 - G);
+//   P_RS with A = block-S write-key rows, B = block-R query rows gives P_RS^T.
+// KM is the key mode (PDN_KEY_*).
+template <bool AVEC, bool BVEC, bool PRE, int KM>
 __global__ void __launch_bounds__(256) vec_prep_kernel(PrepParams p) {
     __shared__ __attribute__((aligned(16))) float scr_all[4][2 * SCR_STRIDE];
     const int lane = threadIdx.x & 63;
@@ -303,10 +315,11 @@ __global__ void __launch_bounds__(256) vec_prep_kernel(PrepParams p) {
     }
     Decay ds;
     if constexpr (!AVEC) ds = decay_factors(lgs[0], lgs[1]);
+    // per-token key gain: sqrt(beta') for symmetric keys, else beta' itself
     float sbs[2] = {0.0f, 0.0f};
     if constexpr (!BVEC && !PRE) {
-        sbs[0] = sqrt_hw(bes[0]);
-        sbs[1] = sqrt_hw(bes[1]);
+        sbs[0] = KM == PDN_KEY_SYMMETRIC ? sqrt_hw(bes[0]) : bes[0];
+        sbs[1] = KM == PDN_KEY_SYMMETRIC ? sqrt_hw(bes[1]) : bes[1];
     }
 
     f32x4 t00 = {0.f, 0.f, 0.f, 0.f}, t11 = t00, t10 = t00, p00 = t00, p11 = t00, p10 = t00;
@@ -388,27 +401,31 @@ __global__ void __launch_bounds__(256) vec_prep_kernel(PrepParams p) {
                     b0 *= __builtin_amdgcn_rcpf(a0 + p.eps);
                     b1 *= __builtin_amdgcn_rcpf(a1 + p.eps);
                 }
-                sb0 = sqrt_hw(b0);
-                sb1 = sqrt_hw(b1);
+                sb0 = KM == PDN_KEY_SYMMETRIC ? sqrt_hw(b0) : b0;
+                sb1 = KM == PDN_KEY_SYMMETRIC ? sqrt_hw(b1) : b1;
             } else {
                 sb0 = sbs[0];
                 sb1 = sbs[1];
             }
-            const float kt0 = sb0 * k0, kt1 = sb1 * k1;
-            kg[0][j] = kt0 * d.gm0;
-            kg[1][j] = kt1 * d.gm1;
+            // read and write keys (the same value for symmetric keys)
+            const float kr0 = KM == PDN_KEY_WRITE_GATE ? k0 : sb0 * k0;
+            const float kr1 = KM == PDN_KEY_WRITE_GATE ? k1 : sb1 * k1;
+            const float kw0 = KM == PDN_KEY_ERASE_GATE ? k0 : sb0 * k0;
+            const float kw1 = KM == PDN_KEY_ERASE_GATE ? k1 : sb1 * k1;
+            kg[0][j] = kr0 * d.gm0;
+            kg[1][j] = kr1 * d.gm1;
             qg[0][j] = q0 * d.gm0;
             qg[1][j] = q1 * d.gm1;
-            kd[0][j] = kt0 * d.kd0;
-            kd[1][j] = kt1 * d.kd1;
+            kd[0][j] = kw0 * d.kd0;
+            kd[1][j] = kw1 * d.kd1;
             gcv[j] = d.gc;
-            const float bd0 = kt0 * d.ei0, bd1 = kt1 * d.ei1;
-            const float bo = kt0 * d.f0;
-            t00 = mfma4(bd0, kt0 * d.e0, t00);
+            const float bd0 = kw0 * d.ei0, bd1 = kw1 * d.ei1;
+            const float bo = kw0 * d.f0;
+            t00 = mfma4(bd0, kr0 * d.e0, t00);
             p00 = mfma4(bd0, q0 * d.e0, p00);
-            t11 = mfma4(bd1, kt1 * d.e1, t11);
+            t11 = mfma4(bd1, kr1 * d.e1, t11);
             p11 = mfma4(bd1, q1 * d.e1, p11);
-            t10 = mfma4(kt1 * d.f1, bo, t10);
+            t10 = mfma4(kr1 * d.f1, bo, t10);
             p10 = mfma4(bo, q1 * d.f1, p10);
         }
         // gate-scaled operand rows for the chain, hi/lo, into the swizzled tiles
@@ -737,7 +754,7 @@ __global__ void __launch_bounds__(NTHR) vec_chain_kernel(ChainParams p) {
             __syncthreads();
         }
     } else {
-        // wave 3: value tile of a chunk, scaled by sqrt(gamma), transposed:
+        // wave 3: value tile of a chunk, scaled by sqrt(gamma), gamma or 1, transposed:
         // lane (ln, g) holds tokens 2 ln, 2 ln + 1 of columns j0 + 8g .. + 7.
         // Registers are refilled one chunk ahead; rows past T get 0.
         uint4 vr[2];
@@ -767,7 +784,8 @@ __global__ void __launch_bounds__(NTHR) vec_chain_kernel(ChainParams p) {
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
                     const float gam = p.gvec ? gv[i][cc >> 2][cc & 3] : gs[i];
-                    v2[i] = okt[i] ? bf16_at(vr[i], cc) * sqrt_hw(gam) : 0.0f;
+                    const float sc = p.vmode == VAL_SQRT_GAIN ? sqrt_hw(gam) : (p.vmode == VAL_GAIN ? gam : 1.0f);
+                    v2[i] = okt[i] ? bf16_at(vr[i], cc) * sc : 0.0f;
                 }
                 *reinterpret_cast<f32x2*>(sVt + (8 * g + cc) * VTS + 2 * ln) = v2;
             }
@@ -795,14 +813,18 @@ bool vec_gates(const pdn_chunk_fwd_args& a) {
 long num_chunks(const pdn_chunk_fwd_args& a) { return (static_cast<long>(a.T) + VC - 1) / VC; }
 
 template <bool AVEC, bool BVEC, bool PRE>
-void launch_prep(const PrepParams& pp, long nblk, hipStream_t stream) {
-    vec_prep_kernel<AVEC, BVEC, PRE><<<dim3(static_cast<unsigned>(nblk)), dim3(256), 0, stream>>>(pp);
+void launch_prep(const PrepParams& pp, int km, long nblk, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(nblk)), block(256);
+    if (km == PDN_KEY_ERASE_GATE) vec_prep_kernel<AVEC, BVEC, PRE, PDN_KEY_ERASE_GATE><<<grid, block, 0, stream>>>(pp);
+    else if (km == PDN_KEY_WRITE_GATE) vec_prep_kernel<AVEC, BVEC, PRE, PDN_KEY_WRITE_GATE><<<grid, block, 0, stream>>>(pp);
+    else vec_prep_kernel<AVEC, BVEC, PRE, PDN_KEY_SYMMETRIC><<<grid, block, 0, stream>>>(pp);
 }
 
 }  // namespace
 
 bool chunk_vec_supported(const pdn_chunk_fwd_args& a) {
-    return a.qkv_dtype == PDN_BF16 && a.dk == DK && a.dv % DVT == 0 && vec_gates(a);
+    return a.qkv_dtype == PDN_BF16 && a.dk == DK && a.dv % DVT == 0 &&
+           (vec_gates(a) || a.key_mode != PDN_KEY_SYMMETRIC);
 }
 
 size_t chunk_vec_workspace_bytes(const pdn_chunk_fwd_args& a) {
@@ -839,12 +861,13 @@ hipError_t launch_chunk_vec(const pdn_chunk_fwd_args& a, hipStream_t stream) {
     pp.eps = pre ? a.precond_eps : 0.0f;
     const long nblk = (nbh * nc + 3) / 4;
     const bool avec = a.alpha_mode == PDN_ALPHA_VEC, bvec = a.beta_mode == PDN_GATE_VEC;
+    const int km = a.key_mode;
     if (avec) {
-        if (bvec) pre ? launch_prep<true, true, true>(pp, nblk, stream) : launch_prep<true, true, false>(pp, nblk, stream);
-        else pre ? launch_prep<true, false, true>(pp, nblk, stream) : launch_prep<true, false, false>(pp, nblk, stream);
+        if (bvec) pre ? launch_prep<true, true, true>(pp, km, nblk, stream) : launch_prep<true, true, false>(pp, km, nblk, stream);
+        else pre ? launch_prep<true, false, true>(pp, km, nblk, stream) : launch_prep<true, false, false>(pp, km, nblk, stream);
     } else {
-        if (bvec) pre ? launch_prep<false, true, true>(pp, nblk, stream) : launch_prep<false, true, false>(pp, nblk, stream);
-        else pre ? launch_prep<false, false, true>(pp, nblk, stream) : launch_prep<false, false, false>(pp, nblk, stream);
+        if (bvec) pre ? launch_prep<false, true, true>(pp, km, nblk, stream) : launch_prep<false, true, false>(pp, km, nblk, stream);
+        else pre ? launch_prep<false, false, true>(pp, km, nblk, stream) : launch_prep<false, false, false>(pp, km, nblk, stream);
     }
 
     ChainParams cp;
@@ -859,6 +882,9 @@ hipError_t launch_chunk_vec(const pdn_chunk_fwd_args& a, hipStream_t stream) {
     } else {
         cp.gsrc = a.beta; cp.gts = 1; cp.gvec = 0;
     }
+    if (a.key_mode == PDN_KEY_SYMMETRIC) cp.vmode = VAL_SQRT_GAIN;
+    else if (a.key_mode == PDN_KEY_WRITE_GATE && a.gamma_mode == PDN_GAMMA_SAME_AS_BETA) cp.vmode = VAL_UNIT;
+    else cp.vmode = VAL_GAIN;
     cp.S0 = a.S0;
     cp.ST = a.ST;
     cp.o = a.o;

@@ -3,10 +3,14 @@
 // Per (b,h), with the state S (dk x dv, row i = key channel) read once from
 // HBM and written once:
 //   A   = Diag(alpha) S                     (alpha = exp(log_alpha))
-//   u   = vt - A^T kt                       (kt = sqrt(beta') k, vt = sqrt(gamma) v)
+//   u   = vw - A^T kr
 //   p   = A^T q
-//   S'  = A + kt u^T
-//   o   = S'^T q = p + u (kt . q)
+//   S'  = A + kw u^T
+//   o   = S'^T q = p + u (kw . q)
+// with the read key kr, write key kw and written value vw of the key mode:
+// kr = kw = sqrt(beta') k, vw = sqrt(gamma) v (symmetric); kw = k,
+// kr = beta' k, vw = gamma v (erase gate); kw = beta' k, kr = k, vw = v or
+// gamma v (write gate).
 // Both column reductions over the key channels are taken in the same pass over
 // the state, so the state streams through registers exactly once.  This is the
 // recurrent (inference) form of the update in "FG^2-GDN" 2.1 / "Gated
@@ -34,7 +38,7 @@ struct DecodeParams {
     float* S;
     void* o;
     float precond_eps;
-    int alpha_mode, beta_mode, gamma_mode;
+    int alpha_mode, beta_mode, gamma_mode, key_mode;
 };
 
 template <int DK, int DV, bool BF16IN, bool BF16OUT>
@@ -48,7 +52,7 @@ __global__ void __launch_bounds__(256, 3) decode_kernel(DecodeParams p, long nbh
     const int cg = tid % NCG;
     const int rg = tid / NCG;
 
-    __shared__ float s_alpha[DK], s_kt[DK], s_q[DK], s_vt[DV], s_u[DV];
+    __shared__ float s_alpha[DK], s_kr[DK], s_kw[DK], s_q[DK], s_vw[DV], s_u[DV];
     __shared__ f32x4 s_red[NRG][2][NCG];
     __shared__ float s_kq[4];
 
@@ -83,11 +87,19 @@ __global__ void __launch_bounds__(256, 3) decode_kernel(DecodeParams p, long nbh
                 p.precond_A[bh * DK + i] = A;
                 b = b / (A + p.precond_eps);
             }
-            const float kt = sqrtf(b) * kk;
+            float kr, kw;
+            if (p.key_mode == PDN_KEY_ERASE_GATE) {
+                kr = b * kk; kw = kk;
+            } else if (p.key_mode == PDN_KEY_WRITE_GATE) {
+                kr = kk; kw = b * kk;
+            } else {
+                kr = kw = sqrtf(b) * kk;
+            }
             s_alpha[i] = expf(la);
-            s_kt[i] = kt;
+            s_kr[i] = kr;
+            s_kw[i] = kw;
             s_q[i] = qq;
-            const float part = wave_sum(kt * qq);
+            const float part = wave_sum(kw * qq);
             if ((tid & 63) == 0) s_kq[tid >> 6] = part;
         }
         if (tid < DV) {
@@ -99,7 +111,9 @@ __global__ void __launch_bounds__(256, 3) decode_kernel(DecodeParams p, long nbh
                 g = p.gamma[bh];
             else
                 g = p.gamma[bh * DV + j];
-            s_vt[j] = sqrtf(g) * load_in<BF16IN>(p.v, bh * DV + j);
+            if (p.key_mode == PDN_KEY_SYMMETRIC) g = sqrtf(g);
+            else if (p.key_mode == PDN_KEY_WRITE_GATE && p.gamma_mode == PDN_GAMMA_SAME_AS_BETA) g = 1.0f;
+            s_vw[j] = g * load_in<BF16IN>(p.v, bh * DV + j);
         }
         __syncthreads();
 
@@ -109,7 +123,7 @@ __global__ void __launch_bounds__(256, 3) decode_kernel(DecodeParams p, long nbh
         for (int m = 0; m < RPT; ++m) {
             const int row = rg + NRG * m;
             s[m] *= s_alpha[row];
-            u += s[m] * s_kt[row];
+            u += s[m] * s_kr[row];
             pq += s[m] * s_q[row];
         }
         s_red[rg][0][cg] = u;
@@ -126,7 +140,7 @@ __global__ void __launch_bounds__(256, 3) decode_kernel(DecodeParams p, long nbh
             }
             float kq = s_kq[0];
             if constexpr (DK > 64) kq += s_kq[1];
-            const float uj = s_vt[j] - su;
+            const float uj = s_vw[j] - su;
             const float oj = sp + uj * kq;
             if constexpr (BF16OUT)
                 static_cast<uint16_t*>(p.o)[bh * DV + j] = f32_to_bf16_bits(oj);
@@ -140,7 +154,7 @@ __global__ void __launch_bounds__(256, 3) decode_kernel(DecodeParams p, long nbh
 #pragma unroll
         for (int m = 0; m < RPT; ++m) {
             const int row = rg + NRG * m;
-            s[m] += s_kt[row] * uc;
+            s[m] += s_kw[row] * uc;
             *reinterpret_cast<f32x4*>(S + (long)row * DV + 4 * cg) = s[m];
         }
 #pragma unroll
@@ -173,6 +187,7 @@ hipError_t launch_decode(const pdn_decode_args& a, hipStream_t stream) {
     p.precond_A = a.precond_A; p.S = a.S; p.o = a.o;
     p.precond_eps = a.precond_eps;
     p.alpha_mode = a.alpha_mode; p.beta_mode = a.beta_mode; p.gamma_mode = a.gamma_mode;
+    p.key_mode = a.key_mode;
     const long nbh = static_cast<long>(a.B) * a.H;
     const bool bi = a.qkv_dtype == PDN_BF16, bo = a.o_dtype == PDN_BF16;
     if (a.dk == 128 && a.dv == 128) return launch_dk_dv<128, 128>(p, bi, bo, nbh, stream);

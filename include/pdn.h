@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define PDN_ABI_VERSION 1
+#define PDN_ABI_VERSION 2
 
 /* Return codes. */
 #define PDN_OK 0
@@ -70,6 +70,22 @@ extern "C" {
 #define PDN_GATE_VEC 2
 #define PDN_GAMMA_SAME_AS_BETA 3
 
+/* Read / write key modes.  Every mode is S_t = A + kw (vw - A^T kr)^T with
+ * A = Diag(alpha_t) S_{t-1} and beta' the erase gain with the preconditioner
+ * folded in:
+ *   SYMMETRIC   kw = kr = sqrt(beta') (.) k, vw = sqrt(gamma') (.) v
+ *               ("FG^2-GDN" 2.1; the default, value 0)
+ *   ERASE_GATE  kw = k, kr = beta' (.) k, vw = gamma' (.) v
+ *               ("Gated DeltaNet-2" method 1: (I - k (b (.) k)^T) D S + k (w (.) v)^T)
+ *   WRITE_GATE  kw = beta' (.) k, kr = k, vw = v when gamma is "same as beta"
+ *               (the gain rides on the write key), else gamma (.) v
+ *               ("Preconditioned DeltaNet" 2.2: apply-to-key write key)
+ * The asymmetric modes need bf16 q/k/v with dk == 128 and dv % 32 == 0 in
+ * the prefill (PDN_EUNSUPPORTED otherwise); decode takes every mode. */
+#define PDN_KEY_SYMMETRIC 0
+#define PDN_KEY_ERASE_GATE 1
+#define PDN_KEY_WRITE_GATE 2
+
 /*
  * Prefill over whole sequences, chunkwise-parallel on the GPU.
  *
@@ -89,6 +105,7 @@ extern "C" {
  *   gamma_mode        PDN_GATE_SCALAR [B,H,T], PDN_GATE_VEC [B,H,T,dv] or
  *                     PDN_GAMMA_SAME_AS_BETA (gamma NULL; a VEC beta then needs
  *                     dk == dv); fp32 >= 0.
+ *   key_mode          PDN_KEY_* (0 = symmetric, the default).
  *   precond_eps       < 0: preconditioner off.  >= 0: on, with this epsilon.
  *   precond_A0        [B,H,dk] fp32 start of the running k(.)k sum; NULL = zeros.
  *   precond_AT        [B,H,dk] fp32 running sum after token T; NULL = not written.
@@ -112,6 +129,7 @@ typedef struct pdn_chunk_fwd_args {
     const float *beta;
     int32_t gamma_mode;
     const float *gamma;
+    int32_t key_mode;
     float precond_eps;
     const float *precond_A0;
     float *precond_AT;
@@ -130,7 +148,7 @@ typedef struct pdn_chunk_fwd_args {
  *   o_dtype           PDN_F32 or PDN_BF16;  o: [B,H,dv].
  *   alpha_mode, log_alpha ([B,H] or [B,H,dk]), beta_mode, beta ([B,H] or
  *   [B,H,dk]), gamma_mode, gamma ([B,H] or [B,H,dv]): as for the prefill with
- *   T == 1 (no clamp on log_alpha here).
+ *   T == 1 (no clamp on log_alpha here).  key_mode as for the prefill.
  *   precond_eps       < 0 off; >= 0 on, and then precond_A ([B,H,dk] fp32) is
  *                     read, advanced by k(.)k and written back in place.
  *   S                 [B,H,dk,dv] fp32, read and overwritten with S_t; 16-byte
@@ -149,6 +167,7 @@ typedef struct pdn_decode_args {
     const float *beta;
     int32_t gamma_mode;
     const float *gamma;
+    int32_t key_mode;
     float precond_eps;
     float *precond_A;
     float *S;

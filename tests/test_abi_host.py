@@ -45,7 +45,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strerror(lib):
-    assert pdn.pdn_abi_version() == 1
+    assert pdn.pdn_abi_version() == 2
     for code in (0, -1, -2, -3, -4):
         assert pdn.pdn_strerror(code)
     assert "unknown" in pdn.pdn_strerror(-99)
@@ -140,6 +140,10 @@ def test_workspace_size_and_check(lib):
     f = _chunk_ok()
     f.qkv_dtype = pdn.PDN_F32
     assert _ws_size(lib, f) == 0
+    # asymmetric keys run on the record-based kernels even with scalar gates
+    for km in (pdn.PDN_KEY_ERASE_GATE, pdn.PDN_KEY_WRITE_GATE):
+        s.key_mode = km
+        assert _ws_size(lib, s) == n
     # too small or missing: PDN_EWORKSPACE, before any launch
     a = _chunk_ok()
     a.workspace_bytes = n - 1
@@ -172,6 +176,13 @@ def test_workspace_size_and_check(lib):
     (lambda a: setattr(a, "dv", 512), pdn.PDN_EUNSUPPORTED),
     (lambda a: (setattr(a, "B", 1 << 20), setattr(a, "H", 1 << 10)), pdn.PDN_EUNSUPPORTED),
     (lambda a: (setattr(a, "S0", FAKE), setattr(a, "ST", FAKE + 64)), pdn.PDN_EINVAL),
+    (lambda a: setattr(a, "key_mode", 3), pdn.PDN_EINVAL),
+    (lambda a: setattr(a, "key_mode", -1), pdn.PDN_EINVAL),
+    # asymmetric keys: bf16 inputs with dk = 128 only
+    (lambda a: (setattr(a, "key_mode", pdn.PDN_KEY_ERASE_GATE), setattr(a, "qkv_dtype", pdn.PDN_F32)),
+     pdn.PDN_EUNSUPPORTED),
+    (lambda a: (setattr(a, "key_mode", pdn.PDN_KEY_WRITE_GATE), setattr(a, "dk", 64),
+                setattr(a, "gamma_mode", pdn.PDN_GATE_SCALAR)), pdn.PDN_EUNSUPPORTED),
 ])
 def test_chunk_validation_codes(lib, mutate, code):
     a = _chunk_ok()
@@ -179,6 +190,21 @@ def test_chunk_validation_codes(lib, mutate, code):
     assert _ccheck(lib, a) == code
     # the launching entry point returns the same code before touching the GPU
     assert lib.pdn_chunk_fwd(ctypes.byref(a), None) == code
+
+
+@pytest.mark.parametrize("km", [pdn.PDN_KEY_ERASE_GATE, pdn.PDN_KEY_WRITE_GATE])
+def test_chunk_asymmetric_keys_accepted(lib, km):
+    a = _chunk_ok()
+    a.key_mode = km
+    assert _ccheck(lib, a) == pdn.PDN_OK
+    a.alpha_mode, a.beta_mode, a.gamma_mode = (pdn.PDN_ALPHA_SCALAR, pdn.PDN_GATE_SCALAR,
+                                               pdn.PDN_GAMMA_SAME_AS_BETA)
+    assert _ccheck(lib, a) == pdn.PDN_OK
+    a.T = 0
+    a.q = a.k = a.v = a.o = None
+    assert _ccheck(lib, a) == pdn.PDN_OK
+    a.qkv_dtype = pdn.PDN_F32  # the shape rule holds for empty sequences too
+    assert _ccheck(lib, a) == pdn.PDN_EUNSUPPORTED
 
 
 def test_chunk_allows_in_place_state(lib):
@@ -206,12 +232,22 @@ def test_chunk_empty_sequence_needs_no_tensors(lib):
     (lambda a: setattr(a, "precond_eps", 1e-6), pdn.PDN_EINVAL),  # no precond_A
     (lambda a: setattr(a, "dk", 32), pdn.PDN_EUNSUPPORTED),
     (lambda a: setattr(a, "dv", 256), pdn.PDN_EUNSUPPORTED),
+    (lambda a: setattr(a, "key_mode", 3), pdn.PDN_EINVAL),
 ])
 def test_decode_validation_codes(lib, mutate, code):
     a = _decode_ok()
     mutate(a)
     assert _dcheck(lib, a) == code
     assert lib.pdn_decode_step(ctypes.byref(a), None) == code
+
+
+@pytest.mark.parametrize("km", [pdn.PDN_KEY_ERASE_GATE, pdn.PDN_KEY_WRITE_GATE])
+def test_decode_asymmetric_keys_any_shape(lib, km):
+    a = _decode_ok()
+    a.key_mode = km
+    assert _dcheck(lib, a) == pdn.PDN_OK
+    a.dk, a.qkv_dtype = 64, pdn.PDN_F32
+    assert _dcheck(lib, a) == pdn.PDN_OK
 
 
 def test_null_args_pointer(lib):

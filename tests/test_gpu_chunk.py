@@ -24,7 +24,7 @@ pytestmark = pytest.mark.gpu
 
 
 def run_chunk(w, S0="from_workload", want_state=True, o_bf16=False, A0=None,
-              in_place=False):
+              in_place=False, key_mode=0):
     """Run pdn_chunk_fwd on a synth.Workload; returns numpy (o, ST, AT)."""
     import gated_delta_rule_77_amd as pdn
     torch = torch_mod()
@@ -46,7 +46,7 @@ def run_chunk(w, S0="from_workload", want_state=True, o_bf16=False, A0=None,
     AT = torch.empty((w.B, w.H, w.dk), device="cuda") if pre else None
     pdn.pdn_chunk_fwd(q, k, v, o, log_alpha=la, beta=be, gamma=ga,
                       precond_eps=(w.precond_eps if pre else None),
-                      precond_A0=A0d, precond_AT=AT, S0=S0d, ST=ST)
+                      precond_A0=A0d, precond_AT=AT, S0=S0d, ST=ST, key_mode=key_mode)
     torch.cuda.synchronize()
     return host(o), (host(ST) if ST is not None else None), (host(AT) if AT is not None else None)
 
@@ -60,11 +60,11 @@ def sub(w, b0, b1, h0, h1):
                           precond_eps=w.precond_eps, A0=s(w.A0), S0=s(w.S0))
 
 
-def check(name, w, tol, A0=None, **kw):
-    o, ST, AT = run_chunk(w, A0=A0, **kw)
+def check(name, w, tol, A0=None, key_mode=0, **kw):
+    o, ST, AT = run_chunk(w, A0=A0, key_mode=key_mode, **kw)
     o_ref, S_ref, A_ref = oracle.delta_rule(w.q, w.k, w.v, w.alpha_mode, w.log_alpha,
                                             w.beta_mode, w.beta, w.gamma_mode, w.gamma,
-                                            w.precond_eps, A0, w.S0)
+                                            w.precond_eps, A0, w.S0, key_mode=key_mode)
     eo, es = rel_l2(o, o_ref), rel_l2(ST, S_ref)
     report(name, o=eo, S=es)
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(ST))
@@ -129,13 +129,13 @@ def test_fp32_inputs_dk128_precond():
 # full-size workloads, sampled (batch, head) pairs
 # ---------------------------------------------------------------------------
 
-def _sampled(name, w, pairs, tol):
-    o, ST, AT = run_chunk(w)
+def _sampled(name, w, pairs, tol, key_mode=0):
+    o, ST, AT = run_chunk(w, key_mode=key_mode)
     for (b, h) in pairs:
         ws = sub(w, b, b + 1, h, h + 1)
         o_ref, S_ref, A_ref = oracle.delta_rule(ws.q, ws.k, ws.v, ws.alpha_mode, ws.log_alpha,
                                                 ws.beta_mode, ws.beta, ws.gamma_mode, ws.gamma,
-                                                ws.precond_eps, None, ws.S0)
+                                                ws.precond_eps, None, ws.S0, key_mode=key_mode)
         eo = rel_l2(o[b:b + 1, h:h + 1], o_ref)
         es = rel_l2(ST[b:b + 1, h:h + 1], S_ref)
         report("%s (b=%d,h=%d)" % (name, b, h), o=eo, S=es)
@@ -380,3 +380,102 @@ def test_deterministic():
     np.testing.assert_array_equal(o1, o2)
     np.testing.assert_array_equal(S1, S2)
     np.testing.assert_array_equal(A1, A2)
+
+
+# ---------------------------------------------------------------------------
+# read / write key modes (erase gate, write gate)
+# ---------------------------------------------------------------------------
+
+KEY_MODES = {"erase": oracle.KEY_ERASE_GATE, "write": oracle.KEY_WRITE_GATE}
+
+
+@pytest.mark.parametrize("pre", [False, True])
+@pytest.mark.parametrize("gmode", ["same", "scalar", "vec"])
+@pytest.mark.parametrize("bmode", ["scalar", "vec"])
+@pytest.mark.parametrize("amode", ["none", "scalar", "vec"])
+@pytest.mark.parametrize("km", ["erase", "write"])
+def test_key_mode_matrix(km, amode, bmode, gmode, pre):
+    """Asymmetric read/write keys under every gate combination (ragged length,
+    non-zero start state and start sum); all of them run the per-channel-gate
+    kernels, scalar gates included."""
+    seed = ((["none", "scalar", "vec"].index(amode) * 2 + ["scalar", "vec"].index(bmode)) * 6
+            + ["same", "scalar", "vec"].index(gmode) * 2 + int(pre)) * 2 + int(km == "write")
+    rng = np.random.default_rng(300 + seed)
+    w = synth.kda_fg2(B=1, H=2, T=147, d=128, seed=23)
+    if amode == "none":
+        w.alpha_mode, w.log_alpha = synth.ALPHA_NONE, None
+    elif amode == "scalar":
+        w.alpha_mode, w.log_alpha = synth.ALPHA_SCALAR, np.ascontiguousarray(w.log_alpha[..., 0])
+    if bmode == "scalar":
+        w.beta_mode, w.beta = synth.GATE_SCALAR, np.ascontiguousarray(w.beta[..., 0])
+    if gmode == "same":
+        w.gamma_mode, w.gamma = synth.GAMMA_SAME_AS_BETA, None
+    elif gmode == "scalar":
+        w.gamma_mode = synth.GATE_SCALAR
+        w.gamma = (1.0 / (1.0 + np.exp(-rng.standard_normal((1, 2, 147))))).astype(np.float32)
+    else:
+        w.gamma_mode = synth.GATE_VEC
+        w.gamma = (1.0 / (1.0 + np.exp(-rng.standard_normal((1, 2, 147, 128))))).astype(np.float32)
+    w.S0 = (0.1 * rng.standard_normal((1, 2, 128, 128))).astype(np.float32)
+    A0 = None
+    if pre:
+        w.precond_eps = 1e-6
+        A0 = rng.uniform(0.0, 2.0, (1, 2, 128)).astype(np.float32)
+    check("keys=%s a=%s b=%s g=%s pre=%d" % (km, amode, bmode, gmode, pre), w, TOL_BF16,
+          A0=A0, key_mode=KEY_MODES[km])
+
+
+@pytest.mark.parametrize("T", [1, 31, 32, 33, 95, 96, 97])
+@pytest.mark.parametrize("km", ["erase", "write"])
+def test_key_mode_boundary_lengths(km, T):
+    # 32-token chunks of the per-channel-gate kernels: lengths around the edges
+    w = synth.gdn2_precond(B=1, H=2, T=T, d=128, seed=T, n_pairs=0)
+    w.S0 = (0.2 * np.random.default_rng(T).standard_normal((1, 2, 128, 128))).astype(np.float32)
+    A0 = np.full((1, 2, 128), 0.25, np.float32)
+    check("keys=%s T=%d" % (km, T), w, TOL_BF16, A0=A0, key_mode=KEY_MODES[km])
+
+
+@pytest.mark.parametrize("km", ["erase", "write"])
+def test_key_mode_tied_gain_matches_symmetric(km):
+    # one scalar gain per token as erase gate, write gate and key gain: both
+    # asymmetric updates reduce to the symmetric one (Gated DeltaNet), which
+    # runs on the factored scalar-gate kernel -- two independent code paths
+    w = synth.gdn(B=1, H=4, T=300, d=128, seed=19)
+    o_s, S_s, _ = run_chunk(w)
+    o_a, S_a, _ = run_chunk(w, key_mode=KEY_MODES[km])
+    assert rel_l2(o_a, o_s) < 1e-4
+    assert rel_l2(S_a, S_s) < 1e-4
+
+
+@pytest.mark.timeout(1200)
+def test_gdn2_erase_gate_full_size_sampled():
+    # the long-context workload (B1 H16 T65536, erase gain per key channel,
+    # write gain per value channel, preconditioner) in the literal erase-gate
+    # form of Gated DeltaNet-2
+    w = synth.gdn2_precond()
+    _sampled("gdn2 erase gate B1 H16 T65536", w, [(0, 9)], TOL_BF16,
+             key_mode=oracle.KEY_ERASE_GATE)
+
+
+@pytest.mark.parametrize("km", ["erase", "write"])
+def test_key_mode_prefill_matches_decode_steps(km):
+    import gated_delta_rule_77_amd as pdn
+    torch = torch_mod()
+    w = synth.gdn2_precond(B=2, H=3, T=70, d=128, seed=29, n_pairs=0)
+    w.S0 = (0.05 * np.random.default_rng(4).standard_normal((2, 3, 128, 128))).astype(np.float32)
+    A0 = np.full((2, 3, 128), 0.5, np.float32)
+    o_pf, S_pf, A_pf = run_chunk(w, A0=A0, key_mode=KEY_MODES[km])
+    S, A = dev(w.S0), dev(A0)
+    outs = []
+    for t in range(w.T):
+        o = torch.empty((2, 3, 128), device="cuda")
+        pdn.pdn_decode_step(dev(w.q[:, :, t], True), dev(w.k[:, :, t], True),
+                            dev(w.v[:, :, t], True), o, S, log_alpha=dev(w.log_alpha[:, :, t]),
+                            beta=dev(w.beta[:, :, t]), gamma=dev(w.gamma[:, :, t]),
+                            precond_eps=w.precond_eps, precond_A=A, key_mode=KEY_MODES[km])
+        outs.append(o)
+    torch.cuda.synchronize()
+    o_dec = np.stack([host(x) for x in outs], axis=2)
+    assert rel_l2(o_pf, o_dec) < 1e-4
+    assert rel_l2(S_pf, host(S)) < 1e-4
+    assert rel_l2(A_pf, host(A)) < 1e-6

@@ -14,7 +14,7 @@ from gpu_util import TOL_BF16, TOL_F32, dev, host, report, torch_mod
 pytestmark = pytest.mark.gpu
 
 
-def _run_gpu_decode(w, steps, bf16_out=False, A0=None):
+def _run_gpu_decode(w, steps, bf16_out=False, A0=None, key_mode=0):
     import gated_delta_rule_77_amd as pdn
     torch = torch_mod()
     bf = w.qkv_dtype == synth.DT_BF16
@@ -32,18 +32,18 @@ def _run_gpu_decode(w, steps, bf16_out=False, A0=None):
                         dtype=torch.bfloat16 if bf16_out else torch.float32)
         pdn.pdn_decode_step(q, k, v, o, S, log_alpha=la, beta=be, gamma=ga,
                             precond_eps=(w.precond_eps if w.precond_eps >= 0 else None),
-                            precond_A=A)
+                            precond_A=A, key_mode=key_mode)
         outs.append(o)
     torch.cuda.synchronize()
     o_all = np.stack([host(x) for x in outs], axis=2)
     return o_all, host(S), (host(A) if A is not None else None)
 
 
-def _oracle(w, steps, A0=None):
+def _oracle(w, steps, A0=None, key_mode=0):
     sl = lambda x: None if x is None else x[:, :, :steps]
     return oracle.delta_rule(sl(w.q), sl(w.k), sl(w.v), w.alpha_mode, sl(w.log_alpha),
                              w.beta_mode, sl(w.beta), w.gamma_mode, sl(w.gamma),
-                             w.precond_eps, A0, w.S0)
+                             w.precond_eps, A0, w.S0, key_mode=key_mode)
 
 
 def test_decode_config5_shape_few_steps():
@@ -130,3 +130,34 @@ def test_decode_bf16_output():
     # bf16 storage of o adds one rounding (2^-9 relative per element)
     assert rel_l2(o, o_ref) < 4e-3
     assert rel_l2(S, S_ref) < TOL_BF16
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 128), (128, 64)])
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("bf16", [True, False])
+@pytest.mark.parametrize("km", [oracle.KEY_ERASE_GATE, oracle.KEY_WRITE_GATE])
+def test_decode_key_modes(km, dk, dv, mode, bf16):
+    # read key / write key split: erase gate and apply-to-key write gate
+    amode, bmode, gmode, pre = mode
+    if gmode == synth.GAMMA_SAME_AS_BETA and bmode == synth.GATE_VEC and dk != dv:
+        pytest.skip("same-as-beta vector gain needs dk == dv")
+    w = _mode_case(dk, dv, amode, bmode, gmode, pre, bf16, seed=7 * km + dk + dv + amode)
+    A0 = np.abs(np.random.default_rng(2).standard_normal((w.B, w.H, dk))).astype(np.float32) if pre else None
+    o, S, A = _run_gpu_decode(w, w.T, A0=A0, key_mode=km)
+    o_ref, S_ref, A_ref = _oracle(w, w.T, A0=A0, key_mode=km)
+    tol = TOL_BF16 if bf16 else TOL_F32
+    eo, es = rel_l2(o, o_ref), rel_l2(S, S_ref)
+    report("decode keys=%d dk%d dv%d %s bf16=%s" % (km, dk, dv, mode, bf16), o=eo, S=es)
+    assert eo < tol and es < tol
+    if pre:
+        assert rel_l2(A, A_ref) < 1e-6
+
+
+@pytest.mark.parametrize("km", [oracle.KEY_ERASE_GATE, oracle.KEY_WRITE_GATE])
+def test_decode_key_mode_full_shape_few_steps(km):
+    w = synth.decode(B=256, H=16, d=128, steps=3, seed=9)
+    o, S, _ = _run_gpu_decode(w, 3, key_mode=km)
+    o_ref, S_ref, _ = _oracle(w, 3, key_mode=km)
+    eo, es = rel_l2(o, o_ref), rel_l2(S, S_ref)
+    report("decode keys=%d B256 H16 d128 3 steps" % km, o=eo, S=es)
+    assert eo < TOL_BF16 and es < TOL_BF16
