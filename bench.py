@@ -10,9 +10,10 @@ timed region.  The same run also times the recurrent decode
 vector key gain, scalar value gain), the per-channel-gate prefill on the
 KDA / FG^2-GDN workload (B=2, H=32, T=8192, channel-wise decay and key gain)
 and the Gated DeltaNet-2 + preconditioner workload (B=1, H=16, T=65536,
-channel-wise decay, key and value gains; also in the literal erase-gate form of
-Gated DeltaNet-2, with separate read and write keys), and, on rank 0, the fp64
-CPU oracle on a bounded sample of the prefill workload.
+channel-wise decay, key and value gains; also with separate read and write keys:
+the literal erase-gate form of Gated DeltaNet-2 and the write-gate
+(apply-to-key) form of Preconditioned DeltaNet), and, on rank 0, the fp64 CPU
+oracle on a bounded sample of the prefill workload.
 
 Prints one JSON line.  `value` is prefill tokens/s (tokens = batch x sequence
 positions, all heads); the roofline object describes the prefill kernel
@@ -220,10 +221,16 @@ def bench_gated(args):
     from gated_delta_rule_77_amd import synth
 
     res = {}
-    erase = pdn.PDN_KEY_ERASE_GATE
-    for mk, steps, km, tag in ((synth.kda_fg2, 10, pdn.PDN_KEY_SYMMETRIC, ""),
-                               (synth.gdn2_precond, 5, pdn.PDN_KEY_SYMMETRIC, ""),
-                               (synth.gdn2_precond, 5, erase, "_erase_gate")):
+    keys = {
+        pdn.PDN_KEY_SYMMETRIC: ("", "symmetric: sqrt(beta') (.) k, sqrt(gamma) (.) v"),
+        pdn.PDN_KEY_ERASE_GATE: ("_erase_gate",
+                                 "erase gate: write key k, read key beta' (.) k, value gamma (.) v"),
+        pdn.PDN_KEY_WRITE_GATE: ("_write_gate",
+                                 "write gate: write key beta' (.) k, read key k, value gamma (.) v"),
+    }
+    all_modes = (pdn.PDN_KEY_SYMMETRIC, pdn.PDN_KEY_ERASE_GATE, pdn.PDN_KEY_WRITE_GATE)
+    for mk, steps, modes in ((synth.kda_fg2, 10, (pdn.PDN_KEY_SYMMETRIC,)),
+                             (synth.gdn2_precond, 5, all_modes)):
         w = mk()
         q, k, v = to_dev(w.q, True), to_dev(w.k, True), to_dev(w.v, True)
         la, be, ga = to_dev(w.log_alpha), to_dev(w.beta), to_dev(w.gamma)
@@ -232,38 +239,40 @@ def bench_gated(args):
         ST = torch.empty((w.B, w.H, w.dk, w.dv), device="cuda", dtype=torch.float32)
         AT = torch.empty((w.B, w.H, w.dk), device="cuda", dtype=torch.float32) if pre else None
         S0 = to_dev(w.S0)
-        kw = dict(log_alpha=la, beta=be, gamma=ga, precond_eps=(w.precond_eps if pre else None),
-                  precond_AT=AT, S0=S0, ST=ST, key_mode=km)
-        ws = torch.empty(pdn.pdn_chunk_fwd_workspace_size(q, k, v, o, **kw), dtype=torch.uint8,
-                         device="cuda")
-        for _ in range(3):
-            pdn.pdn_chunk_fwd(q, k, v, o, workspace=ws, **kw)
-        torch.cuda.synchronize()
-        stream = torch.cuda.current_stream()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(steps)]
-        for i in range(steps):
-            ev[i][0].record(stream)
-            pdn.pdn_chunk_fwd(q, k, v, o, workspace=ws, **kw)
-            ev[i][1].record(stream)
-        torch.cuda.synchronize()
-        ms = sum(a.elapsed_time(b) for a, b in ev) / steps
-        BH, T, dk, dv = w.B * w.H, w.T, w.dk, w.dv
-        gate = lambda x: 0 if x is None else x.size * 4
-        alg = (BH * T * (2 * dk + dv) * 2 + gate(w.log_alpha) + gate(w.beta) + gate(w.gamma)
-               + BH * T * dv * 4 + BH * dk * dv * 4 * (2 if w.S0 is not None else 1)
-               + (BH * dk * 4 if pre else 0))
-        gbs = alg / (ms / 1e3) / 1e9
-        res["%s%s_B%d_H%d_T%d_d%d" % (w.name, tag, w.B, w.H, w.T, w.dk)] = {
-            "B": w.B, "H": w.H, "T": T, "dk": dk, "dv": dv, "steps": steps,
-            "keys": ("erase gate: write key k, read key beta' (.) k, value gamma (.) v"
-                     if km == erase else "symmetric: sqrt(beta') (.) k, sqrt(gamma) (.) v"),
-            "call_ms": ms, "tokens_per_s": w.B * T / (ms / 1e3),
-            "alg_bytes_per_call": alg, "workspace_bytes": ws.numel(),
-            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": gbs / HBM_PEAK_GBS},
-        }
-        del q, k, v, la, be, ga, o, ST, AT, S0, ws, w
+        for km in modes:
+            kw = dict(log_alpha=la, beta=be, gamma=ga,
+                      precond_eps=(w.precond_eps if pre else None),
+                      precond_AT=AT, S0=S0, ST=ST, key_mode=km)
+            ws = torch.empty(pdn.pdn_chunk_fwd_workspace_size(q, k, v, o, **kw),
+                             dtype=torch.uint8, device="cuda")
+            for _ in range(3):
+                pdn.pdn_chunk_fwd(q, k, v, o, workspace=ws, **kw)
+            torch.cuda.synchronize()
+            stream = torch.cuda.current_stream()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(steps)]
+            for i in range(steps):
+                ev[i][0].record(stream)
+                pdn.pdn_chunk_fwd(q, k, v, o, workspace=ws, **kw)
+                ev[i][1].record(stream)
+            torch.cuda.synchronize()
+            ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+            BH, T, dk, dv = w.B * w.H, w.T, w.dk, w.dv
+            gate = lambda x: 0 if x is None else x.size * 4
+            alg = (BH * T * (2 * dk + dv) * 2 + gate(w.log_alpha) + gate(w.beta) + gate(w.gamma)
+                   + BH * T * dv * 4 + BH * dk * dv * 4 * (2 if w.S0 is not None else 1)
+                   + (BH * dk * 4 if pre else 0))
+            gbs = alg / (ms / 1e3) / 1e9
+            tag, desc = keys[km]
+            res["%s%s_B%d_H%d_T%d_d%d" % (w.name, tag, w.B, w.H, w.T, w.dk)] = {
+                "B": w.B, "H": w.H, "T": T, "dk": dk, "dv": dv, "steps": steps, "keys": desc,
+                "call_ms": ms, "tokens_per_s": w.B * T / (ms / 1e3),
+                "alg_bytes_per_call": alg, "workspace_bytes": ws.numel(),
+                "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
+                             "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS},
+            }
+            del ws
+        del q, k, v, la, be, ga, o, ST, AT, S0, w
         torch.cuda.empty_cache()
     return res
 

@@ -3,6 +3,11 @@ oracle (tests infrastructure; nothing in the product imports this file).
 
 * ``unrolled_product`` -- explicit product of per-token transition matrices.
 * ``chunked_wy``       -- chunkwise UT/WY form with a triangular solve.
+* ``ridge_memory``, ``apply_to_key_exact``, ``apply_to_query_exact`` -- the
+  exact-preconditioner references of "Preconditioned DeltaNet" (Theorem 3.1):
+  the (ridge-regularised) least-squares memory and the two recurrences that
+  reach it, DeltaNet with the inverse Gram matrix on the write key and linear
+  attention with it on the query.
 
 Both take the per-token gates from ``oracle._gates_per_token`` so that the
 pins exercise the recurrence algebra; the gate definitions themselves are
@@ -117,3 +122,63 @@ def chunked_wy(q, k, v, alpha_mode, log_alpha, beta_mode, beta, gamma_mode,
                 S = np.exp(G[-1])[:, None] * S + (Kt * np.exp(G[-1] - G)).T @ U
             ST[b, h] = S
     return o, ST
+
+
+# ---------------------------------------------------------------------------
+# exact preconditioner ("Preconditioned DeltaNet", Theorem 3.1)
+# ---------------------------------------------------------------------------
+
+def ridge_memory(k, v, lam):
+    """Per prefix t, the memory S_t = argmin_S lam ||S||^2 + sum_{i<=t} ||S^T k_i - v_i||^2
+    = (lam I + K_t^T K_t)^-1 K_t^T V_t, by a dense solve.  k [T, dk], v [T, dv] -> [T, dk, dv]."""
+    k, v = np.asarray(k, np.float64), np.asarray(v, np.float64)
+    T, dk = k.shape
+    out = np.zeros((T, dk, v.shape[1]))
+    for t in range(T):
+        K, V = k[:t + 1], v[:t + 1]
+        out[t] = np.linalg.solve(lam * np.eye(dk) + K.T @ K, K.T @ V)
+    return out
+
+
+def apply_to_key_exact(q, k, v, lam):
+    """DeltaNet with the exact preconditioner on the write key: read key k_t,
+    write key G_t^-1 k_t with G_t = lam I + sum_{i<=t} k_i k_i^T, unit gain, no
+    decay, S_0 = 0.  Returns (o [T, dv], S_T)."""
+    q, k, v = (np.asarray(x, np.float64) for x in (q, k, v))
+    T, dk = k.shape
+    G = lam * np.eye(dk)
+    S = np.zeros((dk, v.shape[1]))
+    o = np.zeros((T, v.shape[1]))
+    for t in range(T):
+        G += np.outer(k[t], k[t])
+        kw = np.linalg.solve(G, k[t])
+        S = S + np.outer(kw, v[t] - S.T @ k[t])
+        o[t] = S.T @ q[t]
+    return o, S
+
+
+def apply_to_query_exact(q, k, v, lam):
+    """Linear attention with the exact preconditioner on the query:
+    o_t = sum_{i<=t} ((G_t^-1 q_t) . k_i) v_i, G_t as in apply_to_key_exact."""
+    q, k, v = (np.asarray(x, np.float64) for x in (q, k, v))
+    T, dk = k.shape
+    G = lam * np.eye(dk)
+    M = np.zeros((dk, v.shape[1]))  # sum k_i v_i^T
+    o = np.zeros((T, v.shape[1]))
+    for t in range(T):
+        G += np.outer(k[t], k[t])
+        M += np.outer(k[t], v[t])
+        o[t] = M.T @ np.linalg.solve(G, q[t])
+    return o
+
+
+def axis_key_case(rng, T, dk, dv, n_axes):
+    """Keys along coordinate axes (random axis among the first n_axes, random
+    bf16-exact magnitude), so every Gram matrix sum k k^T is diagonal."""
+    axis = rng.integers(0, n_axes, T)
+    mag = rng.choice(np.array([0.25, 0.5, 0.75, 1.0, 1.5, 2.0]), T) * rng.choice([-1.0, 1.0], T)
+    k = np.zeros((T, dk))
+    k[np.arange(T), axis] = mag
+    q = rng.standard_normal((T, dk))
+    v = rng.standard_normal((T, dv))
+    return q, k, v

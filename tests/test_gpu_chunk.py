@@ -479,3 +479,38 @@ def test_key_mode_prefill_matches_decode_steps(km):
     assert rel_l2(o_pf, o_dec) < 1e-4
     assert rel_l2(S_pf, host(S)) < 1e-4
     assert rel_l2(A_pf, host(A)) < 1e-6
+
+
+@pytest.mark.parametrize("eps", [1e-3, 0.5])
+def test_write_gate_diagonal_preconditioner_is_least_squares(eps):
+    # "Preconditioned DeltaNet" Theorem 3.1 on the GPU path: with keys along
+    # coordinate axes the running k (.) k sum is the whole Gram matrix, so the
+    # write-gate mode with unit gain, no decay and the preconditioner is the
+    # exact (ridge, lam = eps) preconditioner.  Its outputs and final state are
+    # compared with the least-squares memory from a dense solve, which shares
+    # nothing with either the oracle or the kernels.
+    from formulations import axis_key_case, ridge_memory
+    rng = np.random.default_rng(65)
+    B, H, T, d = 1, 2, 300, 128
+    q = np.zeros((B, H, T, d), np.float32)
+    k = np.zeros_like(q)
+    v = np.zeros((B, H, T, d), np.float32)
+    for h in range(H):
+        qh, kh, vh = axis_key_case(rng, T, d, d, n_axes=100)
+        q[0, h], k[0, h], v[0, h] = qh, kh, vh
+    q, v = synth.round_to_bf16(q), synth.round_to_bf16(v)
+    k = k.astype(np.float32)  # magnitudes are bf16-exact
+    w = synth.Workload("axis_keys", B, H, T, d, d, synth.DT_BF16, q, k, v,
+                       synth.ALPHA_NONE, None, synth.GATE_SCALAR, np.ones((B, H, T), np.float32),
+                       synth.GAMMA_SAME_AS_BETA, None, precond_eps=eps)
+    o, ST, AT = run_chunk(w, key_mode=oracle.KEY_WRITE_GATE)
+    o_ls = np.zeros((B, H, T, d))
+    S_ls = np.zeros((B, H, d, d))
+    for h in range(H):
+        ridge = ridge_memory(k[0, h], v[0, h], eps)
+        o_ls[0, h] = np.einsum("tkv,tk->tv", ridge, q[0, h].astype(np.float64))
+        S_ls[0, h] = ridge[-1]
+    eo, es = rel_l2(o, o_ls), rel_l2(ST, S_ls)
+    report("write gate = least squares eps=%g" % eps, o=eo, S=es)
+    assert eo < TOL_BF16 and es < TOL_BF16
+    check("write gate axis keys eps=%g" % eps, w, TOL_BF16, key_mode=oracle.KEY_WRITE_GATE)

@@ -18,7 +18,8 @@ import pytest
 import oracle
 from oracle import (ALPHA_NONE, ALPHA_SCALAR, ALPHA_VEC, GATE_SCALAR, GATE_VEC,
                     GAMMA_SAME_AS_BETA, rel_l2)
-from formulations import chunked_wy, unrolled_product
+from formulations import (apply_to_key_exact, apply_to_query_exact, axis_key_case, chunked_wy,
+                          ridge_memory, unrolled_product)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_examples.txt")
 
@@ -477,3 +478,71 @@ def test_key_modes_differ_with_vector_gains():
     for i in range(3):
         for j in range(i + 1, 3):
             assert rel_l2(outs[i], outs[j]) > 1e-3
+
+
+# ---------------------------------------------------------------------------
+# exact preconditioner ("Preconditioned DeltaNet", Theorem 3.1)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("lam", [1e-3, 1.0])
+def test_exact_preconditioner_atk_atq_and_least_squares_agree(lam):
+    # With the inverse (ridge) Gram matrix as preconditioner, DeltaNet on the
+    # write key and linear attention on the query both return the
+    # least-squares memory's prediction at every step.
+    rng = np.random.default_rng(61)
+    T, dk, dv = 40, 8, 5
+    q, k, v = rng.standard_normal((T, dk)), rng.standard_normal((T, dk)), rng.standard_normal((T, dv))
+    ridge = ridge_memory(k, v, lam)
+    o_ref = np.einsum("tkv,tk->tv", ridge, q)
+    o_atk, S_atk = apply_to_key_exact(q, k, v, lam)
+    o_atq = apply_to_query_exact(q, k, v, lam)
+    np.testing.assert_allclose(o_atk, o_ref, rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(o_atq, o_ref, rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(S_atk, ridge[-1], rtol=1e-9, atol=1e-11)
+
+
+def test_exact_preconditioner_reaches_unregularised_least_squares():
+    # once t >= dk the keys span the space and the vanishing-ridge memory is
+    # the ordinary least-squares solution (numpy's lstsq, an independent routine)
+    rng = np.random.default_rng(62)
+    T, dk, dv = 30, 6, 4
+    q, k, v = rng.standard_normal((T, dk)), rng.standard_normal((T, dk)), rng.standard_normal((T, dv))
+    o_atk, _ = apply_to_key_exact(q, k, v, 1e-10)
+    for t in range(dk, T):
+        S_ls = np.linalg.lstsq(k[:t + 1], v[:t + 1], rcond=None)[0]
+        np.testing.assert_allclose(o_atk[t], S_ls.T @ q[t], rtol=1e-6, atol=1e-8)
+
+
+def test_first_order_delta_rule_is_not_least_squares():
+    # the plain delta rule (unit gain, no preconditioner) is a gradient step,
+    # not the least-squares solution: the references must tell them apart
+    rng = np.random.default_rng(63)
+    T, dk, dv = 30, 6, 4
+    q, k, v = rng.standard_normal((T, dk)), rng.standard_normal((T, dk)), rng.standard_normal((T, dv))
+    k /= np.linalg.norm(k, axis=1, keepdims=True)
+    o_ls = np.einsum("tkv,tk->tv", ridge_memory(k, v, 1e-10), q)
+    o_dn, _, _ = oracle.delta_rule(q[None, None], k[None, None], v[None, None], ALPHA_NONE, None,
+                                   GATE_SCALAR, np.ones((1, 1, T)), GAMMA_SAME_AS_BETA, None)
+    assert np.abs(o_dn[0, 0, dk:] - o_ls[dk:]).max() > 1e-2
+
+
+@pytest.mark.parametrize("eps", [1e-3, 0.5])
+def test_diagonal_preconditioner_is_exact_for_axis_keys(eps):
+    # For keys along coordinate axes the running k (.) k sum is the whole Gram
+    # matrix, so the diagonal preconditioner 1/(A_t + eps) on the write key
+    # (write-gate mode, unit gain, no decay) is the exact ridge preconditioner
+    # with lam = eps: the oracle must return the ridge memory.
+    rng = np.random.default_rng(64)
+    T, dk, dv = 50, 10, 6
+    q, k, v = axis_key_case(rng, T, dk, dv, n_axes=7)
+    o, S, _ = oracle.delta_rule(q[None, None], k[None, None], v[None, None], ALPHA_NONE, None,
+                                GATE_SCALAR, np.ones((1, 1, T)), GAMMA_SAME_AS_BETA, None,
+                                precond_eps=eps, key_mode=oracle.KEY_WRITE_GATE)
+    ridge = ridge_memory(k, v, eps)
+    np.testing.assert_allclose(o[0, 0], np.einsum("tkv,tk->tv", ridge, q), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(S[0, 0], ridge[-1], rtol=1e-10, atol=1e-12)
+    # the erase-gate and symmetric forms are not the exact preconditioner
+    o_e, _, _ = oracle.delta_rule(q[None, None], k[None, None], v[None, None], ALPHA_NONE, None,
+                                  GATE_SCALAR, np.ones((1, 1, T)), GAMMA_SAME_AS_BETA, None,
+                                  precond_eps=eps, key_mode=oracle.KEY_SYMMETRIC)
+    assert np.abs(o_e[0, 0] - np.einsum("tkv,tk->tv", ridge, q)).max() > 1e-3
