@@ -182,9 +182,9 @@ const char *pdn_strerror(int code);
 
 /* Device scratch bytes pdn_chunk_fwd needs for these arguments (0 is valid).
  * Returns PDN_OK and writes *bytes, or a PDN_E* code for invalid arguments.
- * Non-zero only for bf16 q/k/v with dk == 128 and a per-channel gate or the
- * preconditioner: those calls first write, for every (b, h) and 32-token
- * chunk, a 56 KiB record of gate-scaled operands and solve blocks (plus 512
+ * Non-zero only for bf16 q/k/v with dk == 128 and a per-channel gate, the
+ * preconditioner or asymmetric keys: those calls first write, for every (b, h)
+ * and 32-token chunk, a 56 KiB record of gate-scaled operands and solve blocks (plus 512
  * bytes of k(.)k sums with the preconditioner), which the state-carrying
  * kernel then reads once.  The workspace holds no state between calls. */
 int pdn_chunk_fwd_workspace_size(const pdn_chunk_fwd_args *args, size_t *bytes);
