@@ -511,6 +511,7 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
     // Row factors carry sb_r only for T (wave 2), not for P (wave 3).
     struct GateVals {
         float gl, sb, G2last;
+        float fa, ff;  // this lane's FA and FF factors (token = lane)
     };
     float* gw = reinterpret_cast<float*>(smem + GA) + (w2 ? 0 : NGF * CH);
     enum { FA = 0, FB = CH, FF = 2 * CH, FE = 3 * CH, SG = 6 * CH };
@@ -529,9 +530,11 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
         const float gm = R == 0 ? gm0 : (R == 1 ? gm1 : (R == 2 ? gm2 : gm3));
         const float geR = R == 0 ? ge0 : (R == 1 ? ge1 : ge2);  // unused for R == 3
         const float rs = row_sb ? v.sb : 1.0f;
-        gw[FA + lane] = rs * ex2(v.gl - gm);
+        v.fa = rs * ex2(v.gl - gm);
+        v.ff = v.sb * ex2(fminf(geR - v.gl, 0.0f));
+        gw[FA + lane] = v.fa;
         gw[FB + lane] = v.sb * ex2(gm - v.gl);
-        gw[FF + lane] = v.sb * ex2(fminf(geR - v.gl, 0.0f));
+        gw[FF + lane] = v.ff;
         gw[FE + lane] = rs * ex2(fminf(v.gl - ge0, 0.0f));
         gw[FE + CH + lane] = rs * ex2(fminf(v.gl - ge1, 0.0f));
         gw[FE + 2 * CH + lane] = rs * ex2(fminf(v.gl - ge2, 0.0f));
@@ -549,7 +552,10 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
         // that nothing reads any more, which keeps the destination a constant)
         constexpr int S = decltype(slot)::value;
         dma_keys(c + 1, kslot(std::integral_constant<int, (S + 1) % 3>{}));
-        if (c + 1 < nchunks) load_gates(c + 1, R2.la, R2.be);
+        // unconditional as well (the token index is clamped): a load issued on
+        // one path only makes the compiler drain every outstanding load,
+        // including the key DMA just issued, before the next LDS read
+        load_gates(c + 1, R2.la, R2.be);
         const uint16_t* kt = (const uint16_t*)kslot(slot);
         f32x4 tr[4][4];
 #pragma unroll
@@ -579,15 +585,18 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
 #pragma unroll
             for (int J = 0; J <= R; ++J) {
                 f32x4 acc = tr[R][J];
+                // per-row scalars by lane permute, not from LDS: this wave has
+                // just issued the next key DMA, and the compiler would make an
+                // LDS read it cannot tell apart from that DMA wait for all of it
                 if (J == R) {
                     const f32x4 cf = *reinterpret_cast<const f32x4*>(gw + FB + 16 * R + 4 * g);
-                    const float rf = gw[FA + 16 * R + ln];
+                    const float rf = lane_get(gv.fa, 16 * R + ln);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) acc[e] = (4 * g + e < ln) ? acc[e] * rf * cf[e] : 0.0f;
                     *reinterpret_cast<f32x4*>(scr + R * SCR_STRIDE + ln * 20 + 4 * g) = acc;
                 } else {
                     const f32x4 rf = *reinterpret_cast<const f32x4*>(gw + FE + J * CH + 16 * R + 4 * g);
-                    tc[R][J] = acc * rf * gw[FF + 16 * J + ln];
+                    tc[R][J] = acc * rf * lane_get(gv.ff, 16 * J + ln);
                 }
             }
         // diagonal blocks: D_R = (I + T_RR)^-1 row by row, one row per lane

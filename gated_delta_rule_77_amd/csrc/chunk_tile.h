@@ -67,6 +67,12 @@ __device__ __forceinline__ void split_pair(const f32x4& lo4, const f32x4& hi4, b
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8, u); }
 
+// x as held by lane src (0..63) of this wave (a lane permute through the LDS
+// crossbar; no LDS memory is read)
+__device__ __forceinline__ float lane_get(float x, int src) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, x)));
+}
+
 // Hardware exp2 / sqrt (about 1 ulp).  Decay exponents here are <= 0, so
 // exp2 only ever underflows towards 0.
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
