@@ -578,7 +578,9 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
         }
         float* scr = reinterpret_cast<float*>(smem + SCR);
         // tc[R][J] holds T[16R + 4g + e][16J + ln] for J < R (T_RJ in accumulator
-        // layout); diagonal blocks (row ln, columns 4g + e) go to the scratch.
+        // layout); diagonal blocks (row ln, columns 4g + e) go to the scratch
+        // negated, as the solve consumes them (a negation folded into the solve's
+        // FMAs would keep them from taking the row broadcast as a DPP operand).
         f32x4 tc[4][4];
 #pragma unroll
         for (int R = 0; R < 4; ++R)
@@ -592,7 +594,7 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
                     const f32x4 cf = *reinterpret_cast<const f32x4*>(gw + FB + 16 * R + 4 * g);
                     const float rf = lane_get(gv.fa, 16 * R + ln);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[e] = (4 * g + e < ln) ? acc[e] * rf * cf[e] : 0.0f;
+                    for (int e = 0; e < 4; ++e) acc[e] = (4 * g + e < ln) ? -(acc[e] * rf * cf[e]) : 0.0f;
                     *reinterpret_cast<f32x4*>(scr + R * SCR_STRIDE + ln * 20 + 4 * g) = acc;
                 } else {
                     const f32x4 rf = *reinterpret_cast<const f32x4*>(gw + FE + J * CH + 16 * R + 4 * g);
@@ -604,7 +606,7 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
         // is final it is broadcast across its block and every row r takes
         // x_r -= T_rj x_j; rows r <= j have T_rj = 0 and stay unchanged, and
         // x_j is zero beyond column j, so step j touches columns 0..j only.
-        // D_R overwrites T_RR in the scratch (row-major, row stride 20).
+        // D_R overwrites -T_RR in the scratch (row-major, row stride 20).
         {
             float* Brow = scr + (lane >> 4) * SCR_STRIDE + (lane & 15) * 20;
             float ntr[16];
@@ -612,7 +614,7 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
             for (int q = 0; q < 4; ++q) {
                 const f32x4 v = *reinterpret_cast<const f32x4*>(Brow + 4 * q);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) ntr[4 * q + e] = -v[e];
+                for (int e = 0; e < 4; ++e) ntr[4 * q + e] = v[e];
             }
             float x[16];
 #pragma unroll

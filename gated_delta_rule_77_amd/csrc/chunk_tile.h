@@ -138,16 +138,33 @@ __device__ __forceinline__ float row_bcast(float x) {
 // 16-lane DPP row.  Lane r starts with x = e_r and ntr = -(row r of L); step j
 // broadcasts the finished row j across the block and every row r takes
 // x_r += ntr_j x_j.  Rows r <= j have L_rj = 0 and stay unchanged, and x_j is
-// zero beyond column j, so step j touches columns 0..j only.  Steps J .. 14:
-template <int J>
+// zero beyond column j, so step j touches columns 0..j only (steps 0 .. 14).
+//
+// Each step is one FMA per column with the broadcast as its DPP source
+// (v_fmac_f32 with row_newbcast), written out because the compiler keeps the
+// broadcast as a separate move.  One asm block per step: the leading s_nop 1
+// gives the two wait states a DPP source needs after a VALU write of it, and
+// inside a block every source was written at least two instructions earlier
+// (in the previous block).  No memory is accessed.
+#define PDN_FMAC_BCAST(J, D) "v_fmac_f32_dpp %" #D ", %" #D ", %[n] row_newbcast:" #J " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
 __device__ __forceinline__ void block_row_solve(float (&x)[16], const float (&ntr)[16]) {
-    if constexpr (J < 15) {
-#pragma unroll
-        for (int c = 0; c <= J; ++c) x[c] = fmaf(row_bcast<J>(x[c]), ntr[J], x[c]);
-        block_row_solve<J + 1>(x, ntr);
-    }
+    asm volatile("s_nop 1\n\t" PDN_FMAC_BCAST(0, 0) : "+v"(x[0]) : [n] "v"(ntr[0]));
+    asm volatile("s_nop 1\n\t" PDN_FMAC_BCAST(1, 0) PDN_FMAC_BCAST(1, 1) : "+v"(x[0]), "+v"(x[1]) : [n] "v"(ntr[1]));
+    asm volatile("s_nop 1\n\t" PDN_FMAC_BCAST(2, 0) PDN_FMAC_BCAST(2, 1) PDN_FMAC_BCAST(2, 2) : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]) : [n] "v"(ntr[2]));
+    asm volatile("s_nop 1\n\t" PDN_FMAC_BCAST(3, 0) PDN_FMAC_BCAST(3, 1) PDN_FMAC_BCAST(3, 2) PDN_FMAC_BCAST(3, 3) : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]) : [n] "v"(ntr[3]));
+    asm volatile("s_nop 1\n\t" PDN_FMAC_BCAST(4, 0) PDN_FMAC_BCAST(4, 1) PDN_FMAC_BCAST(4, 2) PDN_FMAC_BCAST(4, 3) PDN_FMAC_BCAST(4, 4) : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]) : [n] "v"(ntr[4]));
+    asm volatile("s_nop 1\n\t" PDN_FMAC_BCAST(5, 0) PDN_FMAC_BCAST(5, 1) PDN_FMAC_BCAST(5, 2) PDN_FMAC_BCAST(5, 3) PDN_FMAC_BCAST(5, 4) PDN_FMAC_BCAST(5, 5) : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]) : [n] "v"(ntr[5]));
+    asm volatile("s_nop 1\n\t" PDN_FMAC_BCAST(6, 0) PDN_FMAC_BCAST(6, 1) PDN_FMAC_BCAST(6, 2) PDN_FMAC_BCAST(6, 3) PDN_FMAC_BCAST(6, 4) PDN_FMAC_BCAST(6, 5) PDN_FMAC_BCAST(6, 6) : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]) : [n] "v"(ntr[6]));
+    asm volatile("s_nop 1\n\t" PDN_FMAC_BCAST(7, 0) PDN_FMAC_BCAST(7, 1) PDN_FMAC_BCAST(7, 2) PDN_FMAC_BCAST(7, 3) PDN_FMAC_BCAST(7, 4) PDN_FMAC_BCAST(7, 5) PDN_FMAC_BCAST(7, 6) PDN_FMAC_BCAST(7, 7) : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]), "+v"(x[7]) : [n] "v"(ntr[7]));
+    asm volatile("s_nop 1\n\t" PDN_FMAC_BCAST(8, 0) PDN_FMAC_BCAST(8, 1) PDN_FMAC_BCAST(8, 2) PDN_FMAC_BCAST(8, 3) PDN_FMAC_BCAST(8, 4) PDN_FMAC_BCAST(8, 5) PDN_FMAC_BCAST(8, 6) PDN_FMAC_BCAST(8, 7) PDN_FMAC_BCAST(8, 8) : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]), "+v"(x[7]), "+v"(x[8]) : [n] "v"(ntr[8]));
+    asm volatile("s_nop 1\n\t" PDN_FMAC_BCAST(9, 0) PDN_FMAC_BCAST(9, 1) PDN_FMAC_BCAST(9, 2) PDN_FMAC_BCAST(9, 3) PDN_FMAC_BCAST(9, 4) PDN_FMAC_BCAST(9, 5) PDN_FMAC_BCAST(9, 6) PDN_FMAC_BCAST(9, 7) PDN_FMAC_BCAST(9, 8) PDN_FMAC_BCAST(9, 9) : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]), "+v"(x[7]), "+v"(x[8]), "+v"(x[9]) : [n] "v"(ntr[9]));
+    asm volatile("s_nop 1\n\t" PDN_FMAC_BCAST(10, 0) PDN_FMAC_BCAST(10, 1) PDN_FMAC_BCAST(10, 2) PDN_FMAC_BCAST(10, 3) PDN_FMAC_BCAST(10, 4) PDN_FMAC_BCAST(10, 5) PDN_FMAC_BCAST(10, 6) PDN_FMAC_BCAST(10, 7) PDN_FMAC_BCAST(10, 8) PDN_FMAC_BCAST(10, 9) PDN_FMAC_BCAST(10, 10) : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]), "+v"(x[7]), "+v"(x[8]), "+v"(x[9]), "+v"(x[10]) : [n] "v"(ntr[10]));
+    asm volatile("s_nop 1\n\t" PDN_FMAC_BCAST(11, 0) PDN_FMAC_BCAST(11, 1) PDN_FMAC_BCAST(11, 2) PDN_FMAC_BCAST(11, 3) PDN_FMAC_BCAST(11, 4) PDN_FMAC_BCAST(11, 5) PDN_FMAC_BCAST(11, 6) PDN_FMAC_BCAST(11, 7) PDN_FMAC_BCAST(11, 8) PDN_FMAC_BCAST(11, 9) PDN_FMAC_BCAST(11, 10) PDN_FMAC_BCAST(11, 11) : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]), "+v"(x[7]), "+v"(x[8]), "+v"(x[9]), "+v"(x[10]), "+v"(x[11]) : [n] "v"(ntr[11]));
+    asm volatile("s_nop 1\n\t" PDN_FMAC_BCAST(12, 0) PDN_FMAC_BCAST(12, 1) PDN_FMAC_BCAST(12, 2) PDN_FMAC_BCAST(12, 3) PDN_FMAC_BCAST(12, 4) PDN_FMAC_BCAST(12, 5) PDN_FMAC_BCAST(12, 6) PDN_FMAC_BCAST(12, 7) PDN_FMAC_BCAST(12, 8) PDN_FMAC_BCAST(12, 9) PDN_FMAC_BCAST(12, 10) PDN_FMAC_BCAST(12, 11) PDN_FMAC_BCAST(12, 12) : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]), "+v"(x[7]), "+v"(x[8]), "+v"(x[9]), "+v"(x[10]), "+v"(x[11]), "+v"(x[12]) : [n] "v"(ntr[12]));
+    asm volatile("s_nop 1\n\t" PDN_FMAC_BCAST(13, 0) PDN_FMAC_BCAST(13, 1) PDN_FMAC_BCAST(13, 2) PDN_FMAC_BCAST(13, 3) PDN_FMAC_BCAST(13, 4) PDN_FMAC_BCAST(13, 5) PDN_FMAC_BCAST(13, 6) PDN_FMAC_BCAST(13, 7) PDN_FMAC_BCAST(13, 8) PDN_FMAC_BCAST(13, 9) PDN_FMAC_BCAST(13, 10) PDN_FMAC_BCAST(13, 11) PDN_FMAC_BCAST(13, 12) PDN_FMAC_BCAST(13, 13) : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]), "+v"(x[7]), "+v"(x[8]), "+v"(x[9]), "+v"(x[10]), "+v"(x[11]), "+v"(x[12]), "+v"(x[13]) : [n] "v"(ntr[13]));
+    asm volatile("s_nop 1\n\t" PDN_FMAC_BCAST(14, 0) PDN_FMAC_BCAST(14, 1) PDN_FMAC_BCAST(14, 2) PDN_FMAC_BCAST(14, 3) PDN_FMAC_BCAST(14, 4) PDN_FMAC_BCAST(14, 5) PDN_FMAC_BCAST(14, 6) PDN_FMAC_BCAST(14, 7) PDN_FMAC_BCAST(14, 8) PDN_FMAC_BCAST(14, 9) PDN_FMAC_BCAST(14, 10) PDN_FMAC_BCAST(14, 11) PDN_FMAC_BCAST(14, 12) PDN_FMAC_BCAST(14, 13) PDN_FMAC_BCAST(14, 14) : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]), "+v"(x[7]), "+v"(x[8]), "+v"(x[9]), "+v"(x[10]), "+v"(x[11]), "+v"(x[12]), "+v"(x[13]), "+v"(x[14]) : [n] "v"(ntr[14]));
 }
-__device__ __forceinline__ void block_row_solve(float (&x)[16], const float (&ntr)[16]) { block_row_solve<0>(x, ntr); }
+#undef PDN_FMAC_BCAST
 
 }  // namespace tile
 }  // namespace pdn

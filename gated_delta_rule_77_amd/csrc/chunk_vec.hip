@@ -462,13 +462,14 @@ __global__ void __launch_bounds__(256) vec_prep_kernel(PrepParams p) {
     }
     }
 
-    // strictly lower part of the diagonal T blocks (row ln, columns 4g + e) to
-    // the scratch; the upper part may hold overflowed products and is dropped
+    // strictly lower part of the diagonal T blocks (row ln, columns 4g + e),
+    // negated as the solve consumes it, to the scratch; the upper part may hold
+    // overflowed products and is dropped
 #pragma unroll
     for (int R = 0; R < 2; ++R) {
         f32x4 acc = R == 0 ? t00 : t11;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] = (4 * g + e < ln) ? acc[e] : 0.0f;
+        for (int e = 0; e < 4; ++e) acc[e] = (4 * g + e < ln) ? -acc[e] : 0.0f;
         *reinterpret_cast<f32x4*>(scr + R * SCR_STRIDE + ln * 20 + 4 * g) = acc;
     }
     // D_R = (I + T_RR)^-1, one row per lane; lanes 32..63 repeat lanes 0..31
@@ -479,7 +480,7 @@ __global__ void __launch_bounds__(256) vec_prep_kernel(PrepParams p) {
         for (int q = 0; q < 4; ++q) {
             const f32x4 v = *reinterpret_cast<const f32x4*>(Brow + 4 * q);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) ntr[4 * q + e] = -v[e];
+            for (int e = 0; e < 4; ++e) ntr[4 * q + e] = v[e];
         }
         float x[16];
 #pragma unroll
