@@ -256,3 +256,11 @@ def test_null_args_pointer(lib):
     assert lib.pdn_chunk_fwd(None, None) == pdn.PDN_EINVAL
     assert lib.pdn_decode_step(None, None) == pdn.PDN_EINVAL
     assert lib.pdn_chunk_fwd_workspace_size(None, None) == pdn.PDN_EINVAL
+
+
+def test_c_abi_program_builds_and_links(tmp_path, lib):
+    # the C test program compiles warning-free against include/pdn.h and links
+    # against libpdn.so (it runs in the GPU tests)
+    from cabi import build_c_abi_check
+    import os
+    assert os.access(build_c_abi_check(tmp_path), os.X_OK)
