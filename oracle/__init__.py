@@ -9,9 +9,14 @@ library never does, and this package imports nothing from it.
                            (batch, head)), built from ``recurrence.c``.
 * ``delta_rule_py``     -- the same recurrence as a numpy loop for tiny cases.
 
-Parity unpinned: nothing here.  Every function is pinned by tests in
-``tests/test_oracle.py`` against closed forms, invariants and two other
-formulations of the same recurrence kept in ``tests/formulations.py``.
+Every function is pinned by tests in ``tests/test_oracle.py`` against closed
+forms, invariants and two other formulations of the same recurrence kept in
+``tests/formulations.py``.  Parity unpinned: the stabilised preconditioner
+(``precond_mode=PRECOND_STABILISED``, "Preconditioned DeltaNet" Eq. 9).  The
+pages give its steps (log of the running second moment, centring, the squash
+r / (1 + |r|), an exponent mapping into [1/x, x]) but not the centring constant,
+the base or the sign; the form here (centring on the channel mean of
+ln(A + eps), B = x^-s) is a reading, pinned by its own closed forms only.
 """
 from __future__ import annotations
 
@@ -32,6 +37,7 @@ _lib = None
 ALPHA_NONE, ALPHA_SCALAR, ALPHA_VEC = 0, 1, 2
 GATE_SCALAR, GATE_VEC, GAMMA_SAME_AS_BETA = 1, 2, 3
 KEY_SYMMETRIC, KEY_ERASE_GATE, KEY_WRITE_GATE = 0, 1, 2
+PRECOND_INVERSE, PRECOND_STABILISED = 0, 1
 
 
 def build(force: bool = False) -> str:
@@ -54,7 +60,7 @@ def _load():
             P = ctypes.c_void_p
             I = ctypes.c_int
             f.argtypes = [I, I, I, I, I, P, P, P, I, P, I, P, I, P,
-                          ctypes.c_double, P, P, P, P, P, I]
+                          ctypes.c_double, P, P, P, P, P, I, I, ctypes.c_double]
             f.restype = I
             lib.oracle_num_threads.argtypes = []
             lib.oracle_num_threads.restype = I
@@ -79,11 +85,13 @@ def _ptr(x):
 
 def delta_rule(q, k, v, alpha_mode, log_alpha, beta_mode, beta, gamma_mode,
                gamma, precond_eps: float = -1.0, A0=None, S0=None,
-               want_state: bool = True, key_mode: int = KEY_SYMMETRIC):
+               want_state: bool = True, key_mode: int = KEY_SYMMETRIC,
+               precond_mode: int = PRECOND_INVERSE, precond_x: float = 1.5):
     """Run the fp64 recurrence.  Returns (o, S_T, A_T) as float64 arrays.
 
     Shapes follow the C ABI: q, k [B,H,T,dk]; v [B,H,T,dv]; gates and
-    ``key_mode`` as in ``recurrence.c``.  A_T is None unless the
+    ``key_mode`` and ``precond_mode`` / ``precond_x`` (the bound x of the
+    stabilised coefficient) as in ``recurrence.c``.  A_T is None unless the
     preconditioner is on.
     """
     lib = _load()
@@ -99,7 +107,7 @@ def delta_rule(q, k, v, alpha_mode, log_alpha, beta_mode, beta, gamma_mode,
                                int(alpha_mode), _ptr(la), int(beta_mode), _ptr(be),
                                int(gamma_mode), _ptr(ga), float(precond_eps),
                                _ptr(A0), _ptr(AT), _ptr(S0), _ptr(ST), _ptr(o),
-                               int(key_mode))
+                               int(key_mode), int(precond_mode), float(precond_x))
     if rc != 0:
         raise ValueError("oracle_delta_rule failed with code %d" % rc)
     return o, ST, AT
@@ -126,8 +134,19 @@ def keys_and_value(key_mode, b, g, k, v, gamma_same):
     raise ValueError("unknown key mode %r" % (key_mode,))
 
 
+def precond_coeff(A, eps, precond_mode=PRECOND_INVERSE, precond_x=1.5):
+    """Preconditioner coefficient per key channel from the running second
+    moment A [..., dk]: 1 / (A + eps), or the stabilised reading
+    x^-(r / (1 + |r|)) with r = ln(A + eps) - mean over channels."""
+    if precond_mode == PRECOND_INVERSE:
+        return 1.0 / (A + eps)
+    lg = np.log(A + eps)
+    r = lg - lg.mean(axis=-1, keepdims=True)
+    return np.exp(-(r / (1.0 + np.abs(r))) * np.log(precond_x))
+
+
 def _gates_per_token(alpha_mode, log_alpha, beta_mode, beta, gamma_mode, gamma,
-                     precond_eps, A0, k, dk, dv):
+                     precond_eps, A0, k, dk, dv, precond_mode=PRECOND_INVERSE, precond_x=1.5):
     """Per-token decay, erase gain and write gain for one (b, h): [T, dk/dv]."""
     T = k.shape[0]
     if alpha_mode == ALPHA_NONE:
@@ -147,13 +166,17 @@ def _gates_per_token(alpha_mode, log_alpha, beta_mode, beta, gamma_mode, gamma,
     if precond_eps >= 0:
         # A_t is the inclusive running sum of k (.) k, plus A0 when given.
         acc = np.cumsum(k * k, axis=0) + (0.0 if A0 is None else A0[None, :])
-        b = b / (acc + precond_eps)
+        if precond_mode == PRECOND_INVERSE:
+            b = b / (acc + precond_eps)
+        else:
+            b = b * precond_coeff(acc, precond_eps, precond_mode, precond_x)
         A_T = acc[-1] if T > 0 else (np.zeros(dk) if A0 is None else A0.copy())
     return alpha, b, g, A_T
 
 
 def delta_rule_py(q, k, v, alpha_mode, log_alpha, beta_mode, beta, gamma_mode,
-                  gamma, precond_eps=-1.0, A0=None, S0=None, key_mode=KEY_SYMMETRIC):
+                  gamma, precond_eps=-1.0, A0=None, S0=None, key_mode=KEY_SYMMETRIC,
+                  precond_mode=PRECOND_INVERSE, precond_x=1.5):
     """Numpy token loop for tiny inputs (same definition as the C oracle)."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, H, T, dk = q.shape
@@ -166,7 +189,8 @@ def delta_rule_py(q, k, v, alpha_mode, log_alpha, beta_mode, beta, gamma_mode,
             sel = lambda x: None if x is None else _f64(x)[b, h]
             alpha, be, ga, aT = _gates_per_token(alpha_mode, sel(log_alpha), beta_mode,
                                                  sel(beta), gamma_mode, sel(gamma),
-                                                 precond_eps, sel(A0), k[b, h], dk, dv)
+                                                 precond_eps, sel(A0), k[b, h], dk, dv,
+                                                 precond_mode, precond_x)
             S = np.zeros((dk, dv)) if S0 is None else _f64(S0)[b, h].copy()
             for t in range(T):
                 kw, kr, vw = keys_and_value(key_mode, be[t], ga[t], k[b, h, t], v[b, h, t],

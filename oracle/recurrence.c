@@ -17,6 +17,14 @@
  *                                         gain (Preconditioned DeltaNet,
  *                                         section 2.2 "diagonal preconditioner")
  *   else beta'_t = beta_t
+ *   precond_mode 1 (stabilised, "Preconditioned DeltaNet" Eq. 9 as read
+ *   here; the pages do not print the centring constant, the exponent base or
+ *   the sign, so this form is a reading and its parity with the pages is
+ *   unpinned):
+ *       l_i = ln(A_t,i + eps), mu = mean_i l_i     log second moment, centred
+ *       r_i = l_i - mu, s_i = r_i / (1 + |r_i|)    squashed into (-1, 1)
+ *       B_i = x^(-s_i)                             in (1/x, x); larger A, smaller B
+ *       beta'_t = beta_t (.) B_t
  *   gamma'_t = beta_t (raw) when gamma is "same as beta", else gamma_t
  *   kt = sqrt(beta'_t) (.) k_t            symmetric square-root gain on the
  *   vt = sqrt(gamma'_t) (.) v_t           key and the value (FG^2-GDN, 2.1;
@@ -58,6 +66,8 @@
 #define OR_KEY_SYMMETRIC 0
 #define OR_KEY_ERASE_GATE 1
 #define OR_KEY_WRITE_GATE 2
+#define OR_PRECOND_INVERSE 0
+#define OR_PRECOND_STABILISED 1
 
 /* Returns 0 on success, -1 on a bad argument, -2 when out of memory. */
 int oracle_delta_rule(int B, int H, int T, int dk, int dv,
@@ -66,7 +76,8 @@ int oracle_delta_rule(int B, int H, int T, int dk, int dv,
                       int beta_mode, const double *beta,
                       int gamma_mode, const double *gamma,
                       double precond_eps, const double *A0, double *AT,
-                      const double *S0, double *ST, double *o, int key_mode)
+                      const double *S0, double *ST, double *o, int key_mode,
+                      int precond_mode, double precond_x)
 {
     if (B < 0 || H < 0 || T < 0 || dk <= 0 || dv <= 0) return -1;
     if (alpha_mode != OR_ALPHA_NONE && alpha_mode != OR_ALPHA_SCALAR &&
@@ -79,6 +90,8 @@ int oracle_delta_rule(int B, int H, int T, int dk, int dv,
     if (!beta || (gamma_mode != OR_GAMMA_SAME && !gamma)) return -1;
     if (key_mode != OR_KEY_SYMMETRIC && key_mode != OR_KEY_ERASE_GATE &&
         key_mode != OR_KEY_WRITE_GATE) return -1;
+    if (precond_mode != OR_PRECOND_INVERSE && precond_mode != OR_PRECOND_STABILISED) return -1;
+    if (precond_mode == OR_PRECOND_STABILISED && !(precond_x > 1.0)) return -1;
 
     const long BH = (long)B * H;
     int failed = 0;
@@ -92,10 +105,11 @@ int oracle_delta_rule(int B, int H, int T, int dk, int dv,
         double *kr = (double *)malloc(sizeof(double) * (size_t)dk);
         double *vt = (double *)malloc(sizeof(double) * (size_t)dv);
         double *u = (double *)malloc(sizeof(double) * (size_t)dv);
-        if (!S || !A || !al || !kt || !kr || !vt || !u) {
+        double *pb = (double *)malloc(sizeof(double) * (size_t)dk);
+        if (!S || !A || !al || !kt || !kr || !vt || !u || !pb) {
 #pragma omp atomic write
             failed = 1;
-            free(S); free(A); free(al); free(kt); free(kr); free(vt); free(u);
+            free(S); free(A); free(al); free(kt); free(kr); free(vt); free(u); free(pb);
             continue;
         }
         if (S0) memcpy(S, S0 + bh * dk * dv, sizeof(double) * (size_t)dk * dv);
@@ -114,14 +128,26 @@ int oracle_delta_rule(int B, int H, int T, int dk, int dv,
                 else if (alpha_mode == OR_ALPHA_SCALAR) al[i] = exp(log_alpha[tok]);
                 else al[i] = exp(log_alpha[tok * dk + i]);
             }
+            /* preconditioner coefficient per key channel */
+            if (precond_eps >= 0.0) {
+                for (int i = 0; i < dk; ++i) A[i] += kk[i] * kk[i];
+                if (precond_mode == OR_PRECOND_STABILISED) {
+                    double mu = 0.0;
+                    for (int i = 0; i < dk; ++i) mu += log(A[i] + precond_eps);
+                    mu /= dk;
+                    for (int i = 0; i < dk; ++i) {
+                        const double r = log(A[i] + precond_eps) - mu;
+                        const double sq = r / (1.0 + fabs(r));
+                        pb[i] = exp(-sq * log(precond_x));
+                    }
+                }
+            }
             /* key-side gain, with the preconditioner folded in; kt is the
                write key and kr the read key */
             for (int i = 0; i < dk; ++i) {
                 double b = (beta_mode == OR_GATE_SCALAR) ? beta[tok] : beta[tok * dk + i];
-                if (precond_eps >= 0.0) {
-                    A[i] += kk[i] * kk[i];
-                    b = b / (A[i] + precond_eps);
-                }
+                if (precond_eps >= 0.0)
+                    b = (precond_mode == OR_PRECOND_INVERSE) ? b / (A[i] + precond_eps) : b * pb[i];
                 if (key_mode == OR_KEY_SYMMETRIC) {
                     kt[i] = sqrt(b) * kk[i];
                     kr[i] = kt[i];
@@ -162,7 +188,7 @@ int oracle_delta_rule(int B, int H, int T, int dk, int dv,
         }
         if (ST) memcpy(ST + bh * dk * dv, S, sizeof(double) * (size_t)dk * dv);
         if (AT) for (int i = 0; i < dk; ++i) AT[bh * dk + i] = A[i];
-        free(S); free(A); free(al); free(kt); free(kr); free(vt); free(u);
+        free(S); free(A); free(al); free(kt); free(kr); free(vt); free(u); free(pb);
     }
     return failed ? -2 : 0;
 }

@@ -21,7 +21,8 @@ from oracle import _gates_per_token, _f64, keys_and_value
 
 
 def unrolled_product(q, k, v, alpha_mode, log_alpha, beta_mode, beta, gamma_mode,
-                     gamma, precond_eps=-1.0, A0=None, S0=None, key_mode=KEY_SYMMETRIC):
+                     gamma, precond_eps=-1.0, A0=None, S0=None, key_mode=KEY_SYMMETRIC,
+                     precond_mode=0, precond_x=1.5):
     """Explicit transition-matrix form for tiny inputs.
 
     With write key kw, read key kr and written value vw of each token (equal
@@ -42,7 +43,8 @@ def unrolled_product(q, k, v, alpha_mode, log_alpha, beta_mode, beta, gamma_mode
             sel = lambda x: None if x is None else _f64(x)[b, h]
             alpha, be, ga, _ = _gates_per_token(alpha_mode, sel(log_alpha), beta_mode,
                                                 sel(beta), gamma_mode, sel(gamma),
-                                                precond_eps, sel(A0), k[b, h], dk, dv)
+                                                precond_eps, sel(A0), k[b, h], dk, dv,
+                                                precond_mode, precond_x)
             kv = [keys_and_value(key_mode, be[t], ga[t], k[b, h, t], v[b, h, t],
                                  gamma_mode == GAMMA_SAME_AS_BETA) for t in range(T)]
             kts = [x[0] for x in kv]
@@ -70,7 +72,8 @@ def unrolled_product(q, k, v, alpha_mode, log_alpha, beta_mode, beta, gamma_mode
 
 
 def chunked_wy(q, k, v, alpha_mode, log_alpha, beta_mode, beta, gamma_mode,
-               gamma, precond_eps=-1.0, A0=None, S0=None, C=16, key_mode=KEY_SYMMETRIC):
+               gamma, precond_eps=-1.0, A0=None, S0=None, C=16, key_mode=KEY_SYMMETRIC,
+               precond_mode=0, precond_x=1.5):
     """Chunkwise-parallel form with a per-chunk unit-lower-triangular solve.
 
     Within a chunk (positions r = 1..C, cumulative log-decay G_r per key
@@ -95,7 +98,8 @@ def chunked_wy(q, k, v, alpha_mode, log_alpha, beta_mode, beta, gamma_mode,
             sel = lambda x: None if x is None else _f64(x)[b, h]
             alpha, be, ga, _ = _gates_per_token(alpha_mode, sel(log_alpha), beta_mode,
                                                 sel(beta), gamma_mode, sel(gamma),
-                                                precond_eps, sel(A0), k[b, h], dk, dv)
+                                                precond_eps, sel(A0), k[b, h], dk, dv,
+                                                precond_mode, precond_x)
             logal = np.log(alpha)
             S = np.zeros((dk, dv)) if S0 is None else _f64(S0)[b, h].copy()
             for c0 in range(0, T, C):

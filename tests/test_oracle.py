@@ -546,3 +546,104 @@ def test_diagonal_preconditioner_is_exact_for_axis_keys(eps):
                                   GATE_SCALAR, np.ones((1, 1, T)), GAMMA_SAME_AS_BETA, None,
                                   precond_eps=eps, key_mode=oracle.KEY_SYMMETRIC)
     assert np.abs(o_e[0, 0] - np.einsum("tkv,tk->tv", ridge, q)).max() > 1e-3
+
+
+# ---------------------------------------------------------------------------
+# stabilised preconditioner (the reading of "Preconditioned DeltaNet" Eq. 9:
+# B = x^-(r / (1 + |r|)), r = ln(A + eps) - mean over channels).  These pin the
+# reading; its parity with the pages' own formula is unpinned.
+# ---------------------------------------------------------------------------
+
+def _no_precond(c):
+    c.pop("precond_eps")
+    c.pop("A0")
+    return c
+
+
+def _coeff_from_one_token(A, eps, x, beta=0.64, gamma=0.81):
+    """Run the C oracle for one token from a zero state with k = sqrt(A)
+    (so the running sum is A) and read the coefficient back from
+    S_1 = sqrt(beta B) k (sqrt(gamma) v)^T."""
+    dk = len(A)
+    k = np.sqrt(np.asarray(A, np.float64))
+    v = np.linspace(0.5, 1.5, 3)
+    q = np.ones(dk)
+    _, S, _ = oracle.delta_rule(q[None, None, None], k[None, None, None], v[None, None, None],
+                                ALPHA_NONE, None, GATE_SCALAR, np.full((1, 1, 1), beta),
+                                GATE_SCALAR, np.full((1, 1, 1), gamma), precond_eps=eps,
+                                precond_mode=oracle.PRECOND_STABILISED, precond_x=x)
+    return (S[0, 0] / (k[:, None] * np.sqrt(gamma) * v[None, :])) ** 2 / beta
+
+
+def test_stabilised_coefficient_closed_form():
+    # ln A = (1, -1): mean 0, r = (1, -1), s = (1/2, -1/2), B = (x^-1/2, x^1/2);
+    # ln A = (2, 0, 0, -2): s = (2/3, 0, 0, -2/3)
+    x, eps = 1.5, 0.0
+    B = _coeff_from_one_token([np.e, np.exp(-1.0)], eps, x)
+    np.testing.assert_allclose(B, np.repeat([[x ** -0.5], [x ** 0.5]], 3, axis=1), rtol=1e-12)
+    B = _coeff_from_one_token([np.exp(2.0), 1.0, 1.0, np.exp(-2.0)], eps, x)
+    want = np.array([x ** (-2 / 3), 1.0, 1.0, x ** (2 / 3)])
+    np.testing.assert_allclose(B, np.repeat(want[:, None], 3, axis=1), rtol=1e-12)
+    # eps enters inside the logarithm
+    B = _coeff_from_one_token([np.e - 0.25, np.exp(-1.0) - 0.25], 0.25, 2.0)
+    np.testing.assert_allclose(B[:, 0], [2.0 ** -0.5, 2.0 ** 0.5], rtol=1e-12)
+
+
+@pytest.mark.parametrize("x", [1.2, 1.5, 2.0])
+def test_stabilised_coefficient_bounds_and_scale_invariance(x):
+    rng = np.random.default_rng(71)
+    A = np.exp(rng.normal(0.0, 4.0, 16))  # heavy-tailed second moments
+    B = _coeff_from_one_token(A, 0.0, x)[:, 0]
+    assert np.all(B > 1.0 / x) and np.all(B < x)
+    # larger second moment, smaller coefficient
+    order = np.argsort(A)
+    assert np.all(np.diff(B[order]) <= 1e-12)
+    # scaling every key by c shifts ln A by 2 ln c: the centred r, hence B, is unchanged
+    np.testing.assert_allclose(_coeff_from_one_token(A * 9.0, 0.0, x)[:, 0], B, rtol=1e-10)
+    np.testing.assert_allclose(oracle.precond_coeff(A, 0.0, oracle.PRECOND_STABILISED, x), B,
+                               rtol=1e-10)
+
+
+def test_stabilised_is_identity_for_equal_channel_moments():
+    # keys whose entries have equal magnitude in every channel give equal
+    # running sums, so r = 0 and B = 1: the recurrence is the one without a
+    # preconditioner, for every gate mode
+    rng = np.random.default_rng(72)
+    B_, H, T, dk, dv = 1, 2, 40, 8, 5
+    c = _no_precond(_rand_case(rng, B_, H, T, dk, dv, ALPHA_VEC, GATE_VEC, GATE_VEC))
+    c["k"] = rng.choice([-1.0, 1.0], (B_, H, T, dk)) / np.sqrt(dk)
+    plain = oracle.delta_rule(**c)
+    stab = oracle.delta_rule(**c, precond_eps=0.0, precond_mode=oracle.PRECOND_STABILISED,
+                             precond_x=1.5)
+    np.testing.assert_allclose(stab[0], plain[0], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(stab[1], plain[1], rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("key_mode", KEY_MODES)
+def test_stabilised_c_matches_numpy_loop_and_chunked_form(key_mode):
+    rng = np.random.default_rng(73)
+    c = _no_precond(_rand_case(rng, 1, 2, 37, 6, 4, ALPHA_VEC, GATE_VEC, GATE_SCALAR))
+    A0 = rng.uniform(0.0, 1.0, (1, 2, 6))
+    kw = dict(precond_eps=1e-3, A0=A0, precond_mode=oracle.PRECOND_STABILISED, precond_x=1.5,
+              key_mode=key_mode)
+    o, S, AT = oracle.delta_rule(**c, **kw)
+    o2, S2, AT2 = oracle.delta_rule_py(**c, **kw)
+    np.testing.assert_allclose(o, o2, rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(S, S2, rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(AT, AT2, rtol=1e-13)
+    o3, S3 = chunked_wy(**c, **kw, C=8)
+    np.testing.assert_allclose(o, o3, rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(S, S3, rtol=1e-9, atol=1e-11)
+
+
+def test_stabilised_differs_from_inverse_and_rejects_bad_x():
+    rng = np.random.default_rng(74)
+    c = _no_precond(_rand_case(rng, 1, 1, 20, 6, 4, ALPHA_SCALAR, GATE_SCALAR, GAMMA_SAME_AS_BETA))
+    inv = oracle.delta_rule(**c, precond_eps=1e-6)
+    stab = oracle.delta_rule(**c, precond_eps=1e-6, precond_mode=oracle.PRECOND_STABILISED,
+                             precond_x=1.5)
+    assert np.abs(inv[0] - stab[0]).max() > 1e-3
+    np.testing.assert_array_equal(inv[2], stab[2])  # the running sum itself is the same
+    with pytest.raises(ValueError):
+        oracle.delta_rule(**c, precond_eps=1e-6, precond_mode=oracle.PRECOND_STABILISED,
+                          precond_x=1.0)
