@@ -230,8 +230,13 @@ def bench_gated(args):
         pdn.PDN_KEY_WRITE_GATE: ("_write_gate",
                                  "write gate: write key beta' (.) k, read key k, value gamma (.) v"),
     }
-    all_modes = (pdn.PDN_KEY_SYMMETRIC, pdn.PDN_KEY_ERASE_GATE, pdn.PDN_KEY_WRITE_GATE)
-    for mk, steps, modes in ((synth.kda_fg2, 10, (pdn.PDN_KEY_SYMMETRIC,)),
+    # (key mode, preconditioner coefficient) pairs; "stabilised" is the reading
+    # of Preconditioned DeltaNet Eq. 9 with x = 1.5
+    sym = (pdn.PDN_KEY_SYMMETRIC, pdn.PDN_PRECOND_INVERSE)
+    all_modes = (sym, (pdn.PDN_KEY_ERASE_GATE, pdn.PDN_PRECOND_INVERSE),
+                 (pdn.PDN_KEY_WRITE_GATE, pdn.PDN_PRECOND_INVERSE),
+                 (pdn.PDN_KEY_SYMMETRIC, pdn.PDN_PRECOND_STABILISED))
+    for mk, steps, modes in ((synth.kda_fg2, 10, (sym,)),
                              (synth.gdn2_precond, 5, all_modes)):
         w = mk()
         q, k, v = to_dev(w.q, True), to_dev(w.k, True), to_dev(w.v, True)
@@ -241,10 +246,10 @@ def bench_gated(args):
         ST = torch.empty((w.B, w.H, w.dk, w.dv), device="cuda", dtype=torch.float32)
         AT = torch.empty((w.B, w.H, w.dk), device="cuda", dtype=torch.float32) if pre else None
         S0 = to_dev(w.S0)
-        for km in modes:
+        for km, pm in modes:
             kw = dict(log_alpha=la, beta=be, gamma=ga,
                       precond_eps=(w.precond_eps if pre else None),
-                      precond_AT=AT, S0=S0, ST=ST, key_mode=km)
+                      precond_AT=AT, S0=S0, ST=ST, key_mode=km, precond_mode=pm, precond_x=1.5)
             ws = torch.empty(pdn.pdn_chunk_fwd_workspace_size(q, k, v, o, **kw),
                              dtype=torch.uint8, device="cuda")
             # untimed; about 20 ms of work (these calls take at least 0.1 ms per
@@ -269,6 +274,9 @@ def bench_gated(args):
                    + (BH * dk * 4 if pre else 0))
             gbs = alg / (ms / 1e3) / 1e9
             tag, desc = keys[km]
+            if pm == pdn.PDN_PRECOND_STABILISED:
+                tag += "_stabilised"
+                desc += "; stabilised preconditioner x^-(r/(1+|r|)), x = 1.5"
             res["%s%s_B%d_H%d_T%d_d%d" % (w.name, tag, w.B, w.H, w.T, w.dk)] = {
                 "B": w.B, "H": w.H, "T": T, "dk": dk, "dv": dv, "steps": steps, "keys": desc,
                 "call_ms": ms, "tokens_per_s": w.B * T / (ms / 1e3),

@@ -23,11 +23,15 @@ import threading
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpdn.so")
 
+# The argument structs below mirror this version of include/pdn.h.
+PDN_ABI_VERSION = 3
+
 PDN_OK, PDN_EINVAL, PDN_EUNSUPPORTED, PDN_EWORKSPACE, PDN_EHIP = 0, -1, -2, -3, -4
 PDN_F32, PDN_BF16 = 0, 1
 PDN_ALPHA_NONE, PDN_ALPHA_SCALAR, PDN_ALPHA_VEC = 0, 1, 2
 PDN_GATE_SCALAR, PDN_GATE_VEC, PDN_GAMMA_SAME_AS_BETA = 1, 2, 3
 PDN_KEY_SYMMETRIC, PDN_KEY_ERASE_GATE, PDN_KEY_WRITE_GATE = 0, 1, 2
+PDN_PRECOND_INVERSE, PDN_PRECOND_STABILISED = 0, 1
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int32
@@ -42,7 +46,8 @@ class ChunkFwdArgs(ctypes.Structure):
                 ("beta_mode", _I), ("beta", _P),
                 ("gamma_mode", _I), ("gamma", _P),
                 ("key_mode", _I),
-                ("precond_eps", ctypes.c_float), ("precond_A0", _P), ("precond_AT", _P),
+                ("precond_eps", ctypes.c_float), ("precond_mode", _I), ("precond_x", ctypes.c_float),
+                ("precond_A0", _P), ("precond_AT", _P),
                 ("S0", _P), ("ST", _P), ("o", _P),
                 ("workspace", _P), ("workspace_bytes", ctypes.c_size_t)]
 
@@ -56,7 +61,8 @@ class DecodeArgs(ctypes.Structure):
                 ("beta_mode", _I), ("beta", _P),
                 ("gamma_mode", _I), ("gamma", _P),
                 ("key_mode", _I),
-                ("precond_eps", ctypes.c_float), ("precond_A", _P),
+                ("precond_eps", ctypes.c_float), ("precond_mode", _I), ("precond_x", ctypes.c_float),
+                ("precond_A", _P),
                 ("S", _P), ("o", _P)]
 
 
@@ -100,6 +106,13 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         lib.pdn_decode_check.restype = ctypes.c_int
         lib.pdn_decode_step.argtypes = [ctypes.POINTER(DecodeArgs), _P]
         lib.pdn_decode_step.restype = ctypes.c_int
+        # a library built from another header version would read the
+        # argument structs at other offsets (device pointers included)
+        ver = int(lib.pdn_abi_version())
+        if ver != PDN_ABI_VERSION:
+            raise RuntimeError("%s has ABI version %d, this binding mirrors version %d: "
+                               "rebuild it with `python -m gated_delta_rule_77_amd.build`"
+                               % (p, ver, PDN_ABI_VERSION))
         if path is None:
             _lib = lib
         return lib
@@ -166,8 +179,15 @@ def _gate_mode(g, lead):
     return PDN_GATE_SCALAR if g.dim() == lead else PDN_GATE_VEC
 
 
+def _precond_fields(a, precond_eps, precond_mode, precond_x):
+    a.precond_eps = -1.0 if precond_eps is None else float(precond_eps)
+    a.precond_mode = int(precond_mode)
+    a.precond_x = float(precond_x)
+
+
 def _chunk_args(q, k, v, o, log_alpha, beta, gamma, precond_eps, precond_A0,
-                precond_AT, S0, ST, workspace, key_mode):
+                precond_AT, S0, ST, workspace, key_mode, precond_mode=PDN_PRECOND_INVERSE,
+                precond_x=1.5):
     B, H, T, dk = q.shape
     dv = v.shape[-1]
     if tuple(k.shape) != (B, H, T, dk) or tuple(v.shape[:3]) != (B, H, T):
@@ -191,7 +211,7 @@ def _chunk_args(q, k, v, o, log_alpha, beta, gamma, precond_eps, precond_A0,
     a.gamma_mode = PDN_GAMMA_SAME_AS_BETA if gamma is None else _gate_mode(gamma, 3)
     a.gamma = _ptr(gamma)
     a.key_mode = int(key_mode)
-    a.precond_eps = -1.0 if precond_eps is None else float(precond_eps)
+    _precond_fields(a, precond_eps, precond_mode, precond_x)
     a.precond_A0, a.precond_AT = _ptr(precond_A0), _ptr(precond_AT)
     a.S0, a.ST = _ptr(S0), _ptr(ST)
     if workspace is not None:
@@ -202,9 +222,10 @@ def _chunk_args(q, k, v, o, log_alpha, beta, gamma, precond_eps, precond_A0,
 
 def pdn_chunk_fwd_workspace_size(q, k, v, o, log_alpha=None, beta=None, gamma=None,
                                  precond_eps=None, precond_A0=None, precond_AT=None,
-                                 S0=None, ST=None, key_mode=PDN_KEY_SYMMETRIC) -> int:
+                                 S0=None, ST=None, key_mode=PDN_KEY_SYMMETRIC,
+                                 precond_mode=PDN_PRECOND_INVERSE, precond_x=1.5) -> int:
     a = _chunk_args(q, k, v, o, log_alpha, beta, gamma, precond_eps, precond_A0,
-                    precond_AT, S0, ST, None, key_mode)
+                    precond_AT, S0, ST, None, key_mode, precond_mode, precond_x)
     n = ctypes.c_size_t(0)
     rc = load_library().pdn_chunk_fwd_workspace_size(ctypes.byref(a), ctypes.byref(n))
     if rc != PDN_OK:
@@ -214,13 +235,15 @@ def pdn_chunk_fwd_workspace_size(q, k, v, o, log_alpha=None, beta=None, gamma=No
 
 def pdn_chunk_fwd(q, k, v, o, log_alpha=None, beta=None, gamma=None, precond_eps=None,
                   precond_A0=None, precond_AT=None, S0=None, ST=None, workspace=None,
-                  stream=None, key_mode=PDN_KEY_SYMMETRIC) -> None:
+                  stream=None, key_mode=PDN_KEY_SYMMETRIC, precond_mode=PDN_PRECOND_INVERSE,
+                  precond_x=1.5) -> None:
     """Prefill.  Tensors are device tensors in the layouts of include/pdn.h.
 
     The gate modes follow from the tensors' ranks: log_alpha None / [B,H,T] /
     [B,H,T,dk]; beta [B,H,T] / [B,H,T,dk]; gamma None (same as beta) / [B,H,T]
-    / [B,H,T,dv].  key_mode is one of PDN_KEY_*.  o (float32 or bfloat16)
-    receives the output; ST and
+    / [B,H,T,dv].  key_mode is one of PDN_KEY_*; precond_mode one of
+    PDN_PRECOND_* (precond_x is the stabilised mode's bound).  o (float32 or
+    bfloat16) receives the output; ST and
     precond_AT, when given, receive the final state and running k(.)k sum.
     workspace: a device tensor of at least pdn_chunk_fwd_workspace_size() bytes.
     When None and the call needs one, it is allocated here with torch's caching
@@ -228,7 +251,7 @@ def pdn_chunk_fwd(q, k, v, o, log_alpha=None, beta=None, gamma=None, precond_eps
     stream; pass one explicitly when launching on another stream.
     """
     a = _chunk_args(q, k, v, o, log_alpha, beta, gamma, precond_eps, precond_A0,
-                    precond_AT, S0, ST, workspace, key_mode)
+                    precond_AT, S0, ST, workspace, key_mode, precond_mode, precond_x)
     lib = load_library()
     if workspace is None:
         n = ctypes.c_size_t(0)
@@ -245,7 +268,8 @@ def pdn_chunk_fwd(q, k, v, o, log_alpha=None, beta=None, gamma=None, precond_eps
         raise PdnError(rc, "pdn_chunk_fwd")
 
 
-def _decode_args(q, k, v, o, S, log_alpha, beta, gamma, precond_eps, precond_A, key_mode):
+def _decode_args(q, k, v, o, S, log_alpha, beta, gamma, precond_eps, precond_A, key_mode,
+                 precond_mode=PDN_PRECOND_INVERSE, precond_x=1.5):
     B, H, dk = q.shape
     dv = v.shape[-1]
     if tuple(k.shape) != (B, H, dk) or tuple(v.shape[:2]) != (B, H):
@@ -268,17 +292,18 @@ def _decode_args(q, k, v, o, S, log_alpha, beta, gamma, precond_eps, precond_A, 
     a.gamma_mode = PDN_GAMMA_SAME_AS_BETA if gamma is None else _gate_mode(gamma, 2)
     a.gamma = _ptr(gamma)
     a.key_mode = int(key_mode)
-    a.precond_eps = -1.0 if precond_eps is None else float(precond_eps)
+    _precond_fields(a, precond_eps, precond_mode, precond_x)
     a.precond_A = _ptr(precond_A)
     return a
 
 
 def pdn_decode_step(q, k, v, o, S, log_alpha=None, beta=None, gamma=None,
                     precond_eps=None, precond_A=None, stream=None,
-                    key_mode=PDN_KEY_SYMMETRIC) -> None:
+                    key_mode=PDN_KEY_SYMMETRIC, precond_mode=PDN_PRECOND_INVERSE,
+                    precond_x=1.5) -> None:
     """One decode token for all (b,h); S (and precond_A) updated in place."""
     a = _decode_args(q, k, v, o, S, log_alpha, beta, gamma, precond_eps, precond_A,
-                     key_mode)
+                     key_mode, precond_mode, precond_x)
     rc = load_library().pdn_decode_step(ctypes.byref(a), _stream(stream))
     if rc != PDN_OK:
         raise PdnError(rc, "pdn_decode_step")

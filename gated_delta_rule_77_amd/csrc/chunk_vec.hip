@@ -46,7 +46,11 @@
 // With the preconditioner, beta'_t = beta_t / (A_t + eps) with the running
 // sum A_t = A_0 + sum_{s<=t} k_s (.) k_s ("Preconditioned DeltaNet" 2.2):
 // vec_ksq_kernel sums k (.) k per chunk and vec_kscan_kernel turns the sums
-// into the value of A before every chunk (and A_T).
+// into the value of A before every chunk (and A_T).  In the stabilised mode
+// (Eq. 9 as read here) beta'_t = beta_t x^-(r / (1 + |r|)) with
+// r = ln(A_t + eps) minus its mean over the key channels of token t; the
+// preparation kernel forms the per-token means in a pass over the chunk's key
+// rows before the main one.
 #include "chunk_tile.h"
 #include "kernels.h"
 
@@ -105,6 +109,7 @@ struct PrepParams {
     long nbh;
     float eps;
     int has_alpha;
+    float l2x;  // stabilised preconditioner: log2 of its bound x
 };
 
 // How the written value follows from v and the value gain gamma.
@@ -145,6 +150,14 @@ __device__ __forceinline__ void split8(const float (&x)[8], uint4& h, uint4& l) 
     split2(x[2], x[3], h.y, l.y);
     split2(x[4], x[5], h.z, l.z);
     split2(x[6], x[7], h.w, l.w);
+}
+
+// Stabilised preconditioner coefficient x^-(r / (1 + |r|)) of a channel with
+// A + eps = aeps, r = ln(aeps) - (mean of ln over the channels); mu2 is that
+// mean in log2 units and l2x = log2(x).
+__device__ __forceinline__ float stab_coeff(float aeps, float mu2, float l2x) {
+    const float r = (__builtin_amdgcn_logf(aeps) - mu2) * kLn2;
+    return __builtin_amdgcn_exp2f(-(r / (1.0f + fabsf(r))) * l2x);
 }
 
 // Decay factors of one channel (or of a scalar decay) for the two tokens a
@@ -283,8 +296,9 @@ __global__ void __launch_bounds__(KSCAN_SEG * DK) vec_kscan_kernel(float* ks, co
 //     lane (ln, g) holds row ln, columns 4g + e of T_RR;
 //   T_10 with A = block-1 Kr rows 2^(G - G_15), B = block-0 Kw rows 2^(G_15 - G);
 //   P_RS with A = block-S write-key rows, B = block-R query rows gives P_RS^T.
-// KM is the key mode (PDN_KEY_*).
-template <bool AVEC, bool BVEC, bool PRE, int KM>
+// KM is the key mode (PDN_KEY_*); STAB selects the stabilised preconditioner
+// coefficient (with PRE).
+template <bool AVEC, bool BVEC, bool PRE, int KM, bool STAB>
 __global__ void __launch_bounds__(256) vec_prep_kernel(PrepParams p) {
     __shared__ __attribute__((aligned(16))) float scr_all[4][2 * SCR_STRIDE];
     const int lane = threadIdx.x & 63;
@@ -320,6 +334,41 @@ __global__ void __launch_bounds__(256) vec_prep_kernel(PrepParams p) {
     if constexpr (!BVEC && !PRE) {
         sbs[0] = KM == PDN_KEY_SYMMETRIC ? sqrt_hw(bes[0]) : bes[0];
         sbs[1] = KM == PDN_KEY_SYMMETRIC ? sqrt_hw(bes[1]) : bes[1];
+    }
+
+    // stabilised preconditioner: mean of log2(A + eps) over the 128 key
+    // channels of each of this lane's two tokens (lanes ln, 16 + ln, 32 + ln,
+    // 48 + ln hold four disjoint channel groups of the same tokens)
+    float mu2[2] = {0.0f, 0.0f};
+    if constexpr (PRE && STAB) {
+        {
+            float sl[2] = {0.0f, 0.0f};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int cb = 32 * t + 8 * g;
+                uint4 kv[2];
+#pragma unroll
+                for (int b = 0; b < 2; ++b) kv[b] = *reinterpret_cast<const uint4*>(p.k + row[b] * DK + cb);
+                const float* ap = p.astart + id * DK + cb;
+                const f32x4 a0v = *reinterpret_cast<const f32x4*>(ap);
+                const f32x4 a1v = *reinterpret_cast<const f32x4*>(ap + 4);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float k0 = ok[0] ? bf16_at(kv[0], j) : 0.0f;
+                    const float k1 = ok[1] ? bf16_at(kv[1], j) : 0.0f;
+                    const float a0 = row_incl_scan(k0 * k0) + (j < 4 ? a0v[j] : a1v[j - 4]);
+                    const float a1 = row_incl_scan(k1 * k1) + row_bcast<15>(a0);
+                    sl[0] += __builtin_amdgcn_logf(a0 + p.eps);
+                    sl[1] += __builtin_amdgcn_logf(a1 + p.eps);
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                sl[b] += __shfl_xor(sl[b], 16, 64);
+                sl[b] += __shfl_xor(sl[b], 32, 64);
+                mu2[b] = sl[b] * (1.0f / DK);
+            }
+        }
     }
 
     f32x4 t00 = {0.f, 0.f, 0.f, 0.f}, t11 = t00, t10 = t00, p00 = t00, p11 = t00, p10 = t00;
@@ -398,8 +447,13 @@ __global__ void __launch_bounds__(256) vec_prep_kernel(PrepParams p) {
                 if constexpr (PRE) {
                     const float a0 = row_incl_scan(k0 * k0) + as[j];
                     const float a1 = row_incl_scan(k1 * k1) + row_bcast<15>(a0);
-                    b0 *= __builtin_amdgcn_rcpf(a0 + p.eps);
-                    b1 *= __builtin_amdgcn_rcpf(a1 + p.eps);
+                    if constexpr (STAB) {
+                        b0 *= stab_coeff(a0 + p.eps, mu2[0], p.l2x);
+                        b1 *= stab_coeff(a1 + p.eps, mu2[1], p.l2x);
+                    } else {
+                        b0 *= __builtin_amdgcn_rcpf(a0 + p.eps);
+                        b1 *= __builtin_amdgcn_rcpf(a1 + p.eps);
+                    }
                 }
                 sb0 = KM == PDN_KEY_SYMMETRIC ? sqrt_hw(b0) : b0;
                 sb1 = KM == PDN_KEY_SYMMETRIC ? sqrt_hw(b1) : b1;
@@ -813,12 +867,24 @@ bool vec_gates(const pdn_chunk_fwd_args& a) {
 
 long num_chunks(const pdn_chunk_fwd_args& a) { return (static_cast<long>(a.T) + VC - 1) / VC; }
 
-template <bool AVEC, bool BVEC, bool PRE>
-void launch_prep(const PrepParams& pp, int km, long nblk, hipStream_t stream) {
+template <bool AVEC, bool BVEC, bool PRE, bool STAB>
+void launch_prep_km(const PrepParams& pp, int km, long nblk, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(nblk)), block(256);
-    if (km == PDN_KEY_ERASE_GATE) vec_prep_kernel<AVEC, BVEC, PRE, PDN_KEY_ERASE_GATE><<<grid, block, 0, stream>>>(pp);
-    else if (km == PDN_KEY_WRITE_GATE) vec_prep_kernel<AVEC, BVEC, PRE, PDN_KEY_WRITE_GATE><<<grid, block, 0, stream>>>(pp);
-    else vec_prep_kernel<AVEC, BVEC, PRE, PDN_KEY_SYMMETRIC><<<grid, block, 0, stream>>>(pp);
+    if (km == PDN_KEY_ERASE_GATE) vec_prep_kernel<AVEC, BVEC, PRE, PDN_KEY_ERASE_GATE, STAB><<<grid, block, 0, stream>>>(pp);
+    else if (km == PDN_KEY_WRITE_GATE) vec_prep_kernel<AVEC, BVEC, PRE, PDN_KEY_WRITE_GATE, STAB><<<grid, block, 0, stream>>>(pp);
+    else vec_prep_kernel<AVEC, BVEC, PRE, PDN_KEY_SYMMETRIC, STAB><<<grid, block, 0, stream>>>(pp);
+}
+// the stabilised coefficient is a separate instantiation so that it costs the
+// other modes no registers
+template <bool AVEC, bool BVEC, bool PRE>
+void launch_prep(const PrepParams& pp, int km, bool stab, long nblk, hipStream_t stream) {
+    if constexpr (PRE) {
+        if (stab) {
+            launch_prep_km<AVEC, BVEC, PRE, true>(pp, km, nblk, stream);
+            return;
+        }
+    }
+    launch_prep_km<AVEC, BVEC, PRE, false>(pp, km, nblk, stream);
 }
 
 }  // namespace
@@ -860,15 +926,17 @@ hipError_t launch_chunk_vec(const pdn_chunk_fwd_args& a, hipStream_t stream) {
     pp.nc = nc;
     pp.nbh = nbh;
     pp.eps = pre ? a.precond_eps : 0.0f;
+    const bool stab = pre && a.precond_mode == PDN_PRECOND_STABILISED;
+    pp.l2x = stab ? std::log2(a.precond_x) : 0.0f;
     const long nblk = (nbh * nc + 3) / 4;
     const bool avec = a.alpha_mode == PDN_ALPHA_VEC, bvec = a.beta_mode == PDN_GATE_VEC;
     const int km = a.key_mode;
     if (avec) {
-        if (bvec) pre ? launch_prep<true, true, true>(pp, km, nblk, stream) : launch_prep<true, true, false>(pp, km, nblk, stream);
-        else pre ? launch_prep<true, false, true>(pp, km, nblk, stream) : launch_prep<true, false, false>(pp, km, nblk, stream);
+        if (bvec) pre ? launch_prep<true, true, true>(pp, km, stab, nblk, stream) : launch_prep<true, true, false>(pp, km, stab, nblk, stream);
+        else pre ? launch_prep<true, false, true>(pp, km, stab, nblk, stream) : launch_prep<true, false, false>(pp, km, stab, nblk, stream);
     } else {
-        if (bvec) pre ? launch_prep<false, true, true>(pp, km, nblk, stream) : launch_prep<false, true, false>(pp, km, nblk, stream);
-        else pre ? launch_prep<false, false, true>(pp, km, nblk, stream) : launch_prep<false, false, false>(pp, km, nblk, stream);
+        if (bvec) pre ? launch_prep<false, true, true>(pp, km, stab, nblk, stream) : launch_prep<false, true, false>(pp, km, stab, nblk, stream);
+        else pre ? launch_prep<false, false, true>(pp, km, stab, nblk, stream) : launch_prep<false, false, false>(pp, km, stab, nblk, stream);
     }
 
     ChainParams cp;

@@ -1,6 +1,7 @@
 // Device helpers shared by the gfx950 kernels of libpdn.so (not a public header).
 #pragma once
 #include <hip/hip_runtime.h>
+#include <cmath>
 #include <stdint.h>
 
 #include "pdn.h"
@@ -18,6 +19,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 // block, and the clamp keeps both factors inside the fp32/bf16 range.
 constexpr float kLogAlphaMin = -10.0f;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);

@@ -10,7 +10,10 @@
 // with the read key kr, write key kw and written value vw of the key mode:
 // kr = kw = sqrt(beta') k, vw = sqrt(gamma) v (symmetric); kw = k,
 // kr = beta' k, vw = gamma v (erase gate); kw = beta' k, kr = k, vw = v or
-// gamma v (write gate).
+// gamma v (write gate).  beta' = beta / (A + eps) with the diagonal
+// preconditioner, or beta x^-(r / (1 + |r|)) with r = ln(A + eps) minus its
+// mean over the key channels in the stabilised mode (one more block
+// reduction per pair).
 // Both column reductions over the key channels are taken in the same pass over
 // the state, so the state streams through registers exactly once.  This is the
 // recurrent (inference) form of the update in "FG^2-GDN" 2.1 / "Gated
@@ -38,7 +41,8 @@ struct DecodeParams {
     float* S;
     void* o;
     float precond_eps;
-    int alpha_mode, beta_mode, gamma_mode, key_mode;
+    float precond_l2x;  // log2 of the stabilised mode's bound x
+    int alpha_mode, beta_mode, gamma_mode, key_mode, precond_mode;
 };
 
 template <int DK, int DV, bool BF16IN, bool BF16OUT>
@@ -55,6 +59,7 @@ __global__ void __launch_bounds__(256, 3) decode_kernel(DecodeParams p, long nbh
     __shared__ float s_alpha[DK], s_kr[DK], s_kw[DK], s_q[DK], s_vw[DV], s_u[DV];
     __shared__ f32x4 s_red[NRG][2][NCG];
     __shared__ float s_kq[4];
+    __shared__ float s_mu[2];
 
     // Persistent workgroups: each walks (b,h) pairs with a stride of the grid
     // and loads the next pair's state while it finishes the current one, so
@@ -74,19 +79,40 @@ __global__ void __launch_bounds__(256, 3) decode_kernel(DecodeParams p, long nbh
         if (bn < nbh) load_state(bn, sn);
         float* S = p.S + bh * DK * DV;
 
+        // running k (.) k sum and, in the stabilised mode, the coefficient
+        // x^-(r / (1 + |r|)), r = ln(A + eps) - mean over the key channels
+        const bool pre = p.precond_eps >= 0.0f;
+        const bool stab = pre && p.precond_mode == PDN_PRECOND_STABILISED;
+        float kk = 0.0f, Aeps = 1.0f, pc = 1.0f;
+        if (tid < DK) {
+            kk = load_in<BF16IN>(p.k, bh * DK + tid);
+            if (pre) {
+                const float A = p.precond_A[bh * DK + tid] + kk * kk;
+                p.precond_A[bh * DK + tid] = A;
+                Aeps = A + p.precond_eps;
+            }
+        }
+        if (stab) {
+            const float lg = __builtin_amdgcn_logf(Aeps);  // log2
+            if (tid < DK) {
+                const float part = wave_sum(lg);
+                if ((tid & 63) == 0) s_mu[tid >> 6] = part;
+            }
+            __syncthreads();
+            float mu = s_mu[0];
+            if constexpr (DK > 64) mu += s_mu[1];
+            const float r = (lg - mu * (1.0f / DK)) * kLn2;
+            pc = __builtin_amdgcn_exp2f(-(r / (1.0f + fabsf(r))) * p.precond_l2x);
+        }
         if (tid < DK) {
             const int i = tid;
-            const float kk = load_in<BF16IN>(p.k, bh * DK + i);
             const float qq = load_in<BF16IN>(p.q, bh * DK + i);
             float la = 0.0f;
             if (p.alpha_mode == PDN_ALPHA_SCALAR) la = p.log_alpha[bh];
             else if (p.alpha_mode == PDN_ALPHA_VEC) la = p.log_alpha[bh * DK + i];
             float b = (p.beta_mode == PDN_GATE_SCALAR) ? p.beta[bh] : p.beta[bh * DK + i];
-            if (p.precond_eps >= 0.0f) {
-                const float A = p.precond_A[bh * DK + i] + kk * kk;
-                p.precond_A[bh * DK + i] = A;
-                b = b / (A + p.precond_eps);
-            }
+            if (stab) b = b * pc;
+            else if (pre) b = b / Aeps;
             float kr, kw;
             if (p.key_mode == PDN_KEY_ERASE_GATE) {
                 kr = b * kk; kw = kk;
@@ -186,6 +212,8 @@ hipError_t launch_decode(const pdn_decode_args& a, hipStream_t stream) {
     p.log_alpha = a.log_alpha; p.beta = a.beta; p.gamma = a.gamma;
     p.precond_A = a.precond_A; p.S = a.S; p.o = a.o;
     p.precond_eps = a.precond_eps;
+    p.precond_mode = a.precond_mode;
+    p.precond_l2x = a.precond_mode == PDN_PRECOND_STABILISED ? std::log2(a.precond_x) : 0.0f;
     p.alpha_mode = a.alpha_mode; p.beta_mode = a.beta_mode; p.gamma_mode = a.gamma_mode;
     p.key_mode = a.key_mode;
     const long nbh = static_cast<long>(a.B) * a.H;

@@ -22,6 +22,12 @@ bool valid_gamma(int32_t m) {
 bool valid_key(int32_t m) {
     return m == PDN_KEY_SYMMETRIC || m == PDN_KEY_ERASE_GATE || m == PDN_KEY_WRITE_GATE;
 }
+// preconditioner mode and bound; x is only read in the stabilised mode
+bool valid_precond(float eps, int32_t mode, float x) {
+    if (mode != PDN_PRECOND_INVERSE && mode != PDN_PRECOND_STABILISED) return false;
+    if (eps >= 0.0f && mode == PDN_PRECOND_STABILISED && !(x > 1.0f && x <= 2.0f)) return false;
+    return true;
+}
 
 // Largest B*H (and B*H*T) the launch grids and 32/64-bit index math accept.
 constexpr long kMaxBH = 1L << 24;
@@ -55,6 +61,7 @@ int check_chunk(const pdn_chunk_fwd_args* a) {
                          a->gamma, a->precond_eps, a->dk, a->dv, a->T > 0);
     if (rc != PDN_OK) return rc;
     if (!valid_key(a->key_mode)) return PDN_EINVAL;
+    if (!valid_precond(a->precond_eps, a->precond_mode, a->precond_x)) return PDN_EINVAL;
     if (a->T > 0 && (!a->q || !a->k || !a->v || !a->o)) return PDN_EINVAL;
     // the kernels use 16-byte vector loads and stores
     const void* ptrs[] = {a->q, a->k, a->v, a->o, a->log_alpha, a->beta, a->gamma,
@@ -66,8 +73,10 @@ int check_chunk(const pdn_chunk_fwd_args* a) {
     const bool vec = a->alpha_mode == PDN_ALPHA_VEC || a->beta_mode == PDN_GATE_VEC ||
                      a->precond_eps >= 0.0f;
     if (vec && a->dv % 32 != 0) return PDN_EUNSUPPORTED;
-    // asymmetric keys run on the bf16, dk = 128 per-channel-gate kernels only
-    if (a->key_mode != PDN_KEY_SYMMETRIC &&
+    // asymmetric keys and the stabilised preconditioner run on the bf16,
+    // dk = 128 per-channel-gate kernels only
+    const bool stabilised = a->precond_eps >= 0.0f && a->precond_mode == PDN_PRECOND_STABILISED;
+    if ((a->key_mode != PDN_KEY_SYMMETRIC || stabilised) &&
         (a->qkv_dtype != PDN_BF16 || a->dk != 128 || a->dv % 32 != 0))
         return PDN_EUNSUPPORTED;
     if (a->S0 && a->ST && a->S0 != a->ST) {
@@ -91,6 +100,7 @@ int check_decode(const pdn_decode_args* a) {
                          a->gamma, a->precond_eps, a->dk, a->dv, true);
     if (rc != PDN_OK) return rc;
     if (!valid_key(a->key_mode)) return PDN_EINVAL;
+    if (!valid_precond(a->precond_eps, a->precond_mode, a->precond_x)) return PDN_EINVAL;
     if (a->precond_eps >= 0.0f && !a->precond_A) return PDN_EINVAL;
     if (!aligned16(a->S)) return PDN_EINVAL;  // streamed with 16-byte accesses
     if (static_cast<long>(a->B) * a->H > kMaxBH) return PDN_EUNSUPPORTED;

@@ -5,8 +5,11 @@
  *
  *   state S in R^{dk x dv};  for t = 1..T:
  *     alpha_t = exp(log_alpha_t)                 decay, scalar or per key channel
- *     beta'_t = beta_t / (A_t + eps),            when the diagonal preconditioner
+ *     beta'_t = beta_t (.) P(A_t),               when the diagonal preconditioner
  *       A_t = A_{t-1} + k_t (.) k_t              is on (A_t includes k_t); else beta_t
+ *       P = 1 / (A_t + eps)                      (PDN_PRECOND_INVERSE), or
+ *       P = x^-(r / (1 + |r|)),                  (PDN_PRECOND_STABILISED)
+ *         r = ln(A_t + eps) - mean over the dk channels of ln(A_t + eps)
  *     kt = sqrt(beta'_t) (.) k_t,  vt = sqrt(gamma_t) (.) v_t
  *     S_t = Diag(alpha_t) S_{t-1} + kt (vt - (Diag(alpha_t) S_{t-1})^T kt)^T
  *     o_t = S_t^T q_t
@@ -22,7 +25,11 @@
  *     (chunkwise WY form with a lower-triangular (I+T)^-1 solve).
  *   - "Preconditioned DeltaNet: Curvature-aware Sequence Modeling for Linear
  *     Recurrences", section 2.2 / 2B (running diagonal A_t = A_{t-1} + k_t (.) k_t,
- *     P_t = Diag(A_t)^-1), folded here into the erase gain beta.
+ *     P_t = Diag(A_t)^-1), folded here into the erase gain beta; Eq. 9 for the
+ *     stabilised coefficient (log space, centring, the squash r / (1 + |r|),
+ *     values in [1/x, x]).  The pages do not print the centring constant, the
+ *     base or the sign; the mean of ln(A + eps) over the channels and x^-s are
+ *     this library's reading.
  *   gamma is never preconditioned; "gamma same as beta" means the raw beta.
  *   There is no 1/sqrt(dk) scaling inside the op.
  *
@@ -47,7 +54,7 @@
 extern "C" {
 #endif
 
-#define PDN_ABI_VERSION 2
+#define PDN_ABI_VERSION 3
 
 /* Return codes. */
 #define PDN_OK 0
@@ -86,6 +93,12 @@ extern "C" {
 #define PDN_KEY_ERASE_GATE 1
 #define PDN_KEY_WRITE_GATE 2
 
+/* Preconditioner coefficient (when precond_eps >= 0). */
+#define PDN_PRECOND_INVERSE 0     /* 1 / (A_t + eps) */
+#define PDN_PRECOND_STABILISED 1  /* x^-(r/(1+|r|)), see above; needs 1 < precond_x <= 2,
+                                     and in the prefill bf16 q/k/v with dk == 128 and
+                                     dv % 32 == 0 (PDN_EUNSUPPORTED otherwise) */
+
 /*
  * Prefill over whole sequences, chunkwise-parallel on the GPU.
  *
@@ -107,6 +120,8 @@ extern "C" {
  *                     dk == dv); fp32 >= 0.
  *   key_mode          PDN_KEY_* (0 = symmetric, the default).
  *   precond_eps       < 0: preconditioner off.  >= 0: on, with this epsilon.
+ *   precond_mode      PDN_PRECOND_INVERSE (0) or PDN_PRECOND_STABILISED (1).
+ *   precond_x         stabilised mode: the bound x, 1 < x <= 2 (the pages use 1.5).
  *   precond_A0        [B,H,dk] fp32 start of the running k(.)k sum; NULL = zeros.
  *   precond_AT        [B,H,dk] fp32 running sum after token T; NULL = not written.
  *   S0                [B,H,dk,dv] fp32 initial state; NULL = zeros.
@@ -131,6 +146,8 @@ typedef struct pdn_chunk_fwd_args {
     const float *gamma;
     int32_t key_mode;
     float precond_eps;
+    int32_t precond_mode;
+    float precond_x;
     const float *precond_A0;
     float *precond_AT;
     const float *S0;
@@ -151,6 +168,7 @@ typedef struct pdn_chunk_fwd_args {
  *   T == 1 (no clamp on log_alpha here).  key_mode as for the prefill.
  *   precond_eps       < 0 off; >= 0 on, and then precond_A ([B,H,dk] fp32) is
  *                     read, advanced by k(.)k and written back in place.
+ *   precond_mode, precond_x  as for the prefill (every shape takes both modes).
  *   S                 [B,H,dk,dv] fp32, read and overwritten with S_t; 16-byte
  *                     aligned.
  */
@@ -169,6 +187,8 @@ typedef struct pdn_decode_args {
     const float *gamma;
     int32_t key_mode;
     float precond_eps;
+    int32_t precond_mode;
+    float precond_x;
     float *precond_A;
     float *S;
     void *o;

@@ -27,7 +27,7 @@ int oracle_delta_rule(int B, int H, int T, int dk, int dv, const double *q, cons
                       const double *v, int alpha_mode, const double *log_alpha, int beta_mode,
                       const double *beta, int gamma_mode, const double *gamma, double precond_eps,
                       const double *A0, double *AT, const double *S0, double *ST, double *o,
-                      int key_mode);
+                      int key_mode, int precond_mode, double precond_x);
 
 static int failures = 0;
 
@@ -178,7 +178,7 @@ static void prefill_case(int vec, hipStream_t st) {
     double *o_ref = malloc(nv * 8), *s_ref = malloc(ns * 8), *a_ref = malloc(na * 8);
     if (oracle_delta_rule(B, H, T, dk, dv, q, k, v, a.alpha_mode, la, a.beta_mode, be, a.gamma_mode,
                           vec ? ga : NULL, vec ? 1e-6 : -1.0, vec ? a0 : NULL, vec ? a_ref : NULL, s0,
-                          s_ref, o_ref, a.key_mode) != 0) {
+                          s_ref, o_ref, a.key_mode, PDN_PRECOND_INVERSE, 1.5) != 0) {
         printf("oracle failed  FAIL\n");
         ++failures;
         return;
@@ -277,7 +277,7 @@ static void decode_case(hipStream_t st) {
     }
     double *o_ref = malloc(nv * 8), *s_ref = malloc(ns * 8);
     oracle_delta_rule(B, H, T, dk, dv, q, k, v, PDN_ALPHA_VEC, la, PDN_GATE_VEC, be, PDN_GATE_SCALAR, ga,
-                      -1.0, NULL, NULL, s0, s_ref, o_ref, PDN_KEY_WRITE_GATE);
+                      -1.0, NULL, NULL, s0, s_ref, o_ref, PDN_KEY_WRITE_GATE, PDN_PRECOND_INVERSE, 1.5);
     float *s = malloc(ns * 4);
     HIP_CHECK(hipMemcpy(s, dS, ns * 4, hipMemcpyDeviceToHost));
     printf("pdn_decode_step x %d (write gate)\n", T);

@@ -45,7 +45,10 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strerror(lib):
-    assert pdn.pdn_abi_version() == 2
+    assert pdn.pdn_abi_version() == 3
+    # the binding's struct mirrors follow the header's version
+    m = re.search(r"#define PDN_ABI_VERSION (\d+)", open(HEADER).read())
+    assert int(m.group(1)) == pdn.PDN_ABI_VERSION == pdn.pdn_abi_version()
     for code in (0, -1, -2, -3, -4):
         assert pdn.pdn_strerror(code)
     assert "unknown" in pdn.pdn_strerror(-99)
@@ -178,6 +181,16 @@ def test_workspace_size_and_check(lib):
     (lambda a: (setattr(a, "S0", FAKE), setattr(a, "ST", FAKE + 64)), pdn.PDN_EINVAL),
     (lambda a: setattr(a, "key_mode", 3), pdn.PDN_EINVAL),
     (lambda a: setattr(a, "key_mode", -1), pdn.PDN_EINVAL),
+    (lambda a: setattr(a, "precond_mode", 2), pdn.PDN_EINVAL),
+    # stabilised preconditioner: 1 < x <= 2, bf16 with dk = 128 in the prefill
+    (lambda a: (setattr(a, "precond_eps", 1e-6), setattr(a, "precond_mode", pdn.PDN_PRECOND_STABILISED),
+                setattr(a, "precond_x", 1.0)), pdn.PDN_EINVAL),
+    (lambda a: (setattr(a, "precond_eps", 1e-6), setattr(a, "precond_mode", pdn.PDN_PRECOND_STABILISED),
+                setattr(a, "precond_x", 2.5)), pdn.PDN_EINVAL),
+    (lambda a: (setattr(a, "precond_eps", 1e-6), setattr(a, "precond_mode", pdn.PDN_PRECOND_STABILISED),
+                setattr(a, "precond_x", float("nan"))), pdn.PDN_EINVAL),
+    (lambda a: (setattr(a, "precond_eps", 1e-6), setattr(a, "precond_mode", pdn.PDN_PRECOND_STABILISED),
+                setattr(a, "precond_x", 1.5), setattr(a, "qkv_dtype", pdn.PDN_F32)), pdn.PDN_EUNSUPPORTED),
     # asymmetric keys: bf16 inputs with dk = 128 only
     (lambda a: (setattr(a, "key_mode", pdn.PDN_KEY_ERASE_GATE), setattr(a, "qkv_dtype", pdn.PDN_F32)),
      pdn.PDN_EUNSUPPORTED),
@@ -233,6 +246,9 @@ def test_chunk_empty_sequence_needs_no_tensors(lib):
     (lambda a: setattr(a, "dk", 32), pdn.PDN_EUNSUPPORTED),
     (lambda a: setattr(a, "dv", 256), pdn.PDN_EUNSUPPORTED),
     (lambda a: setattr(a, "key_mode", 3), pdn.PDN_EINVAL),
+    (lambda a: (setattr(a, "precond_eps", 1e-6), setattr(a, "precond_A", FAKE),
+                setattr(a, "precond_mode", pdn.PDN_PRECOND_STABILISED), setattr(a, "precond_x", 0.5)),
+     pdn.PDN_EINVAL),
 ])
 def test_decode_validation_codes(lib, mutate, code):
     a = _decode_ok()
@@ -250,6 +266,22 @@ def test_decode_asymmetric_keys_any_shape(lib, km):
     assert _dcheck(lib, a) == pdn.PDN_OK
 
 
+def test_stabilised_preconditioner_accepted(lib):
+    a = _chunk_ok()
+    a.precond_eps, a.precond_mode, a.precond_x = 1e-6, pdn.PDN_PRECOND_STABILISED, 1.5
+    assert _ccheck(lib, a) == pdn.PDN_OK
+    a.precond_x = 2.0
+    assert _ccheck(lib, a) == pdn.PDN_OK
+    # x is not read when the preconditioner is off or in the inverse mode
+    a.precond_eps, a.precond_x = -1.0, 0.0
+    assert _ccheck(lib, a) == pdn.PDN_OK
+    d = _decode_ok()
+    d.precond_eps, d.precond_A = 1e-6, FAKE
+    d.precond_mode, d.precond_x = pdn.PDN_PRECOND_STABILISED, 1.5
+    d.dk, d.qkv_dtype = 64, pdn.PDN_F32  # decode takes every shape
+    assert _dcheck(lib, d) == pdn.PDN_OK
+
+
 def test_null_args_pointer(lib):
     assert lib.pdn_chunk_fwd_check(None) == pdn.PDN_EINVAL
     assert lib.pdn_decode_check(None) == pdn.PDN_EINVAL
@@ -264,3 +296,18 @@ def test_c_abi_program_builds_and_links(tmp_path, lib):
     from cabi import build_c_abi_check
     import os
     assert os.access(build_c_abi_check(tmp_path), os.X_OK)
+
+
+def test_binding_refuses_a_library_of_another_abi_version(tmp_path):
+    # a library built from another header version would read the argument
+    # structs at other offsets: load_library must refuse it before any call
+    stub = tmp_path / "stub.c"
+    stub.write_text("\n".join(
+        ["int pdn_abi_version(void) { return %d; }" % (pdn.PDN_ABI_VERSION - 1),
+         "const char *pdn_strerror(int c) { (void)c; return \"stub\"; }"] +
+        ["int %s(void *a, void *b) { (void)a; (void)b; return -1; }" % n
+         for n in pdn.EXPORTED if n not in ("pdn_abi_version", "pdn_strerror")]))
+    so = tmp_path / "libstub.so"
+    subprocess.check_call(["gcc", "-shared", "-fPIC", str(stub), "-o", str(so)])
+    with pytest.raises(RuntimeError, match="ABI version"):
+        pdn.load_library(str(so))

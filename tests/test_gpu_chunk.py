@@ -24,7 +24,7 @@ pytestmark = pytest.mark.gpu
 
 
 def run_chunk(w, S0="from_workload", want_state=True, o_bf16=False, A0=None,
-              in_place=False, key_mode=0):
+              in_place=False, key_mode=0, precond_mode=0, precond_x=1.5):
     """Run pdn_chunk_fwd on a synth.Workload; returns numpy (o, ST, AT)."""
     import gated_delta_rule_77_amd as pdn
     torch = torch_mod()
@@ -46,7 +46,8 @@ def run_chunk(w, S0="from_workload", want_state=True, o_bf16=False, A0=None,
     AT = torch.empty((w.B, w.H, w.dk), device="cuda") if pre else None
     pdn.pdn_chunk_fwd(q, k, v, o, log_alpha=la, beta=be, gamma=ga,
                       precond_eps=(w.precond_eps if pre else None),
-                      precond_A0=A0d, precond_AT=AT, S0=S0d, ST=ST, key_mode=key_mode)
+                      precond_A0=A0d, precond_AT=AT, S0=S0d, ST=ST, key_mode=key_mode,
+                      precond_mode=precond_mode, precond_x=precond_x)
     torch.cuda.synchronize()
     return host(o), (host(ST) if ST is not None else None), (host(AT) if AT is not None else None)
 
@@ -60,11 +61,13 @@ def sub(w, b0, b1, h0, h1):
                           precond_eps=w.precond_eps, A0=s(w.A0), S0=s(w.S0))
 
 
-def check(name, w, tol, A0=None, key_mode=0, **kw):
-    o, ST, AT = run_chunk(w, A0=A0, key_mode=key_mode, **kw)
+def check(name, w, tol, A0=None, key_mode=0, precond_mode=0, precond_x=1.5, **kw):
+    o, ST, AT = run_chunk(w, A0=A0, key_mode=key_mode, precond_mode=precond_mode,
+                          precond_x=precond_x, **kw)
     o_ref, S_ref, A_ref = oracle.delta_rule(w.q, w.k, w.v, w.alpha_mode, w.log_alpha,
                                             w.beta_mode, w.beta, w.gamma_mode, w.gamma,
-                                            w.precond_eps, A0, w.S0, key_mode=key_mode)
+                                            w.precond_eps, A0, w.S0, key_mode=key_mode,
+                                            precond_mode=precond_mode, precond_x=precond_x)
     eo, es = rel_l2(o, o_ref), rel_l2(ST, S_ref)
     report(name, o=eo, S=es)
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(ST))
@@ -129,13 +132,14 @@ def test_fp32_inputs_dk128_precond():
 # full-size workloads, sampled (batch, head) pairs
 # ---------------------------------------------------------------------------
 
-def _sampled(name, w, pairs, tol, key_mode=0):
-    o, ST, AT = run_chunk(w, key_mode=key_mode)
+def _sampled(name, w, pairs, tol, key_mode=0, precond_mode=0, precond_x=1.5):
+    o, ST, AT = run_chunk(w, key_mode=key_mode, precond_mode=precond_mode, precond_x=precond_x)
     for (b, h) in pairs:
         ws = sub(w, b, b + 1, h, h + 1)
         o_ref, S_ref, A_ref = oracle.delta_rule(ws.q, ws.k, ws.v, ws.alpha_mode, ws.log_alpha,
                                                 ws.beta_mode, ws.beta, ws.gamma_mode, ws.gamma,
-                                                ws.precond_eps, None, ws.S0, key_mode=key_mode)
+                                                ws.precond_eps, None, ws.S0, key_mode=key_mode,
+                                                precond_mode=precond_mode, precond_x=precond_x)
         eo = rel_l2(o[b:b + 1, h:h + 1], o_ref)
         es = rel_l2(ST[b:b + 1, h:h + 1], S_ref)
         report("%s (b=%d,h=%d)" % (name, b, h), o=eo, S=es)
@@ -514,3 +518,72 @@ def test_write_gate_diagonal_preconditioner_is_least_squares(eps):
     report("write gate = least squares eps=%g" % eps, o=eo, S=es)
     assert eo < TOL_BF16 and es < TOL_BF16
     check("write gate axis keys eps=%g" % eps, w, TOL_BF16, key_mode=oracle.KEY_WRITE_GATE)
+
+
+# ---------------------------------------------------------------------------
+# stabilised preconditioner (a reading of "Preconditioned DeltaNet" Eq. 9;
+# parity with the oracle's reading, the pages' own formula is not printed)
+# ---------------------------------------------------------------------------
+
+STAB = oracle.PRECOND_STABILISED
+
+
+@pytest.mark.parametrize("bmode", ["scalar", "vec"])
+@pytest.mark.parametrize("amode", ["none", "scalar", "vec"])
+@pytest.mark.parametrize("km", ["symmetric", "erase", "write"])
+def test_stabilised_preconditioner_matrix(km, amode, bmode):
+    kmode = {"symmetric": oracle.KEY_SYMMETRIC, **KEY_MODES}[km]
+    seed = (["none", "scalar", "vec"].index(amode) * 2 + ["scalar", "vec"].index(bmode)) * 3 \
+        + ["symmetric", "erase", "write"].index(km)
+    rng = np.random.default_rng(500 + seed)
+    w = synth.gdn2_precond(B=1, H=2, T=147, d=128, seed=31, n_pairs=0)
+    if amode == "none":
+        w.alpha_mode, w.log_alpha = synth.ALPHA_NONE, None
+    elif amode == "scalar":
+        w.alpha_mode, w.log_alpha = synth.ALPHA_SCALAR, np.ascontiguousarray(w.log_alpha[..., 0])
+    if bmode == "scalar":
+        w.beta_mode, w.beta = synth.GATE_SCALAR, np.ascontiguousarray(w.beta[..., 0])
+    w.S0 = (0.1 * rng.standard_normal((1, 2, 128, 128))).astype(np.float32)
+    A0 = rng.uniform(0.0, 2.0, (1, 2, 128)).astype(np.float32)
+    check("stabilised keys=%s a=%s b=%s" % (km, amode, bmode), w, TOL_BF16, A0=A0,
+          key_mode=kmode, precond_mode=STAB, precond_x=1.5)
+
+
+@pytest.mark.parametrize("x", [1.1, 2.0])
+@pytest.mark.parametrize("T", [1, 31, 32, 33, 97])
+def test_stabilised_preconditioner_boundary_lengths(T, x):
+    # from an empty running sum (A0 = 0): channels not yet seen have A = 0
+    w = synth.gdn2_precond(B=1, H=2, T=T, d=128, seed=40 + T, n_pairs=0)
+    w.S0 = (0.2 * np.random.default_rng(T).standard_normal((1, 2, 128, 128))).astype(np.float32)
+    check("stabilised x=%g T=%d" % (x, T), w, TOL_BF16, precond_mode=STAB, precond_x=x)
+
+
+@pytest.mark.timeout(1200)
+def test_gdn2_stabilised_full_size_sampled():
+    w = synth.gdn2_precond()             # B1 H16 T65536 d128
+    _sampled("gdn2 stabilised B1 H16 T65536", w, [(0, 3)], TOL_BF16, precond_mode=STAB,
+             precond_x=1.5)
+
+
+def test_stabilised_prefill_matches_decode_steps():
+    import gated_delta_rule_77_amd as pdn
+    torch = torch_mod()
+    w = synth.gdn2_precond(B=2, H=3, T=70, d=128, seed=37, n_pairs=0)
+    w.S0 = (0.05 * np.random.default_rng(5).standard_normal((2, 3, 128, 128))).astype(np.float32)
+    A0 = np.full((2, 3, 128), 0.5, np.float32)
+    o_pf, S_pf, A_pf = run_chunk(w, A0=A0, key_mode=oracle.KEY_ERASE_GATE, precond_mode=STAB)
+    S, A = dev(w.S0), dev(A0)
+    outs = []
+    for t in range(w.T):
+        o = torch.empty((2, 3, 128), device="cuda")
+        pdn.pdn_decode_step(dev(w.q[:, :, t], True), dev(w.k[:, :, t], True),
+                            dev(w.v[:, :, t], True), o, S, log_alpha=dev(w.log_alpha[:, :, t]),
+                            beta=dev(w.beta[:, :, t]), gamma=dev(w.gamma[:, :, t]),
+                            precond_eps=w.precond_eps, precond_A=A, key_mode=oracle.KEY_ERASE_GATE,
+                            precond_mode=STAB, precond_x=1.5)
+        outs.append(o)
+    torch.cuda.synchronize()
+    o_dec = np.stack([host(x) for x in outs], axis=2)
+    assert rel_l2(o_pf, o_dec) < 1e-4
+    assert rel_l2(S_pf, host(S)) < 1e-4
+    assert rel_l2(A_pf, host(A)) < 1e-6

@@ -14,7 +14,7 @@ from gpu_util import TOL_BF16, TOL_F32, dev, host, report, torch_mod
 pytestmark = pytest.mark.gpu
 
 
-def _run_gpu_decode(w, steps, bf16_out=False, A0=None, key_mode=0):
+def _run_gpu_decode(w, steps, bf16_out=False, A0=None, key_mode=0, precond_mode=0, precond_x=1.5):
     import gated_delta_rule_77_amd as pdn
     torch = torch_mod()
     bf = w.qkv_dtype == synth.DT_BF16
@@ -32,18 +32,20 @@ def _run_gpu_decode(w, steps, bf16_out=False, A0=None, key_mode=0):
                         dtype=torch.bfloat16 if bf16_out else torch.float32)
         pdn.pdn_decode_step(q, k, v, o, S, log_alpha=la, beta=be, gamma=ga,
                             precond_eps=(w.precond_eps if w.precond_eps >= 0 else None),
-                            precond_A=A, key_mode=key_mode)
+                            precond_A=A, key_mode=key_mode, precond_mode=precond_mode,
+                            precond_x=precond_x)
         outs.append(o)
     torch.cuda.synchronize()
     o_all = np.stack([host(x) for x in outs], axis=2)
     return o_all, host(S), (host(A) if A is not None else None)
 
 
-def _oracle(w, steps, A0=None, key_mode=0):
+def _oracle(w, steps, A0=None, key_mode=0, precond_mode=0, precond_x=1.5):
     sl = lambda x: None if x is None else x[:, :, :steps]
     return oracle.delta_rule(sl(w.q), sl(w.k), sl(w.v), w.alpha_mode, sl(w.log_alpha),
                              w.beta_mode, sl(w.beta), w.gamma_mode, sl(w.gamma),
-                             w.precond_eps, A0, w.S0, key_mode=key_mode)
+                             w.precond_eps, A0, w.S0, key_mode=key_mode,
+                             precond_mode=precond_mode, precond_x=precond_x)
 
 
 def test_decode_config5_shape_few_steps():
@@ -161,3 +163,21 @@ def test_decode_key_mode_full_shape_few_steps(km):
     eo, es = rel_l2(o, o_ref), rel_l2(S, S_ref)
     report("decode keys=%d B256 H16 d128 3 steps" % km, o=eo, S=es)
     assert eo < TOL_BF16 and es < TOL_BF16
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 128), (128, 64), (64, 64)])
+@pytest.mark.parametrize("bf16", [True, False])
+@pytest.mark.parametrize("km", [oracle.KEY_SYMMETRIC, oracle.KEY_ERASE_GATE, oracle.KEY_WRITE_GATE])
+def test_decode_stabilised_preconditioner(km, dk, dv, bf16):
+    # every shape and key mode, vector gates, from a non-zero running sum
+    w = _mode_case(dk, dv, synth.ALPHA_VEC, synth.GATE_VEC, synth.GATE_SCALAR, True, bf16,
+                   seed=11 * km + dk + dv)
+    A0 = np.abs(np.random.default_rng(3).standard_normal((w.B, w.H, dk))).astype(np.float32)
+    kw = dict(A0=A0, key_mode=km, precond_mode=oracle.PRECOND_STABILISED, precond_x=1.5)
+    o, S, A = _run_gpu_decode(w, w.T, **kw)
+    o_ref, S_ref, A_ref = _oracle(w, w.T, **kw)
+    tol = TOL_BF16 if bf16 else TOL_F32
+    eo, es = rel_l2(o, o_ref), rel_l2(S, S_ref)
+    report("decode stabilised keys=%d dk%d dv%d bf16=%s" % (km, dk, dv, bf16), o=eo, S=es)
+    assert eo < tol and es < tol
+    assert rel_l2(A, A_ref) < 1e-6
