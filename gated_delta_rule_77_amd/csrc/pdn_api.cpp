@@ -31,7 +31,9 @@ bool valid_precond(float eps, int32_t mode, float x) {
 
 // Largest B*H (and B*H*T) the launch grids and 32/64-bit index math accept.
 constexpr long kMaxBH = 1L << 24;
-constexpr long kMaxTokens = 1L << 40;
+// B * H * T: keeps every launch grid (at most one wave per 32-token chunk and
+// (b, h), four per workgroup) below 2^31 workgroups
+constexpr long kMaxTokens = 1L << 36;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 

@@ -178,6 +178,8 @@ def test_workspace_size_and_check(lib):
     (lambda a: setattr(a, "dv", 40), pdn.PDN_EUNSUPPORTED),
     (lambda a: setattr(a, "dv", 512), pdn.PDN_EUNSUPPORTED),
     (lambda a: (setattr(a, "B", 1 << 20), setattr(a, "H", 1 << 10)), pdn.PDN_EUNSUPPORTED),
+    (lambda a: (setattr(a, "B", 1 << 12), setattr(a, "H", 1 << 10), setattr(a, "T", 1 << 15)),
+     pdn.PDN_EUNSUPPORTED),  # 2^37 tokens: more than the launch grids can index
     (lambda a: (setattr(a, "S0", FAKE), setattr(a, "ST", FAKE + 64)), pdn.PDN_EINVAL),
     (lambda a: setattr(a, "key_mode", 3), pdn.PDN_EINVAL),
     (lambda a: setattr(a, "key_mode", -1), pdn.PDN_EINVAL),

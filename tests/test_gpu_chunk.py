@@ -587,3 +587,16 @@ def test_stabilised_prefill_matches_decode_steps():
     assert rel_l2(o_pf, o_dec) < 1e-4
     assert rel_l2(S_pf, host(S)) < 1e-4
     assert rel_l2(A_pf, host(A)) < 1e-6
+
+
+# ---------------------------------------------------------------------------
+# many short sequences: large launch grids, checked on sampled (b, h) pairs
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cfg", ["gdn", "kda_fg2"])
+def test_many_short_sequences_large_grid(cfg):
+    # B*H = 4096 heads of 45 tokens: 16384 scalar-gate workgroups, or 8192
+    # chunk records and 16384 chain workgroups on the per-channel-gate path
+    w = getattr(synth, cfg)(B=64, H=64, T=45, d=128, seed=77)
+    w.S0 = (0.1 * np.random.default_rng(77).standard_normal((64, 64, 128, 128))).astype(np.float32)
+    _sampled("%s B64 H64 T45" % cfg, w, [(0, 0), (13, 41), (63, 63), (32, 7)], TOL_BF16)

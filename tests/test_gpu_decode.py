@@ -181,3 +181,13 @@ def test_decode_stabilised_preconditioner(km, dk, dv, bf16):
     report("decode stabilised keys=%d dk%d dv%d bf16=%s" % (km, dk, dv, bf16), o=eo, S=es)
     assert eo < tol and es < tol
     assert rel_l2(A, A_ref) < 1e-6
+
+
+def test_decode_many_pairs_persistent_loop():
+    # 16384 (b, h) pairs on the resident workgroups: each walks ~21 pairs
+    w = synth.decode(B=1024, H=16, d=128, steps=2, seed=12)
+    o, S, _ = _run_gpu_decode(w, 2)
+    o_ref, S_ref, _ = _oracle(w, 2)
+    eo, es = rel_l2(o, o_ref), rel_l2(S, S_ref)
+    report("decode B1024 H16 d128 2 steps", o=eo, S=es)
+    assert eo < TOL_BF16 and es < TOL_BF16
