@@ -129,6 +129,16 @@ struct ChainParams {
     long nc;
     int dv;
     int o_bf16;
+    // Sequence segments (few heads, long sequences): segment g covers chunks
+    // [g cps, (g + 1) cps).  Segment 0's value columns start from S0; the
+    // value columns of later segments start from 0, and those segments also
+    // run DK identity-start columns (zero values) whose end state is the
+    // segment's transition and whose outputs are Phi^T q per token.
+    int nseg;      // 1: one pass over the whole sequence
+    long cps;      // chunks per segment
+    float* qh;     // [BH][T][DK] outputs of the identity columns
+    float* nst;    // [BH][nseg][DK][dv] end states of the value columns
+    float* phi;    // [BH][nseg][DK][DK] end states of the identity columns
 };
 
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
@@ -590,6 +600,9 @@ __global__ void __launch_bounds__(256) vec_prep_kernel(PrepParams p) {
 // the chain
 // ---------------------------------------------------------------------------
 
+// SEG: the segmented launch (identity-start columns, segment end states);
+// a separate instantiation so that the one-pass chain carries none of it.
+template <bool SEG>
 __global__ void __launch_bounds__(NTHR) vec_chain_kernel(ChainParams p) {
     __shared__ __attribute__((aligned(16))) char smem[LDS_CHAIN];
     const int tid = threadIdx.x;
@@ -598,27 +611,62 @@ __global__ void __launch_bounds__(NTHR) vec_chain_kernel(ChainParams p) {
     const int g = lane >> 4;
     const int ln = lane & 15;
     const int ntile = p.dv / DVT;
-    // all column tiles of a head on one XCD (when the head count allows), so
-    // that they share its L2 for the chunk records
-    const long nbh = gridDim.x / ntile;
     long bh;
     int tile;
-    if (nbh % 8 == 0) {
-        const long slot = blockIdx.x / 8;
-        tile = static_cast<int>(slot % ntile);
-        bh = (slot / ntile) * 8 + blockIdx.x % 8;
+    int seg = 0;
+    bool ident = false;  // identity-start columns (key channels j0 .. j0 + 31)
+    if constexpr (!SEG) {
+        // all column tiles of a head on one XCD (when the head count allows),
+        // so that they share its L2 for the chunk records
+        const long nbh = gridDim.x / ntile;
+        if (nbh % 8 == 0) {
+            const long slot = blockIdx.x / 8;
+            tile = static_cast<int>(slot % ntile);
+            bh = (slot / ntile) * 8 + blockIdx.x % 8;
+        } else {
+            bh = blockIdx.x / ntile;
+            tile = static_cast<int>(blockIdx.x % ntile);
+        }
     } else {
-        bh = blockIdx.x / ntile;
-        tile = static_cast<int>(blockIdx.x % ntile);
+        // per head: segment 0's value tiles, then for each later segment its
+        // value tiles and the DK / DVT identity tiles; all units of a head on
+        // one XCD when the head count allows, as above
+        const int per_seg = ntile + DK / DVT;
+        const int units = ntile + (p.nseg - 1) * per_seg;
+        const long nbh = gridDim.x / units;
+        int u;
+        if (nbh % 8 == 0) {
+            const long slot = blockIdx.x / 8;
+            u = static_cast<int>(slot % units);
+            bh = (slot / units) * 8 + blockIdx.x % 8;
+        } else {
+            bh = blockIdx.x / units;
+            u = static_cast<int>(blockIdx.x % units);
+        }
+        if (u < ntile) {
+            tile = u;
+        } else {
+            seg = 1 + (u - ntile) / per_seg;
+            const int r = (u - ntile) % per_seg;
+            ident = r >= ntile;
+            tile = ident ? r - ntile : r;
+        }
     }
     const int j0 = tile * DVT;
     const long nc = p.nc;
+    const long c0 = SEG ? seg * p.cps : 0;
+    const long c1 = SEG ? min(c0 + p.cps, nc) : nc;
     const char* recs = p.rec + bh * nc * REC;
 
     if (wave < NCHAIN) {
         f32x4 sacc[8];
         const int col = j0 + 16 * wave + ln;
-        if (p.S0) {
+        if (SEG && ident) {
+#pragma unroll
+            for (int ib = 0; ib < 8; ++ib)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sacc[ib][e] = srow(ib, g, e) == col ? 1.0f : 0.0f;
+        } else if (p.S0 && seg == 0) {
 #pragma unroll
             for (int ib = 0; ib < 8; ++ib)
 #pragma unroll
@@ -627,8 +675,8 @@ __global__ void __launch_bounds__(NTHR) vec_chain_kernel(ChainParams p) {
 #pragma unroll
             for (int ib = 0; ib < 8; ++ib) sacc[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        __syncthreads();  // chunk 0 is staged
-        for (long c = 0; c < nc; ++c) {
+        __syncthreads();  // the first chunk is staged
+        for (long c = c0; c < c1; ++c) {
             const char* cur = smem + (c & 1) * BUFV;
             const uint16_t* kgh = reinterpret_cast<const uint16_t*>(cur + R_KGH);
             const uint16_t* kgl = reinterpret_cast<const uint16_t*>(cur + R_KGL);
@@ -763,7 +811,14 @@ __global__ void __launch_bounds__(NTHR) vec_chain_kernel(ChainParams p) {
             for (int R = 0; R < 2; ++R) oacc[R] = mfma32(bU[1], ap[R][0], oacc[R]);
 #pragma unroll
             for (int R = 0; R < 2; ++R) oacc[R] = mfma32(bU[0], ap[R][0], oacc[R]);
-            {
+            if (SEG && ident) {
+                const int c4 = j0 + 16 * wave + 4 * g;
+#pragma unroll
+                for (int R = 0; R < 2; ++R) {
+                    const long tok = c * VC + 16 * R + ln;
+                    if (tok < p.T) *reinterpret_cast<f32x4*>(p.qh + (bh * p.T + tok) * DK + c4) = oacc[R];
+                }
+            } else {
                 const int c4 = j0 + 16 * wave + 4 * g;
 #pragma unroll
                 for (int R = 0; R < 2; ++R) {
@@ -782,7 +837,17 @@ __global__ void __launch_bounds__(NTHR) vec_chain_kernel(ChainParams p) {
             }
             __syncthreads();
         }
-        if (p.ST) {
+        if constexpr (SEG) {
+            // the segment's end state: value columns, or the transition
+            const long sb = (bh * p.nseg + seg) * DK;
+#pragma unroll
+            for (int ib = 0; ib < 8; ++ib)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (ident) p.phi[(sb + srow(ib, g, e)) * DK + col] = sacc[ib][e];
+                    else p.nst[(sb + srow(ib, g, e)) * p.dv + col] = sacc[ib][e];
+                }
+        } else if (p.ST) {
 #pragma unroll
             for (int ib = 0; ib < 8; ++ib)
 #pragma unroll
@@ -802,20 +867,21 @@ __global__ void __launch_bounds__(NTHR) vec_chain_kernel(ChainParams p) {
                 __builtin_amdgcn_global_load_lds((const void*)(src + m * 1024),
                                                  (__attribute__((address_space(3))) void*)(buf + m * 1024), 16, 0, 0);
         };
-        if (nc > 0) dma(0, smem);
+        if (c0 < c1) dma(c0, smem + (c0 & 1) * BUFV);
         __syncthreads();
-        for (long c = 0; c < nc; ++c) {
-            if (c + 1 < nc) dma(c + 1, smem + ((c + 1) & 1) * BUFV);
+        for (long c = c0; c < c1; ++c) {
+            if (c + 1 < c1) dma(c + 1, smem + ((c + 1) & 1) * BUFV);
             __syncthreads();
         }
     } else {
         // wave 3: value tile of a chunk, scaled by sqrt(gamma), gamma or 1, transposed:
         // lane (ln, g) holds tokens 2 ln, 2 ln + 1 of columns j0 + 8g .. + 7.
         // Registers are refilled one chunk ahead; rows past T get 0.
-        uint4 vr[2];
-        f32x4 gv[2][2];
-        float gs[2];
+        uint4 vr[2] = {};
+        f32x4 gv[2][2] = {};
+        float gs[2] = {0.0f, 0.0f};
         auto load = [&](long c) {
+            if (SEG && ident) return;  // no values (and j0 indexes key channels, not value columns)
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const long r = bh * p.T + min(c * VC + 2 * ln + i, p.T - 1);
@@ -840,23 +906,164 @@ __global__ void __launch_bounds__(NTHR) vec_chain_kernel(ChainParams p) {
                 for (int i = 0; i < 2; ++i) {
                     const float gam = p.gvec ? gv[i][cc >> 2][cc & 3] : gs[i];
                     const float sc = p.vmode == VAL_SQRT_GAIN ? sqrt_hw(gam) : (p.vmode == VAL_GAIN ? gam : 1.0f);
-                    v2[i] = okt[i] ? bf16_at(vr[i], cc) * sc : 0.0f;
+                    v2[i] = (okt[i] && !(SEG && ident)) ? bf16_at(vr[i], cc) * sc : 0.0f;
                 }
                 *reinterpret_cast<f32x2*>(sVt + (8 * g + cc) * VTS + 2 * ln) = v2;
             }
         };
-        if (nc > 0) {
-            load(0);
-            stage(0, smem);
-            if (nc > 1) load(1);
+        if (c0 < c1) {
+            load(c0);
+            stage(c0, smem + (c0 & 1) * BUFV);
+            if (c0 + 1 < c1) load(c0 + 1);
         }
         __syncthreads();
-        for (long c = 0; c < nc; ++c) {
-            if (c + 1 < nc) {
+        for (long c = c0; c < c1; ++c) {
+            if (c + 1 < c1) {
                 stage(c + 1, smem + ((c + 1) & 1) * BUFV);
-                if (c + 2 < nc) load(c + 2);
+                if (c + 2 < c1) load(c + 2);
             }
             __syncthreads();
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// sequence segments: combining the segments' end states, correcting outputs
+// ---------------------------------------------------------------------------
+
+// The recurrence is linear in (state, values): a segment run from start
+// state S has end state Phi S + N and outputs o_t + (Phi_t^T q_t)^T S, with
+// N, o_t from the run with S = 0 and Phi, Phi_t^T q_t from the identity-start
+// columns.  The segments' start states follow S_1 = N_0 (segment 0 ran from
+// the real start state), S_{g+1} = Phi_g S_g + N_g; every column of the state
+// follows its own recurrence, so one workgroup takes one (head, 32-column
+// tile) through all segments.  It stores each S_g (g >= 1) for the output
+// correction and writes the final state.  Products are fp32 16x16x4 MFMAs
+// (exact fp32 products, fp32 accumulation).
+constexpr int SEG_NTHR = 256;
+constexpr int CT = 32;  // state columns per combine workgroup
+__global__ void __launch_bounds__(SEG_NTHR) vec_seg_combine_kernel(const float* nst, const float* phi,
+                                                                   float* sst, float* ST, int nseg, int dv) {
+    __shared__ float sPhi[DK][DK + 4];
+    __shared__ float sS[DK][CT + 16];  // row stride 48: the four k rows a read touches fall in distinct banks
+    const int ntile = dv / CT;
+    const long bh = blockIdx.x / ntile;
+    const int j0 = (blockIdx.x % ntile) * CT;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int ln = lane & 15, g4 = lane >> 4;
+    const float* nb = nst + bh * nseg * DK * dv;
+    float* sb = sst + bh * nseg * DK * dv;
+    // S_1 = N_0 (columns j0 .. j0 + CT - 1)
+    for (int i = tid; i < DK * CT; i += SEG_NTHR) sS[i / CT][i % CT] = nb[(i / CT) * dv + j0 + i % CT];
+    for (int g = 1;; ++g) {
+        __syncthreads();
+        // S_g is in sS: keep it for the correction (g < nseg) or it is the
+        // final state (g == nseg)
+        float* dst = g < nseg ? sb + g * DK * dv : (ST ? ST + bh * DK * dv : nullptr);
+        if (dst)
+            for (int i = tid; i < DK * CT; i += SEG_NTHR) dst[(i / CT) * dv + j0 + i % CT] = sS[i / CT][i % CT];
+        if (g == nseg) break;
+        // S_{g+1} = Phi_g S_g + N_g
+        const float* P = phi + (bh * nseg + g) * DK * DK;
+        for (int i = tid; i < DK * DK; i += SEG_NTHR) sPhi[i / DK][i % DK] = P[i];
+        __syncthreads();
+        // wave w: rows 32w .. 32w + 31 (two 16-row blocks) x 32 columns (two blocks)
+        f32x4 acc[2][2];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    acc[rb][cb][e] = nb[(g * DK + 32 * wave + 16 * rb + 4 * g4 + e) * dv + j0 + 16 * cb + ln];
+        for (int k = 0; k < DK; k += 4) {
+            float a[2], b[2];
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) a[rb] = sPhi[32 * wave + 16 * rb + ln][k + g4];
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) b[cb] = sS[k + g4][16 * cb + ln];
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = mfma4(a[rb], b[cb], acc[rb][cb]);
+        }
+        __syncthreads();  // every wave has read S_g
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sS[32 * wave + 16 * rb + 4 * g4 + e][16 * cb + ln] = acc[rb][cb][e];
+    }
+}
+
+// o_t += (Phi_t^T q_t)^T S_g for the tokens of segments g >= 1: one workgroup
+// per (head, segment, 256-token tile), S_g staged in LDS once per 128-column
+// pass; wave w takes 16-token blocks w, w + 4, ... with fp32 16x16x4 MFMAs.
+// In k-step s lane group h contracts key channel 32 h + s, so a lane reads its
+// 32 channels of a qh row as eight 16-byte loads; LDS row 4 s + h holds state
+// row 32 h + s, so the four lane groups of a k-step hit distinct banks.
+constexpr int COR_TOK = 256;
+constexpr int COR_CB = 128;
+__global__ void __launch_bounds__(SEG_NTHR, 2) vec_seg_correct_kernel(const float* qh, const float* sst, float* o,
+                                                                   long T, int nseg, long cps, int dv,
+                                                                   long tiles_per_seg) {
+    __shared__ __attribute__((aligned(16))) float sS[DK][COR_CB + 16];
+    const long unit = blockIdx.x;
+    const long per_bh = (nseg - 1) * tiles_per_seg;
+    const long bh = unit / per_bh;
+    const int g = 1 + static_cast<int>((unit % per_bh) / tiles_per_seg);
+    const long tile = (unit % per_bh) % tiles_per_seg;
+    const long t0 = g * cps * VC + tile * COR_TOK;
+    const long t1 = min(min(t0 + COR_TOK, (g + 1) * cps * VC), T);
+    if (t0 >= t1) return;  // whole workgroup
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int ln = lane & 15, h = lane >> 4;
+    const float* S = sst + (bh * nseg + g) * DK * dv;
+    for (int jb = 0; jb < dv; jb += COR_CB) {
+        const int nj = min(COR_CB, dv - jb);  // a multiple of 32
+        __syncthreads();
+        for (int i = tid; i < DK * COR_CB / 4; i += SEG_NTHR) {
+            const int r = i / (COR_CB / 4), c4 = i % (COR_CB / 4);
+            const f32x4 v = 4 * c4 < nj ? *reinterpret_cast<const f32x4*>(S + r * dv + jb + 4 * c4)
+                                        : f32x4{0.f, 0.f, 0.f, 0.f};
+            *reinterpret_cast<f32x4*>(&sS[4 * (r % 32) + r / 32][4 * c4]) = v;
+        }
+        __syncthreads();
+        for (long tb = t0 + 16 * wave; tb < t1; tb += 64) {
+            const long ta = tb + ln;  // this lane's qh row
+            const float* qrow = qh + (bh * T + ta) * DK + 32 * h;
+            f32x4 an = ta < t1 ? *reinterpret_cast<const f32x4*>(qrow) : f32x4{0.f, 0.f, 0.f, 0.f};
+            // lane (ln, h) holds tokens tb + 4 h + e, column jb + 16 cb + ln
+            float ov[COR_CB / 16][4];
+#pragma unroll
+            for (int cb = 0; cb < COR_CB / 16; ++cb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const long t = tb + 4 * h + e;
+                    ov[cb][e] = 16 * cb < nj && t < t1 ? o[(bh * T + t) * dv + jb + 16 * cb + ln] : 0.f;
+                }
+            f32x4 acc[COR_CB / 16];
+#pragma unroll
+            for (int cb = 0; cb < COR_CB / 16; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+            for (int i = 0; i < 8; ++i) {
+                const f32x4 ai = an;  // channels 32 h + 4 i .. + 3
+                if (i < 7 && ta < t1) an = *reinterpret_cast<const f32x4*>(qrow + 4 * (i + 1));
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int srow = 4 * (4 * i + u) + h;
+#pragma unroll
+                    for (int cb = 0; cb < COR_CB / 16; ++cb) acc[cb] = mfma4(ai[u], sS[srow][16 * cb + ln], acc[cb]);
+                }
+            }
+#pragma unroll
+            for (int cb = 0; cb < COR_CB / 16; ++cb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const long t = tb + 4 * h + e;
+                    if (16 * cb < nj && t < t1) o[(bh * T + t) * dv + jb + 16 * cb + ln] = ov[cb][e] + acc[cb][e];
+                }
         }
     }
 }
@@ -889,6 +1096,37 @@ void launch_prep(const PrepParams& pp, int km, bool stab, long nblk, hipStream_t
 
 }  // namespace
 
+// Sequence segments for few-head prefills: as many as fit one wave of chain
+// workgroups (one per CU), at least 8 chunks each, at most 8; fp32 output only
+// (the correction adds to the stored outputs).
+constexpr long kChainSlots = 256;
+int vec_segments(const pdn_chunk_fwd_args& a) {
+    if (a.o_dtype != PDN_F32) return 1;
+    const long nbh = static_cast<long>(a.B) * a.H, nc = num_chunks(a);
+    const long vt = a.dv / DVT, it = DK / DVT;
+    int G = 1;
+    for (int g = 2; g <= 8; ++g) {
+        if (nc < 8L * g || nbh * (vt * g + it * (g - 1)) > kChainSlots) break;
+        G = g;
+    }
+    return G;
+}
+
+// workspace pieces after the chunk records (and the k.k sums)
+struct SegBufs {
+    size_t qh, nst, phi, sst, end;
+};
+SegBufs seg_layout(const pdn_chunk_fwd_args& a, size_t start, int G) {
+    const size_t nbh = static_cast<size_t>(a.B) * a.H;
+    SegBufs b;
+    b.qh = start;
+    b.nst = b.qh + (G > 1 ? nbh * a.T * DK * sizeof(float) : 0);
+    b.phi = b.nst + (G > 1 ? nbh * G * DK * a.dv * sizeof(float) : 0);
+    b.sst = b.phi + (G > 1 ? nbh * G * DK * DK * sizeof(float) : 0);
+    b.end = b.sst + (G > 1 ? nbh * G * DK * a.dv * sizeof(float) : 0);
+    return b;
+}
+
 bool chunk_vec_supported(const pdn_chunk_fwd_args& a) {
     return a.qkv_dtype == PDN_BF16 && a.dk == DK && a.dv % DVT == 0 &&
            (vec_gates(a) || a.key_mode != PDN_KEY_SYMMETRIC);
@@ -898,7 +1136,7 @@ size_t chunk_vec_workspace_bytes(const pdn_chunk_fwd_args& a) {
     const long nrec = static_cast<long>(a.B) * a.H * num_chunks(a);
     size_t n = static_cast<size_t>(nrec) * REC;
     if (a.precond_eps >= 0.0f) n += static_cast<size_t>(nrec) * DK * sizeof(float);
-    return n;
+    return seg_layout(a, n, vec_segments(a)).end;
 }
 
 hipError_t launch_chunk_vec(const pdn_chunk_fwd_args& a, hipStream_t stream) {
@@ -961,8 +1199,27 @@ hipError_t launch_chunk_vec(const pdn_chunk_fwd_args& a, hipStream_t stream) {
     cp.nc = nc;
     cp.dv = a.dv;
     cp.o_bf16 = a.o_dtype == PDN_BF16;
-    const long nwg = nbh * (a.dv / DVT);
-    vec_chain_kernel<<<dim3(static_cast<unsigned>(nwg)), dim3(NTHR), 0, stream>>>(cp);
+    const int G = vec_segments(a);
+    const long vt = a.dv / DVT, it = DK / DVT;
+    size_t recs_end = static_cast<size_t>(nbh * nc) * REC;
+    if (pre) recs_end += static_cast<size_t>(nbh * nc) * DK * sizeof(float);
+    const SegBufs sb = seg_layout(a, recs_end, G);
+    cp.nseg = G;
+    cp.cps = G > 1 ? (nc + G - 1) / G : nc;
+    cp.qh = reinterpret_cast<float*>(ws + sb.qh);
+    cp.nst = reinterpret_cast<float*>(ws + sb.nst);
+    cp.phi = reinterpret_cast<float*>(ws + sb.phi);
+    const long nwg = nbh * (vt + (G - 1) * (vt + it));
+    if (G > 1) vec_chain_kernel<true><<<dim3(static_cast<unsigned>(nwg)), dim3(NTHR), 0, stream>>>(cp);
+    else vec_chain_kernel<false><<<dim3(static_cast<unsigned>(nwg)), dim3(NTHR), 0, stream>>>(cp);
+    if (G > 1) {
+        float* sst = reinterpret_cast<float*>(ws + sb.sst);
+        vec_seg_combine_kernel<<<dim3(static_cast<unsigned>(nbh * (a.dv / CT))), dim3(SEG_NTHR), 0, stream>>>(
+            cp.nst, cp.phi, sst, a.ST, G, a.dv);
+        const long tiles = (cp.cps * VC + COR_TOK - 1) / COR_TOK;
+        vec_seg_correct_kernel<<<dim3(static_cast<unsigned>(nbh * (G - 1) * tiles)), dim3(SEG_NTHR), 0, stream>>>(
+            cp.qh, sst, static_cast<float*>(a.o), a.T, G, cp.cps, a.dv, tiles);
+    }
     return hipGetLastError();
 }
 

@@ -313,3 +313,16 @@ def test_binding_refuses_a_library_of_another_abi_version(tmp_path):
     subprocess.check_call(["gcc", "-shared", "-fPIC", str(stub), "-o", str(so)])
     with pytest.raises(RuntimeError, match="ABI version"):
         pdn.load_library(str(so))
+
+
+def test_workspace_for_sequence_segments(lib):
+    # two heads, 1000 tokens, fp32 output: four segments, which add the
+    # identity-column outputs [B,H,T,dk] and three [B,H,segments,dk,dv|dk]
+    # state arrays (fp32); bf16 output keeps one pass and no extra
+    a = _chunk_ok()
+    a.B, a.H, a.T = 1, 2, 1000
+    a.o_dtype = pdn.PDN_BF16
+    one = _ws_size(lib, a)
+    a.o_dtype = pdn.PDN_F32
+    seg = _ws_size(lib, a)
+    assert seg - one == 2 * 1000 * 128 * 4 + 3 * 2 * 4 * 128 * 128 * 4

@@ -600,3 +600,34 @@ def test_many_short_sequences_large_grid(cfg):
     w = getattr(synth, cfg)(B=64, H=64, T=45, d=128, seed=77)
     w.S0 = (0.1 * np.random.default_rng(77).standard_normal((64, 64, 128, 128))).astype(np.float32)
     _sampled("%s B64 H64 T45" % cfg, w, [(0, 0), (13, 41), (63, 63), (32, 7)], TOL_BF16)
+
+
+# ---------------------------------------------------------------------------
+# sequence segments (few heads, long sequences, fp32 output): the library runs
+# the segments in parallel and corrects them by their start states
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T", [512, 1000, 2047])   # 2, 4 and 8 segments for two heads
+@pytest.mark.parametrize("mode", ["gdn2", "kda_fg2", "erase", "write", "stabilised"])
+def test_sequence_segments(mode, T):
+    rng = np.random.default_rng(600 + T)
+    if mode == "kda_fg2":
+        w = synth.kda_fg2(B=1, H=2, T=T, d=128, seed=T)
+        A0 = None
+    else:
+        w = synth.gdn2_precond(B=1, H=2, T=T, d=128, seed=T, n_pairs=8)
+        A0 = rng.uniform(0.0, 2.0, (1, 2, 128)).astype(np.float32)
+    w.S0 = (0.1 * rng.standard_normal((1, 2, 128, 128))).astype(np.float32)
+    km = {"erase": oracle.KEY_ERASE_GATE, "write": oracle.KEY_WRITE_GATE}.get(mode, 0)
+    pm = STAB if mode == "stabilised" else 0
+    check("segments %s T=%d" % (mode, T), w, TOL_BF16, A0=A0, key_mode=km, precond_mode=pm)
+
+
+def test_sequence_segments_match_one_pass():
+    # bf16 output keeps the one-pass chain; the final states of both runs agree
+    w = synth.gdn2_precond(B=1, H=3, T=1500, d=128, seed=81, n_pairs=4)
+    w.S0 = (0.1 * np.random.default_rng(81).standard_normal((1, 3, 128, 128))).astype(np.float32)
+    o_seg, S_seg, _ = run_chunk(w)
+    o_one, S_one, _ = run_chunk(w, o_bf16=True)
+    assert rel_l2(S_seg, S_one) < 1e-5
+    assert rel_l2(o_one, o_seg) < 4e-3   # bf16 rounding of o
