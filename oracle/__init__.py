@@ -8,10 +8,16 @@ library never does, and this package imports nothing from it.
 * ``delta_rule``        -- the token-by-token recurrence (C, fp64, OpenMP over
                            (batch, head)), built from ``recurrence.c``.
 * ``delta_rule_py``     -- the same recurrence as a numpy loop for tiny cases.
+* ``delta_rule_bwd``    -- its backward pass (reverse mode through the token
+                           recurrence, fp64, C): gradients of
+                           sum <dO, o> + <dST, S_T> with respect to q, k, v,
+                           the decay, the gains, S0 and A0.
 
 Every function is pinned by tests in ``tests/test_oracle.py`` against closed
 forms, invariants and two other formulations of the same recurrence kept in
-``tests/formulations.py``.  Parity unpinned: the stabilised preconditioner
+``tests/formulations.py``; the backward by ``tests/test_oracle_bwd.py``
+(finite differences of the forward in every mode, Euler identities, a closed
+form, autodiff of the transition-product form).  Parity unpinned: the stabilised preconditioner
 (``precond_mode=PRECOND_STABILISED``, "Preconditioned DeltaNet" Eq. 9).  The
 pages give its steps (log of the running second moment, centring, the squash
 r / (1 + |r|), an exponent mapping into [1/x, x]) but not the centring constant,
@@ -62,6 +68,10 @@ def _load():
             f.argtypes = [I, I, I, I, I, P, P, P, I, P, I, P, I, P,
                           ctypes.c_double, P, P, P, P, P, I, I, ctypes.c_double]
             f.restype = I
+            g = lib.oracle_delta_rule_bwd
+            g.argtypes = [I, I, I, I, I, P, P, P, I, P, I, P, I, P, ctypes.c_double, P, P,
+                          I, I, ctypes.c_double, P, P, P, P, P, P, P, P, P, P]
+            g.restype = I
             lib.oracle_num_threads.argtypes = []
             lib.oracle_num_threads.restype = I
             _lib = lib
@@ -111,6 +121,47 @@ def delta_rule(q, k, v, alpha_mode, log_alpha, beta_mode, beta, gamma_mode,
     if rc != 0:
         raise ValueError("oracle_delta_rule failed with code %d" % rc)
     return o, ST, AT
+
+
+def delta_rule_bwd(q, k, v, alpha_mode, log_alpha, beta_mode, beta, gamma_mode,
+                   gamma, dO, dST=None, precond_eps: float = -1.0, A0=None, S0=None,
+                   key_mode: int = KEY_SYMMETRIC, precond_mode: int = PRECOND_INVERSE,
+                   precond_x: float = 1.5):
+    """Gradients of L = sum <dO, o> + <dST, S_T> for the recurrence of
+    ``delta_rule`` (same arguments; dST None means zero).
+
+    Returns a dict of float64 arrays: dq, dk [B,H,T,dk]; dv [B,H,T,dv];
+    dlog_alpha (shape of log_alpha, None without decay); dbeta (shape of
+    beta); dgamma (shape of gamma, None when gamma is "same as beta", whose
+    gradient is in dbeta); dS0 [B,H,dk,dv]; dA0 [B,H,dk] (None without the
+    preconditioner).
+    """
+    lib = _load()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    la, be, ga = _f64(log_alpha), _f64(beta), _f64(gamma)
+    A0, S0, dO, dST = _f64(A0), _f64(S0), _f64(dO), _f64(dST)
+    out = {
+        "dq": np.zeros((B, H, T, dk)), "dk": np.zeros((B, H, T, dk)),
+        "dv": np.zeros((B, H, T, dv)),
+        "dlog_alpha": None if alpha_mode == ALPHA_NONE else np.zeros(la.shape),
+        "dbeta": np.zeros(be.shape),
+        "dgamma": None if gamma_mode == GAMMA_SAME_AS_BETA else np.zeros(ga.shape),
+        "dS0": np.zeros((B, H, dk, dv)),
+        "dA0": np.zeros((B, H, dk)) if precond_eps >= 0 else None,
+    }
+    rc = lib.oracle_delta_rule_bwd(B, H, T, dk, dv, _ptr(q), _ptr(k), _ptr(v),
+                                   int(alpha_mode), _ptr(la), int(beta_mode), _ptr(be),
+                                   int(gamma_mode), _ptr(ga), float(precond_eps),
+                                   _ptr(A0), _ptr(S0), int(key_mode), int(precond_mode),
+                                   float(precond_x), _ptr(dO), _ptr(dST),
+                                   _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                                   _ptr(out["dlog_alpha"]), _ptr(out["dbeta"]),
+                                   _ptr(out["dgamma"]), _ptr(out["dS0"]), _ptr(out["dA0"]))
+    if rc != 0:
+        raise ValueError("oracle_delta_rule_bwd failed with code %d" % rc)
+    return out
 
 
 def run_workload(w, S0="from_workload", want_state=True):
