@@ -12,6 +12,8 @@ Entry points (same names as the C ABI):
     pdn_chunk_fwd(...)                 prefill over [B,H,T,d]
     pdn_chunk_fwd_workspace_size(...)  scratch bytes the prefill needs
     pdn_decode_step(...)               one token against a resident state
+    pdn_chunk_bwd(...)                 gradients of the prefill
+    pdn_chunk_bwd_workspace_size(...)  scratch bytes the backward needs
     pdn_abi_version(), pdn_strerror(code)
 """
 from __future__ import annotations
@@ -24,7 +26,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpdn.so")
 
 # The argument structs below mirror this version of include/pdn.h.
-PDN_ABI_VERSION = 3
+PDN_ABI_VERSION = 4
 
 PDN_OK, PDN_EINVAL, PDN_EUNSUPPORTED, PDN_EWORKSPACE, PDN_EHIP = 0, -1, -2, -3, -4
 PDN_F32, PDN_BF16 = 0, 1
@@ -52,6 +54,15 @@ class ChunkFwdArgs(ctypes.Structure):
                 ("workspace", _P), ("workspace_bytes", ctypes.c_size_t)]
 
 
+class ChunkBwdArgs(ctypes.Structure):
+    """Mirror of ``pdn_chunk_bwd_args``."""
+    _fields_ = [("fwd", ChunkFwdArgs), ("dO", _P), ("dST", _P),
+                ("dq", _P), ("dk", _P), ("dv", _P),
+                ("dlog_alpha", _P), ("dbeta", _P), ("dgamma", _P),
+                ("dS0", _P), ("dA0", _P),
+                ("workspace", _P), ("workspace_bytes", ctypes.c_size_t)]
+
+
 class DecodeArgs(ctypes.Structure):
     """Mirror of ``pdn_decode_args``."""
     _fields_ = [("B", _I), ("H", _I), ("dk", _I), ("dv", _I),
@@ -67,7 +78,8 @@ class DecodeArgs(ctypes.Structure):
 
 
 EXPORTED = ("pdn_abi_version", "pdn_strerror", "pdn_chunk_fwd_workspace_size",
-            "pdn_chunk_fwd_check", "pdn_chunk_fwd", "pdn_decode_check", "pdn_decode_step")
+            "pdn_chunk_fwd_check", "pdn_chunk_fwd", "pdn_decode_check", "pdn_decode_step",
+            "pdn_chunk_bwd_workspace_size", "pdn_chunk_bwd_check", "pdn_chunk_bwd")
 
 _lib = None
 _lock = threading.Lock()
@@ -102,6 +114,13 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         lib.pdn_chunk_fwd_check.restype = ctypes.c_int
         lib.pdn_chunk_fwd.argtypes = [ctypes.POINTER(ChunkFwdArgs), _P]
         lib.pdn_chunk_fwd.restype = ctypes.c_int
+        lib.pdn_chunk_bwd_workspace_size.argtypes = [ctypes.POINTER(ChunkBwdArgs),
+                                                     ctypes.POINTER(ctypes.c_size_t)]
+        lib.pdn_chunk_bwd_workspace_size.restype = ctypes.c_int
+        lib.pdn_chunk_bwd_check.argtypes = [ctypes.POINTER(ChunkBwdArgs)]
+        lib.pdn_chunk_bwd_check.restype = ctypes.c_int
+        lib.pdn_chunk_bwd.argtypes = [ctypes.POINTER(ChunkBwdArgs), _P]
+        lib.pdn_chunk_bwd.restype = ctypes.c_int
         lib.pdn_decode_check.argtypes = [ctypes.POINTER(DecodeArgs)]
         lib.pdn_decode_check.restype = ctypes.c_int
         lib.pdn_decode_step.argtypes = [ctypes.POINTER(DecodeArgs), _P]
@@ -266,6 +285,86 @@ def pdn_chunk_fwd(q, k, v, o, log_alpha=None, beta=None, gamma=None, precond_eps
     rc = lib.pdn_chunk_fwd(ctypes.byref(a), _stream(stream))
     if rc != PDN_OK:
         raise PdnError(rc, "pdn_chunk_fwd")
+
+
+def _bwd_args(q, k, v, dO, dq, dk, dv, dlog_alpha, dbeta, dgamma, dS0, dA0, log_alpha, beta,
+              gamma, precond_eps, precond_A0, S0, dST, workspace, key_mode, precond_mode,
+              precond_x):
+    f = _chunk_args(q, k, v, dO, log_alpha, beta, gamma, precond_eps, precond_A0, None, S0,
+                    None, None, key_mode, precond_mode, precond_x)
+    f.o = None
+    B, H, T, dkk = q.shape
+    dvv = v.shape[-1]
+    if tuple(dq.shape) != (B, H, T, dkk) or tuple(dk.shape) != (B, H, T, dkk):
+        raise ValueError("dq, dk must be [B,H,T,dk]")
+    if tuple(dv.shape) != (B, H, T, dvv):
+        raise ValueError("dv must be [B,H,T,dv]")
+    for name, t, like in (("dlog_alpha", dlog_alpha, log_alpha), ("dbeta", dbeta, beta),
+                          ("dgamma", dgamma, gamma)):
+        if (t is None) != (like is None):
+            raise ValueError("%s must be given exactly when its gate is" % name)
+        if t is not None and tuple(t.shape) != tuple(like.shape):
+            raise ValueError("%s must have the shape of its gate" % name)
+    for name, t in (("dO", dO), ("dST", dST), ("dq", dq), ("dk", dk), ("dv", dv),
+                    ("dlog_alpha", dlog_alpha), ("dbeta", dbeta), ("dgamma", dgamma),
+                    ("dS0", dS0), ("dA0", dA0)):
+        _f32(t, name)
+    a = ChunkBwdArgs()
+    a.fwd = f
+    a.dO, a.dST = _ptr(dO), _ptr(dST)
+    a.dq, a.dk, a.dv = _ptr(dq), _ptr(dk), _ptr(dv)
+    a.dlog_alpha, a.dbeta, a.dgamma = _ptr(dlog_alpha), _ptr(dbeta), _ptr(dgamma)
+    a.dS0, a.dA0 = _ptr(dS0), _ptr(dA0)
+    if workspace is not None:
+        a.workspace = _ptr(workspace)
+        a.workspace_bytes = workspace.numel() * workspace.element_size()
+    return a
+
+
+def pdn_chunk_bwd_workspace_size(q, k, v, dO, dq, dk, dv, dlog_alpha=None, dbeta=None,
+                                 dgamma=None, dS0=None, dA0=None, log_alpha=None, beta=None,
+                                 gamma=None, precond_eps=None, precond_A0=None, S0=None,
+                                 dST=None, key_mode=PDN_KEY_SYMMETRIC,
+                                 precond_mode=PDN_PRECOND_INVERSE, precond_x=1.5) -> int:
+    a = _bwd_args(q, k, v, dO, dq, dk, dv, dlog_alpha, dbeta, dgamma, dS0, dA0, log_alpha,
+                  beta, gamma, precond_eps, precond_A0, S0, dST, None, key_mode, precond_mode,
+                  precond_x)
+    n = ctypes.c_size_t(0)
+    rc = load_library().pdn_chunk_bwd_workspace_size(ctypes.byref(a), ctypes.byref(n))
+    if rc != PDN_OK:
+        raise PdnError(rc, "pdn_chunk_bwd_workspace_size")
+    return int(n.value)
+
+
+def pdn_chunk_bwd(q, k, v, dO, dq, dk, dv, dlog_alpha=None, dbeta=None, dgamma=None,
+                  dS0=None, dA0=None, log_alpha=None, beta=None, gamma=None, precond_eps=None,
+                  precond_A0=None, S0=None, dST=None, workspace=None, stream=None,
+                  key_mode=PDN_KEY_SYMMETRIC, precond_mode=PDN_PRECOND_INVERSE,
+                  precond_x=1.5) -> None:
+    """Backward of the prefill: writes the gradients of
+    sum <dO, o> + <dST, S_T> into the caller's fp32 tensors dq, dk [B,H,T,dk],
+    dv [B,H,T,dv], dlog_alpha / dbeta / dgamma (shapes of their gates; given
+    exactly when the gate is), dS0 [B,H,dk,dv] and dA0 [B,H,dk] (optional).
+    The forward inputs are passed as to pdn_chunk_fwd.  workspace as for
+    pdn_chunk_fwd (allocated here from torch's caching allocator when None).
+    """
+    a = _bwd_args(q, k, v, dO, dq, dk, dv, dlog_alpha, dbeta, dgamma, dS0, dA0, log_alpha,
+                  beta, gamma, precond_eps, precond_A0, S0, dST, workspace, key_mode,
+                  precond_mode, precond_x)
+    lib = load_library()
+    if workspace is None:
+        n = ctypes.c_size_t(0)
+        rc = lib.pdn_chunk_bwd_workspace_size(ctypes.byref(a), ctypes.byref(n))
+        if rc != PDN_OK:
+            raise PdnError(rc, "pdn_chunk_bwd_workspace_size")
+        if n.value:
+            import torch
+            workspace = torch.empty(int(n.value), dtype=torch.uint8, device=q.device)
+            a.workspace = _ptr(workspace)
+            a.workspace_bytes = int(n.value)
+    rc = lib.pdn_chunk_bwd(ctypes.byref(a), _stream(stream))
+    if rc != PDN_OK:
+        raise PdnError(rc, "pdn_chunk_bwd")
 
 
 def _decode_args(q, k, v, o, S, log_alpha, beta, gamma, precond_eps, precond_A, key_mode,

@@ -26,4 +26,8 @@ hipError_t launch_chunk_vec(const pdn_chunk_fwd_args& a, hipStream_t stream);
 // Scratch bytes the prefill needs for these (valid) arguments.
 size_t chunk_fwd_workspace_bytes(const pdn_chunk_fwd_args& a);
 
+// Backward of the prefill (any q/k/v dtype, dk in {64, 128}, dv % 32 == 0).
+size_t chunk_bwd_workspace_bytes(const pdn_chunk_bwd_args& a);
+hipError_t launch_chunk_bwd(const pdn_chunk_bwd_args& a, hipStream_t stream);
+
 }  // namespace pdn

@@ -93,6 +93,41 @@ int check_chunk(const pdn_chunk_fwd_args* a) {
     return PDN_OK;
 }
 
+// B * H * T for the backward: its per-chunk grids stay below 2^31 workgroups
+constexpr long kMaxBwdTokens = 1L << 35;
+
+int check_bwd(const pdn_chunk_bwd_args* a) {
+    if (!a) return PDN_EINVAL;
+    const pdn_chunk_fwd_args& f = a->fwd;
+    if (f.B < 1 || f.H < 1 || f.T < 0 || f.dk < 1 || f.dv < 1) return PDN_EINVAL;
+    if (!valid_dtype(f.qkv_dtype)) return PDN_EINVAL;
+    if (static_cast<long>(f.B) * f.H > kMaxBH) return PDN_EUNSUPPORTED;
+    if (static_cast<long>(f.B) * f.H * f.T > kMaxBwdTokens) return PDN_EUNSUPPORTED;
+    const bool data = f.T > 0;
+    int rc = check_gates(f.alpha_mode, f.log_alpha, f.beta_mode, f.beta, f.gamma_mode, f.gamma,
+                         f.precond_eps, f.dk, f.dv, data);
+    if (rc != PDN_OK) return rc;
+    if (!valid_key(f.key_mode)) return PDN_EINVAL;
+    if (!valid_precond(f.precond_eps, f.precond_mode, f.precond_x)) return PDN_EINVAL;
+    if (data) {
+        if (!f.q || !f.k || !f.v || !a->dO || !a->dq || !a->dk || !a->dv || !a->dbeta)
+            return PDN_EINVAL;
+        if (f.alpha_mode != PDN_ALPHA_NONE && !a->dlog_alpha) return PDN_EINVAL;
+        if (f.gamma_mode != PDN_GAMMA_SAME_AS_BETA && !a->dgamma) return PDN_EINVAL;
+    }
+    const void* ptrs[] = {f.q, f.k, f.v, f.log_alpha, f.beta, f.gamma, f.precond_A0, f.S0,
+                          a->dO, a->dST, a->dq, a->dk, a->dv, a->dlog_alpha, a->dbeta,
+                          a->dgamma, a->dS0, a->dA0};
+    for (const void* ptr : ptrs)
+        if (ptr && !aligned16(ptr)) return PDN_EINVAL;
+    if (f.dk != 64 && f.dk != 128) return PDN_EUNSUPPORTED;
+    if (f.dv % 32 != 0 || f.dv > 256) return PDN_EUNSUPPORTED;
+    if (f.precond_eps >= 0.0f && f.precond_mode != PDN_PRECOND_INVERSE) return PDN_EUNSUPPORTED;
+    const size_t need = pdn::chunk_bwd_workspace_bytes(*a);
+    if (need > 0 && (!a->workspace || a->workspace_bytes < need)) return PDN_EWORKSPACE;
+    return PDN_OK;
+}
+
 int check_decode(const pdn_decode_args* a) {
     if (!a) return PDN_EINVAL;
     if (a->B < 1 || a->H < 1 || a->dk < 1 || a->dv < 1) return PDN_EINVAL;
@@ -160,6 +195,41 @@ int pdn_chunk_fwd(const pdn_chunk_fwd_args* args, void* stream) {
         if (rc != PDN_OK) return rc;
         const hipError_t e = pdn::launch_chunk_fwd(*args, static_cast<hipStream_t>(stream));
         if (e == hipErrorNotSupported) return PDN_EUNSUPPORTED;
+        return e == hipSuccess ? PDN_OK : PDN_EHIP;
+    } catch (...) {
+        return PDN_EHIP;
+    }
+}
+
+int pdn_chunk_bwd_workspace_size(const pdn_chunk_bwd_args* args, size_t* bytes) {
+    if (!args || !bytes) return PDN_EINVAL;
+    try {
+        pdn_chunk_bwd_args probe = *args;
+        const size_t need = pdn::chunk_bwd_workspace_bytes(probe);
+        probe.workspace_bytes = need;
+        probe.workspace = need ? reinterpret_cast<void*>(uintptr_t(256)) : nullptr;
+        const int rc = check_bwd(&probe);
+        if (rc != PDN_OK) return rc;
+        *bytes = need;
+        return PDN_OK;
+    } catch (...) {
+        return PDN_EINVAL;
+    }
+}
+
+int pdn_chunk_bwd_check(const pdn_chunk_bwd_args* args) {
+    try {
+        return check_bwd(args);
+    } catch (...) {
+        return PDN_EINVAL;
+    }
+}
+
+int pdn_chunk_bwd(const pdn_chunk_bwd_args* args, void* stream) {
+    try {
+        const int rc = check_bwd(args);
+        if (rc != PDN_OK) return rc;
+        const hipError_t e = pdn::launch_chunk_bwd(*args, static_cast<hipStream_t>(stream));
         return e == hipSuccess ? PDN_OK : PDN_EHIP;
     } catch (...) {
         return PDN_EHIP;

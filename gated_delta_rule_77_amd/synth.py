@@ -210,6 +210,16 @@ def headline(B=4, H=16, T=8192, d=128, seed=0) -> Workload:
     return w
 
 
+def upstream_grads(w: Workload, seed: int = 1):
+    """Seeded upstream gradients for the backward of a prefill workload:
+    dO [B,H,T,dv] and dST [B,H,dk,dv], both N(0,1) float32 (the gradient of a
+    loss that weighs every output and the final state alike)."""
+    rng = np.random.default_rng(seed)
+    dO = rng.standard_normal((w.B, w.H, w.T, w.dv), dtype=np.float32)
+    dST = rng.standard_normal((w.B, w.H, w.dk, w.dv), dtype=np.float32)
+    return dO, dST
+
+
 CONFIGS = {
     "deltanet_fp32": deltanet_fp32,
     "gdn": gdn,

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define PDN_ABI_VERSION 3
+#define PDN_ABI_VERSION 4
 
 /* Return codes. */
 #define PDN_OK 0
@@ -194,6 +194,53 @@ typedef struct pdn_decode_args {
     void *o;
 } pdn_decode_args;
 
+/*
+ * Backward of the prefill: gradients of
+ *
+ *   L = sum_{b,h,t} <dO_t, o_t> + sum_{b,h} <dST, S_T>
+ *
+ * with respect to q, k, v, log_alpha, beta, gamma, S0 and precond_A0 (the
+ * gate-aware backward of "Gated DeltaNet-2", section 3 on chunkwise training:
+ * with per-channel gates the decay cannot be pulled out of the dot products,
+ * so the backward differentiates through the gate-scaled operands).  The forward is recomputed inside the call; nothing from a
+ * previous pdn_chunk_fwd is needed.
+ *
+ *   fwd               the forward's arguments: sizes, q, k, v, gates, key_mode,
+ *                     preconditioner (inverse mode only), precond_A0, S0.  Its
+ *                     o, ST, precond_AT, workspace and workspace_bytes are
+ *                     ignored.  q/k/v fp32 or bf16; dk in {64, 128}; dv a
+ *                     multiple of 32 and <= 256.  log_alpha is clamped at -10
+ *                     as in the forward, and its gradient is zero where clamped.
+ *   dO                [B,H,T,dv] fp32.          dST: [B,H,dk,dv] fp32, NULL = 0.
+ *   dq, dk            [B,H,T,dk] fp32.          dv:  [B,H,T,dv] fp32.
+ *   dlog_alpha        shape of log_alpha; NULL exactly when alpha_mode is NONE.
+ *   dbeta             shape of beta.
+ *   dgamma            shape of gamma; NULL exactly when gamma is "same as beta"
+ *                     (that gradient is added into dbeta).
+ *   dS0               [B,H,dk,dv] fp32; NULL = not written.
+ *   dA0               [B,H,dk] fp32 (preconditioner on); NULL = not written.
+ *   workspace, workspace_bytes   caller-owned device scratch of at least
+ *                     pdn_chunk_bwd_workspace_size() bytes.
+ * Every pointer 16-byte aligned; outputs must not overlap inputs or each
+ * other.  In the symmetric key mode the gradient of sqrt(beta') is unbounded
+ * at beta' = 0 (likewise gamma): such tokens give inf or NaN gradients.
+ */
+typedef struct pdn_chunk_bwd_args {
+    pdn_chunk_fwd_args fwd;
+    const float *dO;
+    const float *dST;
+    float *dq;
+    float *dk;
+    float *dv;
+    float *dlog_alpha;
+    float *dbeta;
+    float *dgamma;
+    float *dS0;
+    float *dA0;
+    void *workspace;
+    size_t workspace_bytes;
+} pdn_chunk_bwd_args;
+
 /* PDN_ABI_VERSION of the loaded library. */
 int pdn_abi_version(void);
 
@@ -223,6 +270,20 @@ int pdn_decode_check(const pdn_decode_args *args);
 
 /* Decode one token for all (b,h): o, S in place, precond_A in place. */
 int pdn_decode_step(const pdn_decode_args *args, void *stream);
+
+/* Device scratch bytes pdn_chunk_bwd needs (PDN_OK and *bytes, or a PDN_E*
+ * code).  Per (b, h) and 32-token chunk: the chunk's gate-scaled operands and
+ * solve blocks, its start state and the gradient of its end state
+ * (dk x dv fp32 each), and dq/dk-side intermediates: about 9 KB per
+ * token-head at dk = dv = 128.  The workspace holds no state between calls. */
+int pdn_chunk_bwd_workspace_size(const pdn_chunk_bwd_args *args, size_t *bytes);
+
+/* Validate only (no HIP call, no launch). */
+int pdn_chunk_bwd_check(const pdn_chunk_bwd_args *args);
+
+/* Backward of the prefill: every gradient listed above, asynchronously on
+ * `stream`.  Chunk length 32; T need not be a multiple of it. */
+int pdn_chunk_bwd(const pdn_chunk_bwd_args *args, void *stream);
 
 #ifdef __cplusplus
 }

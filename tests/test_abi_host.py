@@ -45,7 +45,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strerror(lib):
-    assert pdn.pdn_abi_version() == 3
+    assert pdn.pdn_abi_version() == 4
     # the binding's struct mirrors follow the header's version
     m = re.search(r"#define PDN_ABI_VERSION (\d+)", open(HEADER).read())
     assert int(m.group(1)) == pdn.PDN_ABI_VERSION == pdn.pdn_abi_version()
@@ -58,7 +58,11 @@ def test_struct_layout_matches_header(tmp_path):
     prog = tmp_path / "layout.c"
     fields_c = [f for f, _ in pdn.ChunkFwdArgs._fields_]
     fields_d = [f for f, _ in pdn.DecodeArgs._fields_]
+    fields_b = [f for f, _ in pdn.ChunkBwdArgs._fields_]
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "pdn.h"', 'int main(void){']
+    lines.append('printf("bwd %zu\\n", sizeof(pdn_chunk_bwd_args));')
+    for f in fields_b:
+        lines.append('printf("b.%s %%zu\\n", offsetof(pdn_chunk_bwd_args, %s));' % (f, f))
     lines.append('printf("chunk %zu\\n", sizeof(pdn_chunk_fwd_args));')
     for f in fields_c:
         lines.append('printf("c.%s %%zu\\n", offsetof(pdn_chunk_fwd_args, %s));' % (f, f))
@@ -77,6 +81,9 @@ def test_struct_layout_matches_header(tmp_path):
         assert int(got["c." + f]) == getattr(pdn.ChunkFwdArgs, f).offset, f
     for f in fields_d:
         assert int(got["d." + f]) == getattr(pdn.DecodeArgs, f).offset, f
+    assert int(got["bwd"]) == ctypes.sizeof(pdn.ChunkBwdArgs)
+    for f in fields_b:
+        assert int(got["b." + f]) == getattr(pdn.ChunkBwdArgs, f).offset, f
 
 
 def _chunk_ok():
@@ -326,3 +333,95 @@ def test_workspace_for_sequence_segments(lib):
     a.o_dtype = pdn.PDN_F32
     seg = _ws_size(lib, a)
     assert seg - one == 2 * 1000 * 128 * 4 + 3 * 2 * 4 * 128 * 128 * 4
+
+
+def _bwd_ok():
+    a = pdn.ChunkBwdArgs()
+    a.fwd = _chunk_ok()
+    a.fwd.o = None
+    a.dO = a.dST = a.dq = a.dk = a.dv = FAKE
+    a.dlog_alpha = a.dbeta = a.dgamma = a.dS0 = FAKE
+    a.workspace, a.workspace_bytes = FAKE, 1 << 40
+    return a
+
+
+def _bcheck(lib, a):
+    return lib.pdn_chunk_bwd_check(ctypes.byref(a))
+
+
+def _bws(lib, a):
+    n = ctypes.c_size_t(123)
+    rc = lib.pdn_chunk_bwd_workspace_size(ctypes.byref(a), ctypes.byref(n))
+    return rc, n.value
+
+
+BWD_BAD = [
+    (lambda a: setattr(a, "dq", None), pdn.PDN_EINVAL),
+    (lambda a: setattr(a, "dO", None), pdn.PDN_EINVAL),
+    (lambda a: setattr(a, "dlog_alpha", None), pdn.PDN_EINVAL),
+    (lambda a: setattr(a, "dbeta", None), pdn.PDN_EINVAL),
+    (lambda a: setattr(a, "dgamma", None), pdn.PDN_EINVAL),
+    (lambda a: setattr(a, "dv", FAKE + 4), pdn.PDN_EINVAL),          # misaligned
+    (lambda a: setattr(a.fwd, "key_mode", 3), pdn.PDN_EINVAL),
+    (lambda a: setattr(a.fwd, "dk", 96), pdn.PDN_EUNSUPPORTED),
+    (lambda a: setattr(a.fwd, "dv", 48), pdn.PDN_EUNSUPPORTED),       # dv % 32
+    (lambda a: setattr(a.fwd, "dv", 288), pdn.PDN_EUNSUPPORTED),
+    (lambda a: (setattr(a.fwd, "precond_eps", 1e-6),
+                setattr(a.fwd, "precond_mode", pdn.PDN_PRECOND_STABILISED),
+                setattr(a.fwd, "precond_x", 1.5)), pdn.PDN_EUNSUPPORTED),
+    (lambda a: setattr(a, "workspace_bytes", 1000), pdn.PDN_EWORKSPACE),
+    (lambda a: setattr(a, "workspace", None), pdn.PDN_EWORKSPACE),
+    (lambda a: setattr(a.fwd, "T", -1), pdn.PDN_EINVAL),
+]
+
+
+def test_bwd_valid_arguments(lib):
+    assert _bcheck(lib, _bwd_ok()) == pdn.PDN_OK
+    a = _bwd_ok()
+    # fp32 inputs, dk = 64, scalar gates, every key mode, the inverse preconditioner
+    a.fwd.qkv_dtype, a.fwd.dk, a.fwd.dv = pdn.PDN_F32, 64, 64
+    a.fwd.alpha_mode, a.fwd.beta_mode = pdn.PDN_ALPHA_SCALAR, pdn.PDN_GATE_SCALAR
+    a.fwd.gamma_mode, a.fwd.gamma, a.dgamma = pdn.PDN_GAMMA_SAME_AS_BETA, None, None
+    a.fwd.precond_eps = 1e-6
+    for km in (0, 1, 2):
+        a.fwd.key_mode = km
+        assert _bcheck(lib, a) == pdn.PDN_OK
+    # no decay: no d log alpha needed
+    a.fwd.alpha_mode, a.fwd.log_alpha, a.dlog_alpha = pdn.PDN_ALPHA_NONE, None, None
+    assert _bcheck(lib, a) == pdn.PDN_OK
+    assert lib.pdn_chunk_bwd_check(None) == pdn.PDN_EINVAL
+    assert lib.pdn_chunk_bwd(None, None) == pdn.PDN_EINVAL
+
+
+@pytest.mark.parametrize("mutate,code", BWD_BAD)
+def test_bwd_validation(lib, mutate, code):
+    a = _bwd_ok()
+    mutate(a)
+    assert _bcheck(lib, a) == code
+    # the launching entry point returns the same code without touching memory
+    assert lib.pdn_chunk_bwd(ctypes.byref(a), None) == code
+
+
+def test_bwd_workspace_size(lib):
+    # per (b, h) and 32-token chunk, fp32: the record (3 32 x dk operand blocks,
+    # 32 x dv values, two 32 x 32 blocks, dk), the chunk start state (one more
+    # for S_T), the end-state gradient, U and Z (32 x dv each) and the gradient
+    # record (3 32 x dk, two 32 x 32, dk); each array 256-byte aligned
+    a = _bwd_ok()
+    a.fwd.B, a.fwd.H, a.fwd.T, a.fwd.dk, a.fwd.dv = 1, 2, 100, 128, 64
+    rc, n = _bws(lib, a)
+    assert rc == pdn.PDN_OK
+    nbh, nc, dk, dv = 2, 4, 128, 64
+    al = lambda x: (x + 255) // 256 * 256
+    want = (al(nbh * nc * (3 * 32 * dk + 32 * dv + 2 * 32 * 32 + dk) * 4)
+            + al(nbh * (nc + 1) * dk * dv * 4) + al(nbh * nc * dk * dv * 4)
+            + 2 * al(nbh * nc * 32 * dv * 4) + al(nbh * nc * (3 * 32 * dk + 2 * 32 * 32 + dk) * 4))
+    assert n == want
+    # the preconditioner adds four [B,H,chunks,dk] arrays and one [B,H,chunks*32,dk]
+    a.fwd.precond_eps = 1e-6
+    rc, n2 = _bws(lib, a)
+    assert rc == pdn.PDN_OK
+    assert n2 - n == 4 * al(nbh * nc * dk * 4) + al(nbh * nc * 32 * dk * 4)
+    # T = 0 needs none
+    a.fwd.T = 0
+    assert _bws(lib, a) == (pdn.PDN_OK, 0)

@@ -1,0 +1,279 @@
+"""GPU parity of pdn_chunk_bwd against the oracle's backward (through the C ABI).
+
+* the gate / key / preconditioner matrix at a size the oracle finishes at
+  once (several 32-token chunks and a ragged tail), fp32 and bf16 inputs,
+  dk 64 and 128;
+* the prefill workloads at reduced sizes, and at full size in the benchmark's
+  launch configuration on sampled (batch, head) pairs that the oracle
+  recomputes over the whole sequence;
+* edge cases: T = 0, 1, 31, 32, 33; no dST; no S0; dv 32 and 256; the
+  preconditioner's A0;
+* properties at full size: Euler's identity sum v dv + sum S0 dS0 = L for the
+  loss L = <dO, o> + <dST, S_T> of the GPU forward, and bitwise determinism.
+
+Tolerance.  The backward computes in fp32 throughout (exact fp32 products),
+from bf16-exact or fp32 inputs.  Its bound is the fp32 one, 1e-5 relative L2,
+except where a gradient is itself ill-conditioned: the oracle's own change
+when every input is perturbed at fp32 rounding (2^-24 relative, worst of three
+draws) is measured per case and per gradient, and the bound is
+max(1e-5, 16 x that change); 16 covers the amplification of the kernel's
+internal fp32 rounding over accumulations of up to 128 terms.  (The inverse
+preconditioner makes dA0 such a gradient: beta' = beta / (A + eps) reaches
+1e5 on early tokens whose running k (.) k is still tiny.)  The full-size
+sampled checks use the fp32 bound 1e-5 (the oracle's perturbation runs would
+take minutes there).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import rel_l2
+from gated_delta_rule_77_amd import synth
+from gpu_util import TOL_F32, dev, host, report, torch_mod
+
+pytestmark = pytest.mark.gpu
+
+GRADS = ("dq", "dk", "dv", "dlog_alpha", "dbeta", "dgamma", "dS0", "dA0")
+
+
+def run_bwd(w, dO, dST, key_mode=0, A0=None, want_dS0=True, want_dA0=True, workspace=None):
+    """pdn_chunk_bwd on a synth.Workload; returns a dict of numpy gradients."""
+    import gated_delta_rule_77_amd as pdn
+    torch = torch_mod()
+    bf = w.qkv_dtype == synth.DT_BF16
+    q, k, v = dev(w.q, bf), dev(w.k, bf), dev(w.v, bf)
+    la, be, ga = dev(w.log_alpha), dev(w.beta), dev(w.gamma)
+    pre = w.precond_eps >= 0
+    z = lambda shape: torch.full(shape, float("nan"), device="cuda")
+    out = {
+        "dq": z((w.B, w.H, w.T, w.dk)), "dk": z((w.B, w.H, w.T, w.dk)),
+        "dv": z((w.B, w.H, w.T, w.dv)),
+        "dlog_alpha": None if la is None else z(tuple(la.shape)),
+        "dbeta": z(tuple(be.shape)),
+        "dgamma": None if ga is None else z(tuple(ga.shape)),
+        "dS0": z((w.B, w.H, w.dk, w.dv)) if want_dS0 else None,
+        "dA0": z((w.B, w.H, w.dk)) if (pre and want_dA0) else None,
+    }
+    pdn.pdn_chunk_bwd(q, k, v, dev(dO), out["dq"], out["dk"], out["dv"],
+                      dlog_alpha=out["dlog_alpha"], dbeta=out["dbeta"], dgamma=out["dgamma"],
+                      dS0=out["dS0"], dA0=out["dA0"], log_alpha=la, beta=be, gamma=ga,
+                      precond_eps=(w.precond_eps if pre else None),
+                      precond_A0=dev(A0) if (pre and A0 is not None) else None,
+                      S0=dev(w.S0), dST=dev(dST), key_mode=key_mode, workspace=workspace)
+    torch.cuda.synchronize()
+    return {n: (host(t) if t is not None else None) for n, t in out.items()}
+
+
+def ref_bwd(w, dO, dST, key_mode=0, A0=None):
+    return oracle.delta_rule_bwd(w.q, w.k, w.v, w.alpha_mode, w.log_alpha, w.beta_mode,
+                                 w.beta, w.gamma_mode, w.gamma, dO, dST, w.precond_eps, A0,
+                                 w.S0, key_mode=key_mode)
+
+
+def compare(name, g, ref, tol, skip=()):
+    """tol: a number, or a dict gradient name -> bound."""
+    errs = {}
+    for n in GRADS:
+        if n in skip or ref.get(n) is None or g.get(n) is None:
+            continue
+        assert np.all(np.isfinite(g[n])), (name, n)
+        errs[n] = rel_l2(g[n], ref[n])
+    report(name, **errs)
+    for n, e in errs.items():
+        bound = tol[n] if isinstance(tol, dict) else tol
+        assert e < bound, (name, n, e, bound)
+    return errs
+
+
+def conditioning_tol(w, dO, dST, key_mode=0, A0=None, draws=3):
+    """Per-gradient bound max(1e-5, 16 f), f = the oracle's own relative change
+    under 2^-24 relative perturbations of every input."""
+    rng = np.random.default_rng(12345)
+    ref = ref_bwd(w, dO, dST, key_mode=key_mode, A0=A0)
+    f = {n: 0.0 for n in GRADS}
+    pert = lambda x: None if x is None else x.astype(np.float64) * (
+        1.0 + 2.0 ** -24 * rng.standard_normal(x.shape))
+    for _ in range(draws):
+        wp = synth.Workload(w.name, w.B, w.H, w.T, w.dk, w.dv, w.qkv_dtype, pert(w.q), pert(w.k),
+                            pert(w.v), w.alpha_mode, pert(w.log_alpha), w.beta_mode, pert(w.beta),
+                            w.gamma_mode, pert(w.gamma), precond_eps=w.precond_eps, A0=w.A0,
+                            S0=pert(w.S0))
+        rp = ref_bwd(wp, pert(dO), pert(dST), key_mode=key_mode, A0=pert(A0))
+        for n in GRADS:
+            if ref[n] is not None:
+                f[n] = max(f[n], rel_l2(rp[n], ref[n]))
+    return ref, {n: max(TOL_F32, 16.0 * v) for n, v in f.items()}
+
+
+def check_bwd(name, w, key_mode=0, A0=None, seed=1, with_dST=True):
+    dO, dST = synth.upstream_grads(w, seed)
+    if not with_dST:
+        dST = None
+    g = run_bwd(w, dO, dST, key_mode=key_mode, A0=A0)
+    ref, tol = conditioning_tol(w, dO, dST, key_mode=key_mode, A0=A0)
+    return compare(name, g, ref, tol)
+
+
+def rand_workload(seed, B, H, T, dk, dv, amode, bmode, gmode, pre, bf16, s0=True):
+    """Seeded inputs of the configs' distributions in any gate mode."""
+    rng = np.random.default_rng(seed)
+    rnd = synth.round_to_bf16 if bf16 else (lambda x: x.astype(np.float32))
+    nrm = lambda x: x / np.linalg.norm(x, axis=-1, keepdims=True)
+    q = rnd(nrm(rng.standard_normal((B, H, T, dk))).astype(np.float32))
+    k = rnd(nrm(rng.standard_normal((B, H, T, dk))).astype(np.float32))
+    v = rnd(rng.standard_normal((B, H, T, dv)).astype(np.float32))
+    sig = lambda x: (1 / (1 + np.exp(-x))).astype(np.float32)
+    la = None
+    if amode == synth.ALPHA_SCALAR:
+        la = (-np.log1p(np.exp(rng.standard_normal((B, H, T))))).astype(np.float32)
+    elif amode == synth.ALPHA_VEC:
+        la = (-np.log1p(np.exp(rng.standard_normal((B, H, T, dk))))).astype(np.float32)
+    be = sig(rng.standard_normal((B, H, T) if bmode == synth.GATE_SCALAR else (B, H, T, dk)))
+    ga = None
+    if gmode == synth.GATE_SCALAR:
+        ga = sig(rng.standard_normal((B, H, T)))
+    elif gmode == synth.GATE_VEC:
+        ga = sig(rng.standard_normal((B, H, T, dv)))
+    S0 = (0.1 * rng.standard_normal((B, H, dk, dv))).astype(np.float32) if s0 else None
+    return synth.Workload("rand", B, H, T, dk, dv, synth.DT_BF16 if bf16 else synth.DT_F32,
+                          q, k, v, amode, la, bmode, be, gmode, ga,
+                          precond_eps=(1e-6 if pre else -1.0), S0=S0)
+
+
+GATE_MODES = [(a, b, g) for a in (synth.ALPHA_NONE, synth.ALPHA_SCALAR, synth.ALPHA_VEC)
+              for b in (synth.GATE_SCALAR, synth.GATE_VEC)
+              for g in (synth.GAMMA_SAME_AS_BETA, synth.GATE_SCALAR, synth.GATE_VEC)]
+
+
+@pytest.mark.parametrize("pre", [False, True])
+@pytest.mark.parametrize("key_mode", [0, 1, 2])
+@pytest.mark.parametrize("amode,bmode,gmode", GATE_MODES)
+def test_bwd_gate_matrix_fp32(amode, bmode, gmode, key_mode, pre):
+    """fp32 inputs, dk = dv = 64, T = 97 (three chunks and a one-token tail)."""
+    w = rand_workload(100 + 7 * key_mode + pre, 1, 2, 97, 64, 64, amode, bmode, gmode, pre, False)
+    check_bwd("bwd a%d b%d g%d key%d pre%d fp32 T97" % (amode, bmode, gmode, key_mode, pre), w,
+              key_mode=key_mode)
+
+
+@pytest.mark.parametrize("pre", [False, True])
+@pytest.mark.parametrize("key_mode", [0, 1, 2])
+def test_bwd_bf16_dk128(key_mode, pre):
+    """bf16 inputs, dk = dv = 128, vector gates, T = 200."""
+    w = rand_workload(200 + key_mode, 2, 2, 200, 128, 128, synth.ALPHA_VEC, synth.GATE_VEC,
+                      synth.GATE_VEC, pre, True)
+    check_bwd("bwd bf16 d128 key%d pre%d T200" % (key_mode, pre), w, key_mode=key_mode)
+
+
+def test_bwd_deltanet_fp32_config():
+    w = synth.deltanet_fp32()  # B1 H1 T256 d64 fp32, the whole configuration
+    check_bwd("bwd deltanet_fp32 B1 H1 T256 d64", w)
+
+
+def test_bwd_gdn_small():
+    check_bwd("bwd gdn B1 H3 T300 d128", synth.gdn(B=1, H=3, T=300, d=128, seed=1))
+
+
+def test_bwd_kda_fg2_small():
+    check_bwd("bwd kda_fg2 B1 H2 T257 d128", synth.kda_fg2(B=1, H=2, T=257, d=128, seed=2))
+
+
+@pytest.mark.parametrize("key_mode", [0, 1, 2])
+def test_bwd_gdn2_precond_small(key_mode):
+    w = synth.gdn2_precond(B=1, H=2, T=400, d=128, seed=3, n_pairs=8)
+    A0 = np.random.default_rng(9).uniform(0.5, 2.0, (1, 2, 128)).astype(np.float32)
+    check_bwd("bwd gdn2_precond key%d B1 H2 T400 (A0)" % key_mode, w, key_mode=key_mode, A0=A0)
+
+
+@pytest.mark.parametrize("T", [1, 31, 32, 33, 64])
+def test_bwd_short_sequences(T):
+    w = rand_workload(300 + T, 1, 2, T, 128, 64, synth.ALPHA_VEC, synth.GATE_SCALAR,
+                      synth.GATE_SCALAR, True, False)
+    check_bwd("bwd T%d" % T, w)
+
+
+def test_bwd_empty_sequence():
+    torch = torch_mod()
+    import gated_delta_rule_77_amd as pdn
+    w = rand_workload(5, 2, 2, 0, 64, 64, synth.ALPHA_SCALAR, synth.GATE_SCALAR,
+                      synth.GATE_SCALAR, True, False)
+    dO, dST = synth.upstream_grads(w, 1)
+    g = run_bwd(w, dO, dST)
+    np.testing.assert_array_equal(g["dS0"], dST.astype(np.float64))
+    np.testing.assert_array_equal(g["dA0"], np.zeros((2, 2, 64)))
+    assert torch is not None and pdn is not None
+
+
+def test_bwd_without_dST_and_S0():
+    w = rand_workload(7, 1, 2, 150, 64, 64, synth.ALPHA_VEC, synth.GATE_VEC, synth.GATE_SCALAR,
+                      False, False, s0=False)
+    check_bwd("bwd no dST no S0 T150", w, with_dST=False)
+
+
+@pytest.mark.parametrize("dv", [32, 256])
+def test_bwd_value_widths(dv):
+    w = rand_workload(8 + dv, 1, 2, 120, 128, dv, synth.ALPHA_VEC, synth.GATE_VEC,
+                      synth.GATE_VEC, True, True)
+    check_bwd("bwd dk128 dv%d T120" % dv, w)
+
+
+# ---------------------------------------------------------------------------
+# full size, launch configuration of the benchmark, sampled pairs
+# ---------------------------------------------------------------------------
+
+def sub(w, b, h):
+    s = lambda x: None if x is None else np.ascontiguousarray(x[b:b + 1, h:h + 1])
+    return synth.Workload(w.name, 1, 1, w.T, w.dk, w.dv, w.qkv_dtype, s(w.q), s(w.k), s(w.v),
+                          w.alpha_mode, s(w.log_alpha), w.beta_mode, s(w.beta), w.gamma_mode,
+                          s(w.gamma), precond_eps=w.precond_eps, A0=s(w.A0), S0=s(w.S0))
+
+
+def full_size(name, w, pairs, key_mode=0):
+    dO, dST = synth.upstream_grads(w, 1)
+    g = run_bwd(w, dO, dST, key_mode=key_mode)
+    for b, h in pairs:
+        ws = sub(w, b, h)
+        ref = ref_bwd(ws, dO[b:b + 1, h:h + 1], dST[b:b + 1, h:h + 1], key_mode=key_mode,
+                      A0=ws.A0)
+        gs = {n: (None if g[n] is None else g[n][b:b + 1, h:h + 1]) for n in GRADS}
+        compare("%s (b=%d,h=%d)" % (name, b, h), gs, ref, TOL_F32)
+    return g, dO, dST
+
+
+def test_bwd_headline_full_size():
+    w = synth.headline()  # B4 H16 T8192 d128, scalar decay and gain, bf16
+    full_size("bwd headline B4 H16 T8192", w, [(0, 0), (3, 15)])
+
+
+def test_bwd_kda_fg2_full_size():
+    w = synth.kda_fg2()  # B2 H32 T8192 d128, per-channel decay and gain
+    full_size("bwd kda_fg2 B2 H32 T8192", w, [(1, 17)])
+
+
+def test_bwd_gdn2_precond_full_size_and_euler():
+    """B1 H16 T65536 with the preconditioner: one sampled head against the
+    oracle, and Euler's identity over all heads against the GPU forward."""
+    import gated_delta_rule_77_amd as pdn
+    torch = torch_mod()
+    w = synth.gdn2_precond()
+    g, dO, dST = full_size("bwd gdn2_precond B1 H16 T65536", w, [(0, 6)])
+    q, k, v = dev(w.q, True), dev(w.k, True), dev(w.v, True)
+    o = torch.empty((w.B, w.H, w.T, w.dv), device="cuda")
+    ST = torch.empty((w.B, w.H, w.dk, w.dv), device="cuda")
+    pdn.pdn_chunk_fwd(q, k, v, o, log_alpha=dev(w.log_alpha), beta=dev(w.beta), gamma=dev(w.gamma),
+                      precond_eps=w.precond_eps, S0=dev(w.S0), ST=ST)
+    torch.cuda.synchronize()
+    L = float((host(o) * dO).sum() + (host(ST) * dST).sum())
+    S0 = np.zeros((w.B, w.H, w.dk, w.dv)) if w.S0 is None else w.S0
+    lin = float((w.v.astype(np.float64) * g["dv"]).sum() + (S0 * g["dS0"]).sum())
+    report("bwd gdn2_precond Euler identity", rel=abs(lin - L) / abs(L))
+    assert abs(lin - L) <= 1e-4 * abs(L)
+
+
+def test_bwd_deterministic():
+    w = synth.kda_fg2(B=1, H=4, T=1000, d=128, seed=11)
+    dO, dST = synth.upstream_grads(w, 2)
+    a = run_bwd(w, dO, dST)
+    b = run_bwd(w, dO, dST)
+    for n in GRADS:
+        if a[n] is not None:
+            assert np.array_equal(a[n], b[n]), n
