@@ -12,8 +12,11 @@ KDA / FG^2-GDN workload (B=2, H=32, T=8192, channel-wise decay and key gain)
 and the Gated DeltaNet-2 + preconditioner workload (B=1, H=16, T=65536,
 channel-wise decay, key and value gains; also with separate read and write keys:
 the literal erase-gate form of Gated DeltaNet-2 and the write-gate
-(apply-to-key) form of Preconditioned DeltaNet), and, on rank 0, the fp64 CPU
-oracle on a bounded sample of the prefill workload.
+(apply-to-key) form of Preconditioned DeltaNet), the backward of the prefill
+(pdn_chunk_bwd: every input gradient from seeded upstream gradients of o and
+S_T) on the throughput, KDA / FG^2-GDN and Gated DeltaNet-2 + preconditioner
+workloads, and, on rank 0, the fp64 CPU oracle on a bounded sample of the
+prefill workload.
 
 Prints one JSON line.  `value` is prefill tokens/s (tokens = batch x sequence
 positions, all heads); the roofline object describes the prefill kernel
@@ -21,6 +24,7 @@ positions, all heads); the roofline object describes the prefill kernel
 its own roofline.
 
     python bench.py [--steps K] [--warmup W] [--decode-steps N] [--no-cpu-baseline] [--no-gated]
+                    [--no-bwd]
     python bench.py --copy-probe     # plain 1 GiB copy, to calibrate PMC byte counters
 """
 from __future__ import annotations
@@ -60,6 +64,7 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-gated", action="store_true",
                     help="skip the per-channel-gate prefill workloads")
+    ap.add_argument("--no-bwd", action="store_true", help="skip the backward legs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
@@ -290,6 +295,67 @@ def bench_gated(args):
     return res
 
 
+def bench_backward(args):
+    """Backward of the prefill (pdn_chunk_bwd) on the prefill workloads, timed
+    per call with the workspace and every gradient buffer allocated before the
+    timed region.  Algorithmic bytes: q, k, v, the gates, dO, dST and S0 read
+    once; dq, dk, dv, the gate gradients, dS0 (and dA0) written once."""
+    import torch
+    import gated_delta_rule_77_amd as pdn
+    from gated_delta_rule_77_amd import synth
+
+    res = {}
+    for mk, steps in ((synth.headline, 10), (synth.kda_fg2, 5), (synth.gdn2_precond, 3)):
+        w = mk()
+        dO_h, dST_h = synth.upstream_grads(w, 1)
+        q, k, v = to_dev(w.q, True), to_dev(w.k, True), to_dev(w.v, True)
+        la, be, ga = to_dev(w.log_alpha), to_dev(w.beta), to_dev(w.gamma)
+        S0, dO, dST = to_dev(w.S0), to_dev(dO_h), to_dev(dST_h)
+        pre = w.precond_eps >= 0
+        e = lambda shape: torch.empty(shape, device="cuda", dtype=torch.float32)
+        like = lambda t: None if t is None else torch.empty_like(t)
+        kw = dict(dlog_alpha=like(la), dbeta=like(be), dgamma=like(ga),
+                  dS0=e((w.B, w.H, w.dk, w.dv)), dA0=e((w.B, w.H, w.dk)) if pre else None,
+                  log_alpha=la, beta=be, gamma=ga, precond_eps=(w.precond_eps if pre else None),
+                  S0=S0, dST=dST)
+        dq, dk, dv = e((w.B, w.H, w.T, w.dk)), e((w.B, w.H, w.T, w.dk)), e((w.B, w.H, w.T, w.dv))
+        ws = torch.empty(pdn.pdn_chunk_bwd_workspace_size(q, k, v, dO, dq, dk, dv, **kw),
+                         dtype=torch.uint8, device="cuda")
+        # untimed: about 20 ms of work first (at least 1 ms per 512K token-heads)
+        est_ms = 1.0 * w.B * w.H * w.T / 524288
+        for _ in range(max(2, int(20.0 / est_ms))):
+            pdn.pdn_chunk_bwd(q, k, v, dO, dq, dk, dv, workspace=ws, **kw)
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for i in range(steps):
+            ev[i][0].record(stream)
+            pdn.pdn_chunk_bwd(q, k, v, dO, dq, dk, dv, workspace=ws, **kw)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+        BH, T, dk_, dv_ = w.B * w.H, w.T, w.dk, w.dv
+        gate = lambda x: 0 if x is None else x.size * 4
+        gates = gate(w.log_alpha) + gate(w.beta) + gate(w.gamma)
+        state = BH * dk_ * dv_ * 4
+        alg = (BH * T * (2 * dk_ + dv_) * 2 + gates + BH * T * dv_ * 4      # q, k, v, gates, dO
+               + state * (2 if w.S0 is not None else 1)                       # dST, S0
+               + BH * T * (2 * dk_ + dv_) * 4 + gates + state                 # dq, dk, dv, dgates, dS0
+               + (BH * dk_ * 4 if pre else 0))                               # dA0
+        gbs = alg / (ms / 1e3) / 1e9
+        res["%s_bwd_B%d_H%d_T%d_d%d" % (w.name, w.B, w.H, T, dk_)] = {
+            "B": w.B, "H": w.H, "T": T, "dk": dk_, "dv": dv_, "steps": steps,
+            "call_ms": ms, "tokens_per_s": w.B * T / (ms / 1e3),
+            "alg_bytes_per_call": alg, "workspace_bytes": ws.numel(),
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS},
+        }
+        del ws, q, k, v, la, be, ga, S0, dO, dST, dq, dk, dv, kw, w
+        torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(w, target_s: float):
     """The fp64 oracle on a bounded sample of the prefill workload."""
     import numpy as np
@@ -348,6 +414,7 @@ def main():
     pf = bench_prefill(args)
     dec = None if args.no_decode else bench_decode(args)
     gated = None if args.no_gated else bench_gated(args)
+    bwd = None if args.no_bwd else bench_backward(args)
     cpu = None
     if not args.no_cpu_baseline and int(os.environ.get("RANK", "0")) == 0:
         cpu = cpu_baseline(pf["sample"], args.cpu_seconds)
@@ -385,6 +452,7 @@ def main():
                  / (BF16_PEAK_TFLOPS * 1e12)},
         "decode": dec,
         "per_channel_gates": gated,
+        "backward": bwd,
         "cpu_baseline": cpu,
         "kernel_source_hash": kernel_source_hash(),
     }

@@ -107,32 +107,52 @@ __host__ __device__ constexpr long dgr_floats() { return 3L * BC * DK + 2L * BC 
 // per-token gates (shared by the prep and the gradient kernels)
 // ---------------------------------------------------------------------------
 
+// Per-token gate values.  Every load is unconditional (the token index is
+// clamped to T - 1 and the mode picks a base pointer and stride), and the
+// result is selected afterwards, so that a column's loads issue back to back.
+__device__ __forceinline__ long tclamp(const BwdParams& p, long t) { return t < p.T ? t : p.T - 1; }
+
+// raw log decay of token t, channel i (without decay: some valid element)
+template <int DK>
+__device__ __forceinline__ float tok_la_raw(const BwdParams& p, long bh, long t, int i) {
+    const long tc = tclamp(p, t);
+    const bool vec = p.amode == PDN_ALPHA_VEC;
+    const float* base = p.amode == PDN_ALPHA_NONE ? p.beta : p.la;
+    return base[vec ? (bh * p.T + tc) * DK + i : bh * p.T + tc];
+}
 // clamped natural-log decay of token t (0 beyond T or without decay)
 template <int DK>
 __device__ __forceinline__ float tok_la(const BwdParams& p, long bh, long t, int i) {
-    if (t >= p.T || p.amode == PDN_ALPHA_NONE) return 0.f;
-    const float x = p.amode == PDN_ALPHA_SCALAR ? p.la[bh * p.T + t] : p.la[(bh * p.T + t) * DK + i];
-    return fmaxf(x, kLogAlphaMin);
+    const float x = tok_la_raw<DK>(p, bh, t, i);
+    return (t < p.T && p.amode != PDN_ALPHA_NONE) ? fmaxf(x, kLogAlphaMin) : 0.f;
 }
-template <int DK>
-__device__ __forceinline__ bool tok_la_clamped(const BwdParams& p, long bh, long t, int i) {
-    if (t >= p.T || p.amode == PDN_ALPHA_NONE) return true;
-    const float x = p.amode == PDN_ALPHA_SCALAR ? p.la[bh * p.T + t] : p.la[(bh * p.T + t) * DK + i];
-    return x < kLogAlphaMin;
+// whether d log alpha is zero there (no decay, beyond T, or clamped)
+__device__ __forceinline__ bool la_dead(const BwdParams& p, long t, float raw) {
+    return !(t < p.T && p.amode != PDN_ALPHA_NONE) || raw < kLogAlphaMin;
 }
 // raw erase gain (1 beyond T, so that padded rows carry finite zero gradients)
 template <int DK>
 __device__ __forceinline__ float tok_beta(const BwdParams& p, long bh, long t, int i) {
-    if (t >= p.T) return 1.f;
-    return p.bmode == PDN_GATE_SCALAR ? p.beta[bh * p.T + t] : p.beta[(bh * p.T + t) * DK + i];
+    const long tc = tclamp(p, t);
+    const float x = p.beta[p.bmode == PDN_GATE_VEC ? (bh * p.T + tc) * DK + i : bh * p.T + tc];
+    return t < p.T ? x : 1.f;
 }
 // raw value gain of column j (raw beta when gamma is "same as beta")
 template <int DK>
 __device__ __forceinline__ float tok_gamma(const BwdParams& p, long bh, long t, int j) {
-    if (t >= p.T) return 1.f;
-    if (p.gmode == PDN_GAMMA_SAME_AS_BETA)
-        return p.bmode == PDN_GATE_SCALAR ? p.beta[bh * p.T + t] : p.beta[(bh * p.T + t) * DK + j];
-    return p.gmode == PDN_GATE_SCALAR ? p.gamma[bh * p.T + t] : p.gamma[(bh * p.T + t) * p.dv + j];
+    const long tc = tclamp(p, t);
+    const bool same = p.gmode == PDN_GAMMA_SAME_AS_BETA;
+    const bool vec = same ? p.bmode == PDN_GATE_VEC : p.gmode == PDN_GATE_VEC;
+    const float* base = same ? p.beta : p.gamma;
+    const long idx = vec ? (bh * p.T + tc) * (same ? DK : p.dv) + j : bh * p.T + tc;
+    const float x = base[idx];
+    return t < p.T ? x : 1.f;
+}
+// q / k / v element (0 beyond T)
+template <bool BF16>
+__device__ __forceinline__ float tok_in(const BwdParams& p, const void* x, long bh, long t, int w, int i) {
+    const float v = load_in<BF16>(x, (bh * p.T + tclamp(p, t)) * w + i);
+    return t < p.T ? v : 0.f;
 }
 
 // write key, read key of one channel from k and the erase gain b
@@ -174,14 +194,12 @@ __global__ void __launch_bounds__(DK) bwd_ksum_kernel(BwdParams p) {
     const long bh = blockIdx.x / p.nc;
     const long c = blockIdx.x % p.nc;
     const int i = threadIdx.x;
+    float kk[BC];
+#pragma unroll
+    for (int r = 0; r < BC; ++r) kk[r] = tok_in<BF16>(p, p.k, bh, c * BC + r, DK, i);
     float s = 0.f;
-    for (int r = 0; r < BC; ++r) {
-        const long t = c * BC + r;
-        if (t < p.T) {
-            const float kk = ld<BF16>(p.k, (bh * p.T + t) * DK + i);
-            s += kk * kk;
-        }
-    }
+#pragma unroll
+    for (int r = 0; r < BC; ++r) s += kk[r] * kk[r];
     p.ksum[(bh * p.nc + c) * DK + i] = s;
 }
 
@@ -190,7 +208,18 @@ __global__ void __launch_bounds__(DK) bwd_kscan_kernel(BwdParams p) {
     const long bh = blockIdx.x;
     const int i = threadIdx.x;
     float run = p.A0 ? p.A0[bh * DK + i] : 0.f;
-    for (long c = 0; c < p.nc; ++c) {
+    long c = 0;
+    for (; c + 8 <= p.nc; c += 8) {
+        float x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = p.ksum[(bh * p.nc + c + u) * DK + i];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            p.apre[(bh * p.nc + c + u) * DK + i] = run;
+            run += x[u];
+        }
+    }
+    for (; c < p.nc; ++c) {
         p.apre[(bh * p.nc + c) * DK + i] = run;
         run += p.ksum[(bh * p.nc + c) * DK + i];
     }
@@ -199,100 +228,187 @@ __global__ void __launch_bounds__(DK) bwd_kscan_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------
 // per-chunk record
 // ---------------------------------------------------------------------------
+// T and P as fp32 MFMA products over the key channels: with the decay split
+// at the middle row m_b of each 16-token block (L_r = e^(G_r - G_mb),
+// R_s = e^(G_mb - G_s), L_r R_s = e^(G_r - G_s) inside a block, both factors
+// within e^(+-80) by the clamp on log alpha), T_rs = sum_i (kr L)_ri (kw R)_si
+// and P_rs = sum_i (q L)_ri (kw R)_si on the two diagonal 16 x 16 blocks; the
+// block below the diagonal uses (kw R c)_s with c = e^(G_24 - G_8), since
+// e^(G_r - G_s) = L_r c R_s there.
 template <int DK, bool BF16>
-__global__ void __launch_bounds__(NT) bwd_prep_kernel(BwdParams p) {
-    __shared__ float sKr[BC][DK + 1];
-    __shared__ float sKw[BC][DK + 1];
-    __shared__ float sQ[BC][DK + 1];
-    __shared__ float sG[BC][DK + 1];  // log2 units
+__global__ void __launch_bounds__(NT, 2) bwd_prep_kernel(BwdParams p) {
+    constexpr int LS = DK + 4;  // read as [row][k]
+    __shared__ float sKrL[BC][LS];
+    __shared__ float sQL[BC][LS];
+    __shared__ float sKwR[BC][LS];
+    __shared__ float sKwRc[16][LS];
     __shared__ float sT[BC][BC + 1];
-    __shared__ float sM[BC][BC + 1];
     const long bh = blockIdx.x / p.nc;
     const long c = blockIdx.x % p.nc;
     const long t0 = c * BC;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int ln = lane & 15, g4 = lane >> 4;
     float* R = p.rec + (bh * p.nc + c) * rec_floats<DK>(p.dv);
     if (tid < DK) {
         const int i = tid;
-        float G = 0.f;
-        float A = p.pre ? p.apre[(bh * p.nc + c) * DK + i] : 0.f;
+        // every load of the column first, then the scans
+        float kk[BC], qq[BC], la[BC], bb[BC];
+#pragma unroll
         for (int r = 0; r < BC; ++r) {
             const long t = t0 + r;
-            const float kk = t < p.T ? ld<BF16>(p.k, (bh * p.T + t) * DK + i) : 0.f;
-            const float qq = t < p.T ? ld<BF16>(p.q, (bh * p.T + t) * DK + i) : 0.f;
-            G += tok_la<DK>(p, bh, t, i);
-            float b = tok_beta<DK>(p, bh, t, i);
+            kk[r] = tok_in<BF16>(p, p.k, bh, t, DK, i);
+            qq[r] = tok_in<BF16>(p, p.q, bh, t, DK, i);
+            la[r] = tok_la<DK>(p, bh, t, i);
+            bb[r] = tok_beta<DK>(p, bh, t, i);
+        }
+        float G = 0.f;
+        float A = p.pre ? p.apre[(bh * p.nc + c) * DK + i] : 0.f;
+        float kr[BC], kw[BC], g[BC];
+#pragma unroll
+        for (int r = 0; r < BC; ++r) {
+            G += la[r];
+            g[r] = G;
+            float b = bb[r];
             if (p.pre) {
-                A += kk * kk;
+                A += kk[r] * kk[r];
                 b = b / (A + p.eps);
             }
-            float kw, kr;
-            keys_of(p.kmode, b, kk, kw, kr);
-            sKr[r][i] = kr;
-            sKw[r][i] = kw;
-            sQ[r][i] = qq;
-            sG[r][i] = G * kLog2e;
+            keys_of(p.kmode, b, kk[r], kw[r], kr[r]);
         }
-        const float gc = G * kLog2e;
+        const float gc = g[BC - 1];
+        const float cst = __expf(g[24] - g[8]);
+#pragma unroll
         for (int r = 0; r < BC; ++r) {
-            const float e = exp2f(sG[r][i]);
-            R[r * DK + i] = sKr[r][i] * e;
-            R[BC * DK + r * DK + i] = sQ[r][i] * e;
-            R[2 * BC * DK + r * DK + i] = sKw[r][i] * exp2f(gc - sG[r][i]);
+            const float e = __expf(g[r]);
+            R[r * DK + i] = kr[r] * e;
+            R[BC * DK + r * DK + i] = qq[r] * e;
+            R[2 * BC * DK + r * DK + i] = kw[r] * __expf(gc - g[r]);
+            const float gm = r < 16 ? g[8] : g[24];
+            const float L = __expf(g[r] - gm), Rs = __expf(gm - g[r]);
+            sKrL[r][i] = kr[r] * L;
+            sQL[r][i] = qq[r] * L;
+            sKwR[r][i] = kw[r] * Rs;
+            if (r < 16) sKwRc[r][i] = kw[r] * Rs * cst;
         }
-        R[rec_gc<DK>(p.dv) + i] = exp2f(gc);
+        R[rec_gc<DK>(p.dv) + i] = __expf(gc);
     }
     float* Rvw = R + rec_vw<DK>(p.dv);
-    for (int idx = tid; idx < BC * p.dv; idx += NT) {
-        const int r = idx / p.dv, j = idx % p.dv;
-        const long t = t0 + r;
-        const float vv = t < p.T ? ld<BF16>(p.v, (bh * p.T + t) * p.dv + j) : 0.f;
-        Rvw[idx] = vv * value_scale(p.kmode, p.gmode, tok_gamma<DK>(p, bh, t, j));
-    }
-    __syncthreads();
-    float* Rp = R + rec_p<DK>(p.dv);
-    for (int idx = tid; idx < BC * BC; idx += NT) {
-        const int r = idx / BC, s = idx % BC;
-        float tv = 0.f, pv = 0.f;
-        if (s <= r) {
-            for (int i = 0; i < DK; ++i) {
-                const float w = sKw[s][i] * exp2f(sG[r][i] - sG[s][i]);
-                tv += sKr[r][i] * w;
-                pv += sQ[r][i] * w;
+    {
+        // at most BC * 256 / NT = 32 values per thread, loads issued together
+        constexpr int MAXV = BC * 256 / NT;
+        float vv[MAXV], sc[MAXV];
+#pragma unroll
+        for (int m = 0; m < MAXV; ++m) {
+            const int idx = tid + m * NT;
+            vv[m] = 0.f;
+            sc[m] = 0.f;
+            if (idx < BC * p.dv) {
+                const int r = idx / p.dv, j = idx % p.dv;
+                const long t = t0 + r;
+                vv[m] = tok_in<BF16>(p, p.v, bh, t, p.dv, j);
+                sc[m] = value_scale(p.kmode, p.gmode, tok_gamma<DK>(p, bh, t, j));
             }
         }
-        sT[r][s] = s < r ? tv : 0.f;
-        Rp[idx] = pv;  // zero above the diagonal
+#pragma unroll
+        for (int m = 0; m < MAXV; ++m) {
+            const int idx = tid + m * NT;
+            if (idx < BC * p.dv) Rvw[idx] = vv[m] * sc[m];
+        }
+    }
+    __syncthreads();
+    // six 16 x 16 tiles: T (0,0), (1,1), (1,0) and P likewise; wave w takes
+    // tile w and, for w < 2, tile w + 4
+    float* Rp = R + rec_p<DK>(p.dv);
+    for (int tile = w; tile < 6; tile += 4) {
+        const bool isP = tile >= 3;
+        const int which = tile % 3;  // 0: (0,0), 1: (1,1), 2: (1,0)
+        const int rb = which == 0 ? 0 : 1, sb = which == 1 ? 1 : 0;
+        const float(*Aop)[LS] = isP ? sQL : sKrL;
+        const float(*Bop)[LS] = which == 2 ? sKwRc : sKwR;
+        const int brow = which == 2 ? 0 : 16 * sb;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+        for (int k = 0; k < DK; k += 4)
+            acc = mfma4(Aop[16 * rb + ln][k + g4], Bop[brow + ln][k + g4], acc);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 16 * rb + 4 * g4 + e, s2 = 16 * sb + ln;
+            if (isP) {
+                Rp[r * BC + s2] = s2 <= r ? acc[e] : 0.f;
+            } else {
+                sT[r][s2] = s2 < r ? acc[e] : 0.f;
+            }
+        }
+    }
+    // the upper-right blocks: zero in both
+    for (int idx = tid; idx < 16 * 16; idx += NT) {
+        const int r = idx / 16, s2 = 16 + idx % 16;
+        sT[r][s2] = 0.f;
+        Rp[r * BC + s2] = 0.f;
     }
     __syncthreads();
     // M = (I + T)^-1, one column per thread: x_r = [r == j] - sum_{s<r} T_rs x_s
+    float* Rm = R + rec_m<DK>(p.dv);
     if (tid < BC) {
+        // column j in registers; T rows are broadcast reads (x_s = 0 for s < j)
         const int j = tid;
+        float x[BC];
+#pragma unroll
         for (int r = 0; r < BC; ++r) {
             float acc = r == j ? 1.f : 0.f;
-            for (int s = j; s < r; ++s) acc -= sT[r][s] * sM[s][j];
-            sM[r][j] = r < j ? 0.f : acc;
+#pragma unroll
+            for (int s2 = 0; s2 < r; ++s2) acc -= sT[r][s2] * x[s2];
+            x[r] = r < j ? 0.f : acc;
+            Rm[r * BC + j] = x[r];
         }
     }
-    __syncthreads();
-    float* Rm = R + rec_m<DK>(p.dv);
-    for (int idx = tid; idx < BC * BC; idx += NT) Rm[idx] = sM[idx / BC][idx % BC];
 }
 
 // ---------------------------------------------------------------------------
 // state passes: one workgroup per (b, h, 32 value columns); state tile
 // DK x 32 in MFMA accumulators, (DK / 16) x 2 tiles of 16 x 16 over 4 waves.
 // ---------------------------------------------------------------------------
+// staged copy of [rows][W] floats (W % 4 == 0, rows * W / 4 == n4) from
+// global to registers and from registers to an LDS array with row stride LS
+template <int W, int N4>
+struct Tile4 {
+    static constexpr int PER = (N4 + NT - 1) / NT;
+    f32x4 v[PER];
+    __device__ __forceinline__ void load(const float* g, long gstride) {
+        const int tid = threadIdx.x;
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int idx = tid + u * NT;
+            if (N4 % NT == 0 || idx < N4) {
+                const int r = idx / (W / 4), c4 = idx % (W / 4);
+                v[u] = *reinterpret_cast<const f32x4*>(g + r * gstride + 4 * c4);
+            }
+        }
+    }
+    template <int LS>
+    __device__ __forceinline__ void store(float* l) const {
+        const int tid = threadIdx.x;
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int idx = tid + u * NT;
+            if (N4 % NT == 0 || idx < N4) {
+                const int r = idx / (W / 4), c4 = idx % (W / 4);
+                *reinterpret_cast<f32x4*>(l + r * LS + 4 * c4) = v[u];
+            }
+        }
+    }
+};
+
 template <int DK>
 __global__ void __launch_bounds__(NT) bwd_state_fwd_kernel(BwdParams p) {
     constexpr int NSB = DK / 16 * 2 / 4;  // state tiles per wave
-    __shared__ float sKg[BC][DK + 4];     // read as [row][k]: stride 4 mod 64 banks
-    __shared__ float sKd[BC][DK + 16];    // read as [k][col]: stride 16 mod 64
-    __shared__ float sM[BC][BC + 4];
-    __shared__ float sX[BC][JT + 16];
-    __shared__ float sU[BC][JT + 16];
-    __shared__ float sS[DK][JT + 16];
-    __shared__ float sGc[DK];
+    __shared__ __attribute__((aligned(16))) float sKg[BC][DK + 4];   // read as [row][k]: stride 4 mod 64 banks
+    __shared__ __attribute__((aligned(16))) float sKd[BC][DK + 16];  // read as [k][col]: stride 16 mod 64
+    __shared__ __attribute__((aligned(16))) float sM[BC][BC + 4];
+    __shared__ __attribute__((aligned(16))) float sX[BC][JT + 16];
+    __shared__ __attribute__((aligned(16))) float sU[BC][JT + 16];
+    __shared__ __attribute__((aligned(16))) float sS[DK][JT + 16];
+    __shared__ __attribute__((aligned(16))) float sGc[DK];
     const int ntile = p.dv / JT;
     const long bh = blockIdx.x / ntile;
     const int j0 = (blockIdx.x % ntile) * JT;
@@ -300,6 +416,7 @@ __global__ void __launch_bounds__(NT) bwd_state_fwd_kernel(BwdParams p) {
     const int ln = lane & 15, g4 = lane >> 4;
     const long Tp = static_cast<long>(p.nc) * BC;
     const long SZ = static_cast<long>(DK) * p.dv;
+    const long RF = rec_floats<DK>(p.dv);
     f32x4 sacc[NSB];
 #pragma unroll
     for (int m = 0; m < NSB; ++m) {
@@ -314,23 +431,34 @@ __global__ void __launch_bounds__(NT) bwd_state_fwd_kernel(BwdParams p) {
         }
     }
     const int rb = w >> 1, xcb = w & 1;
-    for (long c = 0; c < p.nc; ++c) {
-        const float* R = p.rec + (bh * p.nc + c) * rec_floats<DK>(p.dv);
-        __syncthreads();
-        for (int idx = tid; idx < BC * DK; idx += NT) {
-            const int r = idx / DK, i = idx % DK;
-            sKg[r][i] = R[idx];
-            sKd[r][i] = R[2 * BC * DK + idx];
-        }
-        const float* Rm = R + rec_m<DK>(p.dv);
-        for (int idx = tid; idx < BC * BC; idx += NT) sM[idx / BC][idx % BC] = Rm[idx];
-        for (int i = tid; i < DK; i += NT) sGc[i] = R[rec_gc<DK>(p.dv) + i];
-        __syncthreads();
-        // X = Vw - Kg S: tile (rb, xcb)
+    // the next chunk's operands, loaded while the current one is processed
+    Tile4<DK, BC * DK / 4> nKg, nKd;
+    Tile4<BC, BC * BC / 4> nM;
+    Tile4<DK, DK / 4> nGc;
+    float nVw[4];
+    auto fetch = [&](long c) {
+        const float* R = p.rec + (bh * p.nc + c) * RF;
+        nKg.load(R, DK);
+        nKd.load(R + 2 * BC * DK, DK);
+        nM.load(R + rec_m<DK>(p.dv), BC);
+        nGc.load(R + rec_gc<DK>(p.dv), DK);
         const float* Rvw = R + rec_vw<DK>(p.dv);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) nVw[e] = Rvw[(16 * rb + 4 * g4 + e) * p.dv + j0 + 16 * xcb + ln];
+    };
+    fetch(0);
+    for (long c = 0; c < p.nc; ++c) {
+        __syncthreads();  // the previous chunk's LDS reads are done
+        nKg.template store<DK + 4>(&sKg[0][0]);
+        nKd.template store<DK + 16>(&sKd[0][0]);
+        nM.template store<BC + 4>(&sM[0][0]);
+        nGc.template store<DK>(&sGc[0]);
         f32x4 x;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = Rvw[(16 * rb + 4 * g4 + e) * p.dv + j0 + 16 * xcb + ln];
+        for (int e = 0; e < 4; ++e) x[e] = nVw[e];
+        __syncthreads();
+        if (c + 1 < p.nc) fetch(c + 1);
+        // X = Vw - Kg S: tile (rb, xcb)
 #pragma unroll 8
         for (int k = 0; k < DK; k += 4) x = mfma4(-sKg[16 * rb + ln][k + g4], sS[k + g4][16 * xcb + ln], x);
 #pragma unroll
@@ -369,16 +497,16 @@ __global__ void __launch_bounds__(NT) bwd_state_fwd_kernel(BwdParams p) {
 template <int DK>
 __global__ void __launch_bounds__(NT) bwd_state_bwd_kernel(BwdParams p) {
     constexpr int NSB = DK / 16 * 2 / 4;
-    __shared__ float sQg[BC][DK + 16];  // read as [k][col]
-    __shared__ float sKg[BC][DK + 16];
-    __shared__ float sKd[BC][DK + 4];   // read as [row][k]
-    __shared__ float sM[BC][BC + 16];   // read transposed: [k][col]
-    __shared__ float sP[BC][BC + 16];
-    __shared__ float sdO[BC][JT + 16];
-    __shared__ float sY[BC][JT + 16];
-    __shared__ float sZ[BC][JT + 16];
-    __shared__ float sdS[DK][JT + 16];
-    __shared__ float sGc[DK];
+    __shared__ __attribute__((aligned(16))) float sQg[BC][DK + 16];  // read as [k][col]
+    __shared__ __attribute__((aligned(16))) float sKg[BC][DK + 16];
+    __shared__ __attribute__((aligned(16))) float sKd[BC][DK + 4];   // read as [row][k]
+    __shared__ __attribute__((aligned(16))) float sM[BC][BC + 16];   // read transposed: [k][col]
+    __shared__ __attribute__((aligned(16))) float sP[BC][BC + 16];
+    __shared__ __attribute__((aligned(16))) float sdO[BC][JT + 16];
+    __shared__ __attribute__((aligned(16))) float sY[BC][JT + 16];
+    __shared__ __attribute__((aligned(16))) float sZ[BC][JT + 16];
+    __shared__ __attribute__((aligned(16))) float sdS[DK][JT + 16];
+    __shared__ __attribute__((aligned(16))) float sGc[DK];
     const int ntile = p.dv / JT;
     const long bh = blockIdx.x / ntile;
     const int j0 = (blockIdx.x % ntile) * JT;
@@ -386,6 +514,7 @@ __global__ void __launch_bounds__(NT) bwd_state_bwd_kernel(BwdParams p) {
     const int ln = lane & 15, g4 = lane >> 4;
     const long Tp = static_cast<long>(p.nc) * BC;
     const long SZ = static_cast<long>(DK) * p.dv;
+    const long RF = rec_floats<DK>(p.dv);
     f32x4 dacc[NSB];
 #pragma unroll
     for (int m = 0; m < NSB; ++m) {
@@ -399,6 +528,24 @@ __global__ void __launch_bounds__(NT) bwd_state_bwd_kernel(BwdParams p) {
         }
     }
     const int rb = w >> 1, xcb = w & 1;
+    Tile4<DK, BC * DK / 4> nKg, nQg, nKd;
+    Tile4<BC, BC * BC / 4> nM, nP;
+    Tile4<DK, DK / 4> nGc;
+    f32x4 ndO;  // one 4-column group of the dO tile per thread
+    const int dr = tid / (JT / 4), dc4 = tid % (JT / 4);
+    auto fetch = [&](long c) {
+        const float* R = p.rec + (bh * p.nc + c) * RF;
+        nKg.load(R, DK);
+        nQg.load(R + BC * DK, DK);
+        nKd.load(R + 2 * BC * DK, DK);
+        nM.load(R + rec_m<DK>(p.dv), BC);
+        nP.load(R + rec_p<DK>(p.dv), BC);
+        nGc.load(R + rec_gc<DK>(p.dv), DK);
+        const long t = c * BC + dr;
+        ndO = *reinterpret_cast<const f32x4*>(p.dO + (bh * p.T + tclamp(p, t)) * p.dv + j0 + 4 * dc4);
+        if (t >= p.T) ndO = f32x4{0.f, 0.f, 0.f, 0.f};
+    };
+    fetch(p.nc - 1);
     for (long c = p.nc - 1; c >= 0; --c) {
         // gradient with respect to the state after chunk c
 #pragma unroll
@@ -408,27 +555,16 @@ __global__ void __launch_bounds__(NT) bwd_state_bwd_kernel(BwdParams p) {
             for (int e = 0; e < 4; ++e)
                 p.dst[(bh * p.nc + c) * SZ + (16 * ib + 4 * g4 + e) * p.dv + j0 + 16 * cb + ln] = dacc[m][e];
         }
-        const float* R = p.rec + (bh * p.nc + c) * rec_floats<DK>(p.dv);
         __syncthreads();
-        for (int idx = tid; idx < BC * DK; idx += NT) {
-            const int r = idx / DK, i = idx % DK;
-            sKg[r][i] = R[idx];
-            sQg[r][i] = R[BC * DK + idx];
-            sKd[r][i] = R[2 * BC * DK + idx];
-        }
-        const float* Rm = R + rec_m<DK>(p.dv);
-        const float* Rp = R + rec_p<DK>(p.dv);
-        for (int idx = tid; idx < BC * BC; idx += NT) {
-            sM[idx / BC][idx % BC] = Rm[idx];
-            sP[idx / BC][idx % BC] = Rp[idx];
-        }
-        for (int i = tid; i < DK; i += NT) sGc[i] = R[rec_gc<DK>(p.dv) + i];
-        for (int idx = tid; idx < BC * JT; idx += NT) {
-            const int r = idx / JT, j = idx % JT;
-            const long t = c * BC + r;
-            sdO[r][j] = t < p.T ? p.dO[(bh * p.T + t) * p.dv + j0 + j] : 0.f;
-        }
+        nKg.template store<DK + 16>(&sKg[0][0]);
+        nQg.template store<DK + 16>(&sQg[0][0]);
+        nKd.template store<DK + 4>(&sKd[0][0]);
+        nM.template store<BC + 16>(&sM[0][0]);
+        nP.template store<BC + 16>(&sP[0][0]);
+        nGc.template store<DK>(&sGc[0]);
+        *reinterpret_cast<f32x4*>(&sdO[dr][4 * dc4]) = ndO;
         __syncthreads();
+        if (c > 0) fetch(c - 1);
         // Y = P^T dO + Kd dS'
         f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -481,11 +617,11 @@ __global__ void __launch_bounds__(NT) bwd_state_bwd_kernel(BwdParams p) {
 template <int DK>
 __global__ void __launch_bounds__(NT) bwd_dgrad_kernel(BwdParams p) {
     constexpr int IBW = DK / 16 / 4;  // 16-channel blocks per wave
-    __shared__ float sS[DK][JT + 4];  // all read as [row][k]
-    __shared__ float sE[DK][JT + 4];
-    __shared__ float sdO[BC][JT + 4];
-    __shared__ float sZ[BC][JT + 4];
-    __shared__ float sU[BC][JT + 4];
+    __shared__ __attribute__((aligned(16))) float sS[DK][JT + 4];  // all read as [row][k]
+    __shared__ __attribute__((aligned(16))) float sE[DK][JT + 4];
+    __shared__ __attribute__((aligned(16))) float sdO[BC][JT + 4];
+    __shared__ __attribute__((aligned(16))) float sZ[BC][JT + 4];
+    __shared__ __attribute__((aligned(16))) float sU[BC][JT + 4];
     const long bh = blockIdx.x / p.nc;
     const long c = blockIdx.x % p.nc;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -494,6 +630,8 @@ __global__ void __launch_bounds__(NT) bwd_dgrad_kernel(BwdParams p) {
     const long SZ = static_cast<long>(DK) * p.dv;
     const float* S = p.st + (bh * (p.nc + 1) + c) * SZ;
     const float* E = p.dst + (bh * p.nc + c) * SZ;
+    const float* Zc = p.Z + (bh * Tp + c * BC) * p.dv;
+    const float* Uc = p.U + (bh * Tp + c * BC) * p.dv;
     f32x4 aQ[2][IBW], aK[2][IBW], aD[2][IBW], aP, aT;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
@@ -507,21 +645,30 @@ __global__ void __launch_bounds__(NT) bwd_dgrad_kernel(BwdParams p) {
     aT = f32x4{0.f, 0.f, 0.f, 0.f};
     const int prb = w >> 1, pcb = w & 1;
     float gacc = 0.f;
+    // the next 32 value columns, loaded while the current ones are used
+    Tile4<JT, DK * JT / 4> nS, nE;
+    Tile4<JT, BC * JT / 4> nZ, nU;
+    f32x4 ndO;
+    const int dr = tid / (JT / 4), dc4 = tid % (JT / 4);
+    auto fetch = [&](int jc) {
+        nS.load(S + jc, p.dv);
+        nE.load(E + jc, p.dv);
+        nZ.load(Zc + jc, p.dv);
+        nU.load(Uc + jc, p.dv);
+        const long t = c * BC + dr;
+        ndO = *reinterpret_cast<const f32x4*>(p.dO + (bh * p.T + tclamp(p, t)) * p.dv + jc + 4 * dc4);
+        if (t >= p.T) ndO = f32x4{0.f, 0.f, 0.f, 0.f};
+    };
+    fetch(0);
     for (int jc = 0; jc < p.dv; jc += JT) {
         __syncthreads();
-        for (int idx = tid; idx < DK * JT; idx += NT) {
-            const int i = idx / JT, j = idx % JT;
-            sS[i][j] = S[i * p.dv + jc + j];
-            sE[i][j] = E[i * p.dv + jc + j];
-        }
-        for (int idx = tid; idx < BC * JT; idx += NT) {
-            const int r = idx / JT, j = idx % JT;
-            const long t = c * BC + r;
-            sdO[r][j] = t < p.T ? p.dO[(bh * p.T + t) * p.dv + jc + j] : 0.f;
-            sZ[r][j] = p.Z[(bh * Tp + c * BC + r) * p.dv + jc + j];
-            sU[r][j] = p.U[(bh * Tp + c * BC + r) * p.dv + jc + j];
-        }
+        nS.template store<JT + 4>(&sS[0][0]);
+        nE.template store<JT + 4>(&sE[0][0]);
+        nZ.template store<JT + 4>(&sZ[0][0]);
+        nU.template store<JT + 4>(&sU[0][0]);
+        *reinterpret_cast<f32x4*>(&sdO[dr][4 * dc4]) = ndO;
         __syncthreads();
+        if (jc + JT < p.dv) fetch(jc + JT);
         if (tid < DK)
 #pragma unroll 8
             for (int j = 0; j < JT; ++j) gacc += sS[tid][j] * sE[tid][j];
@@ -575,152 +722,266 @@ __global__ void __launch_bounds__(NT) bwd_dgrad_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------------------
 // from the operand gradients to q, k, v and the gates
+//
+// The pairwise sums (per key channel i, e_rs = e^(G_ri - G_si) <= 1 for s <= r)
+//   A1_r = sum_{s<r} dT_rs kw_s e_rs     A3_r = sum_{s<=r} dP_rs kw_s e_rs
+//   A2_s = sum_{r>s} dT_rs kr_r e_rs     A4_s = sum_{r>=s} dP_rs q_r e_rs
+// are fp32 MFMA products once e_rs is split at a reference row: inside a
+// 16-token block b at its middle row m_b (8 or 24), e_rs = L_r R_s with
+// L_r = e^(G_r - G_mb), R_s = e^(G_mb - G_s), both within e^(+-80) by the
+// clamp on log alpha; across the blocks (r >= 16 > s) at row 15, where both
+// factors are <= 1 and differ from the in-block ones by the per-channel
+// constant e^(G_24 - G_8) <= 1.  So with W = kw (.) R, Rk = kr (.) L, Rq = q (.) L:
+//   A1 = L (.) [dT W]_in-block + L (.) c (.) [dT_(1,0) W_0]
+//   A2 = R (.) [dT^T Rk]_in-block + R (.) c (.) [dT_(1,0)^T Rk_1]   (c = e^(G_24 - G_8))
+// and likewise A3, A4 with dP.
 // ---------------------------------------------------------------------------
 template <int DK, bool BF16>
-__global__ void __launch_bounds__(NT) bwd_gates_kernel(BwdParams p) {
-    __shared__ float sKr[BC][DK + 1];
-    __shared__ float sKw[BC][DK + 1];
-    __shared__ float sQ[BC][DK + 1];
-    __shared__ float sG[BC][DK + 1];  // natural log
+__global__ void __launch_bounds__(NT, 2) bwd_gates_kernel(BwdParams p) {
+    constexpr int CTW = DK / 16 / 4;  // 16-channel column tiles per wave
+    constexpr int OS = DK + 16;       // operand row stride (read as [k][col])
+    constexpr int AS = DK + 1;        // result row stride (read per channel)
     __shared__ float sdT[BC][BC + 1];
     __shared__ float sdP[BC][BC + 1];
-    __shared__ float sW[BC][DK + 1];   // dKw, then the per-row dbeta terms
-    __shared__ float sDG[BC][DK + 1];  // dG (s side), then d log alpha
-    __shared__ float sRowG[BC];        // row sums of dgamma'
+    constexpr int SBUF = 3 * BC * OS > 4 * BC * AS ? 3 * BC * OS : 4 * BC * AS;
+    __shared__ __attribute__((aligned(16))) float sbuf[SBUF];  // operands, then A1..A4
+    __shared__ float sCst[DK];
+    __shared__ float sRowG[BC];  // row sums of dgamma'
+    float(*sW)[OS] = reinterpret_cast<float(*)[OS]>(sbuf);
+    float(*sRk)[OS] = reinterpret_cast<float(*)[OS]>(sbuf + BC * OS);
+    float(*sRq)[OS] = reinterpret_cast<float(*)[OS]>(sbuf + 2 * BC * OS);
+    // A1..A4, then per row: dkr (in A1), dkw (in A3), dG (in A2), the per-row
+    // sums for scalar gates: d log alpha (in A4), dbeta (in A1); dA (in A3)
+    float(*sA1)[AS] = reinterpret_cast<float(*)[AS]>(sbuf);
+    float(*sA3)[AS] = reinterpret_cast<float(*)[AS]>(sbuf + BC * AS);
+    float(*sA2)[AS] = reinterpret_cast<float(*)[AS]>(sbuf + 2 * BC * AS);
+    float(*sA4)[AS] = reinterpret_cast<float(*)[AS]>(sbuf + 3 * BC * AS);
+    float(*sRa)[AS] = sA4;
+    float(*sRb)[AS] = sA1;
     const long bh = blockIdx.x / p.nc;
     const long c = blockIdx.x % p.nc;
     const long t0 = c * BC;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int ln = lane & 15, g4 = lane >> 4;
     const long Tp = static_cast<long>(p.nc) * BC;
     const float* D = p.dgr + (bh * p.nc + c) * dgr_floats<DK>();
     const float* DdQg = D;
     const float* DdKg = D + BC * DK;
     const float* DdKd = D + 2 * BC * DK;
     const float* DdGc = D + 3 * BC * DK + 2 * BC * BC;
-    for (int idx = tid; idx < BC * BC; idx += NT) {
-        sdP[idx / BC][idx % BC] = D[3 * BC * DK + idx];
-        sdT[idx / BC][idx % BC] = D[3 * BC * DK + BC * BC + idx];
+    {
+        constexpr int PER = BC * BC / NT;
+        float tv[PER], pv[PER];
+#pragma unroll
+        for (int m = 0; m < PER; ++m) {
+            pv[m] = D[3 * BC * DK + tid + m * NT];
+            tv[m] = D[3 * BC * DK + BC * BC + tid + m * NT];
+        }
+#pragma unroll
+        for (int m = 0; m < PER; ++m) {
+            const int idx = tid + m * NT;
+            sdP[idx / BC][idx % BC] = pv[m];
+            sdT[idx / BC][idx % BC] = tv[m];
+        }
     }
-    // dv and dgamma' (wave w: rows w, w + 4, ...)
-    const bool gsum = p.gmode == PDN_GATE_SCALAR || (p.gmode == PDN_GAMMA_SAME_AS_BETA && p.bmode == PDN_GATE_SCALAR);
+    // dv and dgamma' (wave w: rows w, w + 4, ...; lanes over columns)
+    const bool gsum = p.gmode == PDN_GATE_SCALAR ||
+                      (p.gmode == PDN_GAMMA_SAME_AS_BETA && p.bmode == PDN_GATE_SCALAR);
+#pragma unroll 2
     for (int r = w; r < BC; r += 4) {
         const long t = t0 + r;
         float part = 0.f;
-        for (int j = lane; j < p.dv; j += 64) {
-            const float z = p.Z[(bh * Tp + t) * p.dv + j];
-            const float g = tok_gamma<DK>(p, bh, t, j);
-            const float vv = t < p.T ? ld<BF16>(p.v, (bh * p.T + t) * p.dv + j) : 0.f;
-            const float dg = z * vv * value_dscale(p.kmode, p.gmode, g);
-            if (t < p.T) {
-                p.dvo[(bh * p.T + t) * p.dv + j] = z * value_scale(p.kmode, p.gmode, g);
-                if (p.gmode == PDN_GATE_VEC) p.dgamma[(bh * p.T + t) * p.dv + j] = dg;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int j = lane + 64 * m;
+            if (j < p.dv) {
+                const float z = p.Z[(bh * Tp + t) * p.dv + j];
+                const float g = tok_gamma<DK>(p, bh, t, j);
+                const float vv = tok_in<BF16>(p, p.v, bh, t, p.dv, j);
+                const float dg = z * vv * value_dscale(p.kmode, p.gmode, g);
+                if (t < p.T) {
+                    p.dvo[(bh * p.T + t) * p.dv + j] = z * value_scale(p.kmode, p.gmode, g);
+                    if (p.gmode == PDN_GATE_VEC) p.dgamma[(bh * p.T + t) * p.dv + j] = dg;
+                }
+                part += dg;
             }
-            part += dg;
         }
         if (gsum) {
             part = wave_sum(part);
             if (lane == 0) sRowG[r] = part;
         }
     }
-    const int i = tid % DK, part = tid / DK;
-    // per-channel columns of the chunk (part 0)
-    if (part == 0) {
-        float G = 0.f;
-        float A = p.pre ? p.apre[(bh * p.nc + c) * DK + i] : 0.f;
+    // one thread per key channel: the chunk's column, every load first; the
+    // keys follow per row from the running k (.) k sum (keys_at)
+    const int i = tid;
+    float G[BC], kk[BC], qv[BC], bb[BC];
+    uint32_t dead = 0;  // rows whose d log alpha is zero
+    auto column = [&]() {
+#pragma unroll
         for (int r = 0; r < BC; ++r) {
             const long t = t0 + r;
-            const float kk = t < p.T ? ld<BF16>(p.k, (bh * p.T + t) * DK + i) : 0.f;
-            const float qq = t < p.T ? ld<BF16>(p.q, (bh * p.T + t) * DK + i) : 0.f;
-            G += tok_la<DK>(p, bh, t, i);
-            float b = tok_beta<DK>(p, bh, t, i);
-            if (p.pre) {
-                A += kk * kk;
-                b = b / (A + p.eps);
-            }
-            float kw, kr;
-            keys_of(p.kmode, b, kk, kw, kr);
-            sKr[r][i] = kr;
-            sKw[r][i] = kw;
-            sQ[r][i] = qq;
-            sG[r][i] = G;
+            kk[r] = tok_in<BF16>(p, p.k, bh, t, DK, i);
+            qv[r] = tok_in<BF16>(p, p.q, bh, t, DK, i);
+            G[r] = tok_la_raw<DK>(p, bh, t, i);
+            bb[r] = tok_beta<DK>(p, bh, t, i);
         }
+        float g = 0.f;
+#pragma unroll
+        for (int r = 0; r < BC; ++r) {
+            const long t = t0 + r;
+            if (la_dead(p, t, G[r])) dead |= 1u << r;
+            g += (t < p.T && p.amode != PDN_ALPHA_NONE) ? fmaxf(G[r], kLogAlphaMin) : 0.f;
+            G[r] = g;
+        }
+    };
+    // erase gain with the preconditioner folded in, advancing the running sum
+    auto gain_at = [&](int r, float& A, float& ainv) {
+        float b = bb[r];
+        ainv = 1.f;
+        if (p.pre) {
+            A += kk[r] * kk[r];
+            ainv = 1.f / (A + p.eps);
+            b = b * ainv;
+        }
+        return b;
+    };
+    const float A0c = p.pre ? p.apre[(bh * p.nc + c) * DK + i] : 0.f;
+    if (tid < DK) {
+        column();
+        float A = A0c, ainv;
+#pragma unroll
+        for (int r = 0; r < BC; ++r) {
+            float kwr, krr;
+            keys_of(p.kmode, gain_at(r, A, ainv), kk[r], kwr, krr);
+            const float gm = r < 16 ? G[8] : G[24];
+            const float L = __expf(G[r] - gm), R = __expf(gm - G[r]);
+            sW[r][i] = kwr * R;
+            sRk[r][i] = krr * L;
+            sRq[r][i] = qv[r] * L;
+        }
+        sCst[i] = __expf(G[24] - G[8]);
     }
     __syncthreads();
-    const float Gc = sG[BC - 1][i];
-    if (part == 1) {
-        // s side: A2 = sum_{r>s} dT_rs kr_r e, A4 = sum_{r>=s} dP_rs q_r e
+    // MFMA: wave w, column tiles CTW w .. CTW w + CTW - 1
+    f32x4 a1[CTW][2], a3[CTW][2], a2[CTW][2], a4[CTW][2];
+#pragma unroll
+    for (int m = 0; m < CTW; ++m) {
+        const int col = 16 * (CTW * w + m) + ln;
+        f32x4 x1[3], x3[3], x2[3], x4[3];  // [in block 0, in block 1, across]
+#pragma unroll
+        for (int u = 0; u < 3; ++u) {
+            x1[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            x3[u] = x1[u];
+            x2[u] = x1[u];
+            x4[u] = x1[u];
+        }
+#pragma unroll
+        for (int k = 0; k < 16; k += 4) {
+            const int kk0 = k + g4, kk1 = 16 + k + g4;
+            const float w0 = sW[kk0][col], w1 = sW[kk1][col];
+            const float rk0 = sRk[kk0][col], rk1 = sRk[kk1][col];
+            const float rq0 = sRq[kk0][col], rq1 = sRq[kk1][col];
+            // r side: rows of block b times the W rows of the s block
+            x1[0] = mfma4(sdT[ln][kk0], w0, x1[0]);
+            x1[1] = mfma4(sdT[16 + ln][kk1], w1, x1[1]);
+            x1[2] = mfma4(sdT[16 + ln][kk0], w0, x1[2]);
+            x3[0] = mfma4(sdP[ln][kk0], w0, x3[0]);
+            x3[1] = mfma4(sdP[16 + ln][kk1], w1, x3[1]);
+            x3[2] = mfma4(sdP[16 + ln][kk0], w0, x3[2]);
+            // s side: transposed blocks times the Rk / Rq rows of the r block
+            x2[0] = mfma4(sdT[kk0][ln], rk0, x2[0]);
+            x2[1] = mfma4(sdT[kk1][16 + ln], rk1, x2[1]);
+            x2[2] = mfma4(sdT[kk1][ln], rk1, x2[2]);
+            x4[0] = mfma4(sdP[kk0][ln], rq0, x4[0]);
+            x4[1] = mfma4(sdP[kk1][16 + ln], rq1, x4[1]);
+            x4[2] = mfma4(sdP[kk1][ln], rq1, x4[2]);
+        }
+        const float cst = sCst[col];
+        // rows (r side) / columns (s side) of block 1 get the across-block term
+        // (r side), block 0 (s side)
+        a1[m][0] = x1[0];
+        a3[m][0] = x3[0];
+        a2[m][1] = x2[1];
+        a4[m][1] = x4[1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            a1[m][1][e] = x1[1][e] + cst * x1[2][e];
+            a3[m][1][e] = x3[1][e] + cst * x3[2][e];
+            a2[m][0][e] = x2[0][e] + cst * x2[2][e];
+            a4[m][0][e] = x4[0][e] + cst * x4[2][e];
+        }
+    }
+    __syncthreads();  // every wave has read the operands: the buffer takes A1..A4
+#pragma unroll
+    for (int m = 0; m < CTW; ++m) {
+        const int col = 16 * (CTW * w + m) + ln;
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * b + 4 * g4 + e;
+                sA1[r][col] = a1[m][b][e];
+                sA3[r][col] = a3[m][b][e];
+                sA2[r][col] = a2[m][b][e];
+                sA4[r][col] = a4[m][b][e];
+            }
+    }
+    __syncthreads();
+    if (tid < DK) {
+        column();  // reloaded: nothing large stays live across the products
+        const float Gc = G[BC - 1];
         float kdsum = 0.f;
-        for (int s = 0; s < BC; ++s) {
-            const float gs = sG[s][i];
-            float a2 = 0.f, a4 = 0.f;
-            for (int r = s; r < BC; ++r) {
-                const float e = __expf(sG[r][i] - gs);
-                a2 += sdT[r][s] * sKr[r][i] * e;
-                a4 += sdP[r][s] * sQ[r][i] * e;
-            }
-            const float ed = __expf(Gc - gs);
-            const float dkd = DdKd[s * DK + i];
-            const float kd = sKw[s][i] * ed;
-            kdsum += dkd * kd;
-            sW[s][i] = dkd * ed + a2 + a4;
-            sDG[s][i] = -dkd * kd - sKw[s][i] * (a2 + a4);
-        }
-        sDG[BC - 1][i] += kdsum + DdGc[i] * __expf(Gc);
-    }
-    __syncthreads();
-    if (part == 0) {
-        // r side: A1 = sum_{s<r} dT_rs kw_s e, A3 = sum_{s<=r} dP_rs kw_s e
+        float A = A0c, ainv;
+#pragma unroll
         for (int r = 0; r < BC; ++r) {
-            const float gr = sG[r][i];
-            float a1 = 0.f, a3 = 0.f;
-            for (int s = 0; s <= r; ++s) {
-                const float wv = sKw[s][i] * __expf(gr - sG[s][i]);
-                a1 += sdT[r][s] * wv;
-                a3 += sdP[r][s] * wv;
-            }
-            const float eg = __expf(gr);
-            const float dqg = DdQg[r * DK + i], dkg = DdKg[r * DK + i];
-            const float dq = dqg * eg + a3;
-            const float dkr = dkg * eg + a1;
+            float kwr, krr;
+            keys_of(p.kmode, gain_at(r, A, ainv), kk[r], kwr, krr);
+            const float gm = r < 16 ? G[8] : G[24];
+            const float L = __expf(G[r] - gm), R = __expf(gm - G[r]);
+            const float A1 = L * sA1[r][i], A3 = L * sA3[r][i];
+            const float A2 = R * sA2[r][i], A4 = R * sA4[r][i];
+            const float eg = __expf(G[r]);
+            const float ed = __expf(Gc - G[r]);
+            const float dqg = DdQg[r * DK + i], dkg = DdKg[r * DK + i], dkd = DdKd[r * DK + i];
             const long t = t0 + r;
-            if (t < p.T) p.dq[(bh * p.T + t) * DK + i] = dq;
-            sDG[r][i] += dkg * sKr[r][i] * eg + dqg * sQ[r][i] * eg + sKr[r][i] * a1 + sQ[r][i] * a3;
-            // reuse sKr[r][i] for dkr (only this thread reads it from here on)
-            sKr[r][i] = dkr;
+            if (t < p.T) p.dq[(bh * p.T + t) * DK + i] = dqg * eg + A3;
+            const float kd = kwr * ed;
+            kdsum += dkd * kd;
+            sA1[r][i] = dkg * eg + A1;         // dkr
+            sA3[r][i] = dkd * ed + A2 + A4;    // dkw
+            sA2[r][i] = dkg * krr * eg + dqg * qv[r] * eg + krr * A1 + qv[r] * A3 -
+                        dkd * kd - kwr * (A2 + A4);  // dG
         }
+        sA2[BC - 1][i] += kdsum + DdGc[i] * __expf(Gc);
         // d log alpha: reverse cumulative sum of dG over the chunk
         float run = 0.f;
+#pragma unroll
         for (int r = BC - 1; r >= 0; --r) {
-            run += sDG[r][i];
+            run += sA2[r][i];
             const long t = t0 + r;
-            const float dla = tok_la_clamped<DK>(p, bh, t, i) ? 0.f : run;
+            const float dla = ((dead >> r) & 1u) ? 0.f : run;
             if (p.amode == PDN_ALPHA_VEC && t < p.T) p.dla[(bh * p.T + t) * DK + i] = dla;
-            sDG[r][i] = dla;
+            sRa[r][i] = dla;
         }
         // keys to k and the gains; the preconditioner's dA
-        float A = p.pre ? p.apre[(bh * p.nc + c) * DK + i] : 0.f;
+        A = A0c;
+#pragma unroll
         for (int r = 0; r < BC; ++r) {
             const long t = t0 + r;
-            const float kk = t < p.T ? ld<BF16>(p.k, (bh * p.T + t) * DK + i) : 0.f;
-            const float braw = tok_beta<DK>(p, bh, t, i);
-            float b = braw, ainv = 1.f;
-            if (p.pre) {
-                A += kk * kk;
-                ainv = 1.f / (A + p.eps);
-                b = braw * ainv;
-            }
-            const float dkw = sW[r][i], dkr = sKr[r][i];
+            const float braw = bb[r];
+            const float b = gain_at(r, A, ainv);
+            const float dkwr = sA3[r][i], dkrr = sA1[r][i];
             float dkk, db;
             if (p.kmode == PDN_KEY_SYMMETRIC) {
                 const float sb = sqrtf(b);
-                dkk = (dkw + dkr) * sb;
-                db = (dkw + dkr) * kk * 0.5f / sb;
+                dkk = (dkwr + dkrr) * sb;
+                db = (dkwr + dkrr) * kk[r] * 0.5f / sb;
             } else if (p.kmode == PDN_KEY_ERASE_GATE) {
-                dkk = dkw + dkr * b;
-                db = dkr * kk;
+                dkk = dkwr + dkrr * b;
+                db = dkrr * kk[r];
             } else {
-                dkk = dkw * b + dkr;
-                db = dkw * kk;
+                dkk = dkwr * b + dkrr;
+                db = dkwr * kk[r];
             }
             float dA = 0.f;
             if (p.pre) {
@@ -730,20 +991,21 @@ __global__ void __launch_bounds__(NT) bwd_gates_kernel(BwdParams p) {
             if (p.gmode == PDN_GAMMA_SAME_AS_BETA && p.bmode == PDN_GATE_VEC && t < p.T) {
                 // beta also scales the value of column i (dk == dv)
                 const float z = p.Z[(bh * Tp + t) * p.dv + i];
-                const float vv = ld<BF16>(p.v, (bh * p.T + t) * p.dv + i);
+                const float vv = load_in<BF16>(p.v, (bh * p.T + t) * p.dv + i);
                 db += z * vv * value_dscale(p.kmode, p.gmode, braw);
             }
             if (t < p.T) {
                 p.dk[(bh * p.T + t) * DK + i] = dkk;
                 if (p.bmode == PDN_GATE_VEC) p.dbeta[(bh * p.T + t) * DK + i] = db;
             }
-            sW[r][i] = db;
-            sQ[r][i] = dA;  // reuse: dA per row
+            sRb[r][i] = db;
+            sA3[r][i] = dA;
         }
         if (p.pre) {
             float suf = 0.f;
+#pragma unroll
             for (int r = BC - 1; r >= 0; --r) {
-                suf += sQ[r][i];
+                suf += sA3[r][i];
                 p.dAin[(bh * Tp + t0 + r) * DK + i] = suf;
             }
             p.dAc[(bh * p.nc + c) * DK + i] = suf;
@@ -756,15 +1018,15 @@ __global__ void __launch_bounds__(NT) bwd_gates_kernel(BwdParams p) {
         const long t = t0 + r;
         if (t < p.T) {
             if (p.amode == PDN_ALPHA_SCALAR) {
-                float s = 0.f;
-                for (int ii = 0; ii < DK; ++ii) s += sDG[r][ii];
-                p.dla[bh * p.T + t] = s;
+                float sm = 0.f;
+                for (int ii = 0; ii < DK; ++ii) sm += sRa[r][ii];
+                p.dla[bh * p.T + t] = sm;
             }
             if (p.bmode == PDN_GATE_SCALAR) {
-                float s = 0.f;
-                for (int ii = 0; ii < DK; ++ii) s += sW[r][ii];
-                if (p.gmode == PDN_GAMMA_SAME_AS_BETA) s += sRowG[r];
-                p.dbeta[bh * p.T + t] = s;
+                float sm = 0.f;
+                for (int ii = 0; ii < DK; ++ii) sm += sRb[r][ii];
+                if (p.gmode == PDN_GAMMA_SAME_AS_BETA) sm += sRowG[r];
+                p.dbeta[bh * p.T + t] = sm;
             }
             if (p.gmode == PDN_GATE_SCALAR) p.dgamma[bh * p.T + t] = sRowG[r];
         }
@@ -779,7 +1041,18 @@ __global__ void __launch_bounds__(DK) bwd_dA_scan_kernel(BwdParams p) {
     const long bh = blockIdx.x;
     const int i = threadIdx.x;
     float run = 0.f;
-    for (long c = p.nc - 1; c >= 0; --c) {
+    long c = p.nc - 1;
+    for (; c >= 7; c -= 8) {
+        float x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = p.dAc[(bh * p.nc + c - u) * DK + i];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            p.dAsuf[(bh * p.nc + c - u) * DK + i] = run;
+            run += x[u];
+        }
+    }
+    for (; c >= 0; --c) {
         p.dAsuf[(bh * p.nc + c) * DK + i] = run;
         run += p.dAc[(bh * p.nc + c) * DK + i];
     }
