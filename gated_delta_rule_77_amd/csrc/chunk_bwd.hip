@@ -736,28 +736,61 @@ __global__ void __launch_bounds__(NT) bwd_dgrad_kernel(BwdParams p) {
 //   A2 = R (.) [dT^T Rk]_in-block + R (.) c (.) [dT_(1,0)^T Rk_1]   (c = e^(G_24 - G_8))
 // and likewise A3, A4 with dP.
 // ---------------------------------------------------------------------------
+// Per-thread views of one key channel's per-token inputs over a chunk: base
+// pointers and strides are fixed once; a row index beyond T is clamped (the
+// value is then masked by the caller).
+template <int DK, bool BF16>
+struct ColView {
+    const void* k;
+    const void* q;
+    const float* la;
+    const float* be;
+    long kq_row, la_row, be_row;  // element strides per token
+    int rmax;                     // last valid row of the chunk
+    __device__ ColView(const BwdParams& p, long bh, long t0, int i) {
+        const long tok0 = bh * p.T + t0;
+        rmax = static_cast<int>(min(static_cast<long>(BC - 1), p.T - 1 - t0));
+        const size_t esz = BF16 ? 2 : 4;
+        k = static_cast<const char*>(p.k) + (tok0 * DK + i) * esz;
+        q = static_cast<const char*>(p.q) + (tok0 * DK + i) * esz;
+        kq_row = DK;
+        const bool lav = p.amode == PDN_ALPHA_VEC;
+        la = (p.amode == PDN_ALPHA_NONE ? p.beta + tok0 : p.la + (lav ? tok0 * DK + i : tok0));
+        la_row = lav ? DK : 1;
+        const bool bv = p.bmode == PDN_GATE_VEC;
+        be = p.beta + (bv ? tok0 * DK + i : tok0);
+        be_row = bv ? DK : 1;
+    }
+    __device__ __forceinline__ int rc(int r) const { return r < rmax ? r : rmax; }
+    __device__ __forceinline__ float kv(int r) const { return load_in<BF16>(k, rc(r) * kq_row); }
+    __device__ __forceinline__ float qv(int r) const { return load_in<BF16>(q, rc(r) * kq_row); }
+    __device__ __forceinline__ float lav(int r) const { return la[rc(r) * la_row]; }
+    __device__ __forceinline__ float bev(int r) const { return be[rc(r) * be_row]; }
+};
+
 template <int DK, bool BF16>
 __global__ void __launch_bounds__(NT, 2) bwd_gates_kernel(BwdParams p) {
     constexpr int CTW = DK / 16 / 4;  // 16-channel column tiles per wave
     constexpr int OS = DK + 16;       // operand row stride (read as [k][col])
     constexpr int AS = DK + 1;        // result row stride (read per channel)
+    constexpr int NH = NT / DK;       // threads per channel
+    constexpr int RPT = BC / NH;      // rows per thread
     __shared__ float sdT[BC][BC + 1];
     __shared__ float sdP[BC][BC + 1];
     constexpr int SBUF = 3 * BC * OS > 4 * BC * AS ? 3 * BC * OS : 4 * BC * AS;
     __shared__ __attribute__((aligned(16))) float sbuf[SBUF];  // operands, then A1..A4
-    __shared__ float sCst[DK];
-    __shared__ float sRowG[BC];  // row sums of dgamma'
+    __shared__ float sX[NH][4][DK];  // per-part partial sums exchanged between the parts of a channel
+    __shared__ float sRef[3][DK];    // G_8, G_24, G_C of each channel
+    __shared__ float sRowG[BC];      // row sums of dgamma'
     float(*sW)[OS] = reinterpret_cast<float(*)[OS]>(sbuf);
     float(*sRk)[OS] = reinterpret_cast<float(*)[OS]>(sbuf + BC * OS);
     float(*sRq)[OS] = reinterpret_cast<float(*)[OS]>(sbuf + 2 * BC * OS);
-    // A1..A4, then per row: dkr (in A1), dkw (in A3), dG (in A2), the per-row
-    // sums for scalar gates: d log alpha (in A4), dbeta (in A1); dA (in A3)
+    // A1..A4, then per row: dkr (in A1), dkw (in A3), dG (in A2), dq (in A4);
+    // later the per-row sums for scalar gates: d log alpha (A4), dbeta (A1), dA (A3)
     float(*sA1)[AS] = reinterpret_cast<float(*)[AS]>(sbuf);
     float(*sA3)[AS] = reinterpret_cast<float(*)[AS]>(sbuf + BC * AS);
     float(*sA2)[AS] = reinterpret_cast<float(*)[AS]>(sbuf + 2 * BC * AS);
     float(*sA4)[AS] = reinterpret_cast<float(*)[AS]>(sbuf + 3 * BC * AS);
-    float(*sRa)[AS] = sA4;
-    float(*sRb)[AS] = sA1;
     const long bh = blockIdx.x / p.nc;
     const long c = blockIdx.x % p.nc;
     const long t0 = c * BC;
@@ -765,10 +798,6 @@ __global__ void __launch_bounds__(NT, 2) bwd_gates_kernel(BwdParams p) {
     const int ln = lane & 15, g4 = lane >> 4;
     const long Tp = static_cast<long>(p.nc) * BC;
     const float* D = p.dgr + (bh * p.nc + c) * dgr_floats<DK>();
-    const float* DdQg = D;
-    const float* DdKg = D + BC * DK;
-    const float* DdKd = D + 2 * BC * DK;
-    const float* DdGc = D + 3 * BC * DK + 2 * BC * BC;
     {
         constexpr int PER = BC * BC / NT;
         float tv[PER], pv[PER];
@@ -784,82 +813,134 @@ __global__ void __launch_bounds__(NT, 2) bwd_gates_kernel(BwdParams p) {
             sdT[idx / BC][idx % BC] = tv[m];
         }
     }
-    // dv and dgamma' (wave w: rows w, w + 4, ...; lanes over columns)
+    // dv and dgamma' (wave w: rows w, w + 4, ...; lanes over columns), in four
+    // batches of two rows, every load of a batch before its stores
     const bool gsum = p.gmode == PDN_GATE_SCALAR ||
                       (p.gmode == PDN_GAMMA_SAME_AS_BETA && p.bmode == PDN_GATE_SCALAR);
-#pragma unroll 2
-    for (int r = w; r < BC; r += 4) {
-        const long t = t0 + r;
-        float part = 0.f;
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int j = lane + 64 * m;
-            if (j < p.dv) {
-                const float z = p.Z[(bh * Tp + t) * p.dv + j];
-                const float g = tok_gamma<DK>(p, bh, t, j);
-                const float vv = tok_in<BF16>(p, p.v, bh, t, p.dv, j);
-                const float dg = z * vv * value_dscale(p.kmode, p.gmode, g);
-                if (t < p.T) {
-                    p.dvo[(bh * p.T + t) * p.dv + j] = z * value_scale(p.kmode, p.gmode, g);
-                    if (p.gmode == PDN_GATE_VEC) p.dgamma[(bh * p.T + t) * p.dv + j] = dg;
-                }
-                part += dg;
+    for (int quarter = 0; quarter < 4; ++quarter) {
+        float zv[2][4], gv[2][4], vv[2][4];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int r = w + 4 * (2 * quarter + m);
+            const long t = t0 + r;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int j = min(lane + 64 * u, p.dv - 1);
+                zv[m][u] = p.Z[(bh * Tp + t) * p.dv + j];
+                gv[m][u] = tok_gamma<DK>(p, bh, t, j);
+                vv[m][u] = tok_in<BF16>(p, p.v, bh, t, p.dv, j);
             }
         }
-        if (gsum) {
-            part = wave_sum(part);
-            if (lane == 0) sRowG[r] = part;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int r = w + 4 * (2 * quarter + m);
+            const long t = t0 + r;
+            float part = 0.f;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int j = lane + 64 * u;
+                if (j < p.dv) {
+                    const float dg = zv[m][u] * vv[m][u] * value_dscale(p.kmode, p.gmode, gv[m][u]);
+                    if (t < p.T) {
+                        p.dvo[(bh * p.T + t) * p.dv + j] =
+                            zv[m][u] * value_scale(p.kmode, p.gmode, gv[m][u]);
+                        if (p.gmode == PDN_GATE_VEC) p.dgamma[(bh * p.T + t) * p.dv + j] = dg;
+                    }
+                    part += dg;
+                }
+            }
+            if (gsum) {
+                part = wave_sum(part);
+                if (lane == 0) sRowG[r] = part;
+            }
         }
     }
-    // one thread per key channel: the chunk's column, every load first; the
-    // keys follow per row from the running k (.) k sum (keys_at)
-    const int i = tid;
-    float G[BC], kk[BC], qv[BC], bb[BC];
-    uint32_t dead = 0;  // rows whose d log alpha is zero
+    // thread (channel i, part h) owns rows h RPT .. h RPT + RPT - 1 of channel i
+    const int i = tid % DK, h = tid / DK, r0 = h * RPT;
+    const ColView<DK, BF16> cv(p, bh, t0, i);
+    const bool has_decay = p.amode != PDN_ALPHA_NONE;
+    float G[RPT], kk[RPT], qv[RPT], bb[RPT];
+    uint32_t dead = 0;  // own rows whose d log alpha is zero
+    float Gin = 0.f, Ain = 0.f;  // cumulative log decay and k (.) k before the own rows
     auto column = [&]() {
 #pragma unroll
-        for (int r = 0; r < BC; ++r) {
-            const long t = t0 + r;
-            kk[r] = tok_in<BF16>(p, p.k, bh, t, DK, i);
-            qv[r] = tok_in<BF16>(p, p.q, bh, t, DK, i);
-            G[r] = tok_la_raw<DK>(p, bh, t, i);
-            bb[r] = tok_beta<DK>(p, bh, t, i);
+        for (int u = 0; u < RPT; ++u) {
+            kk[u] = cv.kv(r0 + u);
+            qv[u] = cv.qv(r0 + u);
+            G[u] = cv.lav(r0 + u);
+            bb[u] = cv.bev(r0 + u);
         }
-        float g = 0.f;
 #pragma unroll
-        for (int r = 0; r < BC; ++r) {
-            const long t = t0 + r;
-            if (la_dead(p, t, G[r])) dead |= 1u << r;
-            g += (t < p.T && p.amode != PDN_ALPHA_NONE) ? fmaxf(G[r], kLogAlphaMin) : 0.f;
-            G[r] = g;
+        for (int u = 0; u < RPT; ++u) {
+            const bool valid = t0 + r0 + u < p.T;
+            if (!valid || !has_decay || G[u] < kLogAlphaMin) dead |= 1u << u;
+            G[u] = (valid && has_decay) ? fmaxf(G[u], kLogAlphaMin) : 0.f;
+            if (!valid) {
+                kk[u] = 0.f;
+                qv[u] = 0.f;
+                bb[u] = 1.f;
+            }
         }
     };
+    column();
+    {
+        // prefix over the parts: local sums, exchanged, then made inclusive
+        float gs = 0.f, as = 0.f;
+#pragma unroll
+        for (int u = 0; u < RPT; ++u) {
+            gs += G[u];
+            as += kk[u] * kk[u];
+        }
+        sX[h][0][i] = gs;
+        sX[h][1][i] = as;
+        __syncthreads();
+        for (int h2 = 0; h2 < h; ++h2) {
+            Gin += sX[h2][0][i];
+            Ain += sX[h2][1][i];
+        }
+        if (p.pre) Ain += p.apre[(bh * p.nc + c) * DK + i];
+        float g = Gin;
+#pragma unroll
+        for (int u = 0; u < RPT; ++u) {
+            g += G[u];
+            G[u] = g;
+        }
+        // the reference rows 8 and 24 and the last row, for every part of the channel
+#pragma unroll
+        for (int u = 0; u < RPT; ++u) {
+            const int r = r0 + u;
+            if (r == 8) sRef[0][i] = G[u];
+            if (r == 24) sRef[1][i] = G[u];
+            if (r == BC - 1) sRef[2][i] = G[u];
+        }
+        __syncthreads();
+    }
+    const float G8 = sRef[0][i], G24 = sRef[1][i], Gc = sRef[2][i];
     // erase gain with the preconditioner folded in, advancing the running sum
-    auto gain_at = [&](int r, float& A, float& ainv) {
-        float b = bb[r];
+    auto gain_at = [&](int u, float& A, float& ainv) {
+        float b = bb[u];
         ainv = 1.f;
         if (p.pre) {
-            A += kk[r] * kk[r];
+            A += kk[u] * kk[u];
             ainv = 1.f / (A + p.eps);
             b = b * ainv;
         }
         return b;
     };
-    const float A0c = p.pre ? p.apre[(bh * p.nc + c) * DK + i] : 0.f;
-    if (tid < DK) {
-        column();
-        float A = A0c, ainv;
+    {
+        float A = Ain, ainv;
 #pragma unroll
-        for (int r = 0; r < BC; ++r) {
+        for (int u = 0; u < RPT; ++u) {
+            const int r = r0 + u;
             float kwr, krr;
-            keys_of(p.kmode, gain_at(r, A, ainv), kk[r], kwr, krr);
-            const float gm = r < 16 ? G[8] : G[24];
-            const float L = __expf(G[r] - gm), R = __expf(gm - G[r]);
+            keys_of(p.kmode, gain_at(u, A, ainv), kk[u], kwr, krr);
+            const float gm = r < 16 ? G8 : G24;
+            const float L = __expf(G[u] - gm), R = __expf(gm - G[u]);
             sW[r][i] = kwr * R;
             sRk[r][i] = krr * L;
-            sRq[r][i] = qv[r] * L;
+            sRq[r][i] = qv[u] * L;
         }
-        sCst[i] = __expf(G[24] - G[8]);
     }
     __syncthreads();
     // MFMA: wave w, column tiles CTW w .. CTW w + CTW - 1
@@ -896,9 +977,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_gates_kernel(BwdParams p) {
             x4[1] = mfma4(sdP[kk1][16 + ln], rq1, x4[1]);
             x4[2] = mfma4(sdP[kk1][ln], rq1, x4[2]);
         }
-        const float cst = sCst[col];
-        // rows (r side) / columns (s side) of block 1 get the across-block term
-        // (r side), block 0 (s side)
+        const float cst = __expf(sRef[1][col] - sRef[0][col]);  // e^(G_24 - G_8)
         a1[m][0] = x1[0];
         a3[m][0] = x3[0];
         a2[m][1] = x2[1];
@@ -927,61 +1006,92 @@ __global__ void __launch_bounds__(NT, 2) bwd_gates_kernel(BwdParams p) {
             }
     }
     __syncthreads();
-    if (tid < DK) {
-        column();  // reloaded: nothing large stays live across the products
-        const float Gc = G[BC - 1];
-        float kdsum = 0.f;
-        float A = A0c, ainv;
+    const float* DdQg = D + i;
+    const float* DdKg = D + BC * DK + i;
+    const float* DdKd = D + 2 * BC * DK + i;
+    float kdsum = 0.f;
+    {
+        float dqg[RPT], dkg[RPT], dkd[RPT];
 #pragma unroll
-        for (int r = 0; r < BC; ++r) {
+        for (int u = 0; u < RPT; ++u) {
+            dqg[u] = DdQg[(r0 + u) * DK];
+            dkg[u] = DdKg[(r0 + u) * DK];
+            dkd[u] = DdKd[(r0 + u) * DK];
+        }
+        float A = Ain, ainv;
+#pragma unroll
+        for (int u = 0; u < RPT; ++u) {
+            const int r = r0 + u;
             float kwr, krr;
-            keys_of(p.kmode, gain_at(r, A, ainv), kk[r], kwr, krr);
-            const float gm = r < 16 ? G[8] : G[24];
-            const float L = __expf(G[r] - gm), R = __expf(gm - G[r]);
+            keys_of(p.kmode, gain_at(u, A, ainv), kk[u], kwr, krr);
+            const float gm = r < 16 ? G8 : G24;
+            const float L = __expf(G[u] - gm), R = __expf(gm - G[u]);
             const float A1 = L * sA1[r][i], A3 = L * sA3[r][i];
             const float A2 = R * sA2[r][i], A4 = R * sA4[r][i];
-            const float eg = __expf(G[r]);
-            const float ed = __expf(Gc - G[r]);
-            const float dqg = DdQg[r * DK + i], dkg = DdKg[r * DK + i], dkd = DdKd[r * DK + i];
-            const long t = t0 + r;
-            if (t < p.T) p.dq[(bh * p.T + t) * DK + i] = dqg * eg + A3;
+            const float eg = __expf(G[u]);
+            const float ed = __expf(Gc - G[u]);
             const float kd = kwr * ed;
-            kdsum += dkd * kd;
-            sA1[r][i] = dkg * eg + A1;         // dkr
-            sA3[r][i] = dkd * ed + A2 + A4;    // dkw
-            sA2[r][i] = dkg * krr * eg + dqg * qv[r] * eg + krr * A1 + qv[r] * A3 -
-                        dkd * kd - kwr * (A2 + A4);  // dG
+            kdsum += dkd[u] * kd;
+            sA4[r][i] = dqg[u] * eg + A3;         // dq
+            sA1[r][i] = dkg[u] * eg + A1;         // dkr
+            sA3[r][i] = dkd[u] * ed + A2 + A4;    // dkw
+            sA2[r][i] = dkg[u] * krr * eg + dqg[u] * qv[u] * eg + krr * A1 + qv[u] * A3 -
+                        dkd[u] * kd - kwr * (A2 + A4);  // dG
         }
-        sA2[BC - 1][i] += kdsum + DdGc[i] * __expf(Gc);
+    }
+    sX[h][2][i] = kdsum;
+    __syncthreads();
+    if (h == NH - 1) {
+        float tot = 0.f;
+#pragma unroll
+        for (int h2 = 0; h2 < NH; ++h2) tot += sX[h2][2][i];
+        sA2[BC - 1][i] += tot + D[3 * BC * DK + 2 * BC * BC + i] * __expf(Gc);
+    }
+#pragma unroll
+    for (int u = 0; u < RPT; ++u)
+        if (t0 + r0 + u < p.T) p.dq[(bh * p.T + t0 + r0 + u) * DK + i] = sA4[r0 + u][i];
+    // dG totals of the parts, for the reverse cumulative sum across them
+    {
+        float tot = 0.f;
+#pragma unroll
+        for (int u = 0; u < RPT; ++u) tot += sA2[r0 + u][i];
+        sX[h][3][i] = tot;
+    }
+    __syncthreads();
+    {
         // d log alpha: reverse cumulative sum of dG over the chunk
         float run = 0.f;
+        for (int h2 = h + 1; h2 < NH; ++h2) run += sX[h2][3][i];
 #pragma unroll
-        for (int r = BC - 1; r >= 0; --r) {
+        for (int u = RPT - 1; u >= 0; --u) {
+            const int r = r0 + u;
             run += sA2[r][i];
             const long t = t0 + r;
-            const float dla = ((dead >> r) & 1u) ? 0.f : run;
+            const float dla = ((dead >> u) & 1u) ? 0.f : run;
             if (p.amode == PDN_ALPHA_VEC && t < p.T) p.dla[(bh * p.T + t) * DK + i] = dla;
-            sRa[r][i] = dla;
+            sA4[r][i] = dla;
         }
         // keys to k and the gains; the preconditioner's dA
-        A = A0c;
+        float A = Ain, ainv;
+        float dAsum = 0.f;
 #pragma unroll
-        for (int r = 0; r < BC; ++r) {
+        for (int u = 0; u < RPT; ++u) {
+            const int r = r0 + u;
             const long t = t0 + r;
-            const float braw = bb[r];
-            const float b = gain_at(r, A, ainv);
+            const float braw = bb[u];
+            const float b = gain_at(u, A, ainv);
             const float dkwr = sA3[r][i], dkrr = sA1[r][i];
             float dkk, db;
             if (p.kmode == PDN_KEY_SYMMETRIC) {
                 const float sb = sqrtf(b);
                 dkk = (dkwr + dkrr) * sb;
-                db = (dkwr + dkrr) * kk[r] * 0.5f / sb;
+                db = (dkwr + dkrr) * kk[u] * 0.5f / sb;
             } else if (p.kmode == PDN_KEY_ERASE_GATE) {
                 dkk = dkwr + dkrr * b;
-                db = dkrr * kk[r];
+                db = dkrr * kk[u];
             } else {
                 dkk = dkwr * b + dkrr;
-                db = dkwr * kk[r];
+                db = dkwr * kk[u];
             }
             float dA = 0.f;
             if (p.pre) {
@@ -998,20 +1108,23 @@ __global__ void __launch_bounds__(NT, 2) bwd_gates_kernel(BwdParams p) {
                 p.dk[(bh * p.T + t) * DK + i] = dkk;
                 if (p.bmode == PDN_GATE_VEC) p.dbeta[(bh * p.T + t) * DK + i] = db;
             }
-            sRb[r][i] = db;
+            sA1[r][i] = db;
             sA3[r][i] = dA;
+            dAsum += dA;
         }
-        if (p.pre) {
-            float suf = 0.f;
-#pragma unroll
-            for (int r = BC - 1; r >= 0; --r) {
-                suf += sA3[r][i];
-                p.dAin[(bh * Tp + t0 + r) * DK + i] = suf;
-            }
-            p.dAc[(bh * p.nc + c) * DK + i] = suf;
-        }
+        if (p.pre) sX[h][0][i] = dAsum;
     }
     __syncthreads();
+    if (p.pre) {
+        float suf = 0.f;
+        for (int h2 = h + 1; h2 < NH; ++h2) suf += sX[h2][0][i];
+#pragma unroll
+        for (int u = RPT - 1; u >= 0; --u) {
+            suf += sA3[r0 + u][i];
+            p.dAin[(bh * Tp + t0 + r0 + u) * DK + i] = suf;
+        }
+        if (h == 0) p.dAc[(bh * p.nc + c) * DK + i] = suf;
+    }
     // per-token sums for scalar gates
     if (tid < BC) {
         const int r = tid;
@@ -1019,12 +1132,12 @@ __global__ void __launch_bounds__(NT, 2) bwd_gates_kernel(BwdParams p) {
         if (t < p.T) {
             if (p.amode == PDN_ALPHA_SCALAR) {
                 float sm = 0.f;
-                for (int ii = 0; ii < DK; ++ii) sm += sRa[r][ii];
+                for (int ii = 0; ii < DK; ++ii) sm += sA4[r][ii];
                 p.dla[bh * p.T + t] = sm;
             }
             if (p.bmode == PDN_GATE_SCALAR) {
                 float sm = 0.f;
-                for (int ii = 0; ii < DK; ++ii) sm += sRb[r][ii];
+                for (int ii = 0; ii < DK; ++ii) sm += sA1[r][ii];
                 if (p.gmode == PDN_GAMMA_SAME_AS_BETA) sm += sRowG[r];
                 p.dbeta[bh * p.T + t] = sm;
             }
