@@ -8,7 +8,12 @@
  *      erase-gate keys, a start state, caller-allocated workspace;
  *   2. scalar-gate prefill (Gated DeltaNet gating), bf16 output, no workspace;
  *   3. five decode steps against a resident fp32 state, write-gate keys;
- *   4. error paths: a workspace one byte short, an unknown key mode.
+ *   4. the backward of a prefill (fp32 q/k/v, dk = dv = 64, T = 70, per-channel
+ *      decay and key gain, per-token value gain, write-gate keys, the
+ *      preconditioner with a start sum, a start state and dST): every
+ *      gradient against the oracle's backward;
+ *   5. error paths: a workspace one byte short (prefill and backward), an
+ *      unknown key mode, the stabilised preconditioner in the backward.
  *
  * Inputs come from a counter-based generator (splitmix64 of a running index),
  * rounded to bf16 where the GPU reads bf16, and the same values (widened to
@@ -28,6 +33,14 @@ int oracle_delta_rule(int B, int H, int T, int dk, int dv, const double *q, cons
                       const double *beta, int gamma_mode, const double *gamma, double precond_eps,
                       const double *A0, double *AT, const double *S0, double *ST, double *o,
                       int key_mode, int precond_mode, double precond_x);
+
+int oracle_delta_rule_bwd(int B, int H, int T, int dk, int dv, const double *q, const double *k,
+                          const double *v, int alpha_mode, const double *log_alpha, int beta_mode,
+                          const double *beta, int gamma_mode, const double *gamma,
+                          double precond_eps, const double *A0, const double *S0, int key_mode,
+                          int precond_mode, double precond_x, const double *dO, const double *dST,
+                          double *dq, double *dk_out, double *dv_out, double *dlog_alpha, double *dbeta,
+                          double *dgamma, double *dS0, double *dA0);
 
 static int failures = 0;
 
@@ -290,6 +303,100 @@ static void decode_case(hipStream_t st) {
     free(bes); free(gas); free(o); free(o_ref); free(s_ref); free(s);
 }
 
+/* ---- 4: backward ---- */
+static void bwd_case(hipStream_t st) {
+    const int B = 1, H = 2, T = 70, dk = 64, dv = 64;
+    const long nq = (long)B * H * T * dk, nv = (long)B * H * T * dv, nt = (long)B * H * T;
+    const long ns = (long)B * H * dk * dv, na = (long)B * H * dk;
+    float *q_f = malloc(nq * 4), *k_f = malloc(nq * 4), *v_f = malloc(nv * 4);
+    double *q = malloc(nq * 8), *k = malloc(nq * 8), *v = malloc(nv * 8);
+    for (long r = 0; r < nq / dk; ++r) {
+        double a[64], b[64], sa = 0.0, sb = 0.0;
+        for (int i = 0; i < dk; ++i) { a[i] = normal01(); b[i] = normal01(); sa += a[i] * a[i]; sb += b[i] * b[i]; }
+        for (int i = 0; i < dk; ++i) {
+            q_f[r * dk + i] = (float)(a[i] / sqrt(sa)); q[r * dk + i] = q_f[r * dk + i];
+            k_f[r * dk + i] = (float)(b[i] / sqrt(sb)); k[r * dk + i] = k_f[r * dk + i];
+        }
+    }
+    fill_f32(v_f, v, nv, ident, 1.0);
+    float *la_f = malloc(nq * 4), *be_f = malloc(nq * 4), *ga_f = malloc(nt * 4);
+    double *la = malloc(nq * 8), *be = malloc(nq * 8), *ga = malloc(nt * 8);
+    fill_f32(la_f, la, nq, neg_softplus, 1.0);
+    fill_f32(be_f, be, nq, sigmoid, 1.0);
+    fill_f32(ga_f, ga, nt, sigmoid, 1.0);
+    float *s0_f = malloc(ns * 4), *a0_f = malloc(na * 4), *dO_f = malloc(nv * 4), *dST_f = malloc(ns * 4);
+    double *s0 = malloc(ns * 8), *a0 = malloc(na * 8), *dO = malloc(nv * 8), *dST = malloc(ns * 8);
+    fill_f32(s0_f, s0, ns, ident, 0.1);
+    for (long i = 0; i < na; ++i) { a0_f[i] = (float)(0.5 + uniform01()); a0[i] = a0_f[i]; }
+    fill_f32(dO_f, dO, nv, ident, 1.0);
+    fill_f32(dST_f, dST, ns, ident, 1.0);
+
+    pdn_chunk_bwd_args a;
+    memset(&a, 0, sizeof a);
+    a.fwd.B = B; a.fwd.H = H; a.fwd.T = T; a.fwd.dk = dk; a.fwd.dv = dv;
+    a.fwd.qkv_dtype = PDN_F32;
+    a.fwd.o_dtype = PDN_F32;
+    a.fwd.q = dcopy(q_f, nq * 4); a.fwd.k = dcopy(k_f, nq * 4); a.fwd.v = dcopy(v_f, nv * 4);
+    a.fwd.alpha_mode = PDN_ALPHA_VEC; a.fwd.log_alpha = dcopy(la_f, nq * 4);
+    a.fwd.beta_mode = PDN_GATE_VEC; a.fwd.beta = dcopy(be_f, nq * 4);
+    a.fwd.gamma_mode = PDN_GATE_SCALAR; a.fwd.gamma = dcopy(ga_f, nt * 4);
+    a.fwd.key_mode = PDN_KEY_WRITE_GATE;
+    a.fwd.precond_eps = 1e-6f;
+    a.fwd.precond_mode = PDN_PRECOND_INVERSE;
+    a.fwd.precond_A0 = dcopy(a0_f, na * 4);
+    a.fwd.S0 = dcopy(s0_f, ns * 4);
+    a.dO = dcopy(dO_f, nv * 4);
+    a.dST = dcopy(dST_f, ns * 4);
+    a.dq = dmalloc(nq * 4); a.dk = dmalloc(nq * 4); a.dv = dmalloc(nv * 4);
+    a.dlog_alpha = dmalloc(nq * 4); a.dbeta = dmalloc(nq * 4); a.dgamma = dmalloc(nt * 4);
+    a.dS0 = dmalloc(ns * 4); a.dA0 = dmalloc(na * 4);
+    size_t ws = 0;
+    expect_code("backward workspace size", pdn_chunk_bwd_workspace_size(&a, &ws), PDN_OK);
+    a.workspace = dmalloc(ws);
+    a.workspace_bytes = ws - 1;
+    expect_code("pdn_chunk_bwd with a workspace one byte short", pdn_chunk_bwd(&a, st), PDN_EWORKSPACE);
+    a.workspace_bytes = ws;
+    a.fwd.precond_mode = PDN_PRECOND_STABILISED;
+    a.fwd.precond_x = 1.5f;
+    expect_code("pdn_chunk_bwd, stabilised preconditioner", pdn_chunk_bwd(&a, st), PDN_EUNSUPPORTED);
+    a.fwd.precond_mode = PDN_PRECOND_INVERSE;
+    expect_code("pdn_chunk_bwd (vector gates, write gate, preconditioner)", pdn_chunk_bwd(&a, st), PDN_OK);
+    HIP_CHECK(hipStreamSynchronize(st));
+
+    double *r_dq = malloc(nq * 8), *r_dk = malloc(nq * 8), *r_dv = malloc(nv * 8);
+    double *r_dla = malloc(nq * 8), *r_dbe = malloc(nq * 8), *r_dga = malloc(nt * 8);
+    double *r_dS0 = malloc(ns * 8), *r_dA0 = malloc(na * 8);
+    if (oracle_delta_rule_bwd(B, H, T, dk, dv, q, k, v, PDN_ALPHA_VEC, la, PDN_GATE_VEC, be,
+                              PDN_GATE_SCALAR, ga, 1e-6, a0, s0, PDN_KEY_WRITE_GATE,
+                              PDN_PRECOND_INVERSE, 1.5, dO, dST, r_dq, r_dk, r_dv, r_dla, r_dbe,
+                              r_dga, r_dS0, r_dA0) != 0) {
+        printf("oracle backward failed  FAIL\n");
+        ++failures;
+        return;
+    }
+    struct { const char *name; void *dev; const double *ref; long n; } g[] = {
+        {"  dq vs oracle", a.dq, r_dq, nq}, {"  dk vs oracle", a.dk, r_dk, nq},
+        {"  dv vs oracle", a.dv, r_dv, nv}, {"  d log alpha vs oracle", a.dlog_alpha, r_dla, nq},
+        {"  dbeta vs oracle", a.dbeta, r_dbe, nq}, {"  dgamma vs oracle", a.dgamma, r_dga, nt},
+        {"  dS0 vs oracle", a.dS0, r_dS0, ns}, {"  dA0 vs oracle", a.dA0, r_dA0, na}};
+    float *h = malloc(nq * 4);
+    for (int j = 0; j < 8; ++j) {
+        HIP_CHECK(hipMemcpy(h, g[j].dev, g[j].n * 4, hipMemcpyDeviceToHost));
+        /* fp32 arithmetic throughout; the start sum keeps the preconditioner well conditioned */
+        check(g[j].name, rel_l2(g[j].ref, h, g[j].n), 1e-5);
+        hipFree(g[j].dev);
+    }
+    free(h);
+    hipFree((void *)a.fwd.q); hipFree((void *)a.fwd.k); hipFree((void *)a.fwd.v);
+    hipFree((void *)a.fwd.log_alpha); hipFree((void *)a.fwd.beta); hipFree((void *)a.fwd.gamma);
+    hipFree((void *)a.fwd.precond_A0); hipFree((void *)a.fwd.S0);
+    hipFree((void *)a.dO); hipFree((void *)a.dST); hipFree(a.workspace);
+    free(q_f); free(k_f); free(v_f); free(q); free(k); free(v); free(la_f); free(be_f); free(ga_f);
+    free(la); free(be); free(ga); free(s0_f); free(a0_f); free(dO_f); free(dST_f); free(s0); free(a0);
+    free(dO); free(dST); free(r_dq); free(r_dk); free(r_dv); free(r_dla); free(r_dbe); free(r_dga);
+    free(r_dS0); free(r_dA0);
+}
+
 int main(void) {
     int ndev = 0;
     HIP_CHECK(hipGetDeviceCount(&ndev));
@@ -301,6 +408,7 @@ int main(void) {
     prefill_case(1, st);
     prefill_case(0, st);
     decode_case(st);
+    bwd_case(st);
     HIP_CHECK(hipStreamDestroy(st));
     printf("%s\n", failures ? "FAILED" : "all C-ABI checks passed");
     return failures ? 1 : 0;
