@@ -60,6 +60,8 @@ struct BwdParams {
     const float* gamma;
     float eps;
     int pre;
+    int stab;   // stabilised preconditioner coefficient x^-(r / (1 + |r|))
+    float lnx;  // ln x of that coefficient
     const float* A0;
     const float* S0;
     const float* dO;
@@ -84,6 +86,7 @@ struct BwdParams {
     float* dAin;   // [BH][nc*BC][DK] in-chunk suffix sums of dA
     float* dAc;    // [BH][nc][DK] chunk totals of dA
     float* dAsuf;  // [BH][nc][DK] sums of dA over the later chunks
+    float* mu;     // [BH][nc*BC] stabilised mode: channel mean of ln(A + eps) per token
 };
 
 // record of one chunk: Kg, Qg, Kd [BC][DK]; Vw [BC][dv]; M, P [BC][BC]; e^G_C [DK]
@@ -235,7 +238,7 @@ __global__ void __launch_bounds__(DK) bwd_kscan_kernel(BwdParams p) {
 // and P_rs = sum_i (q L)_ri (kw R)_si on the two diagonal 16 x 16 blocks; the
 // block below the diagonal uses (kw R c)_s with c = e^(G_24 - G_8), since
 // e^(G_r - G_s) = L_r c R_s there.
-template <int DK, bool BF16>
+template <int DK, bool BF16, bool STAB>
 __global__ void __launch_bounds__(NT, 2) bwd_prep_kernel(BwdParams p) {
     constexpr int LS = DK + 4;  // read as [row][k]
     __shared__ float sKrL[BC][LS];
@@ -249,10 +252,10 @@ __global__ void __launch_bounds__(NT, 2) bwd_prep_kernel(BwdParams p) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int ln = lane & 15, g4 = lane >> 4;
     float* R = p.rec + (bh * p.nc + c) * rec_floats<DK>(p.dv);
+    const int i = tid;
+    // every load of the column first, then the scans
+    float kk[BC], qq[BC], la[BC], bb[BC];
     if (tid < DK) {
-        const int i = tid;
-        // every load of the column first, then the scans
-        float kk[BC], qq[BC], la[BC], bb[BC];
 #pragma unroll
         for (int r = 0; r < BC; ++r) {
             const long t = t0 + r;
@@ -261,6 +264,29 @@ __global__ void __launch_bounds__(NT, 2) bwd_prep_kernel(BwdParams p) {
             la[r] = tok_la<DK>(p, bh, t, i);
             bb[r] = tok_beta<DK>(p, bh, t, i);
         }
+    }
+    __shared__ float sMu[BC];
+    if constexpr (STAB) {
+        // the channel mean of ln(A + eps) per token (sKrL holds ln(A + eps) for now)
+        if (tid < DK) {
+            float A = p.apre[(bh * p.nc + c) * DK + i];
+#pragma unroll
+            for (int r = 0; r < BC; ++r) {
+                A += kk[r] * kk[r];
+                sKrL[r][i] = logf(A + p.eps);
+            }
+        }
+        __syncthreads();
+        if (tid < BC) {
+            float m = 0.f;
+            for (int ii = 0; ii < DK; ++ii) m += sKrL[tid][ii];
+            m *= 1.f / DK;
+            sMu[tid] = m;
+            p.mu[bh * static_cast<long>(p.nc) * BC + t0 + tid] = m;
+        }
+        __syncthreads();
+    }
+    if (tid < DK) {
         float G = 0.f;
         float A = p.pre ? p.apre[(bh * p.nc + c) * DK + i] : 0.f;
         float kr[BC], kw[BC], g[BC];
@@ -271,7 +297,12 @@ __global__ void __launch_bounds__(NT, 2) bwd_prep_kernel(BwdParams p) {
             float b = bb[r];
             if (p.pre) {
                 A += kk[r] * kk[r];
-                b = b / (A + p.eps);
+                if constexpr (STAB) {
+                    const float x = logf(A + p.eps) - sMu[r];
+                    b = b * __expf(-(x / (1.f + fabsf(x))) * p.lnx);
+                } else {
+                    b = b / (A + p.eps);
+                }
             }
             keys_of(p.kmode, b, kk[r], kw[r], kr[r]);
         }
@@ -782,6 +813,8 @@ __global__ void __launch_bounds__(NT, 2) bwd_gates_kernel(BwdParams p) {
     __shared__ float sX[NH][4][DK];  // per-part partial sums exchanged between the parts of a channel
     __shared__ float sRef[3][DK];    // G_8, G_24, G_C of each channel
     __shared__ float sRowG[BC];      // row sums of dgamma'
+    __shared__ float sMu[BC];        // stabilised mode: channel mean of ln(A + eps) per row
+    __shared__ float sDrm[BC];       // stabilised mode: channel mean of dr per row
     float(*sW)[OS] = reinterpret_cast<float(*)[OS]>(sbuf);
     float(*sRk)[OS] = reinterpret_cast<float(*)[OS]>(sbuf + BC * OS);
     float(*sRq)[OS] = reinterpret_cast<float(*)[OS]>(sbuf + 2 * BC * OS);
@@ -798,6 +831,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_gates_kernel(BwdParams p) {
     const int ln = lane & 15, g4 = lane >> 4;
     const long Tp = static_cast<long>(p.nc) * BC;
     const float* D = p.dgr + (bh * p.nc + c) * dgr_floats<DK>();
+    if (p.pre && p.stab && tid < BC) sMu[tid] = p.mu[bh * Tp + t0 + tid];
     {
         constexpr int PER = BC * BC / NT;
         float tv[PER], pv[PER];
@@ -917,24 +951,33 @@ __global__ void __launch_bounds__(NT, 2) bwd_gates_kernel(BwdParams p) {
         __syncthreads();
     }
     const float G8 = sRef[0][i], G24 = sRef[1][i], Gc = sRef[2][i];
-    // erase gain with the preconditioner folded in, advancing the running sum
-    auto gain_at = [&](int u, float& A, float& ainv) {
+    // erase gain with the preconditioner folded in, advancing the running sum;
+    // aux is the coefficient (1 / (A + eps), or x^-(r / (1 + |r|)) in the
+    // stabilised mode, where den = 1 + |r|)
+    auto gain_at = [&](int u, float& A, float& aux, float& den) {
         float b = bb[u];
-        ainv = 1.f;
+        aux = 1.f;
+        den = 1.f;
         if (p.pre) {
             A += kk[u] * kk[u];
-            ainv = 1.f / (A + p.eps);
-            b = b * ainv;
+            if (p.stab) {
+                const float x = logf(A + p.eps) - sMu[r0 + u];
+                den = 1.f + fabsf(x);
+                aux = __expf(-(x / den) * p.lnx);
+            } else {
+                aux = 1.f / (A + p.eps);
+            }
+            b = b * aux;
         }
         return b;
     };
     {
-        float A = Ain, ainv;
+        float A = Ain, aux, den;
 #pragma unroll
         for (int u = 0; u < RPT; ++u) {
             const int r = r0 + u;
             float kwr, krr;
-            keys_of(p.kmode, gain_at(u, A, ainv), kk[u], kwr, krr);
+            keys_of(p.kmode, gain_at(u, A, aux, den), kk[u], kwr, krr);
             const float gm = r < 16 ? G8 : G24;
             const float L = __expf(G[u] - gm), R = __expf(gm - G[u]);
             sW[r][i] = kwr * R;
@@ -1018,12 +1061,12 @@ __global__ void __launch_bounds__(NT, 2) bwd_gates_kernel(BwdParams p) {
             dkg[u] = DdKg[(r0 + u) * DK];
             dkd[u] = DdKd[(r0 + u) * DK];
         }
-        float A = Ain, ainv;
+        float A = Ain, aux, den;
 #pragma unroll
         for (int u = 0; u < RPT; ++u) {
             const int r = r0 + u;
             float kwr, krr;
-            keys_of(p.kmode, gain_at(u, A, ainv), kk[u], kwr, krr);
+            keys_of(p.kmode, gain_at(u, A, aux, den), kk[u], kwr, krr);
             const float gm = r < 16 ? G8 : G24;
             const float L = __expf(G[u] - gm), R = __expf(gm - G[u]);
             const float A1 = L * sA1[r][i], A3 = L * sA3[r][i];
@@ -1071,15 +1114,16 @@ __global__ void __launch_bounds__(NT, 2) bwd_gates_kernel(BwdParams p) {
             if (p.amode == PDN_ALPHA_VEC && t < p.T) p.dla[(bh * p.T + t) * DK + i] = dla;
             sA4[r][i] = dla;
         }
-        // keys to k and the gains; the preconditioner's dA
-        float A = Ain, ainv;
+        // keys to k and the gains; the preconditioner's dA (the stabilised mode
+        // first leaves dr in A2 for its channel mean)
+        float A = Ain, aux, den;
         float dAsum = 0.f;
 #pragma unroll
         for (int u = 0; u < RPT; ++u) {
             const int r = r0 + u;
             const long t = t0 + r;
             const float braw = bb[u];
-            const float b = gain_at(u, A, ainv);
+            const float b = gain_at(u, A, aux, den);
             const float dkwr = sA3[r][i], dkrr = sA1[r][i];
             float dkk, db;
             if (p.kmode == PDN_KEY_SYMMETRIC) {
@@ -1095,8 +1139,13 @@ __global__ void __launch_bounds__(NT, 2) bwd_gates_kernel(BwdParams p) {
             }
             float dA = 0.f;
             if (p.pre) {
-                dA = -db * braw * ainv * ainv;
-                db *= ainv;
+                if (p.stab) {
+                    // B = x^-s, s = x_r / (1 + |x_r|), x_r = ln(A + eps) - mean
+                    sA2[r][i] = -db * braw * aux * p.lnx / (den * den);
+                } else {
+                    dA = -db * braw * aux * aux;
+                }
+                db *= aux;
             }
             if (p.gmode == PDN_GAMMA_SAME_AS_BETA && p.bmode == PDN_GATE_VEC && t < p.T) {
                 // beta also scales the value of column i (dk == dv)
@@ -1115,6 +1164,26 @@ __global__ void __launch_bounds__(NT, 2) bwd_gates_kernel(BwdParams p) {
         if (p.pre) sX[h][0][i] = dAsum;
     }
     __syncthreads();
+    if (p.pre && p.stab) {
+        // dl = dr - mean over channels of dr; dA = dl / (A + eps)
+        if (tid < BC) {
+            float m = 0.f;
+            for (int ii = 0; ii < DK; ++ii) m += sA2[tid][ii];
+            sDrm[tid] = m * (1.f / DK);
+        }
+        __syncthreads();
+        float A = Ain, dAsum = 0.f;
+#pragma unroll
+        for (int u = 0; u < RPT; ++u) {
+            const int r = r0 + u;
+            A += kk[u] * kk[u];
+            const float dA = (sA2[r][i] - sDrm[r]) / (A + p.eps);
+            sA3[r][i] = dA;
+            dAsum += dA;
+        }
+        sX[h][0][i] = dAsum;
+        __syncthreads();
+    }
     if (p.pre) {
         float suf = 0.f;
         for (int h2 = h + 1; h2 < NH; ++h2) suf += sX[h2][0][i];
@@ -1197,7 +1266,7 @@ __global__ void bwd_copy_kernel(float* dst, const float* src, long n) {
 // host side
 // ---------------------------------------------------------------------------
 struct BwdLayout {
-    size_t rec, st, dst, U, Z, dgr, apre, ksum, dAin, dAc, dAsuf, end;
+    size_t rec, st, dst, U, Z, dgr, apre, ksum, dAin, dAc, dAsuf, mu, end;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -1228,6 +1297,7 @@ BwdLayout bwd_layout(const pdn_chunk_bwd_args& a) {
     L.dAin = take(pre ? nbh * nc * BC * dk : 0);
     L.dAc = take(pre ? nbh * nc * dk : 0);
     L.dAsuf = take(pre ? nbh * nc * dk : 0);
+    L.mu = take(pre && f.precond_mode == PDN_PRECOND_STABILISED ? nbh * nc * BC : 0);
     L.end = o;
     return L;
 }
@@ -1242,7 +1312,8 @@ hipError_t run_bwd(const pdn_chunk_bwd_args& a, const BwdParams& p, hipStream_t 
         bwd_ksum_kernel<DK, BF16><<<nch, DK, 0, s>>>(p);
         bwd_kscan_kernel<DK><<<nbh, DK, 0, s>>>(p);
     }
-    bwd_prep_kernel<DK, BF16><<<nch, NT, 0, s>>>(p);
+    if (p.stab) bwd_prep_kernel<DK, BF16, true><<<nch, NT, 0, s>>>(p);
+    else bwd_prep_kernel<DK, BF16, false><<<nch, NT, 0, s>>>(p);
     bwd_state_fwd_kernel<DK><<<ntl, NT, 0, s>>>(p);
     bwd_state_bwd_kernel<DK><<<ntl, NT, 0, s>>>(p);
     bwd_dgrad_kernel<DK><<<nch, NT, 0, s>>>(p);
@@ -1289,6 +1360,8 @@ hipError_t launch_chunk_bwd(const pdn_chunk_bwd_args& a, hipStream_t stream) {
     p.gamma = f.gamma;
     p.eps = f.precond_eps;
     p.pre = f.precond_eps >= 0.0f;
+    p.stab = p.pre && f.precond_mode == PDN_PRECOND_STABILISED;
+    p.lnx = p.stab ? logf(f.precond_x) : 0.f;
     p.A0 = f.precond_A0;
     p.S0 = f.S0;
     p.dO = a.dO;
@@ -1315,6 +1388,7 @@ hipError_t launch_chunk_bwd(const pdn_chunk_bwd_args& a, hipStream_t stream) {
     p.dAin = at(L.dAin);
     p.dAc = at(L.dAc);
     p.dAsuf = at(L.dAsuf);
+    p.mu = at(L.mu);
     const bool bf = f.qkv_dtype == PDN_BF16;
     if (f.dk == 128) return bf ? run_bwd<128, true>(a, p, stream) : run_bwd<128, false>(a, p, stream);
     return bf ? run_bwd<64, true>(a, p, stream) : run_bwd<64, false>(a, p, stream);

@@ -122,7 +122,6 @@ int check_bwd(const pdn_chunk_bwd_args* a) {
         if (ptr && !aligned16(ptr)) return PDN_EINVAL;
     if (f.dk != 64 && f.dk != 128) return PDN_EUNSUPPORTED;
     if (f.dv % 32 != 0 || f.dv > 256) return PDN_EUNSUPPORTED;
-    if (f.precond_eps >= 0.0f && f.precond_mode != PDN_PRECOND_INVERSE) return PDN_EUNSUPPORTED;
     const size_t need = pdn::chunk_bwd_workspace_bytes(*a);
     if (need > 0 && (!a->workspace || a->workspace_bytes < need)) return PDN_EWORKSPACE;
     return PDN_OK;

@@ -206,7 +206,7 @@ typedef struct pdn_decode_args {
  * previous pdn_chunk_fwd is needed.
  *
  *   fwd               the forward's arguments: sizes, q, k, v, gates, key_mode,
- *                     preconditioner (inverse mode only), precond_A0, S0.  Its
+ *                     preconditioner (both modes), precond_A0, S0.  Its
  *                     o, ST, precond_AT, workspace and workspace_bytes are
  *                     ignored.  q/k/v fp32 or bf16; dk in {64, 128}; dv a
  *                     multiple of 32 and <= 256.  log_alpha is clamped at -10

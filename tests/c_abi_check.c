@@ -13,7 +13,7 @@
  *      preconditioner with a start sum, a start state and dST): every
  *      gradient against the oracle's backward;
  *   5. error paths: a workspace one byte short (prefill and backward), an
- *      unknown key mode, the stabilised preconditioner in the backward.
+ *      unknown key mode, an unsupported value width in the backward.
  *
  * Inputs come from a counter-based generator (splitmix64 of a running index),
  * rounded to bf16 where the GPU reads bf16, and the same values (widened to
@@ -356,10 +356,9 @@ static void bwd_case(hipStream_t st) {
     a.workspace_bytes = ws - 1;
     expect_code("pdn_chunk_bwd with a workspace one byte short", pdn_chunk_bwd(&a, st), PDN_EWORKSPACE);
     a.workspace_bytes = ws;
-    a.fwd.precond_mode = PDN_PRECOND_STABILISED;
-    a.fwd.precond_x = 1.5f;
-    expect_code("pdn_chunk_bwd, stabilised preconditioner", pdn_chunk_bwd(&a, st), PDN_EUNSUPPORTED);
-    a.fwd.precond_mode = PDN_PRECOND_INVERSE;
+    a.fwd.dv = 48;
+    expect_code("pdn_chunk_bwd with dv = 48", pdn_chunk_bwd(&a, st), PDN_EUNSUPPORTED);
+    a.fwd.dv = dv;
     expect_code("pdn_chunk_bwd (vector gates, write gate, preconditioner)", pdn_chunk_bwd(&a, st), PDN_OK);
     HIP_CHECK(hipStreamSynchronize(st));
 

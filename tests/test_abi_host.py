@@ -368,7 +368,7 @@ BWD_BAD = [
     (lambda a: setattr(a.fwd, "dv", 288), pdn.PDN_EUNSUPPORTED),
     (lambda a: (setattr(a.fwd, "precond_eps", 1e-6),
                 setattr(a.fwd, "precond_mode", pdn.PDN_PRECOND_STABILISED),
-                setattr(a.fwd, "precond_x", 1.5)), pdn.PDN_EUNSUPPORTED),
+                setattr(a.fwd, "precond_x", 2.5)), pdn.PDN_EINVAL),              # x out of (1, 2]
     (lambda a: setattr(a, "workspace_bytes", 1000), pdn.PDN_EWORKSPACE),
     (lambda a: setattr(a, "workspace", None), pdn.PDN_EWORKSPACE),
     (lambda a: setattr(a.fwd, "T", -1), pdn.PDN_EINVAL),
@@ -386,6 +386,10 @@ def test_bwd_valid_arguments(lib):
     for km in (0, 1, 2):
         a.fwd.key_mode = km
         assert _bcheck(lib, a) == pdn.PDN_OK
+    # the stabilised preconditioner
+    a.fwd.precond_mode, a.fwd.precond_x = pdn.PDN_PRECOND_STABILISED, 1.5
+    assert _bcheck(lib, a) == pdn.PDN_OK
+    a.fwd.precond_mode = pdn.PDN_PRECOND_INVERSE
     # no decay: no d log alpha needed
     a.fwd.alpha_mode, a.fwd.log_alpha, a.dlog_alpha = pdn.PDN_ALPHA_NONE, None, None
     assert _bcheck(lib, a) == pdn.PDN_OK
@@ -422,6 +426,10 @@ def test_bwd_workspace_size(lib):
     rc, n2 = _bws(lib, a)
     assert rc == pdn.PDN_OK
     assert n2 - n == 4 * al(nbh * nc * dk * 4) + al(nbh * nc * 32 * dk * 4)
+    # the stabilised preconditioner adds the per-token channel means [B,H,chunks*32]
+    a.fwd.precond_mode, a.fwd.precond_x = pdn.PDN_PRECOND_STABILISED, 1.5
+    rc, n3 = _bws(lib, a)
+    assert rc == pdn.PDN_OK and n3 - n2 == al(nbh * nc * 32 * 4)
     # T = 0 needs none
     a.fwd.T = 0
     assert _bws(lib, a) == (pdn.PDN_OK, 0)

@@ -36,7 +36,8 @@ pytestmark = pytest.mark.gpu
 GRADS = ("dq", "dk", "dv", "dlog_alpha", "dbeta", "dgamma", "dS0", "dA0")
 
 
-def run_bwd(w, dO, dST, key_mode=0, A0=None, want_dS0=True, want_dA0=True, workspace=None):
+def run_bwd(w, dO, dST, key_mode=0, A0=None, want_dS0=True, want_dA0=True, workspace=None,
+            precond_mode=0):
     """pdn_chunk_bwd on a synth.Workload; returns a dict of numpy gradients."""
     import gated_delta_rule_77_amd as pdn
     torch = torch_mod()
@@ -59,15 +60,17 @@ def run_bwd(w, dO, dST, key_mode=0, A0=None, want_dS0=True, want_dA0=True, works
                       dS0=out["dS0"], dA0=out["dA0"], log_alpha=la, beta=be, gamma=ga,
                       precond_eps=(w.precond_eps if pre else None),
                       precond_A0=dev(A0) if (pre and A0 is not None) else None,
-                      S0=dev(w.S0), dST=dev(dST), key_mode=key_mode, workspace=workspace)
+                      S0=dev(w.S0), dST=dev(dST), key_mode=key_mode, workspace=workspace,
+                      precond_mode=precond_mode, precond_x=1.5)
     torch.cuda.synchronize()
     return {n: (host(t) if t is not None else None) for n, t in out.items()}
 
 
-def ref_bwd(w, dO, dST, key_mode=0, A0=None):
+def ref_bwd(w, dO, dST, key_mode=0, A0=None, precond_mode=0):
     return oracle.delta_rule_bwd(w.q, w.k, w.v, w.alpha_mode, w.log_alpha, w.beta_mode,
                                  w.beta, w.gamma_mode, w.gamma, dO, dST, w.precond_eps, A0,
-                                 w.S0, key_mode=key_mode)
+                                 w.S0, key_mode=key_mode, precond_mode=precond_mode,
+                                 precond_x=1.5)
 
 
 def compare(name, g, ref, tol, skip=()):
@@ -85,11 +88,11 @@ def compare(name, g, ref, tol, skip=()):
     return errs
 
 
-def conditioning_tol(w, dO, dST, key_mode=0, A0=None, draws=3):
+def conditioning_tol(w, dO, dST, key_mode=0, A0=None, draws=3, precond_mode=0):
     """Per-gradient bound max(1e-5, 16 f), f = the oracle's own relative change
     under 2^-24 relative perturbations of every input."""
     rng = np.random.default_rng(12345)
-    ref = ref_bwd(w, dO, dST, key_mode=key_mode, A0=A0)
+    ref = ref_bwd(w, dO, dST, key_mode=key_mode, A0=A0, precond_mode=precond_mode)
     f = {n: 0.0 for n in GRADS}
     pert = lambda x: None if x is None else x.astype(np.float64) * (
         1.0 + 2.0 ** -24 * rng.standard_normal(x.shape))
@@ -98,19 +101,20 @@ def conditioning_tol(w, dO, dST, key_mode=0, A0=None, draws=3):
                             pert(w.v), w.alpha_mode, pert(w.log_alpha), w.beta_mode, pert(w.beta),
                             w.gamma_mode, pert(w.gamma), precond_eps=w.precond_eps, A0=w.A0,
                             S0=pert(w.S0))
-        rp = ref_bwd(wp, pert(dO), pert(dST), key_mode=key_mode, A0=pert(A0))
+        rp = ref_bwd(wp, pert(dO), pert(dST), key_mode=key_mode, A0=pert(A0),
+                     precond_mode=precond_mode)
         for n in GRADS:
             if ref[n] is not None:
                 f[n] = max(f[n], rel_l2(rp[n], ref[n]))
     return ref, {n: max(TOL_F32, 16.0 * v) for n, v in f.items()}
 
 
-def check_bwd(name, w, key_mode=0, A0=None, seed=1, with_dST=True):
+def check_bwd(name, w, key_mode=0, A0=None, seed=1, with_dST=True, precond_mode=0):
     dO, dST = synth.upstream_grads(w, seed)
     if not with_dST:
         dST = None
-    g = run_bwd(w, dO, dST, key_mode=key_mode, A0=A0)
-    ref, tol = conditioning_tol(w, dO, dST, key_mode=key_mode, A0=A0)
+    g = run_bwd(w, dO, dST, key_mode=key_mode, A0=A0, precond_mode=precond_mode)
+    ref, tol = conditioning_tol(w, dO, dST, key_mode=key_mode, A0=A0, precond_mode=precond_mode)
     return compare(name, g, ref, tol)
 
 
@@ -162,6 +166,27 @@ def test_bwd_bf16_dk128(key_mode, pre):
     w = rand_workload(200 + key_mode, 2, 2, 200, 128, 128, synth.ALPHA_VEC, synth.GATE_VEC,
                       synth.GATE_VEC, pre, True)
     check_bwd("bwd bf16 d128 key%d pre%d T200" % (key_mode, pre), w, key_mode=key_mode)
+
+
+@pytest.mark.parametrize("key_mode", [0, 1, 2])
+@pytest.mark.parametrize("amode,bmode,gmode", [
+    (synth.ALPHA_VEC, synth.GATE_VEC, synth.GATE_VEC),
+    (synth.ALPHA_SCALAR, synth.GATE_SCALAR, synth.GAMMA_SAME_AS_BETA),
+    (synth.ALPHA_NONE, synth.GATE_VEC, synth.GATE_SCALAR)])
+def test_bwd_stabilised_fp32(amode, bmode, gmode, key_mode):
+    """The stabilised preconditioner (x = 1.5), fp32 inputs, dk = dv = 64, T = 97."""
+    w = rand_workload(400 + 7 * key_mode + amode, 1, 2, 97, 64, 64, amode, bmode, gmode, True, False)
+    check_bwd("bwd stabilised a%d b%d g%d key%d fp32 T97" % (amode, bmode, gmode, key_mode), w,
+              key_mode=key_mode, precond_mode=1)
+
+
+@pytest.mark.parametrize("key_mode", [0, 1, 2])
+def test_bwd_stabilised_gdn2_small(key_mode):
+    """The stabilised preconditioner on the GDN-2 workload (bf16, d = 128), with A0."""
+    w = synth.gdn2_precond(B=1, H=2, T=300, d=128, seed=13, n_pairs=8)
+    A0 = np.random.default_rng(14).uniform(0.5, 2.0, (1, 2, 128)).astype(np.float32)
+    check_bwd("bwd stabilised gdn2_precond key%d B1 H2 T300 (A0)" % key_mode, w, key_mode=key_mode,
+              A0=A0, precond_mode=1)
 
 
 def test_bwd_deltanet_fp32_config():
