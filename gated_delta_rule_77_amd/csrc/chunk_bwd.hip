@@ -26,14 +26,15 @@
 //   bwd_state_bwd          same, chunks in reverse: dS' per chunk, Z, dS0
 //   bwd_dgrad              per chunk: the dv contractions (dQg, dKg, dKd, dP,
 //                          dT, dGamma_C), fp32 16x16x4 MFMAs
-//   bwd_gates              per chunk and key channel: dq, dk, dv, d log alpha,
+//   bwd_gates              per chunk: the pairwise sums (MFMA), then dq, dk, dv, d log alpha,
 //                          dbeta, dgamma, and the preconditioner's dA
 //   bwd_dA_scan / bwd_dA_apply   preconditioner: dk += 2 k (.) sum_{s>=t} dA_s
 //
 // Every product is an fp32 MFMA (exact fp32 products, fp32 accumulation) or
-// fp32 VALU; the pairwise decays are exact exponentials, so no clamp-driven
-// splitting is needed here (log alpha is still clamped at -10 as in the
-// forward, with zero gradient where it clamps).
+// fp32 VALU.  The pairwise decays e^(G_r - G_s) inside a chunk enter the MFMA
+// products split at a reference row (the middle of each 16-token block, or
+// the block boundary), which the clamp of log alpha at -10 keeps within the
+// fp32 range; the gradient of log alpha is zero where the clamp acts.
 #include "common.h"
 #include "kernels.h"
 
@@ -129,10 +130,6 @@ __device__ __forceinline__ float tok_la(const BwdParams& p, long bh, long t, int
     const float x = tok_la_raw<DK>(p, bh, t, i);
     return (t < p.T && p.amode != PDN_ALPHA_NONE) ? fmaxf(x, kLogAlphaMin) : 0.f;
 }
-// whether d log alpha is zero there (no decay, beyond T, or clamped)
-__device__ __forceinline__ bool la_dead(const BwdParams& p, long t, float raw) {
-    return !(t < p.T && p.amode != PDN_ALPHA_NONE) || raw < kLogAlphaMin;
-}
 // raw erase gain (1 beyond T, so that padded rows carry finite zero gradients)
 template <int DK>
 __device__ __forceinline__ float tok_beta(const BwdParams& p, long bh, long t, int i) {
@@ -182,11 +179,6 @@ __device__ __forceinline__ float value_dscale(int kmode, int gmode, float g) {
     if (kmode == PDN_KEY_SYMMETRIC) return 0.5f / sqrtf(g);
     if (kmode == PDN_KEY_WRITE_GATE && gmode == PDN_GAMMA_SAME_AS_BETA) return 0.f;
     return 1.f;
-}
-
-template <bool BF16>
-__device__ __forceinline__ float ld(const void* p, long i) {
-    return load_in<BF16>(p, i);
 }
 
 // ---------------------------------------------------------------------------
@@ -1250,7 +1242,7 @@ __global__ void __launch_bounds__(NT) bwd_dA_apply_kernel(BwdParams p) {
         const int r = idx / DK, i = idx % DK;
         const long t = c * BC + r;
         if (t >= p.T) continue;
-        const float kk = ld<BF16>(p.k, (bh * p.T + t) * DK + i);
+        const float kk = load_in<BF16>(p.k, (bh * p.T + t) * DK + i);
         p.dk[(bh * p.T + t) * DK + i] +=
             2.f * kk * (p.dAin[(bh * Tp + t) * DK + i] + p.dAsuf[(bh * p.nc + c) * DK + i]);
     }
