@@ -7,7 +7,7 @@
   launch configuration on sampled (batch, head) pairs that the oracle
   recomputes over the whole sequence;
 * edge cases: T = 0, 1, 31, 32, 33; no dST; no S0; dv 32 and 256; the
-  preconditioner's A0;
+  preconditioner's A0; bf16 at dk = 64; 4096 (b, h) pairs in one call;
 * properties at full size: Euler's identity sum v dv + sum S0 dS0 = L for the
   loss L = <dO, o> + <dST, S_T> of the GPU forward, and bitwise determinism.
 
@@ -187,6 +187,28 @@ def test_bwd_stabilised_gdn2_small(key_mode):
     A0 = np.random.default_rng(14).uniform(0.5, 2.0, (1, 2, 128)).astype(np.float32)
     check_bwd("bwd stabilised gdn2_precond key%d B1 H2 T300 (A0)" % key_mode, w, key_mode=key_mode,
               A0=A0, precond_mode=1)
+
+
+@pytest.mark.parametrize("pre", [False, True])
+def test_bwd_bf16_dk64(pre):
+    """bf16 inputs at dk = dv = 64 (the remaining kernel instantiation), vector gates."""
+    w = rand_workload(500 + pre, 2, 2, 150, 64, 64, synth.ALPHA_VEC, synth.GATE_VEC,
+                      synth.GATE_SCALAR, pre, True)
+    check_bwd("bwd bf16 d64 pre%d T150" % pre, w)
+
+
+def test_bwd_large_grid():
+    """4096 (b, h) pairs of 40 tokens (two chunks, the second ragged), dk = dv = 64:
+    the per-chunk grids reach 8192 workgroups; sampled pairs against the oracle."""
+    w = rand_workload(600, 64, 64, 40, 64, 64, synth.ALPHA_VEC, synth.GATE_VEC, synth.GATE_SCALAR,
+                      True, True)
+    dO, dST = synth.upstream_grads(w, 3)
+    g = run_bwd(w, dO, dST)
+    for b, h in [(0, 0), (17, 41), (63, 63)]:
+        ws = sub(w, b, h)
+        ref = ref_bwd(ws, dO[b:b + 1, h:h + 1], dST[b:b + 1, h:h + 1])
+        gs = {n: (None if g[n] is None else g[n][b:b + 1, h:h + 1]) for n in GRADS}
+        compare("bwd large grid B64 H64 T40 (b=%d,h=%d)" % (b, h), gs, ref, TOL_F32)
 
 
 def test_bwd_deltanet_fp32_config():
