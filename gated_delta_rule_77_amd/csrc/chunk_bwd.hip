@@ -422,19 +422,28 @@ struct Tile4 {
     }
 };
 
+// LDS of the forward state pass, in floats
 template <int DK>
-__global__ void __launch_bounds__(NT) bwd_state_fwd_kernel(BwdParams p) {
+constexpr int fwd_lds_floats() {
+    return BC * (DK + 4) + BC * (DK + 16) + BC * (BC + 4) + 2 * BC * (JT + 16) + DK * (JT + 16) + DK;
+}
+
+// forward state pass of workgroup `unit` (b, h, 32 value columns)
+template <int DK>
+__device__ __forceinline__ void state_fwd_body(const BwdParams& p, float* smem, long unit) {
     constexpr int NSB = DK / 16 * 2 / 4;  // state tiles per wave
-    __shared__ __attribute__((aligned(16))) float sKg[BC][DK + 4];   // read as [row][k]: stride 4 mod 64 banks
-    __shared__ __attribute__((aligned(16))) float sKd[BC][DK + 16];  // read as [k][col]: stride 16 mod 64
-    __shared__ __attribute__((aligned(16))) float sM[BC][BC + 4];
-    __shared__ __attribute__((aligned(16))) float sX[BC][JT + 16];
-    __shared__ __attribute__((aligned(16))) float sU[BC][JT + 16];
-    __shared__ __attribute__((aligned(16))) float sS[DK][JT + 16];
-    __shared__ __attribute__((aligned(16))) float sGc[DK];
+    // sKg read as [row][k] (stride 4 mod 64 banks); sKd read as [k][col] (stride 16 mod 64)
+    float(*sKg)[DK + 4] = reinterpret_cast<float(*)[DK + 4]>(smem);
+    float(*sKd)[DK + 16] = reinterpret_cast<float(*)[DK + 16]>(smem + BC * (DK + 4));
+    float(*sM)[BC + 4] = reinterpret_cast<float(*)[BC + 4]>(smem + BC * (DK + 4) + BC * (DK + 16));
+    float* base = smem + BC * (DK + 4) + BC * (DK + 16) + BC * (BC + 4);
+    float(*sX)[JT + 16] = reinterpret_cast<float(*)[JT + 16]>(base);
+    float(*sU)[JT + 16] = reinterpret_cast<float(*)[JT + 16]>(base + BC * (JT + 16));
+    float(*sS)[JT + 16] = reinterpret_cast<float(*)[JT + 16]>(base + 2 * BC * (JT + 16));
+    float* sGc = base + 2 * BC * (JT + 16) + DK * (JT + 16);
     const int ntile = p.dv / JT;
-    const long bh = blockIdx.x / ntile;
-    const int j0 = (blockIdx.x % ntile) * JT;
+    const long bh = unit / ntile;
+    const int j0 = static_cast<int>(unit % ntile) * JT;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int ln = lane & 15, g4 = lane >> 4;
     const long Tp = static_cast<long>(p.nc) * BC;
@@ -517,22 +526,30 @@ __global__ void __launch_bounds__(NT) bwd_state_fwd_kernel(BwdParams p) {
     }
 }
 
+// LDS of the reverse state pass, in floats.  M and P reach the MFMAs from
+// registers, Z reuses Y's buffer, and the tiles use narrow row strides (some
+// two-way bank conflicts), so that both passes fit on one CU together.
 template <int DK>
-__global__ void __launch_bounds__(NT) bwd_state_bwd_kernel(BwdParams p) {
+constexpr int bwd_lds_floats() {
+    return 3 * BC * (DK + 4) + 2 * BC * (JT + 4) + DK * (JT + 4) + DK;
+}
+
+// reverse state pass of workgroup `unit` (b, h, 32 value columns)
+template <int DK>
+__device__ __forceinline__ void state_bwd_body(const BwdParams& p, float* smem, long unit) {
     constexpr int NSB = DK / 16 * 2 / 4;
-    __shared__ __attribute__((aligned(16))) float sQg[BC][DK + 16];  // read as [k][col]
-    __shared__ __attribute__((aligned(16))) float sKg[BC][DK + 16];
-    __shared__ __attribute__((aligned(16))) float sKd[BC][DK + 4];   // read as [row][k]
-    __shared__ __attribute__((aligned(16))) float sM[BC][BC + 16];   // read transposed: [k][col]
-    __shared__ __attribute__((aligned(16))) float sP[BC][BC + 16];
-    __shared__ __attribute__((aligned(16))) float sdO[BC][JT + 16];
-    __shared__ __attribute__((aligned(16))) float sY[BC][JT + 16];
-    __shared__ __attribute__((aligned(16))) float sZ[BC][JT + 16];
-    __shared__ __attribute__((aligned(16))) float sdS[DK][JT + 16];
-    __shared__ __attribute__((aligned(16))) float sGc[DK];
+    // sQg, sKg read as [k][col]; sKd as [row][k]
+    float(*sQg)[DK + 4] = reinterpret_cast<float(*)[DK + 4]>(smem);
+    float(*sKg)[DK + 4] = reinterpret_cast<float(*)[DK + 4]>(smem + BC * (DK + 4));
+    float(*sKd)[DK + 4] = reinterpret_cast<float(*)[DK + 4]>(smem + 2 * BC * (DK + 4));
+    float* base = smem + 3 * BC * (DK + 4);
+    float(*sdO)[JT + 4] = reinterpret_cast<float(*)[JT + 4]>(base);
+    float(*sY)[JT + 4] = reinterpret_cast<float(*)[JT + 4]>(base + BC * (JT + 4));  // then Z
+    float(*sdS)[JT + 4] = reinterpret_cast<float(*)[JT + 4]>(base + 2 * BC * (JT + 4));
+    float* sGc = base + 2 * BC * (JT + 4) + DK * (JT + 4);
     const int ntile = p.dv / JT;
-    const long bh = blockIdx.x / ntile;
-    const int j0 = (blockIdx.x % ntile) * JT;
+    const long bh = unit / ntile;
+    const int j0 = static_cast<int>(unit % ntile) * JT;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int ln = lane & 15, g4 = lane >> 4;
     const long Tp = static_cast<long>(p.nc) * BC;
@@ -552,18 +569,23 @@ __global__ void __launch_bounds__(NT) bwd_state_bwd_kernel(BwdParams p) {
     }
     const int rb = w >> 1, xcb = w & 1;
     Tile4<DK, BC * DK / 4> nKg, nQg, nKd;
-    Tile4<BC, BC * BC / 4> nM, nP;
     Tile4<DK, DK / 4> nGc;
     f32x4 ndO;  // one 4-column group of the dO tile per thread
+    float nPt[BC / 4], nMt[BC / 4];  // this lane's P^T and M^T operands: P[4 k + g4][16 rb + ln]
     const int dr = tid / (JT / 4), dc4 = tid % (JT / 4);
     auto fetch = [&](long c) {
         const float* R = p.rec + (bh * p.nc + c) * RF;
         nKg.load(R, DK);
         nQg.load(R + BC * DK, DK);
         nKd.load(R + 2 * BC * DK, DK);
-        nM.load(R + rec_m<DK>(p.dv), BC);
-        nP.load(R + rec_p<DK>(p.dv), BC);
         nGc.load(R + rec_gc<DK>(p.dv), DK);
+        const float* Rm = R + rec_m<DK>(p.dv);
+        const float* Rp = R + rec_p<DK>(p.dv);
+#pragma unroll
+        for (int k = 0; k < BC / 4; ++k) {
+            nPt[k] = Rp[(4 * k + g4) * BC + 16 * rb + ln];
+            nMt[k] = Rm[(4 * k + g4) * BC + 16 * rb + ln];
+        }
         const long t = c * BC + dr;
         ndO = *reinterpret_cast<const f32x4*>(p.dO + (bh * p.T + tclamp(p, t)) * p.dv + j0 + 4 * dc4);
         if (t >= p.T) ndO = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -579,32 +601,37 @@ __global__ void __launch_bounds__(NT) bwd_state_bwd_kernel(BwdParams p) {
                 p.dst[(bh * p.nc + c) * SZ + (16 * ib + 4 * g4 + e) * p.dv + j0 + 16 * cb + ln] = dacc[m][e];
         }
         __syncthreads();
-        nKg.template store<DK + 16>(&sKg[0][0]);
-        nQg.template store<DK + 16>(&sQg[0][0]);
+        nKg.template store<DK + 4>(&sKg[0][0]);
+        nQg.template store<DK + 4>(&sQg[0][0]);
         nKd.template store<DK + 4>(&sKd[0][0]);
-        nM.template store<BC + 16>(&sM[0][0]);
-        nP.template store<BC + 16>(&sP[0][0]);
-        nGc.template store<DK>(&sGc[0]);
+        nGc.template store<DK>(sGc);
         *reinterpret_cast<f32x4*>(&sdO[dr][4 * dc4]) = ndO;
+        float aPt[BC / 4], aMt[BC / 4];
+#pragma unroll
+        for (int k = 0; k < BC / 4; ++k) {
+            aPt[k] = nPt[k];
+            aMt[k] = nMt[k];
+        }
         __syncthreads();
         if (c > 0) fetch(c - 1);
         // Y = P^T dO + Kd dS'
         f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int k = 0; k < BC; k += 4) y = mfma4(sP[k + g4][16 * rb + ln], sdO[k + g4][16 * xcb + ln], y);
+        for (int k = 0; k < BC / 4; ++k) y = mfma4(aPt[k], sdO[4 * k + g4][16 * xcb + ln], y);
 #pragma unroll 8
         for (int k = 0; k < DK; k += 4) y = mfma4(sKd[16 * rb + ln][k + g4], sdS[k + g4][16 * xcb + ln], y);
 #pragma unroll
         for (int e = 0; e < 4; ++e) sY[16 * rb + 4 * g4 + e][16 * xcb + ln] = y[e];
         __syncthreads();
-        // Z = M^T Y
+        // Z = M^T Y, into Y's buffer once every wave has read Y
         f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int k = 0; k < BC; k += 4) z = mfma4(sM[k + g4][16 * rb + ln], sY[k + g4][16 * xcb + ln], z);
+        for (int k = 0; k < BC / 4; ++k) z = mfma4(aMt[k], sY[4 * k + g4][16 * xcb + ln], z);
+        __syncthreads();
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = 16 * rb + 4 * g4 + e;
-            sZ[r][16 * xcb + ln] = z[e];
+            sY[r][16 * xcb + ln] = z[e];
             p.Z[(bh * Tp + c * BC + r) * p.dv + j0 + 16 * xcb + ln] = z[e];
         }
         __syncthreads();
@@ -617,7 +644,7 @@ __global__ void __launch_bounds__(NT) bwd_state_bwd_kernel(BwdParams p) {
 #pragma unroll
             for (int k = 0; k < BC; k += 4) {
                 dacc[m] = mfma4(sQg[k + g4][16 * ib + ln], sdO[k + g4][16 * cb + ln], dacc[m]);
-                dacc[m] = mfma4(-sKg[k + g4][16 * ib + ln], sZ[k + g4][16 * cb + ln], dacc[m]);
+                dacc[m] = mfma4(-sKg[k + g4][16 * ib + ln], sY[k + g4][16 * cb + ln], dacc[m]);
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) sdS[16 * ib + 4 * g4 + e][16 * cb + ln] = dacc[m][e];
@@ -632,6 +659,23 @@ __global__ void __launch_bounds__(NT) bwd_state_bwd_kernel(BwdParams p) {
                 p.dS0[bh * SZ + (16 * ib + 4 * g4 + e) * p.dv + j0 + 16 * cb + ln] = dacc[m][e];
         }
     }
+}
+
+// Both state passes in one launch: the reverse pass needs only the record
+// and dO, not the forward states, so the two chains run side by side, one
+// workgroup of each per CU, each filling the other's barrier and memory
+// waits.  Workgroups are dealt to the 8 XCDs in turn, so the roles alternate
+// every 8 workgroups (every XCD gets both); the grid is padded to 16 per 8
+// units and the padding exits at once.
+template <int DK>
+__global__ void __launch_bounds__(NT, 2) bwd_states_kernel(BwdParams p, long units) {
+    constexpr int LDSF = fwd_lds_floats<DK>() > bwd_lds_floats<DK>() ? fwd_lds_floats<DK>()
+                                                                     : bwd_lds_floats<DK>();
+    __shared__ __attribute__((aligned(16))) float smem[LDSF];
+    const long unit = (blockIdx.x >> 4) * 8 + (blockIdx.x & 7);
+    if (unit >= units) return;  // whole workgroup, before any barrier
+    if ((blockIdx.x >> 3) & 1) state_bwd_body<DK>(p, smem, unit);
+    else state_fwd_body<DK>(p, smem, unit);
 }
 
 // ---------------------------------------------------------------------------
@@ -1306,8 +1350,7 @@ hipError_t run_bwd(const pdn_chunk_bwd_args& a, const BwdParams& p, hipStream_t 
     }
     if (p.stab) bwd_prep_kernel<DK, BF16, true><<<nch, NT, 0, s>>>(p);
     else bwd_prep_kernel<DK, BF16, false><<<nch, NT, 0, s>>>(p);
-    bwd_state_fwd_kernel<DK><<<ntl, NT, 0, s>>>(p);
-    bwd_state_bwd_kernel<DK><<<ntl, NT, 0, s>>>(p);
+    bwd_states_kernel<DK><<<16 * ((ntl + 7) / 8), NT, 0, s>>>(p, static_cast<long>(ntl));
     bwd_dgrad_kernel<DK><<<nch, NT, 0, s>>>(p);
     bwd_gates_kernel<DK, BF16><<<nch, NT, 0, s>>>(p);
     if (p.pre) {
