@@ -422,6 +422,21 @@ struct Tile4 {
     }
 };
 
+// (b, h) and first value column of state-pass unit u.  Both workgroups of a
+// unit run on XCD u mod 8 (see bwd_states_kernel); when the head count allows,
+// all column tiles of a head get the same u mod 8, so that they share the
+// chunk records in that XCD's L2.
+__device__ __forceinline__ void unit_tile(const BwdParams& p, long u, long& bh, int& j0) {
+    const int ntile = p.dv / JT;
+    if (p.nbh % 8 == 0) {
+        bh = (u / (8L * ntile)) * 8 + u % 8;
+        j0 = static_cast<int>((u / 8) % ntile) * JT;
+    } else {
+        bh = u / ntile;
+        j0 = static_cast<int>(u % ntile) * JT;
+    }
+}
+
 // LDS of the forward state pass, in floats
 template <int DK>
 constexpr int fwd_lds_floats() {
@@ -441,9 +456,9 @@ __device__ __forceinline__ void state_fwd_body(const BwdParams& p, float* smem, 
     float(*sU)[JT + 16] = reinterpret_cast<float(*)[JT + 16]>(base + BC * (JT + 16));
     float(*sS)[JT + 16] = reinterpret_cast<float(*)[JT + 16]>(base + 2 * BC * (JT + 16));
     float* sGc = base + 2 * BC * (JT + 16) + DK * (JT + 16);
-    const int ntile = p.dv / JT;
-    const long bh = unit / ntile;
-    const int j0 = static_cast<int>(unit % ntile) * JT;
+    long bh;
+    int j0;
+    unit_tile(p, unit, bh, j0);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int ln = lane & 15, g4 = lane >> 4;
     const long Tp = static_cast<long>(p.nc) * BC;
@@ -547,9 +562,9 @@ __device__ __forceinline__ void state_bwd_body(const BwdParams& p, float* smem, 
     float(*sY)[JT + 4] = reinterpret_cast<float(*)[JT + 4]>(base + BC * (JT + 4));  // then Z
     float(*sdS)[JT + 4] = reinterpret_cast<float(*)[JT + 4]>(base + 2 * BC * (JT + 4));
     float* sGc = base + 2 * BC * (JT + 4) + DK * (JT + 4);
-    const int ntile = p.dv / JT;
-    const long bh = unit / ntile;
-    const int j0 = static_cast<int>(unit % ntile) * JT;
+    long bh;
+    int j0;
+    unit_tile(p, unit, bh, j0);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int ln = lane & 15, g4 = lane >> 4;
     const long Tp = static_cast<long>(p.nc) * BC;
