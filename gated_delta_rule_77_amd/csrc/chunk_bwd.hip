@@ -696,16 +696,22 @@ __global__ void __launch_bounds__(NT, 2) bwd_states_kernel(BwdParams p, long uni
 // ---------------------------------------------------------------------------
 // the dv contractions of one chunk
 // ---------------------------------------------------------------------------
+// LDS of the dv contractions, in floats
 template <int DK>
-__global__ void __launch_bounds__(NT) bwd_dgrad_kernel(BwdParams p) {
+constexpr int dgrad_lds_floats() { return 2 * DK * (JT + 4) + 3 * BC * (JT + 4); }
+
+// the dv contractions of chunk `unit` (= bh * nc + c), into the gradient record
+template <int DK>
+__device__ __forceinline__ void dgrad_body(const BwdParams& p, float* smem, long unit) {
     constexpr int IBW = DK / 16 / 4;  // 16-channel blocks per wave
-    __shared__ __attribute__((aligned(16))) float sS[DK][JT + 4];  // all read as [row][k]
-    __shared__ __attribute__((aligned(16))) float sE[DK][JT + 4];
-    __shared__ __attribute__((aligned(16))) float sdO[BC][JT + 4];
-    __shared__ __attribute__((aligned(16))) float sZ[BC][JT + 4];
-    __shared__ __attribute__((aligned(16))) float sU[BC][JT + 4];
-    const long bh = blockIdx.x / p.nc;
-    const long c = blockIdx.x % p.nc;
+    // all read as [row][k]
+    float(*sS)[JT + 4] = reinterpret_cast<float(*)[JT + 4]>(smem);
+    float(*sE)[JT + 4] = reinterpret_cast<float(*)[JT + 4]>(smem + DK * (JT + 4));
+    float(*sdO)[JT + 4] = reinterpret_cast<float(*)[JT + 4]>(smem + 2 * DK * (JT + 4));
+    float(*sZ)[JT + 4] = reinterpret_cast<float(*)[JT + 4]>(smem + 2 * DK * (JT + 4) + BC * (JT + 4));
+    float(*sU)[JT + 4] = reinterpret_cast<float(*)[JT + 4]>(smem + 2 * DK * (JT + 4) + 2 * BC * (JT + 4));
+    const long bh = unit / p.nc;
+    const long c = unit % p.nc;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int ln = lane & 15, g4 = lane >> 4;
     const long Tp = static_cast<long>(p.nc) * BC;
@@ -850,22 +856,34 @@ struct ColView {
     __device__ __forceinline__ float bev(int r) const { return be[rc(r) * be_row]; }
 };
 
+template <int DK>
+constexpr int gates_sbuf_floats() {
+    return 3 * BC * (DK + 16) > 4 * BC * (DK + 1) ? 3 * BC * (DK + 16) : 4 * BC * (DK + 1);
+}
+// LDS of the gate gradients, in floats
+template <int DK>
+constexpr int gates_lds_floats() {
+    return gates_sbuf_floats<DK>() + 2 * BC * (BC + 1) + (NT / DK) * 4 * DK + 3 * DK + 3 * BC;
+}
+
+// the gate gradients of chunk `unit` (= bh * nc + c), from its gradient record
 template <int DK, bool BF16>
-__global__ void __launch_bounds__(NT, 2) bwd_gates_kernel(BwdParams p) {
+__device__ __forceinline__ void gates_body(const BwdParams& p, float* smem, long unit) {
     constexpr int CTW = DK / 16 / 4;  // 16-channel column tiles per wave
     constexpr int OS = DK + 16;       // operand row stride (read as [k][col])
     constexpr int AS = DK + 1;        // result row stride (read per channel)
     constexpr int NH = NT / DK;       // threads per channel
     constexpr int RPT = BC / NH;      // rows per thread
-    __shared__ float sdT[BC][BC + 1];
-    __shared__ float sdP[BC][BC + 1];
-    constexpr int SBUF = 3 * BC * OS > 4 * BC * AS ? 3 * BC * OS : 4 * BC * AS;
-    __shared__ __attribute__((aligned(16))) float sbuf[SBUF];  // operands, then A1..A4
-    __shared__ float sX[NH][4][DK];  // per-part partial sums exchanged between the parts of a channel
-    __shared__ float sRef[3][DK];    // G_8, G_24, G_C of each channel
-    __shared__ float sRowG[BC];      // row sums of dgamma'
-    __shared__ float sMu[BC];        // stabilised mode: channel mean of ln(A + eps) per row
-    __shared__ float sDrm[BC];       // stabilised mode: channel mean of dr per row
+    constexpr int SBUF = gates_sbuf_floats<DK>();
+    float* sbuf = smem;  // operands, then A1..A4
+    float(*sdT)[BC + 1] = reinterpret_cast<float(*)[BC + 1]>(smem + SBUF);
+    float(*sdP)[BC + 1] = reinterpret_cast<float(*)[BC + 1]>(smem + SBUF + BC * (BC + 1));
+    // per-part partial sums exchanged between the parts of a channel
+    float(*sX)[4][DK] = reinterpret_cast<float(*)[4][DK]>(smem + SBUF + 2 * BC * (BC + 1));
+    float(*sRef)[DK] = reinterpret_cast<float(*)[DK]>(smem + SBUF + 2 * BC * (BC + 1) + NH * 4 * DK);  // G_8, G_24, G_C
+    float* sRowG = smem + SBUF + 2 * BC * (BC + 1) + NH * 4 * DK + 3 * DK;  // row sums of dgamma'
+    float* sMu = sRowG + BC;   // stabilised mode: channel mean of ln(A + eps) per row
+    float* sDrm = sMu + BC;    // stabilised mode: channel mean of dr per row
     float(*sW)[OS] = reinterpret_cast<float(*)[OS]>(sbuf);
     float(*sRk)[OS] = reinterpret_cast<float(*)[OS]>(sbuf + BC * OS);
     float(*sRq)[OS] = reinterpret_cast<float(*)[OS]>(sbuf + 2 * BC * OS);
@@ -875,8 +893,8 @@ __global__ void __launch_bounds__(NT, 2) bwd_gates_kernel(BwdParams p) {
     float(*sA3)[AS] = reinterpret_cast<float(*)[AS]>(sbuf + BC * AS);
     float(*sA2)[AS] = reinterpret_cast<float(*)[AS]>(sbuf + 2 * BC * AS);
     float(*sA4)[AS] = reinterpret_cast<float(*)[AS]>(sbuf + 3 * BC * AS);
-    const long bh = blockIdx.x / p.nc;
-    const long c = blockIdx.x % p.nc;
+    const long bh = unit / p.nc;
+    const long c = unit % p.nc;
     const long t0 = c * BC;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int ln = lane & 15, g4 = lane >> 4;
@@ -1266,6 +1284,20 @@ __global__ void __launch_bounds__(NT, 2) bwd_gates_kernel(BwdParams p) {
     }
 }
 
+// The dv contractions and the gate gradients of one chunk in one workgroup:
+// the gradient record goes out and comes back through L2, and two
+// workgroups per CU overlap one's MFMA-heavy contractions with the other's
+// gate work.
+template <int DK, bool BF16>
+__global__ void __launch_bounds__(NT, 2) bwd_grads_kernel(BwdParams p) {
+    constexpr int LDSF = dgrad_lds_floats<DK>() > gates_lds_floats<DK>() ? dgrad_lds_floats<DK>()
+                                                                         : gates_lds_floats<DK>();
+    __shared__ __attribute__((aligned(16))) float smem[LDSF];
+    dgrad_body<DK>(p, smem, blockIdx.x);
+    __syncthreads();  // the record written by every thread is visible to the workgroup
+    gates_body<DK, BF16>(p, smem, blockIdx.x);
+}
+
 // ---------------------------------------------------------------------------
 // preconditioner: dk += 2 k (.) sum_{s >= t} dA_s, dA0
 // ---------------------------------------------------------------------------
@@ -1366,8 +1398,7 @@ hipError_t run_bwd(const pdn_chunk_bwd_args& a, const BwdParams& p, hipStream_t 
     if (p.stab) bwd_prep_kernel<DK, BF16, true><<<nch, NT, 0, s>>>(p);
     else bwd_prep_kernel<DK, BF16, false><<<nch, NT, 0, s>>>(p);
     bwd_states_kernel<DK><<<16 * ((ntl + 7) / 8), NT, 0, s>>>(p, static_cast<long>(ntl));
-    bwd_dgrad_kernel<DK><<<nch, NT, 0, s>>>(p);
-    bwd_gates_kernel<DK, BF16><<<nch, NT, 0, s>>>(p);
+    bwd_grads_kernel<DK, BF16><<<nch, NT, 0, s>>>(p);
     if (p.pre) {
         bwd_dA_scan_kernel<DK><<<nbh, DK, 0, s>>>(p);
         bwd_dA_apply_kernel<DK, BF16><<<nch, NT, 0, s>>>(p);
