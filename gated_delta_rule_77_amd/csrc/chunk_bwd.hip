@@ -21,12 +21,12 @@
 // Kernels, in launch order:
 //   bwd_ksum / bwd_kscan   preconditioner: running k (.) k before each chunk
 //   bwd_prep               per chunk: Kg, Qg, Kd, Vw, M, P, e^G_C (the record)
-//   bwd_state_fwd          per (b, h, 32 value columns), chunks in order: the
-//                          chunk start states S and U
-//   bwd_state_bwd          same, chunks in reverse: dS' per chunk, Z, dS0
-//   bwd_dgrad              per chunk: the dv contractions (dQg, dKg, dKd, dP,
-//                          dT, dGamma_C), fp32 16x16x4 MFMAs
-//   bwd_gates              per chunk: the pairwise sums (MFMA), then dq, dk, dv, d log alpha,
+//   bwd_states             per (b, h, 32 value columns), both passes side by
+//                          side: chunks in order (the chunk start states S
+//                          and U) and in reverse (dS' per chunk, Z, dS0)
+//   bwd_grads              per chunk: the dv contractions (dQg, dKg, dKd, dP,
+//                          dT, dGamma_C), fp32 16x16x4 MFMAs, then
+//                          the pairwise sums (MFMA) and dq, dk, dv, d log alpha,
 //                          dbeta, dgamma, and the preconditioner's dA
 //   bwd_dA_scan / bwd_dA_apply   preconditioner: dk += 2 k (.) sum_{s>=t} dA_s
 //
