@@ -181,6 +181,38 @@ __device__ __forceinline__ float value_dscale(int kmode, int gmode, float g) {
     return 1.f;
 }
 
+// Per-thread views of one key channel's per-token inputs over a chunk: base
+// pointers and strides are fixed once; a row index beyond T is clamped (the
+// value is then masked by the caller).
+template <int DK, bool BF16>
+struct ColView {
+    const void* k;
+    const void* q;
+    const float* la;
+    const float* be;
+    long kq_row, la_row, be_row;  // element strides per token
+    int rmax;                     // last valid row of the chunk
+    __device__ ColView(const BwdParams& p, long bh, long t0, int i) {
+        const long tok0 = bh * p.T + t0;
+        rmax = static_cast<int>(min(static_cast<long>(BC - 1), p.T - 1 - t0));
+        const size_t esz = BF16 ? 2 : 4;
+        k = static_cast<const char*>(p.k) + (tok0 * DK + i) * esz;
+        q = static_cast<const char*>(p.q) + (tok0 * DK + i) * esz;
+        kq_row = DK;
+        const bool lav = p.amode == PDN_ALPHA_VEC;
+        la = (p.amode == PDN_ALPHA_NONE ? p.beta + tok0 : p.la + (lav ? tok0 * DK + i : tok0));
+        la_row = lav ? DK : 1;
+        const bool bv = p.bmode == PDN_GATE_VEC;
+        be = p.beta + (bv ? tok0 * DK + i : tok0);
+        be_row = bv ? DK : 1;
+    }
+    __device__ __forceinline__ int rc(int r) const { return r < rmax ? r : rmax; }
+    __device__ __forceinline__ float kv(int r) const { return load_in<BF16>(k, rc(r) * kq_row); }
+    __device__ __forceinline__ float qv(int r) const { return load_in<BF16>(q, rc(r) * kq_row); }
+    __device__ __forceinline__ float lav(int r) const { return la[rc(r) * la_row]; }
+    __device__ __forceinline__ float bev(int r) const { return be[rc(r) * be_row]; }
+};
+
 // ---------------------------------------------------------------------------
 // preconditioner: A before each chunk
 // ---------------------------------------------------------------------------
@@ -244,29 +276,64 @@ __global__ void __launch_bounds__(NT, 2) bwd_prep_kernel(BwdParams p) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int ln = lane & 15, g4 = lane >> 4;
     float* R = p.rec + (bh * p.nc + c) * rec_floats<DK>(p.dv);
-    const int i = tid;
-    // every load of the column first, then the scans
-    float kk[BC], qq[BC], la[BC], bb[BC];
-    if (tid < DK) {
+    // thread (channel i, part h) owns rows h RPT .. h RPT + RPT - 1 of channel i;
+    // the scans cross the parts through LDS
+    constexpr int NH = NT / DK, RPT = BC / NH;
+    __shared__ float sPart[NH][2][DK];  // per-part sums of the log decay and of k (.) k
+    __shared__ float sRef[3][DK];       // G at rows 8, 24 and 31 of each channel
+    __shared__ float sMu[BC];
+    const int i = tid % DK, h = tid / DK, r0 = h * RPT;
+    const ColView<DK, BF16> cv(p, bh, t0, i);
+    const bool has_decay = p.amode != PDN_ALPHA_NONE;
+    // every load of the own rows first
+    float kk[RPT], qq[RPT], g[RPT], bb[RPT];
 #pragma unroll
-        for (int r = 0; r < BC; ++r) {
-            const long t = t0 + r;
-            kk[r] = tok_in<BF16>(p, p.k, bh, t, DK, i);
-            qq[r] = tok_in<BF16>(p, p.q, bh, t, DK, i);
-            la[r] = tok_la<DK>(p, bh, t, i);
-            bb[r] = tok_beta<DK>(p, bh, t, i);
+    for (int u = 0; u < RPT; ++u) {
+        kk[u] = cv.kv(r0 + u);
+        qq[u] = cv.qv(r0 + u);
+        g[u] = cv.lav(r0 + u);
+        bb[u] = cv.bev(r0 + u);
+    }
+    float gs = 0.f, as = 0.f;
+#pragma unroll
+    for (int u = 0; u < RPT; ++u) {
+        const bool valid = t0 + r0 + u < p.T;
+        g[u] = (valid && has_decay) ? fmaxf(g[u], kLogAlphaMin) : 0.f;
+        if (!valid) {
+            kk[u] = 0.f;
+            qq[u] = 0.f;
+            bb[u] = 1.f;
+        }
+        gs += g[u];
+        as += kk[u] * kk[u];
+    }
+    sPart[h][0][i] = gs;
+    sPart[h][1][i] = as;
+    __syncthreads();
+    float Gin = 0.f, Ain = p.pre ? p.apre[(bh * p.nc + c) * DK + i] : 0.f;
+    for (int h2 = 0; h2 < h; ++h2) {
+        Gin += sPart[h2][0][i];
+        Ain += sPart[h2][1][i];
+    }
+    {
+        float run = Gin;
+#pragma unroll
+        for (int u = 0; u < RPT; ++u) {
+            run += g[u];
+            g[u] = run;
+            const int r = r0 + u;
+            if (r == 8) sRef[0][i] = run;
+            if (r == 24) sRef[1][i] = run;
+            if (r == BC - 1) sRef[2][i] = run;
         }
     }
-    __shared__ float sMu[BC];
     if constexpr (STAB) {
         // the channel mean of ln(A + eps) per token (sKrL holds ln(A + eps) for now)
-        if (tid < DK) {
-            float A = p.apre[(bh * p.nc + c) * DK + i];
+        float A = Ain;
 #pragma unroll
-            for (int r = 0; r < BC; ++r) {
-                A += kk[r] * kk[r];
-                sKrL[r][i] = logf(A + p.eps);
-            }
+        for (int u = 0; u < RPT; ++u) {
+            A += kk[u] * kk[u];
+            sKrL[r0 + u][i] = logf(A + p.eps);
         }
         __syncthreads();
         if (tid < BC) {
@@ -276,19 +343,18 @@ __global__ void __launch_bounds__(NT, 2) bwd_prep_kernel(BwdParams p) {
             sMu[tid] = m;
             p.mu[bh * static_cast<long>(p.nc) * BC + t0 + tid] = m;
         }
-        __syncthreads();
     }
-    if (tid < DK) {
-        float G = 0.f;
-        float A = p.pre ? p.apre[(bh * p.nc + c) * DK + i] : 0.f;
-        float kr[BC], kw[BC], g[BC];
+    __syncthreads();
+    {
+        const float g8 = sRef[0][i], g24 = sRef[1][i], gc = sRef[2][i];
+        const float cst = __expf(g24 - g8);
+        float A = Ain;
 #pragma unroll
-        for (int r = 0; r < BC; ++r) {
-            G += la[r];
-            g[r] = G;
-            float b = bb[r];
+        for (int u = 0; u < RPT; ++u) {
+            const int r = r0 + u;
+            float b = bb[u];
             if (p.pre) {
-                A += kk[r] * kk[r];
+                A += kk[u] * kk[u];
                 if constexpr (STAB) {
                     const float x = logf(A + p.eps) - sMu[r];
                     b = b * __expf(-(x / (1.f + fabsf(x))) * p.lnx);
@@ -296,24 +362,20 @@ __global__ void __launch_bounds__(NT, 2) bwd_prep_kernel(BwdParams p) {
                     b = b / (A + p.eps);
                 }
             }
-            keys_of(p.kmode, b, kk[r], kw[r], kr[r]);
+            float kw, kr;
+            keys_of(p.kmode, b, kk[u], kw, kr);
+            const float e = __expf(g[u]);
+            R[r * DK + i] = kr * e;
+            R[BC * DK + r * DK + i] = qq[u] * e;
+            R[2 * BC * DK + r * DK + i] = kw * __expf(gc - g[u]);
+            const float gm = r < 16 ? g8 : g24;
+            const float L = __expf(g[u] - gm), Rs = __expf(gm - g[u]);
+            sKrL[r][i] = kr * L;
+            sQL[r][i] = qq[u] * L;
+            sKwR[r][i] = kw * Rs;
+            if (r < 16) sKwRc[r][i] = kw * Rs * cst;
         }
-        const float gc = g[BC - 1];
-        const float cst = __expf(g[24] - g[8]);
-#pragma unroll
-        for (int r = 0; r < BC; ++r) {
-            const float e = __expf(g[r]);
-            R[r * DK + i] = kr[r] * e;
-            R[BC * DK + r * DK + i] = qq[r] * e;
-            R[2 * BC * DK + r * DK + i] = kw[r] * __expf(gc - g[r]);
-            const float gm = r < 16 ? g[8] : g[24];
-            const float L = __expf(g[r] - gm), Rs = __expf(gm - g[r]);
-            sKrL[r][i] = kr[r] * L;
-            sQL[r][i] = qq[r] * L;
-            sKwR[r][i] = kw[r] * Rs;
-            if (r < 16) sKwRc[r][i] = kw[r] * Rs * cst;
-        }
-        R[rec_gc<DK>(p.dv) + i] = __expf(gc);
+        if (h == 0) R[rec_gc<DK>(p.dv) + i] = __expf(gc);
     }
     float* Rvw = R + rec_vw<DK>(p.dv);
     {
@@ -824,37 +886,6 @@ __device__ __forceinline__ void dgrad_body(const BwdParams& p, float* smem, long
 //   A2 = R (.) [dT^T Rk]_in-block + R (.) c (.) [dT_(1,0)^T Rk_1]   (c = e^(G_24 - G_8))
 // and likewise A3, A4 with dP.
 // ---------------------------------------------------------------------------
-// Per-thread views of one key channel's per-token inputs over a chunk: base
-// pointers and strides are fixed once; a row index beyond T is clamped (the
-// value is then masked by the caller).
-template <int DK, bool BF16>
-struct ColView {
-    const void* k;
-    const void* q;
-    const float* la;
-    const float* be;
-    long kq_row, la_row, be_row;  // element strides per token
-    int rmax;                     // last valid row of the chunk
-    __device__ ColView(const BwdParams& p, long bh, long t0, int i) {
-        const long tok0 = bh * p.T + t0;
-        rmax = static_cast<int>(min(static_cast<long>(BC - 1), p.T - 1 - t0));
-        const size_t esz = BF16 ? 2 : 4;
-        k = static_cast<const char*>(p.k) + (tok0 * DK + i) * esz;
-        q = static_cast<const char*>(p.q) + (tok0 * DK + i) * esz;
-        kq_row = DK;
-        const bool lav = p.amode == PDN_ALPHA_VEC;
-        la = (p.amode == PDN_ALPHA_NONE ? p.beta + tok0 : p.la + (lav ? tok0 * DK + i : tok0));
-        la_row = lav ? DK : 1;
-        const bool bv = p.bmode == PDN_GATE_VEC;
-        be = p.beta + (bv ? tok0 * DK + i : tok0);
-        be_row = bv ? DK : 1;
-    }
-    __device__ __forceinline__ int rc(int r) const { return r < rmax ? r : rmax; }
-    __device__ __forceinline__ float kv(int r) const { return load_in<BF16>(k, rc(r) * kq_row); }
-    __device__ __forceinline__ float qv(int r) const { return load_in<BF16>(q, rc(r) * kq_row); }
-    __device__ __forceinline__ float lav(int r) const { return la[rc(r) * la_row]; }
-    __device__ __forceinline__ float bev(int r) const { return be[rc(r) * be_row]; }
-};
 
 template <int DK>
 constexpr int gates_sbuf_floats() {
