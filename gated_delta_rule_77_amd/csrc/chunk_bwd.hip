@@ -932,6 +932,19 @@ __device__ __forceinline__ void gates_body(const BwdParams& p, float* smem, long
     const long Tp = static_cast<long>(p.nc) * BC;
     const float* D = p.dgr + (bh * p.nc + c) * dgr_floats<DK>();
     if (p.pre && p.stab && tid < BC) sMu[tid] = p.mu[bh * Tp + t0 + tid];
+    // thread (channel i, part h) owns rows h RPT .. h RPT + RPT - 1 of channel i;
+    // its column is requested first, so these loads overlap those of dv below
+    const int i = tid % DK, h = tid / DK, r0 = h * RPT;
+    const ColView<DK, BF16> cv(p, bh, t0, i);
+    const bool has_decay = p.amode != PDN_ALPHA_NONE;
+    float G[RPT], kk[RPT], qv[RPT], bb[RPT];
+#pragma unroll
+    for (int u = 0; u < RPT; ++u) {
+        kk[u] = cv.kv(r0 + u);
+        qv[u] = cv.qv(r0 + u);
+        G[u] = cv.lav(r0 + u);
+        bb[u] = cv.bev(r0 + u);
+    }
     {
         constexpr int PER = BC * BC / NT;
         float tv[PER], pv[PER];
@@ -947,16 +960,16 @@ __device__ __forceinline__ void gates_body(const BwdParams& p, float* smem, long
             sdT[idx / BC][idx % BC] = tv[m];
         }
     }
-    // dv and dgamma' (wave w: rows w, w + 4, ...; lanes over columns), in four
-    // batches of two rows, every load of a batch before its stores
+    // dv and dgamma' (wave w: rows w, w + 4, ...; lanes over columns), in two
+    // batches of four rows, every load of a batch before its stores
     const bool gsum = p.gmode == PDN_GATE_SCALAR ||
                       (p.gmode == PDN_GAMMA_SAME_AS_BETA && p.bmode == PDN_GATE_SCALAR);
 #pragma unroll
-    for (int quarter = 0; quarter < 4; ++quarter) {
-        float zv[2][4], gv[2][4], vv[2][4];
+    for (int half = 0; half < 2; ++half) {
+        float zv[4][4], gv[4][4], vv[4][4];
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            const int r = w + 4 * (2 * quarter + m);
+        for (int m = 0; m < 4; ++m) {
+            const int r = w + 4 * (4 * half + m);
             const long t = t0 + r;
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
@@ -967,8 +980,8 @@ __device__ __forceinline__ void gates_body(const BwdParams& p, float* smem, long
             }
         }
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            const int r = w + 4 * (2 * quarter + m);
+        for (int m = 0; m < 4; ++m) {
+            const int r = w + 4 * (4 * half + m);
             const long t = t0 + r;
             float part = 0.f;
 #pragma unroll
@@ -990,34 +1003,19 @@ __device__ __forceinline__ void gates_body(const BwdParams& p, float* smem, long
             }
         }
     }
-    // thread (channel i, part h) owns rows h RPT .. h RPT + RPT - 1 of channel i
-    const int i = tid % DK, h = tid / DK, r0 = h * RPT;
-    const ColView<DK, BF16> cv(p, bh, t0, i);
-    const bool has_decay = p.amode != PDN_ALPHA_NONE;
-    float G[RPT], kk[RPT], qv[RPT], bb[RPT];
     uint32_t dead = 0;  // own rows whose d log alpha is zero
     float Gin = 0.f, Ain = 0.f;  // cumulative log decay and k (.) k before the own rows
-    auto column = [&]() {
 #pragma unroll
-        for (int u = 0; u < RPT; ++u) {
-            kk[u] = cv.kv(r0 + u);
-            qv[u] = cv.qv(r0 + u);
-            G[u] = cv.lav(r0 + u);
-            bb[u] = cv.bev(r0 + u);
+    for (int u = 0; u < RPT; ++u) {
+        const bool valid = t0 + r0 + u < p.T;
+        if (!valid || !has_decay || G[u] < kLogAlphaMin) dead |= 1u << u;
+        G[u] = (valid && has_decay) ? fmaxf(G[u], kLogAlphaMin) : 0.f;
+        if (!valid) {
+            kk[u] = 0.f;
+            qv[u] = 0.f;
+            bb[u] = 1.f;
         }
-#pragma unroll
-        for (int u = 0; u < RPT; ++u) {
-            const bool valid = t0 + r0 + u < p.T;
-            if (!valid || !has_decay || G[u] < kLogAlphaMin) dead |= 1u << u;
-            G[u] = (valid && has_decay) ? fmaxf(G[u], kLogAlphaMin) : 0.f;
-            if (!valid) {
-                kk[u] = 0.f;
-                qv[u] = 0.f;
-                bb[u] = 1.f;
-            }
-        }
-    };
-    column();
+    }
     {
         // prefix over the parts: local sums, exchanged, then made inclusive
         float gs = 0.f, as = 0.f;
