@@ -105,7 +105,7 @@ template <int DK>
 __host__ __device__ inline long rec_gc(int dv) { return rec_p<DK>(dv) + BC * BC; }
 // gradient record: dQg, dKg, dKd [BC][DK]; dP, dT [BC][BC]; dGamma_C [DK]
 template <int DK>
-__host__ __device__ constexpr long dgr_floats() { return 3L * BC * DK + 2L * BC * BC + DK; }
+__host__ __device__ constexpr long dgr_floats() { return 3L * BC * DK + DK; }
 
 // ---------------------------------------------------------------------------
 // per-token gates (shared by the prep and the gradient kernels)
@@ -761,10 +761,18 @@ __global__ void __launch_bounds__(NT, 2) bwd_states_kernel(BwdParams p, long uni
 // LDS of the dv contractions, in floats
 template <int DK>
 constexpr int dgrad_lds_floats() { return 2 * DK * (JT + 4) + 3 * BC * (JT + 4); }
+// operand buffer of the gate gradients, in floats; dP and dT follow it
+template <int DK>
+constexpr int gates_sbuf_floats() {
+    return 3 * BC * (DK + 16) > 4 * BC * (DK + 1) ? 3 * BC * (DK + 16) : 4 * BC * (DK + 1);
+}
 
-// the dv contractions of chunk `unit` (= bh * nc + c), into the gradient record
+// the dv contractions of chunk `unit` (= bh * nc + c): dQg, dKg, dKd and dGamma_C
+// into the gradient record, dP and dT into the LDS of the gate phase
 template <int DK>
 __device__ __forceinline__ void dgrad_body(const BwdParams& p, float* smem, long unit) {
+    static_assert(dgrad_lds_floats<DK>() <= gates_sbuf_floats<DK>(),
+                  "dP and dT are written above the buffers of this phase");
     constexpr int IBW = DK / 16 / 4;  // 16-channel blocks per wave
     // all read as [row][k]
     float(*sS)[JT + 4] = reinterpret_cast<float(*)[JT + 4]>(smem);
@@ -861,13 +869,15 @@ __device__ __forceinline__ void dgrad_body(const BwdParams& p, float* smem, long
                 D[BC * DK + r * DK + i] = aK[rb][ib][e];
                 D[2 * BC * DK + r * DK + i] = aD[rb][ib][e];
             }
+    float(*gdT)[BC + 1] = reinterpret_cast<float(*)[BC + 1]>(smem + gates_sbuf_floats<DK>());
+    float(*gdP)[BC + 1] = gdT + BC;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int r = 16 * prb + 4 * g4 + e, s = 16 * pcb + ln;
-        D[3 * BC * DK + r * BC + s] = s <= r ? aP[e] : 0.f;
-        D[3 * BC * DK + BC * BC + r * BC + s] = s < r ? aT[e] : 0.f;
+        gdP[r][s] = s <= r ? aP[e] : 0.f;
+        gdT[r][s] = s < r ? aT[e] : 0.f;
     }
-    if (tid < DK) D[3 * BC * DK + 2 * BC * BC + tid] = gacc;
+    if (tid < DK) D[3 * BC * DK + tid] = gacc;
 }
 
 // ---------------------------------------------------------------------------
@@ -887,10 +897,6 @@ __device__ __forceinline__ void dgrad_body(const BwdParams& p, float* smem, long
 // and likewise A3, A4 with dP.
 // ---------------------------------------------------------------------------
 
-template <int DK>
-constexpr int gates_sbuf_floats() {
-    return 3 * BC * (DK + 16) > 4 * BC * (DK + 1) ? 3 * BC * (DK + 16) : 4 * BC * (DK + 1);
-}
 // LDS of the gate gradients, in floats
 template <int DK>
 constexpr int gates_lds_floats() {
@@ -945,21 +951,7 @@ __device__ __forceinline__ void gates_body(const BwdParams& p, float* smem, long
         G[u] = cv.lav(r0 + u);
         bb[u] = cv.bev(r0 + u);
     }
-    {
-        constexpr int PER = BC * BC / NT;
-        float tv[PER], pv[PER];
-#pragma unroll
-        for (int m = 0; m < PER; ++m) {
-            pv[m] = D[3 * BC * DK + tid + m * NT];
-            tv[m] = D[3 * BC * DK + BC * BC + tid + m * NT];
-        }
-#pragma unroll
-        for (int m = 0; m < PER; ++m) {
-            const int idx = tid + m * NT;
-            sdP[idx / BC][idx % BC] = pv[m];
-            sdT[idx / BC][idx % BC] = tv[m];
-        }
-    }
+    const float dgam = D[3 * BC * DK + i];  // dGamma_C of channel i
     // dv and dgamma' (wave w: rows w, w + 4, ...; lanes over columns), in two
     // batches of four rows, every load of a batch before its stores
     const bool gsum = p.gmode == PDN_GATE_SCALAR ||
@@ -1186,7 +1178,7 @@ __device__ __forceinline__ void gates_body(const BwdParams& p, float* smem, long
         float tot = 0.f;
 #pragma unroll
         for (int h2 = 0; h2 < NH; ++h2) tot += sX[h2][2][i];
-        sA2[BC - 1][i] += tot + D[3 * BC * DK + 2 * BC * BC + i] * __expf(Gc);
+        sA2[BC - 1][i] += tot + dgam * __expf(Gc);
     }
 #pragma unroll
     for (int u = 0; u < RPT; ++u)
@@ -1389,7 +1381,7 @@ BwdLayout bwd_layout(const pdn_chunk_bwd_args& a) {
     const size_t nc = (static_cast<size_t>(f.T) + BC - 1) / BC;
     const size_t dk = f.dk, dv = f.dv;
     const size_t recf = 3 * BC * dk + 2 * BC * BC + dk + BC * dv;
-    const size_t dgrf = 3 * BC * dk + 2 * BC * BC + dk;
+    const size_t dgrf = 3 * BC * dk + dk;
     const bool pre = f.precond_eps >= 0.0f;
     BwdLayout L;
     size_t o = 0;

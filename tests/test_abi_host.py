@@ -419,7 +419,7 @@ def test_bwd_workspace_size(lib):
     al = lambda x: (x + 255) // 256 * 256
     want = (al(nbh * nc * (3 * 32 * dk + 32 * dv + 2 * 32 * 32 + dk) * 4)
             + al(nbh * (nc + 1) * dk * dv * 4) + al(nbh * nc * dk * dv * 4)
-            + 2 * al(nbh * nc * 32 * dv * 4) + al(nbh * nc * (3 * 32 * dk + 2 * 32 * 32 + dk) * 4))
+            + 2 * al(nbh * nc * 32 * dv * 4) + al(nbh * nc * (3 * 32 * dk + dk) * 4))
     assert n == want
     # the preconditioner adds four [B,H,chunks,dk] arrays and one [B,H,chunks*32,dk]
     a.fwd.precond_eps = 1e-6
