@@ -263,13 +263,12 @@ __global__ void __launch_bounds__(DK) bwd_kscan_kernel(BwdParams p) {
 // block below the diagonal uses (kw R c)_s with c = e^(G_24 - G_8), since
 // e^(G_r - G_s) = L_r c R_s there.
 template <int DK, bool BF16, bool STAB>
-__global__ void __launch_bounds__(NT, 2) bwd_prep_kernel(BwdParams p) {
-    constexpr int LS = DK + 4;  // read as [row][k]
-    __shared__ float sKrL[BC][LS];
-    __shared__ float sQL[BC][LS];
-    __shared__ float sKwR[BC][LS];
-    __shared__ float sKwRc[16][LS];
-    __shared__ float sT[BC][BC + 1];
+__global__ void __launch_bounds__(NT, 3) bwd_prep_kernel(BwdParams p) {
+    // 51 KB of LDS, so that three workgroups share a CU
+    constexpr int LS = DK + 4;  // read as [row][k]; the 4 pad columns hold scalars
+    __shared__ float sKrL[BC][LS];  // after the products: T
+    __shared__ float sQL[BC][LS];   // pad column DK: the mean of ln(A + eps) per row
+    __shared__ float sKwR[BC][LS];  // before the operands: the per-part sums; pad: c per channel
     const long bh = blockIdx.x / p.nc;
     const long c = blockIdx.x % p.nc;
     const long t0 = c * BC;
@@ -279,9 +278,12 @@ __global__ void __launch_bounds__(NT, 2) bwd_prep_kernel(BwdParams p) {
     // thread (channel i, part h) owns rows h RPT .. h RPT + RPT - 1 of channel i;
     // the scans cross the parts through LDS
     constexpr int NH = NT / DK, RPT = BC / NH;
-    __shared__ float sPart[NH][2][DK];  // per-part sums of the log decay and of k (.) k
+    static_assert(NH * 2 * DK <= BC * LS && BC * (BC + 1) <= BC * LS && DK <= 4 * BC,
+                  "the aliased scratch fits its buffer");
+    // per-part sums of the log decay and of k (.) k
+    float(*sPart)[2][DK] = reinterpret_cast<float(*)[2][DK]>(&sKwR[0][0]);
+    float(*sT)[BC + 1] = reinterpret_cast<float(*)[BC + 1]>(&sKrL[0][0]);
     __shared__ float sRef[3][DK];       // G at rows 8, 24 and 31 of each channel
-    __shared__ float sMu[BC];
     const int i = tid % DK, h = tid / DK, r0 = h * RPT;
     const ColView<DK, BF16> cv(p, bh, t0, i);
     const bool has_decay = p.amode != PDN_ALPHA_NONE;
@@ -340,7 +342,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_prep_kernel(BwdParams p) {
             float m = 0.f;
             for (int ii = 0; ii < DK; ++ii) m += sKrL[tid][ii];
             m *= 1.f / DK;
-            sMu[tid] = m;
+            sQL[tid][DK] = m;
             p.mu[bh * static_cast<long>(p.nc) * BC + t0 + tid] = m;
         }
     }
@@ -356,7 +358,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_prep_kernel(BwdParams p) {
             if (p.pre) {
                 A += kk[u] * kk[u];
                 if constexpr (STAB) {
-                    const float x = logf(A + p.eps) - sMu[r];
+                    const float x = logf(A + p.eps) - sQL[r][DK];
                     b = b * __expf(-(x / (1.f + fabsf(x))) * p.lnx);
                 } else {
                     b = b / (A + p.eps);
@@ -373,9 +375,11 @@ __global__ void __launch_bounds__(NT, 2) bwd_prep_kernel(BwdParams p) {
             sKrL[r][i] = kr * L;
             sQL[r][i] = qq[u] * L;
             sKwR[r][i] = kw * Rs;
-            if (r < 16) sKwRc[r][i] = kw * Rs * cst;
         }
-        if (h == 0) R[rec_gc<DK>(p.dv) + i] = __expf(gc);
+        if (h == 0) {
+            R[rec_gc<DK>(p.dv) + i] = __expf(gc);
+            sKwR[i / 4][DK + i % 4] = cst;
+        }
     }
     float* Rvw = R + rec_vw<DK>(p.dv);
     {
@@ -404,33 +408,45 @@ __global__ void __launch_bounds__(NT, 2) bwd_prep_kernel(BwdParams p) {
     // six 16 x 16 tiles: T (0,0), (1,1), (1,0) and P likewise; wave w takes
     // tile w and, for w < 2, tile w + 4
     float* Rp = R + rec_p<DK>(p.dv);
+    f32x4 accT = {0.f, 0.f, 0.f, 0.f};  // the T tile of waves 0..2
     for (int tile = w; tile < 6; tile += 4) {
         const bool isP = tile >= 3;
         const int which = tile % 3;  // 0: (0,0), 1: (1,1), 2: (1,0)
         const int rb = which == 0 ? 0 : 1, sb = which == 1 ? 1 : 0;
         const float(*Aop)[LS] = isP ? sQL : sKrL;
-        const float(*Bop)[LS] = which == 2 ? sKwRc : sKwR;
-        const int brow = which == 2 ? 0 : 16 * sb;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (which == 2) {
+            // across the blocks: the kw R rows of block 0 times c of the channel
 #pragma unroll 8
-        for (int k = 0; k < DK; k += 4)
-            acc = mfma4(Aop[16 * rb + ln][k + g4], Bop[brow + ln][k + g4], acc);
+            for (int k = 0; k < DK; k += 4)
+                acc = mfma4(Aop[16 + ln][k + g4], sKwR[ln][k + g4] * sKwR[k / 4][DK + g4], acc);
+        } else {
+#pragma unroll 8
+            for (int k = 0; k < DK; k += 4)
+                acc = mfma4(Aop[16 * rb + ln][k + g4], sKwR[16 * sb + ln][k + g4], acc);
+        }
+        if (isP) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * rb + 4 * g4 + e, s2 = 16 * sb + ln;
+                Rp[r * BC + s2] = s2 <= r ? acc[e] : 0.f;
+            }
+        } else {
+            accT = acc;
+        }
+    }
+    for (int idx = tid; idx < 16 * 16; idx += NT) Rp[(idx / 16) * BC + 16 + idx % 16] = 0.f;
+    __syncthreads();  // every wave is done with the operands: sKrL takes T
+    if (w < 3) {
+        const int rb = w == 0 ? 0 : 1, sb = w == 1 ? 1 : 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = 16 * rb + 4 * g4 + e, s2 = 16 * sb + ln;
-            if (isP) {
-                Rp[r * BC + s2] = s2 <= r ? acc[e] : 0.f;
-            } else {
-                sT[r][s2] = s2 < r ? acc[e] : 0.f;
-            }
+            sT[r][s2] = s2 < r ? accT[e] : 0.f;
         }
     }
-    // the upper-right blocks: zero in both
-    for (int idx = tid; idx < 16 * 16; idx += NT) {
-        const int r = idx / 16, s2 = 16 + idx % 16;
-        sT[r][s2] = 0.f;
-        Rp[r * BC + s2] = 0.f;
-    }
+    // the upper-right block is zero
+    for (int idx = tid; idx < 16 * 16; idx += NT) sT[idx / 16][16 + idx % 16] = 0.f;
     __syncthreads();
     // M = (I + T)^-1, one column per thread: x_r = [r == j] - sum_{s<r} T_rs x_s
     float* Rm = R + rec_m<DK>(p.dv);
