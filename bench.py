@@ -60,7 +60,7 @@ def parse():
     # the GPU leaves its idle clocks only after several milliseconds of work
     # (about 20 headline calls); the default warmup covers that with margin
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--decode-steps", type=int, default=200)
+    ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-gated", action="store_true",
                     help="skip the per-channel-gate prefill workloads")
@@ -123,12 +123,37 @@ def to_dev(x, bf16=False):
     return t.to("cuda").contiguous()
 
 
-def bench_prefill(args):
+CLOCK_RAMP_MS = 30.0  # the GPU leaves its idle clocks only after several ms of work
+
+
+def clock_ramp(call, min_ms=CLOCK_RAMP_MS):
+    """Untimed calls until at least min_ms of wall time has passed on the GPU
+    (synchronised), whatever the warmup count: the clocks ramp up with time,
+    not with the number of calls.  Returns the number of calls made."""
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        for _ in range(4):
+            call()
+        n += 4
+        torch.cuda.synchronize()
+        if (time.perf_counter() - t0) * 1e3 >= min_ms:
+            return n
+
+
+def bench_prefill(args, w=None, steps=None, warmup=None):
+    """Scalar-gate prefill (the throughput kernel) on workload w (default: the
+    B4 H16 T8192 headline): a clock ramp of >= 30 ms, `warmup` untimed calls,
+    then `steps` calls each bracketed by HIP events on the launch stream."""
     import torch
     import gated_delta_rule_77_amd as pdn
     from gated_delta_rule_77_amd import synth
 
-    w = synth.headline()
+    w = w or synth.headline()
+    steps = steps or args.steps
+    warmup = args.warmup if warmup is None else warmup
     q, k, v = to_dev(w.q, True), to_dev(w.k, True), to_dev(w.v, True)
     la, be = to_dev(w.log_alpha), to_dev(w.beta)
     o = torch.empty((w.B, w.H, w.T, w.dv), device="cuda", dtype=torch.float32)
@@ -137,15 +162,16 @@ def bench_prefill(args):
     def step():
         pdn.pdn_chunk_fwd(q, k, v, o, log_alpha=la, beta=be, ST=ST)
 
-    for _ in range(args.warmup):
+    ramp = clock_ramp(step)
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+          for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         ev[i][0].record(stream)
         step()
         ev[i][1].record(stream)
@@ -153,6 +179,7 @@ def bench_prefill(args):
     t1 = time.perf_counter()
     kern_ms = [a.elapsed_time(b) for a, b in ev]
     kernel_ms = sum(kern_ms) / len(kern_ms)
+    del q, k, v, la, be, o, ST
 
     BH, T, dk, dv = w.B * w.H, w.T, w.dk, w.dv
     qkv_bytes = BH * T * (2 * dk + dv) * 2
@@ -167,8 +194,30 @@ def bench_prefill(args):
         "elapsed_s": t1 - t0, "tokens": w.B * T, "kernel_ms": kernel_ms,
         "kernel_ms_min": min(kern_ms), "alg_bytes": alg_bytes, "alg_flops": alg_flops,
         "achieved_gbs": alg_bytes / ks / 1e9, "achieved_tflops": alg_flops / ks / 1e12,
-        "sample": w,
+        "clock_ramp_calls": ramp, "sample": w,
     }
+
+
+def bench_prefill_legs(args):
+    """The scalar-gate prefill at the other shapes: Gated DeltaNet B4 H16 T4096
+    and the headline gating at B=1 (16 heads: 64 workgroups)."""
+    import torch
+    from gated_delta_rule_77_amd import synth
+    res = {}
+    for name, mk, steps in (("gdn_B4_H16_T4096_d128", lambda: synth.gdn(), 30),
+                            ("gdn_B1_H16_T8192_d128", lambda: synth.headline(B=1), 30)):
+        r = bench_prefill(args, w=mk(), steps=steps, warmup=10)
+        res[name] = {
+            "B": r["B"], "H": r["H"], "T": r["T"], "dk": r["dk"], "dv": r["dv"],
+            "steps": steps, "kernel_ms": r["kernel_ms"],
+            "tokens_per_s": r["tokens"] / (r["kernel_ms"] / 1e3),
+            "alg_bytes_per_launch": r["alg_bytes"],
+            "roofline": {"bound": "hbm", "achieved": r["achieved_gbs"], "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": r["achieved_gbs"] / HBM_PEAK_GBS},
+            "mfma_alg_frac_of_peak": r["achieved_tflops"] / BF16_PEAK_TFLOPS,
+        }
+        torch.cuda.empty_cache()
+    return res
 
 
 def bench_decode(args):
@@ -206,12 +255,49 @@ def bench_decode(args):
     t1 = time.perf_counter()
     kern_ms = [a.elapsed_time(b) for a, b in ev]
     kernel_ms = sum(kern_ms) / n
+    kern_sorted = sorted(kern_ms)
+    median_ms = kern_sorted[n // 2]
+
+    # the same steps captured in a HIP graph (one graph of `pool` calls, one
+    # per distinct input slot), replayed until n steps have run: the per-step
+    # time without the host's launch overhead between calls
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):       # eager once on the capture stream first
+        for i in range(pool):
+            step(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        for i in range(pool):
+            step(i)
+    reps = max(1, n // pool)
+    for _ in range(10):
+        graph.replay()
+    torch.cuda.synchronize()
+    gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    tg0 = time.perf_counter()
+    for i in range(reps):
+        gev[i][0].record(stream)
+        graph.replay()
+        gev[i][1].record(stream)
+    torch.cuda.synchronize()
+    tg1 = time.perf_counter()
+    graph_step_ms = sorted(a.elapsed_time(b) for a, b in gev)[reps // 2] / pool
+    del graph
+
     BH, dk, dv = w.B * w.H, w.dk, w.dv
     alg_bytes = BH * (2 * dk * dv * 4 + (2 * dk + dv) * 2 + 2 * dk * 4 + 4 + dv * 4)
     gbs = alg_bytes / (kernel_ms / 1e3) / 1e9
     return {
         "workload": "decode_B256_H16_d128", "steps": n, "ms_per_step": (t1 - t0) * 1e3 / n,
-        "kernel_ms": kernel_ms, "alg_bytes_per_step": alg_bytes,
+        "kernel_ms": kernel_ms, "kernel_ms_median": median_ms,
+        "graph": {"steps": reps * pool, "ms_per_step_median": graph_step_ms,
+                  "wall_ms_per_step": (tg1 - tg0) * 1e3 / (reps * pool),
+                  "gbs": alg_bytes / (graph_step_ms / 1e3) / 1e9},
+        "alg_bytes_per_step": alg_bytes,
         "value": gbs, "unit": "GB/s", "tokens_per_s": w.B / ((t1 - t0) / n),
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS,
@@ -362,7 +448,10 @@ def cpu_baseline(w, target_s: float):
     sys.path.insert(0, ROOT)
     import oracle
 
-    threads = oracle.num_threads()
+    import tempfile
+    tmp = tempfile.mkdtemp(prefix="oracle_native_")
+    lib = oracle.load_native(tmp)   # built here, for this host's CPU
+    threads = oracle.num_threads(lib)
 
     def run(nbh, T):
         b_idx = [i // w.H for i in range(nbh)]
@@ -372,7 +461,7 @@ def cpu_baseline(w, target_s: float):
         args = (sel(w.q), sel(w.k), sel(w.v), w.alpha_mode, sel(w.log_alpha), w.beta_mode,
                 sel(w.beta), w.gamma_mode, sel(w.gamma))
         t0 = time.perf_counter()
-        oracle.delta_rule(*args, want_state=False)
+        oracle.delta_rule(*args, want_state=False, lib=lib)
         return time.perf_counter() - t0
 
     # calibrate on one (b, h) pair, then size the sample to the target time
@@ -392,6 +481,7 @@ def cpu_baseline(w, target_s: float):
             "sample": "%d (batch, head) pairs x first %d tokens of the B%d H%d T%d workload "
                       "(fp64 token recurrence, OpenMP over pairs; tokens/s = token-heads/s / H)"
                       % (nbh, T, w.B, w.H, w.T),
+            "build": "gcc " + " ".join(oracle.BASELINE_FLAGS),
             "seconds": el}
 
 
@@ -412,6 +502,7 @@ def main():
         sys.exit(1)
 
     pf = bench_prefill(args)
+    legs = bench_prefill_legs(args)
     dec = None if args.no_decode else bench_decode(args)
     gated = None if args.no_gated else bench_gated(args)
     bwd = None if args.no_bwd else bench_backward(args)
@@ -450,6 +541,7 @@ def main():
                  "alg_flops_per_launch": pf["alg_flops"],
                  "ceiling_frac_at_hbm_bound": (pf["alg_flops"] / (pf["alg_bytes"] / (HBM_PEAK_GBS * 1e9)))
                  / (BF16_PEAK_TFLOPS * 1e12)},
+        "prefill_legs": legs,
         "decode": dec,
         "per_channel_gates": gated,
         "backward": bwd,

@@ -188,6 +188,30 @@ def _stream(stream):
     return stream.cuda_stream
 
 
+def _shape(t, name, *allowed):
+    """Raise unless tensor t (None allowed only when None is listed) has one
+    of the allowed shapes.  The C ABI receives bare pointers and cannot know
+    a tensor's extent, so a wrongly shaped tensor would be read (or written)
+    past its end: every tensor is checked here before a pointer is taken."""
+    if t is None:
+        if None in allowed:
+            return
+        raise ValueError("%s is required" % name)
+    shapes = [a for a in allowed if a is not None]
+    if tuple(t.shape) not in shapes:
+        raise ValueError("%s must have shape %s, got %s" % (
+            name, " or ".join("[%s]" % ",".join(str(x) for x in a) for a in shapes),
+            list(t.shape)))
+
+
+def _same_device(ref, named):
+    """Every tensor must live on the device of `ref` (q)."""
+    for name, t in named:
+        if t is not None and not isinstance(t, int) and t.device != ref.device:
+            raise ValueError("%s is on %s, q on %s: every tensor must share q's device"
+                             % (name, t.device, ref.device))
+
+
 def _alpha_mode(log_alpha, lead):
     if log_alpha is None:
         return PDN_ALPHA_NONE
@@ -207,14 +231,26 @@ def _precond_fields(a, precond_eps, precond_mode, precond_x):
 def _chunk_args(q, k, v, o, log_alpha, beta, gamma, precond_eps, precond_A0,
                 precond_AT, S0, ST, workspace, key_mode, precond_mode=PDN_PRECOND_INVERSE,
                 precond_x=1.5):
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k must be [B,H,T,dk] and v [B,H,T,dv]")
     B, H, T, dk = q.shape
     dv = v.shape[-1]
     if tuple(k.shape) != (B, H, T, dk) or tuple(v.shape[:3]) != (B, H, T):
         raise ValueError("q, k must be [B,H,T,dk] and v [B,H,T,dv]")
-    if tuple(o.shape) != (B, H, T, dv):
-        raise ValueError("o must be [B,H,T,dv]")
+    _shape(o, "o", (B, H, T, dv))
     if q.dtype != k.dtype or q.dtype != v.dtype:
         raise ValueError("q, k, v must share one dtype")
+    _shape(log_alpha, "log_alpha", None, (B, H, T), (B, H, T, dk))
+    _shape(beta, "beta", (B, H, T), (B, H, T, dk))
+    _shape(gamma, "gamma", None, (B, H, T), (B, H, T, dv))
+    _shape(precond_A0, "precond_A0", None, (B, H, dk))
+    _shape(precond_AT, "precond_AT", None, (B, H, dk))
+    _shape(S0, "S0", None, (B, H, dk, dv))
+    _shape(ST, "ST", None, (B, H, dk, dv))
+    _same_device(q, (("k", k), ("v", v), ("o", o), ("log_alpha", log_alpha), ("beta", beta),
+                     ("gamma", gamma), ("precond_A0", precond_A0),
+                     ("precond_AT", precond_AT), ("S0", S0), ("ST", ST),
+                     ("workspace", workspace)))
     for name, t in (("log_alpha", log_alpha), ("beta", beta), ("gamma", gamma),
                     ("precond_A0", precond_A0), ("precond_AT", precond_AT),
                     ("S0", S0), ("ST", ST)):
@@ -290,21 +326,29 @@ def pdn_chunk_fwd(q, k, v, o, log_alpha=None, beta=None, gamma=None, precond_eps
 def _bwd_args(q, k, v, dO, dq, dk, dv, dlog_alpha, dbeta, dgamma, dS0, dA0, log_alpha, beta,
               gamma, precond_eps, precond_A0, S0, dST, workspace, key_mode, precond_mode,
               precond_x):
-    f = _chunk_args(q, k, v, dO, log_alpha, beta, gamma, precond_eps, precond_A0, None, S0,
-                    None, None, key_mode, precond_mode, precond_x)
-    f.o = None
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k must be [B,H,T,dk] and v [B,H,T,dv]")
     B, H, T, dkk = q.shape
     dvv = v.shape[-1]
     if tuple(dq.shape) != (B, H, T, dkk) or tuple(dk.shape) != (B, H, T, dkk):
         raise ValueError("dq, dk must be [B,H,T,dk]")
     if tuple(dv.shape) != (B, H, T, dvv):
         raise ValueError("dv must be [B,H,T,dv]")
+    _shape(dST, "dST", None, (B, H, dkk, dvv))
+    _shape(dS0, "dS0", None, (B, H, dkk, dvv))
+    _shape(dA0, "dA0", None, (B, H, dkk))
+    _same_device(q, (("dO", dO), ("dST", dST), ("dq", dq), ("dk", dk), ("dv", dv),
+                     ("dlog_alpha", dlog_alpha), ("dbeta", dbeta), ("dgamma", dgamma),
+                     ("dS0", dS0), ("dA0", dA0), ("workspace", workspace)))
     for name, t, like in (("dlog_alpha", dlog_alpha, log_alpha), ("dbeta", dbeta, beta),
                           ("dgamma", dgamma, gamma)):
         if (t is None) != (like is None):
             raise ValueError("%s must be given exactly when its gate is" % name)
         if t is not None and tuple(t.shape) != tuple(like.shape):
             raise ValueError("%s must have the shape of its gate" % name)
+    f = _chunk_args(q, k, v, dO, log_alpha, beta, gamma, precond_eps, precond_A0, None, S0,
+                    None, None, key_mode, precond_mode, precond_x)
+    f.o = None
     for name, t in (("dO", dO), ("dST", dST), ("dq", dq), ("dk", dk), ("dv", dv),
                     ("dlog_alpha", dlog_alpha), ("dbeta", dbeta), ("dgamma", dgamma),
                     ("dS0", dS0), ("dA0", dA0)):
@@ -369,6 +413,8 @@ def pdn_chunk_bwd(q, k, v, dO, dq, dk, dv, dlog_alpha=None, dbeta=None, dgamma=N
 
 def _decode_args(q, k, v, o, S, log_alpha, beta, gamma, precond_eps, precond_A, key_mode,
                  precond_mode=PDN_PRECOND_INVERSE, precond_x=1.5):
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k must be [B,H,dk] and v [B,H,dv]")
     B, H, dk = q.shape
     dv = v.shape[-1]
     if tuple(k.shape) != (B, H, dk) or tuple(v.shape[:2]) != (B, H):
@@ -377,6 +423,12 @@ def _decode_args(q, k, v, o, S, log_alpha, beta, gamma, precond_eps, precond_A, 
         raise ValueError("o must be [B,H,dv] and S [B,H,dk,dv]")
     if q.dtype != k.dtype or q.dtype != v.dtype:
         raise ValueError("q, k, v must share one dtype")
+    _shape(log_alpha, "log_alpha", None, (B, H), (B, H, dk))
+    _shape(beta, "beta", (B, H), (B, H, dk))
+    _shape(gamma, "gamma", None, (B, H), (B, H, dv))
+    _shape(precond_A, "precond_A", None, (B, H, dk))
+    _same_device(q, (("k", k), ("v", v), ("o", o), ("S", S), ("log_alpha", log_alpha),
+                     ("beta", beta), ("gamma", gamma), ("precond_A", precond_A)))
     for name, t in (("log_alpha", log_alpha), ("beta", beta), ("gamma", gamma),
                     ("precond_A", precond_A), ("S", S)):
         _f32(t, name)

@@ -501,14 +501,14 @@ struct Tile4 {
 };
 
 // (b, h) and first value column of state-pass unit u.  Both workgroups of a
-// unit run on XCD u mod 8 (see bwd_states_kernel); when the head count allows,
-// all column tiles of a head get the same u mod 8, so that they share the
-// chunk records in that XCD's L2.
+// unit run on XCD u mod kXcds (see bwd_states_kernel); when the head count
+// allows, all column tiles of a head get the same u mod kXcds, so that they
+// share the chunk records in that XCD's L2.
 __device__ __forceinline__ void unit_tile(const BwdParams& p, long u, long& bh, int& j0) {
     const int ntile = p.dv / JT;
-    if (p.nbh % 8 == 0) {
-        bh = (u / (8L * ntile)) * 8 + u % 8;
-        j0 = static_cast<int>((u / 8) % ntile) * JT;
+    if (p.nbh % kXcds == 0) {
+        bh = (u / (static_cast<long>(kXcds) * ntile)) * kXcds + u % kXcds;
+        j0 = static_cast<int>((u / kXcds) % ntile) * JT;
     } else {
         bh = u / ntile;
         j0 = static_cast<int>(u % ntile) * JT;
@@ -757,17 +757,17 @@ __device__ __forceinline__ void state_bwd_body(const BwdParams& p, float* smem, 
 // Both state passes in one launch: the reverse pass needs only the record
 // and dO, not the forward states, so the two chains run side by side, one
 // workgroup of each per CU, each filling the other's barrier and memory
-// waits.  Workgroups are dealt to the 8 XCDs in turn, so the roles alternate
-// every 8 workgroups (every XCD gets both); the grid is padded to 16 per 8
-// units and the padding exits at once.
+// waits.  Workgroups are dealt to the XCDs in turn, so the roles alternate
+// every kXcds workgroups (every XCD gets both); the grid is padded to
+// 2 kXcds per kXcds units and the padding exits at once.
 template <int DK>
 __global__ void __launch_bounds__(NT, 2) bwd_states_kernel(BwdParams p, long units) {
     constexpr int LDSF = fwd_lds_floats<DK>() > bwd_lds_floats<DK>() ? fwd_lds_floats<DK>()
                                                                      : bwd_lds_floats<DK>();
     __shared__ __attribute__((aligned(16))) float smem[LDSF];
-    const long unit = (blockIdx.x >> 4) * 8 + (blockIdx.x & 7);
+    const long unit = (blockIdx.x / (2 * kXcds)) * kXcds + blockIdx.x % kXcds;
     if (unit >= units) return;  // whole workgroup, before any barrier
-    if ((blockIdx.x >> 3) & 1) state_bwd_body<DK>(p, smem, unit);
+    if ((blockIdx.x / kXcds) & 1) state_bwd_body<DK>(p, smem, unit);
     else state_fwd_body<DK>(p, smem, unit);
 }
 
@@ -1434,7 +1434,8 @@ hipError_t run_bwd(const pdn_chunk_bwd_args& a, const BwdParams& p, hipStream_t 
     }
     if (p.stab) bwd_prep_kernel<DK, BF16, true><<<nch, NT, 0, s>>>(p);
     else bwd_prep_kernel<DK, BF16, false><<<nch, NT, 0, s>>>(p);
-    bwd_states_kernel<DK><<<16 * ((ntl + 7) / 8), NT, 0, s>>>(p, static_cast<long>(ntl));
+    bwd_states_kernel<DK><<<2 * kXcds * ((ntl + kXcds - 1) / kXcds), NT, 0, s>>>(
+        p, static_cast<long>(ntl));
     bwd_grads_kernel<DK, BF16><<<nch, NT, 0, s>>>(p);
     if (p.pre) {
         bwd_dA_scan_kernel<DK><<<nbh, DK, 0, s>>>(p);

@@ -206,16 +206,16 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
     const int g = lane >> 4;
     const int ln = lane & 15;
     const int ntile = p.dv / DVT;
-    // Workgroups are dealt round-robin to the 8 XCDs; when the head count allows,
+    // Workgroups are dealt round-robin to the XCDs; when the head count allows,
     // give all column tiles of a head the same XCD so they share its L2 for the
     // key, query and gate reads.
     const long nbh = gridDim.x / ntile;
     long bh;
     int tile;
-    if (nbh % 8 == 0) {
-        const long slot = blockIdx.x / 8;
+    if (nbh % kXcds == 0) {
+        const long slot = blockIdx.x / kXcds;
         tile = static_cast<int>(slot % ntile);
-        bh = (slot / ntile) * 8 + blockIdx.x % 8;
+        bh = (slot / ntile) * kXcds + blockIdx.x % kXcds;
     } else {
         bh = blockIdx.x / ntile;
         tile = static_cast<int>(blockIdx.x % ntile);

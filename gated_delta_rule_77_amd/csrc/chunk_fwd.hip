@@ -854,18 +854,15 @@ hipError_t launch_nw(const ChunkParams& p, long nbh, int nw, hipStream_t st) {
 
 // Waves per workgroup: the largest that still gives at least one workgroup
 // per compute unit, within what the dv tiling and the gate path allow.
-int choose_nw(long nbh, int dv, bool vec, bool f32in) {
-    const char* env = getenv("PDN_CHUNK_NW");
-    int forced = env ? atoi(env) : 0;
+int choose_nw(long nbh, int dv, bool vec, bool f32in, int ncu) {
     const int cands[3] = {4, 2, 1};
     int best = 0;
     for (int nw : cands) {
         if (dv % (16 * nw) != 0) continue;
         if (vec && nw == 1) continue;
         if (vec && f32in && nw == 4) continue;
-        if (forced && nw != forced) continue;
         if (!best) best = nw;  // largest allowed
-        if (nbh * (dv / (16 * nw)) >= 256) return nw;
+        if (nbh * (dv / (16 * nw)) >= ncu) return nw;
         best = nw;             // keep shrinking toward more workgroups
     }
     return best;
@@ -904,7 +901,7 @@ hipError_t launch_chunk_fwd(const pdn_chunk_fwd_args& a, hipStream_t stream) {
                      a.precond_eps >= 0.0f;
     const bool f32in = a.qkv_dtype == PDN_F32;
     const long nbh = static_cast<long>(a.B) * a.H;
-    const int nw = choose_nw(nbh, a.dv, vec, f32in);
+    const int nw = choose_nw(nbh, a.dv, vec, f32in, device_cu_count());
     if (nw == 0) return hipErrorNotSupported;
     if (a.dk == 128) {
         if (vec) return f32in ? launch_nw<128, true, true>(p, nbh, nw, stream)

@@ -619,10 +619,10 @@ __global__ void __launch_bounds__(NTHR) vec_chain_kernel(ChainParams p) {
         // all column tiles of a head on one XCD (when the head count allows),
         // so that they share its L2 for the chunk records
         const long nbh = gridDim.x / ntile;
-        if (nbh % 8 == 0) {
-            const long slot = blockIdx.x / 8;
+        if (nbh % kXcds == 0) {
+            const long slot = blockIdx.x / kXcds;
             tile = static_cast<int>(slot % ntile);
-            bh = (slot / ntile) * 8 + blockIdx.x % 8;
+            bh = (slot / ntile) * kXcds + blockIdx.x % kXcds;
         } else {
             bh = blockIdx.x / ntile;
             tile = static_cast<int>(blockIdx.x % ntile);
@@ -635,10 +635,10 @@ __global__ void __launch_bounds__(NTHR) vec_chain_kernel(ChainParams p) {
         const int units = ntile + (p.nseg - 1) * per_seg;
         const long nbh = gridDim.x / units;
         int u;
-        if (nbh % 8 == 0) {
-            const long slot = blockIdx.x / 8;
+        if (nbh % kXcds == 0) {
+            const long slot = blockIdx.x / kXcds;
             u = static_cast<int>(slot % units);
-            bh = (slot / units) * 8 + blockIdx.x % 8;
+            bh = (slot / units) * kXcds + blockIdx.x % kXcds;
         } else {
             bh = blockIdx.x / units;
             u = static_cast<int>(blockIdx.x % units);
@@ -1098,7 +1098,9 @@ void launch_prep(const PrepParams& pp, int km, bool stab, long nblk, hipStream_t
 
 // Sequence segments for few-head prefills: as many as fit one wave of chain
 // workgroups (one per CU), at least 8 chunks each, at most 8; fp32 output only
-// (the correction adds to the stored outputs).
+// (the correction adds to the stored outputs).  The slot count is the MI355X
+// CU count as a constant, not a device query: the segment count sets the
+// workspace size, which a caller may ask for before any device is current.
 constexpr long kChainSlots = 256;
 int vec_segments(const pdn_chunk_fwd_args& a) {
     if (a.o_dtype != PDN_F32) return 1;

@@ -195,8 +195,8 @@ hipError_t launch_dk_dv(const DecodeParams& p, bool bf16in, bool bf16out, long n
     // exactly the resident workgroups (three per compute unit: the launch
     // bounds keep the kernel within a third of the register file), each
     // walking many (b,h) pairs
-    constexpr long kResident = 256L * 3;
-    dim3 grid(static_cast<unsigned>(nbh < kResident ? nbh : kResident)), block(256);
+    const long resident = 3L * device_cu_count();
+    dim3 grid(static_cast<unsigned>(nbh < resident ? nbh : resident)), block(256);
     if (bf16in && bf16out) decode_kernel<DK, DV, true, true><<<grid, block, 0, st>>>(p, nbh);
     else if (bf16in) decode_kernel<DK, DV, true, false><<<grid, block, 0, st>>>(p, nbh);
     else if (bf16out) decode_kernel<DK, DV, false, true><<<grid, block, 0, st>>>(p, nbh);

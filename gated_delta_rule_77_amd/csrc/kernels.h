@@ -7,6 +7,15 @@
 
 namespace pdn {
 
+// Compute units of the current device (hipDeviceGetAttribute; 256 on an
+// MI355X), used to size persistent grids and to choose tile widths.
+int device_cu_count();
+
+// Workgroups are dealt to the XCDs of an MI355X (eight, each with its own
+// L2) in turn.  Launches place the workgroups that read the same head's rows
+// on one XCD by this count; it decides L2 locality only, never results.
+constexpr int kXcds = 8;
+
 // Single-token state update for every (b,h); returns a hipError_t.
 hipError_t launch_decode(const pdn_decode_args& a, hipStream_t stream);
 

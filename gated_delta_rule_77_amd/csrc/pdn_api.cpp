@@ -53,7 +53,9 @@ int check_gates(int32_t amode, const float* la, int32_t bmode, const float* beta
     return PDN_OK;
 }
 
-int check_chunk(const pdn_chunk_fwd_args* a) {
+// check_ws false: everything but the workspace (the size query, made before
+// the caller has one)
+int check_chunk(const pdn_chunk_fwd_args* a, bool check_ws = true) {
     if (!a) return PDN_EINVAL;
     if (a->B < 1 || a->H < 1 || a->T < 0 || a->dk < 1 || a->dv < 1) return PDN_EINVAL;
     if (!valid_dtype(a->qkv_dtype) || !valid_dtype(a->o_dtype)) return PDN_EINVAL;
@@ -67,7 +69,8 @@ int check_chunk(const pdn_chunk_fwd_args* a) {
     if (a->T > 0 && (!a->q || !a->k || !a->v || !a->o)) return PDN_EINVAL;
     // the kernels use 16-byte vector loads and stores
     const void* ptrs[] = {a->q, a->k, a->v, a->o, a->log_alpha, a->beta, a->gamma,
-                          a->precond_A0, a->precond_AT, a->S0, a->ST};
+                          a->precond_A0, a->precond_AT, a->S0, a->ST,
+                          check_ws ? a->workspace : nullptr};
     for (const void* ptr : ptrs)
         if (ptr && !aligned16(ptr)) return PDN_EINVAL;
     if (a->dk != 64 && a->dk != 128) return PDN_EUNSUPPORTED;
@@ -88,6 +91,7 @@ int check_chunk(const pdn_chunk_fwd_args* a) {
         const float* st = a->ST;
         if (s0 < st + n && st < s0 + n) return PDN_EINVAL;
     }
+    if (!check_ws) return PDN_OK;
     const size_t need = pdn::chunk_fwd_workspace_bytes(*a);
     if (need > 0 && (!a->workspace || a->workspace_bytes < need)) return PDN_EWORKSPACE;
     return PDN_OK;
@@ -96,7 +100,7 @@ int check_chunk(const pdn_chunk_fwd_args* a) {
 // B * H * T for the backward: its per-chunk grids stay below 2^31 workgroups
 constexpr long kMaxBwdTokens = 1L << 35;
 
-int check_bwd(const pdn_chunk_bwd_args* a) {
+int check_bwd(const pdn_chunk_bwd_args* a, bool check_ws = true) {
     if (!a) return PDN_EINVAL;
     const pdn_chunk_fwd_args& f = a->fwd;
     if (f.B < 1 || f.H < 1 || f.T < 0 || f.dk < 1 || f.dv < 1) return PDN_EINVAL;
@@ -117,11 +121,12 @@ int check_bwd(const pdn_chunk_bwd_args* a) {
     }
     const void* ptrs[] = {f.q, f.k, f.v, f.log_alpha, f.beta, f.gamma, f.precond_A0, f.S0,
                           a->dO, a->dST, a->dq, a->dk, a->dv, a->dlog_alpha, a->dbeta,
-                          a->dgamma, a->dS0, a->dA0};
+                          a->dgamma, a->dS0, a->dA0, check_ws ? a->workspace : nullptr};
     for (const void* ptr : ptrs)
         if (ptr && !aligned16(ptr)) return PDN_EINVAL;
     if (f.dk != 64 && f.dk != 128) return PDN_EUNSUPPORTED;
     if (f.dv % 32 != 0 || f.dv > 256) return PDN_EUNSUPPORTED;
+    if (!check_ws) return PDN_OK;
     const size_t need = pdn::chunk_bwd_workspace_bytes(*a);
     if (need > 0 && (!a->workspace || a->workspace_bytes < need)) return PDN_EWORKSPACE;
     return PDN_OK;
@@ -146,6 +151,19 @@ int check_decode(const pdn_decode_args* a) {
 
 }  // namespace
 
+namespace pdn {
+
+int device_cu_count() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n < 1)
+        return 256;  // the MI355X count; only grid sizes depend on it
+    return n;
+}
+
+}  // namespace pdn
+
 extern "C" {
 
 int pdn_abi_version(void) { return PDN_ABI_VERSION; }
@@ -164,16 +182,11 @@ const char* pdn_strerror(int code) {
 int pdn_chunk_fwd_workspace_size(const pdn_chunk_fwd_args* args, size_t* bytes) {
     if (!args || !bytes) return PDN_EINVAL;
     try {
-        pdn_chunk_fwd_args probe = *args;
-        probe.workspace = nullptr;
-        probe.workspace_bytes = 0;
-        // validate everything except the workspace itself
-        const size_t need = pdn::chunk_fwd_workspace_bytes(probe);
-        probe.workspace_bytes = need;
-        probe.workspace = need ? reinterpret_cast<void*>(uintptr_t(1)) : nullptr;
-        const int rc = check_chunk(&probe);
+        // validate everything except the workspace itself, then size it (the
+        // size arithmetic relies on the validated bounds)
+        const int rc = check_chunk(args, false);
         if (rc != PDN_OK) return rc;
-        *bytes = need;
+        *bytes = pdn::chunk_fwd_workspace_bytes(*args);
         return PDN_OK;
     } catch (...) {
         return PDN_EINVAL;
@@ -203,13 +216,9 @@ int pdn_chunk_fwd(const pdn_chunk_fwd_args* args, void* stream) {
 int pdn_chunk_bwd_workspace_size(const pdn_chunk_bwd_args* args, size_t* bytes) {
     if (!args || !bytes) return PDN_EINVAL;
     try {
-        pdn_chunk_bwd_args probe = *args;
-        const size_t need = pdn::chunk_bwd_workspace_bytes(probe);
-        probe.workspace_bytes = need;
-        probe.workspace = need ? reinterpret_cast<void*>(uintptr_t(256)) : nullptr;
-        const int rc = check_bwd(&probe);
+        const int rc = check_bwd(args, false);
         if (rc != PDN_OK) return rc;
-        *bytes = need;
+        *bytes = pdn::chunk_bwd_workspace_bytes(*args);
         return PDN_OK;
     } catch (...) {
         return PDN_EINVAL;

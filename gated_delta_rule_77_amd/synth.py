@@ -191,16 +191,45 @@ def decode(B=256, H=16, d=128, steps=1000, seed=0) -> Workload:
     la = np.empty_like(q)
     be = np.empty_like(q)
     for t in range(steps):
-        q[:, :, t] = _l2_normalise(rng.standard_normal((B, H, d), dtype=np.float32))
-        k[:, :, t] = _l2_normalise(rng.standard_normal((B, H, d), dtype=np.float32))
-        v[:, :, t] = rng.standard_normal((B, H, d), dtype=np.float32)
-        la[:, :, t] = _neg_softplus(rng.standard_normal((B, H, d), dtype=np.float32))
-        be[:, :, t] = _sigmoid(rng.standard_normal((B, H, d), dtype=np.float32))
+        q[:, :, t], k[:, :, t], v[:, :, t], la[:, :, t], be[:, :, t] = \
+            _decode_step_draws(rng, B, H, d)
     q, k, v = round_to_bf16(q), round_to_bf16(k), round_to_bf16(v)
     gamma = be.astype(np.float64).mean(axis=-1).astype(np.float32)
     S0 = (0.02 * rng.standard_normal((B, H, d, d), dtype=np.float32)).astype(np.float32)
     return Workload("decode", B, H, steps, d, d, DT_BF16, q, k, v,
                     ALPHA_VEC, la, GATE_VEC, be, GATE_SCALAR, gamma, S0=S0)
+
+
+def _decode_step_draws(rng, B, H, d):
+    q = _l2_normalise(rng.standard_normal((B, H, d), dtype=np.float32))
+    k = _l2_normalise(rng.standard_normal((B, H, d), dtype=np.float32))
+    v = rng.standard_normal((B, H, d), dtype=np.float32)
+    la = _neg_softplus(rng.standard_normal((B, H, d), dtype=np.float32))
+    be = _sigmoid(rng.standard_normal((B, H, d), dtype=np.float32))
+    return q, k, v, la, be
+
+
+def decode_stream(B=256, H=16, d=128, steps=1000, seed=0):
+    """The ``decode`` workload without holding all steps in memory.
+
+    Returns (S0, step_iter): S0 [B,H,d,d] as ``decode`` draws it, and an
+    iterator over the steps yielding (q, k, v, log_alpha, beta, gamma), each
+    [B,H,d] (gamma [B,H]), equal to ``decode(...)``'s slices at that step.
+    ``decode`` draws S0 after all steps, so the stream runs the generator
+    twice: once to reach S0, once to yield the steps.
+    """
+    rng = np.random.default_rng(seed)
+    for _ in range(steps):
+        _decode_step_draws(rng, B, H, d)
+    S0 = (0.02 * rng.standard_normal((B, H, d, d), dtype=np.float32)).astype(np.float32)
+
+    def steps_iter():
+        r = np.random.default_rng(seed)
+        for _ in range(steps):
+            q, k, v, la, be = _decode_step_draws(r, B, H, d)
+            gamma = be.astype(np.float64).mean(axis=-1).astype(np.float32)
+            yield round_to_bf16(q), round_to_bf16(k), round_to_bf16(v), la, be, gamma
+    return S0, steps_iter()
 
 
 def headline(B=4, H=16, T=8192, d=128, seed=0) -> Workload:

@@ -249,6 +249,9 @@ const char *pdn_strerror(int code);
 
 /* Device scratch bytes pdn_chunk_fwd needs for these arguments (0 is valid).
  * Returns PDN_OK and writes *bytes, or a PDN_E* code for invalid arguments.
+ * (An int status with the size through a pointer, rather than a bare size_t
+ * return, so that invalid arguments are reported as on every other call; a
+ * size of 0 is a valid answer and cannot double as an error value.)
  * Non-zero only for bf16 q/k/v with dk == 128 and a per-channel gate, the
  * preconditioner or asymmetric keys: those calls first write, for every (b, h)
  * and 32-token chunk, a 56 KiB record of gate-scaled operands and solve blocks (plus 512
@@ -260,15 +263,28 @@ int pdn_chunk_fwd_workspace_size(const pdn_chunk_fwd_args *args, size_t *bytes);
  * would return for these arguments before launching. */
 int pdn_chunk_fwd_check(const pdn_chunk_fwd_args *args);
 
-/* Prefill: o, and ST / precond_AT when given.  Chunk length 64 (32 for the
- * per-channel-gate path above); T need not be a multiple of it and results do
- * not depend on where chunks fall. */
+/* Prefill: o, and ST / precond_AT when given, for the recurrence at the top
+ * of this file, computed chunkwise: per chunk the decayed Gram blocks of the
+ * gain-scaled keys, a unit-lower-triangular (I + T)^-1 solve for the WY
+ * factors, and a state carried from chunk to chunk ("Gated DeltaNet-2",
+ * method section 3: the decay absorbed into the erase and write matrices, the
+ * WY / UT form; "FG^2-GDN" section 2.3: the chunked form with fine-grained
+ * gates).  Chunk length 64 (32 for the per-channel-gate path above); T need
+ * not be a multiple of it and results do not depend on where chunks fall.
+ * Returns PDN_OK, or a PDN_E* code before any launch (see the conventions);
+ * PDN_EHIP if a launch fails. */
 int pdn_chunk_fwd(const pdn_chunk_fwd_args *args, void *stream);
 
 /* Validate only, as pdn_chunk_fwd_check. */
 int pdn_decode_check(const pdn_decode_args *args);
 
-/* Decode one token for all (b,h): o, S in place, precond_A in place. */
+/* Decode one token for all (b,h): the recurrence at the top of this file
+ * with T = 1 against the resident state ("Gated DeltaNet-2", method section 1:
+ * S_t = (I - k k^T) D_t S_{t-1} + k v^T with D_t = Diag(alpha_t), in the
+ * gain placement of "FG^2-GDN" section 2.1; the running k (.) k of
+ * "Preconditioned DeltaNet" section 2.2 advanced by one token).  Writes o,
+ * overwrites S with S_t and precond_A with A_t; one pass over S.  Returns
+ * PDN_OK, or a PDN_E* code before any launch; PDN_EHIP if the launch fails. */
 int pdn_decode_step(const pdn_decode_args *args, void *stream);
 
 /* Device scratch bytes pdn_chunk_bwd needs (PDN_OK and *bytes, or a PDN_E*

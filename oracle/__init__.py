@@ -47,7 +47,8 @@ PRECOND_INVERSE, PRECOND_STABILISED = 0, 1
 
 
 def build(force: bool = False) -> str:
-    """Compile recurrence.c with gcc (plain -O2, OpenMP, no fast-math)."""
+    """Compile recurrence.c with gcc (plain -O2, OpenMP, no fast-math): the
+    library the tests use, portable to any x86-64 host."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp%d" % os.getpid()
         subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared",
@@ -56,31 +57,48 @@ def build(force: bool = False) -> str:
     return _LIB
 
 
+BASELINE_FLAGS = ["-O3", "-march=native", "-ffp-contract=off", "-fopenmp"]
+
+
+def load_native(outdir: str):
+    """The same source built with BASELINE_FLAGS into `outdir` (for timing the
+    oracle as a CPU baseline on the machine it runs on; the arithmetic is the
+    same: no fast-math, no contraction into fused multiply-adds).  Returns a
+    library handle for the `lib=` argument of delta_rule."""
+    so = os.path.join(outdir, "liboracle_native.so")
+    subprocess.check_call(["gcc", *BASELINE_FLAGS, "-fPIC", "-shared", "-std=c99", _SRC,
+                           "-o", so, "-lm"])
+    return _configure(ctypes.CDLL(so))
+
+
+def _configure(lib):
+    f = lib.oracle_delta_rule
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    f.argtypes = [I, I, I, I, I, P, P, P, I, P, I, P, I, P,
+                  ctypes.c_double, P, P, P, P, P, I, I, ctypes.c_double]
+    f.restype = I
+    g = lib.oracle_delta_rule_bwd
+    g.argtypes = [I, I, I, I, I, P, P, P, I, P, I, P, I, P, ctypes.c_double, P, P,
+                  I, I, ctypes.c_double, P, P, P, P, P, P, P, P, P, P]
+    g.restype = I
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = I
+    return lib
+
+
 def _load():
     global _lib
     with _lock:
         if _lib is None:
             build()
-            lib = ctypes.CDLL(_LIB)
-            f = lib.oracle_delta_rule
-            P = ctypes.c_void_p
-            I = ctypes.c_int
-            f.argtypes = [I, I, I, I, I, P, P, P, I, P, I, P, I, P,
-                          ctypes.c_double, P, P, P, P, P, I, I, ctypes.c_double]
-            f.restype = I
-            g = lib.oracle_delta_rule_bwd
-            g.argtypes = [I, I, I, I, I, P, P, P, I, P, I, P, I, P, ctypes.c_double, P, P,
-                          I, I, ctypes.c_double, P, P, P, P, P, P, P, P, P, P]
-            g.restype = I
-            lib.oracle_num_threads.argtypes = []
-            lib.oracle_num_threads.restype = I
-            _lib = lib
+            _lib = _configure(ctypes.CDLL(_LIB))
     return _lib
 
 
-def num_threads() -> int:
+def num_threads(lib=None) -> int:
     """OpenMP threads the oracle runs on (its parallelism is over (b, h))."""
-    return int(_load().oracle_num_threads())
+    return int((lib or _load()).oracle_num_threads())
 
 
 def _f64(x):
@@ -96,15 +114,16 @@ def _ptr(x):
 def delta_rule(q, k, v, alpha_mode, log_alpha, beta_mode, beta, gamma_mode,
                gamma, precond_eps: float = -1.0, A0=None, S0=None,
                want_state: bool = True, key_mode: int = KEY_SYMMETRIC,
-               precond_mode: int = PRECOND_INVERSE, precond_x: float = 1.5):
+               precond_mode: int = PRECOND_INVERSE, precond_x: float = 1.5, lib=None):
     """Run the fp64 recurrence.  Returns (o, S_T, A_T) as float64 arrays.
 
     Shapes follow the C ABI: q, k [B,H,T,dk]; v [B,H,T,dv]; gates and
     ``key_mode`` and ``precond_mode`` / ``precond_x`` (the bound x of the
     stabilised coefficient) as in ``recurrence.c``.  A_T is None unless the
-    preconditioner is on.
+    preconditioner is on.  ``lib``: a handle from load_native (default: the
+    library build() makes).
     """
-    lib = _load()
+    lib = lib or _load()
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, H, T, dk = q.shape
     dv = v.shape[-1]

@@ -433,3 +433,132 @@ def test_bwd_workspace_size(lib):
     # T = 0 needs none
     a.fwd.T = 0
     assert _bws(lib, a) == (pdn.PDN_OK, 0)
+
+
+def test_misaligned_workspace_is_rejected(lib):
+    # the per-channel-gate kernels and the backward move their records with
+    # 16-byte vector and buffer accesses: an offset workspace is refused
+    a = _chunk_ok()
+    a.workspace = FAKE + 8
+    assert _ccheck(lib, a) == pdn.PDN_EINVAL
+    assert lib.pdn_chunk_fwd(ctypes.byref(a), None) == pdn.PDN_EINVAL
+    a.workspace = FAKE + 16
+    assert _ccheck(lib, a) == pdn.PDN_OK
+    b = _bwd_ok()
+    b.workspace = FAKE + 4
+    assert _bcheck(lib, b) == pdn.PDN_EINVAL
+    assert lib.pdn_chunk_bwd(ctypes.byref(b), None) == pdn.PDN_EINVAL
+
+
+# ---------------------------------------------------------------------------
+# the Python binding checks every tensor's shape and device before it takes a
+# pointer (the C ABI cannot know a tensor's extent).  Meta tensors carry a
+# shape and no memory, so these run without a GPU: a shape error is reported
+# by name before the binding would refuse the tensor for not being on a GPU.
+# ---------------------------------------------------------------------------
+
+def _meta(*shape):
+    import torch
+    return torch.empty(shape, device="meta", dtype=torch.float32)
+
+
+def _meta_bf16(*shape):
+    import torch
+    return torch.empty(shape, device="meta", dtype=torch.bfloat16)
+
+
+B_, H_, T_, DK_, DV_ = 2, 3, 10, 128, 64
+
+
+def _fwd_kwargs():
+    return dict(q=_meta_bf16(B_, H_, T_, DK_), k=_meta_bf16(B_, H_, T_, DK_),
+                v=_meta_bf16(B_, H_, T_, DV_), o=_meta(B_, H_, T_, DV_),
+                log_alpha=_meta(B_, H_, T_, DK_), beta=_meta(B_, H_, T_, DK_),
+                gamma=_meta(B_, H_, T_, DV_), precond_eps=1e-6,
+                precond_A0=_meta(B_, H_, DK_), precond_AT=_meta(B_, H_, DK_),
+                S0=_meta(B_, H_, DK_, DV_), ST=_meta(B_, H_, DK_, DV_))
+
+
+@pytest.mark.parametrize("name,bad", [
+    ("o", (B_, H_, T_, DK_)),
+    ("log_alpha", (B_, H_, T_, DV_)),          # per value channel: wrong axis
+    ("log_alpha", (B_, H_)),
+    ("beta", (B_, H_, T_, DV_)),               # a [B,H,T,dv] vector beta with dv < dk
+    ("beta", (B_, H_, T_ + 1)),
+    ("gamma", (B_, H_, T_, DK_)),
+    ("precond_A0", (B_, H_, DV_)),
+    ("precond_AT", (H_, DK_)),
+    ("S0", (B_, H_, DV_, DK_)),
+    ("ST", (H_, DK_, DV_)),                    # [H,dk,dv]: would be written past its end
+])
+def test_binding_rejects_misshaped_chunk_tensors(name, bad):
+    kw = _fwd_kwargs()
+    kw[name] = _meta(*bad)
+    with pytest.raises(ValueError, match=name):
+        pdn.pdn_chunk_fwd(**kw)
+    with pytest.raises(ValueError, match=name):
+        pdn.pdn_chunk_fwd_workspace_size(**kw)
+
+
+def test_binding_requires_beta():
+    kw = _fwd_kwargs()
+    kw["beta"] = None
+    with pytest.raises(ValueError, match="beta"):
+        pdn.pdn_chunk_fwd(**kw)
+
+
+def test_binding_shape_check_accepts_every_gate_rank():
+    # well-shaped meta tensors pass the shape checks and stop only at the
+    # device check (they live in no device memory)
+    for la, be, ga in (((B_, H_, T_), (B_, H_, T_), (B_, H_, T_)),
+                       ((B_, H_, T_, DK_), (B_, H_, T_, DK_), None),
+                       (None, (B_, H_, T_), (B_, H_, T_, DV_))):
+        kw = _fwd_kwargs()
+        kw["log_alpha"] = None if la is None else _meta(*la)
+        kw["beta"] = _meta(*be)
+        kw["gamma"] = None if ga is None else _meta(*ga)
+        with pytest.raises(ValueError, match="device memory"):
+            pdn.pdn_chunk_fwd(**kw)
+
+
+def test_binding_rejects_tensors_on_another_device():
+    import torch
+    kw = _fwd_kwargs()
+    kw["S0"] = torch.zeros((B_, H_, DK_, DV_), dtype=torch.float32)   # host memory
+    with pytest.raises(ValueError, match="S0 is on cpu"):
+        pdn.pdn_chunk_fwd(**kw)
+
+
+@pytest.mark.parametrize("name,bad", [
+    ("log_alpha", (B_, H_, DV_)),
+    ("beta", (B_, H_, DV_)),
+    ("gamma", (B_, H_, DK_)),
+    ("precond_A", (B_, H_, DV_)),
+])
+def test_binding_rejects_misshaped_decode_tensors(name, bad):
+    kw = dict(q=_meta_bf16(B_, H_, DK_), k=_meta_bf16(B_, H_, DK_), v=_meta_bf16(B_, H_, DV_),
+              o=_meta(B_, H_, DV_), S=_meta(B_, H_, DK_, DV_), log_alpha=_meta(B_, H_, DK_),
+              beta=_meta(B_, H_, DK_), gamma=_meta(B_, H_, DV_), precond_eps=1e-6,
+              precond_A=_meta(B_, H_, DK_))
+    kw[name] = _meta(*bad)
+    with pytest.raises(ValueError, match=name):
+        pdn.pdn_decode_step(**kw)
+
+
+@pytest.mark.parametrize("name,bad", [
+    ("dST", (B_, H_, DV_, DK_)),
+    ("dS0", (B_, H_, DK_)),
+    ("dA0", (B_, H_, DK_, 1)),
+    ("dO", (B_, H_, T_, DK_)),
+])
+def test_binding_rejects_misshaped_bwd_tensors(name, bad):
+    f = _fwd_kwargs()
+    kw = dict(q=f["q"], k=f["k"], v=f["v"], dO=_meta(B_, H_, T_, DV_),
+              dq=_meta(B_, H_, T_, DK_), dk=_meta(B_, H_, T_, DK_), dv=_meta(B_, H_, T_, DV_),
+              dlog_alpha=_meta(B_, H_, T_, DK_), dbeta=_meta(B_, H_, T_, DK_),
+              dgamma=_meta(B_, H_, T_, DV_), dS0=_meta(B_, H_, DK_, DV_), dA0=_meta(B_, H_, DK_),
+              log_alpha=f["log_alpha"], beta=f["beta"], gamma=f["gamma"], precond_eps=1e-6,
+              precond_A0=f["precond_A0"], S0=f["S0"], dST=_meta(B_, H_, DK_, DV_))
+    kw[name] = _meta(*bad)
+    with pytest.raises(ValueError, match=name if name != "dO" else "o must"):
+        pdn.pdn_chunk_bwd(**kw)

@@ -324,3 +324,33 @@ def test_bwd_deterministic():
     for n in GRADS:
         if a[n] is not None:
             assert np.array_equal(a[n], b[n]), n
+
+
+# ---------------------------------------------------------------------------
+# strong decay: the backward applies the forward's clamp of log alpha at -10
+# (include/pdn.h), so it is the gradient of the clamped recurrence: compared
+# with the oracle fed the clamped log alpha, with a zero d log alpha wherever
+# the clamp is active
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("amode,bf16", [(synth.ALPHA_SCALAR, False), (synth.ALPHA_VEC, False),
+                                        (synth.ALPHA_VEC, True)])
+def test_bwd_strong_decay(amode, bf16):
+    d = 128 if bf16 else 64
+    w = rand_workload(700 + amode + 2 * bf16, 1, 2, 150, d, d, amode, synth.GATE_VEC,
+                      synth.GATE_SCALAR, False, bf16)
+    rng = np.random.default_rng(701)
+    m = rng.random(w.log_alpha.shape) < 0.08
+    w.log_alpha[m] = rng.uniform(-30.0, -10.0, int(m.sum())).astype(np.float32)
+    w.log_alpha.reshape(-1)[:3] = -30.0
+    clamp_mask = w.log_alpha < -10.0
+    assert clamp_mask.any()
+    dO, dST = synth.upstream_grads(w, 3)
+    g = run_bwd(w, dO, dST)
+    wc = synth.Workload(w.name, w.B, w.H, w.T, w.dk, w.dv, w.qkv_dtype, w.q, w.k, w.v,
+                        w.alpha_mode, np.maximum(w.log_alpha, np.float32(-10.0)), w.beta_mode,
+                        w.beta, w.gamma_mode, w.gamma, precond_eps=w.precond_eps, S0=w.S0)
+    ref, tol = conditioning_tol(wc, dO, dST)
+    compare("bwd strong decay a%d bf16=%d (vs clamped oracle)" % (amode, bf16), g, ref, tol)
+    assert np.all(g["dlog_alpha"][clamp_mask] == 0.0)
+    assert np.all(g["dlog_alpha"][~clamp_mask] != 0.0)
