@@ -351,6 +351,12 @@ def test_bwd_strong_decay(amode, bf16):
                         w.alpha_mode, np.maximum(w.log_alpha, np.float32(-10.0)), w.beta_mode,
                         w.beta, w.gamma_mode, w.gamma, precond_eps=w.precond_eps, S0=w.S0)
     ref, tol = conditioning_tol(wc, dO, dST)
-    compare("bwd strong decay a%d bf16=%d (vs clamped oracle)" % (amode, bf16), g, ref, tol)
+    # the oracle differentiates its input at -10 where the kernel clamps (and
+    # so gives 0 there): d log alpha is compared on the unclamped entries
+    compare("bwd strong decay a%d bf16=%d (vs clamped oracle)" % (amode, bf16), g, ref, tol,
+            skip=("dlog_alpha",))
+    e = rel_l2(g["dlog_alpha"][~clamp_mask], ref["dlog_alpha"][~clamp_mask])
+    report("bwd strong decay a%d bf16=%d d log alpha, unclamped entries" % (amode, bf16), e=e)
+    assert e < tol["dlog_alpha"], (e, tol["dlog_alpha"])
     assert np.all(g["dlog_alpha"][clamp_mask] == 0.0)
     assert np.all(g["dlog_alpha"][~clamp_mask] != 0.0)
