@@ -10,6 +10,7 @@ PyTorch is used for device memory and streams only.
 
 Entry points (same names as the C ABI):
     pdn_chunk_fwd(...)                 prefill over [B,H,T,d]
+    pdn_chunk_fwd_noalloc(...)         the same with the library's static scratch
     pdn_chunk_fwd_workspace_size(...)  scratch bytes the prefill needs
     pdn_decode_step(...)               one token against a resident state
     pdn_chunk_bwd(...)                 gradients of the prefill
@@ -26,9 +27,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpdn.so")
 
 # The argument structs below mirror this version of include/pdn.h.
-PDN_ABI_VERSION = 4
+PDN_ABI_VERSION = 5
 
-PDN_OK, PDN_EINVAL, PDN_EUNSUPPORTED, PDN_EWORKSPACE, PDN_EHIP = 0, -1, -2, -3, -4
+PDN_OK, PDN_EINVAL, PDN_EUNSUPPORTED, PDN_EWORKSPACE, PDN_EHIP, PDN_ESCRATCH = 0, -1, -2, -3, -4, -5
+PDN_NOALLOC_SCRATCH_BYTES = 256 << 20   # static scratch of pdn_chunk_fwd_noalloc
 PDN_F32, PDN_BF16 = 0, 1
 PDN_ALPHA_NONE, PDN_ALPHA_SCALAR, PDN_ALPHA_VEC = 0, 1, 2
 PDN_GATE_SCALAR, PDN_GATE_VEC, PDN_GAMMA_SAME_AS_BETA = 1, 2, 3
@@ -78,8 +80,9 @@ class DecodeArgs(ctypes.Structure):
 
 
 EXPORTED = ("pdn_abi_version", "pdn_strerror", "pdn_chunk_fwd_workspace_size",
-            "pdn_chunk_fwd_check", "pdn_chunk_fwd", "pdn_decode_check", "pdn_decode_step",
-            "pdn_chunk_bwd_workspace_size", "pdn_chunk_bwd_check", "pdn_chunk_bwd")
+            "pdn_chunk_fwd_check", "pdn_chunk_fwd", "pdn_chunk_fwd_noalloc", "pdn_decode_check",
+            "pdn_decode_step", "pdn_chunk_bwd_workspace_size", "pdn_chunk_bwd_check",
+            "pdn_chunk_bwd")
 
 _lib = None
 _lock = threading.Lock()
@@ -114,6 +117,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         lib.pdn_chunk_fwd_check.restype = ctypes.c_int
         lib.pdn_chunk_fwd.argtypes = [ctypes.POINTER(ChunkFwdArgs), _P]
         lib.pdn_chunk_fwd.restype = ctypes.c_int
+        lib.pdn_chunk_fwd_noalloc.argtypes = [ctypes.POINTER(ChunkFwdArgs), _P]
+        lib.pdn_chunk_fwd_noalloc.restype = ctypes.c_int
         lib.pdn_chunk_bwd_workspace_size.argtypes = [ctypes.POINTER(ChunkBwdArgs),
                                                      ctypes.POINTER(ctypes.c_size_t)]
         lib.pdn_chunk_bwd_workspace_size.restype = ctypes.c_int
@@ -321,6 +326,22 @@ def pdn_chunk_fwd(q, k, v, o, log_alpha=None, beta=None, gamma=None, precond_eps
     rc = lib.pdn_chunk_fwd(ctypes.byref(a), _stream(stream))
     if rc != PDN_OK:
         raise PdnError(rc, "pdn_chunk_fwd")
+
+
+def pdn_chunk_fwd_noalloc(q, k, v, o, log_alpha=None, beta=None, gamma=None, precond_eps=None,
+                          precond_A0=None, precond_AT=None, S0=None, ST=None, stream=None,
+                          key_mode=PDN_KEY_SYMMETRIC, precond_mode=PDN_PRECOND_INVERSE,
+                          precond_x=1.5) -> None:
+    """pdn_chunk_fwd without a workspace argument and without any allocation:
+    the scratch comes from the library's static per-GPU array of
+    PDN_NOALLOC_SCRATCH_BYTES (PdnError with PDN_ESCRATCH when the call needs
+    more).  For callers that cannot allocate, e.g. under HIP graph capture.
+    Calls on one GPU share that array: they must not overlap."""
+    a = _chunk_args(q, k, v, o, log_alpha, beta, gamma, precond_eps, precond_A0,
+                    precond_AT, S0, ST, None, key_mode, precond_mode, precond_x)
+    rc = load_library().pdn_chunk_fwd_noalloc(ctypes.byref(a), _stream(stream))
+    if rc != PDN_OK:
+        raise PdnError(rc, "pdn_chunk_fwd_noalloc")
 
 
 def _bwd_args(q, k, v, dO, dq, dk, dv, dlog_alpha, dbeta, dgamma, dS0, dA0, log_alpha, beta,

@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "kernels.h"
 #include "pdn.h"
@@ -149,6 +150,30 @@ int check_decode(const pdn_decode_args* a) {
     return PDN_OK;
 }
 
+// Scratch of pdn_chunk_fwd_noalloc: one copy per GPU, loaded with the code
+// object (no allocation call makes it).  In host code `scratch` is a host-side
+// stand-in for the symbol, never a device address: every use goes through the
+// per-device address from hipGetSymbolAddress below.
+static __device__ __align__(256) unsigned char scratch[PDN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+// Device address of `scratch` on the current device, looked up once per device
+// (with that device current) and kept; nullptr if HIP reports an error.
+void* scratch_on_current_device() {
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        addr[dev] = p;
+    }
+    return addr[dev];
+}
+
 }  // namespace
 
 namespace pdn {
@@ -175,6 +200,9 @@ const char* pdn_strerror(int code) {
         case PDN_EUNSUPPORTED: return "valid request outside what the kernels support";
         case PDN_EWORKSPACE: return "workspace missing or too small";
         case PDN_EHIP: return "HIP runtime error at launch";
+        case PDN_ESCRATCH:
+            return "call needs more scratch than pdn_chunk_fwd_noalloc holds "
+                   "(PDN_NOALLOC_SCRATCH_BYTES): pass a workspace to pdn_chunk_fwd";
         default: return "unknown error code";
     }
 }
@@ -206,6 +234,29 @@ int pdn_chunk_fwd(const pdn_chunk_fwd_args* args, void* stream) {
         const int rc = check_chunk(args);
         if (rc != PDN_OK) return rc;
         const hipError_t e = pdn::launch_chunk_fwd(*args, static_cast<hipStream_t>(stream));
+        if (e == hipErrorNotSupported) return PDN_EUNSUPPORTED;
+        return e == hipSuccess ? PDN_OK : PDN_EHIP;
+    } catch (...) {
+        return PDN_EHIP;
+    }
+}
+
+int pdn_chunk_fwd_noalloc(const pdn_chunk_fwd_args* args, void* stream) {
+    try {
+        int rc = check_chunk(args, false);
+        if (rc != PDN_OK) return rc;
+        pdn_chunk_fwd_args a = *args;
+        const size_t need = pdn::chunk_fwd_workspace_bytes(a);
+        if (need > PDN_NOALLOC_SCRATCH_BYTES) return PDN_ESCRATCH;
+        a.workspace = nullptr;
+        a.workspace_bytes = 0;
+        if (need > 0) {
+            void* p = scratch_on_current_device();
+            if (!p) return PDN_EHIP;
+            a.workspace = p;
+            a.workspace_bytes = PDN_NOALLOC_SCRATCH_BYTES;
+        }
+        const hipError_t e = pdn::launch_chunk_fwd(a, static_cast<hipStream_t>(stream));
         if (e == hipErrorNotSupported) return PDN_EUNSUPPORTED;
         return e == hipSuccess ? PDN_OK : PDN_EHIP;
     } catch (...) {

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define PDN_ABI_VERSION 4
+#define PDN_ABI_VERSION 5
 
 /* Return codes. */
 #define PDN_OK 0
@@ -62,6 +62,8 @@ extern "C" {
 #define PDN_EUNSUPPORTED (-2)  /* valid request outside what the kernels handle   */
 #define PDN_EWORKSPACE (-3)    /* workspace missing or smaller than required      */
 #define PDN_EHIP (-4)          /* the HIP runtime reported an error on launch     */
+#define PDN_ESCRATCH (-5)      /* pdn_chunk_fwd_noalloc: the call needs more than
+                                  PDN_NOALLOC_SCRATCH_BYTES of scratch          */
 
 /* Element types of q, k, v and o. */
 #define PDN_F32 0
@@ -286,6 +288,22 @@ int pdn_decode_check(const pdn_decode_args *args);
  * overwrites S with S_t and precond_A with A_t; one pass over S.  Returns
  * PDN_OK, or a PDN_E* code before any launch; PDN_EHIP if the launch fails. */
 int pdn_decode_step(const pdn_decode_args *args, void *stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): pdn_chunk_fwd
+ * with the scratch taken from a static device array of the library instead of
+ * args->workspace (ignored here; may be NULL).  The array holds
+ * PDN_NOALLOC_SCRATCH_BYTES on every GPU the library runs on, from the first
+ * call on that device until the process ends.  Calls that need more than that
+ * (pdn_chunk_fwd_workspace_size() > PDN_NOALLOC_SCRATCH_BYTES) return
+ * PDN_ESCRATCH before any launch: pass a workspace to pdn_chunk_fwd instead.
+ * The call itself allocates nothing (no hipMalloc, no library allocation).
+ * Every call on one GPU shares that GPU's array, and its contents persist
+ * from call to call: calls on one GPU that overlap (on different streams or
+ * from different threads without ordering) race on it and must not be made.
+ * Inputs, outputs and return codes are those of pdn_chunk_fwd. */
+#define PDN_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+int pdn_chunk_fwd_noalloc(const pdn_chunk_fwd_args *args, void *stream);
 
 /* Device scratch bytes pdn_chunk_bwd needs (PDN_OK and *bytes, or a PDN_E*
  * code).  Per (b, h) and 32-token chunk: the chunk's gate-scaled operands and

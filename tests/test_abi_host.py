@@ -45,12 +45,12 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strerror(lib):
-    assert pdn.pdn_abi_version() == 4
+    assert pdn.pdn_abi_version() == 5
     # the binding's struct mirrors follow the header's version
     m = re.search(r"#define PDN_ABI_VERSION (\d+)", open(HEADER).read())
     assert int(m.group(1)) == pdn.PDN_ABI_VERSION == pdn.pdn_abi_version()
-    for code in (0, -1, -2, -3, -4):
-        assert pdn.pdn_strerror(code)
+    for code in (0, -1, -2, -3, -4, -5):
+        assert pdn.pdn_strerror(code) and "unknown" not in pdn.pdn_strerror(code)
     assert "unknown" in pdn.pdn_strerror(-99)
 
 
@@ -562,3 +562,22 @@ def test_binding_rejects_misshaped_bwd_tensors(name, bad):
     kw[name] = _meta(*bad)
     with pytest.raises(ValueError, match=name if name != "dO" else "o must"):
         pdn.pdn_chunk_bwd(**kw)
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch(lib):
+    # the static scratch of pdn_chunk_fwd_noalloc holds PDN_NOALLOC_SCRATCH_BYTES;
+    # a call that needs more returns PDN_ESCRATCH before touching the GPU
+    m = re.search(r"#define PDN_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)",
+                  open(HEADER).read())
+    assert int(m.group(1)) << int(m.group(2)) == pdn.PDN_NOALLOC_SCRATCH_BYTES
+    a = _chunk_ok()
+    a.workspace, a.workspace_bytes = None, 0      # ignored by the no-allocation call
+    a.B, a.H, a.T = 2, 32, 8192                   # per-channel gates: 0.94 GB of records
+    assert _ws_size(lib, a) > pdn.PDN_NOALLOC_SCRATCH_BYTES
+    assert lib.pdn_chunk_fwd_noalloc(ctypes.byref(a), None) == pdn.PDN_ESCRATCH
+    # invalid arguments keep their own codes
+    a.dk = 96
+    assert lib.pdn_chunk_fwd_noalloc(ctypes.byref(a), None) == pdn.PDN_EUNSUPPORTED
+    a.dk, a.B = 128, 0
+    assert lib.pdn_chunk_fwd_noalloc(ctypes.byref(a), None) == pdn.PDN_EINVAL
+    assert lib.pdn_chunk_fwd_noalloc(None, None) == pdn.PDN_EINVAL
