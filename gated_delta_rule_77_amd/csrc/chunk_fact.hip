@@ -72,7 +72,7 @@ constexpr int B_SC = B_VT + DVT * VTS * 4;
 constexpr int BUF = B_SC + 4 * CH * 4;  // rsKS[64], rq[64], rk[64], gC
 constexpr int SCR = 2 * BUF;            // wave 2: four diagonal 16x16 blocks
 constexpr int SCR_STRIDE = 16 * 20 + 16;
-constexpr int NGF = 7;                        // per-token factor arrays per helper
+constexpr int NGF = 9;                        // per-token factor arrays per helper
 constexpr int GA = SCR + 4 * SCR_STRIDE * 4;  // wave 2 and wave 3 factor arrays
 constexpr int LDS_BYTES = GA + 2 * NGF * CH * 4;
 static_assert(LDS_BYTES + 3 * KTILE <= 160 * 1024, "LDS budget");
@@ -509,16 +509,25 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
     //   off-diagonal R > J (reference Ge_J = G at row 16J + 15, both factors
     //   <= 1): FE_J = [sb_r] 2^(G_r - Ge_J), FF = sb_s 2^(Ge_J - G_s) for s in J.
     // Row factors carry sb_r only for T (wave 2), not for P (wave 3).
+    // The diagonal-block split needs |G_r - Gm| inside the fp32 range, which a
+    // per-token log decay >= kLogAlphaMin guarantees.  A chunk with a stronger
+    // decay (a wave-uniform flag) forms its diagonal blocks element by element
+    // instead, 2^(G_r - G_s) from the per-token G and sb kept in GL and SBV;
+    // log decays are floored at kLogAlphaFloor, where alpha (e^-80) is below
+    // what an fp32 state can resolve, so the result is the recurrence's.
     struct GateVals {
         float gl, sb, G2last;
         float fa, ff;  // this lane's FA and FF factors (token = lane)
+        bool strong;   // some token of the chunk decays below kLogAlphaMin
     };
     float* gw = reinterpret_cast<float*>(smem + GA) + (w2 ? 0 : NGF * CH);
-    enum { FA = 0, FB = CH, FF = 2 * CH, FE = 3 * CH, SG = 6 * CH };
+    enum { FA = 0, FB = CH, FF = 2 * CH, FE = 3 * CH, SG = 6 * CH, GL = 7 * CH, SBV = 8 * CH };
     auto gate_prologue = [&](long c, float la, float be, bool row_sb) {
         GateVals v;
         const bool ok = c * CH + lane < p.T;
-        v.gl = wave_incl_scan((p.has_alpha && ok) ? fmaxf(la, kLogAlphaMin) * kLog2e : 0.0f);
+        const float lac = (p.has_alpha && ok) ? fmaxf(la, kLogAlphaFloor) : 0.0f;
+        v.strong = __builtin_amdgcn_ballot_w64(lac < kLogAlphaMin) != 0;
+        v.gl = wave_incl_scan(lac * kLog2e);
         v.sb = ok ? sqrt_hw(be) : 0.0f;
         auto at = [&](int r) {
             return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v.gl), r));
@@ -538,6 +547,8 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
         gw[FE + lane] = rs * ex2(fminf(v.gl - ge0, 0.0f));
         gw[FE + CH + lane] = rs * ex2(fminf(v.gl - ge1, 0.0f));
         gw[FE + 2 * CH + lane] = rs * ex2(fminf(v.gl - ge2, 0.0f));
+        gw[GL + lane] = v.gl;
+        gw[SBV + lane] = v.sb;
         return v;
     };
 
@@ -591,10 +602,20 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
                 // just issued the next key DMA, and the compiler would make an
                 // LDS read it cannot tell apart from that DMA wait for all of it
                 if (J == R) {
-                    const f32x4 cf = *reinterpret_cast<const f32x4*>(gw + FB + 16 * R + 4 * g);
-                    const float rf = lane_get(gv.fa, 16 * R + ln);
+                    if (!gv.strong) {
+                        const f32x4 cf = *reinterpret_cast<const f32x4*>(gw + FB + 16 * R + 4 * g);
+                        const float rf = lane_get(gv.fa, 16 * R + ln);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[e] = (4 * g + e < ln) ? -(acc[e] * rf * cf[e]) : 0.0f;
+                        for (int e = 0; e < 4; ++e) acc[e] = (4 * g + e < ln) ? -(acc[e] * rf * cf[e]) : 0.0f;
+                    } else {
+                        const f32x4 gs = *reinterpret_cast<const f32x4*>(gw + GL + 16 * R + 4 * g);
+                        const f32x4 bs = *reinterpret_cast<const f32x4*>(gw + SBV + 16 * R + 4 * g);
+                        const float gr = lane_get(gv.gl, 16 * R + ln);
+                        const float br = lane_get(gv.sb, 16 * R + ln);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            acc[e] = (4 * g + e < ln) ? -(acc[e] * br * bs[e] * ex2(gr - gs[e])) : 0.0f;
+                    }
                     *reinterpret_cast<f32x4*>(scr + R * SCR_STRIDE + ln * 20 + 4 * g) = acc;
                 } else {
                     const f32x4 rf = *reinterpret_cast<const f32x4*>(gw + FE + J * CH + 16 * R + 4 * g);
@@ -716,10 +737,19 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
 #pragma unroll
             for (int S = 0; S <= R; ++S) {
                 if (S == R) {
-                    const f32x4 cf = *reinterpret_cast<const f32x4*>(gw + FB + 16 * R + 4 * g);
-                    const float rf = gw[FA + 16 * R + ln];
+                    if (!gv.strong) {
+                        const f32x4 cf = *reinterpret_cast<const f32x4*>(gw + FB + 16 * R + 4 * g);
+                        const float rf = gw[FA + 16 * R + ln];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) pb[R][S][e] = (4 * g + e <= ln) ? pb[R][S][e] * rf * cf[e] : 0.0f;
+                        for (int e = 0; e < 4; ++e) pb[R][S][e] = (4 * g + e <= ln) ? pb[R][S][e] * rf * cf[e] : 0.0f;
+                    } else {
+                        const f32x4 gs = *reinterpret_cast<const f32x4*>(gw + GL + 16 * R + 4 * g);
+                        const f32x4 bs = *reinterpret_cast<const f32x4*>(gw + SBV + 16 * R + 4 * g);
+                        const float gr = gw[GL + 16 * R + ln];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            pb[R][S][e] = (4 * g + e <= ln) ? pb[R][S][e] * bs[e] * ex2(gr - gs[e]) : 0.0f;
+                    }
                 } else {
                     const f32x4 cf = *reinterpret_cast<const f32x4*>(gw + FF + 16 * S + 4 * g);
                     pb[R][S] = pb[R][S] * (gw[FE + S * CH + 16 * R + ln] * cf);

@@ -16,8 +16,12 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // Per-token decay is clamped below at this natural log in the prefill: the
 // chunk algorithm splits exp(G_r - G_s) around a reference inside a 16-token
-// block, and the clamp keeps both factors inside the fp32/bf16 range.
+// block, and the clamp keeps both factors inside the fp32/bf16 range.  (The
+// scalar-decay kernel forms a chunk that decays more strongly element by
+// element instead, and floors log decays only at kLogAlphaFloor: e^-80 is
+// below what an fp32 state resolves.)
 constexpr float kLogAlphaMin = -10.0f;
+constexpr float kLogAlphaFloor = -80.0f;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

@@ -115,7 +115,12 @@ extern "C" {
  *   q, k              [B,H,T,dk].      v: [B,H,T,dv].
  *   alpha_mode        PDN_ALPHA_*;  log_alpha fp32, natural log of alpha, <= 0:
  *                     [B,H,T] (SCALAR) or [B,H,T,dk] (VEC); NULL for NONE.
- *                     Values below -10 (alpha < 4.5e-5) are clamped to -10.
+ *                     The scalar-decay bf16 path (bf16 q/k/v, dk == 128,
+ *                     scalar or no decay, scalar beta, symmetric keys, no
+ *                     preconditioner) takes any value, floored at -80
+ *                     (alpha = e^-80, below what an fp32 state resolves).
+ *                     Every other prefill path clamps values below -10
+ *                     (alpha < 4.5e-5) to -10.
  *   beta_mode         PDN_GATE_SCALAR [B,H,T] or PDN_GATE_VEC [B,H,T,dk]; fp32 >= 0.
  *   gamma_mode        PDN_GATE_SCALAR [B,H,T], PDN_GATE_VEC [B,H,T,dv] or
  *                     PDN_GAMMA_SAME_AS_BETA (gamma NULL; a VEC beta then needs
