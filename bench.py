@@ -62,6 +62,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-legs", action="store_true",
+                    help="skip the extra scalar-gate prefill shapes (B4 H16 T4096, B1 H16 T8192)")
     ap.add_argument("--no-gated", action="store_true",
                     help="skip the per-channel-gate prefill workloads")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward legs")
@@ -158,9 +160,13 @@ def bench_prefill(args, w=None, steps=None, warmup=None):
     la, be = to_dev(w.log_alpha), to_dev(w.beta)
     o = torch.empty((w.B, w.H, w.T, w.dv), device="cuda", dtype=torch.float32)
     ST = torch.empty((w.B, w.H, w.dk, w.dv), device="cuda", dtype=torch.float32)
+    # scratch (few heads: the sequence-segment arrays) allocated before the
+    # timed region
+    nws = pdn.pdn_chunk_fwd_workspace_size(q, k, v, o, log_alpha=la, beta=be, ST=ST)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda") if nws else None
 
     def step():
-        pdn.pdn_chunk_fwd(q, k, v, o, log_alpha=la, beta=be, ST=ST)
+        pdn.pdn_chunk_fwd(q, k, v, o, log_alpha=la, beta=be, ST=ST, workspace=ws)
 
     ramp = clock_ramp(step)
     for _ in range(warmup):
@@ -179,7 +185,7 @@ def bench_prefill(args, w=None, steps=None, warmup=None):
     t1 = time.perf_counter()
     kern_ms = [a.elapsed_time(b) for a, b in ev]
     kernel_ms = sum(kern_ms) / len(kern_ms)
-    del q, k, v, la, be, o, ST
+    del q, k, v, la, be, o, ST, ws
 
     BH, T, dk, dv = w.B * w.H, w.T, w.dk, w.dv
     qkv_bytes = BH * T * (2 * dk + dv) * 2
@@ -194,7 +200,7 @@ def bench_prefill(args, w=None, steps=None, warmup=None):
         "elapsed_s": t1 - t0, "tokens": w.B * T, "kernel_ms": kernel_ms,
         "kernel_ms_min": min(kern_ms), "alg_bytes": alg_bytes, "alg_flops": alg_flops,
         "achieved_gbs": alg_bytes / ks / 1e9, "achieved_tflops": alg_flops / ks / 1e12,
-        "clock_ramp_calls": ramp, "sample": w,
+        "clock_ramp_calls": ramp, "workspace_bytes": nws, "sample": w,
     }
 
 
@@ -211,7 +217,7 @@ def bench_prefill_legs(args):
             "B": r["B"], "H": r["H"], "T": r["T"], "dk": r["dk"], "dv": r["dv"],
             "steps": steps, "kernel_ms": r["kernel_ms"],
             "tokens_per_s": r["tokens"] / (r["kernel_ms"] / 1e3),
-            "alg_bytes_per_launch": r["alg_bytes"],
+            "alg_bytes_per_launch": r["alg_bytes"], "workspace_bytes": r["workspace_bytes"],
             "roofline": {"bound": "hbm", "achieved": r["achieved_gbs"], "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": r["achieved_gbs"] / HBM_PEAK_GBS},
             "mfma_alg_frac_of_peak": r["achieved_tflops"] / BF16_PEAK_TFLOPS,
@@ -502,7 +508,7 @@ def main():
         sys.exit(1)
 
     pf = bench_prefill(args)
-    legs = bench_prefill_legs(args)
+    legs = None if args.no_legs else bench_prefill_legs(args)
     dec = None if args.no_decode else bench_decode(args)
     gated = None if args.no_gated else bench_gated(args)
     bwd = None if args.no_bwd else bench_backward(args)

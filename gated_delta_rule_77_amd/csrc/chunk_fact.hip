@@ -94,6 +94,12 @@ struct FactParams {
     int has_alpha;
     int gvec;
     int o_bf16;
+    // sequence segments (the segmented launch only)
+    int nseg;     // segments per head
+    long cps;     // chunks per segment
+    float* qh;    // [B*H][T][DK]: outputs of the identity-start columns
+    float* nst;   // [B*H][nseg][DK][dv]: segment end states of the value columns
+    float* phi;   // [B*H][nseg][DK][DK]: segment transitions (identity-start end states)
 };
 
 // ---------------------------------------------------------------------------
@@ -179,6 +185,10 @@ __device__ __forceinline__ void put_f16(char* base, int s, int lane, const f32x4
 // the kernel
 // ---------------------------------------------------------------------------
 
+// SEG: the segmented launch (a chunk range per workgroup, identity-start
+// columns, segment end states); a separate instantiation so that the one-pass
+// kernel carries none of it.
+template <bool SEG>
 __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
     // Key tiles: a ring of three slots, chunk c in slot c % 3.  The slots are
     // separate LDS objects so that the compiler can tell the slot being filled
@@ -207,27 +217,52 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
     const int ln = lane & 15;
     const int ntile = p.dv / DVT;
     // Workgroups are dealt round-robin to the XCDs; when the head count allows,
-    // give all column tiles of a head the same XCD so they share its L2 for the
-    // key, query and gate reads.
-    const long nbh = gridDim.x / ntile;
+    // give all workgroups of a head the same XCD so they share its L2 for the
+    // key, query and gate reads.  The segmented launch has, per head, segment
+    // 0's value tiles, then for each later segment its value tiles and the
+    // DK / DVT identity tiles.
+    const int units = SEG ? ntile + (p.nseg - 1) * (ntile + DK / DVT) : ntile;
+    const long nbh = gridDim.x / units;
     long bh;
-    int tile;
+    int u;
     if (nbh % kXcds == 0) {
         const long slot = blockIdx.x / kXcds;
-        tile = static_cast<int>(slot % ntile);
-        bh = (slot / ntile) * kXcds + blockIdx.x % kXcds;
+        u = static_cast<int>(slot % units);
+        bh = (slot / units) * kXcds + blockIdx.x % kXcds;
     } else {
-        bh = blockIdx.x / ntile;
-        tile = static_cast<int>(blockIdx.x % ntile);
+        bh = blockIdx.x / units;
+        u = static_cast<int>(blockIdx.x % units);
+    }
+    int tile = u, seg = 0;
+    bool ident = false;  // identity-start columns (key channels j0 .. j0 + 31)
+    if (SEG && u >= ntile) {
+        const int per_seg = ntile + DK / DVT;
+        seg = 1 + (u - ntile) / per_seg;
+        const int r = (u - ntile) % per_seg;
+        ident = r >= ntile;
+        tile = ident ? r - ntile : r;
     }
     const int j0 = tile * DVT;
-    const long nchunks = (p.T + CH - 1) / CH;
+    // value columns this workgroup reads (identity-start columns read none; 0
+    // keeps their address arithmetic inside the value and gain rows)
+    const int jv = (SEG && ident) ? 0 : j0;
+    // this workgroup's chunks: [c0, c0 + nchunks); chunk indices below are
+    // relative to c0 (key slots and buffers follow them), tokens start at tb
+    const long ntot = (p.T + CH - 1) / CH;
+    const long c0 = SEG ? seg * p.cps : 0;
+    const long nchunks = SEG ? max(0L, min(p.cps, ntot - c0)) : ntot;
+    const long tb = c0 * CH;
 
     if (wave < NCHAIN) {
         // =========================== chain waves ===========================
         f32x4 sacc[8];
         const int col = j0 + 16 * wave + ln;
-        if (p.S0) {
+        if (SEG && ident) {
+#pragma unroll
+            for (int ib = 0; ib < 8; ++ib)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sacc[ib][e] = srow(ib, g, e) == col ? 1.0f : 0.0f;
+        } else if (p.S0 && seg == 0) {
 #pragma unroll
             for (int ib = 0; ib < 8; ++ib)
 #pragma unroll
@@ -245,8 +280,13 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
             const int c4 = j0 + 16 * wave + 4 * g;
 #pragma unroll
             for (int R = 0; R < 4; ++R) {
-                const long tok = cc * CH + 16 * R + ln;
+                const long tok = tb + cc * CH + 16 * R + ln;
                 if (tok >= p.T) continue;
+                if (SEG && ident) {
+                    // Phi_t^T q_t: the output of the identity-start columns
+                    *reinterpret_cast<f32x4*>(p.qh + (bh * p.T + tok) * DK + c4) = opend[R];
+                    continue;
+                }
                 const long oi = (bh * p.T + tok) * p.dv + c4;
                 if (p.o_bf16) {
                     uint2 pk;
@@ -440,7 +480,17 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
             __syncthreads();
         }
         if (nchunks > 0) store_o(nchunks - 1);
-        if (p.ST) {
+        if constexpr (SEG) {
+            // the segment's end state: value columns, or the transition
+            const long sbase = (bh * p.nseg + seg) * DK;
+#pragma unroll
+            for (int ib = 0; ib < 8; ++ib)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (ident) p.phi[(sbase + srow(ib, g, e)) * DK + col] = sacc[ib][e];
+                    else p.nst[(sbase + srow(ib, g, e)) * p.dv + col] = sacc[ib][e];
+                }
+        } else if (p.ST) {
 #pragma unroll
             for (int ib = 0; ib < 8; ++ib)
 #pragma unroll
@@ -458,7 +508,7 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
     // tiles into LDS one chunk ahead.  Loads are clamped to row T - 1; rows past T are
     // finite copies that every product below multiplies by a zero gain.
     auto load_gates = [&](long c, float& la, float& be) {
-        const long tok = bh * p.T + min(c * CH + lane, p.T - 1);
+        const long tok = bh * p.T + min(tb + c * CH + lane, p.T - 1);
         la = p.log_alpha[tok];
         be = p.beta[tok];
     };
@@ -476,20 +526,23 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
     for (int q = 0; q < 4; ++q)
         koff[q] = (lane >> 4) * DK * 2 + 16 * ((lane & 15) ^ (((lane >> 4) << 2) | q));
     auto dma_keys = [&](long c, lds_u16* tile) {
-        const unsigned cb = static_cast<unsigned>(c * CH * DK * 2);
+        const unsigned cb = static_cast<unsigned>((tb + c * CH) * DK * 2);
 #pragma unroll
         for (int m = 0; m < 16; ++m)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)(tile + 4 * m * DK), 16,
                                                      cb + m * 4 * DK * 2 + koff[m & 3], 0, 0, 0);
     };
     auto load3 = [&](long c, Wave3Regs& R3) {
-        const long t0 = c * CH;
+        const long t0 = tb + c * CH;
         load_gates(c, R3.la, R3.be);
         load_rows(R3.q, p.q, bh, p.T, t0, ln, g);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const long tk = bh * p.T + min(t0 + 4 * ln + i, p.T - 1);
-            R3.v[i] = *reinterpret_cast<const uint4*>(p.v + tk * p.dv + j0 + 8 * g);
+            // (unconditional: a load issued on one path only, or a select on the
+            // loaded value here, makes the compiler wait for the load at once;
+            // the identity-start columns zero their values where they are staged)
+            R3.v[i] = *reinterpret_cast<const uint4*>(p.v + tk * p.dv + jv + 8 * g);
         }
         if (!p.gvec) R3.gam1 = p.gsrc[(bh * p.T + min(t0 + lane, p.T - 1)) * p.gts];
     };
@@ -524,7 +577,7 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
     enum { FA = 0, FB = CH, FF = 2 * CH, FE = 3 * CH, SG = 6 * CH, GL = 7 * CH, SBV = 8 * CH };
     auto gate_prologue = [&](long c, float la, float be, bool row_sb) {
         GateVals v;
-        const bool ok = c * CH + lane < p.T;
+        const bool ok = tb + c * CH + lane < p.T;
         const float lac = (p.has_alpha && ok) ? fmaxf(la, kLogAlphaFloor) : 0.0f;
         v.strong = __builtin_amdgcn_ballot_w64(lac < kLogAlphaMin) != 0;
         v.gl = wave_incl_scan(lac * kLog2e);
@@ -556,7 +609,6 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
     // key tile of chunk c + 1.
     auto prepare2 = [&](long c, char* buf, Wave2Regs& R2, auto slot) {
         const float la = R2.la, be = R2.be;
-        const long t0 = c * CH;
         const GateVals gv = gate_prologue(c, la, be, true);
         // ---- wave 2: fetch the next key tile, form T, invert the diagonal blocks ----
         // (unconditional: past the last chunk it refetches row T - 1 into a slot
@@ -675,7 +727,7 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
     };
     auto prepare3 = [&](long c, char* buf, Wave3Regs& R3) {
         const float la = R3.la, be = R3.be;
-        const long t0 = c * CH;
+        const long t0 = tb + c * CH;
         const GateVals gv = gate_prologue(c, la, be, false);
         // ---- wave 3: form P, stage Q, V (transposed), row scales ----
         // raw query-key products (keys from the staged tile) first, so the
@@ -709,7 +761,7 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
         float* sVt = reinterpret_cast<float*>(buf + B_VT);
         f32x4 sg4[8];
         if (!p.gvec) {
-            gw[SG + lane] = (c * CH + lane < p.T) ? sqrt_hw(R3.gam1) : 0.0f;
+            gw[SG + lane] = (tb + c * CH + lane < p.T) ? sqrt_hw(R3.gam1) : 0.0f;
             const f32x4 s4 = *reinterpret_cast<const f32x4*>(gw + SG + 4 * ln);
 #pragma unroll
             for (int cc = 0; cc < 8; ++cc) sg4[cc] = s4;
@@ -717,7 +769,7 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const long tok = t0 + 4 * ln + i;
-                const float* gr = p.gsrc + (bh * p.T + min(tok, p.T - 1)) * p.gts + j0 + 8 * g;
+                const float* gr = p.gsrc + (bh * p.T + min(tok, p.T - 1)) * p.gts + jv + 8 * g;
 #pragma unroll
                 for (int cc = 0; cc < 8; ++cc) sg4[cc][i] = tok < p.T ? sqrt_hw(gr[cc]) : 0.0f;
             }
@@ -728,7 +780,9 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 col4[i] = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(&R3.v[i])[cc]);
-            *reinterpret_cast<f32x4*>(sVt + (8 * g + cc) * VTS + 4 * ln) = sg4[cc] * col4;
+            // identity-start columns run with zero values (j0 indexes key channels)
+            const f32x4 val = (SEG && ident) ? f32x4{0.f, 0.f, 0.f, 0.f} : sg4[cc] * col4;
+            *reinterpret_cast<f32x4*>(sVt + (8 * g + cc) * VTS + 4 * ln) = val;
         }
         if (c + 1 < nchunks) load3(c + 1, R3);
         // P^T blocks: pb[R][S] holds P[16R + ln][16S + 4g + e]
@@ -816,6 +870,50 @@ bool chunk_fact_supported(const pdn_chunk_fwd_args& a) {
            a.precond_eps < 0.0f && a.key_mode == PDN_KEY_SYMMETRIC;
 }
 
+namespace {
+
+// Sequence segments for few heads and long sequences (fp32 output; the
+// correction adds to the stored outputs): as many segments as keep every
+// workgroup of the launch resident at once (one per CU, the MI355X count as a
+// constant: the segment count sets the workspace size, which a caller may ask
+// for before any device is current), at least 8 chunks each, at most 8.
+constexpr long kFactSlots = 256;
+int fact_segments(const pdn_chunk_fwd_args& a) {
+    if (a.o_dtype != PDN_F32) return 1;
+    const long nbh = static_cast<long>(a.B) * a.H;
+    const long nc = (static_cast<long>(a.T) + CH - 1) / CH;
+    const long vt = a.dv / DVT, it = DK / DVT;
+    int G = 1;
+    for (int g = 2; g <= 8; ++g) {
+        if (nc < 8L * g || nbh * (vt * g + it * (g - 1)) > kFactSlots) break;
+        G = g;
+    }
+    return G;
+}
+
+// workspace of a segmented launch: Phi_t^T q_t rows [B*H][T][DK], then the
+// segment end states [B*H][G][DK][dv], transitions [B*H][G][DK][DK] and start
+// states [B*H][G][DK][dv] (fp32)
+struct FactSegBufs {
+    size_t qh, nst, phi, sst, end;
+};
+FactSegBufs fact_seg_layout(const pdn_chunk_fwd_args& a, int G) {
+    const size_t nbh = static_cast<size_t>(a.B) * a.H;
+    FactSegBufs b;
+    b.qh = 0;
+    b.nst = b.qh + (G > 1 ? nbh * a.T * DK * sizeof(float) : 0);
+    b.phi = b.nst + (G > 1 ? nbh * G * DK * a.dv * sizeof(float) : 0);
+    b.sst = b.phi + (G > 1 ? nbh * G * DK * DK * sizeof(float) : 0);
+    b.end = b.sst + (G > 1 ? nbh * G * DK * a.dv * sizeof(float) : 0);
+    return b;
+}
+
+}  // namespace
+
+size_t chunk_fact_workspace_bytes(const pdn_chunk_fwd_args& a) {
+    return fact_seg_layout(a, fact_segments(a)).end;
+}
+
 hipError_t launch_chunk_fact(const pdn_chunk_fwd_args& a, hipStream_t stream) {
     FactParams p;
     p.q = static_cast<const uint16_t*>(a.q);
@@ -837,9 +935,30 @@ hipError_t launch_chunk_fact(const pdn_chunk_fwd_args& a, hipStream_t stream) {
     p.T = a.T;
     p.dv = a.dv;
     p.o_bf16 = a.o_dtype == PDN_BF16;
-    const long nblk = static_cast<long>(a.B) * a.H * (a.dv / DVT);
-    chunk_fact_kernel<<<dim3(static_cast<unsigned>(nblk)), dim3(NTHR), 0, stream>>>(p);
-    return hipGetLastError();
+    const long nbh = static_cast<long>(a.B) * a.H;
+    const int G = fact_segments(a);
+    const long vt = a.dv / DVT, it = DK / DVT;
+    if (G == 1) {
+        p.nseg = 1;
+        p.cps = 0;
+        p.qh = p.nst = p.phi = nullptr;
+        chunk_fact_kernel<false><<<dim3(static_cast<unsigned>(nbh * vt)), dim3(NTHR), 0, stream>>>(p);
+        return hipGetLastError();
+    }
+    const long nc = (static_cast<long>(a.T) + CH - 1) / CH;
+    char* ws = static_cast<char*>(a.workspace);
+    const FactSegBufs sb = fact_seg_layout(a, G);
+    p.nseg = G;
+    p.cps = (nc + G - 1) / G;
+    p.qh = reinterpret_cast<float*>(ws + sb.qh);
+    p.nst = reinterpret_cast<float*>(ws + sb.nst);
+    p.phi = reinterpret_cast<float*>(ws + sb.phi);
+    const long nwg = nbh * (vt + (G - 1) * (vt + it));
+    chunk_fact_kernel<true><<<dim3(static_cast<unsigned>(nwg)), dim3(NTHR), 0, stream>>>(p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_seg_finish(p.nst, p.phi, reinterpret_cast<float*>(ws + sb.sst), a.ST, p.qh,
+                             static_cast<float*>(a.o), nbh, a.T, G, p.cps * CH, a.dv, stream);
 }
 
 }  // namespace pdn

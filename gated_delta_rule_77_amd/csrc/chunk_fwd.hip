@@ -871,7 +871,9 @@ int choose_nw(long nbh, int dv, bool vec, bool f32in, int ncu) {
 }  // namespace
 
 size_t chunk_fwd_workspace_bytes(const pdn_chunk_fwd_args& a) {
-    if (a.T > 0 && !chunk_fact_supported(a) && chunk_vec_supported(a)) return chunk_vec_workspace_bytes(a);
+    if (a.T <= 0) return 0;
+    if (chunk_fact_supported(a)) return chunk_fact_workspace_bytes(a);
+    if (chunk_vec_supported(a)) return chunk_vec_workspace_bytes(a);
     return 0;
 }
 

@@ -1006,7 +1006,7 @@ __global__ void __launch_bounds__(SEG_NTHR) vec_seg_combine_kernel(const float* 
 constexpr int COR_TOK = 256;
 constexpr int COR_CB = 128;
 __global__ void __launch_bounds__(SEG_NTHR, 2) vec_seg_correct_kernel(const float* qh, const float* sst, float* o,
-                                                                   long T, int nseg, long cps, int dv,
+                                                                   long T, int nseg, long seg_tokens, int dv,
                                                                    long tiles_per_seg) {
     __shared__ __attribute__((aligned(16))) float sS[DK][COR_CB + 16];
     const long unit = blockIdx.x;
@@ -1014,8 +1014,8 @@ __global__ void __launch_bounds__(SEG_NTHR, 2) vec_seg_correct_kernel(const floa
     const long bh = unit / per_bh;
     const int g = 1 + static_cast<int>((unit % per_bh) / tiles_per_seg);
     const long tile = (unit % per_bh) % tiles_per_seg;
-    const long t0 = g * cps * VC + tile * COR_TOK;
-    const long t1 = min(min(t0 + COR_TOK, (g + 1) * cps * VC), T);
+    const long t0 = g * seg_tokens + tile * COR_TOK;
+    const long t1 = min(min(t0 + COR_TOK, (g + 1) * seg_tokens), T);
     if (t0 >= t1) return;  // whole workgroup
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ln = lane & 15, h = lane >> 4;
@@ -1214,14 +1214,20 @@ hipError_t launch_chunk_vec(const pdn_chunk_fwd_args& a, hipStream_t stream) {
     const long nwg = nbh * (vt + (G - 1) * (vt + it));
     if (G > 1) vec_chain_kernel<true><<<dim3(static_cast<unsigned>(nwg)), dim3(NTHR), 0, stream>>>(cp);
     else vec_chain_kernel<false><<<dim3(static_cast<unsigned>(nwg)), dim3(NTHR), 0, stream>>>(cp);
-    if (G > 1) {
-        float* sst = reinterpret_cast<float*>(ws + sb.sst);
-        vec_seg_combine_kernel<<<dim3(static_cast<unsigned>(nbh * (a.dv / CT))), dim3(SEG_NTHR), 0, stream>>>(
-            cp.nst, cp.phi, sst, a.ST, G, a.dv);
-        const long tiles = (cp.cps * VC + COR_TOK - 1) / COR_TOK;
-        vec_seg_correct_kernel<<<dim3(static_cast<unsigned>(nbh * (G - 1) * tiles)), dim3(SEG_NTHR), 0, stream>>>(
-            cp.qh, sst, static_cast<float*>(a.o), a.T, G, cp.cps, a.dv, tiles);
-    }
+    if (G > 1)
+        return launch_seg_finish(cp.nst, cp.phi, reinterpret_cast<float*>(ws + sb.sst), a.ST, cp.qh,
+                                 static_cast<float*>(a.o), nbh, a.T, G, cp.cps * VC, a.dv, stream);
+    return hipGetLastError();
+}
+
+hipError_t launch_seg_finish(const float* nst, const float* phi, float* sst, float* ST, const float* qh,
+                             float* o, long nbh, long T, int nseg, long seg_tokens, int dv,
+                             hipStream_t stream) {
+    vec_seg_combine_kernel<<<dim3(static_cast<unsigned>(nbh * (dv / CT))), dim3(SEG_NTHR), 0, stream>>>(
+        nst, phi, sst, ST, nseg, dv);
+    const long tiles = (seg_tokens + COR_TOK - 1) / COR_TOK;
+    vec_seg_correct_kernel<<<dim3(static_cast<unsigned>(nbh * (nseg - 1) * tiles)), dim3(SEG_NTHR), 0, stream>>>(
+        qh, sst, o, T, nseg, seg_tokens, dv, tiles);
     return hipGetLastError();
 }
 

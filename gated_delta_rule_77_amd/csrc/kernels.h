@@ -32,6 +32,20 @@ bool chunk_vec_supported(const pdn_chunk_fwd_args& a);
 size_t chunk_vec_workspace_bytes(const pdn_chunk_fwd_args& a);
 hipError_t launch_chunk_vec(const pdn_chunk_fwd_args& a, hipStream_t stream);
 
+// Sequence segments, after the segment runs (either prefill kernel): the
+// segments' start states S_{g+1} = Phi_g S_g + N_g from the end states nst
+// [nbh][nseg][128][dv] (segment 0 run from the real start state, the others
+// from zero) and transitions phi [nbh][nseg][128][128], kept in sst and the
+// last one written to ST; then o_t += (Phi_t^T q_t)^T S_g for the tokens of
+// segments g >= 1 (qh [nbh][T][128]: the identity-start columns' outputs).
+// Segment g holds tokens [g seg_tokens, (g + 1) seg_tokens); dv % 32 == 0.
+hipError_t launch_seg_finish(const float* nst, const float* phi, float* sst, float* ST, const float* qh,
+                             float* o, long nbh, long T, int nseg, long seg_tokens, int dv,
+                             hipStream_t stream);
+
+// Scalar-gate prefill workspace (sequence segments for few heads; else 0).
+size_t chunk_fact_workspace_bytes(const pdn_chunk_fwd_args& a);
+
 // Scratch bytes the prefill needs for these (valid) arguments.
 size_t chunk_fwd_workspace_bytes(const pdn_chunk_fwd_args& a);
 

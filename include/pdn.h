@@ -256,6 +256,10 @@ const char *pdn_strerror(int code);
 
 /* Device scratch bytes pdn_chunk_fwd needs for these arguments (0 is valid).
  * Returns PDN_OK and writes *bytes, or a PDN_E* code for invalid arguments.
+ * Non-zero (besides the per-channel-gate records below) for few heads with
+ * long sequences and fp32 output: the sequence is then split into segments
+ * that run side by side, from their transitions and end states (fp32
+ * [B,H,T,dk] plus a few [B,H,segments,dk,dv|dk] arrays).
  * (An int status with the size through a pointer, rather than a bare size_t
  * return, so that invalid arguments are reported as on every other call; a
  * size of 0 is a valid answer and cannot double as an error value.)

@@ -661,6 +661,57 @@ def test_sequence_segments(mode, T):
     check("segments %s T=%d" % (mode, T), w, TOL_BF16, A0=A0, key_mode=km, precond_mode=pm)
 
 
+@pytest.mark.parametrize("T", [1024, 2047, 4160])   # 2, 4 and 8 segments for two heads
+@pytest.mark.parametrize("cfg", ["gdn", "gdn_vec_gain"])
+def test_sequence_segments_scalar_gates(cfg, T):
+    # the scalar-decay kernel's segmented launch (few heads, long sequence,
+    # fp32 output), with a start state; a per-value-channel gain too
+    rng = np.random.default_rng(700 + T)
+    w = synth.gdn(B=1, H=2, T=T, d=128, seed=T)
+    if cfg == "gdn_vec_gain":
+        w.gamma_mode = synth.GATE_VEC
+        w.gamma = (1.0 / (1.0 + np.exp(-rng.standard_normal((1, 2, T, 128))))).astype(np.float32)
+    w.S0 = (0.1 * rng.standard_normal((1, 2, 128, 128))).astype(np.float32)
+    o, ST = check("segments scalar gates %s T=%d" % (cfg, T), w, TOL_BF16)
+    o_ref, _, _ = oracle.run_workload(w)
+    wc = max(per_chunk_max(o[0, h], o_ref[0, h]) for h in range(2))
+    report("segments scalar gates %s T=%d per chunk" % (cfg, T), o_worst_chunk=wc)
+    assert wc < TOL_BF16
+
+
+def test_sequence_segments_scalar_gates_in_place_and_dv64():
+    # in-place state (the final state is written by the segment combination,
+    # after segment 0 read the start state), dv = 64 (two value tiles, four
+    # identity tiles), a ragged tail in the last segment
+    rng = np.random.default_rng(71)
+    w = synth.gdn(B=1, H=3, T=1500, d=128, seed=71)
+    w.v = synth.round_to_bf16(rng.standard_normal((1, 3, 1500, 64)).astype(np.float32))
+    w.dv = 64
+    w.S0 = (0.1 * rng.standard_normal((1, 3, 128, 64))).astype(np.float32)
+    o, ST, _ = run_chunk(w, in_place=True)
+    o_ref, S_ref, _ = oracle.run_workload(w)
+    eo, es = rel_l2(o, o_ref), rel_l2(ST, S_ref)
+    report("segments scalar gates in place dv=64 T=1500", o=eo, S=es)
+    assert eo < TOL_BF16 and es < TOL_BF16
+
+
+def test_sequence_segments_scalar_gates_match_one_pass():
+    # bf16 output keeps the one-pass kernel; the final states agree
+    w = synth.gdn(B=1, H=4, T=3000, d=128, seed=72)
+    w.S0 = (0.1 * np.random.default_rng(72).standard_normal((1, 4, 128, 128))).astype(np.float32)
+    o_seg, S_seg, _ = run_chunk(w)
+    o_one, S_one, _ = run_chunk(w, o_bf16=True)
+    assert rel_l2(S_seg, S_one) < 1e-5
+    assert rel_l2(o_one, o_seg) < 4e-3   # bf16 rounding of o
+
+
+@pytest.mark.timeout(900)
+def test_headline_b1_full_size_sampled():
+    # the headline gating at B = 1 (16 heads, T = 8192): the segmented launch
+    w = synth.headline(B=1)
+    _sampled("gdn B1 H16 T8192 (segments)", w, [(0, 0), (0, 9), (0, 15)], TOL_BF16)
+
+
 def test_sequence_segments_match_one_pass():
     # bf16 output keeps the one-pass chain; the final states of both runs agree
     w = synth.gdn2_precond(B=1, H=3, T=1500, d=128, seed=81, n_pairs=4)
