@@ -75,21 +75,33 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_hash() -> str:
-    """Hash of everything that decides the kernels' machine code: the HIP
-    sources and the build script (compiler flags)."""
+# Source files that decide the machine code of the dominant kernel of each
+# workload whose HBM traffic is read from committed PMC summaries (besides the
+# build script and the C-ABI header, which every kernel depends on).
+KERNEL_SOURCES = {
+    "gdn_T8192": ("chunk_fwd.hip", "chunk_fact.hip", "chunk_tile.h", "common.h", "kernels.h"),
+    "decode_B256_H16_d128": ("decode.hip", "common.h", "kernels.h"),
+}
+
+
+def kernel_source_hash(workload: str = None) -> str:
+    """Hash of what decides the kernels' machine code: the HIP sources (all of
+    them, or those of one workload's dominant kernel), the C-ABI header and
+    the build script (compiler flags)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gated_delta_rule_77_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h", ".cpp")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+    files = KERNEL_SOURCES[workload] if workload else sorted(
+        f for f in os.listdir(csrc) if f.endswith((".hip", ".h", ".cpp")))
+    for f in files:
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    h.update(open(os.path.join(ROOT, "include", "pdn.h"), "rb").read())
     h.update(open(os.path.join(ROOT, "gated_delta_rule_77_amd", "build.py"), "rb").read())
     return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str):
     """HBM bytes per launch from committed PMC summaries, if they were taken
-    on the current kernel sources (else None)."""
+    on the current sources of the workload's dominant kernel (else None)."""
     p = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
     if not os.path.exists(p):
         return None
@@ -97,7 +109,7 @@ def measured_traffic(workload: str):
         d = json.load(open(p))
     except ValueError:
         return None
-    if d.get("kernel_source_hash") != kernel_source_hash():
+    if d.get("kernel_source_hash") != kernel_source_hash(workload):
         return None
     return d.get("bytes_per_launch")
 

@@ -998,72 +998,82 @@ __global__ void __launch_bounds__(SEG_NTHR) vec_seg_combine_kernel(const float* 
 }
 
 // o_t += (Phi_t^T q_t)^T S_g for the tokens of segments g >= 1: one workgroup
-// per (head, segment, 256-token tile), S_g staged in LDS once per 128-column
-// pass; wave w takes 16-token blocks w, w + 4, ... with fp32 16x16x4 MFMAs.
-// In k-step s lane group h contracts key channel 32 h + s, so a lane reads its
-// 32 channels of a qh row as eight 16-byte loads; LDS row 4 s + h holds state
-// row 32 h + s, so the four lane groups of a k-step hit distinct banks.
+// per (head, segment, 256-token tile).  For each pass of 128 state columns,
+// S_g^T is staged in LDS as bf16 hi/lo terms (row = state column, its 128
+// channels; 16-byte chunks XOR-swizzled by the row so that the 16 rows an
+// operand read touches fall in distinct banks).  Each wave takes 16-token
+// blocks; per block the transposed product out^T = S_g^T qh^T runs as
+// 16x16x32 bf16 MFMAs on hi/lo terms (hi.hi + hi.lo + lo.hi, fp32
+// accumulation), so that lane (ln, g) ends with token ln, columns 4g .. 4g + 3
+// of each 16-column block and updates o in 16-byte pieces.
 constexpr int COR_TOK = 256;
 constexpr int COR_CB = 128;
+__device__ __forceinline__ int cor_off(int row, int ch) {  // bf16 element offset in a staged tile
+    return row * DK + ((((ch >> 3) ^ (row & 15)) << 3) | (ch & 7));
+}
 __global__ void __launch_bounds__(SEG_NTHR, 2) vec_seg_correct_kernel(const float* qh, const float* sst, float* o,
                                                                    long T, int nseg, long seg_tokens, int dv,
                                                                    long tiles_per_seg) {
-    __shared__ __attribute__((aligned(16))) float sS[DK][COR_CB + 16];
+    __shared__ __attribute__((aligned(16))) uint16_t sH[COR_CB * DK];
+    __shared__ __attribute__((aligned(16))) uint16_t sL[COR_CB * DK];
     const long unit = blockIdx.x;
     const long per_bh = (nseg - 1) * tiles_per_seg;
     const long bh = unit / per_bh;
-    const int g = 1 + static_cast<int>((unit % per_bh) / tiles_per_seg);
+    const int gs = 1 + static_cast<int>((unit % per_bh) / tiles_per_seg);
     const long tile = (unit % per_bh) % tiles_per_seg;
-    const long t0 = g * seg_tokens + tile * COR_TOK;
-    const long t1 = min(min(t0 + COR_TOK, (g + 1) * seg_tokens), T);
+    const long t0 = gs * seg_tokens + tile * COR_TOK;
+    const long t1 = min(min(t0 + COR_TOK, (gs + 1) * seg_tokens), T);
     if (t0 >= t1) return;  // whole workgroup
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int ln = lane & 15, h = lane >> 4;
-    const float* S = sst + (bh * nseg + g) * DK * dv;
+    const int ln = lane & 15, g = lane >> 4;
+    const float* S = sst + (bh * nseg + gs) * DK * dv;
     for (int jb = 0; jb < dv; jb += COR_CB) {
         const int nj = min(COR_CB, dv - jb);  // a multiple of 32
-        __syncthreads();
-        for (int i = tid; i < DK * COR_CB / 4; i += SEG_NTHR) {
-            const int r = i / (COR_CB / 4), c4 = i % (COR_CB / 4);
-            const f32x4 v = 4 * c4 < nj ? *reinterpret_cast<const f32x4*>(S + r * dv + jb + 4 * c4)
-                                        : f32x4{0.f, 0.f, 0.f, 0.f};
-            *reinterpret_cast<f32x4*>(&sS[4 * (r % 32) + r / 32][4 * c4]) = v;
+        __syncthreads();  // the previous pass is done with the staged tile
+        // stage S_g^T (columns jb .. jb + nj) as hi/lo bf16: item (column c,
+        // channels 8m .. 8m + 7), consecutive threads on consecutive columns
+        for (int it = tid; it < COR_CB * (DK / 8); it += SEG_NTHR) {
+            const int c = it % COR_CB, m = it / COR_CB;
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = c < nj ? S[(8 * m + e) * dv + jb + c] : 0.f;
+            uint4 h, l;
+            split8(x, h, l);
+            *reinterpret_cast<uint4*>(sH + cor_off(c, 8 * m)) = h;
+            *reinterpret_cast<uint4*>(sL + cor_off(c, 8 * m)) = l;
         }
         __syncthreads();
         for (long tb = t0 + 16 * wave; tb < t1; tb += 64) {
-            const long ta = tb + ln;  // this lane's qh row
-            const float* qrow = qh + (bh * T + ta) * DK + 32 * h;
-            f32x4 an = ta < t1 ? *reinterpret_cast<const f32x4*>(qrow) : f32x4{0.f, 0.f, 0.f, 0.f};
-            // lane (ln, h) holds tokens tb + 4 h + e, column jb + 16 cb + ln
-            float ov[COR_CB / 16][4];
+            const long tok = tb + ln;  // this lane's token (B operand column)
+            const bool tv = tok < t1;
+            const float* qrow = qh + (bh * T + (tv ? tok : t1 - 1)) * DK;
+            // B operands: qh row `tok`, channels 32 t + 8 g .. + 7, hi/lo
+            bf16x8 bh_[4], bl_[4];
 #pragma unroll
-            for (int cb = 0; cb < COR_CB / 16; ++cb)
+            for (int t = 0; t < 4; ++t) {
+                const f32x4 a0 = *reinterpret_cast<const f32x4*>(qrow + 32 * t + 8 * g);
+                const f32x4 a1 = *reinterpret_cast<const f32x4*>(qrow + 32 * t + 8 * g + 4);
+                bf16x8 hl[2];
+                split_pair(a0, a1, hl);
+                bh_[t] = hl[0];
+                bl_[t] = hl[1];
+            }
+            for (int cb = 0; cb < nj / 16; ++cb) {
+                f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const long t = tb + 4 * h + e;
-                    ov[cb][e] = 16 * cb < nj && t < t1 ? o[(bh * T + t) * dv + jb + 16 * cb + ln] : 0.f;
+                for (int t = 0; t < 4; ++t) {
+                    const bf16x8 ah = *reinterpret_cast<const bf16x8*>(sH + cor_off(16 * cb + ln, 32 * t + 8 * g));
+                    const bf16x8 al = *reinterpret_cast<const bf16x8*>(sL + cor_off(16 * cb + ln, 32 * t + 8 * g));
+                    acc = mfma32(al, bh_[t], acc);
+                    acc = mfma32(ah, bl_[t], acc);
+                    acc = mfma32(ah, bh_[t], acc);
                 }
-            f32x4 acc[COR_CB / 16];
-#pragma unroll
-            for (int cb = 0; cb < COR_CB / 16; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-            for (int i = 0; i < 8; ++i) {
-                const f32x4 ai = an;  // channels 32 h + 4 i .. + 3
-                if (i < 7 && ta < t1) an = *reinterpret_cast<const f32x4*>(qrow + 4 * (i + 1));
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int srow = 4 * (4 * i + u) + h;
-#pragma unroll
-                    for (int cb = 0; cb < COR_CB / 16; ++cb) acc[cb] = mfma4(ai[u], sS[srow][16 * cb + ln], acc[cb]);
+                // acc: token ln, state columns 16 cb + 4 g .. + 3
+                if (tv) {
+                    f32x4* op = reinterpret_cast<f32x4*>(o + (bh * T + tok) * dv + jb + 16 * cb + 4 * g);
+                    *op = *op + acc;
                 }
             }
-#pragma unroll
-            for (int cb = 0; cb < COR_CB / 16; ++cb)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const long t = tb + 4 * h + e;
-                    if (16 * cb < nj && t < t1) o[(bh * T + t) * dv + jb + 16 * cb + ln] = ov[cb][e] + acc[cb][e];
-                }
         }
     }
 }
