@@ -99,9 +99,9 @@ def kernel_source_hash(workload: str = None) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch from committed PMC summaries, if they were taken
-    on the current sources of the workload's dominant kernel (else None)."""
+def measured_counters(workload: str):
+    """The committed PMC summary of the workload's dominant kernel, if it was
+    taken on the current sources of that kernel (else None)."""
     p = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
     if not os.path.exists(p):
         return None
@@ -111,7 +111,25 @@ def measured_traffic(workload: str):
         return None
     if d.get("kernel_source_hash") != kernel_source_hash(workload):
         return None
-    return d.get("bytes_per_launch")
+    return d
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled by the copy
+    probe) from the committed PMC summary, or None."""
+    d = measured_counters(workload)
+    return d.get("bytes_per_launch") if d else None
+
+
+def measured_mfma_busy(workload: str):
+    """MFMA-busy fraction of the dominant kernel from the committed PMC
+    summary: SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / XCDs x SIMDs), and
+    rocprofv3's derived MfmaUtil; None if absent or stale."""
+    d = measured_counters(workload)
+    if not d or "mfma_busy_frac" not in d:
+        return None
+    return {"mfma_busy_frac": d["mfma_busy_frac"], "MfmaUtil_pct": d.get("MfmaUtil_pct"),
+            "source": "profiles/traffic_%s.json (rocprofv3 --pmc)" % workload}
 
 
 def copy_probe():
@@ -554,7 +572,8 @@ def main():
                      "traffic": measured_traffic(pf["workload"])},
         "kernel_ms": pf["kernel_ms"],
         "alg_bytes_per_launch": pf["alg_bytes"],
-        "mfma": {"alg_tflops": pf["achieved_tflops"], "peak_tflops": BF16_PEAK_TFLOPS,
+        "mfma": {"counter_busy": measured_mfma_busy(pf["workload"]),
+                 "alg_tflops": pf["achieved_tflops"], "peak_tflops": BF16_PEAK_TFLOPS,
                  "frac_of_peak": pf["achieved_tflops"] / BF16_PEAK_TFLOPS,
                  "alg_flops_per_launch": pf["alg_flops"],
                  "ceiling_frac_at_hbm_bound": (pf["alg_flops"] / (pf["alg_bytes"] / (HBM_PEAK_GBS * 1e9)))
