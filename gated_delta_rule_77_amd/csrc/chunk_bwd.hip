@@ -475,15 +475,16 @@ template <int W, int N4>
 struct Tile4 {
     static constexpr int PER = (N4 + NT - 1) / NT;
     f32x4 v[PER];
+    // every thread loads (past the tile it rereads a valid element that it
+    // then does not store): a load on one path only would make the compiler
+    // wait for all outstanding loads where the paths join
     __device__ __forceinline__ void load(const float* g, long gstride) {
         const int tid = threadIdx.x;
 #pragma unroll
         for (int u = 0; u < PER; ++u) {
-            const int idx = tid + u * NT;
-            if (N4 % NT == 0 || idx < N4) {
-                const int r = idx / (W / 4), c4 = idx % (W / 4);
-                v[u] = *reinterpret_cast<const f32x4*>(g + r * gstride + 4 * c4);
-            }
+            const int idx = (N4 % NT == 0 || tid + u * NT < N4) ? tid + u * NT : (tid + u * NT) % N4;
+            const int r = idx / (W / 4), c4 = idx % (W / 4);
+            v[u] = *reinterpret_cast<const f32x4*>(g + r * gstride + 4 * c4);
         }
     }
     template <int LS>
@@ -584,7 +585,7 @@ __device__ __forceinline__ void state_fwd_body(const BwdParams& p, float* smem, 
         __syncthreads();
         if (c + 1 < p.nc) fetch(c + 1);
         // X = Vw - Kg S: tile (rb, xcb)
-#pragma unroll 8
+#pragma unroll
         for (int k = 0; k < DK; k += 4) x = mfma4(-sKg[16 * rb + ln][k + g4], sS[k + g4][16 * xcb + ln], x);
 #pragma unroll
         for (int e = 0; e < 4; ++e) sX[16 * rb + 4 * g4 + e][16 * xcb + ln] = x[e];
@@ -679,9 +680,9 @@ __device__ __forceinline__ void state_bwd_body(const BwdParams& p, float* smem, 
             nPt[k] = Rp[(4 * k + g4) * BC + 16 * rb + ln];
             nMt[k] = Rm[(4 * k + g4) * BC + 16 * rb + ln];
         }
-        const long t = c * BC + dr;
-        ndO = *reinterpret_cast<const f32x4*>(p.dO + (bh * p.T + tclamp(p, t)) * p.dv + j0 + 4 * dc4);
-        if (t >= p.T) ndO = f32x4{0.f, 0.f, 0.f, 0.f};
+        // clamped row, zeroed past T when staged: a select on the loaded value
+        // here would make the compiler wait for every load of the fetch
+        ndO = *reinterpret_cast<const f32x4*>(p.dO + (bh * p.T + tclamp(p, c * BC + dr)) * p.dv + j0 + 4 * dc4);
     };
     fetch(p.nc - 1);
     for (long c = p.nc - 1; c >= 0; --c) {
@@ -698,7 +699,7 @@ __device__ __forceinline__ void state_bwd_body(const BwdParams& p, float* smem, 
         nQg.template store<DK + 4>(&sQg[0][0]);
         nKd.template store<DK + 4>(&sKd[0][0]);
         nGc.template store<DK>(sGc);
-        *reinterpret_cast<f32x4*>(&sdO[dr][4 * dc4]) = ndO;
+        *reinterpret_cast<f32x4*>(&sdO[dr][4 * dc4]) = c * BC + dr < p.T ? ndO : f32x4{0.f, 0.f, 0.f, 0.f};
         float aPt[BC / 4], aMt[BC / 4];
 #pragma unroll
         for (int k = 0; k < BC / 4; ++k) {
@@ -711,7 +712,7 @@ __device__ __forceinline__ void state_bwd_body(const BwdParams& p, float* smem, 
         f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int k = 0; k < BC / 4; ++k) y = mfma4(aPt[k], sdO[4 * k + g4][16 * xcb + ln], y);
-#pragma unroll 8
+#pragma unroll
         for (int k = 0; k < DK; k += 4) y = mfma4(sKd[16 * rb + ln][k + g4], sdS[k + g4][16 * xcb + ln], y);
 #pragma unroll
         for (int e = 0; e < 4; ++e) sY[16 * rb + 4 * g4 + e][16 * xcb + ln] = y[e];
@@ -829,10 +830,10 @@ __device__ __forceinline__ void dgrad_body(const BwdParams& p, float* smem, long
         nE.load(E + jc, p.dv);
         nZ.load(Zc + jc, p.dv);
         nU.load(Uc + jc, p.dv);
-        const long t = c * BC + dr;
-        ndO = *reinterpret_cast<const f32x4*>(p.dO + (bh * p.T + tclamp(p, t)) * p.dv + jc + 4 * dc4);
-        if (t >= p.T) ndO = f32x4{0.f, 0.f, 0.f, 0.f};
+        // clamped row, zeroed past T when staged (see the reverse state pass)
+        ndO = *reinterpret_cast<const f32x4*>(p.dO + (bh * p.T + tclamp(p, c * BC + dr)) * p.dv + jc + 4 * dc4);
     };
+    const bool dO_row = c * BC + dr < p.T;
     fetch(0);
     for (int jc = 0; jc < p.dv; jc += JT) {
         __syncthreads();
@@ -840,7 +841,7 @@ __device__ __forceinline__ void dgrad_body(const BwdParams& p, float* smem, long
         nE.template store<JT + 4>(&sE[0][0]);
         nZ.template store<JT + 4>(&sZ[0][0]);
         nU.template store<JT + 4>(&sU[0][0]);
-        *reinterpret_cast<f32x4*>(&sdO[dr][4 * dc4]) = ndO;
+        *reinterpret_cast<f32x4*>(&sdO[dr][4 * dc4]) = dO_row ? ndO : f32x4{0.f, 0.f, 0.f, 0.f};
         __syncthreads();
         if (jc + JT < p.dv) fetch(jc + JT);
         if (tid < DK)
