@@ -501,6 +501,23 @@ struct Tile4 {
     }
 };
 
+// Scheduling hint for the block just emitted: the LDS operand reads run a few
+// MFMAs ahead, and every M MFMAs are followed by one global load (N of them)
+// and the next reads, so that the next chunk's loads issue one at a time
+// between the MFMAs instead of in one burst ahead of them (a burst of ~30 1 KiB
+// loads per wave keeps the CU's address unit busy for ~1,000-2,000 cycles,
+// during which the wave issues nothing else).
+template <int N, int M = 1>
+__device__ __forceinline__ void interleave_loads() {
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // LDS reads
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, M, 0);      // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);      // global load
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * M, 0);  // LDS reads
+    }
+}
+
 // (b, h) and first value column of state-pass unit u.  Both workgroups of a
 // unit run on XCD u mod kXcds (see bwd_states_kernel); when the head count
 // allows, all column tiles of a head get the same u mod kXcds, so that they
@@ -583,10 +600,13 @@ __device__ __forceinline__ void state_fwd_body(const BwdParams& p, float* smem, 
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[e] = nVw[e];
         __syncthreads();
-        if (c + 1 < p.nc) fetch(c + 1);
+        // the next chunk's loads (the last chunk rereads itself, so that no
+        // branch splits them from the MFMAs below)
+        fetch(c + 1 < p.nc ? c + 1 : c);
         // X = Vw - Kg S: tile (rb, xcb)
 #pragma unroll
         for (int k = 0; k < DK; k += 4) x = mfma4(-sKg[16 * rb + ln][k + g4], sS[k + g4][16 * xcb + ln], x);
+        interleave_loads<DK / 4>();
 #pragma unroll
         for (int e = 0; e < 4; ++e) sX[16 * rb + 4 * g4 + e][16 * xcb + ln] = x[e];
         __syncthreads();
@@ -707,13 +727,14 @@ __device__ __forceinline__ void state_bwd_body(const BwdParams& p, float* smem, 
             aMt[k] = nMt[k];
         }
         __syncthreads();
-        if (c > 0) fetch(c - 1);
+        fetch(c > 0 ? c - 1 : 0);  // unconditional, as in the forward pass
         // Y = P^T dO + Kd dS'
         f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int k = 0; k < BC / 4; ++k) y = mfma4(aPt[k], sdO[4 * k + g4][16 * xcb + ln], y);
 #pragma unroll
         for (int k = 0; k < DK; k += 4) y = mfma4(sKd[16 * rb + ln][k + g4], sdS[k + g4][16 * xcb + ln], y);
+        interleave_loads<BC / 4 + DK / 4>();
 #pragma unroll
         for (int e = 0; e < 4; ++e) sY[16 * rb + 4 * g4 + e][16 * xcb + ln] = y[e];
         __syncthreads();
