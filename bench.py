@@ -84,17 +84,27 @@ KERNEL_SOURCES = {
 }
 
 
+def _code_only(path: str) -> bytes:
+    """A C/C++/HIP source with its comments and whitespace removed (the
+    sources hold no string literal that contains a comment marker)."""
+    import re
+    text = open(path, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split()).encode()
+
+
 def kernel_source_hash(workload: str = None) -> str:
     """Hash of what decides the kernels' machine code: the HIP sources (all of
-    them, or those of one workload's dominant kernel), the C-ABI header and
-    the build script (compiler flags)."""
+    them, or those of one workload's dominant kernel) and the C-ABI header,
+    comments and whitespace aside, and the build script (compiler flags)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gated_delta_rule_77_amd", "csrc")
     files = KERNEL_SOURCES[workload] if workload else sorted(
         f for f in os.listdir(csrc) if f.endswith((".hip", ".h", ".cpp")))
     for f in files:
-        h.update(open(os.path.join(csrc, f), "rb").read())
-    h.update(open(os.path.join(ROOT, "include", "pdn.h"), "rb").read())
+        h.update(_code_only(os.path.join(csrc, f)))
+    h.update(_code_only(os.path.join(ROOT, "include", "pdn.h")))
     h.update(open(os.path.join(ROOT, "gated_delta_rule_77_amd", "build.py"), "rb").read())
     return h.hexdigest()[:16]
 

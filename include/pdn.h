@@ -255,19 +255,21 @@ int pdn_abi_version(void);
 const char *pdn_strerror(int code);
 
 /* Device scratch bytes pdn_chunk_fwd needs for these arguments (0 is valid).
- * Returns PDN_OK and writes *bytes, or a PDN_E* code for invalid arguments.
- * Non-zero (besides the per-channel-gate records below) for few heads with
- * long sequences and fp32 output: the sequence is then split into segments
- * that run side by side, from their transitions and end states (fp32
- * [B,H,T,dk] plus a few [B,H,segments,dk,dv|dk] arrays).
- * (An int status with the size through a pointer, rather than a bare size_t
+ * Returns PDN_OK and writes *bytes, or a PDN_E* code for invalid arguments
+ * (an int status with the size through a pointer, rather than a bare size_t
  * return, so that invalid arguments are reported as on every other call; a
- * size of 0 is a valid answer and cannot double as an error value.)
- * Non-zero only for bf16 q/k/v with dk == 128 and a per-channel gate, the
- * preconditioner or asymmetric keys: those calls first write, for every (b, h)
- * and 32-token chunk, a 56 KiB record of gate-scaled operands and solve blocks (plus 512
- * bytes of k(.)k sums with the preconditioner), which the state-carrying
- * kernel then reads once.  The workspace holds no state between calls. */
+ * size of 0 is a valid answer and cannot double as an error value).
+ * Non-zero in two cases:
+ *  - bf16 q/k/v with dk == 128 and a per-channel gate, the preconditioner or
+ *    asymmetric keys: those calls first write, for every (b, h) and 32-token
+ *    chunk, a 56 KiB record of gate-scaled operands and solve blocks (plus 512
+ *    bytes of k(.)k sums with the preconditioner), which the state-carrying
+ *    kernel then reads once;
+ *  - few heads with long sequences and fp32 output (either gating): the
+ *    sequence is then split into segments that run side by side, from their
+ *    transitions and end states (fp32 [B,H,T,dk] plus a few
+ *    [B,H,segments,dk,dv|dk] arrays).
+ * The workspace holds no state between calls. */
 int pdn_chunk_fwd_workspace_size(const pdn_chunk_fwd_args *args, size_t *bytes);
 
 /* Validate only (no HIP call, no launch): PDN_OK or the code pdn_chunk_fwd
