@@ -1006,16 +1006,87 @@ __global__ void __launch_bounds__(SEG_NTHR) vec_seg_combine_kernel(const float* 
 // 16x16x32 bf16 MFMAs on hi/lo terms (hi.hi + hi.lo + lo.hi, fp32
 // accumulation), so that lane (ln, g) ends with token ln, columns 4g .. 4g + 3
 // of each 16-column block and updates o in 16-byte pieces.
+//
+// With two segments (the usual split) S_1 is segment 0's end state N_0 itself,
+// so the correction reads it from there (`direct`) and needs no combine pass;
+// the launch then also holds one workgroup per (head, CT state columns) that
+// forms the final state S_T = Phi_1 N_0 + N_1 (two_seg_final_state), beside
+// the correction workgroups.
 constexpr int COR_TOK = 256;
 constexpr int COR_CB = 128;
 __device__ __forceinline__ int cor_off(int row, int ch) {  // bf16 element offset in a staged tile
     return row * DK + ((((ch >> 3) ^ (row & 15)) << 3) | (ch & 7));
 }
-__global__ void __launch_bounds__(SEG_NTHR, 2) vec_seg_correct_kernel(const float* qh, const float* sst, float* o,
-                                                                   long T, int nseg, long seg_tokens, int dv,
-                                                                   long tiles_per_seg) {
-    __shared__ __attribute__((aligned(16))) uint16_t sH[COR_CB * DK];
-    __shared__ __attribute__((aligned(16))) uint16_t sL[COR_CB * DK];
+
+// S_T = Phi_1 N_0 + N_1 for columns j0 .. j0 + CT - 1 of head bh (two
+// segments), fp32 16x16x4 MFMAs as in the combine pass; the key dimension in
+// two halves of 64 so that Phi's half (row stride 68) and N_0's rows (stride
+// 48) fit in the correction's LDS.
+__device__ __forceinline__ void two_seg_final_state(const float* nst, const float* phi, float* ST, long bh,
+                                                    int j0, int dv, float* fbuf) {
+    constexpr int KH = DK / 2;
+    float(*sPhi)[KH + 4] = reinterpret_cast<float(*)[KH + 4]>(fbuf);
+    float(*sS)[CT + 16] = reinterpret_cast<float(*)[CT + 16]>(fbuf + DK * (KH + 4));
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int ln = lane & 15, g4 = lane >> 4;
+    const float* N0 = nst + (bh * 2) * DK * dv;
+    const float* N1 = N0 + DK * dv;
+    const float* P = phi + (bh * 2 + 1) * DK * DK;
+    // wave w: rows 32w .. 32w + 31 (two 16-row blocks) x CT = 32 columns (two blocks)
+    f32x4 acc[2][2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[rb][cb][e] = N1[(32 * wave + 16 * rb + 4 * g4 + e) * dv + j0 + 16 * cb + ln];
+    for (int kh = 0; kh < DK; kh += KH) {
+        __syncthreads();  // the previous half has been read
+        for (int i = tid; i < DK * KH / 4; i += SEG_NTHR) {
+            const int r = i / (KH / 4), c4 = i % (KH / 4);
+            *reinterpret_cast<f32x4*>(&sPhi[r][4 * c4]) = *reinterpret_cast<const f32x4*>(P + r * DK + kh + 4 * c4);
+        }
+        for (int i = tid; i < KH * CT / 4; i += SEG_NTHR) {
+            const int r = i / (CT / 4), c4 = i % (CT / 4);
+            *reinterpret_cast<f32x4*>(&sS[r][4 * c4]) = *reinterpret_cast<const f32x4*>(N0 + (kh + r) * dv + j0 + 4 * c4);
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int k = 0; k < KH; k += 4) {
+            float a[2], b[2];
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) a[rb] = sPhi[32 * wave + 16 * rb + ln][k + g4];
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) b[cb] = sS[k + g4][16 * cb + ln];
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = mfma4(a[rb], b[cb], acc[rb][cb]);
+        }
+    }
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                ST[(bh * DK + 32 * wave + 16 * rb + 4 * g4 + e) * dv + j0 + 16 * cb + ln] = acc[rb][cb][e];
+}
+
+__global__ void __launch_bounds__(SEG_NTHR, 2) vec_seg_correct_kernel(const float* qh, const float* sst, const float* nst,
+                                                                   const float* phi, float* ST, float* o, long T,
+                                                                   int nseg, long seg_tokens, int dv,
+                                                                   long tiles_per_seg, long ncorr) {
+    __shared__ __attribute__((aligned(16))) uint16_t sbuf[2 * COR_CB * DK];
+    uint16_t* sH = sbuf;
+    uint16_t* sL = sbuf + COR_CB * DK;
+    const bool direct = nseg == 2;  // S_1 = N_0: read segment 0's end state
+    if (blockIdx.x >= ncorr) {      // two segments: a final-state workgroup
+        const long u = blockIdx.x - ncorr;
+        two_seg_final_state(nst, phi, ST, u / (dv / CT), static_cast<int>(u % (dv / CT)) * CT, dv,
+                            reinterpret_cast<float*>(sbuf));
+        return;
+    }
     const long unit = blockIdx.x;
     const long per_bh = (nseg - 1) * tiles_per_seg;
     const long bh = unit / per_bh;
@@ -1026,7 +1097,7 @@ __global__ void __launch_bounds__(SEG_NTHR, 2) vec_seg_correct_kernel(const floa
     if (t0 >= t1) return;  // whole workgroup
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ln = lane & 15, g = lane >> 4;
-    const float* S = sst + (bh * nseg + gs) * DK * dv;
+    const float* S = direct ? nst + (bh * nseg) * DK * dv : sst + (bh * nseg + gs) * DK * dv;
     for (int jb = 0; jb < dv; jb += COR_CB) {
         const int nj = min(COR_CB, dv - jb);  // a multiple of 32
         __syncthreads();  // the previous pass is done with the staged tile
@@ -1233,11 +1304,19 @@ hipError_t launch_chunk_vec(const pdn_chunk_fwd_args& a, hipStream_t stream) {
 hipError_t launch_seg_finish(const float* nst, const float* phi, float* sst, float* ST, const float* qh,
                              float* o, long nbh, long T, int nseg, long seg_tokens, int dv,
                              hipStream_t stream) {
-    vec_seg_combine_kernel<<<dim3(static_cast<unsigned>(nbh * (dv / CT))), dim3(SEG_NTHR), 0, stream>>>(
-        nst, phi, sst, ST, nseg, dv);
     const long tiles = (seg_tokens + COR_TOK - 1) / COR_TOK;
-    vec_seg_correct_kernel<<<dim3(static_cast<unsigned>(nbh * (nseg - 1) * tiles)), dim3(SEG_NTHR), 0, stream>>>(
-        qh, sst, o, T, nseg, seg_tokens, dv, tiles);
+    const long ncorr = nbh * (nseg - 1) * tiles;
+    long nfinal = 0;
+    if (nseg == 2) {
+        // no combine pass: the final state comes from extra workgroups of the
+        // correction launch (none without ST)
+        nfinal = ST ? nbh * (dv / CT) : 0;
+    } else {
+        vec_seg_combine_kernel<<<dim3(static_cast<unsigned>(nbh * (dv / CT))), dim3(SEG_NTHR), 0, stream>>>(
+            nst, phi, sst, ST, nseg, dv);
+    }
+    vec_seg_correct_kernel<<<dim3(static_cast<unsigned>(ncorr + nfinal)), dim3(SEG_NTHR), 0, stream>>>(
+        qh, sst, nst, phi, ST, o, T, nseg, seg_tokens, dv, tiles, ncorr);
     return hipGetLastError();
 }
 

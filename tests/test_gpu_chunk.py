@@ -679,19 +679,21 @@ def test_sequence_segments_scalar_gates(cfg, T):
     assert wc < TOL_BF16
 
 
-def test_sequence_segments_scalar_gates_in_place_and_dv64():
-    # in-place state (the final state is written by the segment combination,
-    # after segment 0 read the start state), dv = 64 (two value tiles, four
+@pytest.mark.parametrize("H,T", [(3, 1500), (2, 1100)])   # 3 segments (combine pass); 2 (no combine)
+def test_sequence_segments_scalar_gates_in_place_and_dv64(H, T):
+    # in-place state (the final state is written after segment 0 read the
+    # start state: by the combine pass, or with two segments by the final-state
+    # workgroups of the correction launch), dv = 64 (two value tiles, four
     # identity tiles), a ragged tail in the last segment
     rng = np.random.default_rng(71)
-    w = synth.gdn(B=1, H=3, T=1500, d=128, seed=71)
-    w.v = synth.round_to_bf16(rng.standard_normal((1, 3, 1500, 64)).astype(np.float32))
+    w = synth.gdn(B=1, H=H, T=T, d=128, seed=71)
+    w.v = synth.round_to_bf16(rng.standard_normal((1, H, T, 64)).astype(np.float32))
     w.dv = 64
-    w.S0 = (0.1 * rng.standard_normal((1, 3, 128, 64))).astype(np.float32)
+    w.S0 = (0.1 * rng.standard_normal((1, H, 128, 64))).astype(np.float32)
     o, ST, _ = run_chunk(w, in_place=True)
     o_ref, S_ref, _ = oracle.run_workload(w)
     eo, es = rel_l2(o, o_ref), rel_l2(ST, S_ref)
-    report("segments scalar gates in place dv=64 T=1500", o=eo, S=es)
+    report("segments scalar gates in place dv=64 H=%d T=%d" % (H, T), o=eo, S=es)
     assert eo < TOL_BF16 and es < TOL_BF16
 
 
