@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <atomic>
 #include <mutex>
 
 #include "kernels.h"
@@ -179,11 +180,13 @@ void* scratch_on_current_device() {
 namespace pdn {
 
 int device_cu_count() {
+    // queried once per device (decode launches ask on every step)
+    static std::atomic<int> cached[kMaxDevices] = {};
     int dev = 0, n = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        n < 1)
-        return 256;  // the MI355X count; only grid sizes depend on it
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;  // the MI355X count; only grid sizes depend on it
+    if (dev < kMaxDevices && (n = cached[dev].load(std::memory_order_relaxed)) > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) return 256;
+    if (dev < kMaxDevices) cached[dev].store(n, std::memory_order_relaxed);
     return n;
 }
 
