@@ -941,6 +941,13 @@ constexpr int gates_lds_floats() {
     return gates_sbuf_floats<DK>() + 2 * BC * (BC + 1) + (NT / DK) * 4 * DK + 3 * DK + 3 * BC;
 }
 
+// An empty asm statement that may change x, y, z: values derived from them
+// past this point are computed afresh rather than reused from earlier
+// (register pressure: reuse would keep them live and spill them).
+__device__ __forceinline__ void rematerialize(float& x, float& y, float& z) {
+    asm volatile("" : "+v"(x), "+v"(y), "+v"(z));
+}
+
 // the gate gradients of chunk `unit` (= bh * nc + c), from its gradient record
 template <int DK, bool BF16>
 __device__ __forceinline__ void gates_body(const BwdParams& p, float* smem, long unit) {
@@ -1193,6 +1200,11 @@ __device__ __forceinline__ void gates_body(const BwdParams& p, float* smem, long
 #pragma unroll
         for (int u = 0; u < RPT; ++u) {
             const int r = r0 + u;
+            // the gains and decay factors of the operand step are recomputed
+            // here, not kept: left to itself the compiler reuses them, keeps
+            // 16 rows of them live across the MFMA step, spills them, and
+            // reloads one per row, each reload waiting for every load in flight
+            rematerialize(G[u], kk[u], bb[u]);
             float kwr, krr;
             keys_of(p.kmode, gain_at(u, A, aux, den), kk[u], kwr, krr);
             const float gm = r < 16 ? G8 : G24;
@@ -1250,6 +1262,7 @@ __device__ __forceinline__ void gates_body(const BwdParams& p, float* smem, long
         for (int u = 0; u < RPT; ++u) {
             const int r = r0 + u;
             const long t = t0 + r;
+            rematerialize(G[u], kk[u], bb[u]);  // as in the per-row step above
             const float braw = bb[u];
             const float b = gain_at(u, A, aux, den);
             const float dkwr = sA3[r][i], dkrr = sA1[r][i];
