@@ -996,7 +996,6 @@ __device__ __forceinline__ void gates_body(const BwdParams& p, float* smem, long
         G[u] = cv.lav(r0 + u);
         bb[u] = cv.bev(r0 + u);
     }
-    const float dgam = D[3 * BC * DK + i];  // dGamma_C of channel i
     // dv and dgamma' (wave w: rows w, w + 4, ...; lanes over columns), in two
     // batches of four rows, every load of a batch before its stores
     const bool gsum = p.gmode == PDN_GATE_SCALAR ||
@@ -1187,6 +1186,10 @@ __device__ __forceinline__ void gates_body(const BwdParams& p, float* smem, long
     const float* DdQg = D + i;
     const float* DdKg = D + BC * DK + i;
     const float* DdKd = D + 2 * BC * DK + i;
+    // dGamma_C of channel i, read with the rows below: read at the start of the
+    // phase, the compiler spilled it at once, and the spill store waited for
+    // every load issued before it (the channel columns)
+    const float dgam = D[3 * BC * DK + i];
     float kdsum = 0.f;
     {
         float dqg[RPT], dkg[RPT], dkd[RPT];
