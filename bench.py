@@ -534,7 +534,7 @@ def cpu_baseline(w, target_s: float):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU only (no multi-GPU path); "
+        print("bench.py: the library runs on one GPU only (no multi-GPU path); "
               "use --gpus 1", file=sys.stderr)
         sys.exit(2)
     if args.copy_probe:
