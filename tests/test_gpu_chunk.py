@@ -661,6 +661,18 @@ def test_sequence_segments(mode, T):
     check("segments %s T=%d" % (mode, T), w, TOL_BF16, A0=A0, key_mode=km, precond_mode=pm)
 
 
+@pytest.mark.parametrize("T", [600, 1000])   # 2 and 4 segments for two heads
+def test_sequence_segments_in_place(T):
+    # in-place state on the per-channel-gate path: the final state is written
+    # after segment 0 read the start state, by the correction launch's extra
+    # workgroups (two segments) or by the combine pass (more)
+    rng = np.random.default_rng(900 + T)
+    w = synth.gdn2_precond(B=1, H=2, T=T, d=128, seed=T, n_pairs=4)
+    A0 = rng.uniform(0.0, 2.0, (1, 2, 128)).astype(np.float32)
+    w.S0 = (0.1 * rng.standard_normal((1, 2, 128, 128))).astype(np.float32)
+    check("segments in place T=%d" % T, w, TOL_BF16, A0=A0, in_place=True)
+
+
 @pytest.mark.parametrize("T", [1024, 2047, 4160])   # 2, 4 and 8 segments for two heads
 @pytest.mark.parametrize("cfg", ["gdn", "gdn_vec_gain"])
 def test_sequence_segments_scalar_gates(cfg, T):
