@@ -522,39 +522,57 @@ __device__ __forceinline__ void interleave_loads() {
 // unit run on XCD u mod kXcds (see bwd_states_kernel); when the head count
 // allows, all column tiles of a head get the same u mod kXcds, so that they
 // share the chunk records in that XCD's L2.
+template <int SJ>
 __device__ __forceinline__ void unit_tile(const BwdParams& p, long u, long& bh, int& j0) {
-    const int ntile = p.dv / JT;
+    const int ntile = p.dv / SJ;
     if (p.nbh % kXcds == 0) {
         bh = (u / (static_cast<long>(kXcds) * ntile)) * kXcds + u % kXcds;
-        j0 = static_cast<int>((u / kXcds) % ntile) * JT;
+        j0 = static_cast<int>((u / kXcds) % ntile) * SJ;
     } else {
         bh = u / ntile;
-        j0 = static_cast<int>(u % ntile) * JT;
+        j0 = static_cast<int>(u % ntile) * SJ;
     }
 }
 
-// LDS of the forward state pass, in floats
-template <int DK>
+// LDS of the forward state pass, in floats (SJ value columns per workgroup)
+template <int DK, int SJ>
 constexpr int fwd_lds_floats() {
-    return BC * (DK + 4) + BC * (DK + 16) + BC * (BC + 4) + 2 * BC * (JT + 16) + DK * (JT + 16) + DK;
+    return BC * (DK + 4) + BC * (DK + 16) + BC * (BC + 4) + 2 * BC * (SJ + 16) + DK * (SJ + 16) + DK;
 }
 
-// forward state pass of workgroup `unit` (b, h, 32 value columns)
-template <int DK>
+// Tile assignment of the state passes (SJ = 32 or 16 value columns per
+// workgroup, four waves): the BC x SJ tiles of X / U (forward) and Y / Z
+// (reverse) go one per wave (with SJ = 16, waves 2 and 3 have none and only
+// take part in the barriers); the DK x SJ state tile is NSB 16 x 16 blocks per
+// wave.  Narrow tiles double the workgroups of a call, for few heads.
+template <int DK, int SJ>
+struct StateTiles {
+    static constexpr int CB = SJ / 16;              // 16-column blocks
+    static constexpr int NSB = DK / 16 * CB / 4;    // state blocks per wave
+    static constexpr int NXT = BC / 16 * CB;        // waves with an X / Y tile
+    static __device__ __forceinline__ int rb(int w) { return CB == 2 ? w >> 1 : w & 1; }
+    static __device__ __forceinline__ int xcb(int w) { return CB == 2 ? w & 1 : 0; }
+    static __device__ __forceinline__ int sib(int q) { return q / CB; }   // state block q: row block
+    static __device__ __forceinline__ int scb(int q) { return q % CB; }   // and column block
+};
+
+// forward state pass of workgroup `unit` (b, h, SJ value columns)
+template <int DK, int SJ>
 __device__ __forceinline__ void state_fwd_body(const BwdParams& p, float* smem, long unit) {
-    constexpr int NSB = DK / 16 * 2 / 4;  // state tiles per wave
+    using ST = StateTiles<DK, SJ>;
+    constexpr int NSB = ST::NSB;  // state tiles per wave
     // sKg read as [row][k] (stride 4 mod 64 banks); sKd read as [k][col] (stride 16 mod 64)
     float(*sKg)[DK + 4] = reinterpret_cast<float(*)[DK + 4]>(smem);
     float(*sKd)[DK + 16] = reinterpret_cast<float(*)[DK + 16]>(smem + BC * (DK + 4));
     float(*sM)[BC + 4] = reinterpret_cast<float(*)[BC + 4]>(smem + BC * (DK + 4) + BC * (DK + 16));
     float* base = smem + BC * (DK + 4) + BC * (DK + 16) + BC * (BC + 4);
-    float(*sX)[JT + 16] = reinterpret_cast<float(*)[JT + 16]>(base);
-    float(*sU)[JT + 16] = reinterpret_cast<float(*)[JT + 16]>(base + BC * (JT + 16));
-    float(*sS)[JT + 16] = reinterpret_cast<float(*)[JT + 16]>(base + 2 * BC * (JT + 16));
-    float* sGc = base + 2 * BC * (JT + 16) + DK * (JT + 16);
+    float(*sX)[SJ + 16] = reinterpret_cast<float(*)[SJ + 16]>(base);
+    float(*sU)[SJ + 16] = reinterpret_cast<float(*)[SJ + 16]>(base + BC * (SJ + 16));
+    float(*sS)[SJ + 16] = reinterpret_cast<float(*)[SJ + 16]>(base + 2 * BC * (SJ + 16));
+    float* sGc = base + 2 * BC * (SJ + 16) + DK * (SJ + 16);
     long bh;
     int j0;
-    unit_tile(p, unit, bh, j0);
+    unit_tile<SJ>(p, unit, bh, j0);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int ln = lane & 15, g4 = lane >> 4;
     const long Tp = static_cast<long>(p.nc) * BC;
@@ -563,7 +581,7 @@ __device__ __forceinline__ void state_fwd_body(const BwdParams& p, float* smem, 
     f32x4 sacc[NSB];
 #pragma unroll
     for (int m = 0; m < NSB; ++m) {
-        const int q = w * NSB + m, ib = q >> 1, cb = q & 1;
+        const int q = w * NSB + m, ib = ST::sib(q), cb = ST::scb(q);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int row = 16 * ib + 4 * g4 + e, col = 16 * cb + ln;
@@ -573,7 +591,9 @@ __device__ __forceinline__ void state_fwd_body(const BwdParams& p, float* smem, 
             p.st[bh * (p.nc + 1) * SZ + row * p.dv + j0 + col] = v;
         }
     }
-    const int rb = w >> 1, xcb = w & 1;
+    // X / Y tile of this wave (SJ = 16: waves 2 and 3 repeat the tiles of waves
+    // 0 and 1, with the same inputs and instructions, and store the same values)
+    const int rb = ST::rb(w), xcb = ST::xcb(w);
     // the next chunk's operands, loaded while the current one is processed
     Tile4<DK, BC * DK / 4> nKg, nKd;
     Tile4<BC, BC * BC / 4> nM;
@@ -624,7 +644,7 @@ __device__ __forceinline__ void state_fwd_body(const BwdParams& p, float* smem, 
         // S <- Diag(e^G_C) S + Kd^T U
 #pragma unroll
         for (int m = 0; m < NSB; ++m) {
-            const int q = w * NSB + m, ib = q >> 1, cb = q & 1;
+            const int q = w * NSB + m, ib = ST::sib(q), cb = ST::scb(q);
 #pragma unroll
             for (int e = 0; e < 4; ++e) sacc[m][e] *= sGc[16 * ib + 4 * g4 + e];
 #pragma unroll
@@ -643,27 +663,28 @@ __device__ __forceinline__ void state_fwd_body(const BwdParams& p, float* smem, 
 // LDS of the reverse state pass, in floats.  M and P reach the MFMAs from
 // registers, Z reuses Y's buffer, and the tiles use narrow row strides (some
 // two-way bank conflicts), so that both passes fit on one CU together.
-template <int DK>
+template <int DK, int SJ>
 constexpr int bwd_lds_floats() {
-    return 3 * BC * (DK + 4) + 2 * BC * (JT + 4) + DK * (JT + 4) + DK;
+    return 3 * BC * (DK + 4) + 2 * BC * (SJ + 4) + DK * (SJ + 4) + DK;
 }
 
-// reverse state pass of workgroup `unit` (b, h, 32 value columns)
-template <int DK>
+// reverse state pass of workgroup `unit` (b, h, SJ value columns)
+template <int DK, int SJ>
 __device__ __forceinline__ void state_bwd_body(const BwdParams& p, float* smem, long unit) {
-    constexpr int NSB = DK / 16 * 2 / 4;
+    using ST = StateTiles<DK, SJ>;
+    constexpr int NSB = ST::NSB;
     // sQg, sKg read as [k][col]; sKd as [row][k]
     float(*sQg)[DK + 4] = reinterpret_cast<float(*)[DK + 4]>(smem);
     float(*sKg)[DK + 4] = reinterpret_cast<float(*)[DK + 4]>(smem + BC * (DK + 4));
     float(*sKd)[DK + 4] = reinterpret_cast<float(*)[DK + 4]>(smem + 2 * BC * (DK + 4));
     float* base = smem + 3 * BC * (DK + 4);
-    float(*sdO)[JT + 4] = reinterpret_cast<float(*)[JT + 4]>(base);
-    float(*sY)[JT + 4] = reinterpret_cast<float(*)[JT + 4]>(base + BC * (JT + 4));  // then Z
-    float(*sdS)[JT + 4] = reinterpret_cast<float(*)[JT + 4]>(base + 2 * BC * (JT + 4));
-    float* sGc = base + 2 * BC * (JT + 4) + DK * (JT + 4);
+    float(*sdO)[SJ + 4] = reinterpret_cast<float(*)[SJ + 4]>(base);
+    float(*sY)[SJ + 4] = reinterpret_cast<float(*)[SJ + 4]>(base + BC * (SJ + 4));  // then Z
+    float(*sdS)[SJ + 4] = reinterpret_cast<float(*)[SJ + 4]>(base + 2 * BC * (SJ + 4));
+    float* sGc = base + 2 * BC * (SJ + 4) + DK * (SJ + 4);
     long bh;
     int j0;
-    unit_tile(p, unit, bh, j0);
+    unit_tile<SJ>(p, unit, bh, j0);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int ln = lane & 15, g4 = lane >> 4;
     const long Tp = static_cast<long>(p.nc) * BC;
@@ -672,7 +693,7 @@ __device__ __forceinline__ void state_bwd_body(const BwdParams& p, float* smem, 
     f32x4 dacc[NSB];
 #pragma unroll
     for (int m = 0; m < NSB; ++m) {
-        const int q = w * NSB + m, ib = q >> 1, cb = q & 1;
+        const int q = w * NSB + m, ib = ST::sib(q), cb = ST::scb(q);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int row = 16 * ib + 4 * g4 + e, col = 16 * cb + ln;
@@ -681,12 +702,16 @@ __device__ __forceinline__ void state_bwd_body(const BwdParams& p, float* smem, 
             sdS[row][col] = v;
         }
     }
-    const int rb = w >> 1, xcb = w & 1;
+    // X / Y tile of this wave (SJ = 16: waves 2 and 3 repeat the tiles of waves
+    // 0 and 1, with the same inputs and instructions, and store the same values)
+    const int rb = ST::rb(w), xcb = ST::xcb(w);
     Tile4<DK, BC * DK / 4> nKg, nQg, nKd;
     Tile4<DK, DK / 4> nGc;
     f32x4 ndO;  // one 4-column group of the dO tile per thread
     float nPt[BC / 4], nMt[BC / 4];  // this lane's P^T and M^T operands: P[4 k + g4][16 rb + ln]
-    const int dr = tid / (JT / 4), dc4 = tid % (JT / 4);
+    // dO staging: row dr, columns 4 dc4 .. + 3 (SJ = 16: the upper half of the
+    // workgroup repeats the rows of the lower half)
+    const int dr = (tid / (SJ / 4)) % BC, dc4 = tid % (SJ / 4);
     auto fetch = [&](long c) {
         const float* R = p.rec + (bh * p.nc + c) * RF;
         nKg.load(R, DK);
@@ -709,7 +734,7 @@ __device__ __forceinline__ void state_bwd_body(const BwdParams& p, float* smem, 
         // gradient with respect to the state after chunk c
 #pragma unroll
         for (int m = 0; m < NSB; ++m) {
-            const int q = w * NSB + m, ib = q >> 1, cb = q & 1;
+            const int q = w * NSB + m, ib = ST::sib(q), cb = ST::scb(q);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 p.dst[(bh * p.nc + c) * SZ + (16 * ib + 4 * g4 + e) * p.dv + j0 + 16 * cb + ln] = dacc[m][e];
@@ -753,7 +778,7 @@ __device__ __forceinline__ void state_bwd_body(const BwdParams& p, float* smem, 
         // dS <- Diag(e^G_C) dS' + Qg^T dO - Kg^T Z
 #pragma unroll
         for (int m = 0; m < NSB; ++m) {
-            const int q = w * NSB + m, ib = q >> 1, cb = q & 1;
+            const int q = w * NSB + m, ib = ST::sib(q), cb = ST::scb(q);
 #pragma unroll
             for (int e = 0; e < 4; ++e) dacc[m][e] *= sGc[16 * ib + 4 * g4 + e];
 #pragma unroll
@@ -768,7 +793,7 @@ __device__ __forceinline__ void state_bwd_body(const BwdParams& p, float* smem, 
     if (p.dS0) {
 #pragma unroll
         for (int m = 0; m < NSB; ++m) {
-            const int q = w * NSB + m, ib = q >> 1, cb = q & 1;
+            const int q = w * NSB + m, ib = ST::sib(q), cb = ST::scb(q);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 p.dS0[bh * SZ + (16 * ib + 4 * g4 + e) * p.dv + j0 + 16 * cb + ln] = dacc[m][e];
@@ -782,15 +807,15 @@ __device__ __forceinline__ void state_bwd_body(const BwdParams& p, float* smem, 
 // waits.  Workgroups are dealt to the XCDs in turn, so the roles alternate
 // every kXcds workgroups (every XCD gets both); the grid is padded to
 // 2 kXcds per kXcds units and the padding exits at once.
-template <int DK>
+template <int DK, int SJ>
 __global__ void __launch_bounds__(NT, 2) bwd_states_kernel(BwdParams p, long units) {
-    constexpr int LDSF = fwd_lds_floats<DK>() > bwd_lds_floats<DK>() ? fwd_lds_floats<DK>()
-                                                                     : bwd_lds_floats<DK>();
+    constexpr int LDSF = fwd_lds_floats<DK, SJ>() > bwd_lds_floats<DK, SJ>() ? fwd_lds_floats<DK, SJ>()
+                                                                             : bwd_lds_floats<DK, SJ>();
     __shared__ __attribute__((aligned(16))) float smem[LDSF];
     const long unit = (blockIdx.x / (2 * kXcds)) * kXcds + blockIdx.x % kXcds;
     if (unit >= units) return;  // whole workgroup, before any barrier
-    if ((blockIdx.x / kXcds) & 1) state_bwd_body<DK>(p, smem, unit);
-    else state_fwd_body<DK>(p, smem, unit);
+    if ((blockIdx.x / kXcds) & 1) state_bwd_body<DK, SJ>(p, smem, unit);
+    else state_fwd_body<DK, SJ>(p, smem, unit);
 }
 
 // ---------------------------------------------------------------------------
@@ -1464,7 +1489,10 @@ template <int DK, bool BF16>
 hipError_t run_bwd(const pdn_chunk_bwd_args& a, const BwdParams& p, hipStream_t s) {
     const unsigned nbh = static_cast<unsigned>(p.nbh);
     const unsigned nch = static_cast<unsigned>(p.nbh * p.nc);
-    const unsigned ntl = static_cast<unsigned>(p.nbh * (p.dv / JT));
+    // state-pass tiles: 32 value columns, or 16 when that still leaves at
+    // least half the CUs without a state-pass workgroup (few heads)
+    const bool narrow = 2L * p.nbh * (p.dv / JT) <= device_cu_count() / 2;
+    const unsigned ntl = static_cast<unsigned>(p.nbh * (p.dv / (narrow ? 16 : JT)));
     (void)a;
     if (p.pre) {
         bwd_ksum_kernel<DK, BF16><<<nch, DK, 0, s>>>(p);
@@ -1472,8 +1500,9 @@ hipError_t run_bwd(const pdn_chunk_bwd_args& a, const BwdParams& p, hipStream_t 
     }
     if (p.stab) bwd_prep_kernel<DK, BF16, true><<<nch, NT, 0, s>>>(p);
     else bwd_prep_kernel<DK, BF16, false><<<nch, NT, 0, s>>>(p);
-    bwd_states_kernel<DK><<<2 * kXcds * ((ntl + kXcds - 1) / kXcds), NT, 0, s>>>(
-        p, static_cast<long>(ntl));
+    const unsigned sgrid = 2 * kXcds * ((ntl + kXcds - 1) / kXcds);
+    if (narrow) bwd_states_kernel<DK, 16><<<sgrid, NT, 0, s>>>(p, static_cast<long>(ntl));
+    else bwd_states_kernel<DK, JT><<<sgrid, NT, 0, s>>>(p, static_cast<long>(ntl));
     bwd_grads_kernel<DK, BF16><<<nch, NT, 0, s>>>(p);
     if (p.pre) {
         bwd_dA_scan_kernel<DK><<<nbh, DK, 0, s>>>(p);
