@@ -591,9 +591,11 @@ __device__ __forceinline__ void state_fwd_body(const BwdParams& p, float* smem, 
             p.st[bh * (p.nc + 1) * SZ + row * p.dv + j0 + col] = v;
         }
     }
-    // X / Y tile of this wave (SJ = 16: waves 2 and 3 repeat the tiles of waves
-    // 0 and 1, with the same inputs and instructions, and store the same values)
+    // X / Y tile of this wave (SJ = 16: waves 2 and 3 compute the tiles of
+    // waves 0 and 1 again, which keeps their loads and MFMAs on the same path,
+    // and store nothing)
     const int rb = ST::rb(w), xcb = ST::xcb(w);
+    const bool xown = w < ST::NXT;
     // the next chunk's operands, loaded while the current one is processed
     Tile4<DK, BC * DK / 4> nKg, nKd;
     Tile4<BC, BC * BC / 4> nM;
@@ -627,19 +629,21 @@ __device__ __forceinline__ void state_fwd_body(const BwdParams& p, float* smem, 
 #pragma unroll
         for (int k = 0; k < DK; k += 4) x = mfma4(-sKg[16 * rb + ln][k + g4], sS[k + g4][16 * xcb + ln], x);
         interleave_loads<DK / 4>();
+        if (xown)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sX[16 * rb + 4 * g4 + e][16 * xcb + ln] = x[e];
+            for (int e = 0; e < 4; ++e) sX[16 * rb + 4 * g4 + e][16 * xcb + ln] = x[e];
         __syncthreads();
         // U = M X
         f32x4 u = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int k = 0; k < BC; k += 4) u = mfma4(sM[16 * rb + ln][k + g4], sX[k + g4][16 * xcb + ln], u);
+        if (xown)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = 16 * rb + 4 * g4 + e;
-            sU[r][16 * xcb + ln] = u[e];
-            p.U[(bh * Tp + c * BC + r) * p.dv + j0 + 16 * xcb + ln] = u[e];
-        }
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * rb + 4 * g4 + e;
+                sU[r][16 * xcb + ln] = u[e];
+                p.U[(bh * Tp + c * BC + r) * p.dv + j0 + 16 * xcb + ln] = u[e];
+            }
         __syncthreads();
         // S <- Diag(e^G_C) S + Kd^T U
 #pragma unroll
@@ -702,15 +706,17 @@ __device__ __forceinline__ void state_bwd_body(const BwdParams& p, float* smem, 
             sdS[row][col] = v;
         }
     }
-    // X / Y tile of this wave (SJ = 16: waves 2 and 3 repeat the tiles of waves
-    // 0 and 1, with the same inputs and instructions, and store the same values)
+    // X / Y tile of this wave (SJ = 16: waves 2 and 3 compute the tiles of
+    // waves 0 and 1 again, which keeps their loads and MFMAs on the same path,
+    // and store nothing)
     const int rb = ST::rb(w), xcb = ST::xcb(w);
+    const bool xown = w < ST::NXT;
     Tile4<DK, BC * DK / 4> nKg, nQg, nKd;
     Tile4<DK, DK / 4> nGc;
     f32x4 ndO;  // one 4-column group of the dO tile per thread
     float nPt[BC / 4], nMt[BC / 4];  // this lane's P^T and M^T operands: P[4 k + g4][16 rb + ln]
     // dO staging: row dr, columns 4 dc4 .. + 3 (SJ = 16: the upper half of the
-    // workgroup repeats the rows of the lower half)
+    // workgroup loads the rows of the lower half again, stores nothing)
     const int dr = (tid / (SJ / 4)) % BC, dc4 = tid % (SJ / 4);
     auto fetch = [&](long c) {
         const float* R = p.rec + (bh * p.nc + c) * RF;
@@ -744,7 +750,8 @@ __device__ __forceinline__ void state_bwd_body(const BwdParams& p, float* smem, 
         nQg.template store<DK + 4>(&sQg[0][0]);
         nKd.template store<DK + 4>(&sKd[0][0]);
         nGc.template store<DK>(sGc);
-        *reinterpret_cast<f32x4*>(&sdO[dr][4 * dc4]) = c * BC + dr < p.T ? ndO : f32x4{0.f, 0.f, 0.f, 0.f};
+        if (tid < BC * SJ / 4)
+            *reinterpret_cast<f32x4*>(&sdO[dr][4 * dc4]) = c * BC + dr < p.T ? ndO : f32x4{0.f, 0.f, 0.f, 0.f};
         float aPt[BC / 4], aMt[BC / 4];
 #pragma unroll
         for (int k = 0; k < BC / 4; ++k) {
@@ -760,20 +767,22 @@ __device__ __forceinline__ void state_bwd_body(const BwdParams& p, float* smem, 
 #pragma unroll
         for (int k = 0; k < DK; k += 4) y = mfma4(sKd[16 * rb + ln][k + g4], sdS[k + g4][16 * xcb + ln], y);
         interleave_loads<BC / 4 + DK / 4>();
+        if (xown)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sY[16 * rb + 4 * g4 + e][16 * xcb + ln] = y[e];
+            for (int e = 0; e < 4; ++e) sY[16 * rb + 4 * g4 + e][16 * xcb + ln] = y[e];
         __syncthreads();
         // Z = M^T Y, into Y's buffer once every wave has read Y
         f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int k = 0; k < BC / 4; ++k) z = mfma4(aMt[k], sY[4 * k + g4][16 * xcb + ln], z);
         __syncthreads();
+        if (xown)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = 16 * rb + 4 * g4 + e;
-            sY[r][16 * xcb + ln] = z[e];
-            p.Z[(bh * Tp + c * BC + r) * p.dv + j0 + 16 * xcb + ln] = z[e];
-        }
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * rb + 4 * g4 + e;
+                sY[r][16 * xcb + ln] = z[e];
+                p.Z[(bh * Tp + c * BC + r) * p.dv + j0 + 16 * xcb + ln] = z[e];
+            }
         __syncthreads();
         // dS <- Diag(e^G_C) dS' + Qg^T dO - Kg^T Z
 #pragma unroll
