@@ -188,7 +188,10 @@ def clock_ramp(call, min_ms=CLOCK_RAMP_MS):
 def bench_prefill(args, w=None, steps=None, warmup=None):
     """Scalar-gate prefill (the throughput kernel) on workload w (default: the
     B4 H16 T8192 headline): a clock ramp of >= 30 ms, `warmup` untimed calls,
-    then `steps` calls each bracketed by HIP events on the launch stream."""
+    then `steps` back-to-back calls between one pair of HIP events on the
+    launch stream (kernel_ms = their elapsed time / steps), then the same
+    number of calls each bracketed by its own events (per-call spread; an
+    event pair per call adds ~2% of its own)."""
     import torch
     import gated_delta_rule_77_amd as pdn
     from gated_delta_rule_77_amd import synth
@@ -213,18 +216,24 @@ def bench_prefill(args, w=None, steps=None, warmup=None):
         step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kernel_ms = e0.elapsed_time(e1) / steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
     for i in range(steps):
         ev[i][0].record(stream)
         step()
         ev[i][1].record(stream)
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
     kern_ms = [a.elapsed_time(b) for a, b in ev]
-    kernel_ms = sum(kern_ms) / len(kern_ms)
     del q, k, v, la, be, o, ST, ws
 
     BH, T, dk, dv = w.B * w.H, w.T, w.dk, w.dv
@@ -238,6 +247,7 @@ def bench_prefill(args, w=None, steps=None, warmup=None):
     return {
         "workload": w.name, "B": w.B, "H": w.H, "T": T, "dk": dk, "dv": dv,
         "elapsed_s": t1 - t0, "tokens": w.B * T, "kernel_ms": kernel_ms,
+        "kernel_ms_per_call_events": sum(kern_ms) / len(kern_ms),
         "kernel_ms_min": min(kern_ms), "alg_bytes": alg_bytes, "alg_flops": alg_flops,
         "achieved_gbs": alg_bytes / ks / 1e9, "achieved_tflops": alg_flops / ks / 1e12,
         "clock_ramp_calls": ramp, "workspace_bytes": nws, "sample": w,
@@ -290,17 +300,26 @@ def bench_decode(args):
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     n = args.decode_steps
+    # n back-to-back steps between one event pair (kernel_ms), then n steps
+    # each between its own events (the per-step median; an event pair per
+    # step adds ~5 us of its own)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(n):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kernel_ms = e0.elapsed_time(e1) / n
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(n)]
-    t0 = time.perf_counter()
     for i in range(n):
         ev[i][0].record(stream)
         step(i)
         ev[i][1].record(stream)
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
     kern_ms = [a.elapsed_time(b) for a, b in ev]
-    kernel_ms = sum(kern_ms) / n
     kern_sorted = sorted(kern_ms)
     median_ms = kern_sorted[n // 2]
 
@@ -581,6 +600,7 @@ def main():
                      "unit": "GB/s", "frac": frac,
                      "traffic": measured_traffic(pf["workload"])},
         "kernel_ms": pf["kernel_ms"],
+        "kernel_ms_per_call_events": pf["kernel_ms_per_call_events"],
         "alg_bytes_per_launch": pf["alg_bytes"],
         "mfma": {"counter_busy": measured_mfma_busy(pf["workload"]),
                  "alg_tflops": pf["achieved_tflops"], "peak_tflops": BF16_PEAK_TFLOPS,
