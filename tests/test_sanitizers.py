@@ -71,5 +71,8 @@ def test_api_validation_under_asan_ubsan(tmp_path):
           "-I" + os.path.join(ROOT, "include"), lib, "-Wl,-rpath," + str(tmp_path),
           "-Wl,-rpath," + os.path.join(ROCM, "lib"), "-o", exe])
     r = _run([exe], env=ENV, timeout=300)
-    assert "argument sets" in r.stdout
+    assert "argument sets" in r.stdout and " 0 inconsistent answers" in r.stdout, r.stdout
+    # the random sets reach the accepting paths too, not only early rejections
+    accepted = int(r.stdout.split(" random, ")[1].split(" of them accepted")[0])
+    assert accepted > 100, r.stdout
     assert "runtime error" not in r.stderr and "AddressSanitizer" not in r.stderr
