@@ -35,8 +35,9 @@
 //     columns); waves 0-1 hold 16 state columns each in registers and run
 //     the sequential part (KS, the block solve U_0 = D_0 X_0,
 //     U_1 = D_1 X_1 - N U_0, QS, PU, the state update), wave 2 copies the
-//     next chunk's record from HBM into LDS by DMA, wave 3 stages the
-//     gain-scaled value tile.  One barrier per chunk.
+//     records from HBM into LDS by DMA two chunks ahead, wave 3 stages the
+//     gain-scaled value tile.  One barrier per chunk, plus an LDS flag per
+//     chain wave that tells wave 2 when a buffer has been read.
 //
 // The per-channel decay inside a 16-token block is split around the block's
 // middle token (2^(G_r - Gm) 2^(Gm - G_s)); the per-token clamp of
@@ -86,13 +87,20 @@ enum { F16_D0 = 0, F16_D1 = 1, F16_N10 = 2 };
 __device__ __forceinline__ int f16_off(int s, int plane, int lane) { return R_F16 + ((s * 2 + plane) * 64 + lane) * 8; }
 __device__ __forceinline__ int pf_off(int R, int plane, int lane) { return R_PF + ((R * 2 + plane) * 64 + lane) * 16; }
 
-// Chain kernel LDS: two buffers, each a record image followed by the value
-// tile transposed (fp32 [32 columns][VTS]).
-constexpr int B_VT = REC;
-constexpr int BUFV = REC + DVT * VTS * 4;
-constexpr int LDS_CHAIN = 2 * BUFV;
+// Chain kernel LDS.  A record goes in as two parts: part A (the Kg and Qg
+// tiles) into a ring of three slots, part B (Kd, the fragments, Gamma_31) into
+// one of two buffers, each followed by the value tile transposed (fp32
+// [32 columns][VTS]).  With three slots, chunk c + 2's part A can be fetched
+// as soon as chunk c starts (its slot was chunk c - 1's); part B waits until
+// the chain waves have read chunk c's buffer.
+constexpr int PA = R_KDH;       // part A: record bytes [0, PA)
+constexpr int PB = REC - PA;    // part B: record bytes [PA, REC)
+constexpr int B_VT = PB;        // value tile, within a part-B buffer
+constexpr int BUFB = PB + DVT * VTS * 4;
+constexpr int L_B = 3 * PA;     // the part-B buffers follow the three slots
+constexpr int LDS_CHAIN = L_B + 2 * BUFB;
 static_assert(LDS_CHAIN <= 160 * 1024, "LDS budget");
-static_assert(REC % 1024 == 0 && BUFV % 16 == 0, "record alignment");
+static_assert(PA % 1024 == 0 && REC % 1024 == 0 && BUFB % 16 == 0, "record alignment");
 
 // Preparation kernel: scratch for the two diagonal blocks of each wave.
 constexpr int SCR_STRIDE = 16 * 20 + 16;
@@ -605,6 +613,10 @@ __global__ void __launch_bounds__(256) vec_prep_kernel(PrepParams p) {
 template <bool SEG>
 __global__ void __launch_bounds__(NTHR) vec_chain_kernel(ChainParams p) {
     __shared__ __attribute__((aligned(16))) char smem[LDS_CHAIN];
+    // per chain wave: the last chunk (counted from the segment start) whose
+    // LDS reads have all returned; a separate LDS object, so that the
+    // compiler can tell it from the DMA target
+    __shared__ int rdone[NCHAIN];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -657,6 +669,7 @@ __global__ void __launch_bounds__(NTHR) vec_chain_kernel(ChainParams p) {
     const long c0 = SEG ? seg * p.cps : 0;
     const long c1 = SEG ? min(c0 + p.cps, nc) : nc;
     const char* recs = p.rec + bh * nc * REC;
+    const int slot0 = static_cast<int>(c0 % 3);  // part-A slot of chunk c0
 
     if (wave < NCHAIN) {
         f32x4 sacc[8];
@@ -675,17 +688,21 @@ __global__ void __launch_bounds__(NTHR) vec_chain_kernel(ChainParams p) {
 #pragma unroll
             for (int ib = 0; ib < 8; ++ib) sacc[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
+        rdone[wave] = -1;
         __syncthreads();  // the first chunk is staged
-        for (long c = c0; c < c1; ++c) {
-            const char* cur = smem + (c & 1) * BUFV;
-            const uint16_t* kgh = reinterpret_cast<const uint16_t*>(cur + R_KGH);
-            const uint16_t* kgl = reinterpret_cast<const uint16_t*>(cur + R_KGL);
-            const uint16_t* qgh = reinterpret_cast<const uint16_t*>(cur + R_QGH);
-            const uint16_t* qgl = reinterpret_cast<const uint16_t*>(cur + R_QGL);
-            const uint16_t* kdh = reinterpret_cast<const uint16_t*>(cur + R_KDH);
-            const uint16_t* kdl = reinterpret_cast<const uint16_t*>(cur + R_KDL);
-            const float* sVt = reinterpret_cast<const float*>(cur + B_VT) + (16 * wave + ln) * VTS;
-            const float* gcs = reinterpret_cast<const float*>(cur + R_GC);
+        int sa = slot0;
+        for (long c = c0; c < c1; ++c, sa = sa == 2 ? 0 : sa + 1) {
+            const char* curA = smem + sa * PA;
+            // part-B buffer; record offsets o >= PA are at curB + (o - PA)
+            const char* curB = smem + L_B + (c & 1) * BUFB - PA;
+            const uint16_t* kgh = reinterpret_cast<const uint16_t*>(curA + R_KGH);
+            const uint16_t* kgl = reinterpret_cast<const uint16_t*>(curA + R_KGL);
+            const uint16_t* qgh = reinterpret_cast<const uint16_t*>(curA + R_QGH);
+            const uint16_t* qgl = reinterpret_cast<const uint16_t*>(curA + R_QGL);
+            const uint16_t* kdh = reinterpret_cast<const uint16_t*>(curB + R_KDH);
+            const uint16_t* kdl = reinterpret_cast<const uint16_t*>(curB + R_KDL);
+            const float* sVt = reinterpret_cast<const float*>(curB + PA + B_VT) + (16 * wave + ln) * VTS;
+            const float* gcs = reinterpret_cast<const float*>(curB + R_GC);
 
             // LDS reads are issued well ahead of their use: Kg first (it starts
             // the recurrence), then Qg, the transposed Kd and the fragments while
@@ -746,8 +763,8 @@ __global__ void __launch_bounds__(NTHR) vec_chain_kernel(ChainParams p) {
 #pragma unroll
             for (int ib = 0; ib < 8; ++ib) gsc[ib] = *reinterpret_cast<const f32x4*>(gcs + srow(ib, g, 0));
             auto a16 = [&](int sl, bf16x4 (&o)[2]) {
-                o[0] = *reinterpret_cast<const bf16x4*>(cur + f16_off(sl, 0, lane));
-                o[1] = *reinterpret_cast<const bf16x4*>(cur + f16_off(sl, 1, lane));
+                o[0] = *reinterpret_cast<const bf16x4*>(curB + f16_off(sl, 0, lane));
+                o[1] = *reinterpret_cast<const bf16x4*>(curB + f16_off(sl, 1, lane));
             };
             bf16x4 ad[2][2], an[2];
             a16(F16_D0, ad[0]);
@@ -759,12 +776,16 @@ __global__ void __launch_bounds__(NTHR) vec_chain_kernel(ChainParams p) {
             bf16x8 ap[2][2];
 #pragma unroll
             for (int R = 0; R < 2; ++R) {
-                ap[R][0] = *reinterpret_cast<const bf16x8*>(cur + pf_off(R, 0, lane));
-                ap[R][1] = *reinterpret_cast<const bf16x8*>(cur + pf_off(R, 1, lane));
+                ap[R][0] = *reinterpret_cast<const bf16x8*>(curB + pf_off(R, 0, lane));
+                ap[R][1] = *reinterpret_cast<const bf16x8*>(curB + pf_off(R, 1, lane));
             }
             // keep the reads above the solve (the scheduler would otherwise sink
             // each one next to its first use and expose its latency)
             __builtin_amdgcn_sched_barrier(0);
+            // this chunk's buffer is no longer read: the DMA wave may refill it
+            // (the release store waits for the reads to return)
+            __hip_atomic_store(&rdone[wave], static_cast<int>(c - c0), __ATOMIC_RELEASE,
+                               __HIP_MEMORY_SCOPE_WORKGROUP);
 
             // X = Vt - Y;  U_0 = D_0 X_0,  U_1 = D_1 X_1 - N U_0
             const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -857,21 +878,66 @@ __global__ void __launch_bounds__(NTHR) vec_chain_kernel(ChainParams p) {
     }
 
     if (wave == NCHAIN) {
-        // wave 2: the next chunk's record, HBM -> LDS by DMA (16 bytes per lane,
-        // 1 KiB per instruction, a straight copy), issued as soon as the
-        // barrier frees its buffer
-        auto dma = [&](long c, char* buf) {
-            const char* src = recs + c * REC + 16 * lane;
+        // wave 2: the records, HBM -> LDS by DMA (16 bytes per lane, 1 KiB per
+        // instruction, a straight copy), two chunks ahead.  In chunk c it
+        // fetches chunk c + 2: part A at once (into chunk c - 1's slot), part B
+        // as soon as both chain waves have read chunk c's buffer.  At the
+        // barrier that ends chunk c only chunk c + 1 must have landed: the wait
+        // leaves chunk c + 2's REC / 1024 loads in flight (the barrier is
+        // issued without the workgroup fence, which would wait for all of them).
+        constexpr int NL = REC / 1024;
+        static_assert(NL <= 63, "one record's loads fit the load counter");
+        static_assert(NCHAIN == 2, "the flag test below reads two chain waves");
+        auto dma = [&](long c, int off, int bytes, char* dst) {
+            const char* src = recs + c * REC + off + 16 * lane;
 #pragma unroll 8
-            for (int m = 0; m < REC / 1024; ++m)
+            for (int m = 0; m < bytes / 1024; ++m)
                 __builtin_amdgcn_global_load_lds((const void*)(src + m * 1024),
-                                                 (__attribute__((address_space(3))) void*)(buf + m * 1024), 16, 0, 0);
+                                                 (__attribute__((address_space(3))) void*)(dst + m * 1024), 16, 0, 0);
         };
-        if (c0 < c1) dma(c0, smem + (c0 & 1) * BUFV);
-        __syncthreads();
-        for (long c = c0; c < c1; ++c) {
-            if (c + 1 < c1) dma(c + 1, smem + ((c + 1) & 1) * BUFV);
-            __syncthreads();
+        auto dma_a = [&](long c, int slot) { dma(c, 0, PA, smem + slot * PA); };
+        auto dma_b = [&](long c) { dma(c, PA, PB, smem + L_B + (c & 1) * BUFB); };
+        // s_waitcnt immediates (gfx9 layout: vmcnt bits 3:0 and 15:14,
+        // expcnt 6:4, lgkmcnt 11:8): vmcnt(NL) and vmcnt(0), the others free
+        constexpr int WAIT_NL = ((NL >> 4) << 14) | (NL & 15) | (7 << 4) | (15 << 8);
+        constexpr int WAIT_0 = (7 << 4) | (15 << 8);
+        auto barrier_after = [&](bool more) {
+            if (more) __builtin_amdgcn_s_waitcnt(WAIT_NL);
+            else __builtin_amdgcn_s_waitcnt(WAIT_0);
+            __builtin_amdgcn_s_barrier();
+        };
+        // A chain wave's flag, read with its own wait: a compiler-generated LDS
+        // read here would first wait for every DMA in flight (it cannot tell
+        // the flag from the DMA targets).
+        auto flag = [&](int w) {
+            int v;
+            const unsigned a = static_cast<unsigned>(
+                reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const int*)(&rdone[w])));
+            asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
+            return v;
+        };
+        const int s1 = slot0 == 2 ? 0 : slot0 + 1;
+        if (c0 < c1) {
+            dma_a(c0, slot0);
+            dma_b(c0);
+        }
+        if (c0 + 1 < c1) {
+            dma_a(c0 + 1, s1);
+            dma_b(c0 + 1);
+        }
+        barrier_after(c0 + 1 < c1);
+        int s2 = s1 == 2 ? 0 : s1 + 1;  // slot of chunk c + 2
+        for (long c = c0; c < c1; ++c, s2 = s2 == 2 ? 0 : s2 + 1) {
+            const bool more = c + 2 < c1;
+            if (more) {
+                dma_a(c + 2, s2);
+                // both chain waves are past their reads of chunk c (they set the
+                // flag before the barrier that ends chunk c, so this ends)
+                const int want = static_cast<int>(c - c0);
+                while (min(flag(0), flag(1)) < want) __builtin_amdgcn_s_sleep(1);
+                dma_b(c + 2);
+            }
+            barrier_after(more);
         }
     } else {
         // wave 3: value tile of a chunk, scaled by sqrt(gamma), gamma or 1, transposed:
@@ -895,7 +961,7 @@ __global__ void __launch_bounds__(NTHR) vec_chain_kernel(ChainParams p) {
             }
         };
         auto stage = [&](long c, char* buf) {
-            float* sVt = reinterpret_cast<float*>(buf + B_VT);
+            float* sVt = reinterpret_cast<float*>(buf + B_VT);  // a part-B buffer
             bool okt[2];
 #pragma unroll
             for (int i = 0; i < 2; ++i) okt[i] = c * VC + 2 * ln + i < p.T;
@@ -913,13 +979,13 @@ __global__ void __launch_bounds__(NTHR) vec_chain_kernel(ChainParams p) {
         };
         if (c0 < c1) {
             load(c0);
-            stage(c0, smem + (c0 & 1) * BUFV);
+            stage(c0, smem + L_B + (c0 & 1) * BUFB);
             if (c0 + 1 < c1) load(c0 + 1);
         }
         __syncthreads();
         for (long c = c0; c < c1; ++c) {
             if (c + 1 < c1) {
-                stage(c + 1, smem + ((c + 1) & 1) * BUFV);
+                stage(c + 1, smem + L_B + ((c + 1) & 1) * BUFB);
                 if (c + 2 < c1) load(c + 2);
             }
             __syncthreads();
