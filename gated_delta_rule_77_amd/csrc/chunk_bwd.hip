@@ -311,7 +311,7 @@ __global__ void __launch_bounds__(NT, 3) bwd_prep_kernel(BwdParams p) {
     }
     sPart[h][0][i] = gs;
     sPart[h][1][i] = as;
-    __syncthreads();
+    lds_barrier();
     float Gin = 0.f, Ain = p.pre ? p.apre[(bh * p.nc + c) * DK + i] : 0.f;
     for (int h2 = 0; h2 < h; ++h2) {
         Gin += sPart[h2][0][i];
@@ -337,7 +337,7 @@ __global__ void __launch_bounds__(NT, 3) bwd_prep_kernel(BwdParams p) {
             A += kk[u] * kk[u];
             sKrL[r0 + u][i] = logf(A + p.eps);
         }
-        __syncthreads();
+        lds_barrier();
         if (tid < BC) {
             float m = 0.f;
             for (int ii = 0; ii < DK; ++ii) m += sKrL[tid][ii];
@@ -346,7 +346,7 @@ __global__ void __launch_bounds__(NT, 3) bwd_prep_kernel(BwdParams p) {
             p.mu[bh * static_cast<long>(p.nc) * BC + t0 + tid] = m;
         }
     }
-    __syncthreads();
+    lds_barrier();
     {
         const float g8 = sRef[0][i], g24 = sRef[1][i], gc = sRef[2][i];
         const float cst = __expf(g24 - g8);
@@ -383,28 +383,36 @@ __global__ void __launch_bounds__(NT, 3) bwd_prep_kernel(BwdParams p) {
     }
     float* Rvw = R + rec_vw<DK>(p.dv);
     {
-        // at most BC * 256 / NT = 32 values per thread, loads issued together
+        // at most BC * 256 / NT = 32 values per thread.  Every load is issued
+        // before any value is used: indices past the tile reread element 0,
+        // rows past T are clamped, and the masks come afterwards (loads behind
+        // a branch made the compiler wait for each one in turn: 32 round
+        // trips instead of one).
         constexpr int MAXV = BC * 256 / NT;
-        float vv[MAXV], sc[MAXV];
+        const int nv = BC * p.dv;
+        const bool same = p.gmode == PDN_GAMMA_SAME_AS_BETA;
+        const bool gvec = same ? p.bmode == PDN_GATE_VEC : p.gmode == PDN_GATE_VEC;
+        const float* gbase = same ? p.beta : p.gamma;
+        const int gw = same ? DK : p.dv;
+        float vv[MAXV], gg[MAXV];
 #pragma unroll
         for (int m = 0; m < MAXV; ++m) {
-            const int idx = tid + m * NT;
-            vv[m] = 0.f;
-            sc[m] = 0.f;
-            if (idx < BC * p.dv) {
-                const int r = idx / p.dv, j = idx % p.dv;
-                const long t = t0 + r;
-                vv[m] = tok_in<BF16>(p, p.v, bh, t, p.dv, j);
-                sc[m] = value_scale(p.kmode, p.gmode, tok_gamma<DK>(p, bh, t, j));
-            }
+            const int idx = tid + m * NT < nv ? tid + m * NT : 0;
+            const int r = idx / p.dv, j = idx % p.dv;
+            const long tc = bh * p.T + tclamp(p, t0 + r);
+            vv[m] = load_in<BF16>(p.v, tc * p.dv + j);
+            gg[m] = gbase[gvec ? tc * gw + j : tc];
         }
 #pragma unroll
         for (int m = 0; m < MAXV; ++m) {
             const int idx = tid + m * NT;
-            if (idx < BC * p.dv) Rvw[idx] = vv[m] * sc[m];
+            const bool live = t0 + idx / p.dv < p.T;
+            const float v = live ? vv[m] : 0.f;
+            const float sc = value_scale(p.kmode, p.gmode, live ? gg[m] : 1.f);
+            if (idx < nv) Rvw[idx] = v * sc;
         }
     }
-    __syncthreads();
+    lds_barrier();
     // six 16 x 16 tiles: T (0,0), (1,1), (1,0) and P likewise; wave w takes
     // tile w and, for w < 2, tile w + 4
     float* Rp = R + rec_p<DK>(p.dv);
@@ -436,7 +444,7 @@ __global__ void __launch_bounds__(NT, 3) bwd_prep_kernel(BwdParams p) {
         }
     }
     for (int idx = tid; idx < 16 * 16; idx += NT) Rp[(idx / 16) * BC + 16 + idx % 16] = 0.f;
-    __syncthreads();  // every wave is done with the operands: sKrL takes T
+    lds_barrier();  // every wave is done with the operands: sKrL takes T
     if (w < 3) {
         const int rb = w == 0 ? 0 : 1, sb = w == 1 ? 1 : 0;
 #pragma unroll
@@ -447,7 +455,7 @@ __global__ void __launch_bounds__(NT, 3) bwd_prep_kernel(BwdParams p) {
     }
     // the upper-right block is zero
     for (int idx = tid; idx < 16 * 16; idx += NT) sT[idx / 16][16 + idx % 16] = 0.f;
-    __syncthreads();
+    lds_barrier();
     // M = (I + T)^-1, one column per thread: x_r = [r == j] - sum_{s<r} T_rs x_s
     float* Rm = R + rec_m<DK>(p.dv);
     if (tid < BC) {
@@ -556,6 +564,25 @@ struct StateTiles {
     static __device__ __forceinline__ int scb(int q) { return q % CB; }   // and column block
 };
 
+// This wave's blocks of a DK x SJ state tile (a null source gives zeros): one
+// branch around all the loads, so that they are issued together (a per-element
+// test would make the compiler wait for each load in turn).
+template <int NSB, class ST>
+__device__ __forceinline__ void load_state_tile(const float* src, long off, int dv, int w, f32x4 (&acc)[NSB]) {
+    const int lane = threadIdx.x & 63, ln = lane & 15, g4 = lane >> 4;
+    if (src) {
+#pragma unroll
+        for (int m = 0; m < NSB; ++m) {
+            const int q = w * NSB + m, ib = ST::sib(q), cb = ST::scb(q);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[m][e] = src[off + (16 * ib + 4 * g4 + e) * dv + 16 * cb + ln];
+        }
+    } else {
+#pragma unroll
+        for (int m = 0; m < NSB; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+}
+
 // forward state pass of workgroup `unit` (b, h, SJ value columns)
 template <int DK, int SJ>
 __device__ __forceinline__ void state_fwd_body(const BwdParams& p, float* smem, long unit) {
@@ -579,16 +606,15 @@ __device__ __forceinline__ void state_fwd_body(const BwdParams& p, float* smem, 
     const long SZ = static_cast<long>(DK) * p.dv;
     const long RF = rec_floats<DK>(p.dv);
     f32x4 sacc[NSB];
+    load_state_tile<NSB, ST>(p.S0, bh * SZ + j0, p.dv, w, sacc);  // every load before any use
 #pragma unroll
     for (int m = 0; m < NSB; ++m) {
         const int q = w * NSB + m, ib = ST::sib(q), cb = ST::scb(q);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int row = 16 * ib + 4 * g4 + e, col = 16 * cb + ln;
-            const float v = p.S0 ? p.S0[bh * SZ + row * p.dv + j0 + col] : 0.f;
-            sacc[m][e] = v;
-            sS[row][col] = v;
-            p.st[bh * (p.nc + 1) * SZ + row * p.dv + j0 + col] = v;
+            sS[row][col] = sacc[m][e];
+            p.st[bh * (p.nc + 1) * SZ + row * p.dv + j0 + col] = sacc[m][e];
         }
     }
     // X / Y tile of this wave (SJ = 16: waves 2 and 3 compute the tiles of
@@ -613,7 +639,7 @@ __device__ __forceinline__ void state_fwd_body(const BwdParams& p, float* smem, 
     };
     fetch(0);
     for (long c = 0; c < p.nc; ++c) {
-        __syncthreads();  // the previous chunk's LDS reads are done
+        lds_barrier();  // the previous chunk's LDS reads are done
         nKg.template store<DK + 4>(&sKg[0][0]);
         nKd.template store<DK + 16>(&sKd[0][0]);
         nM.template store<BC + 4>(&sM[0][0]);
@@ -621,7 +647,7 @@ __device__ __forceinline__ void state_fwd_body(const BwdParams& p, float* smem, 
         f32x4 x;
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[e] = nVw[e];
-        __syncthreads();
+        lds_barrier();
         // the next chunk's loads (the last chunk rereads itself, so that no
         // branch splits them from the MFMAs below)
         fetch(c + 1 < p.nc ? c + 1 : c);
@@ -632,7 +658,7 @@ __device__ __forceinline__ void state_fwd_body(const BwdParams& p, float* smem, 
         if (xown)
 #pragma unroll
             for (int e = 0; e < 4; ++e) sX[16 * rb + 4 * g4 + e][16 * xcb + ln] = x[e];
-        __syncthreads();
+        lds_barrier();
         // U = M X
         f32x4 u = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -644,7 +670,7 @@ __device__ __forceinline__ void state_fwd_body(const BwdParams& p, float* smem, 
                 sU[r][16 * xcb + ln] = u[e];
                 p.U[(bh * Tp + c * BC + r) * p.dv + j0 + 16 * xcb + ln] = u[e];
             }
-        __syncthreads();
+        lds_barrier();
         // S <- Diag(e^G_C) S + Kd^T U
 #pragma unroll
         for (int m = 0; m < NSB; ++m) {
@@ -695,16 +721,12 @@ __device__ __forceinline__ void state_bwd_body(const BwdParams& p, float* smem, 
     const long SZ = static_cast<long>(DK) * p.dv;
     const long RF = rec_floats<DK>(p.dv);
     f32x4 dacc[NSB];
+    load_state_tile<NSB, ST>(p.dST, bh * SZ + j0, p.dv, w, dacc);
 #pragma unroll
     for (int m = 0; m < NSB; ++m) {
         const int q = w * NSB + m, ib = ST::sib(q), cb = ST::scb(q);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int row = 16 * ib + 4 * g4 + e, col = 16 * cb + ln;
-            const float v = p.dST ? p.dST[bh * SZ + row * p.dv + j0 + col] : 0.f;
-            dacc[m][e] = v;
-            sdS[row][col] = v;
-        }
+        for (int e = 0; e < 4; ++e) sdS[16 * ib + 4 * g4 + e][16 * cb + ln] = dacc[m][e];
     }
     // X / Y tile of this wave (SJ = 16: waves 2 and 3 compute the tiles of
     // waves 0 and 1 again, which keeps their loads and MFMAs on the same path,
@@ -745,7 +767,7 @@ __device__ __forceinline__ void state_bwd_body(const BwdParams& p, float* smem, 
             for (int e = 0; e < 4; ++e)
                 p.dst[(bh * p.nc + c) * SZ + (16 * ib + 4 * g4 + e) * p.dv + j0 + 16 * cb + ln] = dacc[m][e];
         }
-        __syncthreads();
+        lds_barrier();
         nKg.template store<DK + 4>(&sKg[0][0]);
         nQg.template store<DK + 4>(&sQg[0][0]);
         nKd.template store<DK + 4>(&sKd[0][0]);
@@ -758,7 +780,7 @@ __device__ __forceinline__ void state_bwd_body(const BwdParams& p, float* smem, 
             aPt[k] = nPt[k];
             aMt[k] = nMt[k];
         }
-        __syncthreads();
+        lds_barrier();
         fetch(c > 0 ? c - 1 : 0);  // unconditional, as in the forward pass
         // Y = P^T dO + Kd dS'
         f32x4 y = {0.f, 0.f, 0.f, 0.f};
@@ -770,12 +792,12 @@ __device__ __forceinline__ void state_bwd_body(const BwdParams& p, float* smem, 
         if (xown)
 #pragma unroll
             for (int e = 0; e < 4; ++e) sY[16 * rb + 4 * g4 + e][16 * xcb + ln] = y[e];
-        __syncthreads();
+        lds_barrier();
         // Z = M^T Y, into Y's buffer once every wave has read Y
         f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int k = 0; k < BC / 4; ++k) z = mfma4(aMt[k], sY[4 * k + g4][16 * xcb + ln], z);
-        __syncthreads();
+        lds_barrier();
         if (xown)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -783,7 +805,7 @@ __device__ __forceinline__ void state_bwd_body(const BwdParams& p, float* smem, 
                 sY[r][16 * xcb + ln] = z[e];
                 p.Z[(bh * Tp + c * BC + r) * p.dv + j0 + 16 * xcb + ln] = z[e];
             }
-        __syncthreads();
+        lds_barrier();
         // dS <- Diag(e^G_C) dS' + Qg^T dO - Kg^T Z
 #pragma unroll
         for (int m = 0; m < NSB; ++m) {
@@ -891,13 +913,13 @@ __device__ __forceinline__ void dgrad_body(const BwdParams& p, float* smem, long
     const bool dO_row = c * BC + dr < p.T;
     fetch(0);
     for (int jc = 0; jc < p.dv; jc += JT) {
-        __syncthreads();
+        lds_barrier();
         nS.template store<JT + 4>(&sS[0][0]);
         nE.template store<JT + 4>(&sE[0][0]);
         nZ.template store<JT + 4>(&sZ[0][0]);
         nU.template store<JT + 4>(&sU[0][0]);
         *reinterpret_cast<f32x4*>(&sdO[dr][4 * dc4]) = dO_row ? ndO : f32x4{0.f, 0.f, 0.f, 0.f};
-        __syncthreads();
+        lds_barrier();
         if (jc + JT < p.dv) fetch(jc + JT);
         if (tid < DK)
 #pragma unroll 8
@@ -1096,7 +1118,7 @@ __device__ __forceinline__ void gates_body(const BwdParams& p, float* smem, long
         }
         sX[h][0][i] = gs;
         sX[h][1][i] = as;
-        __syncthreads();
+        lds_barrier();
         for (int h2 = 0; h2 < h; ++h2) {
             Gin += sX[h2][0][i];
             Ain += sX[h2][1][i];
@@ -1116,7 +1138,7 @@ __device__ __forceinline__ void gates_body(const BwdParams& p, float* smem, long
             if (r == 24) sRef[1][i] = G[u];
             if (r == BC - 1) sRef[2][i] = G[u];
         }
-        __syncthreads();
+        lds_barrier();
     }
     const float G8 = sRef[0][i], G24 = sRef[1][i], Gc = sRef[2][i];
     // erase gain with the preconditioner folded in, advancing the running sum;
@@ -1153,7 +1175,7 @@ __device__ __forceinline__ void gates_body(const BwdParams& p, float* smem, long
             sRq[r][i] = qv[u] * L;
         }
     }
-    __syncthreads();
+    lds_barrier();
     // MFMA: wave w, column tiles CTW w .. CTW w + CTW - 1
     f32x4 a1[CTW][2], a3[CTW][2], a2[CTW][2], a4[CTW][2];
 #pragma unroll
@@ -1201,7 +1223,7 @@ __device__ __forceinline__ void gates_body(const BwdParams& p, float* smem, long
             a4[m][0][e] = x4[0][e] + cst * x4[2][e];
         }
     }
-    __syncthreads();  // every wave has read the operands: the buffer takes A1..A4
+    lds_barrier();  // every wave has read the operands: the buffer takes A1..A4
 #pragma unroll
     for (int m = 0; m < CTW; ++m) {
         const int col = 16 * (CTW * w + m) + ln;
@@ -1216,7 +1238,7 @@ __device__ __forceinline__ void gates_body(const BwdParams& p, float* smem, long
                 sA4[r][col] = a4[m][b][e];
             }
     }
-    __syncthreads();
+    lds_barrier();
     const float* DdQg = D + i;
     const float* DdKg = D + BC * DK + i;
     const float* DdKd = D + 2 * BC * DK + i;
@@ -1260,7 +1282,7 @@ __device__ __forceinline__ void gates_body(const BwdParams& p, float* smem, long
         }
     }
     sX[h][2][i] = kdsum;
-    __syncthreads();
+    lds_barrier();
     if (h == NH - 1) {
         float tot = 0.f;
 #pragma unroll
@@ -1277,7 +1299,7 @@ __device__ __forceinline__ void gates_body(const BwdParams& p, float* smem, long
         for (int u = 0; u < RPT; ++u) tot += sA2[r0 + u][i];
         sX[h][3][i] = tot;
     }
-    __syncthreads();
+    lds_barrier();
     {
         // d log alpha: reverse cumulative sum of dG over the chunk
         float run = 0.f;
@@ -1341,7 +1363,7 @@ __device__ __forceinline__ void gates_body(const BwdParams& p, float* smem, long
         }
         if (p.pre) sX[h][0][i] = dAsum;
     }
-    __syncthreads();
+    lds_barrier();
     if (p.pre && p.stab) {
         // dl = dr - mean over channels of dr; dA = dl / (A + eps)
         if (tid < BC) {
@@ -1349,7 +1371,7 @@ __device__ __forceinline__ void gates_body(const BwdParams& p, float* smem, long
             for (int ii = 0; ii < DK; ++ii) m += sA2[tid][ii];
             sDrm[tid] = m * (1.f / DK);
         }
-        __syncthreads();
+        lds_barrier();
         float A = Ain, dAsum = 0.f;
 #pragma unroll
         for (int u = 0; u < RPT; ++u) {
@@ -1360,7 +1382,7 @@ __device__ __forceinline__ void gates_body(const BwdParams& p, float* smem, long
             dAsum += dA;
         }
         sX[h][0][i] = dAsum;
-        __syncthreads();
+        lds_barrier();
     }
     if (p.pre) {
         float suf = 0.f;
