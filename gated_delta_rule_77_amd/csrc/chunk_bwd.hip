@@ -221,12 +221,16 @@ __global__ void __launch_bounds__(DK) bwd_ksum_kernel(BwdParams p) {
     const long bh = blockIdx.x / p.nc;
     const long c = blockIdx.x % p.nc;
     const int i = threadIdx.x;
+    // every row loaded (clamped) before any is used, rows past T masked after
     float kk[BC];
 #pragma unroll
-    for (int r = 0; r < BC; ++r) kk[r] = tok_in<BF16>(p, p.k, bh, c * BC + r, DK, i);
+    for (int r = 0; r < BC; ++r) kk[r] = load_in<BF16>(p.k, (bh * p.T + tclamp(p, c * BC + r)) * DK + i);
     float s = 0.f;
 #pragma unroll
-    for (int r = 0; r < BC; ++r) s += kk[r] * kk[r];
+    for (int r = 0; r < BC; ++r) {
+        const float x = c * BC + r < p.T ? kk[r] : 0.f;
+        s += x * x;
+    }
     p.ksum[(bh * p.nc + c) * DK + i] = s;
 }
 
@@ -1309,10 +1313,14 @@ __device__ __forceinline__ void gates_body(const BwdParams& p, float* smem, long
             const int r = r0 + u;
             run += sA2[r][i];
             const long t = t0 + r;
-            const float dla = ((dead >> u) & 1u) ? 0.f : run;
-            if (p.amode == PDN_ALPHA_VEC && t < p.T) p.dla[(bh * p.T + t) * DK + i] = dla;
-            sA4[r][i] = dla;
+            sA4[r][i] = ((dead >> u) & 1u) ? 0.f : run;
         }
+        // stored after the loop: a store between the steps above would make
+        // each step's register reload wait for it (one counter serves both)
+        if (p.amode == PDN_ALPHA_VEC)
+#pragma unroll
+            for (int u = 0; u < RPT; ++u)
+                if (t0 + r0 + u < p.T) p.dla[(bh * p.T + t0 + r0 + u) * DK + i] = sA4[r0 + u][i];
         // keys to k and the gains; the preconditioner's dA (the stabilised mode
         // first leaves dr in A2 for its channel mean)
         float A = Ain, aux, den;

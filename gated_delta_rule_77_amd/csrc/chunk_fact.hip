@@ -766,12 +766,20 @@ __global__ void __launch_bounds__(NTHR) chunk_fact_kernel(FactParams p) {
 #pragma unroll
             for (int cc = 0; cc < 8; ++cc) sg4[cc] = s4;
         } else {
+            // all 32 gains loaded (rows past T reread the last row) before the
+            // mask: a load behind the row test would wait for each in turn
+            float gr[4][8];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const long tok = t0 + 4 * ln + i;
-                const float* gr = p.gsrc + (bh * p.T + min(tok, p.T - 1)) * p.gts + jv + 8 * g;
+                const float* src = p.gsrc + (bh * p.T + min(t0 + 4 * ln + i, p.T - 1)) * p.gts + jv + 8 * g;
 #pragma unroll
-                for (int cc = 0; cc < 8; ++cc) sg4[cc][i] = tok < p.T ? sqrt_hw(gr[cc]) : 0.0f;
+                for (int cc = 0; cc < 8; ++cc) gr[i][cc] = src[cc];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float m = t0 + 4 * ln + i < p.T ? 1.0f : 0.0f;
+#pragma unroll
+                for (int cc = 0; cc < 8; ++cc) sg4[cc][i] = sqrt_hw(gr[i][cc]) * m;
             }
         }
 #pragma unroll

@@ -231,16 +231,20 @@ __global__ void __launch_bounds__(KSQ_NTHR) vec_ksq_kernel(const uint16_t* k, fl
     const long t0 = (id % nc) * VC;
     const int ln = lane & 15, g = lane >> 4;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    // every row is loaded (rows past T reread the last one) before any is
+    // used, and rows past T are masked afterwards: a load behind the test
+    // would make the compiler wait for each row in turn
+    uint4 u[VC / 4];
+#pragma unroll
+    for (int s4 = 0; s4 < VC / 4; ++s4)
+        u[s4] = *reinterpret_cast<const uint4*>(k + (bh * T + min(t0 + 4 * s4 + g, T - 1)) * DK + 8 * ln);
 #pragma unroll
     for (int s4 = 0; s4 < VC / 4; ++s4) {
-        const long t = t0 + 4 * s4 + g;
-        if (t < T) {
-            const uint4 u = *reinterpret_cast<const uint4*>(k + (bh * T + t) * DK + 8 * ln);
+        const float m = t0 + 4 * s4 + g < T ? 1.0f : 0.0f;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float x = bf16_at(u, j);
-                acc[j] = fmaf(x, x, acc[j]);
-            }
+        for (int j = 0; j < 8; ++j) {
+            const float x = bf16_at(u[s4], j) * m;
+            acc[j] = fmaf(x, x, acc[j]);
         }
     }
 #pragma unroll
@@ -1107,14 +1111,31 @@ __device__ __forceinline__ void two_seg_final_state(const float* nst, const floa
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[rb][cb][e] = N1[(32 * wave + 16 * rb + 4 * g4 + e) * dv + j0 + 16 * cb + ln];
     for (int kh = 0; kh < DK; kh += KH) {
-        __syncthreads();  // the previous half has been read
-        for (int i = tid; i < DK * KH / 4; i += SEG_NTHR) {
-            const int r = i / (KH / 4), c4 = i % (KH / 4);
-            *reinterpret_cast<f32x4*>(&sPhi[r][4 * c4]) = *reinterpret_cast<const f32x4*>(P + r * DK + kh + 4 * c4);
+        // every load of the half before its LDS stores (a store after each
+        // load would wait for it)
+        constexpr int NP = DK * KH / 4 / SEG_NTHR, NS = KH * CT / 4 / SEG_NTHR;
+        static_assert(NP * SEG_NTHR == DK * KH / 4 && NS * SEG_NTHR == KH * CT / 4, "whole passes");
+        f32x4 pv[NP], sv[NS];
+#pragma unroll
+        for (int u = 0; u < NP; ++u) {
+            const int i = tid + u * SEG_NTHR, r = i / (KH / 4), c4 = i % (KH / 4);
+            pv[u] = *reinterpret_cast<const f32x4*>(P + r * DK + kh + 4 * c4);
         }
-        for (int i = tid; i < KH * CT / 4; i += SEG_NTHR) {
-            const int r = i / (CT / 4), c4 = i % (CT / 4);
-            *reinterpret_cast<f32x4*>(&sS[r][4 * c4]) = *reinterpret_cast<const f32x4*>(N0 + (kh + r) * dv + j0 + 4 * c4);
+#pragma unroll
+        for (int u = 0; u < NS; ++u) {
+            const int i = tid + u * SEG_NTHR, r = i / (CT / 4), c4 = i % (CT / 4);
+            sv[u] = *reinterpret_cast<const f32x4*>(N0 + (kh + r) * dv + j0 + 4 * c4);
+        }
+        __syncthreads();  // the previous half has been read
+#pragma unroll
+        for (int u = 0; u < NP; ++u) {
+            const int i = tid + u * SEG_NTHR, r = i / (KH / 4), c4 = i % (KH / 4);
+            *reinterpret_cast<f32x4*>(&sPhi[r][4 * c4]) = pv[u];
+        }
+#pragma unroll
+        for (int u = 0; u < NS; ++u) {
+            const int i = tid + u * SEG_NTHR, r = i / (CT / 4), c4 = i % (CT / 4);
+            *reinterpret_cast<f32x4*>(&sS[r][4 * c4]) = sv[u];
         }
         __syncthreads();
 #pragma unroll 4
@@ -1166,16 +1187,27 @@ __global__ void __launch_bounds__(SEG_NTHR, 2) vec_seg_correct_kernel(const floa
     const float* S = direct ? nst + (bh * nseg) * DK * dv : sst + (bh * nseg + gs) * DK * dv;
     for (int jb = 0; jb < dv; jb += COR_CB) {
         const int nj = min(COR_CB, dv - jb);  // a multiple of 32
-        __syncthreads();  // the previous pass is done with the staged tile
         // stage S_g^T (columns jb .. jb + nj) as hi/lo bf16: item (column c,
-        // channels 8m .. 8m + 7), consecutive threads on consecutive columns
-        for (int it = tid; it < COR_CB * (DK / 8); it += SEG_NTHR) {
-            const int c = it % COR_CB, m = it / COR_CB;
-            float x[8];
+        // channels 8m .. 8m + 7), consecutive threads on consecutive columns;
+        // every load first (columns past nj reread column jb and are zeroed)
+        constexpr int NIT = COR_CB * (DK / 8) / SEG_NTHR;
+        static_assert(NIT * SEG_NTHR == COR_CB * (DK / 8), "whole passes");
+        float x[NIT][8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = c < nj ? S[(8 * m + e) * dv + jb + c] : 0.f;
+        for (int u = 0; u < NIT; ++u) {
+            const int it = tid + u * SEG_NTHR, c = it % COR_CB, m = it / COR_CB;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[u][e] = S[(8 * m + e) * dv + jb + (c < nj ? c : 0)];
+        }
+        __syncthreads();  // the previous pass is done with the staged tile
+#pragma unroll
+        for (int u = 0; u < NIT; ++u) {
+            const int it = tid + u * SEG_NTHR, c = it % COR_CB, m = it / COR_CB;
+            const float keep = c < nj ? 1.0f : 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[u][e] *= keep;
             uint4 h, l;
-            split8(x, h, l);
+            split8(x[u], h, l);
             *reinterpret_cast<uint4*>(sH + cor_off(c, 8 * m)) = h;
             *reinterpret_cast<uint4*>(sL + cor_off(c, 8 * m)) = l;
         }
@@ -1195,7 +1227,18 @@ __global__ void __launch_bounds__(SEG_NTHR, 2) vec_seg_correct_kernel(const floa
                 bh_[t] = hl[0];
                 bl_[t] = hl[1];
             }
-            for (int cb = 0; cb < nj / 16; ++cb) {
+            // this lane's outputs, all read before the products (a read behind
+            // the token test would be waited for one at a time); past t1 the
+            // last token is read again and not written
+            float* orow = o + (bh * T + (tv ? tok : t1 - 1)) * dv + jb + 4 * g;
+            const int ncb = nj / 16;
+            f32x4 ov[COR_CB / 16];
+#pragma unroll
+            for (int cb = 0; cb < COR_CB / 16; ++cb)
+                ov[cb] = *reinterpret_cast<const f32x4*>(orow + 16 * min(cb, ncb - 1));
+#pragma unroll
+            for (int cb = 0; cb < COR_CB / 16; ++cb) {
+                if (cb >= ncb) break;
                 f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
@@ -1206,10 +1249,7 @@ __global__ void __launch_bounds__(SEG_NTHR, 2) vec_seg_correct_kernel(const floa
                     acc = mfma32(ah, bh_[t], acc);
                 }
                 // acc: token ln, state columns 16 cb + 4 g .. + 3
-                if (tv) {
-                    f32x4* op = reinterpret_cast<f32x4*>(o + (bh * T + tok) * dv + jb + 16 * cb + 4 * g);
-                    *op = *op + acc;
-                }
+                if (tv) *reinterpret_cast<f32x4*>(orow + 16 * cb) = ov[cb] + acc;
             }
         }
     }
