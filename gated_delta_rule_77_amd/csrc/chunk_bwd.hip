@@ -315,7 +315,7 @@ __global__ void __launch_bounds__(NT, 3) bwd_prep_kernel(BwdParams p) {
     }
     sPart[h][0][i] = gs;
     sPart[h][1][i] = as;
-    lds_barrier();
+    __syncthreads();
     float Gin = 0.f, Ain = p.pre ? p.apre[(bh * p.nc + c) * DK + i] : 0.f;
     for (int h2 = 0; h2 < h; ++h2) {
         Gin += sPart[h2][0][i];
@@ -341,7 +341,7 @@ __global__ void __launch_bounds__(NT, 3) bwd_prep_kernel(BwdParams p) {
             A += kk[u] * kk[u];
             sKrL[r0 + u][i] = logf(A + p.eps);
         }
-        lds_barrier();
+        __syncthreads();
         if (tid < BC) {
             float m = 0.f;
             for (int ii = 0; ii < DK; ++ii) m += sKrL[tid][ii];
@@ -350,7 +350,7 @@ __global__ void __launch_bounds__(NT, 3) bwd_prep_kernel(BwdParams p) {
             p.mu[bh * static_cast<long>(p.nc) * BC + t0 + tid] = m;
         }
     }
-    lds_barrier();
+    __syncthreads();
     {
         const float g8 = sRef[0][i], g24 = sRef[1][i], gc = sRef[2][i];
         const float cst = __expf(g24 - g8);
@@ -416,7 +416,7 @@ __global__ void __launch_bounds__(NT, 3) bwd_prep_kernel(BwdParams p) {
             if (idx < nv) Rvw[idx] = v * sc;
         }
     }
-    lds_barrier();
+    __syncthreads();
     // six 16 x 16 tiles: T (0,0), (1,1), (1,0) and P likewise; wave w takes
     // tile w and, for w < 2, tile w + 4
     float* Rp = R + rec_p<DK>(p.dv);
@@ -448,7 +448,7 @@ __global__ void __launch_bounds__(NT, 3) bwd_prep_kernel(BwdParams p) {
         }
     }
     for (int idx = tid; idx < 16 * 16; idx += NT) Rp[(idx / 16) * BC + 16 + idx % 16] = 0.f;
-    lds_barrier();  // every wave is done with the operands: sKrL takes T
+    __syncthreads();  // every wave is done with the operands: sKrL takes T
     if (w < 3) {
         const int rb = w == 0 ? 0 : 1, sb = w == 1 ? 1 : 0;
 #pragma unroll
@@ -459,7 +459,7 @@ __global__ void __launch_bounds__(NT, 3) bwd_prep_kernel(BwdParams p) {
     }
     // the upper-right block is zero
     for (int idx = tid; idx < 16 * 16; idx += NT) sT[idx / 16][16 + idx % 16] = 0.f;
-    lds_barrier();
+    __syncthreads();
     // M = (I + T)^-1, one column per thread: x_r = [r == j] - sum_{s<r} T_rs x_s
     float* Rm = R + rec_m<DK>(p.dv);
     if (tid < BC) {
@@ -643,7 +643,7 @@ __device__ __forceinline__ void state_fwd_body(const BwdParams& p, float* smem, 
     };
     fetch(0);
     for (long c = 0; c < p.nc; ++c) {
-        lds_barrier();  // the previous chunk's LDS reads are done
+        __syncthreads();  // the previous chunk's LDS reads are done
         nKg.template store<DK + 4>(&sKg[0][0]);
         nKd.template store<DK + 16>(&sKd[0][0]);
         nM.template store<BC + 4>(&sM[0][0]);
@@ -651,7 +651,7 @@ __device__ __forceinline__ void state_fwd_body(const BwdParams& p, float* smem, 
         f32x4 x;
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[e] = nVw[e];
-        lds_barrier();
+        __syncthreads();
         // the next chunk's loads (the last chunk rereads itself, so that no
         // branch splits them from the MFMAs below)
         fetch(c + 1 < p.nc ? c + 1 : c);
@@ -662,7 +662,7 @@ __device__ __forceinline__ void state_fwd_body(const BwdParams& p, float* smem, 
         if (xown)
 #pragma unroll
             for (int e = 0; e < 4; ++e) sX[16 * rb + 4 * g4 + e][16 * xcb + ln] = x[e];
-        lds_barrier();
+        __syncthreads();
         // U = M X
         f32x4 u = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -674,7 +674,7 @@ __device__ __forceinline__ void state_fwd_body(const BwdParams& p, float* smem, 
                 sU[r][16 * xcb + ln] = u[e];
                 p.U[(bh * Tp + c * BC + r) * p.dv + j0 + 16 * xcb + ln] = u[e];
             }
-        lds_barrier();
+        __syncthreads();
         // S <- Diag(e^G_C) S + Kd^T U
 #pragma unroll
         for (int m = 0; m < NSB; ++m) {
@@ -771,7 +771,7 @@ __device__ __forceinline__ void state_bwd_body(const BwdParams& p, float* smem, 
             for (int e = 0; e < 4; ++e)
                 p.dst[(bh * p.nc + c) * SZ + (16 * ib + 4 * g4 + e) * p.dv + j0 + 16 * cb + ln] = dacc[m][e];
         }
-        lds_barrier();
+        __syncthreads();
         nKg.template store<DK + 4>(&sKg[0][0]);
         nQg.template store<DK + 4>(&sQg[0][0]);
         nKd.template store<DK + 4>(&sKd[0][0]);
@@ -784,7 +784,7 @@ __device__ __forceinline__ void state_bwd_body(const BwdParams& p, float* smem, 
             aPt[k] = nPt[k];
             aMt[k] = nMt[k];
         }
-        lds_barrier();
+        __syncthreads();
         fetch(c > 0 ? c - 1 : 0);  // unconditional, as in the forward pass
         // Y = P^T dO + Kd dS'
         f32x4 y = {0.f, 0.f, 0.f, 0.f};
@@ -796,12 +796,12 @@ __device__ __forceinline__ void state_bwd_body(const BwdParams& p, float* smem, 
         if (xown)
 #pragma unroll
             for (int e = 0; e < 4; ++e) sY[16 * rb + 4 * g4 + e][16 * xcb + ln] = y[e];
-        lds_barrier();
+        __syncthreads();
         // Z = M^T Y, into Y's buffer once every wave has read Y
         f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int k = 0; k < BC / 4; ++k) z = mfma4(aMt[k], sY[4 * k + g4][16 * xcb + ln], z);
-        lds_barrier();
+        __syncthreads();
         if (xown)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -809,7 +809,7 @@ __device__ __forceinline__ void state_bwd_body(const BwdParams& p, float* smem, 
                 sY[r][16 * xcb + ln] = z[e];
                 p.Z[(bh * Tp + c * BC + r) * p.dv + j0 + 16 * xcb + ln] = z[e];
             }
-        lds_barrier();
+        __syncthreads();
         // dS <- Diag(e^G_C) dS' + Qg^T dO - Kg^T Z
 #pragma unroll
         for (int m = 0; m < NSB; ++m) {
@@ -917,13 +917,13 @@ __device__ __forceinline__ void dgrad_body(const BwdParams& p, float* smem, long
     const bool dO_row = c * BC + dr < p.T;
     fetch(0);
     for (int jc = 0; jc < p.dv; jc += JT) {
-        lds_barrier();
+        __syncthreads();
         nS.template store<JT + 4>(&sS[0][0]);
         nE.template store<JT + 4>(&sE[0][0]);
         nZ.template store<JT + 4>(&sZ[0][0]);
         nU.template store<JT + 4>(&sU[0][0]);
         *reinterpret_cast<f32x4*>(&sdO[dr][4 * dc4]) = dO_row ? ndO : f32x4{0.f, 0.f, 0.f, 0.f};
-        lds_barrier();
+        __syncthreads();
         if (jc + JT < p.dv) fetch(jc + JT);
         if (tid < DK)
 #pragma unroll 8
@@ -1122,7 +1122,7 @@ __device__ __forceinline__ void gates_body(const BwdParams& p, float* smem, long
         }
         sX[h][0][i] = gs;
         sX[h][1][i] = as;
-        lds_barrier();
+        __syncthreads();
         for (int h2 = 0; h2 < h; ++h2) {
             Gin += sX[h2][0][i];
             Ain += sX[h2][1][i];
@@ -1142,7 +1142,7 @@ __device__ __forceinline__ void gates_body(const BwdParams& p, float* smem, long
             if (r == 24) sRef[1][i] = G[u];
             if (r == BC - 1) sRef[2][i] = G[u];
         }
-        lds_barrier();
+        __syncthreads();
     }
     const float G8 = sRef[0][i], G24 = sRef[1][i], Gc = sRef[2][i];
     // erase gain with the preconditioner folded in, advancing the running sum;
@@ -1179,7 +1179,7 @@ __device__ __forceinline__ void gates_body(const BwdParams& p, float* smem, long
             sRq[r][i] = qv[u] * L;
         }
     }
-    lds_barrier();
+    __syncthreads();
     // MFMA: wave w, column tiles CTW w .. CTW w + CTW - 1
     f32x4 a1[CTW][2], a3[CTW][2], a2[CTW][2], a4[CTW][2];
 #pragma unroll
@@ -1227,7 +1227,7 @@ __device__ __forceinline__ void gates_body(const BwdParams& p, float* smem, long
             a4[m][0][e] = x4[0][e] + cst * x4[2][e];
         }
     }
-    lds_barrier();  // every wave has read the operands: the buffer takes A1..A4
+    __syncthreads();  // every wave has read the operands: the buffer takes A1..A4
 #pragma unroll
     for (int m = 0; m < CTW; ++m) {
         const int col = 16 * (CTW * w + m) + ln;
@@ -1242,7 +1242,7 @@ __device__ __forceinline__ void gates_body(const BwdParams& p, float* smem, long
                 sA4[r][col] = a4[m][b][e];
             }
     }
-    lds_barrier();
+    __syncthreads();
     const float* DdQg = D + i;
     const float* DdKg = D + BC * DK + i;
     const float* DdKd = D + 2 * BC * DK + i;
@@ -1286,7 +1286,7 @@ __device__ __forceinline__ void gates_body(const BwdParams& p, float* smem, long
         }
     }
     sX[h][2][i] = kdsum;
-    lds_barrier();
+    __syncthreads();
     if (h == NH - 1) {
         float tot = 0.f;
 #pragma unroll
@@ -1303,7 +1303,7 @@ __device__ __forceinline__ void gates_body(const BwdParams& p, float* smem, long
         for (int u = 0; u < RPT; ++u) tot += sA2[r0 + u][i];
         sX[h][3][i] = tot;
     }
-    lds_barrier();
+    __syncthreads();
     {
         // d log alpha: reverse cumulative sum of dG over the chunk
         float run = 0.f;
@@ -1371,7 +1371,7 @@ __device__ __forceinline__ void gates_body(const BwdParams& p, float* smem, long
         }
         if (p.pre) sX[h][0][i] = dAsum;
     }
-    lds_barrier();
+    __syncthreads();
     if (p.pre && p.stab) {
         // dl = dr - mean over channels of dr; dA = dl / (A + eps)
         if (tid < BC) {
@@ -1379,7 +1379,7 @@ __device__ __forceinline__ void gates_body(const BwdParams& p, float* smem, long
             for (int ii = 0; ii < DK; ++ii) m += sA2[tid][ii];
             sDrm[tid] = m * (1.f / DK);
         }
-        lds_barrier();
+        __syncthreads();
         float A = Ain, dAsum = 0.f;
 #pragma unroll
         for (int u = 0; u < RPT; ++u) {
@@ -1390,7 +1390,7 @@ __device__ __forceinline__ void gates_body(const BwdParams& p, float* smem, long
             dAsum += dA;
         }
         sX[h][0][i] = dAsum;
-        lds_barrier();
+        __syncthreads();
     }
     if (p.pre) {
         float suf = 0.f;

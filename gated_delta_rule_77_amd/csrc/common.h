@@ -43,17 +43,6 @@ __device__ __forceinline__ float load_in(const void* p, long i) {
         return static_cast<const float*>(p)[i];
 }
 
-// Workgroup barrier that orders LDS accesses only.  __syncthreads() also waits
-// for every global load and store the wave has in flight (its fence covers
-// all memory); where the waves share data through LDS alone, this barrier
-// lets stores drain and prefetches stay in flight across it.  A value loaded
-// from global memory is still waited for where it is used.
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
