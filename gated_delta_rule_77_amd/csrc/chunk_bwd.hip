@@ -19,7 +19,7 @@
 // and from those to q, k, v and the gates through the pairwise decays.
 //
 // Kernels, in launch order:
-//   bwd_ksum / bwd_kscan   preconditioner: running k (.) k before each chunk
+//   bwd_ksum / bwd_scan    preconditioner: running k (.) k before each chunk
 //   bwd_prep               per chunk: Kg, Qg, Kd, Vw, M, P, e^G_C (the record)
 //   bwd_states             per (b, h, 32 value columns), both passes side by
 //                          side: chunks in order (the chunk start states S
@@ -28,7 +28,7 @@
 //                          dT, dGamma_C), fp32 16x16x4 MFMAs, then
 //                          the pairwise sums (MFMA) and dq, dk, dv, d log alpha,
 //                          dbeta, dgamma, and the preconditioner's dA
-//   bwd_dA_scan / bwd_dA_apply   preconditioner: dk += 2 k (.) sum_{s>=t} dA_s
+//   bwd_scan (reverse) / bwd_dA_apply   preconditioner: dk += 2 k (.) sum_{s>=t} dA_s
 //
 // Every product is an fp32 MFMA (exact fp32 products, fp32 accumulation) or
 // fp32 VALU.  The pairwise decays e^(G_r - G_s) inside a chunk enter the MFMA
@@ -234,26 +234,58 @@ __global__ void __launch_bounds__(DK) bwd_ksum_kernel(BwdParams p) {
     p.ksum[(bh * p.nc + c) * DK + i] = s;
 }
 
-template <int DK>
-__global__ void __launch_bounds__(DK) bwd_kscan_kernel(BwdParams p) {
-    const long bh = blockIdx.x;
-    const int i = threadIdx.x;
-    float run = p.A0 ? p.A0[bh * DK + i] : 0.f;
-    long c = 0;
-    for (; c + 8 <= p.nc; c += 8) {
-        float x[8];
+// Exclusive running sum over the chunks of each (b, h) and channel, forward
+// (out[c] = init + sum of in[c'] for c' < c) or reverse (REV: the sum over
+// c' > c), with the grand total (init + every chunk) written to `total` if
+// given.  One workgroup per (b, h, 32 channels): thread (segment, channel)
+// sums a run of chunks, the segment totals are prefixed through LDS, and a
+// second pass writes.  Each run is a chain of dependent loads, so the runs
+// are kept short (32 segments per head).
+constexpr int SCAN_SEG = 32;
+constexpr int SCAN_CH = 32;
+template <int DK, bool REV>
+__global__ void __launch_bounds__(SCAN_SEG * SCAN_CH) bwd_scan_kernel(const float* in, float* out, const float* init,
+                                                                      float* total, long nc) {
+    static_assert(DK % SCAN_CH == 0, "whole channel groups");
+    __shared__ float tot[SCAN_SEG][SCAN_CH];
+    const long bh = blockIdx.x / (DK / SCAN_CH);
+    const int ci = threadIdx.x % SCAN_CH;
+    const int i = static_cast<int>(blockIdx.x % (DK / SCAN_CH)) * SCAN_CH + ci;
+    const int sg = threadIdx.x / SCAN_CH;
+    const long len = (nc + SCAN_SEG - 1) / SCAN_SEG;
+    const long q0 = min(sg * len, nc), q1 = min(q0 + len, nc);  // positions in scan order
+    auto at = [&](long q) { return (bh * nc + (REV ? nc - 1 - q : q)) * DK + i; };
+    float sum = 0.f;
+    long q = q0;
+    for (; q + 8 <= q1; q += 8) {
+        float v[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) x[u] = p.ksum[(bh * p.nc + c + u) * DK + i];
+        for (int u = 0; u < 8; ++u) v[u] = in[at(q + u)];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) sum += v[u];
+    }
+    for (; q < q1; ++q) sum += in[at(q)];
+    tot[sg][ci] = sum;
+    __syncthreads();
+    float run = init ? init[bh * DK + i] : 0.f;
+    for (int s2 = 0; s2 < sg; ++s2) run += tot[s2][ci];
+    q = q0;
+    for (; q + 8 <= q1; q += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = in[at(q + u)];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            p.apre[(bh * p.nc + c + u) * DK + i] = run;
-            run += x[u];
+            out[at(q + u)] = run;
+            run += v[u];
         }
     }
-    for (; c < p.nc; ++c) {
-        p.apre[(bh * p.nc + c) * DK + i] = run;
-        run += p.ksum[(bh * p.nc + c) * DK + i];
+    for (; q < q1; ++q) {
+        const float v = in[at(q)];
+        out[at(q)] = run;
+        run += v;
     }
+    if (total && sg == SCAN_SEG - 1) total[bh * DK + i] = run;
 }
 
 // ---------------------------------------------------------------------------
@@ -1440,28 +1472,6 @@ __global__ void __launch_bounds__(NT, 2) bwd_grads_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------
 // preconditioner: dk += 2 k (.) sum_{s >= t} dA_s, dA0
 // ---------------------------------------------------------------------------
-template <int DK>
-__global__ void __launch_bounds__(DK) bwd_dA_scan_kernel(BwdParams p) {
-    const long bh = blockIdx.x;
-    const int i = threadIdx.x;
-    float run = 0.f;
-    long c = p.nc - 1;
-    for (; c >= 7; c -= 8) {
-        float x[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) x[u] = p.dAc[(bh * p.nc + c - u) * DK + i];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            p.dAsuf[(bh * p.nc + c - u) * DK + i] = run;
-            run += x[u];
-        }
-    }
-    for (; c >= 0; --c) {
-        p.dAsuf[(bh * p.nc + c) * DK + i] = run;
-        run += p.dAc[(bh * p.nc + c) * DK + i];
-    }
-    if (p.dA0) p.dA0[bh * DK + i] = run;
-}
 
 template <int DK, bool BF16>
 __global__ void __launch_bounds__(NT) bwd_dA_apply_kernel(BwdParams p) {
@@ -1535,7 +1545,8 @@ hipError_t run_bwd(const pdn_chunk_bwd_args& a, const BwdParams& p, hipStream_t 
     (void)a;
     if (p.pre) {
         bwd_ksum_kernel<DK, BF16><<<nch, DK, 0, s>>>(p);
-        bwd_kscan_kernel<DK><<<nbh, DK, 0, s>>>(p);
+        bwd_scan_kernel<DK, false><<<nbh * (DK / SCAN_CH), SCAN_SEG * SCAN_CH, 0, s>>>(p.ksum, p.apre, p.A0, nullptr,
+                                                                                   p.nc);
     }
     if (p.stab) bwd_prep_kernel<DK, BF16, true><<<nch, NT, 0, s>>>(p);
     else bwd_prep_kernel<DK, BF16, false><<<nch, NT, 0, s>>>(p);
@@ -1544,7 +1555,8 @@ hipError_t run_bwd(const pdn_chunk_bwd_args& a, const BwdParams& p, hipStream_t 
     else bwd_states_kernel<DK, JT><<<sgrid, NT, 0, s>>>(p, static_cast<long>(ntl));
     bwd_grads_kernel<DK, BF16><<<nch, NT, 0, s>>>(p);
     if (p.pre) {
-        bwd_dA_scan_kernel<DK><<<nbh, DK, 0, s>>>(p);
+        bwd_scan_kernel<DK, true><<<nbh * (DK / SCAN_CH), SCAN_SEG * SCAN_CH, 0, s>>>(p.dAc, p.dAsuf, nullptr, p.dA0,
+                                                                                  p.nc);
         bwd_dA_apply_kernel<DK, BF16><<<nch, NT, 0, s>>>(p);
     }
     return hipGetLastError();

@@ -260,15 +260,19 @@ __global__ void __launch_bounds__(KSQ_NTHR) vec_ksq_kernel(const uint16_t* k, fl
 }
 
 // Exclusive running sum over the chunks of each (b, h), in place, starting
-// from A0; the total goes to AT.  One workgroup per (b, h): thread (segment,
-// channel) sums its run of chunks, the segment totals are prefixed through
-// LDS, and a second pass writes the running values.
-constexpr int KSCAN_SEG = 8;
-__global__ void __launch_bounds__(KSCAN_SEG * DK) vec_kscan_kernel(float* ks, const float* A0, float* AT, long nc) {
-    __shared__ float tot[KSCAN_SEG][DK];
-    const long bh = blockIdx.x;
-    const int i = threadIdx.x % DK;
-    const int sg = threadIdx.x / DK;
+// from A0; the total goes to AT.  One workgroup per (b, h, 32 channels):
+// thread (segment, channel) sums its run of chunks, the segment totals are
+// prefixed through LDS, and a second pass writes the running values.  Each
+// thread's run is a chain of dependent loads, so the runs are kept short
+// (32 segments per head).
+constexpr int KSCAN_SEG = 32;
+constexpr int KSCAN_CH = 32;
+__global__ void __launch_bounds__(KSCAN_SEG * KSCAN_CH) vec_kscan_kernel(float* ks, const float* A0, float* AT, long nc) {
+    __shared__ float tot[KSCAN_SEG][KSCAN_CH];
+    const long bh = blockIdx.x / (DK / KSCAN_CH);
+    const int ci = threadIdx.x % KSCAN_CH;
+    const int i = static_cast<int>(blockIdx.x % (DK / KSCAN_CH)) * KSCAN_CH + ci;
+    const int sg = threadIdx.x / KSCAN_CH;
     const long len = (nc + KSCAN_SEG - 1) / KSCAN_SEG;
     const long c0 = min(sg * len, nc), c1 = min(c0 + len, nc);
     float* col = ks + bh * nc * DK + i;
@@ -282,10 +286,10 @@ __global__ void __launch_bounds__(KSCAN_SEG * DK) vec_kscan_kernel(float* ks, co
         for (int u = 0; u < 8; ++u) sum += v[u];
     }
     for (; c < c1; ++c) sum += col[c * DK];
-    tot[sg][i] = sum;
+    tot[sg][ci] = sum;
     __syncthreads();
     float run = A0 ? A0[bh * DK + i] : 0.0f;
-    for (int q = 0; q < sg; ++q) run += tot[q][i];
+    for (int q = 0; q < sg; ++q) run += tot[q][ci];
     c = c0;
     for (; c + 8 <= c1; c += 8) {
         float v[8];
@@ -1338,7 +1342,7 @@ hipError_t launch_chunk_vec(const pdn_chunk_fwd_args& a, hipStream_t stream) {
         const long nid = nbh * nc;
         vec_ksq_kernel<<<dim3(static_cast<unsigned>((nid + 3) / 4)), dim3(KSQ_NTHR), 0, stream>>>(
             static_cast<const uint16_t*>(a.k), ksum, a.T, nc, nid);
-        vec_kscan_kernel<<<dim3(static_cast<unsigned>(nbh)), dim3(KSCAN_SEG * DK), 0, stream>>>(
+        vec_kscan_kernel<<<dim3(static_cast<unsigned>(nbh * (DK / KSCAN_CH))), dim3(KSCAN_SEG * KSCAN_CH), 0, stream>>>(
             ksum, a.precond_A0, a.precond_AT, nc);
     }
     PrepParams pp;
