@@ -323,6 +323,50 @@ __global__ void __launch_bounds__(NT, 3) bwd_prep_kernel(BwdParams p) {
     const int i = tid % DK, h = tid / DK, r0 = h * RPT;
     const ColView<DK, BF16> cv(p, bh, t0, i);
     const bool has_decay = p.amode != PDN_ALPHA_NONE;
+    // The value tile Vw = v (.) scale(gamma), in items of 8 consecutive
+    // columns of one row (items past the tile reread item 0, rows past T
+    // reread row T - 1; both are masked when written).  With bf16 inputs the
+    // loads are issued first of all, so that their round trip overlaps the
+    // scans below; the other instantiations have no registers to spare for
+    // that and issue them where the tile is written.
+    constexpr int MAXI = BC * 256 / 8 / NT;  // dv <= 256
+    constexpr bool kEarly = BF16 && !STAB;
+    const int nit = BC * p.dv / 8;
+    const bool gsame = p.gmode == PDN_GAMMA_SAME_AS_BETA;
+    const bool gvec = gsame ? p.bmode == PDN_GATE_VEC : p.gmode == PDN_GATE_VEC;
+    const float* gbase = gsame ? p.beta : p.gamma;
+    const int gw = gsame ? DK : p.dv;
+    f32x4 vv[MAXI][2], gv[MAXI][2];
+    auto load_v = [&]() {
+#pragma unroll
+    for (int m = 0; m < MAXI; ++m) {
+        const int it = tid + m * NT < nit ? tid + m * NT : 0;
+        const int r = it / (p.dv / 8), j = 8 * (it % (p.dv / 8));
+        const long tc = bh * p.T + tclamp(p, t0 + r);
+        if constexpr (BF16) {
+            const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.v) + tc * p.dv + j);
+            const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                vv[m][e >> 1][2 * (e & 1)] = __uint_as_float(w4[e] << 16);
+                vv[m][e >> 1][2 * (e & 1) + 1] = __uint_as_float(w4[e] & 0xffff0000u);
+            }
+        } else {
+            const float* src = static_cast<const float*>(p.v) + tc * p.dv + j;
+            vv[m][0] = *reinterpret_cast<const f32x4*>(src);
+            vv[m][1] = *reinterpret_cast<const f32x4*>(src + 4);
+        }
+        if (gvec) {
+            gv[m][0] = *reinterpret_cast<const f32x4*>(gbase + tc * gw + j);
+            gv[m][1] = *reinterpret_cast<const f32x4*>(gbase + tc * gw + j + 4);
+        } else {
+            const float x = gbase[tc];
+            gv[m][0] = f32x4{x, x, x, x};
+            gv[m][1] = gv[m][0];
+        }
+    }
+    };
+    if constexpr (kEarly) load_v();
     // every load of the own rows first
     float kk[RPT], qq[RPT], g[RPT], bb[RPT];
 #pragma unroll
@@ -418,35 +462,21 @@ __global__ void __launch_bounds__(NT, 3) bwd_prep_kernel(BwdParams p) {
         }
     }
     float* Rvw = R + rec_vw<DK>(p.dv);
-    {
-        // at most BC * 256 / NT = 32 values per thread.  Every load is issued
-        // before any value is used: indices past the tile reread element 0,
-        // rows past T are clamped, and the masks come afterwards (loads behind
-        // a branch made the compiler wait for each one in turn: 32 round
-        // trips instead of one).
-        constexpr int MAXV = BC * 256 / NT;
-        const int nv = BC * p.dv;
-        const bool same = p.gmode == PDN_GAMMA_SAME_AS_BETA;
-        const bool gvec = same ? p.bmode == PDN_GATE_VEC : p.gmode == PDN_GATE_VEC;
-        const float* gbase = same ? p.beta : p.gamma;
-        const int gw = same ? DK : p.dv;
-        float vv[MAXV], gg[MAXV];
+    if constexpr (!kEarly) load_v();
 #pragma unroll
-        for (int m = 0; m < MAXV; ++m) {
-            const int idx = tid + m * NT < nv ? tid + m * NT : 0;
-            const int r = idx / p.dv, j = idx % p.dv;
-            const long tc = bh * p.T + tclamp(p, t0 + r);
-            vv[m] = load_in<BF16>(p.v, tc * p.dv + j);
-            gg[m] = gbase[gvec ? tc * gw + j : tc];
-        }
+    for (int m = 0; m < MAXI; ++m) {
+        const int it = tid + m * NT;
+        const int r = it / (p.dv / 8), j = 8 * (it % (p.dv / 8));
+        const bool live = t0 + r < p.T;
+        if (it < nit)
 #pragma unroll
-        for (int m = 0; m < MAXV; ++m) {
-            const int idx = tid + m * NT;
-            const bool live = t0 + idx / p.dv < p.T;
-            const float v = live ? vv[m] : 0.f;
-            const float sc = value_scale(p.kmode, p.gmode, live ? gg[m] : 1.f);
-            if (idx < nv) Rvw[idx] = v * sc;
-        }
+            for (int hh = 0; hh < 2; ++hh) {
+                f32x4 o;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    o[e] = live ? vv[m][hh][e] * value_scale(p.kmode, p.gmode, gv[m][hh][e]) : 0.f;
+                *reinterpret_cast<f32x4*>(Rvw + r * p.dv + j + 4 * hh) = o;
+            }
     }
     __syncthreads();
     // six 16 x 16 tiles: T (0,0), (1,1), (1,0) and P likewise; wave w takes
