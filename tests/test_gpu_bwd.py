@@ -256,7 +256,7 @@ def test_bwd_without_dST_and_S0():
     check_bwd("bwd no dST no S0 T150", w, with_dST=False)
 
 
-@pytest.mark.parametrize("dv", [32, 256])
+@pytest.mark.parametrize("dv", [32, 96, 256])
 def test_bwd_value_widths(dv):
     w = rand_workload(8 + dv, 1, 2, 120, 128, dv, synth.ALPHA_VEC, synth.GATE_VEC,
                       synth.GATE_VEC, True, True)
