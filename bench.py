@@ -97,7 +97,9 @@ def _code_only(path: str) -> bytes:
 def kernel_source_hash(workload: str = None) -> str:
     """Hash of what decides the kernels' machine code: the HIP sources (all of
     them, or those of one workload's dominant kernel) and the C-ABI header,
-    comments and whitespace aside, and the build script (compiler flags)."""
+    comments and whitespace aside, and the compiler flags those sources are
+    built with (the common flags and each source's own)."""
+    from gated_delta_rule_77_amd import build
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gated_delta_rule_77_amd", "csrc")
     files = KERNEL_SOURCES[workload] if workload else sorted(
@@ -105,7 +107,10 @@ def kernel_source_hash(workload: str = None) -> str:
     for f in files:
         h.update(_code_only(os.path.join(csrc, f)))
     h.update(_code_only(os.path.join(ROOT, "include", "pdn.h")))
-    h.update(open(os.path.join(ROOT, "gated_delta_rule_77_amd", "build.py"), "rb").read())
+    flags = [build.ARCH] + [c for c in build.COMMON if not c.startswith("-I")]
+    for f in files:
+        flags += [f] + list(build.EXTRA.get(f, []))
+    h.update(json.dumps(flags).encode())
     return h.hexdigest()[:16]
 
 
