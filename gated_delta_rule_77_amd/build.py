@@ -27,16 +27,17 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-I" + INCLUDE, "-I" + CSRC,
 
 
 # Per-source extra flags.  The prefill kernels keep their MFMA accumulators in
-# ordinary VGPRs (no accumulator-register copies around every VALU use).  The
-# per-channel-gate kernels and two of the backward kernels (the sources
-# chunk_bwd_ilp.hip instantiates) are scheduled for instruction-level
-# parallelism: the same operations and results, reordered (B2 H32 T8192
-# prefill 0.81 -> 0.79 ms per call; backward gradient kernel and 32-column
-# state passes 2-3% faster).  The other kernels measured equal or slower with
-# that scheduler.
+# ordinary VGPRs (no accumulator-register copies around every VALU use).  Two
+# of the backward kernels (the ones chunk_bwd_ilp.hip instantiates: the
+# gradient kernel and the 32-column state passes) are scheduled for
+# instruction-level parallelism: the same operations and results, reordered,
+# 2-4% faster.  The other kernels measured equal or slower with that
+# scheduler (the per-channel-gate preparation kernel 3% faster with symmetric
+# keys but 10-20% slower with asymmetric keys or the stabilised
+# preconditioner).
 ILP = ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]
 EXTRA = {"chunk_fact.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-         "chunk_vec.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"] + ILP,
+         "chunk_vec.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
          "chunk_bwd_ilp.hip": ILP}
 
 
