@@ -39,6 +39,11 @@
  *     global state; it never frees or retains caller memory.
  *   - Work is queued asynchronously on `stream` (a hipStream_t; NULL = the
  *     default stream).  Outputs are valid once the stream is synchronised.
+ *     The stream must belong to the current HIP device, the one whose memory
+ *     the pointers address: grids are sized for the current device, and
+ *     pdn_chunk_fwd_noalloc takes its scratch there.
+ *   - The calls only launch kernels (no allocation, memset or copy), so they
+ *     can be captured into a HIP graph and replayed.
  *   - Arguments are validated on the host BEFORE any launch; an invalid call
  *     returns a negative PDN_E* code, touches no memory and launches nothing.
  *     No C++ exception crosses this boundary.
