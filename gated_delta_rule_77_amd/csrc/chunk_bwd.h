@@ -1389,7 +1389,6 @@ __device__ __forceinline__ void gates_body(const BwdParams& p, float* smem, long
         for (int u = RPT - 1; u >= 0; --u) {
             const int r = r0 + u;
             run += sA2[r][i];
-            const long t = t0 + r;
             sA4[r][i] = ((dead >> u) & 1u) ? 0.f : run;
         }
         // stored after the loop: a store between the steps above would make
