@@ -27,17 +27,19 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-I" + INCLUDE, "-I" + CSRC,
 
 
 # Per-source extra flags.  The prefill kernels keep their MFMA accumulators in
-# ordinary VGPRs (no accumulator-register copies around every VALU use).  Two
-# of the backward kernels (the ones chunk_bwd_ilp.hip instantiates: the
-# gradient kernel and the 32-column state passes) are scheduled for
-# instruction-level parallelism: the same operations and results, reordered,
-# 2-4% faster.  The other kernels measured equal or slower with that
-# scheduler (the per-channel-gate preparation kernel 3% faster with symmetric
-# keys but 10-20% slower with asymmetric keys or the stabilised
-# preconditioner).
+# ordinary VGPRs (no accumulator-register copies around every VALU use).  The
+# kernels that the *_ilp.hip sources instantiate are scheduled for
+# instruction-level parallelism: the same operations and results, reordered.
+# That made the backward's gradient kernel and 32-column state passes 2-4%
+# faster and the per-channel-gate preparation kernel with symmetric keys and
+# per-channel decay and gain 3% faster; the other kernels measured equal or
+# slower with it (that preparation kernel 10-20% slower with asymmetric keys or
+# the stabilised preconditioner).
 ILP = ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]
-EXTRA = {"chunk_fact.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-         "chunk_vec.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+EXTRA = {"chunk_fact.hip": VGPR_FORM,
+         "chunk_vec.hip": VGPR_FORM,
+         "chunk_vec_ilp.hip": VGPR_FORM + ILP,
          "chunk_bwd_ilp.hip": ILP}
 
 
